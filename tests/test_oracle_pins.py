@@ -1,0 +1,424 @@
+"""Pins for the CPU oracle: it is checked against things other than itself.
+
+Each test ties an oracle function to something the pages or the mathematics fix:
+  * a hand-worked index table (tests/golden/index_w2.txt) and the exact pair-count invariant;
+  * a brute-force per-output sum over window positions (no matrices, no index table);
+  * the per-window closed form: WBMM equals a zero-padded (2w-1)x(2w-1) depthwise correlation of
+    each window with the 180-degree rotated table, computed with torch's conv2d (CPU, float64)
+    and with a numpy shift-and-add;
+  * exact special cases: one-hot tables give the identity / windowed shifts, all-ones data counts
+    real pixels per window, the dT of all-ones data counts pairs per offset;
+  * the adjoint identity, torch autograd of the closed form, and finite differences for the
+    backward;
+  * torch's conv2d for the 3x3 depthwise mix and its gradients.
+A plausible slip in the oracle (a flipped sign, a transposed matrix, a dropped term, a wrong
+crop/pad) fails at least one of these.
+"""
+import os
+
+import numpy as np
+import pytest
+import torch
+import torch.nn.functional as F
+
+from oracle import wbmm_oracle as O
+from receptive_field_spatial_amd import synth
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def rnd(shape, sigma=1.0, seed=0):
+    return synth.normal_f32(shape, sigma, seed).astype(np.float64)
+
+
+# ----------------------------------------------------------------------------- brute force
+def brute_force(x, T, w):
+    """Per-output sum over the positions of the output's own window (pure Python loops)."""
+    B, C, H, W = x.shape
+    out = np.zeros((B, C, H, W))
+    for b in range(B):
+        for c in range(C):
+            for py in range(H):
+                for px in range(W):
+                    wy0, wx0 = (py // w) * w, (px // w) * w
+                    acc = 0.0
+                    for qy in range(wy0, min(wy0 + w, H)):
+                        for qx in range(wx0, min(wx0 + w, W)):
+                            acc += T[c, py - qy + w - 1, px - qx + w - 1] * x[b, c, qy, qx]
+                    out[b, c, py, px] = acc
+    return out
+
+
+def windows_of(x, w):
+    """(B, C, Hp, Wp) padded map -> (B*nH*nW, C, w, w) stack of windows."""
+    B, C, Hp, Wp = x.shape
+    nH, nW = Hp // w, Wp // w
+    return x.reshape(B, C, nH, w, nW, w).transpose(0, 2, 4, 1, 3, 5).reshape(-1, C, w, w)
+
+
+def unwindows(t, B, Hp, Wp, w):
+    C = t.shape[1]
+    nH, nW = Hp // w, Wp // w
+    return t.reshape(B, nH, nW, C, w, w).transpose(0, 3, 1, 4, 2, 5).reshape(B, C, Hp, Wp)
+
+
+def closed_form_torch(x, T, w):
+    """Per-window depthwise correlation with rot180(T), zero padding w-1, via torch conv2d."""
+    B, C, H, W = x.shape
+    Hp, Wp = O.padded_hw(H, W, w)
+    xp = np.zeros((B, C, Hp, Wp))
+    xp[:, :, :H, :W] = x
+    win = torch.from_numpy(windows_of(xp, w))
+    kern = torch.from_numpy(np.ascontiguousarray(T[:, ::-1, ::-1]))[:, None]
+    out = F.conv2d(win, kern, padding=w - 1, groups=C).numpy()
+    return unwindows(out, B, Hp, Wp, w)[:, :, :H, :W]
+
+
+def closed_form_shift_add(x, T, w):
+    """Same closed form as a numpy shift-and-add over the (2w-1)^2 offsets inside each window."""
+    B, C, H, W = x.shape
+    Hp, Wp = O.padded_hw(H, W, w)
+    xp = np.zeros((B, C, Hp, Wp))
+    xp[:, :, :H, :W] = x
+    win = windows_of(xp, w)
+    out = np.zeros_like(win)
+    for dy in range(-(w - 1), w):
+        for dx in range(-(w - 1), w):
+            # out[y, x] += T[dy + w - 1, dx + w - 1] * in[y - dy, x - dx]
+            ys, yd = (slice(0, w - dy), slice(dy, w)) if dy >= 0 else (slice(-dy, w), slice(0, w + dy))
+            xs, xd = (slice(0, w - dx), slice(dx, w)) if dx >= 0 else (slice(-dx, w), slice(0, w + dx))
+            out[:, :, yd, xd] += T[None, :, dy + w - 1, dx + w - 1, None, None] * win[:, :, ys, xs]
+    return unwindows(out, B, Hp, Wp, w)[:, :, :H, :W]
+
+
+# ----------------------------------------------------------------------------- index / matrix
+def test_index_hand_worked_w2():
+    want = np.loadtxt(os.path.join(GOLDEN, "index_w2.txt"), dtype=np.int64)
+    got = O.build_index(2)
+    assert got.dtype == np.int32
+    assert np.array_equal(got, want)
+
+
+def test_index_w1_is_single_entry():
+    assert np.array_equal(O.build_index(1), np.array([[0]], dtype=np.int32))
+
+
+@pytest.mark.parametrize("w", [1, 2, 3, 4, 7, 14, 28])
+def test_index_pair_counts(w):
+    """Offset (dy, dx) occurs (w-|dy|)(w-|dx|) times among the d*d pairs; all in range."""
+    idx = O.build_index(w)
+    L = (2 * w - 1) ** 2
+    assert idx.min() >= 0 and idx.max() < L
+    counts = np.bincount(idx.ravel(), minlength=L).reshape(2 * w - 1, 2 * w - 1)
+    run = w - np.abs(np.arange(-(w - 1), w))
+    assert np.array_equal(counts, np.outer(run, run))
+    assert counts.sum() == w ** 4
+
+
+@pytest.mark.parametrize("w", [3, 7, 14])
+def test_matrix_structure(w):
+    C = 3
+    T = rnd((C, 2 * w - 1, 2 * w - 1), seed=1).astype(np.float32)
+    M = O.build_matrix(T, w)
+    assert M.dtype == np.float32 and M.shape == (C, w * w, w * w)
+    # diagonal = table centre
+    for c in range(C):
+        assert np.all(np.diag(M[c]) == T[c, w - 1, w - 1])
+    # entry depends only on the position difference (block-Toeplitz with Toeplitz blocks)
+    y, x = np.divmod(np.arange(w * w), w)
+    for c in range(C):
+        for i in range(0, w * w, max(1, w * w // 7)):
+            for j in range(0, w * w, max(1, w * w // 5)):
+                assert M[c, i, j] == T[c, y[i] - y[j] + w - 1, x[i] - x[j] + w - 1]
+    # rotating the table by 180 degrees transposes every M_c exactly
+    Mr = O.build_matrix(np.ascontiguousarray(T[:, ::-1, ::-1]), w)
+    assert np.array_equal(Mr, M.transpose(0, 2, 1))
+
+
+# ----------------------------------------------------------------------------- forward
+def test_forward_brute_force_tiny_workload():
+    wl = synth.WORKLOADS["tiny_w7"]
+    inp = synth.draw_inputs(wl)
+    x, T = inp["x"].astype(np.float64), inp["T"].astype(np.float64)
+    got = O.wbmm_forward(x, wl.w, T=T)
+    want = brute_force(x, T, wl.w)
+    assert np.allclose(got, want, rtol=0, atol=1e-13)
+
+
+@pytest.mark.parametrize("B,C,H,W,w", [(2, 3, 10, 13, 4), (1, 2, 5, 5, 5), (1, 2, 7, 3, 3),
+                                       (2, 1, 4, 4, 1)])
+def test_forward_brute_force_ragged(B, C, H, W, w):
+    x = rnd((B, C, H, W), seed=2)
+    T = rnd((C, 2 * w - 1, 2 * w - 1), 0.5, seed=3)
+    got = O.wbmm_forward(x, w, T=T)
+    assert got.shape == (B, C, H, W)
+    assert np.allclose(got, brute_force(x, T, w), rtol=0, atol=1e-12)
+
+
+@pytest.mark.parametrize("B,C,H,W,w", [(1, 8, 28, 28, 7), (2, 3, 28, 28, 14), (1, 2, 30, 17, 6),
+                                       (1, 2, 56, 56, 28)])
+def test_forward_closed_form(B, C, H, W, w):
+    x = rnd((B, C, H, W), seed=4)
+    T = rnd((C, 2 * w - 1, 2 * w - 1), 0.02, seed=5)
+    got = O.wbmm_forward(x, w, T=T)
+    ref_t = closed_form_torch(x, T, w)
+    ref_n = closed_form_shift_add(x, T, w)
+    scale = np.abs(ref_t).max()
+    assert np.abs(got - ref_t).max() <= 1e-12 * scale
+    assert np.abs(got - ref_n).max() <= 1e-12 * scale
+
+
+def test_forward_unrotated_kernel_is_not_it():
+    """Sanity of the orientation pin: the unrotated table gives a visibly different result."""
+    w = 4
+    x = rnd((1, 2, 8, 8), seed=6)
+    T = rnd((2, 7, 7), seed=7)
+    got = O.wbmm_forward(x, w, T=T)
+    wrong = closed_form_torch(x, np.ascontiguousarray(T[:, ::-1, ::-1]), w)
+    assert np.abs(got - wrong).max() > 1e-2
+
+
+@pytest.mark.parametrize("w", [1, 3, 7])
+def test_one_hot_centre_is_identity(w):
+    x = rnd((2, 2, 2 * w + 1, 3 * w - 1), seed=8)
+    T = np.zeros((2, 2 * w - 1, 2 * w - 1))
+    T[:, w - 1, w - 1] = 1.0
+    assert np.array_equal(O.wbmm_forward(x, w, T=T), x)
+
+
+@pytest.mark.parametrize("a,b", [(1, 0), (0, 1), (-2, 1), (3, -3), (-4, -4)])
+def test_one_hot_offset_is_windowed_shift(a, b):
+    """T one-hot at offset (a, b): out(y, x) = in(y - a, x - b) inside the window, else 0."""
+    w = 5
+    B, C, H, W = 1, 2, 10, 15
+    x = rnd((B, C, H, W), seed=9)
+    T = np.zeros((C, 2 * w - 1, 2 * w - 1))
+    T[:, a + w - 1, b + w - 1] = 1.0
+    got = O.wbmm_forward(x, w, T=T)
+    want = np.zeros_like(x)
+    for py in range(H):
+        for px in range(W):
+            qy, qx = py - a, px - b
+            if (0 <= qy < H and 0 <= qx < W and qy // w == py // w and qx // w == px // w):
+                want[:, :, py, px] = x[:, :, qy, qx]
+    assert np.array_equal(got, want)
+
+
+def test_ones_count_real_pixels_per_window():
+    """x = 1 and T = 1: each output equals the number of unpadded pixels in its window."""
+    w = 4
+    H, W = 10, 13
+    x = np.ones((1, 1, H, W))
+    T = np.ones((1, 2 * w - 1, 2 * w - 1))
+    got = O.wbmm_forward(x, w, T=T)
+    for py in range(H):
+        for px in range(W):
+            rows = min(w, H - (py // w) * w)
+            cols = min(w, W - (px // w) * w)
+            assert got[0, 0, py, px] == rows * cols
+
+
+def test_forward_linearity():
+    w = 4
+    x1, x2 = rnd((1, 2, 8, 12), seed=10), rnd((1, 2, 8, 12), seed=11)
+    T1, T2 = rnd((2, 7, 7), seed=12), rnd((2, 7, 7), seed=13)
+    f = O.wbmm_forward
+    assert np.allclose(f(2 * x1 - 3 * x2, w, T=T1), 2 * f(x1, w, T=T1) - 3 * f(x2, w, T=T1), atol=1e-12)
+    assert np.allclose(f(x1, w, T=0.5 * T1 + T2), 0.5 * f(x1, w, T=T1) + f(x1, w, T=T2), atol=1e-12)
+
+
+def test_cached_matrix_path_matches_table_path():
+    w = 7
+    x = rnd((2, 3, 14, 21), seed=14)
+    T = rnd((3, 13, 13), seed=15)
+    M = O.build_matrix(T, w)
+    assert np.array_equal(O.wbmm_forward(x, w, M=M), O.wbmm_forward(x, w, T=T))
+
+
+# ----------------------------------------------------------------------------- fold
+def test_fold_identity_two_window_sizes():
+    """Folding T_sub into M equals adding a separate s-window WBMM of the same padded map."""
+    w, s = 14, 7
+    x = rnd((2, 3, 28, 30), seed=16)
+    T = rnd((3, 27, 27), 0.02, seed=17).astype(np.float32)
+    Ts = rnd((3, 13, 13), 0.02, seed=18).astype(np.float32)
+    Mf = O.fold_hier(O.build_matrix(T, w), Ts, w, s)
+    got = O.wbmm_forward(x, w, M=Mf)
+    # s-window WBMM on the w-padded map, then crop
+    Hp, Wp = O.padded_hw(28, 30, w)
+    xp = np.zeros((2, 3, Hp, Wp))
+    xp[:, :, :28, :30] = x
+    want = (O.wbmm_forward(x, w, T=T.astype(np.float64))
+            + O.wbmm_forward(xp, s, T=Ts.astype(np.float64))[:, :, :28, :30])
+    # the fold adds in float32, so compare at float32 resolution of M
+    assert np.abs(got - want).max() <= 1e-6
+
+
+def test_fold_touches_only_same_subwindow_pairs():
+    w, s = 14, 7
+    T = rnd((2, 27, 27), 0.02, seed=19).astype(np.float32)
+    Ts = rnd((2, 13, 13), 0.02, seed=20).astype(np.float32)
+    M = O.build_matrix(T, w)
+    Mf = O.fold_hier(M, Ts, w, s)
+    assert Mf.dtype == np.float32
+    y, x = np.divmod(np.arange(w * w), w)
+    n_changed_pairs = 0
+    for i in range(w * w):
+        for j in range(w * w):
+            same = (y[i] // s == y[j] // s) and (x[i] // s == x[j] // s)
+            if same:
+                n_changed_pairs += 1
+                add = Ts[:, y[i] % s - y[j] % s + s - 1, x[i] % s - x[j] % s + s - 1]
+                assert np.array_equal(Mf[:, i, j], (M[:, i, j] + add).astype(np.float32))
+            else:
+                assert np.array_equal(Mf[:, i, j], M[:, i, j])
+    assert n_changed_pairs == 4 * 49 * 49  # 4 sub-windows of 49 pixels each
+
+
+# ----------------------------------------------------------------------------- mix
+def test_mix_forward_matches_torch_conv2d():
+    z = rnd((2, 5, 9, 11), seed=21)
+    Wm = rnd((5, 3, 3), 0.1, seed=22)
+    want = F.conv2d(torch.from_numpy(z), torch.from_numpy(Wm)[:, None], padding=1, groups=5).numpy()
+    assert np.allclose(O.mix_forward(z, Wm), want, rtol=0, atol=1e-14)
+
+
+def test_mix_backward_matches_torch_autograd():
+    z = torch.from_numpy(rnd((2, 5, 9, 11), seed=23)).requires_grad_(True)
+    Wm = torch.from_numpy(rnd((5, 3, 3), 0.1, seed=24)).requires_grad_(True)
+    dy = rnd((2, 5, 9, 11), seed=25)
+    y = F.conv2d(z, Wm[:, None], padding=1, groups=5)
+    y.backward(torch.from_numpy(dy))
+    dz, dW = O.mix_backward(dy, z.detach().numpy(), Wm.detach().numpy())
+    assert np.allclose(dz, z.grad.numpy(), rtol=0, atol=1e-13)
+    assert np.allclose(dW, Wm.grad.numpy(), rtol=0, atol=1e-12)
+
+
+# ----------------------------------------------------------------------------- backward
+def test_dx_adjoint_identity():
+    w = 5
+    x = rnd((2, 3, 12, 9), seed=26)
+    g = rnd((2, 3, 12, 9), seed=27)
+    T = rnd((3, 9, 9), seed=28)
+    dx, _ = O.wbmm_backward(x, g, w, T=T)
+    lhs = np.sum(O.wbmm_forward(x, w, T=T) * g)
+    rhs = np.sum(x * dx)
+    assert abs(lhs - rhs) <= 1e-12 * abs(lhs) + 1e-12
+
+
+def test_backward_matches_torch_autograd_of_closed_form():
+    """dx and dT against autograd through the per-window conv2d route (independent of the matrix form)."""
+    w = 4
+    B, C, H, W = 2, 3, 10, 9
+    x_np = rnd((B, C, H, W), seed=29)
+    T_np = rnd((C, 7, 7), seed=30)
+    g = rnd((B, C, H, W), seed=31)
+    Hp, Wp = O.padded_hw(H, W, w)
+    x = torch.from_numpy(x_np).requires_grad_(True)
+    T = torch.from_numpy(T_np).requires_grad_(True)
+    xp = F.pad(x, (0, Wp - W, 0, Hp - H))
+    nH, nW = Hp // w, Wp // w
+    win = xp.reshape(B, C, nH, w, nW, w).permute(0, 2, 4, 1, 3, 5).reshape(-1, C, w, w)
+    out = F.conv2d(win, torch.flip(T, dims=(1, 2))[:, None], padding=w - 1, groups=C)
+    y = out.reshape(B, nH, nW, C, w, w).permute(0, 3, 1, 4, 2, 5).reshape(B, C, Hp, Wp)[:, :, :H, :W]
+    y.backward(torch.from_numpy(g))
+    dx, dT = O.wbmm_backward(x_np, g, w, T=T_np)
+    assert np.allclose(dx, x.grad.numpy(), rtol=0, atol=1e-12)
+    assert np.allclose(dT, T.grad.numpy(), rtol=0, atol=1e-11)
+
+
+def test_dT_all_ones_counts_pairs():
+    """x = 1, dz = 1, no mix: dT[c, dy, dx] = N * (w-|dy|) * (w-|dx|) exactly."""
+    w = 7
+    B, C, H, W = 3, 2, 14, 21
+    N = B * (H // w) * (W // w)
+    x = np.ones((B, C, H, W))
+    T = rnd((C, 13, 13), seed=32)
+    _, dT = O.wbmm_backward(x, np.ones_like(x), w, T=T)
+    run = w - np.abs(np.arange(-(w - 1), w))
+    for c in range(C):
+        assert np.array_equal(dT[c], N * np.outer(run, run).astype(np.float64))
+
+
+@pytest.mark.slow
+def test_dT_finite_differences_train_slice():
+    """Central differences of L(T) = sum(dY * y(T)) on a 1-channel slice of the training workload.
+
+    L is linear in T, so the central difference equals the derivative up to float64 rounding for
+    any step; the mix is included.
+    """
+    wl = synth.WORKLOADS["train_w14"]
+    inp = synth.draw_inputs(wl)
+    w = wl.w
+    x = inp["x"][:, :1].astype(np.float64)
+    T = inp["T"][:1].astype(np.float64)
+    Wm = inp["Wmix"][:1]
+    dY = inp["dY"][:, :1].astype(np.float64)
+    _, dT, _ = O.layer_backward(x, dY, w, T=T, Wmix=Wm)
+    L0 = (2 * w - 1) ** 2
+    h = 1e-2
+    fd = np.empty(L0)
+    for k in range(L0):
+        Tp = T.copy().reshape(-1)
+        Tm = T.copy().reshape(-1)
+        Tp[k] += h
+        Tm[k] -= h
+        yp, _ = O.layer_forward(x, w, T=Tp.reshape(T.shape), Wmix=Wm)
+        ym, _ = O.layer_forward(x, w, T=Tm.reshape(T.shape), Wmix=Wm)
+        fd[k] = (np.sum(dY * yp) - np.sum(dY * ym)) / (2 * h)
+    err = np.abs(fd - dT.reshape(-1)).max()
+    assert err <= 1e-9 * np.abs(dT).max()
+
+
+def test_mix_finite_differences():
+    z = rnd((1, 2, 6, 7), seed=33)
+    Wm = rnd((2, 3, 3), 0.1, seed=34)
+    dy = rnd((1, 2, 6, 7), seed=35)
+    _, dW = O.mix_backward(dy, z, Wm)
+    h = 1e-3
+    for c in range(2):
+        for u in range(3):
+            for t in range(3):
+                Wp_, Wn_ = Wm.copy(), Wm.copy()
+                Wp_[c, u, t] += h
+                Wn_[c, u, t] -= h
+                fd = (np.sum(dy * O.mix_forward(z, Wp_)) - np.sum(dy * O.mix_forward(z, Wn_))) / (2 * h)
+                assert abs(fd - dW[c, u, t]) <= 1e-10
+
+
+def test_cached_matrix_backward_matches_table_backward():
+    w = 4
+    x = rnd((2, 2, 8, 8), seed=36)
+    g = rnd((2, 2, 8, 8), seed=37)
+    T = rnd((2, 7, 7), seed=38)
+    dx1, dT1 = O.wbmm_backward(x, g, w, T=T)
+    dx2, dT2 = O.wbmm_backward(x, g, w, M=O.build_matrix(T, w))
+    assert np.array_equal(dx1, dx2) and np.array_equal(dT1, dT2)
+
+
+# ----------------------------------------------------------------------------- misc pins
+def test_receptive_field_ratio():
+    """The abstract's 7.8x per-layer receptive field: a 14x14 window covers 196 pixels, a 5x5 kernel 25."""
+    assert round((14 * 14) / (5 * 5), 1) == 7.8
+
+
+def test_bf16_rounding_bits():
+    vals = np.array([1.0, 1.0 + 2.0 ** -8, 1.0 + 3 * 2.0 ** -8, -2.5, 1.0 + 2.0 ** -7,
+                     1.0 + 2.0 ** -8 + 2.0 ** -20], dtype=np.float32)
+    bits = synth.f32_to_bf16_bits(vals)
+    # 1+2^-8 is a tie -> even (1.0); 1+3*2^-8 is a tie -> even (1+2^-6);
+    # 1+2^-8+2^-20 is above the tie -> rounds up to 1+2^-7.
+    assert list(bits) == [0x3F80, 0x3F80, 0x3F82, 0xC020, 0x3F81, 0x3F81]
+    back = synth.bf16_bits_to_f32(bits)
+    assert back[3] == -2.5 and back[2] == np.float32(1.0 + 2 ** -6)
+
+
+def test_inputs_are_seeded_and_ordered():
+    wl = synth.WORKLOADS["tiny_w7"]
+    a = synth.draw_inputs(wl, seed=0)
+    b = synth.draw_inputs(wl, seed=0)
+    assert all(np.array_equal(a[k], b[k]) for k in a)
+    rng = np.random.default_rng(0)
+    x = (rng.standard_normal((1, 8, 28, 28)) * 1.0).astype(np.float32)
+    assert np.array_equal(a["x"], x)
+    assert a["T"].shape == (8, 13, 13) and abs(float(a["T"].std()) - 0.02) < 0.004
