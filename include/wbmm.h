@@ -1,0 +1,167 @@
+/*
+ * wbmm.h — C ABI of libwbmm: WBMM (Windowed Batch Matrix Multiplication) on AMD MI355X (gfx950).
+ *
+ * WBMM cuts a feature map into non-overlapping w x w windows (d = w*w pixels), builds for every
+ * channel c a d x d matrix M_c from a compact (2w-1) x (2w-1) relative-position table T_c, and
+ * mixes every window of every image with one shared matmul out = M_c . x, with no softmax
+ * [gecl.asia reading notes, "Core Idea"; arxivdaily abstract; pith page, Fig. 1 caption].
+ *
+ * Conventions shared by every entry point:
+ *   - Index orientation: M_c[i][j] = T_c[(y_i - y_j) + w - 1][(x_i - x_j) + w - 1], in-window
+ *     position i = y_i * w + x_i (row-major); the table's first axis is vertical.
+ *   - Every pointer argument named as device memory must be a device (HBM) address on the current
+ *     HIP device, 16-byte aligned. Host pointers are never dereferenced except where stated.
+ *   - The caller owns every buffer. The library never allocates or frees device memory and never
+ *     synchronizes: all work is enqueued on `stream` (a hipStream_t passed as void*; NULL = the
+ *     default stream) and runs asynchronously.
+ *   - Arguments are validated on the host before anything is enqueued. On any status other than
+ *     WBMM_OK nothing has been enqueued (except WBMM_E_HIP, which reports a failed launch) and
+ *     wbmm_last_error() returns a message for the calling thread.
+ *   - Outputs are overwritten, never accumulated into.
+ *   - Tensor layouts: feature maps are (B, C, H, W) in WBMM_NCHW or (B, H, W, C) in WBMM_NHWC,
+ *     dense, no strides. Tables are (C, 2w-1, 2w-1), matrices (C, d, d), mix weights (C, 3, 3),
+ *     all dense row-major.
+ *   - H and W need not be multiples of w: the map is treated as zero-padded at the bottom and
+ *     right to the next multiple of w, and outputs are cropped back to H x W.
+ */
+#ifndef WBMM_H
+#define WBMM_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define WBMM_ABI_VERSION 1
+
+typedef enum wbmm_status {
+  WBMM_OK = 0,
+  WBMM_E_INVALID = 1,      /* a size, pointer or combination of arguments is invalid          */
+  WBMM_E_UNSUPPORTED = 2,  /* valid request this build does not provide (e.g. misalignment)   */
+  WBMM_E_WORKSPACE = 3,    /* workspace missing or smaller than the matching *_bytes query    */
+  WBMM_E_HIP = 4           /* a HIP launch failed; wbmm_last_error() carries HIP's message    */
+} wbmm_status;
+
+typedef enum wbmm_dtype { WBMM_F32 = 0, WBMM_BF16 = 1 } wbmm_dtype;
+typedef enum wbmm_layout { WBMM_NCHW = 0, WBMM_NHWC = 1 } wbmm_layout;
+
+/* ABI version this library was built with (WBMM_ABI_VERSION). */
+int wbmm_abi_version(void);
+
+/* Message for the last non-OK status returned on the calling thread ("" if none). The pointer
+ * stays valid until the next wbmm_* call on the same thread. */
+const char* wbmm_last_error(void);
+
+/*
+ * wbmm_build_index — relative-position index of one window.
+ * Defines: the table lookup that turns an in-window pair (i, j) into a table entry
+ *          [gecl.asia reading notes, "Core Idea" and "Method" point 2].
+ *   idx[i*d + j] = ((y_i - y_j) + w - 1) * (2w - 1) + ((x_i - x_j) + w - 1)   (int32, d x d)
+ * w:   window side, 1 <= w <= 32.
+ * idx: device, int32 [d*d], written.
+ * Bit-exact. Errors: WBMM_E_INVALID for w out of range or idx == NULL.
+ */
+wbmm_status wbmm_build_index(int w, int32_t* idx, void* stream);
+
+/*
+ * wbmm_build_matrix — materialize M_c from the table (the pages' inference caching of the
+ * constructed weights) [gecl.asia reading notes, "Core Idea"; "Method", last sentence].
+ *   M[c][i][j] = T[c][idx[i][j]]   (an exact copy in the table's dtype)
+ * T: device [C][2w-1][2w-1], dtype `dtype` (WBMM_F32 or WBMM_BF16).
+ * M: device [C][d][d], same dtype, written. Must not overlap T.
+ * Bit-exact. Errors: WBMM_E_INVALID for C < 1, w out of range, NULL pointers, bad dtype.
+ */
+wbmm_status wbmm_build_matrix(const void* T, int C, int w, int dtype, void* M, void* stream);
+
+/*
+ * wbmm_fold_hier — fold an s x s sub-window table into a w x w window matrix (hierarchical
+ * window reparameterization, zero inference cost) [gecl.asia reading notes, "Method" point 4;
+ * arxivdaily abstract].
+ *   For pairs (i, j) in the same s x s sub-window (sub-windows tile the window from its origin):
+ *     M_out[c][i][j] = M_in[c][i][j] + T_sub[c][idx_s(i, j)]   (one add in `dtype`, RNE)
+ *   otherwise M_out[c][i][j] = M_in[c][i][j]; idx_s is wbmm_build_index's formula with s for w
+ *   applied to the in-sub-window coordinates (y mod s, x mod s).
+ * M_in:  device [C][d][d]; T_sub: device [C][2s-1][2s-1]; M_out: device [C][d][d], written;
+ *        M_out may equal M_in (in place) but must not partially overlap it.
+ * s must divide w and 1 <= s < w. dtype WBMM_F32 or WBMM_BF16 (bf16 adds round to bf16, RNE).
+ * Bit-exact. Errors: WBMM_E_INVALID for bad sizes, s not dividing w, NULL pointers.
+ */
+wbmm_status wbmm_fold_hier(const void* M_in, const void* T_sub, int C, int w, int s, int dtype,
+                           void* M_out, void* stream);
+
+/*
+ * wbmm_forward_workspace_bytes — device workspace wbmm_forward needs for these arguments
+ * (0 when none). Returns 0 for invalid arguments as well; wbmm_forward reports those.
+ */
+size_t wbmm_forward_workspace_bytes(int B, int C, int H, int W, int w, int layout, int has_mix,
+                                    int has_z_save);
+
+/*
+ * wbmm_forward — the WBMM layer forward [gecl.asia reading notes, "Core Idea", "Method";
+ * pith page, "Core claim"; arxivdaily abstract].
+ *   z = crop(reverse(M_c . partition(pad(x))))   for every channel c, window and image;
+ *   y = mix3x3(z, mix_w) if mix_w != NULL, else y = z.
+ * mix3x3 is the inter-block 3x3 depthwise cross-correlation, zero padding 1, stride 1, no bias:
+ *   y[b,c,h,v] = sum_{u,t in 0..2} mix_w[c,u,t] * z[b,c,h+u-1,v+t-1]  (z = 0 outside the map)
+ *   [gecl.asia reading notes, "Method" point 3].
+ * Sizes: B, C, H, W >= 1; 1 <= w <= 32.
+ * layout:    WBMM_NCHW or WBMM_NHWC (x, y and z_save share it).
+ * in_dtype:  WBMM_F32 or WBMM_BF16 for x and for T/M. Products accumulate in fp32.
+ * out_dtype: WBMM_F32 or WBMM_BF16 for y and z_save (bf16 outputs are rounded RNE from fp32).
+ * x:      device map, in_dtype.
+ * T, M:   exactly one non-NULL. T: device [C][2w-1][2w-1] — M_c is formed on chip from T_c.
+ *         M: device [C][d][d] — the cached (possibly folded) matrices are read from memory.
+ * mix_w:  device fp32 [C][3][3] or NULL.
+ * z_save: device map in out_dtype receiving the pre-mix output z (for the backward), or NULL.
+ * y:      device map in out_dtype, written; must not overlap x, T, M, mix_w or z_save.
+ * workspace / workspace_bytes: device scratch of at least wbmm_forward_workspace_bytes(...)
+ *         bytes (may be NULL when that is 0).
+ * Errors: WBMM_E_INVALID (sizes, pointers, both or neither of T/M, overlap of y with x),
+ *         WBMM_E_UNSUPPORTED (misaligned pointer), WBMM_E_WORKSPACE, WBMM_E_HIP.
+ */
+wbmm_status wbmm_forward(int B, int C, int H, int W, int w, int layout, int in_dtype,
+                         int out_dtype, const void* x, const void* T, const void* M,
+                         const float* mix_w, void* z_save, void* y, void* workspace,
+                         size_t workspace_bytes, void* stream);
+
+/*
+ * wbmm_backward_workspace_bytes — device workspace wbmm_backward needs (fp64 partial tables and
+ * arrival counters). Returns 0 for invalid arguments.
+ */
+size_t wbmm_backward_workspace_bytes(int B, int C, int H, int W, int w, int layout, int has_mix);
+
+/*
+ * wbmm_backward — gradients of wbmm_forward (fp32). The pages train with the operator but do not
+ * write out its backward; it follows from the forward by the chain rule:
+ *   dz    = mix3x3 adjoint of dy (correlation with the 180-degree rotated mix_w), or dy if no mix;
+ *   dmix_w[c,u,t] = sum_{b,h,v} dy[b,c,h,v] * z[b,c,h+u-1,v+t-1];
+ *   G_c   = partition(pad(dz));  dx = crop(reverse(M_c^T . G_c));
+ *   dT[c][k] = sum over pairs (i,j) with idx[i][j] = k of (G_c . X_c^T)[i][j].
+ * x, dy:   device fp32 maps in `layout`.
+ * T, M:    exactly one non-NULL (as in wbmm_forward; with M, dT is the gradient with respect to
+ *          the table that M was gathered from).
+ * mix_w:   device fp32 [C][3][3] or NULL; z_saved (the forward's z_save) is required iff mix_w.
+ * dx:      device fp32 map, written, or NULL to skip.
+ * dT:      device fp32 [C][2w-1][2w-1], written, or NULL to skip.
+ * dmix_w:  device fp32 [C][3][3], written, or NULL to skip (ignored without mix_w).
+ * workspace / workspace_bytes: device scratch of at least wbmm_backward_workspace_bytes(...)
+ *          bytes. Its first use must see it zero-filled; every call that completes leaves it
+ *          ready for the next one. Calls that share a workspace must be ordered on one stream.
+ * dT and dmix_w are reduced in a fixed order (no floating-point atomics): results are
+ * bitwise reproducible run to run.
+ * This build supports the backward for 1 <= w <= 16.
+ * Errors: WBMM_E_INVALID, WBMM_E_UNSUPPORTED (w > 16, misaligned pointer), WBMM_E_WORKSPACE,
+ *         WBMM_E_HIP.
+ */
+wbmm_status wbmm_backward(int B, int C, int H, int W, int w, int layout, const float* x,
+                          const float* T, const float* M, const float* mix_w,
+                          const float* z_saved, const float* dy, float* dx, float* dT,
+                          float* dmix_w, void* workspace, size_t workspace_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* WBMM_H */

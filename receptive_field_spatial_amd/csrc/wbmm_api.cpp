@@ -1,0 +1,254 @@
+// C ABI of libwbmm: argument validation (host only, before anything is enqueued), the thread-local
+// error message, and dispatch to the kernel launchers.
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdint>
+#include <cstdio>
+#include <string>
+
+#include "../../include/wbmm.h"
+#include "wbmm_launch.hpp"
+
+#define WBMM_API extern "C" __attribute__((visibility("default")))
+
+namespace {
+
+thread_local std::string g_err;
+
+wbmm_status fail(wbmm_status st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return st;
+}
+
+wbmm_status ok() {
+  g_err.clear();
+  return WBMM_OK;
+}
+
+wbmm_status hip_status(hipError_t e, const char* what) {
+  if (e == hipSuccess) return ok();
+  return fail(WBMM_E_HIP, "%s: HIP error %d (%s)", what, (int)e, hipGetErrorString(e));
+}
+
+constexpr int kMaxW = 32;
+constexpr long long kMaxDim = 1 << 20;
+constexpr long long kMaxElems = 1ll << 38;
+
+bool valid_dtype(int dt) { return dt == WBMM_F32 || dt == WBMM_BF16; }
+bool valid_layout(int l) { return l == WBMM_NCHW || l == WBMM_NHWC; }
+size_t dtype_size(int dt) { return dt == WBMM_BF16 ? 2 : 4; }
+bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+// Byte ranges [p, p + n) and [q, q + m) intersect.
+bool overlaps(const void* p, size_t n, const void* q, size_t m) {
+  if (!p || !q || n == 0 || m == 0) return false;
+  const uintptr_t a = (uintptr_t)p, b = (uintptr_t)q;
+  return a < b + m && b < a + n;
+}
+
+wbmm_status check_map(int B, int C, int H, int W, int w, int layout) {
+  if (w < 1 || w > kMaxW) return fail(WBMM_E_INVALID, "window size w=%d outside [1, %d]", w, kMaxW);
+  if (B < 1 || C < 1 || H < 1 || W < 1)
+    return fail(WBMM_E_INVALID, "sizes must be >= 1 (B=%d C=%d H=%d W=%d)", B, C, H, W);
+  if (C > 65535) return fail(WBMM_E_UNSUPPORTED, "C=%d exceeds 65535", C);
+  if (B > kMaxDim || H > kMaxDim || W > kMaxDim)
+    return fail(WBMM_E_UNSUPPORTED, "a dimension exceeds 2^20");
+  const long long Hp = (H + w - 1) / w * (long long)w, Wp = (W + w - 1) / w * (long long)w;
+  if ((long long)B * C * Hp * Wp > kMaxElems) return fail(WBMM_E_UNSUPPORTED, "map too large");
+  if ((long long)B * (Hp / w) * (Wp / w) >= (1ll << 31))
+    return fail(WBMM_E_UNSUPPORTED, "too many windows per channel");
+  if (!valid_layout(layout)) return fail(WBMM_E_INVALID, "unknown layout %d", layout);
+  return WBMM_OK;
+}
+
+}  // namespace
+
+WBMM_API int wbmm_abi_version(void) { return WBMM_ABI_VERSION; }
+
+WBMM_API const char* wbmm_last_error(void) { return g_err.c_str(); }
+
+WBMM_API wbmm_status wbmm_build_index(int w, int32_t* idx, void* stream) {
+  if (w < 1 || w > kMaxW) return fail(WBMM_E_INVALID, "window size w=%d outside [1, %d]", w, kMaxW);
+  if (!idx) return fail(WBMM_E_INVALID, "idx is NULL");
+  if (!aligned(idx, 4)) return fail(WBMM_E_UNSUPPORTED, "idx not 4-byte aligned");
+  return hip_status(wbmm::launch_build_index(w, idx, (hipStream_t)stream), "wbmm_build_index");
+}
+
+WBMM_API wbmm_status wbmm_build_matrix(const void* T, int C, int w, int dtype, void* M,
+                                       void* stream) {
+  if (w < 1 || w > kMaxW) return fail(WBMM_E_INVALID, "window size w=%d outside [1, %d]", w, kMaxW);
+  if (C < 1) return fail(WBMM_E_INVALID, "C=%d must be >= 1", C);
+  if (!valid_dtype(dtype)) return fail(WBMM_E_INVALID, "unknown dtype %d", dtype);
+  if (!T || !M) return fail(WBMM_E_INVALID, "T and M must be non-NULL");
+  const size_t es = dtype_size(dtype);
+  if (!aligned(T, es) || !aligned(M, es)) return fail(WBMM_E_UNSUPPORTED, "misaligned pointer");
+  const size_t L = (size_t)(2 * w - 1) * (2 * w - 1), d = (size_t)w * w;
+  if (overlaps(T, (size_t)C * L * es, M, (size_t)C * d * d * es))
+    return fail(WBMM_E_INVALID, "M overlaps T");
+  return hip_status(wbmm::launch_build_matrix(T, C, w, dtype == WBMM_BF16, M, (hipStream_t)stream),
+                    "wbmm_build_matrix");
+}
+
+WBMM_API wbmm_status wbmm_fold_hier(const void* M_in, const void* T_sub, int C, int w, int s,
+                                    int dtype, void* M_out, void* stream) {
+  if (w < 1 || w > kMaxW) return fail(WBMM_E_INVALID, "window size w=%d outside [1, %d]", w, kMaxW);
+  if (C < 1) return fail(WBMM_E_INVALID, "C=%d must be >= 1", C);
+  if (s < 1 || s >= w || w % s != 0)
+    return fail(WBMM_E_INVALID, "sub-window s=%d must divide w=%d with 1 <= s < w", s, w);
+  if (!valid_dtype(dtype)) return fail(WBMM_E_INVALID, "unknown dtype %d", dtype);
+  if (!M_in || !T_sub || !M_out) return fail(WBMM_E_INVALID, "NULL pointer");
+  const size_t es = dtype_size(dtype);
+  if (!aligned(M_in, es) || !aligned(T_sub, es) || !aligned(M_out, es))
+    return fail(WBMM_E_UNSUPPORTED, "misaligned pointer");
+  const size_t mbytes = (size_t)C * w * w * w * w * es;
+  if (M_in != M_out && overlaps(M_in, mbytes, M_out, mbytes))
+    return fail(WBMM_E_INVALID, "M_out partially overlaps M_in");
+  const size_t tbytes = (size_t)C * (2 * s - 1) * (2 * s - 1) * es;
+  if (overlaps(T_sub, tbytes, M_out, mbytes)) return fail(WBMM_E_INVALID, "M_out overlaps T_sub");
+  return hip_status(
+      wbmm::launch_fold(M_in, T_sub, C, w, s, dtype == WBMM_BF16, M_out, (hipStream_t)stream),
+      "wbmm_fold_hier");
+}
+
+namespace {
+
+wbmm_status check_forward(const wbmm::FwdRequest& r, int in_dtype, int out_dtype) {
+  wbmm_status st = check_map(r.B, r.C, r.H, r.W, r.w, r.layout);
+  if (st != WBMM_OK) return st;
+  if (!valid_dtype(in_dtype) || !valid_dtype(out_dtype))
+    return fail(WBMM_E_INVALID, "unknown dtype (in %d, out %d)", in_dtype, out_dtype);
+  if (!r.x || !r.y) return fail(WBMM_E_INVALID, "x and y must be non-NULL");
+  if ((r.T == nullptr) == (r.M == nullptr))
+    return fail(WBMM_E_INVALID, "exactly one of T (table) and M (cached matrix) must be given");
+  if (r.mixw && out_dtype != WBMM_F32)
+    return fail(WBMM_E_UNSUPPORTED, "the 3x3 mix is provided with fp32 output only");
+  const size_t ies = dtype_size(in_dtype), oes = dtype_size(out_dtype);
+  if (!aligned(r.x, ies) || (r.T && !aligned(r.T, ies)) || (r.M && !aligned(r.M, ies)) ||
+      !aligned(r.y, oes) || (r.zsave && !aligned(r.zsave, oes)) || (r.mixw && !aligned(r.mixw, 4)))
+    return fail(WBMM_E_UNSUPPORTED, "pointer not aligned to its element size");
+  const size_t elems = (size_t)r.B * r.C * r.H * r.W;
+  const size_t d = (size_t)r.w * r.w, L = (size_t)(2 * r.w - 1) * (2 * r.w - 1);
+  const size_t ybytes = elems * oes;
+  if (overlaps(r.y, ybytes, r.x, elems * ies)) return fail(WBMM_E_INVALID, "y overlaps x");
+  if (overlaps(r.y, ybytes, r.T, (size_t)r.C * L * ies)) return fail(WBMM_E_INVALID, "y overlaps T");
+  if (overlaps(r.y, ybytes, r.M, (size_t)r.C * d * d * ies))
+    return fail(WBMM_E_INVALID, "y overlaps M");
+  if (overlaps(r.y, ybytes, r.mixw, (size_t)r.C * 9 * 4))
+    return fail(WBMM_E_INVALID, "y overlaps mix_w");
+  if (overlaps(r.y, ybytes, r.zsave, ybytes)) return fail(WBMM_E_INVALID, "y overlaps z_save");
+  if (r.zsave && overlaps(r.zsave, ybytes, r.x, elems * ies))
+    return fail(WBMM_E_INVALID, "z_save overlaps x");
+  if (!wbmm::forward_plan_ok(r))
+    return fail(WBMM_E_UNSUPPORTED, "no launch shape fits this problem (w=%d)", r.w);
+  return WBMM_OK;
+}
+
+wbmm::FwdRequest make_fwd(int B, int C, int H, int W, int w, int layout, int in_dtype,
+                          int out_dtype, const void* x, const void* T, const void* M,
+                          const float* mix_w, void* z_save, void* y, void* ws, size_t ws_bytes) {
+  wbmm::FwdRequest r{};
+  r.B = B; r.C = C; r.H = H; r.W = W; r.w = w; r.layout = layout;
+  r.in_bf16 = in_dtype == WBMM_BF16;
+  r.out_bf16 = out_dtype == WBMM_BF16;
+  r.x = x; r.T = T; r.M = M; r.mixw = mix_w; r.zsave = z_save; r.y = y;
+  r.ws = ws; r.ws_bytes = ws_bytes;
+  return r;
+}
+
+}  // namespace
+
+WBMM_API size_t wbmm_forward_workspace_bytes(int B, int C, int H, int W, int w, int layout,
+                                             int has_mix, int has_z_save) {
+  if (check_map(B, C, H, W, w, layout) != WBMM_OK) return 0;
+  static const float dummy = 0.f;
+  wbmm::FwdRequest r = make_fwd(B, C, H, W, w, layout, WBMM_F32, WBMM_F32, &dummy, &dummy, nullptr,
+                                has_mix ? &dummy : nullptr, has_z_save ? (void*)&dummy : nullptr,
+                                (void*)&dummy, nullptr, 0);
+  if (!wbmm::forward_plan_ok(r)) return 0;
+  return wbmm::forward_workspace(r);
+}
+
+WBMM_API wbmm_status wbmm_forward(int B, int C, int H, int W, int w, int layout, int in_dtype,
+                                  int out_dtype, const void* x, const void* T, const void* M,
+                                  const float* mix_w, void* z_save, void* y, void* workspace,
+                                  size_t workspace_bytes, void* stream) {
+  wbmm::FwdRequest r = make_fwd(B, C, H, W, w, layout, in_dtype, out_dtype, x, T, M, mix_w, z_save,
+                                y, workspace, workspace_bytes);
+  wbmm_status st = check_forward(r, in_dtype, out_dtype);
+  if (st != WBMM_OK) return st;
+  const size_t need = wbmm::forward_workspace(r);
+  if (need > 0 && (!workspace || workspace_bytes < need))
+    return fail(WBMM_E_WORKSPACE, "workspace of %zu bytes required, %zu given", need,
+                workspace ? workspace_bytes : (size_t)0);
+  if (need > 0 && !aligned(workspace, 16))
+    return fail(WBMM_E_UNSUPPORTED, "workspace not 16-byte aligned");
+  return hip_status(wbmm::launch_forward(r, (hipStream_t)stream), "wbmm_forward");
+}
+
+namespace {
+
+wbmm::BwdRequest make_bwd(int B, int C, int H, int W, int w, int layout, const float* x,
+                          const float* T, const float* M, const float* mix_w, const float* z_saved,
+                          const float* dy, float* dx, float* dT, float* dmix_w, void* ws,
+                          size_t ws_bytes) {
+  wbmm::BwdRequest r{};
+  r.B = B; r.C = C; r.H = H; r.W = W; r.w = w; r.layout = layout;
+  r.x = x; r.T = T; r.M = M; r.mixw = mix_w; r.zsaved = z_saved; r.dy = dy;
+  r.dx = dx; r.dT = dT; r.dmixw = mix_w ? dmix_w : nullptr;
+  r.ws = ws; r.ws_bytes = ws_bytes;
+  return r;
+}
+
+}  // namespace
+
+WBMM_API size_t wbmm_backward_workspace_bytes(int B, int C, int H, int W, int w, int layout,
+                                              int has_mix) {
+  if (check_map(B, C, H, W, w, layout) != WBMM_OK || w > 16) return 0;
+  static const float dummy = 0.f;
+  wbmm::BwdRequest r = make_bwd(B, C, H, W, w, layout, &dummy, &dummy, nullptr,
+                                has_mix ? &dummy : nullptr, has_mix ? &dummy : nullptr, &dummy,
+                                nullptr, nullptr, nullptr, nullptr, 0);
+  if (!wbmm::backward_plan_ok(r)) return 0;
+  return wbmm::backward_workspace(r);
+}
+
+WBMM_API wbmm_status wbmm_backward(int B, int C, int H, int W, int w, int layout, const float* x,
+                                   const float* T, const float* M, const float* mix_w,
+                                   const float* z_saved, const float* dy, float* dx, float* dT,
+                                   float* dmix_w, void* workspace, size_t workspace_bytes,
+                                   void* stream) {
+  wbmm_status st = check_map(B, C, H, W, w, layout);
+  if (st != WBMM_OK) return st;
+  if (w > 16) return fail(WBMM_E_UNSUPPORTED, "the backward is provided for w <= 16 (w=%d)", w);
+  if (!x || !dy) return fail(WBMM_E_INVALID, "x and dy must be non-NULL");
+  if ((T == nullptr) == (M == nullptr))
+    return fail(WBMM_E_INVALID, "exactly one of T (table) and M (cached matrix) must be given");
+  if ((mix_w == nullptr) != (z_saved == nullptr))
+    return fail(WBMM_E_INVALID, "z_saved is required exactly when mix_w is given");
+  const void* ptrs[] = {x, T, M, mix_w, z_saved, dy, dx, dT, dmix_w};
+  for (const void* p : ptrs)
+    if (p && !aligned(p, 4)) return fail(WBMM_E_UNSUPPORTED, "pointer not 4-byte aligned");
+  const size_t mb = (size_t)B * C * H * W * 4;
+  const size_t tb = (size_t)C * (2 * w - 1) * (2 * w - 1) * 4;
+  if (dx && (overlaps(dx, mb, x, mb) || overlaps(dx, mb, dy, mb) || overlaps(dx, mb, z_saved, mb)))
+    return fail(WBMM_E_INVALID, "dx overlaps an input");
+  if (dT && (overlaps(dT, tb, T, tb) || overlaps(dT, tb, dx, mb)))
+    return fail(WBMM_E_INVALID, "dT overlaps T or dx");
+  wbmm::BwdRequest r = make_bwd(B, C, H, W, w, layout, x, T, M, mix_w, z_saved, dy, dx, dT, dmix_w,
+                                workspace, workspace_bytes);
+  if (!wbmm::backward_plan_ok(r))
+    return fail(WBMM_E_UNSUPPORTED, "no launch shape fits this problem (w=%d)", w);
+  const size_t need = wbmm::backward_workspace(r);
+  if (need > 0 && (!workspace || workspace_bytes < need))
+    return fail(WBMM_E_WORKSPACE, "workspace of %zu bytes required, %zu given", need,
+                workspace ? workspace_bytes : (size_t)0);
+  if (need > 0 && !aligned(workspace, 256))
+    return fail(WBMM_E_UNSUPPORTED, "workspace not 256-byte aligned");
+  return hip_status(wbmm::launch_backward(r, (hipStream_t)stream), "wbmm_backward");
+}

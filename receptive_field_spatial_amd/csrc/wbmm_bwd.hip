@@ -1,0 +1,361 @@
+// WBMM backward on gfx950 (fp32). The pages train with the operator but leave its backward
+// implicit; by the chain rule (forward z = M_c . X_c per window, y = mix3x3(z)):
+//   dz  = mix adjoint of dy;  dWmix[c,u,t] = sum dy[h,v] z[h+u-1, v+t-1];
+//   dX  = M_c^T . G_c  (G = partition(dz));  dT_c[k] = sum_{idx[i][j] = k} (G_c . X_c^T)[i][j].
+// One kernel does all of it in image mode: dz is formed in LDS from dy, dX reuses the forward
+// contraction with the transposed table lookup, and dT is a row-pair MFMA contraction
+//   acc_dy[x1][x2] = sum_{windows n} sum_{y1 - y2 = dy} G_n[y1][x1] * X_n[y2][x2]
+// whose diagonals x1 - x2 = dx give dT[dy][dx]. fp32 MFMA chains over 4 windows are promoted to
+// fp64; per-workgroup partials are summed in a fixed order by the last workgroup of each channel
+// to arrive (no floating-point atomics), so dT and dWmix are bitwise reproducible.
+#include "wbmm_core.hpp"
+#include "wbmm_launch.hpp"
+
+namespace wbmm {
+
+struct BwdArgs {
+  Geo g;
+  const float* x;
+  const float* tab;
+  const float* mat;
+  const float* mixw;
+  const float* zsaved;
+  const float* gsrc;    // dy (mix applied here, or no mix) or dz (mix applied by a prior pass)
+  float* dx;
+  float* dT;
+  float* dmixw;
+  double* partT;        // [C][col_groups][L]
+  double* partW;        // [C][col_groups][9]
+  unsigned* counters;   // [C], zero between calls
+  int mix_here, want_dx, want_dT, want_dW;
+};
+
+// Slot j of wave q covers row offset index t = 4j + (q or 3-q alternating), ordered
+// 0, +1, -1, +2, -2, ...: the four waves get near-equal MFMA counts (w - |dy| per offset).
+__device__ __forceinline__ int slot_dy(int j, int wave, int nd, bool& valid) {
+  const int t = 4 * j + ((j & 1) ? 3 - wave : wave);
+  valid = t < nd;
+  return t == 0 ? 0 : ((t & 1) ? (t + 1) / 2 : -(t / 2));
+}
+
+template <int RPW, int ASRC>
+__global__ void __launch_bounds__(kThreads) k_wbmm_bwd(BwdArgs a) {
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+  __shared__ double s_wred[4][9];
+  __shared__ int s_last;
+  const Geo& g = a.g;
+  const int c = blockIdx.y;
+  const int colgrp = blockIdx.x;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int xtile_bytes = g.NT * g.XR * 4;
+  float* Gt = (float*)(smem + g.lds_big);
+  unsigned char* RA = smem + g.lds_big + xtile_bytes;
+  float* Ts = (float*)(smem + g.lds_tab);
+  int2* Offs = (int2*)(smem + g.lds_off);
+  const int plane = g.PH * g.PW;
+
+  load_table_f32(g, ASRC == 0 ? a.tab : nullptr, c, Ts, Offs);
+
+  double wacc[9];
+#pragma unroll
+  for (int q = 0; q < 9; ++q) wacc[q] = 0.0;
+
+  // ---------------------------------------------------------------- G = partition(dz)
+  if (a.mix_here) {
+    float* Hs = (float*)RA;  // dy planes with a one-pixel zero halo
+    zero_lds(Hs, g.ipw * plane);
+    zero_lds(Gt, g.NT * g.XR);
+    __syncthreads();
+    const int total = g.ipw * g.H * g.W;
+    for (int e = threadIdx.x; e < total; e += kThreads) {
+      uint32_t img, rem, h, v;
+      fdivmod((uint32_t)e, g.fd_HW, img, rem);
+      fdivmod(rem, g.fd_W, h, v);
+      const int b = colgrp * g.ipw + (int)img;
+      if (b >= g.B) continue;
+      Hs[(int)img * plane + (h + 1) * g.PW + v + 1] =
+          a.gsrc[map_off(g.layout, b, c, (int)h, (int)v, g.C, g.H, g.W)];
+    }
+    __syncthreads();
+    float w9[9];
+#pragma unroll
+    for (int q = 0; q < 9; ++q) w9[q] = a.mixw[c * 9 + q];
+    for (int e = threadIdx.x; e < total; e += kThreads) {
+      uint32_t img, rem, p, q;
+      fdivmod((uint32_t)e, g.fd_HW, img, rem);
+      fdivmod(rem, g.fd_W, p, q);
+      const int b = colgrp * g.ipw + (int)img;
+      if (b >= g.B) continue;
+      const float* P = Hs + (int)img * plane;
+      // dz[p][q] = sum_{u,t} W[u][t] dy[p-u+1][q-t+1]; P holds dy shifted by the halo (+1).
+      float dz = 0.f;
+#pragma unroll
+      for (int u = 0; u < 3; ++u)
+#pragma unroll
+        for (int t = 0; t < 3; ++t) dz = fmaf(w9[u * 3 + t], P[(p - u + 2) * g.PW + (q - t + 2)], dz);
+      uint32_t wy, y, wx, xx;
+      fdivmod(p, g.fd_w, wy, y);
+      fdivmod(q, g.fd_w, wx, xx);
+      const int n = (int)img * g.nWin + (int)wy * g.nW + (int)wx;
+      Gt[xs_slot_f32(g, n, (int)y, (int)xx)] = dz;
+      if (a.want_dW) {
+        // dWmix[u][t] = sum_{p,q} z[p][q] * dy[p-u+1][q-t+1]
+        const double zv = a.zsaved[map_off(g.layout, b, c, (int)p, (int)q, g.C, g.H, g.W)];
+#pragma unroll
+        for (int u = 0; u < 3; ++u)
+#pragma unroll
+          for (int t = 0; t < 3; ++t)
+            wacc[u * 3 + t] += zv * (double)P[(p - u + 2) * g.PW + (q - t + 2)];
+      }
+    }
+    __syncthreads();
+  } else {
+    load_xtile<float>(g, a.gsrc, c, colgrp, Gt);
+  }
+
+  // ---------------------------------------------------------------- dX = M^T . G
+  if (a.want_dx) {
+    v4f acc[RPW];
+    contract_f32<RPW, 1, ASRC, true>(g, c, a.mat, Gt, (float*)RA, Ts, Offs, 0, wave, acc);
+    if (g.image_mode) {
+      __syncthreads();
+      float* St = (float*)RA;
+      zero_lds(St, g.ipw * plane);
+      __syncthreads();
+      stage_acc<RPW>(g, colgrp, 0, wave, acc, St);
+      __syncthreads();
+      const int total = g.ipw * g.H * g.W;
+      for (int e = threadIdx.x; e < total; e += kThreads) {
+        uint32_t img, rem, h, v;
+        fdivmod((uint32_t)e, g.fd_HW, img, rem);
+        fdivmod(rem, g.fd_W, h, v);
+        const int b = colgrp * g.ipw + (int)img;
+        if (b >= g.B) continue;
+        a.dx[map_off(g.layout, b, c, (int)h, (int)v, g.C, g.H, g.W)] =
+            St[(int)img * plane + (h + 1) * g.PW + v + 1];
+      }
+    } else {
+      store_acc_direct<RPW>(g, colgrp, 0, wave, acc, c, a.dx, nullptr, 0);
+    }
+  }
+  __syncthreads();
+
+  // ---------------------------------------------------------------- dT partial (row pairs)
+  if (a.want_dT) {
+    float* Xt = (float*)RA;
+    load_xtile<float>(g, a.x, c, colgrp, Xt);
+    int nvalid;
+    if (g.image_mode) {
+      int imgs = g.B - colgrp * g.ipw;
+      if (imgs > g.ipw) imgs = g.ipw;
+      nvalid = imgs * g.nWin;
+    } else {
+      nvalid = g.N - colgrp * g.NT;
+      if (nvalid > g.NT) nvalid = g.NT;
+    }
+    const int nd = 2 * g.w - 1;
+    bool val[8];
+    int dyv[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) dyv[j] = slot_dy(j, wave, nd, val[j]);
+    double acc64[8][4];
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) acc64[j][r] = 0.0;
+    const int x1 = lane & 15, kn = lane >> 4;
+    for (int n0 = 0; n0 < nvalid; n0 += 4) {
+      const float* gcol = Gt + (n0 + kn) * g.XR + x1;
+      const float* xcol = Xt + (n0 + kn) * g.XR + x1;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        if (!val[j]) continue;
+        const int dy = dyv[j];
+        const int y1s = dy > 0 ? dy : 0, y2s = dy > 0 ? 0 : -dy;
+        const int cnt = g.w - (dy > 0 ? dy : -dy);
+        const float* ga = gcol + y1s * g.RP;
+        const float* xb = xcol + y2s * g.RP;
+        v4f a0 = {0.f, 0.f, 0.f, 0.f}, a1 = {0.f, 0.f, 0.f, 0.f};
+        int m = 0;
+        for (; m + 1 < cnt; m += 2) {
+          a0 = mfma_f32(ga[m * g.RP], xb[m * g.RP], a0);
+          a1 = mfma_f32(ga[(m + 1) * g.RP], xb[(m + 1) * g.RP], a1);
+        }
+        if (m < cnt) a0 = mfma_f32(ga[m * g.RP], xb[m * g.RP], a0);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) acc64[j][r] += (double)a0[r] + (double)a1[r];
+      }
+    }
+    __syncthreads();  // all waves done reading the G and X tiles
+    double* scr = (double*)(smem + g.lds_big) + wave * 256;
+    double* pT = a.partT + ((size_t)c * g.col_groups + colgrp) * g.L;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      if (!val[j]) continue;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) scr[(4 * (lane >> 4) + r) * 16 + (lane & 15)] = acc64[j][r];
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+      if (lane < nd) {
+        const int dx = lane - (g.w - 1);
+        double s = 0.0;
+        for (int xa = 0; xa < g.w; ++xa) {
+          const int xb2 = xa - dx;
+          if (xb2 >= 0 && xb2 < g.w) s += scr[xa * 16 + xb2];
+        }
+        pT[(dyv[j] + g.w - 1) * nd + lane] = s;
+      }
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    }
+  }
+
+  // ---------------------------------------------------------------- dWmix partial
+  if (a.want_dW) {
+#pragma unroll
+    for (int q = 0; q < 9; ++q) {
+      double v = wacc[q];
+      for (int off = 32; off > 0; off >>= 1) v += __shfl_down(v, off, 64);
+      if (lane == 0) s_wred[wave][q] = v;
+    }
+    __syncthreads();
+    if (threadIdx.x < 9) {
+      const int q = threadIdx.x;
+      a.partW[((size_t)c * g.col_groups + colgrp) * 9 + q] =
+          ((s_wred[0][q] + s_wred[1][q]) + s_wred[2][q]) + s_wred[3][q];
+    }
+  }
+
+  // ---------------------------------------------------------------- last arrival reduces
+  if (a.want_dT || a.want_dW) {
+    __threadfence();
+    __syncthreads();
+    if (threadIdx.x == 0) {
+      const unsigned prev = atomicAdd(&a.counters[c], 1u);
+      s_last = prev == (unsigned)(g.col_groups - 1);
+    }
+    __syncthreads();
+    if (s_last) {
+      __threadfence();
+      if (a.want_dT) {
+        for (int q = threadIdx.x; q < g.L; q += kThreads) {
+          const double* p = a.partT + (size_t)c * g.col_groups * g.L + q;
+          double s = 0.0;
+          for (int k = 0; k < g.col_groups; ++k) s += __builtin_nontemporal_load(p + (size_t)k * g.L);
+          a.dT[(size_t)c * g.L + q] = (float)s;
+        }
+      }
+      if (a.want_dW && threadIdx.x < 9) {
+        const double* p = a.partW + (size_t)c * g.col_groups * 9 + threadIdx.x;
+        double s = 0.0;
+        for (int k = 0; k < g.col_groups; ++k) s += __builtin_nontemporal_load(p + (size_t)k * 9);
+        a.dmixw[c * 9 + threadIdx.x] = (float)s;
+      }
+      if (threadIdx.x == 0) a.counters[c] = 0u;
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------- dispatch
+template <int RPW, int ASRC>
+static hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t st) {
+  auto fn = k_wbmm_bwd<RPW, ASRC>;
+  hipError_t e = hipFuncSetAttribute((const void*)fn, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                     a.g.lds_total);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(fn, dim3(a.g.col_groups, a.g.C, 1), dim3(kThreads), a.g.lds_total, st, a);
+  return hipGetLastError();
+}
+
+template <int ASRC>
+static hipError_t launch_bwd_tiles(const BwdArgs& a, hipStream_t st) {
+  switch (a.g.RPW) {
+    case 4: return launch_bwd_t<4, ASRC>(a, st);
+    case 7: return launch_bwd_t<7, ASRC>(a, st);
+    case 13: return launch_bwd_t<13, ASRC>(a, st);
+    case 16: return launch_bwd_t<16, ASRC>(a, st);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+static bool plan_bwd(Geo& g, const BwdRequest& r) {
+  if (r.w > 16) return false;
+  const bool cached = r.M != nullptr;
+  const bool mix = r.mixw != nullptr;
+  if (!plan_geo(g, r.B, r.C, r.H, r.W, r.w, r.layout, false, cached, mix, 1)) {
+    if (!plan_geo(g, r.B, r.C, r.H, r.W, r.w, r.layout, false, cached, false, 1)) return false;
+  }
+  return g.WR == 1;
+}
+
+namespace {
+struct BwdWs {
+  size_t counters, partT, partW, dz, total;
+};
+BwdWs bwd_ws_layout(const Geo& g, const BwdRequest& r) {
+  auto al = [](size_t v) { return (v + 255) / 256 * 256; };
+  BwdWs w{};
+  w.counters = 0;
+  w.partT = al((size_t)g.C * sizeof(unsigned));
+  w.partW = w.partT + al((size_t)g.C * g.col_groups * g.L * sizeof(double));
+  w.dz = w.partW + al((size_t)g.C * g.col_groups * 9 * sizeof(double));
+  const bool need_dz = r.mixw && !g.image_mode;
+  w.total = w.dz + (need_dz ? al((size_t)r.B * r.C * r.H * r.W * sizeof(float)) : 0);
+  return w;
+}
+}  // namespace
+
+bool backward_plan_ok(const BwdRequest& r) {
+  Geo g;
+  return plan_bwd(g, r);
+}
+
+size_t backward_workspace(const BwdRequest& r) {
+  Geo g;
+  if (!plan_bwd(g, r)) return 0;
+  return bwd_ws_layout(g, r).total;
+}
+
+hipError_t launch_backward(const BwdRequest& r, hipStream_t st) {
+  BwdArgs a{};
+  if (!plan_bwd(a.g, r)) return hipErrorInvalidValue;
+  const BwdWs wl = bwd_ws_layout(a.g, r);
+  unsigned char* ws = (unsigned char*)r.ws;
+  a.x = r.x;
+  a.tab = r.T;
+  a.mat = r.M;
+  a.mixw = r.mixw;
+  a.zsaved = r.zsaved;
+  a.dx = r.dx;
+  a.dT = r.dT;
+  a.dmixw = r.dmixw;
+  a.counters = (unsigned*)(ws + wl.counters);
+  a.partT = (double*)(ws + wl.partT);
+  a.partW = (double*)(ws + wl.partW);
+  a.want_dx = r.dx != nullptr;
+  a.want_dT = r.dT != nullptr;
+  const bool mix = r.mixw != nullptr;
+  hipError_t e = hipSuccess;
+  if (mix && !a.g.image_mode) {
+    float* dz = (float*)(ws + wl.dz);
+    e = launch_mix_bwd_data(r.dy, r.mixw, dz, r.B, r.C, r.H, r.W, r.layout, st);
+    if (e != hipSuccess) return e;
+    if (r.dmixw) {
+      e = launch_mix_bwd_weight(r.dy, r.zsaved, r.dmixw, r.B, r.C, r.H, r.W, r.layout, st);
+      if (e != hipSuccess) return e;
+    }
+    a.gsrc = dz;
+    a.mix_here = 0;
+    a.want_dW = 0;
+  } else {
+    a.gsrc = r.dy;
+    a.mix_here = mix ? 1 : 0;
+    a.want_dW = (mix && r.dmixw) ? 1 : 0;
+  }
+  if (!a.want_dx && !a.want_dT && !a.want_dW) return hipSuccess;
+  return r.M ? launch_bwd_tiles<1>(a, st) : launch_bwd_tiles<0>(a, st);
+}
+
+}  // namespace wbmm

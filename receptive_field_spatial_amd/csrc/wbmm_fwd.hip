@@ -1,0 +1,184 @@
+// WBMM forward on gfx950: one fused kernel per call in image mode (partition, on-chip M_c,
+// MFMA contraction, reverse, optional 3x3 inter-block mix, optional save of the pre-mix map);
+// window mode adds a separate mix pass when the mix is requested.
+#include "wbmm_core.hpp"
+#include "wbmm_launch.hpp"
+
+namespace wbmm {
+
+struct FwdArgs {
+  Geo g;
+  const void* x;
+  const void* tab;
+  const void* mat;
+  const float* mixw;
+  void* zsave;     // pre-mix output, or null
+  void* y;         // layer output (window mode with a mix: the pre-mix buffer)
+  int out_bf16;
+  int mix_here;    // apply the 3x3 mix in this kernel (image mode only)
+};
+
+template <typename TIn, int RPW, int WR, int ASRC>
+__global__ void __launch_bounds__(kThreads) k_wbmm_fwd(FwdArgs a) {
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+  const Geo& g = a.g;
+  constexpr bool kBf16 = sizeof(TIn) == 2;
+  const int c = blockIdx.y;
+  const int colgrp = blockIdx.x;
+  const int wave = threadIdx.x >> 6;
+  const int wr = wave % WR, ct = wave / WR;
+
+  unsigned char* big = smem + g.lds_big;
+  const int xtile_bytes = g.NT * (kBf16 ? g.XSB * 2 : g.XR * 4);
+  unsigned char* mchunk = big + xtile_bytes;
+  unsigned char* tab = smem + g.lds_tab;
+  int* offs = (int*)(smem + g.lds_off);
+
+  if constexpr (kBf16) {
+    if constexpr (ASRC == 0) load_table_bf16(g, (const uint16_t*)a.tab, c, (uint16_t*)tab, offs);
+  } else {
+    load_table_f32(g, ASRC == 0 ? (const float*)a.tab : nullptr, c, (float*)tab, (int2*)offs);
+  }
+  load_xtile<TIn>(g, (const TIn*)a.x, c, colgrp, big);  // ends with a barrier
+
+  v4f acc[RPW];
+  if constexpr (kBf16) {
+    contract_bf16<RPW, WR, ASRC>(g, c, (const uint16_t*)a.mat, (const uint16_t*)big,
+                                 (uint16_t*)mchunk, (const uint16_t*)tab, offs, wr, ct, acc);
+  } else {
+    contract_f32<RPW, WR, ASRC, false>(g, c, (const float*)a.mat, (const float*)big,
+                                       (float*)mchunk, (const float*)tab, (const int2*)offs, wr,
+                                       ct, acc);
+  }
+
+  if (!g.image_mode) {
+    store_acc_direct<RPW>(g, colgrp, wr, ct, acc, c, a.y, a.zsave, a.out_bf16);
+    return;
+  }
+
+  // Image mode: stage z as (H+2) x (W+2) planes with a zero halo, then write rows out.
+  __syncthreads();  // every wave is done reading the X tile
+  float* St = (float*)big;
+  const int plane = g.PH * g.PW;
+  zero_lds(St, g.ipw * plane);
+  __syncthreads();
+  stage_acc<RPW>(g, colgrp, wr, ct, acc, St);
+  __syncthreads();
+
+  float w9[9];
+  if (a.mix_here) {
+#pragma unroll
+    for (int q = 0; q < 9; ++q) w9[q] = a.mixw[c * 9 + q];
+  }
+  const int total = g.ipw * g.H * g.W;
+  for (int e = threadIdx.x; e < total; e += kThreads) {
+    uint32_t img, rem, h, v;
+    fdivmod((uint32_t)e, g.fd_HW, img, rem);
+    fdivmod(rem, g.fd_W, h, v);
+    const int b = colgrp * g.ipw + (int)img;
+    if (b >= g.B) continue;
+    const float* P = St + (int)img * plane;
+    const float z = P[(h + 1) * g.PW + v + 1];
+    const size_t off = map_off(g.layout, b, c, (int)h, (int)v, g.C, g.H, g.W);
+    if (a.zsave) store_out(a.zsave, off, z, a.out_bf16);
+    float yv = z;
+    if (a.mix_here) {
+      yv = 0.f;
+#pragma unroll
+      for (int u = 0; u < 3; ++u)
+#pragma unroll
+        for (int t = 0; t < 3; ++t) yv = fmaf(w9[u * 3 + t], P[(h + u) * g.PW + v + t], yv);
+    }
+    store_out(a.y, off, yv, a.out_bf16);
+  }
+}
+
+// ---------------------------------------------------------------------------- dispatch
+template <typename TIn, int RPW, int WR, int ASRC>
+static hipError_t launch_fwd_t(const FwdArgs& a, hipStream_t st) {
+  auto fn = k_wbmm_fwd<TIn, RPW, WR, ASRC>;
+  hipError_t e = hipFuncSetAttribute((const void*)fn, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                     a.g.lds_total);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(fn, dim3(a.g.col_groups, a.g.C, 1), dim3(kThreads), a.g.lds_total, st, a);
+  return hipGetLastError();
+}
+
+template <typename TIn, int ASRC>
+static hipError_t launch_fwd_tiles(const FwdArgs& a, hipStream_t st) {
+  const int RPW = a.g.RPW, WR = a.g.WR;
+  if (WR == 1) {
+    if (RPW == 4) return launch_fwd_t<TIn, 4, 1, ASRC>(a, st);
+    if (RPW == 7) return launch_fwd_t<TIn, 7, 1, ASRC>(a, st);
+    if (RPW == 13) return launch_fwd_t<TIn, 13, 1, ASRC>(a, st);
+    if (RPW == 16) return launch_fwd_t<TIn, 16, 1, ASRC>(a, st);
+  } else {
+    if (RPW == 13) return launch_fwd_t<TIn, 13, 4, ASRC>(a, st);
+    if (RPW == 16) return launch_fwd_t<TIn, 16, 4, ASRC>(a, st);
+  }
+  return hipErrorInvalidValue;
+}
+
+// Image mode is used when the mix must run in-kernel, or when whole images fill at least three
+// quarters of a workgroup's columns.
+static bool plan_fwd(Geo& g, const FwdRequest& r) {
+  const bool cached = r.M != nullptr;
+  const bool mix = r.mixw != nullptr;
+  if (!plan_geo(g, r.B, r.C, r.H, r.W, r.w, r.layout, r.in_bf16, cached, true, 0)) {
+    if (!plan_geo(g, r.B, r.C, r.H, r.W, r.w, r.layout, r.in_bf16, cached, false, 0)) return false;
+  }
+  if (g.image_mode && !mix && 4 * g.ipw * g.nWin < 3 * g.NT) {
+    if (!plan_geo(g, r.B, r.C, r.H, r.W, r.w, r.layout, r.in_bf16, cached, false, 0)) return false;
+  }
+  return true;
+}
+
+bool forward_plan_ok(const FwdRequest& r) {
+  Geo g;
+  return plan_fwd(g, r);
+}
+
+size_t forward_workspace(const FwdRequest& r) {
+  Geo g;
+  if (!plan_fwd(g, r)) return 0;
+  if (r.mixw && !g.image_mode && !r.zsave) return (size_t)r.B * r.C * r.H * r.W * sizeof(float);
+  return 0;
+}
+
+hipError_t launch_forward(const FwdRequest& r, hipStream_t st) {
+  FwdArgs a{};
+  if (!plan_fwd(a.g, r)) return hipErrorInvalidValue;
+  a.x = r.x;
+  a.tab = r.T;
+  a.mat = r.M;
+  a.mixw = r.mixw;
+  a.out_bf16 = r.out_bf16;
+  const bool mix = r.mixw != nullptr;
+  float* zbuf = nullptr;
+  if (a.g.image_mode) {
+    a.zsave = r.zsave;
+    a.y = r.y;
+    a.mix_here = mix ? 1 : 0;
+  } else if (mix) {
+    // pre-mix output goes to z_save (fp32 only, checked by the API) or the workspace
+    zbuf = r.zsave ? (float*)r.zsave : (float*)r.ws;
+    a.zsave = nullptr;
+    a.y = zbuf;
+    a.out_bf16 = 0;
+    a.mix_here = 0;
+  } else {
+    a.zsave = r.zsave;
+    a.y = r.y;
+    a.mix_here = 0;
+  }
+  const bool cached = r.M != nullptr;
+  hipError_t e;
+  if (r.in_bf16) e = cached ? launch_fwd_tiles<uint16_t, 1>(a, st) : launch_fwd_tiles<uint16_t, 0>(a, st);
+  else e = cached ? launch_fwd_tiles<float, 1>(a, st) : launch_fwd_tiles<float, 0>(a, st);
+  if (e != hipSuccess) return e;
+  if (!a.g.image_mode && mix)
+    e = launch_mix_fwd(zbuf, r.mixw, r.y, r.out_bf16, r.B, r.C, r.H, r.W, r.layout, st);
+  return e;
+}
+
+}  // namespace wbmm

@@ -1,0 +1,60 @@
+// Host-side launch interface between the C ABI (wbmm_api.cpp) and the kernel translation units.
+// Everything here assumes arguments already validated by the API layer.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace wbmm {
+
+struct FwdRequest {
+  int B, C, H, W, w, layout, in_bf16, out_bf16;
+  const void* x;
+  const void* T;  // exactly one of T / M
+  const void* M;
+  const float* mixw;
+  void* zsave;
+  void* y;
+  void* ws;
+  size_t ws_bytes;
+};
+
+struct BwdRequest {
+  int B, C, H, W, w, layout;
+  const float* x;
+  const float* T;
+  const float* M;
+  const float* mixw;
+  const float* zsaved;
+  const float* dy;
+  float* dx;
+  float* dT;
+  float* dmixw;
+  void* ws;
+  size_t ws_bytes;
+};
+
+hipError_t launch_build_index(int w, int32_t* idx, hipStream_t st);
+hipError_t launch_build_matrix(const void* T, int C, int w, int bf16, void* M, hipStream_t st);
+hipError_t launch_fold(const void* Min, const void* Tsub, int C, int w, int s, int bf16,
+                       void* Mout, hipStream_t st);
+
+// Returns false when no launch shape exists (reported as unsupported by the caller).
+bool forward_plan_ok(const FwdRequest& r);
+size_t forward_workspace(const FwdRequest& r);
+hipError_t launch_forward(const FwdRequest& r, hipStream_t st);
+
+bool backward_plan_ok(const BwdRequest& r);
+size_t backward_workspace(const BwdRequest& r);
+hipError_t launch_backward(const BwdRequest& r, hipStream_t st);
+
+// 3x3 depthwise mix kernels (used by the window-mode paths).
+hipError_t launch_mix_fwd(const float* z, const float* w9, void* y, int out_bf16, int B, int C,
+                          int H, int W, int layout, hipStream_t st);
+hipError_t launch_mix_bwd_data(const float* dy, const float* w9, float* dz, int B, int C, int H,
+                               int W, int layout, hipStream_t st);
+hipError_t launch_mix_bwd_weight(const float* dy, const float* z, float* dw9, int B, int C, int H,
+                                 int W, int layout, hipStream_t st);
+
+}  // namespace wbmm

@@ -1,0 +1,170 @@
+"""C ABI checks that need no GPU: the library loads, exports exactly what include/wbmm.h declares,
+the Python binding's signatures match the header, and invalid arguments are rejected on the host
+(every call here returns before anything is enqueued)."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import receptive_field_spatial_amd as R
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "wbmm.h")
+
+FAKE = 0x100000          # an aligned non-NULL address; never dereferenced by these calls
+FAKE2 = 0x200000
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(R.lib_path()):
+        from receptive_field_spatial_amd.build import build
+        build(verbose=False)
+    return R.load_library()
+
+
+def header_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    decls = re.findall(r"^\s*(?:wbmm_status|int|size_t|const char\*)\s+(wbmm_\w+)\s*\(([^;]*?)\)\s*;",
+                       text, flags=re.M | re.S)
+    out = {}
+    for name, params in decls:
+        params = params.strip()
+        out[name] = 0 if params in ("", "void") else len([p for p in params.split(",") if p.strip()])
+    return out
+
+
+def test_header_declares_the_entry_points():
+    fns = header_functions()
+    for name in ["wbmm_build_index", "wbmm_build_matrix", "wbmm_fold_hier", "wbmm_forward",
+                 "wbmm_backward", "wbmm_forward_workspace_bytes", "wbmm_backward_workspace_bytes",
+                 "wbmm_last_error", "wbmm_abi_version"]:
+        assert name in fns, name
+
+
+def test_library_exports_exactly_the_header(lib):
+    out = subprocess.run(["nm", "-D", "--defined-only", R.lib_path()], capture_output=True,
+                         text=True, check=True).stdout
+    exported = {l.split()[-1] for l in out.splitlines() if " T " in l and l.split()[-1].startswith("wbmm_")}
+    assert exported == set(header_functions())
+    for name in exported:
+        assert hasattr(lib, name)
+
+
+def test_binding_signatures_match_header(lib):
+    for name, nparams in header_functions().items():
+        assert len(getattr(lib, name).argtypes) == nparams, name
+
+
+def test_abi_version(lib):
+    assert lib.wbmm_abi_version() == 1
+
+
+def err(lib):
+    return lib.wbmm_last_error().decode()
+
+
+def test_build_index_validation(lib):
+    assert lib.wbmm_build_index(0, FAKE, None) == R.WBMM_E_INVALID
+    assert "w=0" in err(lib)
+    assert lib.wbmm_build_index(33, FAKE, None) == R.WBMM_E_INVALID
+    assert lib.wbmm_build_index(7, None, None) == R.WBMM_E_INVALID
+    assert lib.wbmm_build_index(7, FAKE + 2, None) == R.WBMM_E_UNSUPPORTED
+
+
+def test_build_matrix_validation(lib):
+    assert lib.wbmm_build_matrix(FAKE, 0, 7, 0, FAKE2, None) == R.WBMM_E_INVALID
+    assert lib.wbmm_build_matrix(FAKE, 4, 7, 5, FAKE2, None) == R.WBMM_E_INVALID
+    assert lib.wbmm_build_matrix(None, 4, 7, 0, FAKE2, None) == R.WBMM_E_INVALID
+    assert lib.wbmm_build_matrix(FAKE, 4, 7, 0, FAKE + 4, None) == R.WBMM_E_INVALID  # overlap
+    assert "overlaps" in err(lib)
+
+
+def test_fold_validation(lib):
+    for w, s in [(14, 5), (14, 14), (14, 0), (7, 7)]:
+        assert lib.wbmm_fold_hier(FAKE, FAKE2, 2, w, s, 0, FAKE, None) == R.WBMM_E_INVALID, (w, s)
+    assert lib.wbmm_fold_hier(FAKE, FAKE2, 2, 14, 7, 0, FAKE + 8, None) == R.WBMM_E_INVALID
+
+
+def fwd(lib, **kw):
+    a = dict(B=1, C=2, H=8, W=8, w=4, layout=0, ind=0, outd=0, x=FAKE, T=FAKE2, M=None, mix=None,
+             z=None, y=0x400000, ws=None, wsb=0)
+    a.update(kw)
+    return lib.wbmm_forward(a["B"], a["C"], a["H"], a["W"], a["w"], a["layout"], a["ind"],
+                            a["outd"], a["x"], a["T"], a["M"], a["mix"], a["z"], a["y"], a["ws"],
+                            a["wsb"], None)
+
+
+def test_forward_validation(lib):
+    assert fwd(lib, w=0) == R.WBMM_E_INVALID
+    assert fwd(lib, w=33) == R.WBMM_E_INVALID
+    assert fwd(lib, B=0) == R.WBMM_E_INVALID
+    assert fwd(lib, layout=3) == R.WBMM_E_INVALID
+    assert fwd(lib, ind=7) == R.WBMM_E_INVALID
+    assert fwd(lib, T=None) == R.WBMM_E_INVALID                 # neither T nor M
+    assert fwd(lib, M=0x800000) == R.WBMM_E_INVALID             # both T and M
+    assert "exactly one" in err(lib)
+    assert fwd(lib, x=None) == R.WBMM_E_INVALID
+    assert fwd(lib, y=FAKE) == R.WBMM_E_INVALID                 # y aliases x
+    assert fwd(lib, mix=0x900000, outd=1) == R.WBMM_E_UNSUPPORTED
+    assert fwd(lib, x=FAKE + 2) == R.WBMM_E_UNSUPPORTED         # misaligned fp32
+    assert fwd(lib, C=70000) == R.WBMM_E_UNSUPPORTED
+
+
+def test_forward_workspace_rules(lib):
+    # a mix on images too large for one workgroup needs an fp32 z buffer unless z_save is given
+    need = lib.wbmm_forward_workspace_bytes(1, 2, 128, 128, 14, 0, 1, 0)
+    assert need == 1 * 2 * 128 * 128 * 4
+    assert lib.wbmm_forward_workspace_bytes(1, 2, 128, 128, 14, 0, 1, 1) == 0
+    assert lib.wbmm_forward_workspace_bytes(1, 2, 100, 100, 14, 0, 1, 0) == 0  # 64 windows: fused
+    assert lib.wbmm_forward_workspace_bytes(64, 192, 28, 28, 14, 0, 1, 0) == 0  # fused in-kernel
+    assert lib.wbmm_forward_workspace_bytes(1, 2, 8, 8, 0, 0, 0, 0) == 0       # invalid -> 0
+    st = fwd(lib, B=1, C=2, H=128, W=128, w=14, mix=0x900000, y=0x40000000, ws=None, wsb=0)
+    assert st == R.WBMM_E_WORKSPACE
+    st = fwd(lib, B=1, C=2, H=128, W=128, w=14, mix=0x900000, y=0x40000000, ws=0xA00000, wsb=need - 1)
+    assert st == R.WBMM_E_WORKSPACE
+
+
+def bwd(lib, **kw):
+    a = dict(B=1, C=2, H=8, W=8, w=4, layout=0, x=FAKE, T=FAKE2, M=None, mix=None, z=None,
+             dy=0x300000, dx=0x400000, dT=0x500000, dW=None, ws=None, wsb=0)
+    a.update(kw)
+    return lib.wbmm_backward(a["B"], a["C"], a["H"], a["W"], a["w"], a["layout"], a["x"], a["T"],
+                             a["M"], a["mix"], a["z"], a["dy"], a["dx"], a["dT"], a["dW"], a["ws"],
+                             a["wsb"], None)
+
+
+def test_backward_validation(lib):
+    assert bwd(lib, w=17) == R.WBMM_E_UNSUPPORTED
+    assert "w <= 16" in err(lib)
+    assert bwd(lib, T=None) == R.WBMM_E_INVALID
+    assert bwd(lib, mix=0x900000) == R.WBMM_E_INVALID           # mix without z_saved
+    assert bwd(lib, z=0x900000) == R.WBMM_E_INVALID             # z_saved without mix
+    assert bwd(lib, dx=FAKE) == R.WBMM_E_INVALID                # dx aliases x
+    assert bwd(lib, dy=None) == R.WBMM_E_INVALID
+    need = lib.wbmm_backward_workspace_bytes(1, 2, 8, 8, 4, 0, 0)
+    assert need > 0
+    assert bwd(lib) == R.WBMM_E_WORKSPACE
+    assert bwd(lib, ws=0xA00000, wsb=need - 1) == R.WBMM_E_WORKSPACE
+    assert bwd(lib, ws=0xA00010, wsb=need) == R.WBMM_E_UNSUPPORTED  # not 256-byte aligned
+    assert lib.wbmm_backward_workspace_bytes(1, 2, 8, 8, 17, 0, 0) == 0
+
+
+def test_last_error_is_per_thread(lib):
+    import threading
+    assert lib.wbmm_build_index(0, FAKE, None) == R.WBMM_E_INVALID
+    seen = []
+    t = threading.Thread(target=lambda: seen.append(lib.wbmm_last_error()))
+    t.start()
+    t.join()
+    assert seen == [b""]
+    assert err(lib) != ""
+
+
+def test_missing_library_fails_loudly(tmp_path):
+    with pytest.raises(R.WbmmError):
+        R.load_library(str(tmp_path / "nope.so"))
+    R.load_library()  # restore

@@ -1,0 +1,380 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle, element by element.
+
+Every case prints its name, shapes and seed before touching the GPU. Inputs come from the seeded
+generators in receptive_field_spatial_amd.synth; expected values come only from oracle/.
+"""
+import numpy as np
+import pytest
+
+from oracle import wbmm_oracle as O
+from receptive_field_spatial_amd import synth
+from tests.parity_util import assert_bf16, assert_f32
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    assert torch.cuda.is_available(), "GPU tests need an MI355X"
+    import receptive_field_spatial_amd as R
+    R.load_library()
+    return R
+
+
+def R():
+    import receptive_field_spatial_amd as mod
+    return mod
+
+
+def say(msg):
+    print(f"\n[case] {msg}", flush=True)
+
+
+def dev(a, dtype=torch.float32):
+    return torch.from_numpy(np.ascontiguousarray(a)).to(dtype).cuda()
+
+
+def dev_bf16(a_f32):
+    """bf16-valued float32 numpy -> torch bfloat16 on the GPU (exact)."""
+    bits = synth.f32_to_bf16_bits(a_f32).view(np.int16)
+    return torch.from_numpy(np.ascontiguousarray(bits)).view(torch.bfloat16).cuda()
+
+
+def host(t):
+    return t.float().cpu().numpy()
+
+
+# ----------------------------------------------------------------------------- index / matrix
+@pytest.mark.parametrize("w", [1, 2, 3, 5, 7, 14, 16, 28, 32])
+def test_build_index_bit_exact(w):
+    say(f"build_index w={w}")
+    got = R().wbmm_build_index(w)
+    torch.cuda.synchronize()
+    assert np.array_equal(got.cpu().numpy(), O.build_index(w))
+
+
+@pytest.mark.parametrize("w,C", [(1, 2), (4, 3), (7, 8), (14, 5), (28, 2)])
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+def test_build_matrix_bit_exact(w, C, dt):
+    say(f"build_matrix w={w} C={C} {dt}")
+    T = synth.normal_f32((C, 2 * w - 1, 2 * w - 1), 0.02, seed=w)
+    if dt == "bf16":
+        T = synth.round_to_bf16(T)
+        got = R().wbmm_build_matrix(dev_bf16(T), w)
+    else:
+        got = R().wbmm_build_matrix(dev(T), w)
+    want = O.build_matrix(T, w)
+    assert np.array_equal(host(got), want)
+
+
+@pytest.mark.parametrize("w,s,C", [(14, 7, 4), (4, 2, 3), (6, 3, 2), (12, 4, 2), (28, 7, 1)])
+def test_fold_bit_exact_f32(w, s, C):
+    say(f"fold_hier f32 w={w} s={s} C={C}")
+    T = synth.normal_f32((C, 2 * w - 1, 2 * w - 1), 0.02, seed=1)
+    Ts = synth.normal_f32((C, 2 * s - 1, 2 * s - 1), 0.02, seed=2)
+    M = R().wbmm_build_matrix(dev(T), w)
+    got = R().wbmm_fold_hier(M, dev(Ts), w, s)
+    want = O.fold_hier(O.build_matrix(T, w), Ts, w, s)
+    assert np.array_equal(host(got), want)
+    # in place
+    R().wbmm_fold_hier(M, dev(Ts), w, s, out=M)
+    assert np.array_equal(host(M), want)
+
+
+def test_fold_bf16_rounds_once():
+    w, s, C = 14, 7, 2
+    say("fold_hier bf16 w=14 s=7")
+    T = synth.round_to_bf16(synth.normal_f32((C, 27, 27), 0.02, seed=3))
+    Ts = synth.round_to_bf16(synth.normal_f32((C, 13, 13), 0.02, seed=4))
+    got = R().wbmm_fold_hier(R().wbmm_build_matrix(dev_bf16(T), w), dev_bf16(Ts), w, s)
+    # oracle: fp32 add of the two bf16 values, then one RNE rounding to bf16
+    want = synth.round_to_bf16(O.fold_hier(O.build_matrix(T, w), Ts, w, s))
+    assert np.array_equal(host(got), want)
+
+
+# ----------------------------------------------------------------------------- forward fp32
+def fwd_case(B, C, H, W, w, *, cached=False, mix=False, layout="NCHW", seed=0, zsave=False):
+    x = synth.normal_f32((B, C, H, W), 1.0, seed=seed)
+    T = synth.normal_f32((C, 2 * w - 1, 2 * w - 1), 0.02, seed=seed + 1)
+    Wm = synth.normal_f32((C, 3, 3), 0.1, seed=seed + 2) if mix else None
+    xd = dev(x if layout == "NCHW" else x.transpose(0, 2, 3, 1))
+    Td = dev(T)
+    kw = {}
+    if cached:
+        kw["M"] = R().wbmm_build_matrix(Td, w)
+    else:
+        kw["T"] = Td
+    zs = torch.empty_like(xd) if zsave else None
+    y = R().wbmm_forward(xd, w, mix_w=dev(Wm) if mix else None, layout=layout, z_save=zs, **kw)
+    yh = host(y)
+    zh = host(zs) if zsave else None
+    if layout == "NHWC":
+        yh = yh.transpose(0, 3, 1, 2)
+        zh = zh.transpose(0, 3, 1, 2) if zsave else None
+    want_y, want_z = O.layer_forward(x.astype(np.float64), w, T=T.astype(np.float64), Wmix=Wm)
+    return yh, want_y, zh, want_z
+
+
+@pytest.mark.parametrize("cached", [False, True])
+def test_forward_tiny_workload(cached):
+    wl = synth.WORKLOADS["tiny_w7"]
+    say(f"forward tiny_w7 cached={cached}")
+    inp = synth.draw_inputs(wl)
+    x, T = inp["x"], inp["T"]
+    kw = {"M": R().wbmm_build_matrix(dev(T), wl.w)} if cached else {"T": dev(T)}
+    y = R().wbmm_forward(dev(x), wl.w, **kw)
+    assert_f32(host(y), O.wbmm_forward(x.astype(np.float64), wl.w, T=T.astype(np.float64)), "y")
+
+
+@pytest.mark.parametrize("B,C,H,W,w", [
+    (2, 3, 10, 13, 4),    # padding on both axes
+    (1, 2, 5, 5, 5),      # one window
+    (3, 2, 7, 3, 3),      # tall/narrow ragged
+    (2, 2, 4, 4, 1),      # w = 1
+    (2, 3, 30, 17, 6),
+    (1, 2, 33, 47, 8),
+    (2, 2, 20, 21, 10),
+    (1, 3, 28, 42, 14),
+    (2, 2, 30, 30, 15),
+    (1, 2, 32, 48, 16),
+    (1, 2, 40, 37, 20),   # w > 16: rows split over waves
+    (1, 1, 56, 56, 28),
+    (1, 1, 40, 64, 32),
+])
+@pytest.mark.parametrize("cached", [False, True])
+def test_forward_shapes(B, C, H, W, w, cached):
+    say(f"forward shapes B={B} C={C} H={H} W={W} w={w} cached={cached}")
+    yh, want, _, _ = fwd_case(B, C, H, W, w, cached=cached)
+    assert_f32(yh, want, "y")
+
+
+@pytest.mark.parametrize("B,C,H,W,w", [(2, 3, 28, 28, 14), (1, 4, 10, 13, 4), (3, 2, 56, 56, 7)])
+@pytest.mark.parametrize("cached", [False, True])
+def test_forward_mix_and_zsave(B, C, H, W, w, cached):
+    say(f"forward mix+zsave B={B} C={C} H={H} W={W} w={w} cached={cached}")
+    yh, want_y, zh, want_z = fwd_case(B, C, H, W, w, cached=cached, mix=True, zsave=True)
+    assert_f32(yh, want_y, "y")
+    assert_f32(zh, want_z, "z")
+
+
+def test_forward_mix_window_mode():
+    """Images too large for one workgroup (100 windows): the mix runs as its own pass."""
+    say("forward mix window mode B=1 C=2 H=W=128 w=14")
+    yh, want_y, zh, want_z = fwd_case(1, 2, 128, 128, 14, mix=True, zsave=True)
+    assert_f32(yh, want_y, "y")
+    assert_f32(zh, want_z, "z")
+    yh, want_y, _, _ = fwd_case(1, 2, 128, 128, 14, mix=True, zsave=False)
+    assert_f32(yh, want_y, "y (workspace)")
+
+
+@pytest.mark.parametrize("w", [4, 7, 14])
+def test_forward_nhwc(w):
+    say(f"forward NHWC w={w}")
+    yh, want, _, _ = fwd_case(2, 5, 2 * w + 3, 3 * w - 2, w, layout="NHWC")
+    assert_f32(yh, want, "y")
+    yh, want, _, _ = fwd_case(2, 5, 28, 28, w, layout="NHWC", mix=True)
+    assert_f32(yh, want, "y mix")
+
+
+@pytest.mark.parametrize("w", [1, 4, 7, 14, 28])
+@pytest.mark.parametrize("cached", [False, True])
+def test_forward_one_hot_identity_bitwise(w, cached):
+    """Centre one-hot table: products with 0 and 1 are exact, so the output equals x bitwise."""
+    say(f"one-hot identity w={w} cached={cached}")
+    C = 3
+    x = synth.normal_f32((2, C, 2 * w + 1, w + 3), 1.0, seed=5)
+    T = np.zeros((C, 2 * w - 1, 2 * w - 1), np.float32)
+    T[:, w - 1, w - 1] = 1.0
+    kw = {"M": R().wbmm_build_matrix(dev(T), w)} if cached else {"T": dev(T)}
+    y = R().wbmm_forward(dev(x), w, **kw)
+    assert np.array_equal(host(y), x)
+
+
+def test_forward_one_hot_shift_bitwise():
+    w, C = 7, 2
+    say("one-hot shift w=7")
+    x = synth.normal_f32((1, C, 14, 21), 1.0, seed=6)
+    T = np.zeros((C, 13, 13), np.float32)
+    T[:, w - 1 + 2, w - 1 - 1] = 1.0  # out(y, x) = in(y - 2, x + 1)
+    y = host(R().wbmm_forward(dev(x), w, T=dev(T)))
+    want = O.wbmm_forward(x.astype(np.float64), w, T=T.astype(np.float64))
+    assert np.array_equal(y, want.astype(np.float32))
+
+
+# ----------------------------------------------------------------------------- forward bf16
+@pytest.mark.parametrize("w", [4, 7, 14, 28])
+@pytest.mark.parametrize("cached", [False, True])
+@pytest.mark.parametrize("out", ["bf16", "f32"])
+def test_forward_bf16(w, cached, out):
+    say(f"forward bf16 w={w} cached={cached} out={out}")
+    B, C, H, W = 2, 3, 2 * w + 5, 2 * w
+    x = synth.round_to_bf16(synth.normal_f32((B, C, H, W), 1.0, seed=7))
+    T = synth.round_to_bf16(synth.normal_f32((C, 2 * w - 1, 2 * w - 1), 0.02, seed=8))
+    Td = dev_bf16(T)
+    kw = {"M": R().wbmm_build_matrix(Td, w)} if cached else {"T": Td}
+    od = torch.bfloat16 if out == "bf16" else torch.float32
+    y = R().wbmm_forward(dev_bf16(x), w, out_dtype=od, **kw)
+    want = O.wbmm_forward(x.astype(np.float64), w, T=T.astype(np.float64))
+    assert_bf16(host(y), want, "y")
+    if out == "f32":  # fp32 output: only accumulation-order differences remain
+        assert_f32(host(y), want, "y (fp32 out)")
+
+
+# ----------------------------------------------------------------------------- workloads
+def _sample_channels(C, k, seed=0):
+    rng = np.random.default_rng(seed + 1000)
+    return np.sort(rng.choice(C, size=min(k, C), replace=False))
+
+
+@pytest.mark.parametrize("cached", [False, True])
+def test_workload_stage1_w14_sampled(cached):
+    wl = synth.WORKLOADS["stage1_w14"]
+    say(f"stage1_w14 full size B={wl.B} C={wl.C} cached={cached}")
+    inp = synth.draw_inputs(wl)
+    x, T = inp["x"], inp["T"]
+    Td = dev(T)
+    kw = {"M": R().wbmm_build_matrix(Td, wl.w)} if cached else {"T": Td}
+    y = host(R().wbmm_forward(dev(x), wl.w, **kw))
+    ch = _sample_channels(wl.C, 6)
+    want = O.wbmm_forward(x[:, ch].astype(np.float64), wl.w, T=T[ch].astype(np.float64))
+    assert_f32(y[:, ch], want, f"y channels {list(ch)}")
+
+
+@pytest.mark.parametrize("name", ["bf16_w7", "bf16_w14", "bf16_w28"])
+def test_workload_bf16_sweep_sampled(name):
+    wl = synth.WORKLOADS[name]
+    say(f"{name} full size B={wl.B} C={wl.C}")
+    inp = synth.draw_inputs(wl)
+    x, T = inp["x"], inp["T"]
+    y = host(R().wbmm_forward(dev_bf16(x), wl.w, T=dev_bf16(T)))
+    ch = _sample_channels(wl.C, 4)
+    want = O.wbmm_forward(x[:, ch].astype(np.float64), wl.w, T=T[ch].astype(np.float64))
+    assert_bf16(y[:, ch], want, f"y channels {list(ch)}")
+
+
+def test_workload_highres_fold_mix():
+    wl = synth.WORKLOADS["highres_w14"]
+    say(f"highres_w14 B={wl.B} C={wl.C} H={wl.H} fold s={wl.s} + mix")
+    inp = synth.draw_inputs(wl)
+    x, T, Ts, Wm = inp["x"], inp["T"], inp["T_sub"], inp["Wmix"]
+    M = R().wbmm_fold_hier(R().wbmm_build_matrix(dev(T), wl.w), dev(Ts), wl.w, wl.s)
+    Mh = host(M)
+    Mo = O.fold_hier(O.build_matrix(T, wl.w), Ts, wl.w, wl.s)
+    assert np.array_equal(Mh, Mo)
+    zs = torch.empty(x.shape, dtype=torch.float32, device="cuda")
+    y = R().wbmm_forward(dev(x), wl.w, M=M, mix_w=dev(Wm), z_save=zs)
+    want_y, want_z = O.layer_forward(x.astype(np.float64), wl.w, M=Mo, Wmix=Wm)
+    assert_f32(host(zs), want_z, "z")
+    assert_f32(host(y), want_y, "y")
+
+
+# ----------------------------------------------------------------------------- backward
+def bwd_case(B, C, H, W, w, *, mix, cached=False, layout="NCHW", seed=0):
+    x = synth.normal_f32((B, C, H, W), 1.0, seed=seed)
+    T = synth.normal_f32((C, 2 * w - 1, 2 * w - 1), 0.02, seed=seed + 1)
+    Wm = synth.normal_f32((C, 3, 3), 0.1, seed=seed + 2) if mix else None
+    dy = synth.normal_f32((B, C, H, W), 1.0, seed=seed + 3)
+    to_l = (lambda a: a) if layout == "NCHW" else (lambda a: a.transpose(0, 2, 3, 1))
+    from_l = (lambda a: a) if layout == "NCHW" else (lambda a: a.transpose(0, 3, 1, 2))
+    xd, dyd, Td = dev(to_l(x)), dev(to_l(dy)), dev(T)
+    kw = {"M": R().wbmm_build_matrix(Td, w)} if cached else {"T": Td}
+    Wd = dev(Wm) if mix else None
+    zs = torch.empty_like(xd) if mix else None
+    R().wbmm_forward(xd, w, mix_w=Wd, z_save=zs, layout=layout, **kw)
+    dx, dT, dW = R().wbmm_backward(xd, dyd, w, mix_w=Wd, z_saved=zs, layout=layout, **kw)
+    # the oracle's backward uses the z the GPU saved (fp32), as the GPU does
+    z_used = from_l(host(zs)).astype(np.float64) if mix else None
+    wdx, wdT, wdW = O.layer_backward(x.astype(np.float64), dy.astype(np.float64), w,
+                                     T=T.astype(np.float64), Wmix=Wm, z=z_used)
+    return (from_l(host(dx)), host(dT), host(dW) if mix else None), (wdx, wdT, wdW)
+
+
+@pytest.mark.parametrize("B,C,H,W,w,mix", [
+    (2, 3, 28, 28, 14, True), (2, 3, 28, 28, 14, False), (3, 2, 10, 13, 4, True),
+    (1, 2, 7, 7, 7, False), (2, 2, 21, 14, 7, True), (2, 1, 4, 4, 1, True),
+    (1, 2, 30, 30, 15, False), (1, 2, 32, 32, 16, True), (1, 2, 100, 100, 14, True),
+    (1, 2, 128, 128, 14, True), (2, 2, 128, 120, 14, False),
+    (2, 2, 17, 23, 5, False),
+])
+@pytest.mark.parametrize("cached", [False, True])
+def test_backward_shapes(B, C, H, W, w, mix, cached):
+    say(f"backward B={B} C={C} H={H} W={W} w={w} mix={mix} cached={cached}")
+    (dx, dT, dW), (wdx, wdT, wdW) = bwd_case(B, C, H, W, w, mix=mix, cached=cached)
+    assert_f32(dx, wdx, "dx")
+    assert_f32(dT, wdT, "dT")
+    if mix:
+        assert_f32(dW, wdW, "dWmix")
+
+
+def test_backward_nhwc():
+    say("backward NHWC B=2 C=3 28x28 w=14 mix")
+    (dx, dT, dW), (wdx, wdT, wdW) = bwd_case(2, 3, 28, 28, 14, mix=True, layout="NHWC")
+    assert_f32(dx, wdx, "dx")
+    assert_f32(dT, wdT, "dT")
+    assert_f32(dW, wdW, "dWmix")
+
+
+def test_workload_train_w14_full():
+    """The training workload at full size: every output against the oracle, plus determinism."""
+    wl = synth.WORKLOADS["train_w14"]
+    say(f"train_w14 full B={wl.B} C={wl.C} H={wl.H} w={wl.w} fwd+bwd")
+    inp = synth.draw_inputs(wl)
+    x, T, Wm, dy = inp["x"], inp["T"], inp["Wmix"], inp["dY"]
+    xd, Td, Wd, dyd = dev(x), dev(T), dev(Wm), dev(dy)
+    zs = torch.empty_like(xd)
+    y = R().wbmm_forward(xd, wl.w, T=Td, mix_w=Wd, z_save=zs)
+    ws = torch.zeros(R().wbmm_backward_workspace_bytes(wl.B, wl.C, wl.H, wl.W, wl.w, has_mix=True),
+                     dtype=torch.uint8, device="cuda")
+    dx, dT, dW = R().wbmm_backward(xd, dyd, wl.w, T=Td, mix_w=Wd, z_saved=zs, workspace=ws)
+    want_y, want_z = O.layer_forward(x.astype(np.float64), wl.w, T=T.astype(np.float64), Wmix=Wm)
+    assert_f32(host(y), want_y, "y")
+    assert_f32(host(zs), want_z, "z")
+    wdx, wdT, wdW = O.layer_backward(x.astype(np.float64), dy.astype(np.float64), wl.w,
+                                     T=T.astype(np.float64), Wmix=Wm, z=host(zs).astype(np.float64))
+    assert_f32(host(dx), wdx, "dx")
+    assert_f32(host(dT), wdT, "dT")
+    assert_f32(host(dW), wdW, "dWmix")
+    # run twice: bitwise identical (fixed-order reductions; workspace reused)
+    y2 = R().wbmm_forward(xd, wl.w, T=Td, mix_w=Wd)
+    dx2, dT2, dW2 = R().wbmm_backward(xd, dyd, wl.w, T=Td, mix_w=Wd, z_saved=zs, workspace=ws)
+    assert torch.equal(y, y2) and torch.equal(dx, dx2)
+    assert torch.equal(dT, dT2) and torch.equal(dW, dW2)
+
+
+def test_backward_partial_outputs():
+    say("backward partial outputs (dT only, dx only)")
+    B, C, H, W, w = 2, 3, 28, 28, 14
+    x = synth.normal_f32((B, C, H, W), 1.0, seed=11)
+    T = synth.normal_f32((C, 27, 27), 0.02, seed=12)
+    dy = synth.normal_f32((B, C, H, W), 1.0, seed=13)
+    _, dT, _ = R().wbmm_backward(dev(x), dev(dy), w, T=dev(T), dx=False)
+    dx, dT2, _ = R().wbmm_backward(dev(x), dev(dy), w, T=dev(T), dT=False)
+    assert dT2 is None
+    wdx, wdT, _ = O.layer_backward(x.astype(np.float64), dy.astype(np.float64), w, T=T.astype(np.float64))
+    assert_f32(host(dT), wdT, "dT")
+    assert_f32(host(dx), wdx, "dx")
+
+
+def test_errors_enqueue_nothing():
+    """Invalid calls fail on the host with a message and leave outputs untouched."""
+    say("error paths")
+    Rm = R()
+    x = torch.zeros((1, 2, 8, 8), device="cuda")
+    y = torch.full_like(x, 7.0)
+    T = torch.zeros((2, 7, 7), device="cuda")
+    with pytest.raises(Rm.WbmmError) as e:
+        Rm.wbmm_forward(x, 4, T=T, M=Rm.wbmm_build_matrix(T, 4), y=y)
+    assert e.value.status == Rm.WBMM_E_INVALID
+    with pytest.raises(Rm.WbmmError) as e:
+        Rm.wbmm_forward(x, 33, T=T, y=y)
+    assert e.value.status == Rm.WBMM_E_INVALID
+    with pytest.raises(Rm.WbmmError) as e:
+        Rm.wbmm_forward(x, 4, T=T, y=x)  # y aliases x
+    assert e.value.status == Rm.WBMM_E_INVALID
+    with pytest.raises(Rm.WbmmError) as e:
+        Rm.wbmm_backward(x, x, 20, T=torch.zeros((2, 39, 39), device="cuda"))
+    assert e.value.status == Rm.WBMM_E_UNSUPPORTED
+    torch.cuda.synchronize()
+    assert torch.all(y == 7.0)
