@@ -1,0 +1,352 @@
+#!/usr/bin/env python3
+"""WBMM benchmark on one MI355X: the layer's training step (forward + backward) at w = 14.
+
+A step is one pass of the whole hot path over one synthetic batch of the training workload
+(B=64, C=192, 28x28, w=14, 3x3 inter-block mix): the fused forward kernel (partition, M_c formed
+on chip from the table, MFMA contraction, reverse, mix, saved pre-mix map) and the fused backward
+kernel (mix adjoint, dX = M^T G, row-pair MFMA table gradient, dWmix, fixed-order reduction).
+
+Prints ONE JSON line on stdout; diagnostics go to stderr.
+
+  python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+  python bench.py --copy-calibration        # plain device copy for HBM counter scaling
+  python bench.py --summarize-pmc DIR ...   # turn rocprofv3 --pmc output into profiles/ json
+"""
+from __future__ import annotations
+
+import argparse
+import csv
+import glob
+import hashlib
+import json
+import os
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+FP32_MFMA_PEAK_TFLOPS = 157.3     # MI355X dense fp32 matrix
+BF16_MFMA_PEAK_TFLOPS = 2516.6    # MI355X dense bf16 matrix
+HBM_PEAK_GBS = 8000.0             # MI355X HBM3E
+METRIC = "WBMM fwd+bwd GFLOP/s & out-elems/s at w=14; % of MFMA/HBM roofline"
+CSRC = os.path.join(ROOT, "receptive_field_spatial_amd", "csrc")
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for p in sorted(glob.glob(os.path.join(CSRC, "*"))):
+        with open(p, "rb") as f:
+            h.update(os.path.basename(p).encode())
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+# ----------------------------------------------------------------------------- accounting
+def accounting(wl):
+    """Algorithmic flops and bytes (the method's minimum), per kernel and per step.
+
+    flops: 2d per output element for the window contraction, 4d for its backward (dX + dT),
+    18 per element for the 3x3 mix and 36 for its backward (data + weight).
+    bytes: every input read once, every output written once, plus the per-channel table.
+    """
+    d = wl.w * wl.w
+    E = wl.B * wl.C * wl.H * wl.W
+    esz = 2 if wl.dtype == "bf16" else 4
+    L = (2 * wl.w - 1) ** 2
+    tab = wl.C * L * esz
+    fwd_flops = E * (2 * d + (18 if wl.mix else 0))
+    fwd_bytes = E * esz * (2 + (1 if wl.backward else 0)) + tab + (wl.C * 36 if wl.mix else 0)
+    acc = {"E": E, "d": d, "fwd_flops": fwd_flops, "fwd_bytes": fwd_bytes}
+    if wl.backward:
+        acc["bwd_flops"] = E * (4 * d + (36 if wl.mix else 0))
+        # reads x, dy, z (mix), table; writes dx, dT, dWmix
+        acc["bwd_bytes"] = E * 4 * (3 + (1 if wl.mix else 0)) + 2 * tab + (wl.C * 72 if wl.mix else 0)
+    acc["step_flops"] = fwd_flops + acc.get("bwd_flops", 0)
+    return acc
+
+
+# ----------------------------------------------------------------------------- CPU baseline
+def cpu_baseline(wl, budget_s: float = 10.0):
+    """Time the oracle (as it is) on the same step, repeated until ~budget_s of CPU work."""
+    import numpy as np
+    from threadpoolctl import threadpool_info
+    from oracle import wbmm_oracle as O
+    from receptive_field_spatial_amd import synth
+
+    inp = synth.draw_inputs(wl)
+    x = inp["x"].astype(np.float64)
+    T = inp["T"].astype(np.float64)
+    Wm = inp.get("Wmix")
+    dy = inp["dY"].astype(np.float64) if wl.backward else None
+    times = []
+    t_start = time.perf_counter()
+    while True:
+        t0 = time.perf_counter()
+        y, z = O.layer_forward(x, wl.w, T=T, Wmix=Wm)
+        if wl.backward:
+            O.layer_backward(x, dy, wl.w, T=T, Wmix=Wm, z=z)
+        times.append(time.perf_counter() - t0)
+        if time.perf_counter() - t_start >= budget_s and len(times) >= 3:
+            break
+    med = statistics.median(times)
+    threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    acc = accounting(wl)
+    return {
+        "value": round(acc["step_flops"] / med / 1e9, 3),
+        "unit": "GFLOP/s",
+        "cores": threads,
+        "kind": "oracle",
+        "sample": f"full {wl.name} step (fwd+bwd, all {wl.C} channels), {len(times)} runs, median "
+                  f"{med:.3f} s; fp64 numpy/OpenBLAS on {len(os.sched_getaffinity(0))} host CPUs",
+    }
+
+
+# ----------------------------------------------------------------------------- traffic
+def load_traffic(workload: str, kernel: str):
+    """HBM bytes per launch from a committed rocprofv3 --pmc summary, if taken on this source."""
+    p = os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
+    if not os.path.exists(p):
+        return None
+    with open(p) as f:
+        rec = json.load(f)
+    if rec.get("src_hash") != kernel_source_hash():
+        return None
+    k = rec.get("kernels", {}).get(kernel)
+    return None if k is None else k.get("hbm_bytes_per_launch")
+
+
+# ----------------------------------------------------------------------------- GPU run
+def run(args):
+    import numpy as np
+    import torch
+
+    import receptive_field_spatial_amd as R
+    from receptive_field_spatial_amd import synth
+
+    R.load_library()
+    wl = synth.WORKLOADS[args.workload]
+    acc = accounting(wl)
+    dev = torch.device("cuda:0")
+    inp = synth.draw_inputs(wl)
+    bf16 = wl.dtype == "bf16"
+
+    def to_dev(a):
+        t = torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+        return t.to(torch.bfloat16) if bf16 else t
+
+    # Rotate among independent input/output sets so that each step reads a batch that is not
+    # already sitting in the 256 MB last-level cache (as in training, where batches change).
+    nsets = max(1, args.rotate)
+    sets = []
+    for _ in range(nsets):
+        s = {"x": to_dev(inp["x"])}
+        s["y"] = torch.empty_like(s["x"])
+        if wl.backward:
+            s["dy"] = to_dev(inp["dY"])
+            s["z"] = torch.empty_like(s["x"])
+            s["dx"] = torch.empty_like(s["x"])
+        sets.append(s)
+    T = to_dev(inp["T"])
+    Wm = to_dev(inp["Wmix"]) if wl.mix else None
+    M = None
+    if wl.s is not None:  # inference caching + hierarchical fold, built once
+        M = R.wbmm_fold_hier(R.wbmm_build_matrix(T, wl.w), to_dev(inp["T_sub"]), wl.w, wl.s)
+    L = 2 * wl.w - 1
+    dT = torch.empty((wl.C, L, L), dtype=torch.float32, device=dev)
+    dW = torch.empty((wl.C, 3, 3), dtype=torch.float32, device=dev) if wl.mix else None
+    ws_b = None
+    if wl.backward:
+        nb = R.wbmm_backward_workspace_bytes(wl.B, wl.C, wl.H, wl.W, wl.w, has_mix=wl.mix)
+        ws_b = torch.zeros(nb, dtype=torch.uint8, device=dev)
+    nf = R.wbmm_forward_workspace_bytes(wl.B, wl.C, wl.H, wl.W, wl.w, has_mix=wl.mix,
+                                        has_z_save=wl.backward)
+    ws_f = torch.empty(max(nf, 1), dtype=torch.uint8, device=dev) if nf else None
+    stream = torch.cuda.current_stream()
+    kw_tab = {"M": M} if M is not None else {"T": T}
+
+    def fwd(s):
+        R.wbmm_forward(s["x"], wl.w, mix_w=Wm, y=s["y"], z_save=s.get("z"), workspace=ws_f,
+                       stream=stream, **kw_tab)
+
+    def bwd(s):
+        R.wbmm_backward(s["x"], s["dy"], wl.w, mix_w=Wm, z_saved=s["z"] if wl.mix else None,
+                        dx=s["dx"], dT=dT, dmix_w=dW if wl.mix else False, workspace=ws_b,
+                        stream=stream, **kw_tab)
+
+    for i in range(args.warmup):
+        s = sets[i % nsets]
+        fwd(s)
+        if wl.backward:
+            bwd(s)
+    torch.cuda.synchronize()
+
+    K = args.steps
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(K)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    start = torch.cuda.Event(enable_timing=True)
+    stop = torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for i in range(K):
+        s = sets[i % nsets]
+        ev[i][0].record(stream)
+        fwd(s)
+        ev[i][1].record(stream)
+        if wl.backward:
+            bwd(s)
+        ev[i][2].record(stream)
+    stop.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    total_ms = start.elapsed_time(stop)
+    ms_step = total_ms / K
+    fwd_ms = [e[0].elapsed_time(e[1]) for e in ev]
+    bwd_ms = [e[1].elapsed_time(e[2]) for e in ev] if wl.backward else []
+    log(f"[bench] {wl.name}: {K} steps in {total_ms:.3f} ms GPU ({wall*1e3:.1f} ms wall); "
+        f"fwd call avg {statistics.mean(fwd_ms)*1e3:.1f} us"
+        + (f", bwd call avg {statistics.mean(bwd_ms)*1e3:.1f} us" if bwd_ms else ""))
+
+    # dominant kernel and its roofline
+    fwd_avg = statistics.mean(fwd_ms) / 1e3
+    kernels = {"k_wbmm_fwd": (fwd_avg, acc["fwd_flops"], acc["fwd_bytes"])}
+    if wl.backward:
+        kernels["k_wbmm_bwd"] = (statistics.mean(bwd_ms) / 1e3, acc["bwd_flops"], acc["bwd_bytes"])
+    kname = max(kernels, key=lambda k: kernels[k][0])
+    ksec, kflops, kbytes = kernels[kname]
+    mfma_bound = not (bf16 and wl.w <= 14)
+    if mfma_bound:
+        peak = BF16_MFMA_PEAK_TFLOPS if bf16 else FP32_MFMA_PEAK_TFLOPS
+        achieved = kflops / ksec / 1e12
+        roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak, "unit": "TFLOP/s",
+                "frac": round(achieved / peak, 4)}
+    else:
+        achieved = kbytes / ksec / 1e9
+        roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(achieved / HBM_PEAK_GBS, 4)}
+    roof["traffic"] = load_traffic(wl.name, kname)
+    roof["kernel"] = kname
+    roof["kernel_us"] = round(ksec * 1e6, 2)
+    roof["algorithmic_per_launch"] = kflops if mfma_bound else kbytes
+
+    value = acc["step_flops"] / (ms_step / 1e3) / 1e9
+    line = {
+        "metric": METRIC,
+        "value": round(value, 1),
+        "unit": "GFLOP/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if bf16 else "f32",
+        "data": "synthetic",
+        "config": {"workload": wl.name, "B": wl.B, "C": wl.C, "H": wl.H, "W": wl.W, "w": wl.w,
+                   "mix": wl.mix, "fold_s": wl.s, "pass": "fwd+bwd" if wl.backward else "fwd",
+                   "matrix": "cached M" if M is not None else "formed on chip from T",
+                   "rotating_batches": nsets},
+        "out_elems_per_s": round(acc["E"] / (ms_step / 1e3), 1),
+        "roofline": roof,
+    }
+    if wl.backward:
+        line["kernels_us"] = {k: round(v[0] * 1e6, 2) for k, v in kernels.items()}
+    if args.cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(wl, args.cpu_budget)
+    return line
+
+
+# ----------------------------------------------------------------------------- profiling helpers
+def copy_calibration(mib: int = 512):
+    """A plain device-to-device copy of known size (read mib MiB, write mib MiB)."""
+    import torch
+    n = mib * 1024 * 1024 // 4
+    a = torch.ones(n, dtype=torch.float32, device="cuda")
+    b = torch.empty_like(a)
+    for _ in range(3):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    log(f"[copy] {mib} MiB copied 3 times")
+
+
+def _pmc_rows(d):
+    rows = []
+    for p in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+        with open(p) as f:
+            rows += list(csv.DictReader(f))
+    return rows
+
+
+def _per_dispatch(rows, counter, name_filter):
+    vals = {}
+    for r in rows:
+        if r.get("Counter_Name") != counter or name_filter not in r.get("Kernel_Name", ""):
+            continue
+        key = r.get("Dispatch_Id")
+        vals[key] = vals.get(key, 0.0) + float(r["Counter_Value"])
+    return statistics.median(vals.values()) if vals else None
+
+
+def summarize_pmc(workload, fetch_dir, write_dir, copy_fetch_dir, copy_write_dir, copy_mib=512):
+    """FETCH_SIZE / WRITE_SIZE (KiB per dispatch) -> bytes, scaled by the copy kernel's reading."""
+    true_kib = copy_mib * 1024.0
+    cf = _per_dispatch(_pmc_rows(copy_fetch_dir), "FETCH_SIZE", "")
+    cw = _per_dispatch(_pmc_rows(copy_write_dir), "WRITE_SIZE", "")
+    f_fac = cf / true_kib
+    w_fac = cw / true_kib
+    rec = {"workload": workload, "src_hash": kernel_source_hash(),
+           "copy_kernel": {"bytes_each_way": copy_mib * 2**20, "fetch_kib": cf, "write_kib": cw,
+                           "fetch_factor": f_fac, "write_factor": w_fac},
+           "kernels": {}}
+    frows, wrows = _pmc_rows(fetch_dir), _pmc_rows(write_dir)
+    for k in ("k_wbmm_fwd", "k_wbmm_bwd"):
+        fk = _per_dispatch(frows, "FETCH_SIZE", k)
+        wk = _per_dispatch(wrows, "WRITE_SIZE", k)
+        if fk is None or wk is None:
+            continue
+        rb = fk / f_fac * 1024.0
+        wb = wk / w_fac * 1024.0
+        rec["kernels"][k] = {"fetch_kib_raw": fk, "write_kib_raw": wk, "read_bytes": rb,
+                             "write_bytes": wb, "hbm_bytes_per_launch": rb + wb}
+    out = os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
+    with open(out, "w") as f:
+        json.dump(rec, f, indent=1)
+    log(f"[pmc] wrote {out}")
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="train_w14")
+    ap.add_argument("--rotate", type=int, default=4, help="independent batches cycled per step")
+    ap.add_argument("--no-cpu-baseline", dest="cpu_baseline", action="store_false")
+    ap.add_argument("--cpu-budget", type=float, default=10.0, help="seconds of oracle CPU work")
+    ap.add_argument("--copy-calibration", action="store_true")
+    ap.add_argument("--summarize-pmc", nargs=4, metavar=("FETCH", "WRITE", "COPY_FETCH", "COPY_WRITE"))
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py: this build measures one GPU only; multi-GPU runs are not part of it "
+              f"(asked for --gpus {args.gpus}, WORLD_SIZE={world}).", file=sys.stderr)
+        sys.exit(2)
+    if args.summarize_pmc:
+        summarize_pmc(args.workload, *args.summarize_pmc)
+        return
+    if args.copy_calibration:
+        copy_calibration()
+        return
+    line = run(args)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()
