@@ -315,10 +315,13 @@ bool backward_plan_ok(const BwdRequest& r) {
 size_t backward_workspace(const BwdRequest& r) {
   Geo g;
   if (!plan_bwd(g, r)) return 0;
-  return bwd_ws_layout(g, r).total;
+  const size_t generic = bwd_ws_layout(g, r).total;
+  const size_t fast = fast_backward_workspace(r);
+  return generic > fast ? generic : fast;
 }
 
 hipError_t launch_backward(const BwdRequest& r, hipStream_t st) {
+  if (fast_backward_ok(r)) return launch_backward_fast(r, st);
   BwdArgs a{};
   if (!plan_bwd(a.g, r)) return hipErrorInvalidValue;
   const BwdWs wl = bwd_ws_layout(a.g, r);

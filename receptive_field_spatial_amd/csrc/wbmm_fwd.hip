@@ -146,6 +146,7 @@ size_t forward_workspace(const FwdRequest& r) {
 }
 
 hipError_t launch_forward(const FwdRequest& r, hipStream_t st) {
+  if (fast_forward_ok(r)) return launch_forward_fast(r, st);
   FwdArgs a{};
   if (!plan_fwd(a.g, r)) return hipErrorInvalidValue;
   a.x = r.x;

@@ -49,6 +49,13 @@ bool backward_plan_ok(const BwdRequest& r);
 size_t backward_workspace(const BwdRequest& r);
 hipError_t launch_backward(const BwdRequest& r, hipStream_t st);
 
+// Fast fp32 paths for w in {7, 14} when whole images fit one wave's 16 windows.
+bool fast_forward_ok(const FwdRequest& r);
+hipError_t launch_forward_fast(const FwdRequest& r, hipStream_t st);
+bool fast_backward_ok(const BwdRequest& r);
+size_t fast_backward_workspace(const BwdRequest& r);
+hipError_t launch_backward_fast(const BwdRequest& r, hipStream_t st);
+
 // 3x3 depthwise mix kernels (used by the window-mode paths).
 hipError_t launch_mix_fwd(const float* z, const float* w9, void* y, int out_bf16, int B, int C,
                           int H, int W, int layout, hipStream_t st);
