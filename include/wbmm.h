@@ -10,7 +10,7 @@
  *   - Index orientation: M_c[i][j] = T_c[(y_i - y_j) + w - 1][(x_i - x_j) + w - 1], in-window
  *     position i = y_i * w + x_i (row-major); the table's first axis is vertical.
  *   - Every pointer argument named as device memory must be a device (HBM) address on the current
- *     HIP device, 16-byte aligned. Host pointers are never dereferenced except where stated.
+ *     HIP device, aligned to its element size (workspaces: see each call).
  *   - The caller owns every buffer. The library never allocates or frees device memory and never
  *     synchronizes: all work is enqueued on `stream` (a hipStream_t passed as void*; NULL = the
  *     default stream) and runs asynchronously.
@@ -127,8 +127,8 @@ wbmm_status wbmm_forward(int B, int C, int H, int W, int w, int layout, int in_d
                          size_t workspace_bytes, void* stream);
 
 /*
- * wbmm_backward_workspace_bytes — device workspace wbmm_backward needs (fp64 partial tables and
- * arrival counters). Returns 0 for invalid arguments.
+ * wbmm_backward_workspace_bytes — device workspace wbmm_backward needs (per-workgroup fp64
+ * partial tables, and a dz buffer when the mix cannot be fused). Returns 0 for invalid arguments.
  */
 size_t wbmm_backward_workspace_bytes(int B, int C, int H, int W, int w, int layout, int has_mix);
 
@@ -147,10 +147,10 @@ size_t wbmm_backward_workspace_bytes(int B, int C, int H, int W, int w, int layo
  * dT:      device fp32 [C][2w-1][2w-1], written, or NULL to skip.
  * dmix_w:  device fp32 [C][3][3], written, or NULL to skip (ignored without mix_w).
  * workspace / workspace_bytes: device scratch of at least wbmm_backward_workspace_bytes(...)
- *          bytes. Its first use must see it zero-filled; every call that completes leaves it
- *          ready for the next one. Calls that share a workspace must be ordered on one stream.
- * dT and dmix_w are reduced in a fixed order (no floating-point atomics): results are
- * bitwise reproducible run to run.
+ *          bytes, 256-byte aligned; no initial contents are required. Calls that share a
+ *          workspace must be ordered on one stream.
+ * dT and dmix_w are reduced in a fixed order (fp64 per-workgroup partials summed by a second,
+ * small kernel; no floating-point atomics): results are bitwise reproducible run to run.
  * This build supports the backward for 1 <= w <= 16.
  * Errors: WBMM_E_INVALID, WBMM_E_UNSUPPORTED (w > 16, misaligned pointer), WBMM_E_WORKSPACE,
  *         WBMM_E_HIP.
@@ -159,6 +159,15 @@ wbmm_status wbmm_backward(int B, int C, int H, int W, int w, int layout, const f
                           const float* T, const float* M, const float* mix_w,
                           const float* z_saved, const float* dy, float* dx, float* dT,
                           float* dmix_w, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * wbmm_set_launch_events — measurement aid, not part of the method. The next wbmm_forward or
+ * wbmm_backward call made on the calling thread records `before` (a hipEvent_t passed as void*)
+ * on its stream immediately before launching its main contraction kernel and `after`
+ * immediately after it; the pair is then cleared. Both NULL clears a pending pair. The caller
+ * owns the events. Errors: WBMM_E_INVALID when exactly one of the two is NULL.
+ */
+wbmm_status wbmm_set_launch_events(void* before, void* after);
 
 #ifdef __cplusplus
 }

@@ -16,7 +16,7 @@ __all__ = [
     "WbmmError", "lib_path", "load_library", "abi_version",
     "wbmm_build_index", "wbmm_build_matrix", "wbmm_fold_hier",
     "wbmm_forward", "wbmm_forward_workspace_bytes",
-    "wbmm_backward", "wbmm_backward_workspace_bytes",
+    "wbmm_backward", "wbmm_backward_workspace_bytes", "wbmm_set_launch_events",
     "WBMM_OK", "WBMM_E_INVALID", "WBMM_E_UNSUPPORTED", "WBMM_E_WORKSPACE", "WBMM_E_HIP",
 ]
 
@@ -51,6 +51,7 @@ def _declare(lib):
         "wbmm_forward": (c_int, [c_int] * 8 + [vp] * 7 + [c_size, vp]),
         "wbmm_backward_workspace_bytes": (c_size, [c_int] * 7),
         "wbmm_backward": (c_int, [c_int] * 6 + [vp] * 10 + [c_size, vp]),
+        "wbmm_set_launch_events": (c_int, [vp, vp]),
     }
     for name, (res, args) in sigs.items():
         fn = getattr(lib, name)
@@ -200,8 +201,7 @@ def wbmm_backward(x, dy, w: int, T=None, M=None, mix_w=None, z_saved=None, *, la
                   dx=True, dT=True, dmix_w=True, workspace=None, stream=None):
     """Layer backward (fp32). Returns (dx, dT, dmix_w); an output passed as False is skipped.
 
-    ``workspace`` (uint8, at least wbmm_backward_workspace_bytes) must be zero-filled before its
-    first use; a fresh zeroed one is made when None.
+    ``workspace`` (uint8, at least wbmm_backward_workspace_bytes); one is allocated when None.
     """
     torch = _torch()
     B, C, H, W = _bchw(x, layout)
@@ -215,9 +215,14 @@ def wbmm_backward(x, dy, w: int, T=None, M=None, mix_w=None, z_saved=None, *, la
         dW_t = torch.empty((C, 3, 3), dtype=torch.float32, device=dev) if dmix_w is True else (dmix_w if dmix_w is not False else None)
     need = wbmm_backward_workspace_bytes(B, C, H, W, w, layout, mix_w is not None)
     if need and (workspace is None or workspace.numel() * workspace.element_size() < need):
-        workspace = torch.zeros(need, dtype=torch.uint8, device=dev)
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(_lib().wbmm_backward(B, C, H, W, int(w), _layout_code(layout), _ptr(x), _ptr(T), _ptr(M),
                                 _ptr(mix_w), _ptr(z_saved), _ptr(dy), _ptr(dx_t), _ptr(dT_t),
                                 _ptr(dW_t), _ptr(workspace), ws_bytes, _stream(stream)))
     return dx_t, dT_t, dW_t
+
+
+def wbmm_set_launch_events(before, after):
+    """Bracket the next forward/backward call's main kernel with two HIP events (raw handles)."""
+    _check(_lib().wbmm_set_launch_events(before, after))

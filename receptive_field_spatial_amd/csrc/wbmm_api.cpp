@@ -15,6 +15,7 @@
 namespace {
 
 thread_local std::string g_err;
+thread_local hipEvent_t g_ev_before = nullptr, g_ev_after = nullptr;
 
 wbmm_status fail(wbmm_status st, const char* fmt, ...) {
   char buf[512];
@@ -69,7 +70,26 @@ wbmm_status check_map(int B, int C, int H, int W, int w, int layout) {
 
 }  // namespace
 
+namespace wbmm {
+void mark_main_kernel(hipStream_t st, bool before) {
+  if (before) {
+    if (g_ev_before) (void)hipEventRecord(g_ev_before, st);
+  } else if (g_ev_after) {
+    (void)hipEventRecord(g_ev_after, st);
+    g_ev_before = g_ev_after = nullptr;  // one call only
+  }
+}
+}  // namespace wbmm
+
 WBMM_API int wbmm_abi_version(void) { return WBMM_ABI_VERSION; }
+
+WBMM_API wbmm_status wbmm_set_launch_events(void* before, void* after) {
+  if ((before == nullptr) != (after == nullptr))
+    return fail(WBMM_E_INVALID, "give both events or neither");
+  g_ev_before = (hipEvent_t)before;
+  g_ev_after = (hipEvent_t)after;
+  return ok();
+}
 
 WBMM_API const char* wbmm_last_error(void) { return g_err.c_str(); }
 

@@ -227,6 +227,35 @@ __global__ void __launch_bounds__(kThreads) k_mix_bwd_weight(const float* __rest
   if (threadIdx.x < 9) dw9[c * 9 + threadIdx.x] = (float)red[threadIdx.x][0];
 }
 
+// dT[c][q] = sum over workgroups k (in order) of partT[c][k][q]; the same for the 9 dWmix values.
+__global__ void __launch_bounds__(kThreads) k_bwd_reduce(const double* __restrict__ partT,
+                                                         const double* __restrict__ partW,
+                                                         int parts, int L, float* __restrict__ dT,
+                                                         float* __restrict__ dmixw) {
+  const int c = blockIdx.x;
+  if (dT) {
+    for (int q = threadIdx.x; q < L; q += kThreads) {
+      const double* p = partT + (size_t)c * parts * L + q;
+      double s = 0.0;
+      for (int k = 0; k < parts; ++k) s += p[(size_t)k * L];
+      dT[(size_t)c * L + q] = (float)s;
+    }
+  }
+  if (dmixw && threadIdx.x < 9) {
+    const double* p = partW + (size_t)c * parts * 9 + threadIdx.x;
+    double s = 0.0;
+    for (int k = 0; k < parts; ++k) s += p[(size_t)k * 9];
+    dmixw[c * 9 + threadIdx.x] = (float)s;
+  }
+}
+
+hipError_t launch_bwd_reduce(const double* partT, const double* partW, int parts, int C, int L,
+                             float* dT, float* dmixw, hipStream_t st) {
+  hipLaunchKernelGGL(k_bwd_reduce, dim3(C), dim3(kThreads), 0, st, partT, partW, parts, L, dT,
+                     dmixw);
+  return hipGetLastError();
+}
+
 hipError_t launch_mix_fwd(const float* z, const float* w9, void* y, int out_bf16, int B, int C,
                           int H, int W, int layout, hipStream_t st) {
   const size_t n = (size_t)B * C * H * W;

@@ -6,8 +6,8 @@
 // contraction with the transposed table lookup, and dT is a row-pair MFMA contraction
 //   acc_dy[x1][x2] = sum_{windows n} sum_{y1 - y2 = dy} G_n[y1][x1] * X_n[y2][x2]
 // whose diagonals x1 - x2 = dx give dT[dy][dx]. fp32 MFMA chains over 4 windows are promoted to
-// fp64; per-workgroup partials are summed in a fixed order by the last workgroup of each channel
-// to arrive (no floating-point atomics), so dT and dWmix are bitwise reproducible.
+// fp64; per-workgroup fp64 partials are summed in a fixed order by a small second kernel (no
+// floating-point atomics, no cross-workgroup fences), so dT and dWmix are bitwise reproducible.
 #include "wbmm_core.hpp"
 #include "wbmm_launch.hpp"
 
@@ -26,7 +26,6 @@ struct BwdArgs {
   float* dmixw;
   double* partT;        // [C][col_groups][L]
   double* partW;        // [C][col_groups][9]
-  unsigned* counters;   // [C], zero between calls
   int mix_here, want_dx, want_dT, want_dW;
 };
 
@@ -42,7 +41,6 @@ template <int RPW, int ASRC>
 __global__ void __launch_bounds__(kThreads) k_wbmm_bwd(BwdArgs a) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   __shared__ double s_wred[4][9];
-  __shared__ int s_last;
   const Geo& g = a.g;
   const int c = blockIdx.y;
   const int colgrp = blockIdx.x;
@@ -228,34 +226,6 @@ __global__ void __launch_bounds__(kThreads) k_wbmm_bwd(BwdArgs a) {
     }
   }
 
-  // ---------------------------------------------------------------- last arrival reduces
-  if (a.want_dT || a.want_dW) {
-    __threadfence();
-    __syncthreads();
-    if (threadIdx.x == 0) {
-      const unsigned prev = atomicAdd(&a.counters[c], 1u);
-      s_last = prev == (unsigned)(g.col_groups - 1);
-    }
-    __syncthreads();
-    if (s_last) {
-      __threadfence();
-      if (a.want_dT) {
-        for (int q = threadIdx.x; q < g.L; q += kThreads) {
-          const double* p = a.partT + (size_t)c * g.col_groups * g.L + q;
-          double s = 0.0;
-          for (int k = 0; k < g.col_groups; ++k) s += __builtin_nontemporal_load(p + (size_t)k * g.L);
-          a.dT[(size_t)c * g.L + q] = (float)s;
-        }
-      }
-      if (a.want_dW && threadIdx.x < 9) {
-        const double* p = a.partW + (size_t)c * g.col_groups * 9 + threadIdx.x;
-        double s = 0.0;
-        for (int k = 0; k < g.col_groups; ++k) s += __builtin_nontemporal_load(p + (size_t)k * 9);
-        a.dmixw[c * 9 + threadIdx.x] = (float)s;
-      }
-      if (threadIdx.x == 0) a.counters[c] = 0u;
-    }
-  }
 }
 
 // ---------------------------------------------------------------------------- dispatch
@@ -265,8 +235,11 @@ static hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t st) {
   hipError_t e = hipFuncSetAttribute((const void*)fn, hipFuncAttributeMaxDynamicSharedMemorySize,
                                      a.g.lds_total);
   if (e != hipSuccess) return e;
+  mark_main_kernel(st, true);
   hipLaunchKernelGGL(fn, dim3(a.g.col_groups, a.g.C, 1), dim3(kThreads), a.g.lds_total, st, a);
-  return hipGetLastError();
+  e = hipGetLastError();
+  mark_main_kernel(st, false);
+  return e;
 }
 
 template <int ASRC>
@@ -292,13 +265,12 @@ static bool plan_bwd(Geo& g, const BwdRequest& r) {
 
 namespace {
 struct BwdWs {
-  size_t counters, partT, partW, dz, total;
+  size_t partT, partW, dz, total;
 };
 BwdWs bwd_ws_layout(const Geo& g, const BwdRequest& r) {
   auto al = [](size_t v) { return (v + 255) / 256 * 256; };
   BwdWs w{};
-  w.counters = 0;
-  w.partT = al((size_t)g.C * sizeof(unsigned));
+  w.partT = 0;
   w.partW = w.partT + al((size_t)g.C * g.col_groups * g.L * sizeof(double));
   w.dz = w.partW + al((size_t)g.C * g.col_groups * 9 * sizeof(double));
   const bool need_dz = r.mixw && !g.image_mode;
@@ -334,7 +306,6 @@ hipError_t launch_backward(const BwdRequest& r, hipStream_t st) {
   a.dx = r.dx;
   a.dT = r.dT;
   a.dmixw = r.dmixw;
-  a.counters = (unsigned*)(ws + wl.counters);
   a.partT = (double*)(ws + wl.partT);
   a.partW = (double*)(ws + wl.partW);
   a.want_dx = r.dx != nullptr;
@@ -358,7 +329,10 @@ hipError_t launch_backward(const BwdRequest& r, hipStream_t st) {
     a.want_dW = (mix && r.dmixw) ? 1 : 0;
   }
   if (!a.want_dx && !a.want_dT && !a.want_dW) return hipSuccess;
-  return r.M ? launch_bwd_tiles<1>(a, st) : launch_bwd_tiles<0>(a, st);
+  e = r.M ? launch_bwd_tiles<1>(a, st) : launch_bwd_tiles<0>(a, st);
+  if (e != hipSuccess || (!a.want_dT && !a.want_dW)) return e;
+  return launch_bwd_reduce(a.partT, a.want_dW ? a.partW : nullptr, a.g.col_groups, r.C, a.g.L,
+                           a.want_dT ? r.dT : nullptr, a.want_dW ? r.dmixw : nullptr, st);
 }
 
 }  // namespace wbmm

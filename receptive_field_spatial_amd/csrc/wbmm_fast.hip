@@ -33,7 +33,6 @@ struct FastArgs {
   float* dmixw;
   double* partT;
   double* partW;
-  unsigned* counters;
   int want_dx, want_dT, want_dW;
 };
 
@@ -47,7 +46,8 @@ struct Shape {
   static constexpr int L1 = 2 * WS - 1;
   static constexpr int L = L1 * L1;
   static constexpr int C0 = 2 * WS * (WS - 1); // table index of offset (0,0) relative shift
-  static constexpr int TSZ = (L + 3) / 4 * 4;
+  static constexpr int XP = (D + 15) / 32 * 32 + 16;  // X-chunk window pitch: lane groups on disjoint banks
+  static constexpr int TSZ = ((L + 3) / 4 * 4) > 4 * XP ? ((L + 3) / 4 * 4) : 4 * XP;  // table, later X chunks
   static constexpr int NWY = IH / WS, NWX = IW / WS, NWIN = NWY * NWX;
   static constexpr int IPW = 16 / NWIN;        // images per wave
   static constexpr int WPITCH = D;             // floats per window in LDS
@@ -268,73 +268,42 @@ __device__ constexpr bool slot_valid(int j) {
   return 4 * j + ((j & 1) ? 3 - Q : Q) < 2 * WS - 1;
 }
 
-// Row-pair contraction over all 64 windows of the workgroup:
-//   acc_j[x1][x2] += sum_n sum_{y1 - y2 = dy_j} G_n[y1][x1] * X_n[y2][x2]
-// G rows from the LDS regions (any wave's), X rows straight from memory, one chunk ahead.
-// Lanes with x1 or x2 >= WS produce rows/columns of acc that are never read.
+// Row-pair contraction for the table gradient, one chunk of 4 windows (MFMA K = window):
+//   acc_j[x1][x2] += sum_{y1 - y2 = dy_j} G_n[y1][x1] * X_n[y2][x2]
+// G rows from the LDS regions (any wave's), X rows from the workgroup's LDS chunk buffer (4
+// windows at pitch XP). Lanes with x1 or x2 >= WS produce rows/columns of acc never read.
 template <class S, int Q>
-__device__ __forceinline__ void dt_wave(const float* regions, const float* __restrict__ x, int B,
-                                        int C, int c, int wg_img0, int lane,
-                                        double (&acc64)[8][4]) {
+__device__ __forceinline__ void dt_chunk(const float* regions, const float* xbuf, int n0, int kn,
+                                         int xc, v4f (&a32)[8], double (&acc64)[8][4],
+                                         bool flush) {
   constexpr int WS = S::WS;
-  const int x1 = lane & 15, kn = lane >> 4;
-  const int xc = x1 < WS ? x1 : WS - 1;
-  auto xrow = [&](int n0, bool& ok) -> const float* {
-    const int n = n0 + kn;
-    const int q = n >> 4, nl = n & 15;
-    const int im = nl / S::NWIN, wi = nl % S::NWIN;
-    const int b = wg_img0 + q * S::IPW + im;
-    ok = b < B;
-    const int wy = wi / S::NWX, wx = wi % S::NWX;
-    return x + ((size_t)(ok ? b : 0) * C + c) * S::PLANE + wy * WS * S::IW + wx * WS + xc;
-  };
-  float Bv[WS], Bn[WS], Av[WS];
-  {
-    bool ok;
-    const float* p = xrow(0, ok);
+  const int n = n0 + kn;
+  const float* g = regions + (n >> 4) * S::RSZ + (n & 15) * S::WPITCH + xc;
+  const float* xb = xbuf + kn * S::XP + xc;
+  float Av[WS], Bv[WS];
 #pragma unroll
-    for (int y2 = 0; y2 < WS; ++y2) Bv[y2] = ok ? p[y2 * S::IW] : 0.f;
+  for (int y = 0; y < WS; ++y) {
+    Av[y] = g[y * WS];
+    Bv[y] = xb[y * WS];
   }
-  v4f a32[8];
 #pragma unroll
-  for (int j = 0; j < 8; ++j) a32[j] = v4f{0.f, 0.f, 0.f, 0.f};
-  for (int n0 = 0; n0 < 64; n0 += 4) {
-    if (n0 + 4 < 64) {
-      bool ok;
-      const float* p = xrow(n0 + 4, ok);
-#pragma unroll
-      for (int y2 = 0; y2 < WS; ++y2) Bn[y2] = ok ? p[y2 * S::IW] : 0.f;
-    }
-    {
-      const int n = n0 + kn;
-      const float* g = regions + (n >> 4) * S::RSZ + (n & 15) * S::WPITCH + xc;
-#pragma unroll
-      for (int y1 = 0; y1 < WS; ++y1) Av[y1] = g[y1 * WS];
-    }
-#pragma unroll
-    for (int y1 = 0; y1 < WS; ++y1) {
+  for (int y1 = 0; y1 < WS; ++y1) {
 #define WBMM_DT_STEP(J)                                                             \
   if constexpr (Slot<WS, Q, J>::valid) {                                            \
     const int y2 = y1 - Slot<WS, Q, J>::dy;                                         \
     if (y2 >= 0 && y2 < WS) a32[J] = mfma_f32(Av[y1], Bv[y2 < 0 ? 0 : (y2 < WS ? y2 : WS - 1)], a32[J]); \
   }
-      WBMM_DT_STEP(0) WBMM_DT_STEP(1) WBMM_DT_STEP(2) WBMM_DT_STEP(3)
-      WBMM_DT_STEP(4) WBMM_DT_STEP(5) WBMM_DT_STEP(6) WBMM_DT_STEP(7)
+    WBMM_DT_STEP(0) WBMM_DT_STEP(1) WBMM_DT_STEP(2) WBMM_DT_STEP(3)
+    WBMM_DT_STEP(4) WBMM_DT_STEP(5) WBMM_DT_STEP(6) WBMM_DT_STEP(7)
 #undef WBMM_DT_STEP
-    }
-    // promote the fp32 chains to fp64 every 8 windows
-    if ((n0 & 7) == 4) {
+  }
+  if (flush) {  // promote the fp32 chains to fp64
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        if (!slot_valid<WS, Q>(j)) continue;
+    for (int j = 0; j < 8; ++j) {
+      if (!slot_valid<WS, Q>(j)) continue;
 #pragma unroll
-        for (int r = 0; r < 4; ++r) acc64[j][r] += (double)a32[j][r];
-        a32[j] = v4f{0.f, 0.f, 0.f, 0.f};
-      }
-    }
-    if (n0 + 4 < 64) {
-#pragma unroll
-      for (int y2 = 0; y2 < WS; ++y2) Bv[y2] = Bn[y2];
+      for (int r = 0; r < 4; ++r) acc64[j][r] += (double)a32[j][r];
+      a32[j] = v4f{0.f, 0.f, 0.f, 0.f};
     }
   }
 }
@@ -368,7 +337,6 @@ template <class S>
 __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3, 8))) k_bwd_fast(FastArgs a) {
   extern __shared__ __attribute__((aligned(16))) float smem_f[];
   __shared__ double s_wred[4][9];
-  __shared__ int s_last;
   const int c = blockIdx.y, wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   float* Ts = smem_f;
   float* regions = smem_f + S::TSZ;
@@ -384,43 +352,71 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3
 
   // ---- G = partition(dz) in place; dz = mix adjoint of dy (correlation with rot180(W)).
   //      dWmix[u][t] = sum z[p][q] dy[p-u+1][q-t+1]: the same 3x3 dy window, times z.
+  //      A sliding 3x3 register window walks each image column; the column's z values are
+  //      loaded up front. Row h of dy is overwritten by G only after its last read.
   if (mix) {
     float w9[9];
 #pragma unroll
-    for (int q = 0; q < 9; ++q) w9[q] = a.mixw[c * 9 + q];
+    for (int q = 0; q < 9; ++q) w9[q] = a.mixw[(c * 9) + (8 - q)];  // rot180: W[2-u][2-t]
+    const bool wantW = a.want_dW;
     double wacc[9];
 #pragma unroll
     for (int q = 0; q < 9; ++q) wacc[q] = 0.0;
-    const bool wantW = a.want_dW;
-    const float* zsv = a.zsaved;
-    // per pass: fp32 column partials, promoted to fp64 after each column
-    float wcol[9];
 #pragma unroll
-    for (int q = 0; q < 9; ++q) wcol[q] = 0.f;
-    sweep_columns<S>(R, lane, [&](int im, int h, int v, const float (&w)[3][3], float* self) {
-      // w[u][t] = dy(h+u-1, v+t-1); dz(h,v) = sum W[u][t] dy(h-u+1, v-t+1) = sum W[2-u][2-t] w[u][t]
-      float g = 0.f;
-#pragma unroll
-      for (int u = 0; u < 3; ++u)
-#pragma unroll
-        for (int t = 0; t < 3; ++t) g = fmaf(w9[(2 - u) * 3 + (2 - t)], w[u][t], g);
+    for (int c0 = 0; c0 < S::COLS; c0 += S::CHUNK_COLS) {
+      const bool active = lane < S::CHUNK_COLS && c0 + lane < S::COLS;
+      const int col = active ? c0 + lane : c0;
+      const int im = col / S::IW, v = col % S::IW;
       const int b = img0 + im;
-      *self = b < B ? g : 0.f;
-      if (wantW && b < B) {
-        const float z = zsv[((size_t)b * C + c) * S::PLANE + h * S::IW + v];
+      const bool real = active && b < B;
+      const bool hasL = v > 0, hasR = v + 1 < S::IW;
+      float* pc = R + col_part<S>(im, v);
+      const float* pl = R + col_part<S>(im, hasL ? v - 1 : v);
+      const float* pr = R + col_part<S>(im, hasR ? v + 1 : v);
+      float zc[S::IH];
+      if (wantW) {
+        const float* zp = a.zsaved + ((size_t)(b < B ? b : B - 1) * C + c) * S::PLANE + v;
 #pragma unroll
-        for (int u = 0; u < 3; ++u)
-#pragma unroll
-          for (int t = 0; t < 3; ++t) wcol[u * 3 + t] = fmaf(z, w[2 - u][2 - t], wcol[u * 3 + t]);
+        for (int h = 0; h < S::IH; ++h) zc[h] = zp[h * S::IW];
       }
-      if (h == S::IH - 1) {
+      float wcol[9];
 #pragma unroll
-        for (int q = 0; q < 9; ++q) {
-          wacc[q] += (double)wcol[q];
-          wcol[q] = 0.f;
+      for (int q = 0; q < 9; ++q) wcol[q] = 0.f;
+      float w[3][3];
+#pragma unroll
+      for (int t = 0; t < 3; ++t) w[0][t] = 0.f;
+      w[1][0] = hasL ? pl[row_part<S>(0)] : 0.f;
+      w[1][1] = pc[row_part<S>(0)];
+      w[1][2] = hasR ? pr[row_part<S>(0)] : 0.f;
+#pragma unroll
+      for (int h = 0; h < S::IH; ++h) {
+        if (h + 1 < S::IH) {
+          w[2][0] = hasL ? pl[row_part<S>(h + 1)] : 0.f;
+          w[2][1] = pc[row_part<S>(h + 1)];
+          w[2][2] = hasR ? pr[row_part<S>(h + 1)] : 0.f;
+        } else {
+          w[2][0] = w[2][1] = w[2][2] = 0.f;
+        }
+        // w[u][t] = dy(h+u-1, v+t-1); dz(h,v) = sum_{u,t} W[2-u][2-t] w[u][t]
+        float gsum = 0.f;
+#pragma unroll
+        for (int q = 0; q < 9; ++q) gsum = fmaf(w9[q], w[q / 3][q % 3], gsum);
+        if (real) pc[row_part<S>(h)] = gsum;
+        if (wantW) {
+          const float z = real ? zc[h] : 0.f;
+          // dWmix[u][t] += z * dy(h-u+1, v-t+1) = z * w[2-u][2-t]
+#pragma unroll
+          for (int q = 0; q < 9; ++q) wcol[q] = fmaf(z, w[2 - q / 3][2 - q % 3], wcol[q]);
+        }
+#pragma unroll
+        for (int t = 0; t < 3; ++t) {
+          w[0][t] = w[1][t];
+          w[1][t] = w[2][t];
         }
       }
-    });
+#pragma unroll
+      for (int q = 0; q < 9; ++q) wacc[q] += (double)wcol[q];
+    }
     if (wantW) {
 #pragma unroll
       for (int q = 0; q < 9; ++q) {
@@ -460,21 +456,65 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3
     }
   }
 
-  // ---- table gradient partial over the workgroup's 64 windows
+  // ---- table gradient partial over the workgroup's 64 windows. X comes in chunks of 4 windows
+  //      through the (now free) table region; the next chunk's global loads are in flight in
+  //      registers while the current one is contracted.
   if (a.want_dT) {
     double acc64[8][4];
 #pragma unroll
     for (int j = 0; j < 8; ++j)
 #pragma unroll
       for (int r = 0; r < 4; ++r) acc64[j][r] = 0.0;
-    switch (wave) {
-      case 0: dt_wave<S, 0>(regions, a.x, B, C, c, wg_img0, lane, acc64); break;
-      case 1: dt_wave<S, 1>(regions, a.x, B, C, c, wg_img0, lane, acc64); break;
-      case 2: dt_wave<S, 2>(regions, a.x, B, C, c, wg_img0, lane, acc64); break;
-      default: dt_wave<S, 3>(regions, a.x, B, C, c, wg_img0, lane, acc64); break;
+    v4f a32[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) a32[j] = v4f{0.f, 0.f, 0.f, 0.f};
+    constexpr int CH_E = 4 * S::D;
+    constexpr int EPT = (CH_E + kThreads - 1) / kThreads;
+    int goff[EPT], loff[EPT], ekn[EPT];
+#pragma unroll
+    for (int j = 0; j < EPT; ++j) {
+      const int e = threadIdx.x + j * kThreads;
+      const int ee = e < CH_E ? e : 0;
+      ekn[j] = ee / S::D;
+      const int p = ee % S::D;
+      goff[j] = (p / S::WS) * S::IW + (p % S::WS);
+      loff[j] = e < CH_E ? ekn[j] * S::XP + p : -1;
+    }
+    float stg[EPT];
+    auto load_chunk = [&](int ci) {
+#pragma unroll
+      for (int j = 0; j < EPT; ++j) {
+        const int n = 4 * ci + ekn[j];
+        const int q = n >> 4, nl = n & 15;
+        const int im = nl / S::NWIN, wi = nl % S::NWIN;
+        int b = wg_img0 + q * S::IPW + im;
+        b = b < B ? b : B - 1;  // windows past the batch have G = 0
+        stg[j] = a.x[((size_t)b * C + c) * S::PLANE + (wi / S::NWX) * S::WS * S::IW +
+                     (wi % S::NWX) * S::WS + goff[j]];
+      }
+    };
+    const int kn = lane >> 4, x1 = lane & 15;
+    const int xc = x1 < S::WS ? x1 : S::WS - 1;
+    float* xbuf = Ts;
+    load_chunk(0);
+    __syncthreads();  // every wave is done with the table (dX)
+    for (int ci = 0; ci < 16; ++ci) {
+      if (ci > 0) __syncthreads();  // chunk ci-1 consumed by every wave
+#pragma unroll
+      for (int j = 0; j < EPT; ++j)
+        if (loff[j] >= 0) xbuf[loff[j]] = stg[j];
+      __syncthreads();
+      if (ci + 1 < 16) load_chunk(ci + 1);
+      const bool flush = (ci & 1) != 0;
+      switch (wave) {
+        case 0: dt_chunk<S, 0>(regions, xbuf, 4 * ci, kn, xc, a32, acc64, flush); break;
+        case 1: dt_chunk<S, 1>(regions, xbuf, 4 * ci, kn, xc, a32, acc64, flush); break;
+        case 2: dt_chunk<S, 2>(regions, xbuf, 4 * ci, kn, xc, a32, acc64, flush); break;
+        default: dt_chunk<S, 3>(regions, xbuf, 4 * ci, kn, xc, a32, acc64, flush); break;
+      }
     }
     double* pT = a.partT + ((size_t)c * a.wgs_per_c + blockIdx.x) * S::L;
-    __syncthreads();  // every wave is done reading the G regions
+    __syncthreads();  // every wave is done reading the G regions and the last chunk
     double* scr = (double*)R;
     switch (wave) {
       case 0: dt_partial_write<S, 0>(scr, acc64, pT, lane); break;
@@ -484,34 +524,6 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3
     }
   }
 
-  // ---- the last workgroup of channel c to arrive sums the partials in a fixed order
-  if (a.want_dT || a.want_dW) {
-    __threadfence();
-    __syncthreads();
-    if (threadIdx.x == 0) {
-      const unsigned prev = atomicAdd(&a.counters[c], 1u);
-      s_last = prev == (unsigned)(a.wgs_per_c - 1);
-    }
-    __syncthreads();
-    if (s_last) {
-      __threadfence();
-      if (a.want_dT) {
-        for (int q = threadIdx.x; q < S::L; q += kThreads) {
-          const double* p = a.partT + (size_t)c * a.wgs_per_c * S::L + q;
-          double s = 0.0;
-          for (int k = 0; k < a.wgs_per_c; ++k) s += __builtin_nontemporal_load(p + (size_t)k * S::L);
-          a.dT[(size_t)c * S::L + q] = (float)s;
-        }
-      }
-      if (a.want_dW && threadIdx.x < 9) {
-        const double* p = a.partW + (size_t)c * a.wgs_per_c * 9 + threadIdx.x;
-        double s = 0.0;
-        for (int k = 0; k < a.wgs_per_c; ++k) s += __builtin_nontemporal_load(p + (size_t)k * 9);
-        a.dmixw[c * 9 + threadIdx.x] = (float)s;
-      }
-      if (threadIdx.x == 0) a.counters[c] = 0u;
-    }
-  }
 }
 
 // ---------------------------------------------------------------------------- dispatch
@@ -540,8 +552,11 @@ hipError_t launch_shape(Fn fn, FastArgs a, hipStream_t st) {
   hipError_t e = hipFuncSetAttribute((const void*)fn, hipFuncAttributeMaxDynamicSharedMemorySize,
                                      lds_bytes<S>());
   if (e != hipSuccess) return e;
+  mark_main_kernel(st, true);
   hipLaunchKernelGGL(fn, dim3(a.wgs_per_c, a.C, 1), dim3(kThreads), lds_bytes<S>(), st, a);
-  return hipGetLastError();
+  e = hipGetLastError();
+  mark_main_kernel(st, false);
+  return e;
 }
 
 using S14 = Shape<14, 14, 14>;
@@ -586,7 +601,7 @@ size_t fast_backward_workspace(const BwdRequest& r) {
   }
   auto al = [](size_t v) { return (v + 255) / 256 * 256; };
   const size_t L = (size_t)(2 * r.w - 1) * (2 * r.w - 1);
-  return al((size_t)r.C * 4) + al((size_t)r.C * wgs * L * 8) + al((size_t)r.C * wgs * 9 * 8);
+  return al((size_t)r.C * wgs * L * 8) + al((size_t)r.C * wgs * 9 * 8);
 }
 
 hipError_t launch_backward_fast(const BwdRequest& r, hipStream_t st) {
@@ -604,9 +619,8 @@ hipError_t launch_backward_fast(const BwdRequest& r, hipStream_t st) {
   auto al = [](size_t v) { return (v + 255) / 256 * 256; };
   const size_t L = (size_t)(2 * r.w - 1) * (2 * r.w - 1);
   unsigned char* ws = (unsigned char*)r.ws;
-  a.counters = (unsigned*)ws;
-  a.partT = (double*)(ws + al((size_t)r.C * 4));
-  a.partW = (double*)(ws + al((size_t)r.C * 4) + al((size_t)r.C * wgs * L * 8));
+  a.partT = (double*)ws;
+  a.partW = (double*)(ws + al((size_t)r.C * wgs * L * 8));
   a.x = r.x;
   a.T = r.T;
   a.mixw = r.mixw;
@@ -618,11 +632,15 @@ hipError_t launch_backward_fast(const BwdRequest& r, hipStream_t st) {
   a.want_dx = r.dx != nullptr;
   a.want_dT = r.dT != nullptr;
   a.want_dW = (r.mixw && r.dmixw) ? 1 : 0;
+  hipError_t e;
   switch (fs) {
-    case FS_14_14_14: return launch_shape<S14>(k_bwd_fast<S14>, a, st);
-    case FS_14_28_28: return launch_shape<S28>(k_bwd_fast<S28>, a, st);
-    default: return launch_shape<S56>(k_bwd_fast<S56>, a, st);
+    case FS_14_14_14: e = launch_shape<S14>(k_bwd_fast<S14>, a, st); break;
+    case FS_14_28_28: e = launch_shape<S28>(k_bwd_fast<S28>, a, st); break;
+    default: e = launch_shape<S56>(k_bwd_fast<S56>, a, st); break;
   }
+  if (e != hipSuccess || (!a.want_dT && !a.want_dW)) return e;
+  return launch_bwd_reduce(a.partT, a.want_dW ? a.partW : nullptr, wgs, r.C, (int)L,
+                           a.want_dT ? r.dT : nullptr, a.want_dW ? r.dmixw : nullptr, st);
 }
 
 }  // namespace wbmm

@@ -56,6 +56,14 @@ bool fast_backward_ok(const BwdRequest& r);
 size_t fast_backward_workspace(const BwdRequest& r);
 hipError_t launch_backward_fast(const BwdRequest& r, hipStream_t st);
 
+// Fixed-order sum of per-workgroup fp64 partials: dT[c][q] = sum_k partT[c][k][q] (and dWmix).
+hipError_t launch_bwd_reduce(const double* partT, const double* partW, int parts, int C, int L,
+                             float* dT, float* dmixw, hipStream_t st);
+
+// Records the caller's timing events (if any were set for this thread) right before (before =
+// true) or right after the launch of a call's main contraction kernel.
+void mark_main_kernel(hipStream_t st, bool before);
+
 // 3x3 depthwise mix kernels (used by the window-mode paths).
 hipError_t launch_mix_fwd(const float* z, const float* w9, void* y, int out_bf16, int B, int C,
                           int H, int W, int layout, hipStream_t st);
