@@ -3,8 +3,9 @@
 
 A step is one pass of the whole hot path over one synthetic batch of the training workload
 (B=64, C=192, 28x28, w=14, 3x3 inter-block mix): the fused forward kernel (partition, M_c formed
-on chip from the table, MFMA contraction, reverse, mix, saved pre-mix map) and the fused backward
-kernel (mix adjoint, dX = M^T G, row-pair MFMA table gradient, dWmix, fixed-order reduction).
+on chip from the table, MFMA contraction, reverse, mix, saved pre-mix map), the fused backward
+kernel (mix adjoint, dX = M^T G, row-pair MFMA table gradient, dWmix partials) and the small
+fixed-order reduction kernel that finishes dT and dWmix.
 
 Prints ONE JSON line on stdout; diagnostics go to stderr.
 
@@ -121,6 +122,33 @@ def load_traffic(workload: str, kernel: str):
     return None if k is None else k.get("hbm_bytes_per_launch")
 
 
+# ----------------------------------------------------------------------------- HIP events
+class HipEvents:
+    """Raw hipEvent_t handles (the library records them around its main kernel launch)."""
+
+    def __init__(self):
+        import ctypes
+        self.ct = ctypes
+        self.hip = ctypes.CDLL("libamdhip64.so")
+        self.hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
+                                                 ctypes.c_void_p]
+
+    def create(self):
+        ev = self.ct.c_void_p()
+        if self.hip.hipEventCreate(self.ct.byref(ev)) != 0:
+            raise RuntimeError("hipEventCreate failed")
+        return ev.value
+
+    def elapsed_ms(self, a, b):
+        ms = self.ct.c_float()
+        if self.hip.hipEventElapsedTime(self.ct.byref(ms), self.ct.c_void_p(a), self.ct.c_void_p(b)) != 0:
+            raise RuntimeError("hipEventElapsedTime failed")
+        return ms.value
+
+    def destroy(self, ev):
+        self.hip.hipEventDestroy(self.ct.c_void_p(ev))
+
+
 # ----------------------------------------------------------------------------- GPU run
 def run(args):
     import numpy as np
@@ -187,7 +215,8 @@ def run(args):
     torch.cuda.synchronize()
 
     K = args.steps
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(K)]
+    hev = HipEvents()
+    kev = [[hev.create() for _ in range(4)] for _ in range(K)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     start = torch.cuda.Event(enable_timing=True)
@@ -195,22 +224,25 @@ def run(args):
     start.record(stream)
     for i in range(K):
         s = sets[i % nsets]
-        ev[i][0].record(stream)
+        R.wbmm_set_launch_events(kev[i][0], kev[i][1])
         fwd(s)
-        ev[i][1].record(stream)
         if wl.backward:
+            R.wbmm_set_launch_events(kev[i][2], kev[i][3])
             bwd(s)
-        ev[i][2].record(stream)
     stop.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     total_ms = start.elapsed_time(stop)
     ms_step = total_ms / K
-    fwd_ms = [e[0].elapsed_time(e[1]) for e in ev]
-    bwd_ms = [e[1].elapsed_time(e[2]) for e in ev] if wl.backward else []
+    # main-kernel durations, recorded by the library right around each launch
+    fwd_ms = [hev.elapsed_ms(e[0], e[1]) for e in kev]
+    bwd_ms = [hev.elapsed_ms(e[2], e[3]) for e in kev] if wl.backward else []
+    for e in kev:
+        for h in e:
+            hev.destroy(h)
     log(f"[bench] {wl.name}: {K} steps in {total_ms:.3f} ms GPU ({wall*1e3:.1f} ms wall); "
-        f"fwd call avg {statistics.mean(fwd_ms)*1e3:.1f} us"
-        + (f", bwd call avg {statistics.mean(bwd_ms)*1e3:.1f} us" if bwd_ms else ""))
+        f"fwd kernel avg {statistics.mean(fwd_ms)*1e3:.1f} us"
+        + (f", bwd kernel avg {statistics.mean(bwd_ms)*1e3:.1f} us" if bwd_ms else ""))
 
     # dominant kernel and its roofline
     fwd_avg = statistics.mean(fwd_ms) / 1e3
