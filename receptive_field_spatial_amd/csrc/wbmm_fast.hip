@@ -2,26 +2,34 @@
 // (multiples of WS) in NCHW, with the images small enough that whole images fill one wave's 16
 // MFMA columns (nWin = (IH/WS)(IW/WS) divides 16).
 //
-// Layout and dataflow (one workgroup = 4 waves = 64 windows of one channel):
-//   * the table T_c sits in LDS once per workgroup; M_c is never formed: each MFMA A operand is
-//     one table entry picked by the pair's relative offset [gecl.asia reading notes, "Core Idea";
-//     the notes' "Limitation"/"Takeaway" name such a non-materializing kernel as future work];
-//   * each wave keeps its 16 windows in its own LDS region, window-major (a window's WS*WS pixels
+// Work is cut into units of 64 windows of one channel (4 wave-units of 16 windows = whole
+// images). One persistent workgroup per CU walks its units in turn with two kinds of waves:
+//   * 4 consumer waves (one per SIMD) run only the MFMA contractions of the current unit;
+//   * 4 producer waves load the next unit (table, image planes -> window-major LDS, and in the
+//     backward the mix adjoint) and run the epilogue (mix, stores) of the previous one,
+// so global traffic and the 3x3 mix overlap the matrix-core work; one barrier per step.
+//
+// Contraction layout:
+//   * the table T_c sits in LDS; M_c is never formed: each MFMA A operand is one table entry
+//     picked by the pair's relative offset [gecl.asia reading notes, "Core Idea"; the notes'
+//     "Limitation"/"Takeaway" name such a non-materializing kernel as future work];
+//   * each wave-unit's 16 windows sit window-major in an LDS region (a window's WS*WS pixels
 //     contiguous, row-major) — one contiguous block per window [pith page, Fig. 2 caption];
 //   * K (the WS*WS pixels of a window) is walked as four (WS/2)x(WS/2) quadrants, one per MFMA
 //     lane group, so for every K-step the table offset splits into a per-lane base plus a
 //     compile-time constant: every A operand is one LDS read with an immediate offset;
-//   * B operands (window pixels) stay in registers for the whole contraction;
 //   * 3x3 mixes walk image columns with a sliding 3x3 register window (3 LDS reads per pixel).
 #include "wbmm_core.hpp"
 #include "wbmm_launch.hpp"
+
+#include <atomic>
 
 namespace wbmm {
 
 struct FastArgs {
   int B, C;
-  int wgs_per_c;
-  const float* x;       // forward: x; backward: x
+  int groups;           // units per channel: ceil(B / images per unit)
+  const float* x;
   const float* T;
   const float* mixw;
   const float* zsaved;  // backward only
@@ -31,10 +39,33 @@ struct FastArgs {
   float* dx;
   float* dT;
   float* dmixw;
-  double* partT;
-  double* partW;
+  double* partT;        // [C * groups][L]: one fp64 table-gradient partial per unit
+  double* partW;        // [C * groups][9]
   int want_dx, want_dT, want_dW;
 };
+
+constexpr int kWsThreads = 12 * 64;  // 8 consumer waves + 4 producer waves
+
+// One unit: 4 wave-units of IPW images each (images uimg0 .. uimg0 + 4*IPW - 1) of channel c.
+// Global addresses are a uniform 64-bit base (the unit's first plane, kept in scalar registers)
+// plus a 32-bit per-lane element offset ir * cp + pixel, ir = image within the unit; the host
+// only takes this path when every such offset fits in an int.
+struct Unit {
+  size_t base;  // element offset of plane (uimg0, c)
+  int c, cp;    // channel; elements between the planes of consecutive images (C * plane)
+  int nimg;     // images of the unit inside the batch (>= 1)
+};
+template <class S>
+__device__ __forceinline__ Unit unit_of(const FastArgs& a, int u) {
+  Unit U;
+  U.c = u / a.groups;
+  const int uimg0 = (u % a.groups) * 4 * S::IPW;
+  U.base = ((size_t)uimg0 * a.C + U.c) * S::PLANE;
+  U.cp = a.C * S::PLANE;
+  const int left = a.B - uimg0;
+  U.nimg = left < 4 * S::IPW ? left : 4 * S::IPW;
+  return U;
+}
 
 template <int WS_, int IH_, int IW_>
 struct Shape {
@@ -46,8 +77,9 @@ struct Shape {
   static constexpr int L1 = 2 * WS - 1;
   static constexpr int L = L1 * L1;
   static constexpr int C0 = 2 * WS * (WS - 1); // table index of offset (0,0) relative shift
+  static constexpr int LP = (L + 3) / 4 * 4;   // padded table size (floats)
   static constexpr int XP = (D + 15) / 32 * 32 + 16;  // X-chunk window pitch: lane groups on disjoint banks
-  static constexpr int TSZ = ((L + 3) / 4 * 4) > 4 * XP ? ((L + 3) / 4 * 4) : 4 * XP;  // table, later X chunks
+  static constexpr int TSZ = LP + 72 > 4 * XP ? LP + 72 : 4 * XP;  // table (+ 36 doubles), later X chunks
   static constexpr int NWY = IH / WS, NWX = IW / WS, NWIN = NWY * NWX;
   static constexpr int IPW = 16 / NWIN;        // images per wave
   static constexpr int WPITCH = D;             // floats per window in LDS
@@ -59,7 +91,15 @@ struct Shape {
   static constexpr int CHUNK_IMGS = IW <= 64 ? (64 / IW < IPW ? 64 / IW : IPW) : 1;
   static constexpr int CHUNK_COLS = CHUNK_IMGS * IW;      // columns per pass (image aligned)
   static_assert(IW <= 64, "image width");
+  static_assert((7 * D + 64) * 2 <= RSZ, "a wave region holds 7 fp64 row-pair tiles + a dump row");
 };
+
+// The lane index, hidden from loop-invariant code motion: per-lane address arithmetic derived
+// from it is redone inside each unit step instead of being held in registers across the loop.
+__device__ __forceinline__ int opaque_lane(int lane) {
+  asm volatile("" : "+v"(lane));
+  return lane;
+}
 
 __device__ __forceinline__ void wave_sync_lds() {
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
@@ -78,28 +118,65 @@ __device__ constexpr int row_part(int h) {
   return (h / S::WS) * S::NWX * S::WPITCH + (h % S::WS) * S::WS;
 }
 
-// Global image planes (NCHW, channel c) of the wave's images -> window-major LDS region.
+// The image planes (NCHW, channel c) of one wave-unit's images, loaded into registers by `issue`
+// (one image column per lane and pass) and scattered window-major into an LDS region by `commit`.
+// Images at or past B read as zero. Splitting the two lets other work run while loads are in
+// flight.
 template <class S>
-__device__ __forceinline__ void load_region(const float* __restrict__ src, int B, int C, int c,
-                                            int img0, float* R, int lane) {
+struct PlaneLoad {
+  static constexpr int NP = (S::COLS + 63) / 64;
+  float v[NP][S::IH];
+  // src: the unit's first plane; ir0: first image of the wave-unit within the unit
+  __device__ __forceinline__ void issue(const float* __restrict__ src, const Unit& U, int ir0,
+                                        int lane) {
 #pragma unroll
-  for (int c0 = 0; c0 < S::COLS; c0 += 64) {
-    const int col = c0 + lane;
-    if (col < S::COLS) {
-      const int im = col / S::IW, v = col % S::IW;
-      const int b = img0 + im;
-      float* dst = R + col_part<S>(im, v);
-      if (b < B) {
-        const float* p = src + ((size_t)b * C + c) * S::PLANE + v;
+    for (int p = 0; p < NP; ++p) {
+      const int col = p * 64 + lane;
+      const int cc = col < S::COLS ? col : S::COLS - 1;
+      const int im = cc / S::IW, vv = cc % S::IW;
+      if (ir0 + im < U.nimg) {
+        const int o = (ir0 + im) * U.cp + vv;
 #pragma unroll
-        for (int h = 0; h < S::IH; ++h) dst[row_part<S>(h)] = p[h * S::IW];
+        for (int h = 0; h < S::IH; ++h) v[p][h] = src[o + h * S::IW];
       } else {
 #pragma unroll
-        for (int h = 0; h < S::IH; ++h) dst[row_part<S>(h)] = 0.f;
+        for (int h = 0; h < S::IH; ++h) v[p][h] = 0.f;
       }
     }
   }
-}
+  __device__ __forceinline__ void commit(float* R, int lane) const {
+#pragma unroll
+    for (int p = 0; p < NP; ++p) {
+      const int col = p * 64 + lane;
+      if (col < S::COLS) {
+        float* dst = R + col_part<S>(col / S::IW, col % S::IW);
+#pragma unroll
+        for (int h = 0; h < S::IH; ++h) dst[row_part<S>(h)] = v[p][h];
+      }
+    }
+  }
+};
+
+// One table (C, L) row into registers (producer threads ptid = 0..255) and then into LDS.
+template <class S>
+struct TableLoad {
+  static constexpr int NT = (S::L + 255) / 256;
+  float v[NT];
+  __device__ __forceinline__ void issue(const float* __restrict__ T, int c, int ptid) {
+#pragma unroll
+    for (int j = 0; j < NT; ++j) {
+      const int q = ptid + 256 * j;
+      v[j] = q < S::L ? T[(size_t)c * S::L + q] : 0.f;
+    }
+  }
+  __device__ __forceinline__ void commit(float* Ts, int ptid) const {
+#pragma unroll
+    for (int j = 0; j < NT; ++j) {
+      const int q = ptid + 256 * j;
+      if (q < S::L) Ts[q] = v[j];
+    }
+  }
+};
 
 // Lane geometry for the MFMA column n = lane % 16 (window n of the wave) and lane group
 // gq = lane / 16 (quadrant (gq >> 1, gq & 1) of the window's pixels).
@@ -122,18 +199,19 @@ __device__ constexpr int kpix(int s) { return (s / S::QW) * S::WS + (s % S::QW);
 template <class S>
 __device__ constexpr int ktab(int s) { return (s / S::QW) * S::L1 + (s % S::QW); }
 
-// acc[t] = sum_s A[16t + lane%16][k(gq, s)] * B[k(gq, s)][n] with A from the table in LDS and B
-// from the wave's region (window n = lane % 16); both are single LDS reads with immediate offsets.
+// acc[t] = sum_s A[16(T0 + t) + lane%16][k(gq, s)] * B[k(gq, s)][n] for the NT row tiles starting
+// at T0, with A from the table in LDS and B from the wave-unit's region (window n = lane % 16);
+// both are single LDS reads with immediate offsets.
 // Non-flipped A entry: base(i) - (qoff + ktab(s)); flipped (M^T): L-1-base(i) + qoff + ktab(s).
-template <class S, bool FLIP>
+template <class S, bool FLIP, int T0, int NT>
 __device__ __forceinline__ void contract(const float* Ts, const float* R, int lane,
-                                         v4f (&acc)[S::RT]) {
+                                         v4f (&acc)[NT]) {
   const LaneGeo<S> lg(lane);
   const float* bsrc = R + lg.qbase();
-  const float* abase[S::RT];
+  const float* abase[NT];
 #pragma unroll
-  for (int t = 0; t < S::RT; ++t) {
-    int i = t * 16 + (lane & 15);
+  for (int t = 0; t < NT; ++t) {
+    int i = (T0 + t) * 16 + (lane & 15);
     if (i > S::D - 1) i = S::D - 1;
     const int base = (i / S::WS) * S::L1 + (i % S::WS) + S::C0;
     // non-flipped address = (base - qoff - CMAX) + (CMAX - ktab(s)), both parts >= 0
@@ -144,61 +222,95 @@ __device__ __forceinline__ void contract(const float* Ts, const float* R, int la
   for (int s = 0; s < S::KQ; ++s) {
     const float bv = bsrc[kpix<S>(s)];
 #pragma unroll
-    for (int t = 0; t < S::RT; ++t) {
+    for (int t = 0; t < NT; ++t) {
       const float av = FLIP ? abase[t][ktab<S>(s)] : abase[t][S::CMAX - ktab<S>(s)];
       acc[t] = mfma_f32(av, bv, acc[t]);
     }
   }
 }
 
-// Accumulators back into the region at the pixel positions they belong to.
-template <class S>
-__device__ __forceinline__ void write_acc(float* R, int lane, const v4f (&acc)[S::RT]) {
+// Accumulators of tiles T0 .. T0+NT-1 back into the region at the pixel positions they belong to.
+template <class S, int T0, int NT>
+__device__ __forceinline__ void write_acc(float* R, int lane, const v4f (&acc)[NT]) {
   float* p = R + (lane & 15) * S::WPITCH + 4 * (lane >> 4);
 #pragma unroll
-  for (int t = 0; t < S::RT; ++t)
+  for (int t = 0; t < NT; ++t)
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       if constexpr (S::D % 16 != 0) {
-        if (t * 16 + 4 * (lane >> 4) + r >= S::D) continue;
+        if ((T0 + t) * 16 + 4 * (lane >> 4) + r >= S::D) continue;
       }
-      p[t * 16 + r] = acc[t][r];
+      p[(T0 + t) * 16 + r] = acc[t][r];
     }
 }
 
-// Walk the wave's image columns; for every pixel call f(h, v_valid, center, 3x3 window w[u][t]
-// = value at (h+u-1, v+t-1), zero outside the image, global element offset within the plane).
-// Columns are processed in image-aligned passes so that neighbour columns are never in another
-// pass. `f` may overwrite the pixel's own LDS slot with `write(value)` (rows above the current
-// one are never read again).
-template <class S, class F>
-__device__ __forceinline__ void sweep_columns(float* R, int lane, F&& f) {
+// One image column of a wave-unit region, as seen by the 3x3 stencils: lane `lane` of pass p owns
+// column col = PW*p + lane (image im, column v); the neighbour columns' LDS bases are clamped to
+// the own column at the image border and the values read there are selected away. A sweep that
+// overwrites its input in place needs image-aligned passes (PW = S::CHUNK_COLS), so that no
+// column's neighbour is rewritten by an earlier pass.
+template <class S, int PW = 64>
+struct Column {
+  static constexpr int NP = (S::COLS + PW - 1) / PW;
+  int im, v;
+  bool active, hasL, hasR;
+  int pc, pl, pr;  // LDS offsets (floats) of row 0 of the column and its neighbours
+  __device__ __forceinline__ Column(int p, int lane) {
+    const int col = p * PW + lane;
+    active = lane < PW && col < S::COLS;
+    const int cc = active ? col : 0;
+    im = cc / S::IW;
+    v = cc % S::IW;
+    hasL = v > 0;
+    hasR = v + 1 < S::IW;
+    pc = col_part<S>(im, v);
+    pl = col_part<S>(im, hasL ? v - 1 : v);
+    pr = col_part<S>(im, hasR ? v + 1 : v);
+  }
+  // 3 values of image row h (zero outside the image)
+  __device__ __forceinline__ void row(const float* R, int h, float (&w)[3]) const {
+    if (h < 0 || h >= S::IH) {
+      w[0] = w[1] = w[2] = 0.f;
+      return;
+    }
+    const float l = R[pl + row_part<S>(h)], c = R[pc + row_part<S>(h)], r = R[pr + row_part<S>(h)];
+    w[0] = hasL ? l : 0.f;
+    w[1] = c;
+    w[2] = hasR ? r : 0.f;
+  }
+};
+
+// Walk one column top to bottom with a sliding 3x3 window w[u][t] = value at (h+u-1, v+t-1),
+// calling f(h, w) for every row. Rows are read from LDS in blocks of RB, the next block's reads in
+// flight while the current one is processed, so LDS latency is paid about once per column. f may
+// overwrite row h of the column in LDS: every read of rows <= h+1 has been issued by then, and
+// later blocks only read rows below.
+template <class S, int RB, class Col, class F>
+__device__ __forceinline__ void sweep_column(const float* R, const Col& col, F&& f) {
+  static_assert(S::IH % RB == 0, "row block");
+  float w[3][3];
+  col.row(R, -1, w[0]);
+  col.row(R, 0, w[1]);
+  float nxt[RB][3];
 #pragma unroll
-  for (int c0 = 0; c0 < S::COLS; c0 += S::CHUNK_COLS) {
-    const bool active = lane < S::CHUNK_COLS && c0 + lane < S::COLS;
-    const int col = active ? c0 + lane : c0;
-    const int im = col / S::IW, v = col % S::IW;
-    const bool hasL = v > 0, hasR = v + 1 < S::IW;
-    float* pc = R + col_part<S>(im, v);
-    const float* pl = R + col_part<S>(im, hasL ? v - 1 : v);
-    const float* pr = R + col_part<S>(im, hasR ? v + 1 : v);
-    float w[3][3];
-    // rows -1 (zero) and 0
+  for (int j = 0; j < RB; ++j) col.row(R, j + 1, nxt[j]);
 #pragma unroll
-    for (int t = 0; t < 3; ++t) w[0][t] = 0.f;
-    w[1][0] = hasL ? pl[row_part<S>(0)] : 0.f;
-    w[1][1] = pc[row_part<S>(0)];
-    w[1][2] = hasR ? pr[row_part<S>(0)] : 0.f;
+  for (int hb = 0; hb < S::IH; hb += RB) {
+    float cur[RB][3];
 #pragma unroll
-    for (int h = 0; h < S::IH; ++h) {
-      if (h + 1 < S::IH) {
-        w[2][0] = hasL ? pl[row_part<S>(h + 1)] : 0.f;
-        w[2][1] = pc[row_part<S>(h + 1)];
-        w[2][2] = hasR ? pr[row_part<S>(h + 1)] : 0.f;
-      } else {
-        w[2][0] = w[2][1] = w[2][2] = 0.f;
-      }
-      if (active) f(im, h, v, w, pc + row_part<S>(h));
+    for (int j = 0; j < RB; ++j)
+#pragma unroll
+      for (int t = 0; t < 3; ++t) cur[j][t] = nxt[j][t];
+    if (hb + RB < S::IH) {
+#pragma unroll
+      for (int j = 0; j < RB; ++j) col.row(R, hb + RB + j + 1, nxt[j]);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int j = 0; j < RB; ++j) {
+#pragma unroll
+      for (int t = 0; t < 3; ++t) w[2][t] = cur[j][t];
+      f(hb + j, w);
 #pragma unroll
       for (int t = 0; t < 3; ++t) {
         w[0][t] = w[1][t];
@@ -209,47 +321,110 @@ __device__ __forceinline__ void sweep_columns(float* R, int lane, F&& f) {
 }
 
 // ---------------------------------------------------------------------------- forward
-template <class S>
-__global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3, 8))) k_fwd_fast(FastArgs a) {
-  extern __shared__ __attribute__((aligned(16))) float smem_f[];
-  const int c = blockIdx.y, wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  float* Ts = smem_f;
-  float* R = smem_f + S::TSZ + wave * S::RSZ;
-  const int img0 = (blockIdx.x * 4 + wave) * S::IPW;
+// 12 waves: 8 consumers (2 per SIMD; consumer c contracts row tiles half c >> 2 of wave-unit
+// c & 3) and 4 producers (wave-unit p). LDS: tables [2][LP] (by step parity) and regions
+// [3][4][RSZ] (unit k in k % 3). Step k:
+//   consumers: contract unit k | barrier | accumulators -> region (z over X) | barrier
+//   producers: issue loads of unit k+1, epilogue (mix, stores) of unit k-1 | barrier |
+//              commit the loads | barrier
+// The mid-step barrier keeps a half from overwriting X while the other half still reads it.
+template <class S, int T0, int NT>
+__device__ __forceinline__ void fwd_consumer(const FastArgs& a, const float* Tb, float* Rg, int wi,
+                                             int nmine, int lane) {
+  for (int k = -1; k <= nmine; ++k) {
+    const bool work = k >= 0 && k < nmine;
+    v4f acc[NT];
+    float* R = Rg + (((k < 0 ? 0 : k) % 3) * 4 + wi) * S::RSZ;
+    if (work) contract<S, false, T0, NT>(Tb + (k & 1) * S::LP, R, lane, acc);
+    __syncthreads();
+    if (work) write_acc<S, T0, NT>(R, lane, acc);
+    __syncthreads();
+  }
+}
 
-  for (int q = threadIdx.x; q < S::L; q += kThreads) Ts[q] = a.T[(size_t)c * S::L + q];
-  load_region<S>(a.x, a.B, a.C, c, img0, R, lane);
-  __syncthreads();
+// z and y = mix3x3(z) (or y = z) of one wave-unit, from the region to global memory.
+template <class S, bool MIX, bool ZS>
+__device__ __forceinline__ void fwd_epilogue(const FastArgs& a, const float* R, const Unit& U,
+                                             int ir0, const float (&w9)[9], int lane) {
+  float* yu = a.y + U.base;
+  float* zu = ZS ? a.zsave + U.base : nullptr;
+#pragma unroll
+  for (int p = 0; p < Column<S>::NP; ++p) {
+    const Column<S> col(p, lane);
+    if (!col.active || ir0 + col.im >= U.nimg) continue;
+    const int o = (ir0 + col.im) * U.cp + col.v;
+    sweep_column<S, 7>(R, col, [&](int h, const float (&w)[3][3]) {
+      const float z = w[1][1];
+      if constexpr (ZS) zu[o + h * S::IW] = z;
+      float yv = z;
+      if constexpr (MIX) {
+        yv = 0.f;
+#pragma unroll
+        for (int u = 0; u < 3; ++u)
+#pragma unroll
+          for (int t = 0; t < 3; ++t) yv = fmaf(w9[u * 3 + t], w[u][t], yv);
+      }
+      yu[o + h * S::IW] = yv;
+    });
+  }
+}
 
-  v4f acc[S::RT];
-  contract<S, false>(Ts, R, lane, acc);
-  wave_sync_lds();
-  write_acc<S>(R, lane, acc);
-  wave_sync_lds();
-
-  const bool mix = a.mixw != nullptr;
-  float w9[9];
+template <class S, bool MIX, bool ZS>
+__device__ __forceinline__ void fwd_producer(const FastArgs& a, float* Tb, float* Rg, int wi,
+                                             int nmine, int lane, int ptid) {
+  for (int k = -1; k <= nmine; ++k) {
+    const bool next = k + 1 < nmine;
+    float w9[9];
+    Unit Up{};
+    if (k >= 1) {
+      Up = unit_of<S>(a, blockIdx.x + (k - 1) * gridDim.x);
+      if constexpr (MIX) {
 #pragma unroll
-  for (int q = 0; q < 9; ++q) w9[q] = mix ? a.mixw[c * 9 + q] : 0.f;
-  const int B = a.B, C = a.C;
-  float* zs = a.zsave;
-  float* yo = a.y;
-  sweep_columns<S>(R, lane, [&](int im, int h, int v, const float (&w)[3][3], float*) {
-    const int b = img0 + im;
-    if (b >= B) return;
-    const size_t off = ((size_t)b * C + c) * S::PLANE + h * S::IW + v;
-    const float z = w[1][1];
-    if (zs) zs[off] = z;
-    float yv = z;
-    if (mix) {
-      yv = 0.f;
-#pragma unroll
-      for (int u = 0; u < 3; ++u)
-#pragma unroll
-        for (int t = 0; t < 3; ++t) yv = fmaf(w9[u * 3 + t], w[u][t], yv);
+        for (int q = 0; q < 9; ++q) w9[q] = a.mixw[Up.c * 9 + q];
+      }
     }
-    yo[off] = yv;
-  });
+    PlaneLoad<S> pl;
+    TableLoad<S> tl;
+    if (next) {
+      const Unit Un = unit_of<S>(a, blockIdx.x + (k + 1) * gridDim.x);
+      tl.issue(a.T, Un.c, ptid);
+      pl.issue(a.x + Un.base, Un, wi * S::IPW, lane);
+    }
+    if (k >= 1)
+      fwd_epilogue<S, MIX, ZS>(a, Rg + (((k - 1) % 3) * 4 + wi) * S::RSZ, Up, wi * S::IPW, w9,
+                               lane);
+    __syncthreads();
+    if (next) {
+      tl.commit(Tb + ((k + 1) & 1) * S::LP, ptid);
+      pl.commit(Rg + (((k + 1) % 3) * 4 + wi) * S::RSZ, lane);
+    }
+    __syncthreads();
+  }
+}
+
+template <class S>
+__global__ void __launch_bounds__(kWsThreads) k_fwd_ws(FastArgs a) {
+  extern __shared__ __attribute__((aligned(16))) float smem_f[];
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  float* Tb = smem_f;
+  float* Rg = smem_f + 2 * S::LP;
+  const int NU = a.C * a.groups;
+  const int nmine = (NU - (int)blockIdx.x + (int)gridDim.x - 1) / (int)gridDim.x;
+  // Role loops run separately, each with the same barriers per step (a workgroup barrier counts
+  // wave arrivals, not program locations), so each keeps only its own registers live.
+  constexpr int H0 = (S::RT + 1) / 2;
+  if (wave < 4) {
+    fwd_consumer<S, 0, H0>(a, Tb, Rg, wave, nmine, lane);
+  } else if (wave < 8) {
+    fwd_consumer<S, H0, S::RT - H0>(a, Tb, Rg, wave - 4, nmine, lane);
+  } else {
+    const int wi = wave - 8, ptid = threadIdx.x - 8 * 64;
+    const bool mix = a.mixw != nullptr, zs = a.zsave != nullptr;
+    if (mix && zs) fwd_producer<S, true, true>(a, Tb, Rg, wi, nmine, lane, ptid);
+    else if (mix) fwd_producer<S, true, false>(a, Tb, Rg, wi, nmine, lane, ptid);
+    else if (zs) fwd_producer<S, false, true>(a, Tb, Rg, wi, nmine, lane, ptid);
+    else fwd_producer<S, false, false>(a, Tb, Rg, wi, nmine, lane, ptid);
+  }
 }
 
 // ---------------------------------------------------------------------------- backward
@@ -308,155 +483,183 @@ __device__ __forceinline__ void dt_chunk(const float* regions, const float* xbuf
   }
 }
 
+// Diagonal sums of the wave's row-pair tiles into the unit's fp64 table partial:
+//   pT[dy_j][dx] = sum over x1 - x2 = dx of acc_j[x1][x2]   (x1, x2 < WS)
+// Every valid tile element goes to LDS once (scr[j][x1][x2], at most 7 tiles per wave); lane
+// (half, d) then sums diagonal d over half of its rows, and the two halves are added in a fixed
+// order, so the result does not depend on scheduling.
 template <class S, int Q>
 __device__ __forceinline__ void dt_partial_write(double* scr, const double (&acc64)[8][4],
                                                  double* pT, int lane) {
-  constexpr int WS = S::WS;
-#define WBMM_DT_OUT(J)                                                                 \
-  if constexpr (Slot<WS, Q, J>::valid) {                                               \
-    _Pragma("unroll") for (int r = 0; r < 4; ++r)                                      \
-        scr[(4 * (lane >> 4) + r) * 16 + (lane & 15)] = acc64[J][r];                   \
-    wave_sync_lds();                                                                   \
-    if (lane < S::L1) {                                                                \
-      const int dxv = lane - (WS - 1);                                                 \
-      double s = 0.0;                                                                  \
-      for (int xa = 0; xa < WS; ++xa) {                                                \
-        const int xb = xa - dxv;                                                       \
-        if (xb >= 0 && xb < WS) s += scr[xa * 16 + xb];                                \
-      }                                                                                \
-      pT[(Slot<WS, Q, J>::dy + WS - 1) * S::L1 + lane] = s;                            \
-    }                                                                                  \
-    wave_sync_lds();                                                                   \
+  constexpr int WS = S::WS, DD = WS * WS, HALF = (WS + 1) / 2;
+  const int x2 = lane & 15, g = lane >> 4;
+  // elements outside the WS x WS tile go to a per-lane dump slot past the seven tiles, so the
+  // stores (and the loads below) need no branches and can all be in flight together
+  const int dump = 7 * DD + lane;
+#define WBMM_DT_PUT(J)                                                        \
+  if constexpr (Slot<WS, Q, J>::valid) {                                      \
+    _Pragma("unroll") for (int r = 0; r < 4; ++r) {                           \
+      const int x1 = 4 * g + r;                                               \
+      scr[(x1 < WS && x2 < WS) ? J * DD + x1 * WS + x2 : dump] = acc64[J][r]; \
+    }                                                                         \
   }
-  WBMM_DT_OUT(0) WBMM_DT_OUT(1) WBMM_DT_OUT(2) WBMM_DT_OUT(3)
-  WBMM_DT_OUT(4) WBMM_DT_OUT(5) WBMM_DT_OUT(6) WBMM_DT_OUT(7)
-#undef WBMM_DT_OUT
+  WBMM_DT_PUT(0) WBMM_DT_PUT(1) WBMM_DT_PUT(2) WBMM_DT_PUT(3)
+  WBMM_DT_PUT(4) WBMM_DT_PUT(5) WBMM_DT_PUT(6) WBMM_DT_PUT(7)
+#undef WBMM_DT_PUT
+  wave_sync_lds();
+  const int h = lane >> 5, dd = lane & 31, dxv = dd - (WS - 1);
+#define WBMM_DT_SUM(J)                                                        \
+  if constexpr (Slot<WS, Q, J>::valid) {                                      \
+    double s = 0.0;                                                           \
+    _Pragma("unroll") for (int k = 0; k < HALF; ++k) {                        \
+      const int x1 = h * HALF + k, xb = x1 - dxv;                             \
+      const bool ok = dd < S::L1 && x1 < WS && xb >= 0 && xb < WS;            \
+      const double v = scr[ok ? J * DD + x1 * WS + xb : J * DD];              \
+      s += ok ? v : 0.0;                                                      \
+    }                                                                         \
+    const double o = __shfl_down(s, 32, 64);                                  \
+    if (lane < S::L1) pT[(Slot<WS, Q, J>::dy + WS - 1) * S::L1 + lane] = s + o; \
+  }
+  WBMM_DT_SUM(0) WBMM_DT_SUM(1) WBMM_DT_SUM(2) WBMM_DT_SUM(3)
+  WBMM_DT_SUM(4) WBMM_DT_SUM(5) WBMM_DT_SUM(6) WBMM_DT_SUM(7)
+#undef WBMM_DT_SUM
 }
 
 template <class S>
-__global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3, 8))) k_bwd_fast(FastArgs a) {
-  extern __shared__ __attribute__((aligned(16))) float smem_f[];
-  __shared__ double s_wred[4][9];
-  const int c = blockIdx.y, wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  float* Ts = smem_f;
-  float* regions = smem_f + S::TSZ;
-  float* R = regions + wave * S::RSZ;
-  const int wg_img0 = blockIdx.x * 4 * S::IPW;
-  const int img0 = wg_img0 + wave * S::IPW;
-  const int B = a.B, C = a.C;
-  const bool mix = a.mixw != nullptr;
+using BwdCol = Column<S, S::CHUNK_COLS>;
 
-  for (int q = threadIdx.x; q < S::L; q += kThreads) Ts[q] = a.T[(size_t)c * S::L + q];
-  load_region<S>(a.dy, B, C, c, img0, R, lane);
-  wave_sync_lds();
-
-  // ---- G = partition(dz) in place; dz = mix adjoint of dy (correlation with rot180(W)).
-  //      dWmix[u][t] = sum z[p][q] dy[p-u+1][q-t+1]: the same 3x3 dy window, times z.
-  //      A sliding 3x3 register window walks each image column; the column's z values are
-  //      loaded up front. Row h of dy is overwritten by G only after its last read.
-  if (mix) {
-    float w9[9];
+// G = partition(dz) of one wave-unit in place; dz = mix adjoint of dy (correlation with
+// rot180(W)). dWmix[u][t] = sum z[p][q] dy[p-u+1][q-t+1]: the same 3x3 dy window, times z. Each
+// lane walks an image column with a sliding 3x3 register window; passes are image-aligned, so no
+// column's neighbours are rewritten by another pass before they are read.
+template <class S, bool WANTW>
+__device__ __forceinline__ void bwd_mix_sweep(float* R, const float (&w9r)[9],
+                                              const float (&zpre)[BwdCol<S>::NP][S::IH],
+                                              int ir0, int nimg, double (&wacc)[9], int lane) {
 #pragma unroll
-    for (int q = 0; q < 9; ++q) w9[q] = a.mixw[(c * 9) + (8 - q)];  // rot180: W[2-u][2-t]
-    const bool wantW = a.want_dW;
-    double wacc[9];
+  for (int p = 0; p < BwdCol<S>::NP; ++p) {
+    const BwdCol<S> col(p, lane);
+    if (!col.active) continue;
+    const bool real = ir0 + col.im < nimg;
+    float wcol[9];
 #pragma unroll
-    for (int q = 0; q < 9; ++q) wacc[q] = 0.0;
+    for (int q = 0; q < 9; ++q) wcol[q] = 0.f;
+    sweep_column<S, 7>(R, col, [&](int h, const float (&w)[3][3]) {
+      // w[u][t] = dy(h+u-1, v+t-1); dz(h,v) = sum_{u,t} W[2-u][2-t] w[u][t]
+      float gsum = 0.f;
 #pragma unroll
-    for (int c0 = 0; c0 < S::COLS; c0 += S::CHUNK_COLS) {
-      const bool active = lane < S::CHUNK_COLS && c0 + lane < S::COLS;
-      const int col = active ? c0 + lane : c0;
-      const int im = col / S::IW, v = col % S::IW;
-      const int b = img0 + im;
-      const bool real = active && b < B;
-      const bool hasL = v > 0, hasR = v + 1 < S::IW;
-      float* pc = R + col_part<S>(im, v);
-      const float* pl = R + col_part<S>(im, hasL ? v - 1 : v);
-      const float* pr = R + col_part<S>(im, hasR ? v + 1 : v);
-      float zc[S::IH];
-      if (wantW) {
-        const float* zp = a.zsaved + ((size_t)(b < B ? b : B - 1) * C + c) * S::PLANE + v;
+      for (int q = 0; q < 9; ++q) gsum = fmaf(w9r[q], w[q / 3][q % 3], gsum);
+      R[col.pc + row_part<S>(h)] = gsum;
+      if constexpr (WANTW) {
+        const float z = real ? zpre[p][h] : 0.f;
+        // dWmix[u][t] += z * dy(h-u+1, v-t+1) = z * w[2-u][2-t]
 #pragma unroll
-        for (int h = 0; h < S::IH; ++h) zc[h] = zp[h * S::IW];
+        for (int q = 0; q < 9; ++q) wcol[q] = fmaf(z, w[2 - q / 3][2 - q % 3], wcol[q]);
       }
-      float wcol[9];
-#pragma unroll
-      for (int q = 0; q < 9; ++q) wcol[q] = 0.f;
-      float w[3][3];
-#pragma unroll
-      for (int t = 0; t < 3; ++t) w[0][t] = 0.f;
-      w[1][0] = hasL ? pl[row_part<S>(0)] : 0.f;
-      w[1][1] = pc[row_part<S>(0)];
-      w[1][2] = hasR ? pr[row_part<S>(0)] : 0.f;
-#pragma unroll
-      for (int h = 0; h < S::IH; ++h) {
-        if (h + 1 < S::IH) {
-          w[2][0] = hasL ? pl[row_part<S>(h + 1)] : 0.f;
-          w[2][1] = pc[row_part<S>(h + 1)];
-          w[2][2] = hasR ? pr[row_part<S>(h + 1)] : 0.f;
-        } else {
-          w[2][0] = w[2][1] = w[2][2] = 0.f;
-        }
-        // w[u][t] = dy(h+u-1, v+t-1); dz(h,v) = sum_{u,t} W[2-u][2-t] w[u][t]
-        float gsum = 0.f;
-#pragma unroll
-        for (int q = 0; q < 9; ++q) gsum = fmaf(w9[q], w[q / 3][q % 3], gsum);
-        if (real) pc[row_part<S>(h)] = gsum;
-        if (wantW) {
-          const float z = real ? zc[h] : 0.f;
-          // dWmix[u][t] += z * dy(h-u+1, v-t+1) = z * w[2-u][2-t]
-#pragma unroll
-          for (int q = 0; q < 9; ++q) wcol[q] = fmaf(z, w[2 - q / 3][2 - q % 3], wcol[q]);
-        }
-#pragma unroll
-        for (int t = 0; t < 3; ++t) {
-          w[0][t] = w[1][t];
-          w[1][t] = w[2][t];
-        }
-      }
+    });
+    if constexpr (WANTW) {
 #pragma unroll
       for (int q = 0; q < 9; ++q) wacc[q] += (double)wcol[q];
     }
+  }
+}
+
+// dX = M^T . G of the wave-unit, stored from the accumulators: lane (n, g) holds pixels
+// p = 16t + 4g + r of window n, and pairs (r, r+1), r even, are neighbours in one window row
+// (WS even), so each pair is one aligned 8-byte store.
+template <class S>
+__device__ __forceinline__ void dx_store(const FastArgs& a, const Unit& U, int ir0,
+                                         const v4f (&acc)[S::RT], int lane) {
+  static_assert(S::WS % 2 == 0 && S::WS > 12, "dX pair stores: even rows, at most one wrap");
+  typedef float f2 __attribute__((ext_vector_type(2)));
+  const int n = lane & 15, g4 = 4 * (lane >> 4);
+  const int ir = ir0 + n / S::NWIN, wnd = n % S::NWIN;
+  if (ir >= U.nimg) return;
+  float* o = a.dx + U.base;
+  const int lofs = ir * U.cp + (wnd / S::NWX) * S::WS * S::IW + (wnd % S::NWX) * S::WS + g4;
+#pragma unroll
+  for (int t = 0; t < S::RT; ++t)
+#pragma unroll
+    for (int r = 0; r < 4; r += 2) {
+      const int c0 = 16 * t + r;  // p = c0 + g4
+      if (c0 + g4 < S::D) {
+        const int yy = c0 / S::WS + ((c0 % S::WS) + g4 >= S::WS ? 1 : 0);
+        *(f2*)(o + lofs + c0 + yy * (S::IW - S::WS)) = f2{acc[t][r], acc[t][r + 1]};
+      }
+    }
+}
+
+// One workgroup (4 waves, one wave-unit each) per unit; three workgroups per CU. Phases:
+//   dy -> G regions (mix adjoint in place, dWmix sums) | dX from the accumulators | table
+//   gradient: X streamed in 4-window chunks through the table region (loads of the next chunk
+//   in flight in registers), row-pair MFMAs per slot set, fp64 partial of the unit.
+template <class S>
+__global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3, 8))) k_bwd_ls(FastArgs a) {
+  extern __shared__ __attribute__((aligned(16))) float smem_f[];
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  float* Ts = smem_f;
+  // per-wave dWmix sums, [4][9] doubles, in the table region's tail (free until the X chunks)
+  double* s_wred = (double*)(smem_f + S::LP);
+  float* regions = smem_f + S::TSZ;
+  float* R = regions + wave * S::RSZ;
+  const int u = blockIdx.x;
+  const Unit U = unit_of<S>(a, u);
+  const int ir0 = wave * S::IPW;
+  const bool mix = a.mixw != nullptr, wantW = mix && a.want_dW;
+
+  // z for the dWmix sums (one register column per pass), table and dy, all in flight together
+  float zpre[BwdCol<S>::NP][S::IH];
+  if (wantW) {
+    const float* zu = a.zsaved + U.base;
+#pragma unroll
+    for (int p = 0; p < BwdCol<S>::NP; ++p) {
+      const BwdCol<S> col(p, lane);
+      const int ir = ir0 + col.im < U.nimg ? ir0 + col.im : U.nimg - 1;
+      const int o = ir * U.cp + col.v;
+#pragma unroll
+      for (int h = 0; h < S::IH; ++h) zpre[p][h] = zu[o + h * S::IW];
+    }
+  }
+  {
+    PlaneLoad<S> pl;
+    pl.issue(a.dy + U.base, U, ir0, lane);
+    for (int q = threadIdx.x; q < S::L; q += kThreads) Ts[q] = a.T[(size_t)U.c * S::L + q];
+    pl.commit(R, lane);
+  }
+  wave_sync_lds();
+  if (mix) {
+    float w9r[9];
+#pragma unroll
+    for (int q = 0; q < 9; ++q) w9r[q] = a.mixw[(U.c * 9) + (8 - q)];  // rot180: W[2-u][2-t]
+    double wacc[9];
+#pragma unroll
+    for (int q = 0; q < 9; ++q) wacc[q] = 0.0;
     if (wantW) {
+      bwd_mix_sweep<S, true>(R, w9r, zpre, ir0, U.nimg, wacc, lane);
 #pragma unroll
       for (int q = 0; q < 9; ++q) {
         double v = wacc[q];
         for (int off = 32; off > 0; off >>= 1) v += __shfl_down(v, off, 64);
-        if (lane == 0) s_wred[wave][q] = v;
+        if (lane == 0) s_wred[wave * 9 + q] = v;
       }
+    } else {
+      bwd_mix_sweep<S, false>(R, w9r, zpre, ir0, U.nimg, wacc, lane);
     }
   }
   __syncthreads();  // table, every wave's G and the dWmix wave sums are in LDS
-  if (a.want_dW && threadIdx.x < 9) {
+  if (wantW && threadIdx.x < 9) {
     const int q = threadIdx.x;
-    a.partW[((size_t)c * a.wgs_per_c + blockIdx.x) * 9 + q] =
-        ((s_wred[0][q] + s_wred[1][q]) + s_wred[2][q]) + s_wred[3][q];
+    a.partW[(size_t)u * 9 + q] = ((s_wred[q] + s_wred[9 + q]) + s_wred[18 + q]) + s_wred[27 + q];
   }
 
   // ---- dX = M^T . G, stored straight from the accumulators (G stays in LDS for dT)
   if (a.want_dx) {
     v4f acc[S::RT];
-    contract<S, true>(Ts, R, lane, acc);
-    const int n = lane & 15, i0 = 4 * (lane >> 4);
-    const int im = n / S::NWIN, wi = n % S::NWIN;
-    const int b = img0 + im;
-    if (b < B) {
-      float* o = a.dx + ((size_t)b * C + c) * S::PLANE + (wi / S::NWX) * S::WS * S::IW +
-                 (wi % S::NWX) * S::WS;
-#pragma unroll
-      for (int t = 0; t < S::RT; ++t)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int i = t * 16 + r + i0;
-          if (i < S::D) {
-            const int yy = i / S::WS, xx = i - yy * S::WS;
-            o[yy * S::IW + xx] = acc[t][r];
-          }
-        }
-    }
+    contract<S, true, 0, S::RT>(Ts, R, lane, acc);
+    dx_store<S>(a, U, ir0, acc, lane);
   }
 
-  // ---- table gradient partial over the workgroup's 64 windows. X comes in chunks of 4 windows
+  // ---- table gradient partial over the unit's 64 windows. X comes in chunks of 4 windows
   //      through the (now free) table region; the next chunk's global loads are in flight in
   //      registers while the current one is contracted.
   if (a.want_dT) {
@@ -480,24 +683,24 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3
       goff[j] = (p / S::WS) * S::IW + (p % S::WS);
       loff[j] = e < CH_E ? ekn[j] * S::XP + p : -1;
     }
+    const float* xu = a.x + U.base;
     float stg[EPT];
     auto load_chunk = [&](int ci) {
 #pragma unroll
       for (int j = 0; j < EPT; ++j) {
         const int n = 4 * ci + ekn[j];
         const int q = n >> 4, nl = n & 15;
-        const int im = nl / S::NWIN, wi = nl % S::NWIN;
-        int b = wg_img0 + q * S::IPW + im;
-        b = b < B ? b : B - 1;  // windows past the batch have G = 0
-        stg[j] = a.x[((size_t)b * C + c) * S::PLANE + (wi / S::NWX) * S::WS * S::IW +
-                     (wi % S::NWX) * S::WS + goff[j]];
+        const int im = nl / S::NWIN, wnd = nl % S::NWIN;
+        int ir = q * S::IPW + im;
+        ir = ir < U.nimg ? ir : U.nimg - 1;  // windows past the batch have G = 0
+        stg[j] = xu[ir * U.cp + (wnd / S::NWX) * S::WS * S::IW + (wnd % S::NWX) * S::WS + goff[j]];
       }
     };
     const int kn = lane >> 4, x1 = lane & 15;
     const int xc = x1 < S::WS ? x1 : S::WS - 1;
     float* xbuf = Ts;
     load_chunk(0);
-    __syncthreads();  // every wave is done with the table (dX)
+    __syncthreads();  // every wave is done with the table (dX) and the dWmix sums
     for (int ci = 0; ci < 16; ++ci) {
       if (ci > 0) __syncthreads();  // chunk ci-1 consumed by every wave
 #pragma unroll
@@ -513,7 +716,7 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3
         default: dt_chunk<S, 3>(regions, xbuf, 4 * ci, kn, xc, a32, acc64, flush); break;
       }
     }
-    double* pT = a.partT + ((size_t)c * a.wgs_per_c + blockIdx.x) * S::L;
+    double* pT = a.partT + (size_t)u * S::L;
     __syncthreads();  // every wave is done reading the G regions and the last chunk
     double* scr = (double*)R;
     switch (wave) {
@@ -523,7 +726,6 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3
       default: dt_partial_write<S, 3>(scr, acc64, pT, lane); break;
     }
   }
-
 }
 
 // ---------------------------------------------------------------------------- dispatch
@@ -540,20 +742,44 @@ FastShape fast_shape(int H, int W, int w, int layout) {
   return FS_NONE;
 }
 
-template <class S>
-int lds_bytes() { return (S::TSZ + 4 * S::RSZ) * 4; }
+// LDS is allocated to workgroups in 1280-byte granules on gfx950 (160 KiB per CU).
+constexpr int kLdsPerCu = 160 * 1024, kLdsGranule = 1280;
+constexpr bool lds_fits(int bytes, int wgs) {
+  return (bytes + kLdsGranule - 1) / kLdsGranule * kLdsGranule * wgs <= kLdsPerCu;
+}
 
 template <class S>
-int wgs_per_c(int B) { return (B + 4 * S::IPW - 1) / (4 * S::IPW); }
+constexpr int fwd_lds() { return (2 * S::LP + 12 * S::RSZ) * 4; }
+template <class S>
+constexpr int bwd_lds() { return (S::TSZ + 4 * S::RSZ) * 4; }
+
+template <class S>
+int groups(int B) { return (B + 4 * S::IPW - 1) / (4 * S::IPW); }
+
+// Compute units of the current device (cached per device); one persistent workgroup per CU.
+int cu_count() {
+  static std::atomic<int> cache[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
+  int n = cache[dev].load(std::memory_order_relaxed);
+  if (n <= 0) {
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+      n = 256;
+    cache[dev].store(n, std::memory_order_relaxed);
+  }
+  return n;
+}
 
 template <class S, class Fn>
-hipError_t launch_shape(Fn fn, FastArgs a, hipStream_t st) {
-  a.wgs_per_c = wgs_per_c<S>(a.B);
-  hipError_t e = hipFuncSetAttribute((const void*)fn, hipFuncAttributeMaxDynamicSharedMemorySize,
-                                     lds_bytes<S>());
+hipError_t launch_ws(Fn fn, int lds, FastArgs a, hipStream_t st) {
+  a.groups = groups<S>(a.B);
+  const int units = a.C * a.groups;
+  const int cus = cu_count();
+  const int grid = units < cus ? units : cus;
+  hipError_t e = hipFuncSetAttribute((const void*)fn, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
   if (e != hipSuccess) return e;
   mark_main_kernel(st, true);
-  hipLaunchKernelGGL(fn, dim3(a.wgs_per_c, a.C, 1), dim3(kThreads), lds_bytes<S>(), st, a);
+  hipLaunchKernelGGL(fn, dim3(grid), dim3(kWsThreads), lds, st, a);
   e = hipGetLastError();
   mark_main_kernel(st, false);
   return e;
@@ -562,16 +788,40 @@ hipError_t launch_shape(Fn fn, FastArgs a, hipStream_t st) {
 using S14 = Shape<14, 14, 14>;
 using S28 = Shape<14, 28, 28>;
 using S56 = Shape<14, 56, 56>;
+static_assert(lds_fits(fwd_lds<S14>(), 1) && lds_fits(fwd_lds<S28>(), 1) &&
+                  lds_fits(fwd_lds<S56>(), 1),
+              "one persistent forward workgroup per CU");
+static_assert(lds_fits(bwd_lds<S14>(), 3) && lds_fits(bwd_lds<S28>(), 3) &&
+                  lds_fits(bwd_lds<S56>(), 3),
+              "three backward workgroups per CU");
+
+// Backward: one workgroup of 4 waves per unit.
+template <class S, class Fn>
+hipError_t launch_ls(Fn fn, int lds, FastArgs a, hipStream_t st) {
+  a.groups = groups<S>(a.B);
+  const int units = a.C * a.groups;
+  hipError_t e = hipFuncSetAttribute((const void*)fn, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+  if (e != hipSuccess) return e;
+  mark_main_kernel(st, true);
+  hipLaunchKernelGGL(fn, dim3(units), dim3(kThreads), lds, st, a);
+  e = hipGetLastError();
+  mark_main_kernel(st, false);
+  return e;
+}
 
 }  // namespace
 
+// Per-lane offsets within a unit are ints: ir * C * plane + pixel, ir < 16 images.
+bool offsets_fit(int C, int H, int W) { return (size_t)16 * C * H * W < ((size_t)1 << 31); }
+
 bool fast_forward_ok(const FwdRequest& r) {
   return !r.in_bf16 && !r.out_bf16 && r.T && !r.M &&
-         fast_shape(r.H, r.W, r.w, r.layout) != FS_NONE;
+         fast_shape(r.H, r.W, r.w, r.layout) != FS_NONE && offsets_fit(r.C, r.H, r.W);
 }
 
 bool fast_backward_ok(const BwdRequest& r) {
-  return r.T && !r.M && fast_shape(r.H, r.W, r.w, r.layout) != FS_NONE;
+  return r.T && !r.M && fast_shape(r.H, r.W, r.w, r.layout) != FS_NONE &&
+         offsets_fit(r.C, r.H, r.W);
 }
 
 hipError_t launch_forward_fast(const FwdRequest& r, hipStream_t st) {
@@ -584,43 +834,43 @@ hipError_t launch_forward_fast(const FwdRequest& r, hipStream_t st) {
   a.zsave = (float*)r.zsave;
   a.y = (float*)r.y;
   switch (fast_shape(r.H, r.W, r.w, r.layout)) {
-    case FS_14_14_14: return launch_shape<S14>(k_fwd_fast<S14>, a, st);
-    case FS_14_28_28: return launch_shape<S28>(k_fwd_fast<S28>, a, st);
-    case FS_14_56_56: return launch_shape<S56>(k_fwd_fast<S56>, a, st);
+    case FS_14_14_14: return launch_ws<S14>(k_fwd_ws<S14>, fwd_lds<S14>(), a, st);
+    case FS_14_28_28: return launch_ws<S28>(k_fwd_ws<S28>, fwd_lds<S28>(), a, st);
+    case FS_14_56_56: return launch_ws<S56>(k_fwd_ws<S56>, fwd_lds<S56>(), a, st);
     default: return hipErrorInvalidValue;
   }
 }
 
 size_t fast_backward_workspace(const BwdRequest& r) {
-  int wgs;
+  int g;
   switch (fast_shape(r.H, r.W, r.w, r.layout)) {
-    case FS_14_14_14: wgs = wgs_per_c<S14>(r.B); break;
-    case FS_14_28_28: wgs = wgs_per_c<S28>(r.B); break;
-    case FS_14_56_56: wgs = wgs_per_c<S56>(r.B); break;
+    case FS_14_14_14: g = groups<S14>(r.B); break;
+    case FS_14_28_28: g = groups<S28>(r.B); break;
+    case FS_14_56_56: g = groups<S56>(r.B); break;
     default: return 0;
   }
   auto al = [](size_t v) { return (v + 255) / 256 * 256; };
   const size_t L = (size_t)(2 * r.w - 1) * (2 * r.w - 1);
-  return al((size_t)r.C * wgs * L * 8) + al((size_t)r.C * wgs * 9 * 8);
+  return al((size_t)r.C * g * L * 8) + al((size_t)r.C * g * 9 * 8);
 }
 
 hipError_t launch_backward_fast(const BwdRequest& r, hipStream_t st) {
   FastArgs a{};
   a.B = r.B;
   a.C = r.C;
-  int wgs;
+  int g;
   const FastShape fs = fast_shape(r.H, r.W, r.w, r.layout);
   switch (fs) {
-    case FS_14_14_14: wgs = wgs_per_c<S14>(r.B); break;
-    case FS_14_28_28: wgs = wgs_per_c<S28>(r.B); break;
-    case FS_14_56_56: wgs = wgs_per_c<S56>(r.B); break;
+    case FS_14_14_14: g = groups<S14>(r.B); break;
+    case FS_14_28_28: g = groups<S28>(r.B); break;
+    case FS_14_56_56: g = groups<S56>(r.B); break;
     default: return hipErrorInvalidValue;
   }
   auto al = [](size_t v) { return (v + 255) / 256 * 256; };
   const size_t L = (size_t)(2 * r.w - 1) * (2 * r.w - 1);
   unsigned char* ws = (unsigned char*)r.ws;
   a.partT = (double*)ws;
-  a.partW = (double*)(ws + al((size_t)r.C * wgs * L * 8));
+  a.partW = (double*)(ws + al((size_t)r.C * g * L * 8));
   a.x = r.x;
   a.T = r.T;
   a.mixw = r.mixw;
@@ -634,12 +884,12 @@ hipError_t launch_backward_fast(const BwdRequest& r, hipStream_t st) {
   a.want_dW = (r.mixw && r.dmixw) ? 1 : 0;
   hipError_t e;
   switch (fs) {
-    case FS_14_14_14: e = launch_shape<S14>(k_bwd_fast<S14>, a, st); break;
-    case FS_14_28_28: e = launch_shape<S28>(k_bwd_fast<S28>, a, st); break;
-    default: e = launch_shape<S56>(k_bwd_fast<S56>, a, st); break;
+    case FS_14_14_14: e = launch_ls<S14>(k_bwd_ls<S14>, bwd_lds<S14>(), a, st); break;
+    case FS_14_28_28: e = launch_ls<S28>(k_bwd_ls<S28>, bwd_lds<S28>(), a, st); break;
+    default: e = launch_ls<S56>(k_bwd_ls<S56>, bwd_lds<S56>(), a, st); break;
   }
   if (e != hipSuccess || (!a.want_dT && !a.want_dW)) return e;
-  return launch_bwd_reduce(a.partT, a.want_dW ? a.partW : nullptr, wgs, r.C, (int)L,
+  return launch_bwd_reduce(a.partT, a.want_dW ? a.partW : nullptr, g, r.C, (int)L,
                            a.want_dT ? r.dT : nullptr, a.want_dW ? r.dmixw : nullptr, st);
 }
 
