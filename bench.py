@@ -42,6 +42,8 @@ def log(*a):
 def kernel_source_hash() -> str:
     h = hashlib.sha256()
     for p in sorted(glob.glob(os.path.join(CSRC, "*"))):
+        if not os.path.isfile(p) or not p.endswith((".hip", ".hpp", ".cpp", ".h")):
+            continue
         with open(p, "rb") as f:
             h.update(os.path.basename(p).encode())
             h.update(f.read())
@@ -308,17 +310,33 @@ def copy_calibration(mib: int = 512):
 
 
 def _pmc_rows(d):
+    """Counter rows of a rocprofv3 --pmc output directory (CSV or rocpd SQLite database)."""
     rows = []
     for p in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
         with open(p) as f:
             rows += list(csv.DictReader(f))
+    for p in glob.glob(os.path.join(d, "**", "*.db"), recursive=True):
+        import sqlite3
+        con = sqlite3.connect(p)
+        try:
+            for disp, kname, cname, val in con.execute(
+                    "select dispatch_id, kernel_name, counter_name, value from counters_collection"):
+                rows.append({"Dispatch_Id": disp, "Kernel_Name": kname, "Counter_Name": cname,
+                             "Counter_Value": val})
+        finally:
+            con.close()
     return rows
 
 
-def _per_dispatch(rows, counter, name_filter):
+# bench label -> names of the kernels that can be that call's main kernel (fast or general path)
+MAIN_KERNELS = {"k_wbmm_fwd": ("k_fwd_ws", "k_wbmm_fwd"), "k_wbmm_bwd": ("k_bwd_ls", "k_wbmm_bwd")}
+
+
+def _per_dispatch(rows, counter, names):
     vals = {}
     for r in rows:
-        if r.get("Counter_Name") != counter or name_filter not in r.get("Kernel_Name", ""):
+        kn = r.get("Kernel_Name", "")
+        if r.get("Counter_Name") != counter or not any(n in kn for n in names):
             continue
         key = r.get("Dispatch_Id")
         vals[key] = vals.get(key, 0.0) + float(r["Counter_Value"])
@@ -328,8 +346,8 @@ def _per_dispatch(rows, counter, name_filter):
 def summarize_pmc(workload, fetch_dir, write_dir, copy_fetch_dir, copy_write_dir, copy_mib=512):
     """FETCH_SIZE / WRITE_SIZE (KiB per dispatch) -> bytes, scaled by the copy kernel's reading."""
     true_kib = copy_mib * 1024.0
-    cf = _per_dispatch(_pmc_rows(copy_fetch_dir), "FETCH_SIZE", "")
-    cw = _per_dispatch(_pmc_rows(copy_write_dir), "WRITE_SIZE", "")
+    cf = _per_dispatch(_pmc_rows(copy_fetch_dir), "FETCH_SIZE", ("copy",))
+    cw = _per_dispatch(_pmc_rows(copy_write_dir), "WRITE_SIZE", ("copy",))
     f_fac = cf / true_kib
     w_fac = cw / true_kib
     rec = {"workload": workload, "src_hash": kernel_source_hash(),
@@ -337,9 +355,9 @@ def summarize_pmc(workload, fetch_dir, write_dir, copy_fetch_dir, copy_write_dir
                            "fetch_factor": f_fac, "write_factor": w_fac},
            "kernels": {}}
     frows, wrows = _pmc_rows(fetch_dir), _pmc_rows(write_dir)
-    for k in ("k_wbmm_fwd", "k_wbmm_bwd"):
-        fk = _per_dispatch(frows, "FETCH_SIZE", k)
-        wk = _per_dispatch(wrows, "WRITE_SIZE", k)
+    for k, names in MAIN_KERNELS.items():
+        fk = _per_dispatch(frows, "FETCH_SIZE", names)
+        wk = _per_dispatch(wrows, "WRITE_SIZE", names)
         if fk is None or wk is None:
             continue
         rb = fk / f_fac * 1024.0
