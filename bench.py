@@ -39,13 +39,20 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def kernel_source_hash() -> str:
+# kernel -> the source file that defines it. A kernel's hash covers that file and the headers
+# with device code; wbmm_launch.hpp (host-side request structs and launcher declarations) and
+# the other kernels' files do not change it.
+KERNEL_FILES = {"k_fwd_ws": "wbmm_fast.hip", "k_bwd_ls": "wbmm_fast.hip",
+                "k_fwd_bf16": "wbmm_fastbf.hip", "k_wbmm_fwd": "wbmm_fwd.hip",
+                "k_wbmm_bwd": "wbmm_bwd.hip"}
+DEVICE_HEADERS = ("wbmm_device.hpp", "wbmm_core.hpp", "wbmm_plan.hpp")
+
+
+def kernel_source_hash(kernel: str) -> str:
     h = hashlib.sha256()
-    for p in sorted(glob.glob(os.path.join(CSRC, "*"))):
-        if not os.path.isfile(p) or not p.endswith((".hip", ".hpp", ".cpp", ".h")):
-            continue
-        with open(p, "rb") as f:
-            h.update(os.path.basename(p).encode())
+    for name in (KERNEL_FILES[kernel],) + DEVICE_HEADERS:
+        with open(os.path.join(CSRC, name), "rb") as f:
+            h.update(name.encode())
             h.update(f.read())
     return h.hexdigest()[:16]
 
@@ -118,10 +125,12 @@ def load_traffic(workload: str, kernel: str):
         return None
     with open(p) as f:
         rec = json.load(f)
-    if rec.get("src_hash") != kernel_source_hash():
-        return None
     k = rec.get("kernels", {}).get(kernel)
-    return None if k is None else k.get("hbm_bytes_per_launch")
+    if k is None or k.get("kernel_name") not in KERNEL_FILES:
+        return None
+    if k.get("src_hash") != kernel_source_hash(k["kernel_name"]):
+        return None  # the kernel changed since the counters were taken
+    return k.get("hbm_bytes_per_launch")
 
 
 # ----------------------------------------------------------------------------- HIP events
@@ -329,18 +338,24 @@ def _pmc_rows(d):
 
 
 # bench label -> names of the kernels that can be that call's main kernel (fast or general path)
-MAIN_KERNELS = {"k_wbmm_fwd": ("k_fwd_ws", "k_wbmm_fwd"), "k_wbmm_bwd": ("k_bwd_ls", "k_wbmm_bwd")}
+MAIN_KERNELS = {"k_wbmm_fwd": ("k_fwd_ws", "k_fwd_bf16", "k_wbmm_fwd"),
+                "k_wbmm_bwd": ("k_bwd_ls", "k_wbmm_bwd")}
 
 
-def _per_dispatch(rows, counter, names):
-    vals = {}
-    for r in rows:
-        kn = r.get("Kernel_Name", "")
-        if r.get("Counter_Name") != counter or not any(n in kn for n in names):
-            continue
-        key = r.get("Dispatch_Id")
-        vals[key] = vals.get(key, 0.0) + float(r["Counter_Value"])
-    return statistics.median(vals.values()) if vals else None
+def _per_dispatch(rows, counter, names, with_name=False):
+    """Median over dispatches of a counter summed over its rows, for the first of `names` that
+    some dispatch's kernel name contains."""
+    for n in names:
+        vals = {}
+        for r in rows:
+            if r.get("Counter_Name") != counter or n not in r.get("Kernel_Name", ""):
+                continue
+            key = r.get("Dispatch_Id")
+            vals[key] = vals.get(key, 0.0) + float(r["Counter_Value"])
+        if vals:
+            med = statistics.median(vals.values())
+            return (med, n) if with_name else med
+    return (None, None) if with_name else None
 
 
 def summarize_pmc(workload, fetch_dir, write_dir, copy_fetch_dir, copy_write_dir, copy_mib=512):
@@ -350,19 +365,20 @@ def summarize_pmc(workload, fetch_dir, write_dir, copy_fetch_dir, copy_write_dir
     cw = _per_dispatch(_pmc_rows(copy_write_dir), "WRITE_SIZE", ("copy",))
     f_fac = cf / true_kib
     w_fac = cw / true_kib
-    rec = {"workload": workload, "src_hash": kernel_source_hash(),
+    rec = {"workload": workload,
            "copy_kernel": {"bytes_each_way": copy_mib * 2**20, "fetch_kib": cf, "write_kib": cw,
                            "fetch_factor": f_fac, "write_factor": w_fac},
            "kernels": {}}
     frows, wrows = _pmc_rows(fetch_dir), _pmc_rows(write_dir)
     for k, names in MAIN_KERNELS.items():
-        fk = _per_dispatch(frows, "FETCH_SIZE", names)
-        wk = _per_dispatch(wrows, "WRITE_SIZE", names)
+        fk, kname = _per_dispatch(frows, "FETCH_SIZE", names, with_name=True)
+        wk = _per_dispatch(wrows, "WRITE_SIZE", (kname,)) if kname else None
         if fk is None or wk is None:
             continue
         rb = fk / f_fac * 1024.0
         wb = wk / w_fac * 1024.0
-        rec["kernels"][k] = {"fetch_kib_raw": fk, "write_kib_raw": wk, "read_bytes": rb,
+        rec["kernels"][k] = {"kernel_name": kname, "src_hash": kernel_source_hash(kname),
+                             "fetch_kib_raw": fk, "write_kib_raw": wk, "read_bytes": rb,
                              "write_bytes": wb, "hbm_bytes_per_launch": rb + wb}
     out = os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
     with open(out, "w") as f:

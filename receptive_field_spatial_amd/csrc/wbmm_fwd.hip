@@ -150,6 +150,7 @@ size_t forward_workspace(const FwdRequest& r) {
 
 hipError_t launch_forward(const FwdRequest& r, hipStream_t st) {
   if (fast_forward_ok(r)) return launch_forward_fast(r, st);
+  if (fast_bf16_forward_ok(r)) return launch_forward_fast_bf16(r, st);
   FwdArgs a{};
   if (!plan_fwd(a.g, r)) return hipErrorInvalidValue;
   a.x = r.x;

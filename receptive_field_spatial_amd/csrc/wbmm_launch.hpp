@@ -49,12 +49,17 @@ bool backward_plan_ok(const BwdRequest& r);
 size_t backward_workspace(const BwdRequest& r);
 hipError_t launch_backward(const BwdRequest& r, hipStream_t st);
 
-// Fast fp32 paths for w in {7, 14} when whole images fit one wave's 16 windows.
+// Fast fp32 paths for w = 14, NCHW, square images of 14, 28 or 56 (whole images per wave).
 bool fast_forward_ok(const FwdRequest& r);
 hipError_t launch_forward_fast(const FwdRequest& r, hipStream_t st);
 bool fast_backward_ok(const BwdRequest& r);
 size_t fast_backward_workspace(const BwdRequest& r);
 hipError_t launch_backward_fast(const BwdRequest& r, hipStream_t st);
+
+// Fast bf16 forward for w = 14, NCHW, square images of 14, 28 or 56, table input, bf16 output,
+// no mix.
+bool fast_bf16_forward_ok(const FwdRequest& r);
+hipError_t launch_forward_fast_bf16(const FwdRequest& r, hipStream_t st);
 
 // Fixed-order sum of per-workgroup fp64 partials: dT[c][q] = sum_k partT[c][k][q] (and dWmix).
 hipError_t launch_bwd_reduce(const double* partT, const double* partW, int parts, int C, int L,

@@ -222,6 +222,67 @@ def test_forward_bf16(w, cached, out):
         assert_f32(host(y), want, "y (fp32 out)")
 
 
+@pytest.mark.parametrize("hw,B", [(14, 3), (28, 5), (28, 16), (28, 33), (56, 3), (56, 6), (56, 9)])
+@pytest.mark.parametrize("zsave", [False, True])
+def test_forward_bf16_fast(hw, B, zsave):
+    """w = 14 bf16 fast path (square NCHW 28x28 and 56x56 images, table, bf16 output; 14x14 goes
+    the general way): batches that fill whole units and ragged ones; z_save equals y bit for bit
+    (no mix)."""
+    w, C = 14, 3
+    say(f"forward bf16 fast w=14 {hw}x{hw} B={B} C={C} zsave={zsave}")
+    x = synth.round_to_bf16(synth.normal_f32((B, C, hw, hw), 1.0, seed=31))
+    T = synth.round_to_bf16(synth.normal_f32((C, 27, 27), 0.02, seed=32))
+    z = torch.empty((B, C, hw, hw), dtype=torch.bfloat16, device="cuda") if zsave else None
+    y = R().wbmm_forward(dev_bf16(x), w, T=dev_bf16(T), out_dtype=torch.bfloat16, z_save=z)
+    want = O.wbmm_forward(x.astype(np.float64), w, T=T.astype(np.float64))
+    assert_bf16(host(y), want, "y")
+    if zsave:
+        assert torch.equal(z.view(torch.int16), y.view(torch.int16))
+
+
+@pytest.mark.parametrize("hw", [14, 28, 56])
+def test_forward_bf16_fast_identity_bitwise(hw):
+    """One-hot table at the centre: M = I, every product is 1 * x or 0 * x and the bf16 output
+    reproduces the bf16 input bit for bit (pins the fast path's operand placement)."""
+    w, B, C = 14, 4, 2
+    say(f"forward bf16 fast identity {hw}x{hw}")
+    x = synth.round_to_bf16(synth.normal_f32((B, C, hw, hw), 1.0, seed=33))
+    T = np.zeros((C, 27, 27), np.float32)
+    T[:, 13, 13] = 1.0
+    y = R().wbmm_forward(dev_bf16(x), w, T=dev_bf16(T), out_dtype=torch.bfloat16)
+    assert np.array_equal(host(y), x)
+
+
+def _window_shift(x, w, dy, dx):
+    """out[i] = x[(y_i - dy, x_i - dx)] inside each window, zero where that pixel lies outside
+    it: the WBMM output for a one-hot table at offset (dy, dx) from the centre, per channel."""
+    B, C, H, W = x.shape
+    out = np.zeros_like(x)
+    for c in range(C):
+        for yi in range(w):
+            for xi in range(w):
+                ys, xs = yi - dy[c], xi - dx[c]
+                if 0 <= ys < w and 0 <= xs < w:
+                    out[:, c, yi::w, xi::w] = x[:, c, ys::w, xs::w]
+    return out
+
+
+@pytest.mark.parametrize("hw,B,C", [(56, 4, 800), (56, 7, 300), (28, 16, 1100)])
+def test_forward_bf16_fast_shift_bitwise(hw, B, C):
+    """One-hot tables at a different offset in every channel: the output is the input shifted
+    inside each window (exact in bf16). More units than resident workgroups, so workgroups walk
+    several units and rebuild the staged table when the channel changes."""
+    w = 14
+    say(f"forward bf16 fast shift {hw}x{hw} B={B} C={C}")
+    x = synth.round_to_bf16(synth.normal_f32((B, C, hw, hw), 1.0, seed=34))
+    dy = (np.arange(C) * 5) % 27 - 13
+    dx = (np.arange(C) * 11 + 3) % 27 - 13
+    T = np.zeros((C, 27, 27), np.float32)
+    T[np.arange(C), dy + 13, dx + 13] = 1.0
+    y = R().wbmm_forward(dev_bf16(x), w, T=dev_bf16(T), out_dtype=torch.bfloat16)
+    assert np.array_equal(host(y), _window_shift(x, w, dy, dx))
+
+
 # ----------------------------------------------------------------------------- workloads
 def _sample_channels(C, k, seed=0):
     rng = np.random.default_rng(seed + 1000)
