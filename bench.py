@@ -245,7 +245,7 @@ def run(args):
     wall = time.perf_counter() - t0
     total_ms = start.elapsed_time(stop)
     ms_step = total_ms / K
-    # main-kernel durations, recorded by the library right around each launch
+    # main-kernel durations: the library attaches the events to each main kernel's dispatch
     fwd_ms = [hev.elapsed_ms(e[0], e[1]) for e in kev]
     bwd_ms = [hev.elapsed_ms(e[2], e[3]) for e in kev] if wl.backward else []
     for e in kev:

@@ -162,10 +162,11 @@ wbmm_status wbmm_backward(int B, int C, int H, int W, int w, int layout, const f
 
 /*
  * wbmm_set_launch_events — measurement aid, not part of the method. The next wbmm_forward or
- * wbmm_backward call made on the calling thread records `before` (a hipEvent_t passed as void*)
- * on its stream immediately before launching its main contraction kernel and `after`
- * immediately after it; the pair is then cleared. Both NULL clears a pending pair. The caller
- * owns the events. Errors: WBMM_E_INVALID when exactly one of the two is NULL.
+ * wbmm_backward call made on the calling thread attaches `before` and `after` (hipEvent_t
+ * handles passed as void*) to the dispatch of its main contraction kernel (hipExtLaunchKernel's
+ * start and stop events), so their elapsed time is that kernel's execution; the pair is then
+ * cleared. Both NULL clears a pending pair. The caller owns the events. Errors: WBMM_E_INVALID
+ * when exactly one of the two is NULL.
  */
 wbmm_status wbmm_set_launch_events(void* before, void* after);
 

@@ -224,5 +224,6 @@ def wbmm_backward(x, dy, w: int, T=None, M=None, mix_w=None, z_saved=None, *, la
 
 
 def wbmm_set_launch_events(before, after):
-    """Bracket the next forward/backward call's main kernel with two HIP events (raw handles)."""
+    """Attach two HIP events (raw handles) to the dispatch of the next forward/backward call's
+    main kernel: their elapsed time is that kernel's execution."""
     _check(_lib().wbmm_set_launch_events(before, after))

@@ -71,13 +71,10 @@ wbmm_status check_map(int B, int C, int H, int W, int w, int layout) {
 }  // namespace
 
 namespace wbmm {
-void mark_main_kernel(hipStream_t st, bool before) {
-  if (before) {
-    if (g_ev_before) (void)hipEventRecord(g_ev_before, st);
-  } else if (g_ev_after) {
-    (void)hipEventRecord(g_ev_after, st);
-    g_ev_before = g_ev_after = nullptr;  // one call only
-  }
+void take_main_events(hipEvent_t* before, hipEvent_t* after) {
+  *before = g_ev_before;
+  *after = g_ev_after;
+  g_ev_before = g_ev_after = nullptr;  // one call only
 }
 }  // namespace wbmm
 

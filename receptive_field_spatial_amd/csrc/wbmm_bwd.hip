@@ -235,11 +235,7 @@ static hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t st) {
   hipError_t e = hipFuncSetAttribute((const void*)fn, hipFuncAttributeMaxDynamicSharedMemorySize,
                                      a.g.lds_total);
   if (e != hipSuccess) return e;
-  mark_main_kernel(st, true);
-  hipLaunchKernelGGL(fn, dim3(a.g.col_groups, a.g.C, 1), dim3(kThreads), a.g.lds_total, st, a);
-  e = hipGetLastError();
-  mark_main_kernel(st, false);
-  return e;
+  return launch_main(fn, dim3(a.g.col_groups, a.g.C, 1), dim3(kThreads), a.g.lds_total, st, a);
 }
 
 template <int ASRC>

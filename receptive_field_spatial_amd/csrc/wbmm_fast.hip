@@ -778,11 +778,7 @@ hipError_t launch_ws(Fn fn, int lds, FastArgs a, hipStream_t st) {
   const int grid = units < cus ? units : cus;
   hipError_t e = hipFuncSetAttribute((const void*)fn, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
   if (e != hipSuccess) return e;
-  mark_main_kernel(st, true);
-  hipLaunchKernelGGL(fn, dim3(grid), dim3(kWsThreads), lds, st, a);
-  e = hipGetLastError();
-  mark_main_kernel(st, false);
-  return e;
+  return launch_main(fn, dim3(grid), dim3(kWsThreads), lds, st, a);
 }
 
 using S14 = Shape<14, 14, 14>;
@@ -802,11 +798,7 @@ hipError_t launch_ls(Fn fn, int lds, FastArgs a, hipStream_t st) {
   const int units = a.C * a.groups;
   hipError_t e = hipFuncSetAttribute((const void*)fn, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
   if (e != hipSuccess) return e;
-  mark_main_kernel(st, true);
-  hipLaunchKernelGGL(fn, dim3(units), dim3(kThreads), lds, st, a);
-  e = hipGetLastError();
-  mark_main_kernel(st, false);
-  return e;
+  return launch_main(fn, dim3(units), dim3(kThreads), lds, st, a);
 }
 
 }  // namespace

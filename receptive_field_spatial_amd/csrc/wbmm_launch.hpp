@@ -2,6 +2,7 @@
 // Everything here assumes arguments already validated by the API layer.
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stddef.h>
 #include <stdint.h>
@@ -65,9 +66,22 @@ hipError_t launch_forward_fast_bf16(const FwdRequest& r, hipStream_t st);
 hipError_t launch_bwd_reduce(const double* partT, const double* partW, int parts, int C, int L,
                              float* dT, float* dmixw, hipStream_t st);
 
-// Records the caller's timing events (if any were set for this thread) right before (before =
-// true) or right after the launch of a call's main contraction kernel.
-void mark_main_kernel(hipStream_t st, bool before);
+// Hands out the caller's timing events (null if none were set for this thread); a pair is used
+// by one launch only.
+void take_main_events(hipEvent_t* before, hipEvent_t* after);
+
+// Launches a call's main contraction kernel. Timing events armed by the caller are attached to
+// the dispatch itself, so they time the kernel's execution rather than the queue around it.
+template <class K, class... A>
+hipError_t launch_main(K kernel, dim3 grid, dim3 block, unsigned lds, hipStream_t st, A... args) {
+  hipEvent_t before = nullptr, after = nullptr;
+  take_main_events(&before, &after);
+  if (before)
+    hipExtLaunchKernelGGL(kernel, grid, block, lds, st, before, after, 0, args...);
+  else
+    hipLaunchKernelGGL(kernel, grid, block, lds, st, args...);
+  return hipGetLastError();
+}
 
 // 3x3 depthwise mix kernels (used by the window-mode paths).
 hipError_t launch_mix_fwd(const float* z, const float* w9, void* y, int out_bf16, int B, int C,
