@@ -35,6 +35,9 @@ typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
 // 16- and 8-byte accesses at 4-byte alignment (window rows start at even 28-byte offsets)
 typedef uint32_t u32x4a __attribute__((ext_vector_type(4), aligned(4)));
 typedef uint32_t u32x2a __attribute__((ext_vector_type(2), aligned(4)));
+// 8-byte stores at 2-byte alignment (w = 7 window rows start at 14-byte offsets); the HSA
+// runtime runs global memory in unaligned-access mode
+typedef uint32_t u32x2a2 __attribute__((ext_vector_type(2), aligned(2)));
 
 struct BfArgs {
   int B, C;
@@ -83,6 +86,35 @@ __device__ __forceinline__ UnitPos unit_pos(const BfArgs& a, int u, int ipu) {
   p.img0 = (u - p.c * a.groups) * ipu;
   p.nimg = min(a.B - p.img0, ipu);
   return p;
+}
+
+// Stages channel c's table into LDS as 8 copies of the reversed table with rows padded to pitch
+// TP, copy r shifted by r entries: copy r holds Rv[q] = Tpad[PT-1-q] at q + r, so an 8-entry run
+// of Rv that starts at q is one aligned 16-byte read from copy (-q) & 7. Entries q >= CS - 7 lie
+// past every read; threads past CS - 8 repeat entry CS - 8 (same value to the same places), so
+// every write is unconditional. All threads of the workgroup take part.
+template <class S>
+__device__ __forceinline__ void stage_table(uint16_t* copies, const uint16_t* T, int c) {
+  constexpr int NQ = (S::CS + kThreads - 1) / kThreads;
+  uint16_t tv[NQ];
+  const uint16_t* Tc = T + (size_t)c * S::L1 * S::L1;
+#pragma unroll
+  for (int j = 0; j < NQ; ++j) {
+    const int q = min((int)threadIdx.x + j * kThreads, S::CS - 8);
+    const int p = S::PT - 1 - q;  // padded table index
+    const bool in = p >= 0 && (p % S::TP) < S::L1;
+    const int ti = in ? (p / S::TP) * S::L1 + (p % S::TP) : 0;
+    tv[j] = Tc[ti];
+    if (!in) tv[j] = 0;
+  }
+  __syncthreads();  // every wave is done with the previous copies
+#pragma unroll
+  for (int j = 0; j < NQ; ++j) {
+    const int q = min((int)threadIdx.x + j * kThreads, S::CS - 8);
+#pragma unroll
+    for (int r = 0; r < 8; ++r) copies[r * S::CS + q + r] = tv[j];
+  }
+  __syncthreads();
 }
 
 // Persistent: workgroup g walks the units [g*units/grid, (g+1)*units/grid) (a run of consecutive
@@ -147,30 +179,8 @@ k_fwd_bf16(BfArgs a) {
   // conditional (a conditional load makes the wait counting fall back to waiting for all).
   auto unit = [&](auto more, const UnitPos& pos, int u_next, u32x4 (&into)[7],
                   const u32x4 (&conv)[7]) {
-    if (pos.c != table_c) {  // uniform: rebuild the 8 reversed, shifted, padded table copies
-      constexpr int NQ = (S::CS + kThreads - 1) / kThreads;
-      uint16_t tv[NQ];
-      const uint16_t* Tc = a.T + (size_t)pos.c * S::L1 * S::L1;
-      // entries q >= CS - 7 lie past every read; threads past CS - 8 repeat entry CS - 8 (same
-      // value to the same places), so every write is unconditional
-#pragma unroll
-      for (int j = 0; j < NQ; ++j) {
-        const int q = min((int)threadIdx.x + j * kThreads, S::CS - 8);
-        const int p = S::PT - 1 - q;  // padded table index
-        const bool in = p >= 0 && (p & (S::TP - 1)) < S::L1;
-        const int ti = in ? (p / S::TP) * S::L1 + (p & (S::TP - 1)) : 0;
-        tv[j] = Tc[ti];
-        if (!in) tv[j] = 0;
-      }
-      __syncthreads();  // every wave is done with the previous copies
-      // copy r holds Rv[q] at q + r
-#pragma unroll
-      for (int j = 0; j < NQ; ++j) {
-        const int q = min((int)threadIdx.x + j * kThreads, S::CS - 8);
-#pragma unroll
-        for (int r = 0; r < 8; ++r) copies[r * S::CS + q + r] = tv[j];
-      }
-      __syncthreads();
+    if (pos.c != table_c) {  // uniform over the workgroup
+      stage_table<S>(copies, a.T, pos.c);
       table_c = pos.c;
     }
     constexpr bool MORE = decltype(more)::value;
@@ -226,12 +236,141 @@ k_fwd_bf16(BfArgs a) {
   unit(kLast, p, u1, raw, raw);
 }
 
-enum BfShapeId { BF_NONE, BF_28, BF_56 };
+
+// ---------------------------------------------------------------------------------- w = 7
+// w = 7 on 56x56 images: 64 windows per image, 49 pixels per window. A wave takes one whole
+// image of a unit (the 4 waves of a workgroup take 4 consecutive images of a channel) as 4
+// wave-units of 16 windows (two window rows). Window rows are padded to 8 pixels, so K = 64 is
+// 2 steps of 32 and lane group g feeds window row 4s + g at step s (row 7 is padding, zero).
+// Output tiles are two window rows: MFMA rows 0..7 are pixels 0, 1, 2, 3, 3, 4, 5, 6 of row 2t,
+// rows 8..15 the same of row 2t + 1 (row 7 of the last tile repeats row 6), so a lane's four
+// accumulators are 4 consecutive pixels of one window row, stored as one 8-byte store (pixel 3
+// twice, same value). The table operand of the 4 tiles x 2 steps is the same for every window:
+// 8 registers of 16 bytes read from the staged table once per channel, so the steady state uses
+// no LDS at all.
+template <int IW_>
+struct Bf7Shape {
+  static constexpr int WS = 7, IH = IW_, IW = IW_;
+  static constexpr int L1 = 2 * WS - 1;
+  static constexpr int PLANE = IH * IW;
+  static constexpr int IPW = 1;                    // images per wave (per unit)
+  static constexpr int TP = 16;                    // padded table row pitch
+  static constexpr int PT = L1 * TP;               // padded table entries
+  static constexpr int CS = 240;                   // bf16 per shifted copy
+  static constexpr int C0 = PT - 1 - (WS - 1) * TP - (WS - 1);
+  static_assert(IW == 56, "shape");
+  // the last entry any table run reads (pixel (0, 0), window row 7, shift 7) lies within what
+  // stage_table writes
+  static_assert(CS % 8 == 0 && C0 + TP * 7 + 7 + 7 <= CS - 8, "copies");
+};
+
+template <class S, bool ZS>
+__global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWgPerCu, 8)))
+k_fwd_bf16_w7(BfArgs a) {
+  extern __shared__ __attribute__((aligned(16))) uint16_t smem_h[];
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  uint16_t* copies = smem_h;  // [8][CS]
+  const int units = a.C * a.groups;
+  const int u0 = (int)((long long)blockIdx.x * units / gridDim.x);
+  const int u1 = (int)((long long)(blockIdx.x + 1) * units / gridDim.x);
+  if (u0 >= u1) return;  // uniform over the workgroup
+  constexpr int IPU = 4 * S::IPW;
+
+  // lane (n, g): MFMA column n = window (n >> 3, n & 7) of the wave-unit's two window rows, MFMA
+  // row n = pixel slot n of the tile; lane group g = K block (window row 4s + g) and output slots
+  // 4g .. 4g + 3 = window row 2t + (g >> 1), pixels 3 (g & 1) .. + 3
+  const int n = lane & 15, g = lane >> 4;
+  const int wyl = n >> 3, wx = n & 7;
+  // window rows start at 14-byte offsets: load 16 bytes from the 4-byte-aligned pixel
+  // 7wx - (wx & 1) (inside the image row) and shift odd windows down by one pixel
+  const bool odd = (wx & 1) != 0;
+  const int px0 = 7 * wx - (wx & 1);
+  const int xo0 = (7 * wyl + g) * S::IW + px0;
+  const int xo1 = (7 * wyl + min(4 + g, S::WS - 1)) * S::IW + px0;  // row 7: padding
+  const bool pad1 = g == 3;
+  const int so = (7 * wyl + (g >> 1)) * S::IW + 7 * wx + 3 * (g & 1);  // tiles t < 3: + 2t rows
+  const int so3 = (7 * wyl + S::WS - 1) * S::IW + 7 * wx + 3 * (g & 1);  // tile 3: row 6
+  const int xs = n & 7, xi = xs < 4 ? xs : xs - 1;
+  const int im = wave * S::IPW;
+
+  auto plane = [&](const UnitPos& p) {
+    const int ic = min(im, p.nimg - 1);  // images past the batch read and write its last image
+    return ((size_t)(p.img0 + ic) * a.C + p.c) * S::PLANE;
+  };
+  u32x4 raw[4][2];
+  auto issue = [&](const UnitPos& p, int q) {
+    const uint16_t* src = a.x + plane(p) + 2 * S::WS * q * S::IW;
+    raw[q][0] = *(const u32x4a*)(src + xo0);
+    raw[q][1] = *(const u32x4a*)(src + xo1);
+  };
+  auto operand = [&](const u32x4& in, bool zero) {
+    u32x4 o;
+    o.x = odd ? __builtin_amdgcn_alignbyte(in.y, in.x, 2) : in.x;
+    o.y = odd ? __builtin_amdgcn_alignbyte(in.z, in.y, 2) : in.y;
+    o.z = odd ? __builtin_amdgcn_alignbyte(in.w, in.z, 2) : in.z;
+    o.w = odd ? in.w >> 16 : in.w & 0xffffu;  // pixel slot 7 is padding
+    if (zero) o = u32x4{0u, 0u, 0u, 0u};
+    return o;
+  };
+
+  u32x4 mvr[4][2];
+  int table_c = -1;
+  auto unit = [&](auto more, const UnitPos& pos, int u_next) {
+    constexpr bool MORE = decltype(more)::value;
+    if (pos.c != table_c) {  // uniform over the workgroup
+      stage_table<S>(copies, a.T, pos.c);
+      table_c = pos.c;
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        const int yi = min(2 * t + (n >> 3), S::WS - 1);
+        const int bi = S::C0 - S::TP * yi - xi;
+        const int rc = (-bi) & 7;
+#pragma unroll
+        for (int s2 = 0; s2 < 2; ++s2)
+          mvr[t][s2] = *(const u32x4*)(copies + rc * S::CS + bi + rc + S::TP * (4 * s2 + g));
+      }
+    }
+    const UnitPos nxt = unit_pos(a, u_next < u1 ? u_next : u1 - 1, IPU);
+    const size_t obase = plane(pos);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const u32x4 op0 = operand(raw[q][0], false), op1 = operand(raw[q][1], pad1);
+      if constexpr (MORE) issue(nxt, q);  // wave-unit q of the next unit
+      v4f acc[4];
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        acc[t] = mfma_bf16(mvr[t][0], op0, v4f{0.f, 0.f, 0.f, 0.f});
+        acc[t] = mfma_bf16(mvr[t][1], op1, acc[t]);
+      }
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        const uint32_t lo = __builtin_bit_cast(uint32_t, __builtin_convertvector((v2f{acc[t][0], acc[t][1]}), v2bf));
+        const uint32_t hi = __builtin_bit_cast(uint32_t, __builtin_convertvector((v2f{acc[t][2], acc[t][3]}), v2bf));
+        const size_t o = obase + 2 * S::WS * q * S::IW + (t < 3 ? so + 2 * t * S::IW : so3);
+        *(u32x2a2*)(a.y + o) = u32x2a2{lo, hi};
+        if constexpr (ZS) *(u32x2a2*)(a.z + o) = u32x2a2{lo, hi};
+      }
+    }
+    return nxt;
+  };
+  constexpr std::true_type kMore{};
+  constexpr std::false_type kLast{};
+
+  UnitPos p = unit_pos(a, u0, IPU);
+#pragma unroll
+  for (int q = 0; q < 4; ++q) issue(p, q);
+  for (int u = u0; u + 1 < u1; ++u) p = unit(kMore, p, u + 1);
+  unit(kLast, p, u1);
+}
+
+enum BfShapeId { BF_NONE, BF_28, BF_56, BF7_56 };
 
 BfShapeId bf_shape(const FwdRequest& r) {
-  if (r.layout != 0 || r.w != 14 || r.H != r.W) return BF_NONE;
-  if (r.H == 28) return BF_28;
-  if (r.H == 56) return BF_56;
+  if (r.layout != 0 || r.H != r.W) return BF_NONE;
+  if (r.w == 14 && r.H == 28) return BF_28;
+  if (r.w == 14 && r.H == 56) return BF_56;
+  if (r.w == 7 && r.H == 56) return BF7_56;
   return BF_NONE;
 }
 
@@ -239,11 +378,12 @@ constexpr int kLdsPerCu = 160 * 1024, kLdsGranule = 1280;
 constexpr bool fits(int bytes) {
   return (bytes + kLdsGranule - 1) / kLdsGranule * kLdsGranule * kWgPerCu <= kLdsPerCu;
 }
-static_assert(fits(bf_lds_bytes<BfShape<28>>()) && fits(bf_lds_bytes<BfShape<56>>()),
+static_assert(fits(bf_lds_bytes<BfShape<28>>()) && fits(bf_lds_bytes<BfShape<56>>()) &&
+                  fits(bf_lds_bytes<Bf7Shape<56>>()),
               "resident workgroups per CU");
 
-template <class S>
-hipError_t launch_bf(const FwdRequest& r, hipStream_t st) {
+template <class S, class K>
+hipError_t launch_bf(const FwdRequest& r, hipStream_t st, K with_z, K without_z) {
   BfArgs a{};
   a.B = r.B;
   a.C = r.C;
@@ -253,8 +393,8 @@ hipError_t launch_bf(const FwdRequest& r, hipStream_t st) {
   a.y = (uint16_t*)r.y;
   a.z = (uint16_t*)r.zsave;
   const int lds = bf_lds_bytes<S>();
-  const void* fn = a.z ? (const void*)k_fwd_bf16<S, true> : (const void*)k_fwd_bf16<S, false>;
-  hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+  const K fn = a.z ? with_z : without_z;
+  hipError_t e = hipFuncSetAttribute((const void*)fn, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
   if (e != hipSuccess) return e;
   int dev = 0, cus = 256;
   if (hipGetDevice(&dev) != hipSuccess ||
@@ -262,8 +402,7 @@ hipError_t launch_bf(const FwdRequest& r, hipStream_t st) {
     cus = 256;
   const int units = a.C * a.groups;
   const int grid = units < kWgPerCu * cus ? units : kWgPerCu * cus;
-  return a.z ? launch_main(k_fwd_bf16<S, true>, dim3(grid), dim3(kThreads), lds, st, a)
-             : launch_main(k_fwd_bf16<S, false>, dim3(grid), dim3(kThreads), lds, st, a);
+  return launch_main(fn, dim3(grid), dim3(kThreads), lds, st, a);
 }
 
 }  // namespace
@@ -276,8 +415,10 @@ bool fast_bf16_forward_ok(const FwdRequest& r) {
 
 hipError_t launch_forward_fast_bf16(const FwdRequest& r, hipStream_t st) {
   switch (bf_shape(r)) {
-    case BF_28: return launch_bf<BfShape<28>>(r, st);
-    case BF_56: return launch_bf<BfShape<56>>(r, st);
+    case BF_28: return launch_bf<BfShape<28>>(r, st, k_fwd_bf16<BfShape<28>, true>, k_fwd_bf16<BfShape<28>, false>);
+    case BF_56: return launch_bf<BfShape<56>>(r, st, k_fwd_bf16<BfShape<56>, true>, k_fwd_bf16<BfShape<56>, false>);
+    case BF7_56:
+      return launch_bf<Bf7Shape<56>>(r, st, k_fwd_bf16_w7<Bf7Shape<56>, true>, k_fwd_bf16_w7<Bf7Shape<56>, false>);
     default: return hipErrorInvalidValue;
   }
 }

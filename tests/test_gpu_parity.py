@@ -222,16 +222,18 @@ def test_forward_bf16(w, cached, out):
         assert_f32(host(y), want, "y (fp32 out)")
 
 
-@pytest.mark.parametrize("hw,B", [(14, 3), (28, 5), (28, 16), (28, 33), (56, 3), (56, 6), (56, 9)])
+@pytest.mark.parametrize("w,hw,B", [(14, 14, 3), (14, 28, 5), (14, 28, 16), (14, 28, 33), (14, 56, 3),
+                                    (14, 56, 6), (14, 56, 9), (7, 56, 3), (7, 56, 4), (7, 56, 9)])
 @pytest.mark.parametrize("zsave", [False, True])
-def test_forward_bf16_fast(hw, B, zsave):
-    """w = 14 bf16 fast path (square NCHW 28x28 and 56x56 images, table, bf16 output; 14x14 goes
-    the general way): batches that fill whole units and ragged ones; z_save equals y bit for bit
-    (no mix)."""
-    w, C = 14, 3
-    say(f"forward bf16 fast w=14 {hw}x{hw} B={B} C={C} zsave={zsave}")
+def test_forward_bf16_fast(w, hw, B, zsave):
+    """bf16 fast paths (w = 14 on square NCHW 28x28 and 56x56 images, w = 7 on 56x56; table,
+    bf16 output; 14x14 goes the general way): batches that fill whole units and ragged ones;
+    z_save equals y bit for bit (no mix)."""
+    C = 3
+    L1 = 2 * w - 1
+    say(f"forward bf16 fast w={w} {hw}x{hw} B={B} C={C} zsave={zsave}")
     x = synth.round_to_bf16(synth.normal_f32((B, C, hw, hw), 1.0, seed=31))
-    T = synth.round_to_bf16(synth.normal_f32((C, 27, 27), 0.02, seed=32))
+    T = synth.round_to_bf16(synth.normal_f32((C, L1, L1), 0.02, seed=32))
     z = torch.empty((B, C, hw, hw), dtype=torch.bfloat16, device="cuda") if zsave else None
     y = R().wbmm_forward(dev_bf16(x), w, T=dev_bf16(T), out_dtype=torch.bfloat16, z_save=z)
     want = O.wbmm_forward(x.astype(np.float64), w, T=T.astype(np.float64))
@@ -240,15 +242,15 @@ def test_forward_bf16_fast(hw, B, zsave):
         assert torch.equal(z.view(torch.int16), y.view(torch.int16))
 
 
-@pytest.mark.parametrize("hw", [14, 28, 56])
-def test_forward_bf16_fast_identity_bitwise(hw):
+@pytest.mark.parametrize("w,hw", [(14, 14), (14, 28), (14, 56), (7, 56)])
+def test_forward_bf16_fast_identity_bitwise(w, hw):
     """One-hot table at the centre: M = I, every product is 1 * x or 0 * x and the bf16 output
     reproduces the bf16 input bit for bit (pins the fast path's operand placement)."""
-    w, B, C = 14, 4, 2
-    say(f"forward bf16 fast identity {hw}x{hw}")
+    B, C = 4, 2
+    say(f"forward bf16 fast identity w={w} {hw}x{hw}")
     x = synth.round_to_bf16(synth.normal_f32((B, C, hw, hw), 1.0, seed=33))
-    T = np.zeros((C, 27, 27), np.float32)
-    T[:, 13, 13] = 1.0
+    T = np.zeros((C, 2 * w - 1, 2 * w - 1), np.float32)
+    T[:, w - 1, w - 1] = 1.0
     y = R().wbmm_forward(dev_bf16(x), w, T=dev_bf16(T), out_dtype=torch.bfloat16)
     assert np.array_equal(host(y), x)
 
@@ -267,18 +269,19 @@ def _window_shift(x, w, dy, dx):
     return out
 
 
-@pytest.mark.parametrize("hw,B,C", [(56, 4, 800), (56, 7, 300), (28, 16, 1100)])
-def test_forward_bf16_fast_shift_bitwise(hw, B, C):
+@pytest.mark.parametrize("w,hw,B,C", [(14, 56, 4, 800), (14, 56, 7, 300), (14, 28, 16, 1100),
+                                      (7, 56, 4, 900), (7, 56, 5, 300)])
+def test_forward_bf16_fast_shift_bitwise(w, hw, B, C):
     """One-hot tables at a different offset in every channel: the output is the input shifted
     inside each window (exact in bf16). More units than resident workgroups, so workgroups walk
     several units and rebuild the staged table when the channel changes."""
-    w = 14
-    say(f"forward bf16 fast shift {hw}x{hw} B={B} C={C}")
+    say(f"forward bf16 fast shift w={w} {hw}x{hw} B={B} C={C}")
     x = synth.round_to_bf16(synth.normal_f32((B, C, hw, hw), 1.0, seed=34))
-    dy = (np.arange(C) * 5) % 27 - 13
-    dx = (np.arange(C) * 11 + 3) % 27 - 13
-    T = np.zeros((C, 27, 27), np.float32)
-    T[np.arange(C), dy + 13, dx + 13] = 1.0
+    L1 = 2 * w - 1
+    dy = (np.arange(C) * 5) % L1 - (w - 1)
+    dx = (np.arange(C) * 11 + 3) % L1 - (w - 1)
+    T = np.zeros((C, L1, L1), np.float32)
+    T[np.arange(C), dy + w - 1, dx + w - 1] = 1.0
     y = R().wbmm_forward(dev_bf16(x), w, T=dev_bf16(T), out_dtype=torch.bfloat16)
     assert np.array_equal(host(y), _window_shift(x, w, dy, dx))
 
