@@ -93,14 +93,14 @@ __device__ __forceinline__ UnitPos unit_pos(const BfArgs& a, int u, int ipu) {
 // of Rv that starts at q is one aligned 16-byte read from copy (-q) & 7. Entries q >= CS - 7 lie
 // past every read; threads past CS - 8 repeat entry CS - 8 (same value to the same places), so
 // every write is unconditional. All threads of the workgroup take part.
-template <class S>
+template <class S, int NTH = kThreads>
 __device__ __forceinline__ void stage_table(uint16_t* copies, const uint16_t* T, int c) {
-  constexpr int NQ = (S::CS + kThreads - 1) / kThreads;
+  constexpr int NQ = (S::CS + NTH - 1) / NTH;
   uint16_t tv[NQ];
   const uint16_t* Tc = T + (size_t)c * S::L1 * S::L1;
 #pragma unroll
   for (int j = 0; j < NQ; ++j) {
-    const int q = min((int)threadIdx.x + j * kThreads, S::CS - 8);
+    const int q = min((int)threadIdx.x + j * NTH, S::CS - 8);
     const int p = S::PT - 1 - q;  // padded table index
     const bool in = p >= 0 && (p % S::TP) < S::L1;
     const int ti = in ? (p / S::TP) * S::L1 + (p % S::TP) : 0;
@@ -110,7 +110,7 @@ __device__ __forceinline__ void stage_table(uint16_t* copies, const uint16_t* T,
   __syncthreads();  // every wave is done with the previous copies
 #pragma unroll
   for (int j = 0; j < NQ; ++j) {
-    const int q = min((int)threadIdx.x + j * kThreads, S::CS - 8);
+    const int q = min((int)threadIdx.x + j * NTH, S::CS - 8);
 #pragma unroll
     for (int r = 0; r < 8; ++r) copies[r * S::CS + q + r] = tv[j];
   }
@@ -364,13 +364,168 @@ k_fwd_bf16_w7(BfArgs a) {
   unit(kLast, p, u1);
 }
 
-enum BfShapeId { BF_NONE, BF_28, BF_56, BF7_56 };
+// --------------------------------------------------------------------------------- w = 28
+// w = 28 on 56x56 images: 4 windows of 784 pixels per image, so a channel is a 784 x 784 by
+// 784 x (4B) product and the work is matrix-bound. One workgroup of 8 waves per CU takes a block
+// of 64 windows (16 images) of one channel and computes all 784 output pixels for them with
+// v_mfma_f32_32x32x16_bf16 (32 pixels x 32 windows x 16 K per instruction):
+//   * output tiles are window rows (32 MFMA rows: pixels 0..27, then 24..27 again), 28 tiles x
+//     2 window tiles; the two waves of a SIMD share its 7 window rows (4 and 3 rows, both
+//     window tiles), so every SIMD does the same matrix work;
+//   * K is walked window row by window row (rows padded to 32 pixels: 2 K steps of 16);
+//   * table operand: the staged, reversed, shifted table copies (pitch 64), one aligned 16-byte
+//     LDS read per row tile and K step, base + immediates;
+//   * window operand: window rows stream through a double-buffered LDS chunk (2 window rows of
+//     the 64 windows, rows padded with zeros), loaded two chunks ahead into registers (one
+//     16-byte load and one 16-byte LDS write per thread and chunk); one LDS read per window
+//     tile and K step;
+//   * accumulators leave as 4 consecutive pixels of a window row: 8-byte stores.
+template <int IW_>
+struct Bf28Shape {
+  static constexpr int WS = 28, IH = IW_, IW = IW_;
+  static constexpr int L1 = 2 * WS - 1;
+  static constexpr int PLANE = IH * IW;
+  static constexpr int TP = 64;                    // padded table row pitch
+  static constexpr int PT = L1 * TP;
+  static constexpr int CS = 3544;
+  static constexpr int C0 = PT - 1 - (WS - 1) * TP - (WS - 1);
+  static constexpr int NWB = 64;                   // windows per block (16 images)
+  static constexpr int IPB = NWB / 4;              // images per block
+  static constexpr int RC = 2;                     // window rows per chunk
+  static constexpr int NCH = WS / RC;              // chunks
+  static constexpr int XWP = RC * 32 + 8;          // bf16 per window in a chunk buffer (+16 B)
+  static constexpr int XBUF = NWB * XWP;           // bf16 per chunk buffer
+  static constexpr int NTH = 512;                  // threads per workgroup
+  static_assert(IW == 56, "shape");
+  // the last entry a table run reads (pixel (0, 0), window row 27, pixels 24..31, shift 7)
+  static_assert(CS % 8 == 0 && C0 + TP * (WS - 1) + 24 + 7 + 7 <= CS - 8, "copies");
+  static_assert(NWB * RC * 4 == NTH, "one chunk load per thread");
+};
+
+template <class S>
+constexpr int bf28_lds_bytes() { return (8 * S::CS + 2 * S::XBUF) * 2; }
+
+typedef float v16f __attribute__((ext_vector_type(16)));
+
+__device__ __forceinline__ v16f mfma32_bf16(u32x4 a, u32x4 b, v16f c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(v8bf, a),
+                                                 __builtin_bit_cast(v8bf, b), c, 0, 0, 0);
+}
+
+template <class S, bool ZS>
+__global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
+k_fwd_bf16_w28(BfArgs a) {
+  extern __shared__ __attribute__((aligned(16))) uint16_t smem_h[];
+  uint16_t* copies = smem_h;                  // [8][CS]
+  uint16_t* xbuf = smem_h + 8 * S::CS;        // [2][NWB][XWP]
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  const int c = blockIdx.x / a.groups;
+  const int img0 = (blockIdx.x - c * a.groups) * S::IPB;
+  const int nimg = min(a.B - img0, S::IPB);
+  // element offset of the plane of image im of the block (images past the batch read and write
+  // its last image: same values)
+  auto plane = [&](int im) { return ((size_t)(img0 + min(im, nimg - 1)) * a.C + c) * S::PLANE; };
+
+  // chunk loads: thread -> window jw, chunk row r, 8-pixel segment k (segment 3 loads pixels
+  // 20..27 and keeps 24..27, padding 28..31 with zeros, so no load leaves the window row)
+  const int tid = threadIdx.x;
+  const int jw = tid >> 3, r_ld = (tid >> 2) & 1, k_ld = tid & 3;
+  const size_t ld_base = plane(jw >> 2) + (size_t)(S::WS * ((jw >> 1) & 1) + r_ld) * S::IW +
+                         S::WS * (jw & 1) + (k_ld < 3 ? 8 * k_ld : 20);
+  const int st_off = jw * S::XWP + r_ld * 32 + 8 * k_ld;
+  auto load_chunk = [&](int ch) {
+    return *(const u32x4a*)(a.x + ld_base + (size_t)(S::RC * ch) * S::IW);
+  };
+  auto store_chunk = [&](const u32x4& v, int buf) {
+    const u32x4 w = k_ld < 3 ? v : u32x4{v.z, v.w, 0u, 0u};
+    *(u32x4*)(xbuf + buf * S::XBUF + st_off) = w;
+  };
+
+  u32x4 pre0 = load_chunk(0), pre1 = load_chunk(1);
+  stage_table<S, S::NTH>(copies, a.T, c);  // ends with a barrier
+  store_chunk(pre0, 0);
+  __syncthreads();
+
+  // lane (l32, kh): MFMA row l32 = pixel slot, column l32 = window of the tile, K half kh
+  const int l32 = lane & 31, kh = lane >> 5;
+  const int xi = l32 < S::WS ? l32 : l32 - 4;  // slots 28..31 repeat pixels 24..27
+  const int bi0 = S::C0 - xi;
+  const int rc = (-bi0) & 7;
+  const int simd = wave & 3, hi = wave >> 2;
+  const int t0 = 7 * simd + (hi ? 4 : 0);     // first window row (output tile) of this wave
+  // table run of output row yi, K window row yk, K half hs: ab + TP (yk - yi) + 16 hs
+  const int ab = rc * S::CS + bi0 + rc + 8 * kh - S::TP * t0;
+  const int xb = l32 * S::XWP + 8 * kh;       // window tile ct adds 32 XWP
+
+  auto body = [&](auto ntc) {
+    constexpr int NT = decltype(ntc)::value;
+    v16f acc[NT][2];
+#pragma unroll
+    for (int t = 0; t < NT; ++t)
+#pragma unroll
+      for (int ct = 0; ct < 2; ++ct)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) acc[t][ct][e] = 0.f;
+    auto chunk = [&](int ch, int buf, u32x4& pre_next, u32x4& pre_after) {
+      // pixels of chunk ch + 2 in flight (the last chunks re-read chunk NCH - 1)
+      pre_after = load_chunk(min(ch + 2, S::NCH - 1));
+      const uint16_t* xs = xbuf + buf * S::XBUF + xb;
+      const uint16_t* as = copies + ab + S::TP * (S::RC * ch);
+#pragma unroll
+      for (int r = 0; r < S::RC; ++r)
+#pragma unroll
+        for (int hs = 0; hs < 2; ++hs) {
+          u32x4 bv[2], av[NT];
+#pragma unroll
+          for (int ct = 0; ct < 2; ++ct) bv[ct] = *(const u32x4*)(xs + ct * 32 * S::XWP + r * 32 + 16 * hs);
+#pragma unroll
+          for (int t = 0; t < NT; ++t) av[t] = *(const u32x4*)(as + S::TP * (r - t) + 16 * hs);
+#pragma unroll
+          for (int t = 0; t < NT; ++t)
+#pragma unroll
+            for (int ct = 0; ct < 2; ++ct) acc[t][ct] = mfma32_bf16(av[t], bv[ct], acc[t][ct]);
+        }
+      // chunk ch + 1 into the other buffer (every wave is past chunk ch - 1, which used it)
+      store_chunk(pre_next, buf ^ 1);
+      __syncthreads();
+    };
+    for (int ch = 0; ch < S::NCH; ch += 2) {
+      chunk(ch, 0, pre1, pre0);
+      chunk(ch + 1, 1, pre0, pre1);
+    }
+    // stores: lane (window l32 of tile ct, kh) holds rows 8g + 4kh .. +3 = 4 consecutive pixels
+    // of its window row (group 3 of the upper half repeats pixels 24..27)
+#pragma unroll
+    for (int ct = 0; ct < 2; ++ct) {
+      const int j = 32 * ct + l32;
+      const size_t ob = plane(j >> 2) + (size_t)(S::WS * ((j >> 1) & 1) + t0) * S::IW + S::WS * (j & 1);
+#pragma unroll
+      for (int t = 0; t < NT; ++t)
+#pragma unroll
+        for (int gi = 0; gi < 4; ++gi) {
+          const v16f& d = acc[t][ct];
+          const uint32_t lo = __builtin_bit_cast(uint32_t, __builtin_convertvector((v2f{d[4 * gi], d[4 * gi + 1]}), v2bf));
+          const uint32_t hi2 = __builtin_bit_cast(uint32_t, __builtin_convertvector((v2f{d[4 * gi + 2], d[4 * gi + 3]}), v2bf));
+          const int px = gi < 3 ? 8 * gi + 4 * kh : 24;
+          const size_t o = ob + (size_t)t * S::IW + px;
+          *(u32x2a*)(a.y + o) = u32x2a{lo, hi2};
+          if constexpr (ZS) *(u32x2a*)(a.z + o) = u32x2a{lo, hi2};
+        }
+    }
+  };
+  if (hi) body(std::integral_constant<int, 3>{});
+  else body(std::integral_constant<int, 4>{});
+}
+
+enum BfShapeId { BF_NONE, BF_28, BF_56, BF7_56, BF28_56 };
 
 BfShapeId bf_shape(const FwdRequest& r) {
   if (r.layout != 0 || r.H != r.W) return BF_NONE;
   if (r.w == 14 && r.H == 28) return BF_28;
   if (r.w == 14 && r.H == 56) return BF_56;
   if (r.w == 7 && r.H == 56) return BF7_56;
+  if (r.w == 28 && r.H == 56) return BF28_56;
   return BF_NONE;
 }
 
@@ -405,6 +560,25 @@ hipError_t launch_bf(const FwdRequest& r, hipStream_t st, K with_z, K without_z)
   return launch_main(fn, dim3(grid), dim3(kThreads), lds, st, a);
 }
 
+// One workgroup of 8 waves per block of 64 windows of a channel.
+template <class S>
+hipError_t launch_bf28(const FwdRequest& r, hipStream_t st) {
+  BfArgs a{};
+  a.B = r.B;
+  a.C = r.C;
+  a.groups = (r.B + S::IPB - 1) / S::IPB;
+  a.x = (const uint16_t*)r.x;
+  a.T = (const uint16_t*)r.T;
+  a.y = (uint16_t*)r.y;
+  a.z = (uint16_t*)r.zsave;
+  const int lds = bf28_lds_bytes<S>();
+  auto fn = a.z ? k_fwd_bf16_w28<S, true> : k_fwd_bf16_w28<S, false>;
+  hipError_t e = hipFuncSetAttribute((const void*)fn, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+  if (e != hipSuccess) return e;
+  return launch_main(fn, dim3(a.C * a.groups), dim3(S::NTH), lds, st, a);
+}
+static_assert(bf28_lds_bytes<Bf28Shape<56>>() <= kLdsPerCu, "w = 28 workgroup LDS");
+
 }  // namespace
 
 bool fast_bf16_forward_ok(const FwdRequest& r) {
@@ -419,6 +593,7 @@ hipError_t launch_forward_fast_bf16(const FwdRequest& r, hipStream_t st) {
     case BF_56: return launch_bf<BfShape<56>>(r, st, k_fwd_bf16<BfShape<56>, true>, k_fwd_bf16<BfShape<56>, false>);
     case BF7_56:
       return launch_bf<Bf7Shape<56>>(r, st, k_fwd_bf16_w7<Bf7Shape<56>, true>, k_fwd_bf16_w7<Bf7Shape<56>, false>);
+    case BF28_56: return launch_bf28<Bf28Shape<56>>(r, st);
     default: return hipErrorInvalidValue;
   }
 }

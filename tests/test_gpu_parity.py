@@ -223,7 +223,8 @@ def test_forward_bf16(w, cached, out):
 
 
 @pytest.mark.parametrize("w,hw,B", [(14, 14, 3), (14, 28, 5), (14, 28, 16), (14, 28, 33), (14, 56, 3),
-                                    (14, 56, 6), (14, 56, 9), (7, 56, 3), (7, 56, 4), (7, 56, 9)])
+                                    (14, 56, 6), (14, 56, 9), (7, 56, 3), (7, 56, 4), (7, 56, 9),
+                                    (28, 56, 3), (28, 56, 16), (28, 56, 21)])
 @pytest.mark.parametrize("zsave", [False, True])
 def test_forward_bf16_fast(w, hw, B, zsave):
     """bf16 fast paths (w = 14 on square NCHW 28x28 and 56x56 images, w = 7 on 56x56; table,
@@ -242,7 +243,7 @@ def test_forward_bf16_fast(w, hw, B, zsave):
         assert torch.equal(z.view(torch.int16), y.view(torch.int16))
 
 
-@pytest.mark.parametrize("w,hw", [(14, 14), (14, 28), (14, 56), (7, 56)])
+@pytest.mark.parametrize("w,hw", [(14, 14), (14, 28), (14, 56), (7, 56), (28, 56)])
 def test_forward_bf16_fast_identity_bitwise(w, hw):
     """One-hot table at the centre: M = I, every product is 1 * x or 0 * x and the bf16 output
     reproduces the bf16 input bit for bit (pins the fast path's operand placement)."""
@@ -270,7 +271,7 @@ def _window_shift(x, w, dy, dx):
 
 
 @pytest.mark.parametrize("w,hw,B,C", [(14, 56, 4, 800), (14, 56, 7, 300), (14, 28, 16, 1100),
-                                      (7, 56, 4, 900), (7, 56, 5, 300)])
+                                      (7, 56, 4, 900), (7, 56, 5, 300), (28, 56, 17, 40)])
 def test_forward_bf16_fast_shift_bitwise(w, hw, B, C):
     """One-hot tables at a different offset in every channel: the output is the input shifted
     inside each window (exact in bf16). More units than resident workgroups, so workgroups walk
