@@ -26,6 +26,7 @@
 #include "wbmm_launch.hpp"
 
 #include <type_traits>
+#include <utility>
 
 namespace wbmm {
 namespace {
@@ -88,33 +89,60 @@ __device__ __forceinline__ UnitPos unit_pos(const BfArgs& a, int u, int ipu) {
   return p;
 }
 
+// A value hidden from the optimizer at this point of the program (it cannot be computed
+// earlier than here).
+__device__ __forceinline__ int opaque(int v) {
+  asm volatile("" : "+v"(v));
+  return v;
+}
+
 // Stages channel c's table into LDS as 8 copies of the reversed table with rows padded to pitch
 // TP, copy r shifted by r entries: copy r holds Rv[q] = Tpad[PT-1-q] at q + r, so an 8-entry run
 // of Rv that starts at q is one aligned 16-byte read from copy (-q) & 7. Entries q >= CS - 7 lie
 // past every read; threads past CS - 8 repeat entry CS - 8 (same value to the same places), so
-// every write is unconditional. All threads of the workgroup take part.
+// every write is unconditional. All threads of the workgroup take part. Split in two so that a
+// caller can put other loads in flight between them: the memory counter completes in order, so
+// waiting for the table entries never waits for loads issued after them.
+template <class S, int NTH>
+struct TableStage {
+  static constexpr int NQ = (S::CS + NTH - 1) / NTH;
+  uint16_t tv[NQ];
+  uint32_t pad;  // bit j: entry j is padding (zero); applied at write time, so that nothing
+                 // waits for the loads before write
+  __device__ __forceinline__ void load(const uint16_t* T, int c) {
+    const uint16_t* Tc = T + (size_t)c * S::L1 * S::L1;
+    // the thread index is made opaque so that the per-entry indices are computed here, not kept
+    // in registers from the kernel's start (a persistent caller stages rarely)
+    const int tid = opaque(threadIdx.x);
+    pad = 0;
+#pragma unroll
+    for (int j = 0; j < NQ; ++j) {
+      const int q = min(tid + j * NTH, S::CS - 8);
+      const int p = S::PT - 1 - q;  // padded table index
+      const bool in = p >= 0 && (p % S::TP) < S::L1;
+      const int ti = in ? (p / S::TP) * S::L1 + (p % S::TP) : 0;
+      tv[j] = Tc[ti];
+      pad |= in ? 0u : 1u << j;
+    }
+  }
+  __device__ __forceinline__ void write(uint16_t* copies) const {
+    __syncthreads();  // every wave is done with the previous copies
+    const int tid = opaque(threadIdx.x);
+#pragma unroll
+    for (int j = 0; j < NQ; ++j) {
+      const int q = min(tid + j * NTH, S::CS - 8);
+      const uint16_t v = (pad >> j) & 1u ? (uint16_t)0 : tv[j];
+#pragma unroll
+      for (int r = 0; r < 8; ++r) copies[r * S::CS + q + r] = v;
+    }
+    __syncthreads();
+  }
+};
 template <class S, int NTH = kThreads>
 __device__ __forceinline__ void stage_table(uint16_t* copies, const uint16_t* T, int c) {
-  constexpr int NQ = (S::CS + NTH - 1) / NTH;
-  uint16_t tv[NQ];
-  const uint16_t* Tc = T + (size_t)c * S::L1 * S::L1;
-#pragma unroll
-  for (int j = 0; j < NQ; ++j) {
-    const int q = min((int)threadIdx.x + j * NTH, S::CS - 8);
-    const int p = S::PT - 1 - q;  // padded table index
-    const bool in = p >= 0 && (p % S::TP) < S::L1;
-    const int ti = in ? (p / S::TP) * S::L1 + (p % S::TP) : 0;
-    tv[j] = Tc[ti];
-    if (!in) tv[j] = 0;
-  }
-  __syncthreads();  // every wave is done with the previous copies
-#pragma unroll
-  for (int j = 0; j < NQ; ++j) {
-    const int q = min((int)threadIdx.x + j * NTH, S::CS - 8);
-#pragma unroll
-    for (int r = 0; r < 8; ++r) copies[r * S::CS + q + r] = tv[j];
-  }
-  __syncthreads();
+  TableStage<S, NTH> ts;
+  ts.load(T, c);
+  ts.write(copies);
 }
 
 // Persistent: workgroup g walks the units [g*units/grid, (g+1)*units/grid) (a run of consecutive
@@ -366,19 +394,19 @@ k_fwd_bf16_w7(BfArgs a) {
 
 // --------------------------------------------------------------------------------- w = 28
 // w = 28 on 56x56 images: 4 windows of 784 pixels per image, so a channel is a 784 x 784 by
-// 784 x (4B) product and the work is matrix-bound. One workgroup of 8 waves per CU takes a block
-// of 64 windows (16 images) of one channel and computes all 784 output pixels for them with
-// v_mfma_f32_32x32x16_bf16 (32 pixels x 32 windows x 16 K per instruction):
-//   * output tiles are window rows (32 MFMA rows: pixels 0..27, then 24..27 again), 28 tiles x
-//     2 window tiles; the two waves of a SIMD share its 7 window rows (4 and 3 rows, both
-//     window tiles), so every SIMD does the same matrix work;
+// 784 x (4B) product and the work is matrix-bound. A workgroup of 4 waves takes a block of 32
+// windows (8 images) of one channel and computes all 784 output pixels for them with
+// v_mfma_f32_32x32x16_bf16 (32 pixels x 32 windows x 16 K per instruction); two workgroups run
+// per CU, so one's end-of-block store burst overlaps the other's matrix work:
+//   * output tiles are window rows (32 MFMA rows: pixels 0..27, then 24..27 again), 28 tiles;
+//     wave k owns window rows 7k .. 7k+6: 7 accumulators of 16 registers;
 //   * K is walked window row by window row (rows padded to 32 pixels: 2 K steps of 16);
 //   * table operand: the staged, reversed, shifted table copies (pitch 64), one aligned 16-byte
-//     LDS read per row tile and K step, base + immediates;
+//     LDS read per operand; the matrix is block Toeplitz in window rows, so a wave's 7 row
+//     tiles need only one new table operand per K step (2 LDS reads per 7 MFMAs);
 //   * window operand: window rows stream through a double-buffered LDS chunk (2 window rows of
-//     the 64 windows, rows padded with zeros), loaded two chunks ahead into registers (one
-//     16-byte load and one 16-byte LDS write per thread and chunk); one LDS read per window
-//     tile and K step;
+//     the 32 windows, rows padded with zeros) with one 16-byte load and LDS write per thread and
+//     chunk; the loads run PF = 7 chunks ahead; one LDS read per K step;
 //   * accumulators leave as 4 consecutive pixels of a window row: 8-byte stores.
 template <int IW_>
 struct Bf28Shape {
@@ -389,21 +417,37 @@ struct Bf28Shape {
   static constexpr int PT = L1 * TP;
   static constexpr int CS = 3544;
   static constexpr int C0 = PT - 1 - (WS - 1) * TP - (WS - 1);
-  static constexpr int NWB = 64;                   // windows per block (16 images)
+  static constexpr int NWB = 32;                   // windows per block (8 images)
   static constexpr int IPB = NWB / 4;              // images per block
   static constexpr int RC = 2;                     // window rows per chunk
   static constexpr int NCH = WS / RC;              // chunks
   static constexpr int XWP = RC * 32 + 8;          // bf16 per window in a chunk buffer (+16 B)
   static constexpr int XBUF = NWB * XWP;           // bf16 per chunk buffer
-  static constexpr int NTH = 512;                  // threads per workgroup
+  static constexpr int NTH = 256;                  // threads per workgroup (two per CU)
+  static constexpr int LPT = NWB * RC * 4 / NTH;   // 16-byte chunk loads per thread
+  static constexpr int PF = 7;                     // chunks in flight
+  static constexpr int NT = WS / 4;                // output row tiles per wave
+  static constexpr int NCT = NWB / 32;             // window tiles
+  static_assert(NCT == 1 && NCH % PF == 0 && NCH % 2 == 0, "block shape");
   static_assert(IW == 56, "shape");
   // the last entry a table run reads (pixel (0, 0), window row 27, pixels 24..31, shift 7)
   static_assert(CS % 8 == 0 && C0 + TP * (WS - 1) + 24 + 7 + 7 <= CS - 8, "copies");
-  static_assert(NWB * RC * 4 == NTH, "one chunk load per thread");
+  static_assert(NWB * RC * 4 == LPT * NTH, "chunk loads per thread");
+  static_assert(NCH >= PF, "chunk ring");
 };
 
 template <class S>
 constexpr int bf28_lds_bytes() { return (8 * S::CS + 2 * S::XBUF) * 2; }
+
+template <class F, int... I>
+__device__ __forceinline__ void static_for_impl(F& f, std::integer_sequence<int, I...>) {
+  (f(std::integral_constant<int, I>{}), ...);
+}
+// f(integral_constant<int, 0>) .. f(integral_constant<int, N-1>), in order
+template <int N, class F>
+__device__ __forceinline__ void static_for(F&& f) {
+  static_for_impl(f, std::make_integer_sequence<int, N>{});
+}
 
 typedef float v16f __attribute__((ext_vector_type(16)));
 
@@ -413,38 +457,69 @@ __device__ __forceinline__ v16f mfma32_bf16(u32x4 a, u32x4 b, v16f c) {
 }
 
 template <class S, bool ZS>
-__global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
 k_fwd_bf16_w28(BfArgs a) {
   extern __shared__ __attribute__((aligned(16))) uint16_t smem_h[];
   uint16_t* copies = smem_h;                  // [8][CS]
   uint16_t* xbuf = smem_h + 8 * S::CS;        // [2][NWB][XWP]
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
-  const int c = blockIdx.x / a.groups;
-  const int img0 = (blockIdx.x - c * a.groups) * S::IPB;
-  const int nimg = min(a.B - img0, S::IPB);
-  // element offset of the plane of image im of the block (images past the batch read and write
-  // its last image: same values)
-  auto plane = [&](int im) { return ((size_t)(img0 + min(im, nimg - 1)) * a.C + c) * S::PLANE; };
+  // persistent: workgroup g walks the blocks [g nb / grid, (g+1) nb / grid); consecutive blocks
+  // mostly share a channel (the table is restaged only when it changes) and the window chunks
+  // run PF ahead across block boundaries
+  const int nb = a.C * a.groups;
+  const int b0 = (int)((long long)blockIdx.x * nb / gridDim.x);
+  const int b1 = (int)((long long)(blockIdx.x + 1) * nb / gridDim.x);
+  if (b0 >= b1) return;  // uniform over the workgroup
+  struct Blk {
+    int c, img0, nimg;
+  };
+  auto blk = [&](int b) {
+    Blk k;
+    k.c = b / a.groups;
+    k.img0 = (b - k.c * a.groups) * S::IPB;
+    k.nimg = min(a.B - k.img0, S::IPB);
+    return k;
+  };
+  // element offset of the plane of image im of block k (images past the batch read and write its
+  // last image: same values)
+  auto plane = [&](const Blk& k, int im) {
+    return ((size_t)(k.img0 + min(im, k.nimg - 1)) * a.C + k.c) * S::PLANE;
+  };
 
   // chunk loads: thread -> window jw, chunk row r, 8-pixel segment k (segment 3 loads pixels
   // 20..27 and keeps 24..27, padding 28..31 with zeros, so no load leaves the window row)
-  const int tid = threadIdx.x;
-  const int jw = tid >> 3, r_ld = (tid >> 2) & 1, k_ld = tid & 3;
-  const size_t ld_base = plane(jw >> 2) + (size_t)(S::WS * ((jw >> 1) & 1) + r_ld) * S::IW +
-                         S::WS * (jw & 1) + (k_ld < 3 ? 8 * k_ld : 20);
+  static_assert(S::LPT == 1, "one chunk load per thread");
+  const int jw = threadIdx.x >> 3, r_ld = (threadIdx.x >> 2) & 1, k_ld = threadIdx.x & 3;
+  const int ld_off = (S::WS * ((jw >> 1) & 1) + r_ld) * S::IW + S::WS * (jw & 1) + (k_ld < 3 ? 8 * k_ld : 20);
   const int st_off = jw * S::XWP + r_ld * 32 + 8 * k_ld;
-  auto load_chunk = [&](int ch) {
-    return *(const u32x4a*)(a.x + ld_base + (size_t)(S::RC * ch) * S::IW);
+  auto ld_base = [&](const Blk& k) { return plane(k, jw >> 2) + ld_off; };
+  auto load_chunk = [&](size_t base, int ch) {
+    return *(const u32x4a*)(a.x + base + (size_t)(S::RC * ch) * S::IW);
   };
   auto store_chunk = [&](const u32x4& v, int buf) {
-    const u32x4 w = k_ld < 3 ? v : u32x4{v.z, v.w, 0u, 0u};
+    // the segment test is made opaque here, so the compiler cannot move the select (and with it
+    // a wait for the load) up to where the load was issued
+    const bool s3 = opaque(k_ld) == 3;
+    const u32x4 w = s3 ? u32x4{v.z, v.w, 0u, 0u} : v;
     *(u32x4*)(xbuf + buf * S::XBUF + st_off) = w;
   };
 
-  u32x4 pre0 = load_chunk(0), pre1 = load_chunk(1);
-  stage_table<S, S::NTH>(copies, a.T, c);  // ends with a barrier
-  store_chunk(pre0, 0);
+  Blk cur = blk(b0);
+  size_t base_cur = ld_base(cur);
+  int table_c = cur.c;
+  u32x4 pre[S::PF];  // chunk k of the stream in slot k % PF
+  {
+    TableStage<S, S::NTH> ts;
+    ts.load(a.T, cur.c);  // before the pixel loads: waiting for it never waits for them
+#pragma unroll
+    for (int k = 0; k < S::PF; ++k) {
+      pre[k] = load_chunk(base_cur, k);
+      __builtin_amdgcn_sched_barrier(0);  // in chunk order: chunk 0's wait is then the shortest
+    }
+    ts.write(copies);  // ends with a barrier
+  }
+  store_chunk(pre[0], 0);
   __syncthreads();
 
   // lane (l32, kh): MFMA row l32 = pixel slot, column l32 = window of the tile, K half kh
@@ -452,59 +527,65 @@ k_fwd_bf16_w28(BfArgs a) {
   const int xi = l32 < S::WS ? l32 : l32 - 4;  // slots 28..31 repeat pixels 24..27
   const int bi0 = S::C0 - xi;
   const int rc = (-bi0) & 7;
-  const int simd = wave & 3, hi = wave >> 2;
-  const int t0 = 7 * simd + (hi ? 4 : 0);     // first window row (output tile) of this wave
+  const int t0 = S::NT * wave;                 // first window row (output tile) of this wave
   // table run of output row yi, K window row yk, K half hs: ab + TP (yk - yi) + 16 hs
   const int ab = rc * S::CS + bi0 + rc + 8 * kh - S::TP * t0;
-  const int xb = l32 * S::XWP + 8 * kh;       // window tile ct adds 32 XWP
+  const int xb = l32 * S::XWP + 8 * kh;
 
-  auto body = [&](auto ntc) {
-    constexpr int NT = decltype(ntc)::value;
-    v16f acc[NT][2];
+  for (int b = b0; b < b1; ++b) {
+    const Blk nxt = blk(b + 1 < b1 ? b + 1 : b);  // the last block's lookahead re-reads itself
+    const size_t base_nxt = ld_base(nxt);
+    if (cur.c != table_c) {  // uniform; every wave is past the previous block's last chunk
+      stage_table<S, S::NTH>(copies, a.T, cur.c);
+      table_c = cur.c;
+    }
+    v16f acc[S::NT];
 #pragma unroll
-    for (int t = 0; t < NT; ++t)
+    for (int t = 0; t < S::NT; ++t)
 #pragma unroll
-      for (int ct = 0; ct < 2; ++ct)
-#pragma unroll
-        for (int e = 0; e < 16; ++e) acc[t][ct][e] = 0.f;
-    auto chunk = [&](int ch, int buf, u32x4& pre_next, u32x4& pre_after) {
-      // pixels of chunk ch + 2 in flight (the last chunks re-read chunk NCH - 1)
-      pre_after = load_chunk(min(ch + 2, S::NCH - 1));
-      const uint16_t* xs = xbuf + buf * S::XBUF + xb;
-      const uint16_t* as = copies + ab + S::TP * (S::RC * ch);
+      for (int e = 0; e < 16; ++e) acc[t][e] = 0.f;
+    // The table operand of output row yi and K window row yk depends only on d = yk - yi (the
+    // matrix is block Toeplitz in window rows): wave rows t0 + t, t < NT, at K row yk use
+    // d - d0 = yk - t with d0 = -t0, so at each K row only tile 0 needs a new operand and the
+    // other tiles take over the operand tile t - 1 used one K row earlier. With the K loop fully
+    // unrolled these are plain registers: areg[yk - t + NT - 1][hs], each live for NT K rows.
+    u32x4 areg[S::WS + S::NT - 1][2];
+    // chunk ch sits in register slot ch % PF and LDS buffer ch % 2 (NCH is a multiple of both):
+    // its slot is free once it is in LDS, so chunk ch + PF of the stream (of this block or the
+    // next) goes in flight there; at the end chunk ch + 1 is written to the other buffer
+    static_for<S::NCH>([&](auto chc) {
+      constexpr int CH = decltype(chc)::value, SL = CH % S::PF, BUF = CH % 2;
+      pre[SL] = CH + S::PF < S::NCH ? load_chunk(base_cur, CH + S::PF)
+                                    : load_chunk(base_nxt, CH + S::PF - S::NCH);
+      const uint16_t* xs = xbuf + BUF * S::XBUF + xb;
 #pragma unroll
       for (int r = 0; r < S::RC; ++r)
 #pragma unroll
         for (int hs = 0; hs < 2; ++hs) {
-          u32x4 bv[2], av[NT];
+          const int yk = S::RC * CH + r;
+          const u32x4 bv = *(const u32x4*)(xs + r * 32 + 16 * hs);
 #pragma unroll
-          for (int ct = 0; ct < 2; ++ct) bv[ct] = *(const u32x4*)(xs + ct * 32 * S::XWP + r * 32 + 16 * hs);
+          for (int t = 0; t < S::NT; ++t)
+            if (t == 0 || yk == 0)  // first use of d = yk - t
+              areg[yk - t + S::NT - 1][hs] = *(const u32x4*)(copies + ab + S::TP * (yk - t) + 16 * hs);
 #pragma unroll
-          for (int t = 0; t < NT; ++t) av[t] = *(const u32x4*)(as + S::TP * (r - t) + 16 * hs);
-#pragma unroll
-          for (int t = 0; t < NT; ++t)
-#pragma unroll
-            for (int ct = 0; ct < 2; ++ct) acc[t][ct] = mfma32_bf16(av[t], bv[ct], acc[t][ct]);
+          for (int t = 0; t < S::NT; ++t)
+            acc[t] = mfma32_bf16(areg[yk - t + S::NT - 1][hs], bv, acc[t]);
         }
       // chunk ch + 1 into the other buffer (every wave is past chunk ch - 1, which used it)
-      store_chunk(pre_next, buf ^ 1);
+      store_chunk(pre[(SL + 1) % S::PF], BUF ^ 1);
       __syncthreads();
-    };
-    for (int ch = 0; ch < S::NCH; ch += 2) {
-      chunk(ch, 0, pre1, pre0);
-      chunk(ch + 1, 1, pre0, pre1);
-    }
-    // stores: lane (window l32 of tile ct, kh) holds rows 8g + 4kh .. +3 = 4 consecutive pixels
-    // of its window row (group 3 of the upper half repeats pixels 24..27)
+    });
+    // stores: lane (window l32, kh) holds rows 8g + 4kh .. +3 = 4 consecutive pixels of its
+    // window row (group 3 of the upper half repeats pixels 24..27)
+    {
+      const int j = l32;
+      const size_t ob = plane(cur, j >> 2) + (size_t)(S::WS * ((j >> 1) & 1) + t0) * S::IW + S::WS * (j & 1);
 #pragma unroll
-    for (int ct = 0; ct < 2; ++ct) {
-      const int j = 32 * ct + l32;
-      const size_t ob = plane(j >> 2) + (size_t)(S::WS * ((j >> 1) & 1) + t0) * S::IW + S::WS * (j & 1);
-#pragma unroll
-      for (int t = 0; t < NT; ++t)
+      for (int t = 0; t < S::NT; ++t)
 #pragma unroll
         for (int gi = 0; gi < 4; ++gi) {
-          const v16f& d = acc[t][ct];
+          const v16f& d = acc[t];
           const uint32_t lo = __builtin_bit_cast(uint32_t, __builtin_convertvector((v2f{d[4 * gi], d[4 * gi + 1]}), v2bf));
           const uint32_t hi2 = __builtin_bit_cast(uint32_t, __builtin_convertvector((v2f{d[4 * gi + 2], d[4 * gi + 3]}), v2bf));
           const int px = gi < 3 ? 8 * gi + 4 * kh : 24;
@@ -513,9 +594,9 @@ k_fwd_bf16_w28(BfArgs a) {
           if constexpr (ZS) *(u32x2a*)(a.z + o) = u32x2a{lo, hi2};
         }
     }
-  };
-  if (hi) body(std::integral_constant<int, 3>{});
-  else body(std::integral_constant<int, 4>{});
+    cur = nxt;
+    base_cur = base_nxt;
+  }
 }
 
 enum BfShapeId { BF_NONE, BF_28, BF_56, BF7_56, BF28_56 };
@@ -560,7 +641,7 @@ hipError_t launch_bf(const FwdRequest& r, hipStream_t st, K with_z, K without_z)
   return launch_main(fn, dim3(grid), dim3(kThreads), lds, st, a);
 }
 
-// One workgroup of 8 waves per block of 64 windows of a channel.
+// Persistent workgroups of 4 waves, two per CU, each walking a run of blocks of 32 windows.
 template <class S>
 hipError_t launch_bf28(const FwdRequest& r, hipStream_t st) {
   BfArgs a{};
@@ -575,9 +656,17 @@ hipError_t launch_bf28(const FwdRequest& r, hipStream_t st) {
   auto fn = a.z ? k_fwd_bf16_w28<S, true> : k_fwd_bf16_w28<S, false>;
   hipError_t e = hipFuncSetAttribute((const void*)fn, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
   if (e != hipSuccess) return e;
-  return launch_main(fn, dim3(a.C * a.groups), dim3(S::NTH), lds, st, a);
+  int dev = 0, cus = 256;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+    cus = 256;
+  const int nb = a.C * a.groups;
+  const int grid = nb < 2 * cus ? nb : 2 * cus;  // two resident workgroups per CU
+  return launch_main(fn, dim3(grid), dim3(S::NTH), lds, st, a);
 }
-static_assert(bf28_lds_bytes<Bf28Shape<56>>() <= kLdsPerCu, "w = 28 workgroup LDS");
+static_assert(2 * ((bf28_lds_bytes<Bf28Shape<56>>() + kLdsGranule - 1) / kLdsGranule * kLdsGranule) <=
+                  kLdsPerCu,
+              "two w = 28 workgroups per CU");
 
 }  // namespace
 
