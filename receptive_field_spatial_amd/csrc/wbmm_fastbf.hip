@@ -577,22 +577,37 @@ k_fwd_bf16_w28(BfArgs a) {
       __syncthreads();
     });
     // stores: lane (window l32, kh) holds rows 8g + 4kh .. +3 = 4 consecutive pixels of its
-    // window row (group 3 of the upper half repeats pixels 24..27)
+    // window row (group 3 of the upper half repeats pixels 24..27). Swapping groups between lane
+    // halves (v_permlane32_swap) gives the lower lanes pixels 0..7 and 16..23 and the upper
+    // lanes 8..15 and 20..27 (20..23 also stored by the lower lanes, same values): two 16-byte
+    // stores per tile.
     {
       const int j = l32;
       const size_t ob = plane(cur, j >> 2) + (size_t)(S::WS * ((j >> 1) & 1) + t0) * S::IW + S::WS * (j & 1);
+      const size_t o1 = ob + (kh ? 8 : 0), o2 = ob + (kh ? 20 : 16);
 #pragma unroll
-      for (int t = 0; t < S::NT; ++t)
+      for (int t = 0; t < S::NT; ++t) {
+        const v16f& d = acc[t];
+        uint32_t pk[8];  // group g: pk[2g], pk[2g + 1]
 #pragma unroll
-        for (int gi = 0; gi < 4; ++gi) {
-          const v16f& d = acc[t];
-          const uint32_t lo = __builtin_bit_cast(uint32_t, __builtin_convertvector((v2f{d[4 * gi], d[4 * gi + 1]}), v2bf));
-          const uint32_t hi2 = __builtin_bit_cast(uint32_t, __builtin_convertvector((v2f{d[4 * gi + 2], d[4 * gi + 3]}), v2bf));
-          const int px = gi < 3 ? 8 * gi + 4 * kh : 24;
-          const size_t o = ob + (size_t)t * S::IW + px;
-          *(u32x2a*)(a.y + o) = u32x2a{lo, hi2};
-          if constexpr (ZS) *(u32x2a*)(a.z + o) = u32x2a{lo, hi2};
+        for (int q = 0; q < 8; ++q)
+          pk[q] = __builtin_bit_cast(uint32_t, __builtin_convertvector((v2f{d[2 * q], d[2 * q + 1]}), v2bf));
+        const uint32_t g2lo = pk[4], g2hi = pk[5];
+        // (group 0, group 1) and (group 2, group 3): lower lanes receive the upper lanes' first
+        // group, upper lanes the lower lanes' second group
+        auto sw01a = __builtin_amdgcn_permlane32_swap(pk[0], pk[2], false, false);
+        auto sw01b = __builtin_amdgcn_permlane32_swap(pk[1], pk[3], false, false);
+        auto sw23a = __builtin_amdgcn_permlane32_swap(pk[4], pk[6], false, false);
+        auto sw23b = __builtin_amdgcn_permlane32_swap(pk[5], pk[7], false, false);
+        const u32x4 v1 = u32x4{sw01a[0], sw01b[0], sw01a[1], sw01b[1]};
+        const u32x4 v2 = kh ? u32x4{g2lo, g2hi, sw23a[0], sw23b[0]} : u32x4{sw23a[0], sw23b[0], sw23a[1], sw23b[1]};
+        *(u32x4a*)(a.y + o1 + (size_t)t * S::IW) = v1;
+        *(u32x4a*)(a.y + o2 + (size_t)t * S::IW) = v2;
+        if constexpr (ZS) {
+          *(u32x4a*)(a.z + o1 + (size_t)t * S::IW) = v1;
+          *(u32x4a*)(a.z + o2 + (size_t)t * S::IW) = v2;
         }
+      }
     }
     cur = nxt;
     base_cur = base_nxt;
