@@ -171,9 +171,11 @@ k_fwd_bf16(BfArgs a) {
   const int kq = gq >> 1, kh = gq & 1;
   const int im = wave * S::IPW + n / S::NWIN;  // image of window n within the unit
   const int xo = win_off<S>(n) + kq * S::IW + 6 * kh;
-  const int so = win_off<S>(n) + (gq < 3 ? 4 * gq : S::WS - 4);
+  // tiles leave in pairs (t, t + 1): lane group gq stores 8 pixels of tile t + (gq & 1),
+  // pixels 0..7 (gq < 2) or 6..13
+  const int so = win_off<S>(n) + (gq & 1) * S::IW + (gq < 2 ? 0 : S::WS - 8);
   // table run of tile t (pixel (t, xi)), step s at ab + TP (WS-1-t) + 2 TP s; immediates >= 0
-  const int xi = n < 12 ? n : n - 2;
+  const int xi = n < 8 ? n : n - 2;
   const int bi0 = S::C0 - xi;          // row t subtracts TP t, which keeps the copy index
   const int rc = (-bi0) & 7;           // copy whose runs from bi (mod 8) are 16-byte aligned
   const int ab = rc * S::CS + bi0 + rc + S::TP * kq + 8 * kh - S::TP * (S::WS - 1);
@@ -239,17 +241,28 @@ k_fwd_bf16(BfArgs a) {
         // keep this order: the scheduler otherwise trades the read-ahead for registers
         __builtin_amdgcn_sched_barrier(0);
       }
+      // lane group gq holds pixels 4gq .. 4gq+3 (groups 2, 3: 6 .. 13) of tile t; swapping the
+      // odd groups of tile t with the even groups of tile t + 1 (v_permlane16_swap) leaves every
+      // lane 8 consecutive pixels of one tile: one 16-byte store per lane and tile pair
+      static_assert(NT % 2 == 0, "tile pairs");
 #pragma unroll
-      for (int t = 0; t < NT; ++t) {
-        const uint32_t lo = __builtin_bit_cast(uint32_t, __builtin_convertvector((v2f{acc[t][0], acc[t][1]}), v2bf));
-        const uint32_t hi = __builtin_bit_cast(uint32_t, __builtin_convertvector((v2f{acc[t][2], acc[t][3]}), v2bf));
+      for (int t = 0; t < NT; t += 2) {
+        uint32_t pk[2][2];
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+          pk[u][0] = __builtin_bit_cast(uint32_t, __builtin_convertvector((v2f{acc[t + u][0], acc[t + u][1]}), v2bf));
+          pk[u][1] = __builtin_bit_cast(uint32_t, __builtin_convertvector((v2f{acc[t + u][2], acc[t + u][3]}), v2bf));
+        }
+        const auto lo = __builtin_amdgcn_permlane16_swap(pk[0][0], pk[1][0], false, false);
+        const auto hi = __builtin_amdgcn_permlane16_swap(pk[0][1], pk[1][1], false, false);
+        const u32x4 v = u32x4{lo[0], hi[0], lo[1], hi[1]};
         const size_t o = obase + (size_t)(T0 + t) * S::IW;
-        *(u32x2a*)(a.y + o) = u32x2a{lo, hi};
-        if constexpr (ZS) *(u32x2a*)(a.z + o) = u32x2a{lo, hi};
+        *(u32x4a*)(a.y + o) = v;
+        if constexpr (ZS) *(u32x4a*)(a.z + o) = v;
       }
     };
-    half(std::integral_constant<int, 0>{}, std::integral_constant<int, 7>{});
-    half(std::integral_constant<int, 7>{}, std::integral_constant<int, 7>{});
+    half(std::integral_constant<int, 0>{}, std::integral_constant<int, 8>{});
+    half(std::integral_constant<int, 8>{}, std::integral_constant<int, 6>{});
     if constexpr (MORE) convert(conv);
     return nxt;
   };
