@@ -43,8 +43,9 @@ def log(*a):
 # with device code; wbmm_launch.hpp (host-side request structs and launcher declarations) and
 # the other kernels' files do not change it.
 KERNEL_FILES = {"k_fwd_ws": "wbmm_fast.hip", "k_bwd_ls": "wbmm_fast.hip",
-                "k_fwd_bf16": "wbmm_fastbf.hip", "k_wbmm_fwd": "wbmm_fwd.hip",
-                "k_wbmm_bwd": "wbmm_bwd.hip"}
+                "k_fwd_bf16_w7": "wbmm_fastbf.hip",
+                "k_fwd_bf16_w28": "wbmm_fastbf.hip", "k_fwd_bf16": "wbmm_fastbf.hip",
+                "k_wbmm_fwd": "wbmm_fwd.hip", "k_wbmm_bwd": "wbmm_bwd.hip"}
 DEVICE_HEADERS = ("wbmm_device.hpp", "wbmm_core.hpp", "wbmm_plan.hpp")
 
 
@@ -338,7 +339,7 @@ def _pmc_rows(d):
 
 
 # bench label -> names of the kernels that can be that call's main kernel (fast or general path)
-MAIN_KERNELS = {"k_wbmm_fwd": ("k_fwd_ws", "k_fwd_bf16", "k_wbmm_fwd"),
+MAIN_KERNELS = {"k_wbmm_fwd": ("k_fwd_ws", "k_fwd_bf16_w7", "k_fwd_bf16_w28", "k_fwd_bf16", "k_wbmm_fwd"),
                 "k_wbmm_bwd": ("k_bwd_ls", "k_wbmm_bwd")}
 
 

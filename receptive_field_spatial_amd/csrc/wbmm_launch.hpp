@@ -57,8 +57,8 @@ bool fast_backward_ok(const BwdRequest& r);
 size_t fast_backward_workspace(const BwdRequest& r);
 hipError_t launch_backward_fast(const BwdRequest& r, hipStream_t st);
 
-// Fast bf16 forward for w = 14, NCHW, square images of 14, 28 or 56, table input, bf16 output,
-// no mix.
+// Fast bf16 forwards for NCHW table input, bf16 output, no mix: w = 14 on 28x28 and 56x56
+// images, w = 7 and w = 28 on 56x56 images.
 bool fast_bf16_forward_ok(const FwdRequest& r);
 hipError_t launch_forward_fast_bf16(const FwdRequest& r, hipStream_t st);
 

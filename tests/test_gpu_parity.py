@@ -150,6 +150,48 @@ def test_forward_shapes(B, C, H, W, w, cached):
     assert_f32(yh, want, "y")
 
 
+@pytest.mark.parametrize("B,C", [(1, 3), (5, 2), (16, 2), (17, 3), (33, 2)])
+@pytest.mark.parametrize("mix", [False, True])
+@pytest.mark.parametrize("zsave", [False, True])
+def test_forward_f32_28x28_w14(B, C, mix, zsave):
+    """fp32 w = 14 on 28x28 NCHW images (the training shape's own forward kernel): ragged batches
+    (images past the batch are clamped), with and without the fused mix and z_save."""
+    say(f"forward f32 28x28 w=14 B={B} C={C} mix={mix} zsave={zsave}")
+    yh, want_y, zh, want_z = fwd_case(B, C, 28, 28, 14, cached=False, mix=mix, zsave=zsave)
+    assert_f32(yh, want_y, "y")
+    if zsave:
+        assert_f32(zh, want_z, "z")
+
+
+@pytest.mark.parametrize("B,C,mix", [(16, 600, False), (5, 300, False), (16, 600, True),
+                                     (64, 1800, True), (37, 1000, True)])
+def test_forward_f32_28x28_w14_shift_bitwise(B, C, mix):
+    """One-hot tables at a different offset in every channel (fp32, 28x28, w = 14): the output is
+    the input shifted inside each window, bit for bit. More units than resident workgroups, so
+    workgroups walk several units and restage the table when the channel changes. With `mix`,
+    the mix weights are the identity (one-hot centre) and z_save is taken: both y and z_save are
+    the shifted input, bit for bit, which checks the mix sweep's addressing over many units."""
+    w = 14
+    say(f"forward f32 28x28 shift B={B} C={C} mix={mix}")
+    x = synth.normal_f32((B, C, 28, 28), 1.0, seed=35)
+    dy = (np.arange(C) * 5) % 27 - 13
+    dx = (np.arange(C) * 11 + 3) % 27 - 13
+    T = np.zeros((C, 27, 27), np.float32)
+    T[np.arange(C), dy + 13, dx + 13] = 1.0
+    want = _window_shift(x, w, dy, dx)
+    if not mix:
+        y = R().wbmm_forward(dev(x), w, T=dev(T))
+        assert np.array_equal(host(y), want)
+        return
+    W9 = np.zeros((C, 3, 3), np.float32)
+    W9[:, 1, 1] = 1.0
+    xd = dev(x)
+    z = torch.empty_like(xd)
+    y = R().wbmm_forward(xd, w, T=dev(T), mix_w=dev(W9), z_save=z)
+    assert np.array_equal(host(z), want)
+    assert np.array_equal(host(y), want)
+
+
 @pytest.mark.parametrize("B,C,H,W,w", [(2, 3, 28, 28, 14), (1, 4, 10, 13, 4), (3, 2, 56, 56, 7)])
 @pytest.mark.parametrize("cached", [False, True])
 def test_forward_mix_and_zsave(B, C, H, W, w, cached):
