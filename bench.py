@@ -52,10 +52,27 @@ DEVICE_HEADERS = ("wbmm_device.hpp", "wbmm_core.hpp", "wbmm_plan.hpp")
 def kernel_source_hash(kernel: str) -> str:
     h = hashlib.sha256()
     for name in (KERNEL_FILES[kernel],) + DEVICE_HEADERS:
-        with open(os.path.join(CSRC, name), "rb") as f:
+        with open(os.path.join(CSRC, name), encoding="utf-8") as f:
             h.update(name.encode())
-            h.update(f.read())
+            h.update(_code_only(f.read()).encode())
     return h.hexdigest()[:16]
+
+
+def _code_only(src: str) -> str:
+    """C++ source without comments and with whitespace runs collapsed, so that editing a comment
+    does not invalidate counters taken with the same code."""
+    out, i, n = [], 0, len(src)
+    while i < n:
+        if src.startswith("//", i):
+            j = src.find("\n", i)
+            i = n if j < 0 else j
+        elif src.startswith("/*", i):
+            j = src.find("*/", i + 2)
+            i = n if j < 0 else j + 2
+        else:
+            out.append(src[i])
+            i += 1
+    return " ".join("".join(out).split())
 
 
 # ----------------------------------------------------------------------------- accounting

@@ -18,10 +18,12 @@
 //     K step, so all of a lane's table reads are one base plus immediates;
 //   * output tiles are window rows: MFMA rows 0..11 are pixels 0..11 of the row and rows 12..15
 //     pixels 10..13 again, so a lane's four accumulators are 4 consecutive pixels of one window
-//     row, rounded to bf16 (RNE, v_cvt_pk_bf16_f32) and stored straight to HBM as one 8-byte
-//     store (pixels 10, 11 are written twice with the same value). Images past the batch read
-//     and write the batch's last image (same values again), so no store needs a branch and the
-//     wait for the next unit's loads never waits for stores.
+//     row, rounded to bf16 (RNE, v_cvt_pk_bf16_f32); tiles leave in pairs, the odd lane groups
+//     of one tile swapped with the even groups of the next (v_permlane16_swap), so each lane
+//     stores 8 consecutive pixels of one row as one 16-byte store straight to HBM (pixels 10, 11
+//     are written twice with the same value). Images past the batch read and write the batch's
+//     last image (same values again), so no store needs a branch and the wait for the next
+//     unit's loads never waits for stores.
 #include "wbmm_device.hpp"
 #include "wbmm_launch.hpp"
 
@@ -420,7 +422,9 @@ k_fwd_bf16_w7(BfArgs a) {
 //   * window operand: window rows stream through a double-buffered LDS chunk (2 window rows of
 //     the 32 windows, rows padded with zeros) with one 16-byte load and LDS write per thread and
 //     chunk; the loads run PF = 7 chunks ahead; one LDS read per K step;
-//   * accumulators leave as 4 consecutive pixels of a window row: 8-byte stores.
+//   * accumulators hold 4 consecutive pixels of a window row per lane; swapping lane groups
+//     between the wave halves (v_permlane32_swap) makes that 8 + 8 pixels: two 16-byte stores
+//     per lane and tile.
 template <int IW_>
 struct Bf28Shape {
   static constexpr int WS = 28, IH = IW_, IW = IW_;
