@@ -37,7 +37,8 @@ import numpy as np
 __all__ = [
     "padded_hw", "build_index", "build_matrix", "fold_hier", "sub_index",
     "pad_map", "partition", "reverse", "wbmm_forward", "mix_forward", "mix_backward",
-    "wbmm_backward", "layer_forward", "layer_backward",
+    "wbmm_backward", "layer_forward", "layer_backward", "wbmm_backward_hier",
+    "layer_forward_hier", "layer_backward_hier",
 ]
 
 
@@ -222,6 +223,39 @@ def wbmm_backward(x: np.ndarray, dz: np.ndarray, w: int, T: Optional[np.ndarray]
     return dx, dT.reshape(C, 2 * w - 1, 2 * w - 1)
 
 
+def wbmm_backward_hier(x: np.ndarray, dz: np.ndarray, w: int, s: int, T: np.ndarray,
+                       T_sub: np.ndarray) -> Tuple[np.ndarray, np.ndarray, np.ndarray]:
+    """Gradients of the hierarchical forward, z = M' . x with M' = fold_hier(M(T), T_sub):
+    (dx, dT, dT_sub), float64.
+
+    The pages overlay an s x s sub-window table on the w x w window [gecl.asia reading notes,
+    "Method" point 4] and train the result, but do not write its backward. By the chain rule, with
+    dM_c = G_c X_c^T per channel: dX_c = M'_c^T G_c; M' copies T_c[idx] at every pair, so dT_c[k]
+    is the sum of dM_c over the pairs with idx = k (as without the fold); M' adds T_sub_c[idx_s]
+    only at same-sub-window pairs (reading R5), so dT_sub_c[k'] is the sum of dM_c over the
+    same-sub-window pairs with idx_s = k'. M' is formed in T's dtype (float32 tables give the
+    float32-rounded fold).
+    """
+    B, C, H, W = x.shape
+    Hp, Wp = padded_hw(H, W, w)
+    Mf = fold_hier(build_matrix(T, w), T_sub, w, s)
+    X = partition(pad_map(x, w), w)
+    G = partition(pad_map(dz, w), w)
+    idx = build_index(w).ravel()
+    same, idx_s = sub_index(w, s)
+    L, Ls = (2 * w - 1) ** 2, (2 * s - 1) ** 2
+    dX = np.empty_like(X)
+    dT = np.empty((C, L), dtype=np.float64)
+    dTs = np.empty((C, Ls), dtype=np.float64)
+    for c in range(C):
+        dX[c] = Mf[c].astype(np.float64).T @ G[c]
+        P = G[c] @ X[c].T
+        dT[c] = np.bincount(idx, weights=P.ravel(), minlength=L)
+        dTs[c] = np.bincount(idx_s[same], weights=P[same], minlength=Ls)
+    dx = reverse(dX, B, Hp, Wp, w)[:, :, :H, :W]
+    return dx, dT.reshape(C, 2 * w - 1, 2 * w - 1), dTs.reshape(C, 2 * s - 1, 2 * s - 1)
+
+
 # ----------------------------------------------------------------------------- full layer
 def layer_forward(x, w, T=None, M=None, Wmix=None):
     """WBMM then, if Wmix is given, the 3x3 mix. Returns (y, z) with z the pre-mix output."""
@@ -240,3 +274,23 @@ def layer_backward(x, dy, w, T=None, M=None, Wmix=None, z=None):
         dz, dW = dy.astype(np.float64), None
     dx, dT = wbmm_backward(x, dz, w, T=T, M=M)
     return dx, dT, dW
+
+
+def layer_forward_hier(x, w, s, T, T_sub, Wmix=None):
+    """Hierarchical layer: WBMM with M' = fold_hier(M(T), T_sub), then the optional 3x3 mix.
+    Returns (y, z)."""
+    z = wbmm_forward(x, w, M=fold_hier(build_matrix(T, w), T_sub, w, s))
+    y = mix_forward(z, Wmix) if Wmix is not None else z
+    return y, z
+
+
+def layer_backward_hier(x, dy, w, s, T, T_sub, Wmix=None, z=None):
+    """Backward of ``layer_forward_hier``: (dx, dT, dT_sub, dWmix-or-None)."""
+    if Wmix is not None:
+        if z is None:
+            _, z = layer_forward_hier(x, w, s, T, T_sub)
+        dz, dW = mix_backward(dy, z, Wmix)
+    else:
+        dz, dW = dy.astype(np.float64), None
+    dx, dT, dTs = wbmm_backward_hier(x, dz, w, s, T, T_sub)
+    return dx, dT, dTs, dW

@@ -396,6 +396,103 @@ def test_cached_matrix_backward_matches_table_backward():
     assert np.array_equal(dx1, dx2) and np.array_equal(dT1, dT2)
 
 
+# ----------------------------------------------------------------------------- hierarchical backward
+def hier_brute_force(x, g, T, Ts, w, s):
+    """Pure loops over images, windows and pixel pairs: (dx, dT, dT_sub) of the folded layer,
+    with the pair weight T[dy][dx] + (same s-sub-window ? T_sub[dy%][dx%] : 0) written out."""
+    B, C, H, W = x.shape
+    dx = np.zeros_like(x)
+    dT = np.zeros_like(T)
+    dTs = np.zeros_like(Ts)
+    for b in range(B):
+        for c in range(C):
+            for wy0 in range(0, H, w):
+                for wx0 in range(0, W, w):
+                    pix = [(py, px) for py in range(wy0, min(wy0 + w, H))
+                           for px in range(wx0, min(wx0 + w, W))]
+                    for (py, px) in pix:      # output pixel i
+                        for (qy, qx) in pix:  # input pixel j
+                            yi, xi, yj, xj = py - wy0, px - wx0, qy - wy0, qx - wx0
+                            same = yi // s == yj // s and xi // s == xj // s
+                            m = T[c, yi - yj + w - 1, xi - xj + w - 1]
+                            if same:
+                                m += Ts[c, yi % s - yj % s + s - 1, xi % s - xj % s + s - 1]
+                            dx[b, c, qy, qx] += m * g[b, c, py, px]
+                            gx = g[b, c, py, px] * x[b, c, qy, qx]
+                            dT[c, yi - yj + w - 1, xi - xj + w - 1] += gx
+                            if same:
+                                dTs[c, yi % s - yj % s + s - 1, xi % s - xj % s + s - 1] += gx
+    return dx, dT, dTs
+
+
+@pytest.mark.parametrize("B,C,H,W,w,s", [(2, 2, 8, 8, 4, 2), (1, 2, 10, 7, 4, 2), (1, 1, 6, 6, 6, 3)])
+def test_hier_backward_brute_force(B, C, H, W, w, s):
+    x = rnd((B, C, H, W), seed=51)
+    g = rnd((B, C, H, W), seed=52)
+    T = rnd((C, 2 * w - 1, 2 * w - 1), seed=53)
+    Ts = rnd((C, 2 * s - 1, 2 * s - 1), seed=54)
+    dx, dT, dTs = O.wbmm_backward_hier(x, g, w, s, T, Ts)
+    bx, bT, bTs = hier_brute_force(x, g, T, Ts, w, s)
+    assert np.allclose(dx, bx, rtol=0, atol=1e-12)
+    assert np.allclose(dT, bT, rtol=0, atol=1e-12)
+    assert np.allclose(dTs, bTs, rtol=0, atol=1e-12)
+
+
+def test_hier_finite_differences_with_mix():
+    """Central differences of L = sum(dY * y(T, T_sub, x)) through the fold and the mix: exact up to
+    rounding, since L is linear in each of T_sub, T and x."""
+    w, s = 4, 2
+    x = rnd((2, 2, 8, 8), seed=55)
+    T = rnd((2, 7, 7), 0.1, seed=56)
+    Ts = rnd((2, 3, 3), 0.1, seed=57)
+    Wm = rnd((2, 3, 3), 0.1, seed=58)
+    dY = rnd((2, 2, 8, 8), seed=59)
+    dx, dT, dTs, dW = O.layer_backward_hier(x, dY, w, s, T, Ts, Wmix=Wm)
+
+    def L(x_=x, T_=T, Ts_=Ts):
+        return np.sum(dY * O.layer_forward_hier(x_, w, s, T_, Ts_, Wmix=Wm)[0])
+
+    h = 1e-3
+    for k in range(Ts.size):
+        P, Mn = Ts.copy().reshape(-1), Ts.copy().reshape(-1)
+        P[k] += h
+        Mn[k] -= h
+        fd = (L(Ts_=P.reshape(Ts.shape)) - L(Ts_=Mn.reshape(Ts.shape))) / (2 * h)
+        assert abs(fd - dTs.reshape(-1)[k]) <= 1e-9
+    for k in (0, 11, 24, 48, 97):
+        P, Mn = T.copy().reshape(-1), T.copy().reshape(-1)
+        P[k] += h
+        Mn[k] -= h
+        fd = (L(T_=P.reshape(T.shape)) - L(T_=Mn.reshape(T.shape))) / (2 * h)
+        assert abs(fd - dT.reshape(-1)[k]) <= 1e-9
+    for k in (0, 37, 64, 255):
+        P, Mn = x.copy().reshape(-1), x.copy().reshape(-1)
+        P[k] += h
+        Mn[k] -= h
+        fd = (L(x_=P.reshape(x.shape)) - L(x_=Mn.reshape(x.shape))) / (2 * h)
+        assert abs(fd - dx.reshape(-1)[k]) <= 1e-9
+
+
+def test_hier_zero_sub_table_is_plain_backward():
+    """T_sub = 0: dx and dT are exactly the unfolded ones; dT_sub sums the same-sub-window part."""
+    w, s = 14, 7
+    x = rnd((1, 2, 28, 14), seed=60)
+    g = rnd((1, 2, 28, 14), seed=61)
+    T = rnd((2, 27, 27), 0.02, seed=62)
+    dx, dT, dTs = O.wbmm_backward_hier(x, g, w, s, T, np.zeros((2, 13, 13)))
+    dx0, dT0 = O.wbmm_backward(x, g, w, T=T)
+    assert np.array_equal(dx, dx0) and np.array_equal(dT, dT0)
+    # same-sub-window offsets are the central 13 x 13 of dT: dT_sub is at most that, and every
+    # same-sub-window pair is also counted in dT
+    assert dTs.shape == (2, 13, 13)
+    ones = np.ones_like(x)
+    _, dT1, dTs1 = O.wbmm_backward_hier(ones, ones, w, s, T, np.zeros((2, 13, 13)))
+    run = s - np.abs(np.arange(-(s - 1), s))
+    n_sub = 2 * 4  # windows x sub-windows per window
+    for c in range(2):
+        assert np.array_equal(dTs1[c], n_sub * np.outer(run, run).astype(np.float64))
+
+
 # ----------------------------------------------------------------------------- misc pins
 def test_receptive_field_ratio():
     """The abstract's 7.8x per-layer receptive field: a 14x14 window covers 196 pixels, a 5x5 kernel 25."""
