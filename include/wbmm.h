@@ -161,6 +161,59 @@ wbmm_status wbmm_backward(int B, int C, int H, int W, int w, int layout, const f
                           float* dmix_w, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * wbmm_forward_hier_workspace_bytes — device workspace wbmm_forward_hier needs (0 when none, and
+ * 0 for invalid arguments, which wbmm_forward_hier reports).
+ */
+size_t wbmm_forward_hier_workspace_bytes(int B, int C, int H, int W, int w, int s, int layout,
+                                         int has_mix, int has_z_save);
+
+/*
+ * wbmm_forward_hier — the layer forward with the hierarchical reparameterization folded on chip
+ * [gecl.asia reading notes, "Method" point 4: a sub-window table overlays 7x7 structure in a
+ * 14x14 window at no inference cost]. The matrix is
+ *   M'_c[i][j] = M_c[i][j] + T_sub[c][idx_s(i, j)]   for pairs i, j in one s x s sub-window,
+ *   M'_c[i][j] = M_c[i][j]                           otherwise,
+ * each sum one fp32 add (RNE): exactly what wbmm_fold_hier stores, but M' is never formed in
+ * memory. Then z and y as in wbmm_forward. fp32 only; this build folds on chip for w = 2s
+ * (other s | w: wbmm_fold_hier + wbmm_forward with the cached matrix).
+ * x, y, z_save: device fp32 maps in `layout`; T: device fp32 [C][2w-1][2w-1];
+ * T_sub: device fp32 [C][2s-1][2s-1]; mix_w, z_save, workspace as in wbmm_forward
+ * (workspace size from wbmm_forward_hier_workspace_bytes).
+ * Errors: WBMM_E_INVALID (sizes, NULL or overlapping pointers), WBMM_E_UNSUPPORTED (w != 2s,
+ *         misaligned pointer), WBMM_E_WORKSPACE, WBMM_E_HIP.
+ */
+wbmm_status wbmm_forward_hier(int B, int C, int H, int W, int w, int s, int layout, const float* x,
+                              const float* T, const float* T_sub, const float* mix_w,
+                              float* z_save, float* y, void* workspace, size_t workspace_bytes,
+                              void* stream);
+
+/*
+ * wbmm_backward_hier_workspace_bytes — device workspace wbmm_backward_hier needs (0 for invalid
+ * arguments).
+ */
+size_t wbmm_backward_hier_workspace_bytes(int B, int C, int H, int W, int w, int s, int layout,
+                                          int has_mix);
+
+/*
+ * wbmm_backward_hier — gradients of wbmm_forward_hier (fp32). As wbmm_backward with M' in place
+ * of M, and in addition the sub-table's gradient:
+ *   dx = crop(reverse(M'_c^T . G_c));   dT[c][k] = sum over pairs (i,j) with idx[i][j] = k of
+ *   (G_c . X_c^T)[i][j];   dT_sub[c][k'] = the same sum over the pairs inside one s x s
+ *   sub-window with idx_s[i][j] = k'.
+ * T, T_sub: as in wbmm_forward_hier. dx, dT, dT_sub, dmix_w: written, or NULL to skip
+ * (dT_sub: device fp32 [C][2s-1][2s-1]). mix_w, z_saved, dy, workspace as in wbmm_backward.
+ * dT, dT_sub and dmix_w are reduced in a fixed order: bitwise reproducible run to run.
+ * This build provides it for w = 2s <= 16.
+ * Errors: WBMM_E_INVALID, WBMM_E_UNSUPPORTED (w != 2s, w > 16, misaligned pointer),
+ *         WBMM_E_WORKSPACE, WBMM_E_HIP.
+ */
+wbmm_status wbmm_backward_hier(int B, int C, int H, int W, int w, int s, int layout,
+                               const float* x, const float* T, const float* T_sub,
+                               const float* mix_w, const float* z_saved, const float* dy,
+                               float* dx, float* dT, float* dT_sub, float* dmix_w,
+                               void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * wbmm_set_launch_events — measurement aid, not part of the method. The next wbmm_forward or
  * wbmm_backward call made on the calling thread attaches `before` and `after` (hipEvent_t
  * handles passed as void*) to the dispatch of its main contraction kernel (hipExtLaunchKernel's

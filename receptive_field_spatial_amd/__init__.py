@@ -17,6 +17,8 @@ __all__ = [
     "wbmm_build_index", "wbmm_build_matrix", "wbmm_fold_hier",
     "wbmm_forward", "wbmm_forward_workspace_bytes",
     "wbmm_backward", "wbmm_backward_workspace_bytes", "wbmm_set_launch_events",
+    "wbmm_forward_hier", "wbmm_forward_hier_workspace_bytes",
+    "wbmm_backward_hier", "wbmm_backward_hier_workspace_bytes",
     "WBMM_OK", "WBMM_E_INVALID", "WBMM_E_UNSUPPORTED", "WBMM_E_WORKSPACE", "WBMM_E_HIP",
 ]
 
@@ -52,6 +54,10 @@ def _declare(lib):
         "wbmm_backward_workspace_bytes": (c_size, [c_int] * 7),
         "wbmm_backward": (c_int, [c_int] * 6 + [vp] * 10 + [c_size, vp]),
         "wbmm_set_launch_events": (c_int, [vp, vp]),
+        "wbmm_forward_hier_workspace_bytes": (c_size, [c_int] * 9),
+        "wbmm_forward_hier": (c_int, [c_int] * 7 + [vp] * 7 + [c_size, vp]),
+        "wbmm_backward_hier_workspace_bytes": (c_size, [c_int] * 8),
+        "wbmm_backward_hier": (c_int, [c_int] * 7 + [vp] * 11 + [c_size, vp]),
     }
     for name, (res, args) in sigs.items():
         fn = getattr(lib, name)
@@ -221,6 +227,65 @@ def wbmm_backward(x, dy, w: int, T=None, M=None, mix_w=None, z_saved=None, *, la
                                 _ptr(mix_w), _ptr(z_saved), _ptr(dy), _ptr(dx_t), _ptr(dT_t),
                                 _ptr(dW_t), _ptr(workspace), ws_bytes, _stream(stream)))
     return dx_t, dT_t, dW_t
+
+
+def wbmm_forward_hier_workspace_bytes(B, C, H, W, w, s, layout="NCHW", has_mix=False,
+                                      has_z_save=False) -> int:
+    return int(_lib().wbmm_forward_hier_workspace_bytes(B, C, H, W, int(w), int(s),
+                                                        _layout_code(layout), int(bool(has_mix)),
+                                                        int(bool(has_z_save))))
+
+
+def wbmm_forward_hier(x, w: int, s: int, T, T_sub, mix_w=None, *, layout: str = "NCHW", y=None,
+                      z_save=None, workspace=None, stream=None):
+    """Layer forward (fp32) with the s x s sub-window tables T_sub (C, 2s-1, 2s-1) folded into
+    the matrix on chip. Returns y (and z_save, when given, holds the pre-mix output)."""
+    torch = _torch()
+    B, C, H, W = _bchw(x, layout)
+    if y is None:
+        y = torch.empty_like(x)
+    need = wbmm_forward_hier_workspace_bytes(B, C, H, W, w, s, layout, mix_w is not None,
+                                             z_save is not None)
+    if need and (workspace is None or workspace.numel() * workspace.element_size() < need):
+        workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(_lib().wbmm_forward_hier(B, C, H, W, int(w), int(s), _layout_code(layout), _ptr(x),
+                                    _ptr(T), _ptr(T_sub), _ptr(mix_w), _ptr(z_save), _ptr(y),
+                                    _ptr(workspace), ws_bytes, _stream(stream)))
+    return y
+
+
+def wbmm_backward_hier_workspace_bytes(B, C, H, W, w, s, layout="NCHW", has_mix=False) -> int:
+    return int(_lib().wbmm_backward_hier_workspace_bytes(B, C, H, W, int(w), int(s),
+                                                         _layout_code(layout), int(bool(has_mix))))
+
+
+def wbmm_backward_hier(x, dy, w: int, s: int, T, T_sub, mix_w=None, z_saved=None, *,
+                       layout: str = "NCHW", dx=True, dT=True, dT_sub=True, dmix_w=True,
+                       workspace=None, stream=None):
+    """Backward of wbmm_forward_hier (fp32). Returns (dx, dT, dT_sub, dmix_w); an output passed as
+    False is skipped."""
+    torch = _torch()
+    B, C, H, W = _bchw(x, layout)
+    L, Ls = 2 * w - 1, 2 * s - 1
+    dev = x.device
+
+    def out(v, shape):
+        return torch.empty(shape, dtype=torch.float32, device=dev) if v is True else (v if v is not False else None)
+
+    dx_t = out(dx, tuple(x.shape))
+    dT_t = out(dT, (C, L, L))
+    dTs_t = out(dT_sub, (C, Ls, Ls))
+    dW_t = None if mix_w is None else out(dmix_w, (C, 3, 3))
+    need = wbmm_backward_hier_workspace_bytes(B, C, H, W, w, s, layout, mix_w is not None)
+    if need and (workspace is None or workspace.numel() * workspace.element_size() < need):
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(_lib().wbmm_backward_hier(B, C, H, W, int(w), int(s), _layout_code(layout), _ptr(x),
+                                     _ptr(T), _ptr(T_sub), _ptr(mix_w), _ptr(z_saved), _ptr(dy),
+                                     _ptr(dx_t), _ptr(dT_t), _ptr(dTs_t), _ptr(dW_t),
+                                     _ptr(workspace), ws_bytes, _stream(stream)))
+    return dx_t, dT_t, dTs_t, dW_t
 
 
 def wbmm_set_launch_events(before, after):

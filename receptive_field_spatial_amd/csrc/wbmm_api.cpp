@@ -269,3 +269,106 @@ WBMM_API wbmm_status wbmm_backward(int B, int C, int H, int W, int w, int layout
     return fail(WBMM_E_UNSUPPORTED, "workspace not 256-byte aligned");
   return hip_status(wbmm::launch_backward(r, (hipStream_t)stream), "wbmm_backward");
 }
+namespace {
+// Shared checks of the hierarchical entry points: fp32 table path with the s x s sub-window
+// tables folded on chip, which this build provides for w = 2s.
+wbmm_status check_hier(int w, int s, const float* T, const float* T_sub) {
+  if (s < 1 || 2 * s != w)
+    return fail(WBMM_E_UNSUPPORTED,
+                "the on-chip fold is provided for w = 2s (w=%d, s=%d); fold other sub-windows "
+                "with wbmm_fold_hier and pass the cached matrix", w, s);
+  if (!T || !T_sub) return fail(WBMM_E_INVALID, "T and T_sub must be non-NULL");
+  if (!aligned(T, 4) || !aligned(T_sub, 4)) return fail(WBMM_E_UNSUPPORTED, "misaligned pointer");
+  return WBMM_OK;
+}
+}  // namespace
+WBMM_API size_t wbmm_forward_hier_workspace_bytes(int B, int C, int H, int W, int w, int s,
+                                                  int layout, int has_mix, int has_z_save) {
+  if (check_map(B, C, H, W, w, layout) != WBMM_OK || s < 1 || 2 * s != w) return 0;
+  static const float dummy = 0.f;
+  wbmm::FwdRequest r = make_fwd(B, C, H, W, w, layout, WBMM_F32, WBMM_F32, &dummy, &dummy, nullptr,
+                                has_mix ? &dummy : nullptr, has_z_save ? (void*)&dummy : nullptr,
+                                (void*)&dummy, nullptr, 0);
+  r.Tsub = &dummy;
+  r.s = s;
+  if (!wbmm::forward_plan_ok(r)) return 0;
+  return wbmm::forward_workspace(r);
+}
+WBMM_API wbmm_status wbmm_forward_hier(int B, int C, int H, int W, int w, int s, int layout,
+                                       const float* x, const float* T, const float* T_sub,
+                                       const float* mix_w, float* z_save, float* y,
+                                       void* workspace, size_t workspace_bytes, void* stream) {
+  wbmm_status st = check_map(B, C, H, W, w, layout);
+  if (st != WBMM_OK) return st;
+  st = check_hier(w, s, T, T_sub);
+  if (st != WBMM_OK) return st;
+  wbmm::FwdRequest r = make_fwd(B, C, H, W, w, layout, WBMM_F32, WBMM_F32, x, T, nullptr, mix_w,
+                                z_save, y, workspace, workspace_bytes);
+  r.Tsub = T_sub;
+  r.s = s;
+  st = check_forward(r, WBMM_F32, WBMM_F32);
+  if (st != WBMM_OK) return st;
+  const size_t elems = (size_t)B * C * H * W;
+  if (overlaps(y, elems * 4, T_sub, (size_t)C * (2 * s - 1) * (2 * s - 1) * 4))
+    return fail(WBMM_E_INVALID, "y overlaps T_sub");
+  const size_t need = wbmm::forward_workspace(r);
+  if (need > 0 && (!workspace || workspace_bytes < need))
+    return fail(WBMM_E_WORKSPACE, "workspace of %zu bytes required, %zu given", need,
+                workspace ? workspace_bytes : (size_t)0);
+  if (need > 0 && !aligned(workspace, 16))
+    return fail(WBMM_E_UNSUPPORTED, "workspace not 16-byte aligned");
+  return hip_status(wbmm::launch_forward(r, (hipStream_t)stream), "wbmm_forward_hier");
+}
+WBMM_API size_t wbmm_backward_hier_workspace_bytes(int B, int C, int H, int W, int w, int s,
+                                                   int layout, int has_mix) {
+  if (check_map(B, C, H, W, w, layout) != WBMM_OK || w > 16 || s < 1 || 2 * s != w) return 0;
+  static const float dummy = 0.f;
+  wbmm::BwdRequest r = make_bwd(B, C, H, W, w, layout, &dummy, &dummy, nullptr,
+                                has_mix ? &dummy : nullptr, has_mix ? &dummy : nullptr, &dummy,
+                                nullptr, nullptr, nullptr, nullptr, 0);
+  r.Tsub = &dummy;
+  r.s = s;
+  if (!wbmm::backward_plan_ok(r)) return 0;
+  return wbmm::backward_workspace(r);
+}
+WBMM_API wbmm_status wbmm_backward_hier(int B, int C, int H, int W, int w, int s, int layout,
+                                        const float* x, const float* T, const float* T_sub,
+                                        const float* mix_w, const float* z_saved, const float* dy,
+                                        float* dx, float* dT, float* dT_sub, float* dmix_w,
+                                        void* workspace, size_t workspace_bytes, void* stream) {
+  wbmm_status st = check_map(B, C, H, W, w, layout);
+  if (st != WBMM_OK) return st;
+  if (w > 16) return fail(WBMM_E_UNSUPPORTED, "the backward is provided for w <= 16 (w=%d)", w);
+  st = check_hier(w, s, T, T_sub);
+  if (st != WBMM_OK) return st;
+  if (!x || !dy) return fail(WBMM_E_INVALID, "x and dy must be non-NULL");
+  if ((mix_w == nullptr) != (z_saved == nullptr))
+    return fail(WBMM_E_INVALID, "z_saved is required exactly when mix_w is given");
+  const void* ptrs[] = {x, mix_w, z_saved, dy, dx, dT, dT_sub, dmix_w};
+  for (const void* p : ptrs)
+    if (p && !aligned(p, 4)) return fail(WBMM_E_UNSUPPORTED, "pointer not 4-byte aligned");
+  const size_t mb = (size_t)B * C * H * W * 4;
+  const size_t tb = (size_t)C * (2 * w - 1) * (2 * w - 1) * 4;
+  const size_t sb = (size_t)C * (2 * s - 1) * (2 * s - 1) * 4;
+  if (dx && (overlaps(dx, mb, x, mb) || overlaps(dx, mb, dy, mb) || overlaps(dx, mb, z_saved, mb)))
+    return fail(WBMM_E_INVALID, "dx overlaps an input");
+  if (dT && (overlaps(dT, tb, T, tb) || overlaps(dT, tb, T_sub, sb) || overlaps(dT, tb, dx, mb)))
+    return fail(WBMM_E_INVALID, "dT overlaps T, T_sub or dx");
+  if (dT_sub && (overlaps(dT_sub, sb, T, tb) || overlaps(dT_sub, sb, T_sub, sb) ||
+                 overlaps(dT_sub, sb, dx, mb) || overlaps(dT_sub, sb, dT, tb)))
+    return fail(WBMM_E_INVALID, "dT_sub overlaps T, T_sub, dx or dT");
+  wbmm::BwdRequest r = make_bwd(B, C, H, W, w, layout, x, T, nullptr, mix_w, z_saved, dy, dx, dT,
+                                dmix_w, workspace, workspace_bytes);
+  r.Tsub = T_sub;
+  r.s = s;
+  r.dTsub = dT_sub;
+  if (!wbmm::backward_plan_ok(r))
+    return fail(WBMM_E_UNSUPPORTED, "no launch shape fits this problem (w=%d)", w);
+  const size_t need = wbmm::backward_workspace(r);
+  if (need > 0 && (!workspace || workspace_bytes < need))
+    return fail(WBMM_E_WORKSPACE, "workspace of %zu bytes required, %zu given", need,
+                workspace ? workspace_bytes : (size_t)0);
+  if (need > 0 && !aligned(workspace, 256))
+    return fail(WBMM_E_UNSUPPORTED, "workspace not 256-byte aligned");
+  return hip_status(wbmm::launch_backward(r, (hipStream_t)stream), "wbmm_backward_hier");
+}

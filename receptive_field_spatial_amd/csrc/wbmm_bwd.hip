@@ -27,6 +27,9 @@ struct BwdArgs {
   double* partT;        // [C][col_groups][L]
   double* partW;        // [C][col_groups][9]
   int mix_here, want_dx, want_dT, want_dW;
+  const float* tsub;    // sub-window tables folded on chip (HIER), or null
+  double* partTs;       // HIER: [C][col_groups][(2s-1)^2]
+  int want_dTs;
 };
 
 // Slot j of wave q covers row offset index t = 4j + (q or 3-q alternating), ordered
@@ -37,7 +40,12 @@ __device__ __forceinline__ int slot_dy(int j, int wave, int nd, bool& valid) {
   return t == 0 ? 0 : ((t & 1) ? (t + 1) / 2 : -(t / 2));
 }
 
-template <int RPW, int ASRC>
+// HIER (the on-chip fold, w = 2s): dX uses the folded matrix, and the table gradient also yields
+// the sub-table's: dT_sub[dy][dx] sums (G . X^T)[i][j] over pairs inside one s x s sub-window,
+// i.e. row pairs in one band of s rows (y1 / s == y2 / s) and, within them, column pairs in one
+// band of s columns. Row offsets |dy| < s keep those row pairs in a second fp32 chain; dT takes
+// both chains, dT_sub the second one's band-restricted diagonals.
+template <int RPW, int ASRC, bool HIER = false>
 __global__ void __launch_bounds__(kThreads) k_wbmm_bwd(BwdArgs a) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   __shared__ double s_wred[4][9];
@@ -52,7 +60,7 @@ __global__ void __launch_bounds__(kThreads) k_wbmm_bwd(BwdArgs a) {
   int2* Offs = (int2*)(smem + g.lds_off);
   const int plane = g.PH * g.PW;
 
-  load_table_f32(g, ASRC == 0 ? a.tab : nullptr, c, Ts, Offs);
+  load_table_f32(g, ASRC == 0 ? a.tab : nullptr, c, Ts, Offs, a.tsub);
 
   double wacc[9];
 #pragma unroll
@@ -114,7 +122,7 @@ __global__ void __launch_bounds__(kThreads) k_wbmm_bwd(BwdArgs a) {
   // ---------------------------------------------------------------- dX = M^T . G
   if (a.want_dx) {
     v4f acc[RPW];
-    contract_f32<RPW, 1, ASRC, true>(g, c, a.mat, Gt, (float*)RA, Ts, Offs, 0, wave, acc);
+    contract_f32<RPW, 1, ASRC, true, HIER>(g, c, a.mat, Gt, (float*)RA, Ts, Offs, 0, wave, acc);
     if (g.image_mode) {
       __syncthreads();
       float* St = (float*)RA;
@@ -157,10 +165,15 @@ __global__ void __launch_bounds__(kThreads) k_wbmm_bwd(BwdArgs a) {
 #pragma unroll
     for (int j = 0; j < 8; ++j) dyv[j] = slot_dy(j, wave, nd, val[j]);
     double acc64[8][4];
+    double accs[HIER ? 8 : 1][4];  // HIER: the same-band part of slots with |dy| < s
 #pragma unroll
     for (int j = 0; j < 8; ++j)
 #pragma unroll
       for (int r = 0; r < 4; ++r) acc64[j][r] = 0.0;
+#pragma unroll
+    for (int j = 0; j < (HIER ? 8 : 1); ++j)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) accs[j][r] = 0.0;
     const int x1 = lane & 15, kn = lane >> 4;
     for (int n0 = 0; n0 < nvalid; n0 += 4) {
       const float* gcol = Gt + (n0 + kn) * g.XR + x1;
@@ -173,6 +186,21 @@ __global__ void __launch_bounds__(kThreads) k_wbmm_bwd(BwdArgs a) {
         const int cnt = g.w - (dy > 0 ? dy : -dy);
         const float* ga = gcol + y1s * g.RP;
         const float* xb = xcol + y2s * g.RP;
+        if constexpr (HIER) {
+          if (dy > -g.s && dy < g.s) {  // uniform
+            v4f a0 = {0.f, 0.f, 0.f, 0.f}, b0 = {0.f, 0.f, 0.f, 0.f};
+            for (int m = 0; m < cnt; ++m) {
+              if ((y1s + m) / g.s == (y2s + m) / g.s) b0 = mfma_f32(ga[m * g.RP], xb[m * g.RP], b0);
+              else a0 = mfma_f32(ga[m * g.RP], xb[m * g.RP], a0);
+            }
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+              acc64[j][r] += (double)a0[r] + (double)b0[r];
+              accs[j][r] += (double)b0[r];
+            }
+            continue;
+          }
+        }
         v4f a0 = {0.f, 0.f, 0.f, 0.f}, a1 = {0.f, 0.f, 0.f, 0.f};
         int m = 0;
         for (; m + 1 < cnt; m += 2) {
@@ -208,6 +236,32 @@ __global__ void __launch_bounds__(kThreads) k_wbmm_bwd(BwdArgs a) {
       __builtin_amdgcn_wave_barrier();
       __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
     }
+    if constexpr (HIER) {
+      // dT_sub partial: diagonals of the same-band tiles over column pairs in one band
+      const int ns = 2 * g.s - 1;
+      double* pTs = a.partTs + ((size_t)c * g.col_groups + colgrp) * ns * ns;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        if (!val[j] || dyv[j] <= -g.s || dyv[j] >= g.s) continue;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) scr[(4 * (lane >> 4) + r) * 16 + (lane & 15)] = accs[j][r];
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        if (lane < ns) {
+          const int dx = lane - (g.s - 1);
+          double s = 0.0;
+          for (int xa = 0; xa < g.w; ++xa) {
+            const int xb2 = xa - dx;
+            if (xb2 >= 0 && xb2 < g.w && xa / g.s == xb2 / g.s) s += scr[xa * 16 + xb2];
+          }
+          pTs[(dyv[j] + g.s - 1) * ns + lane] = s;
+        }
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+      }
+    }
   }
 
   // ---------------------------------------------------------------- dWmix partial
@@ -229,22 +283,22 @@ __global__ void __launch_bounds__(kThreads) k_wbmm_bwd(BwdArgs a) {
 }
 
 // ---------------------------------------------------------------------------- dispatch
-template <int RPW, int ASRC>
+template <int RPW, int ASRC, bool HIER = false>
 static hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t st) {
-  auto fn = k_wbmm_bwd<RPW, ASRC>;
+  auto fn = k_wbmm_bwd<RPW, ASRC, HIER>;
   hipError_t e = hipFuncSetAttribute((const void*)fn, hipFuncAttributeMaxDynamicSharedMemorySize,
                                      a.g.lds_total);
   if (e != hipSuccess) return e;
   return launch_main(fn, dim3(a.g.col_groups, a.g.C, 1), dim3(kThreads), a.g.lds_total, st, a);
 }
 
-template <int ASRC>
+template <int ASRC, bool HIER = false>
 static hipError_t launch_bwd_tiles(const BwdArgs& a, hipStream_t st) {
   switch (a.g.RPW) {
-    case 4: return launch_bwd_t<4, ASRC>(a, st);
-    case 7: return launch_bwd_t<7, ASRC>(a, st);
-    case 13: return launch_bwd_t<13, ASRC>(a, st);
-    case 16: return launch_bwd_t<16, ASRC>(a, st);
+    case 4: return launch_bwd_t<4, ASRC, HIER>(a, st);
+    case 7: return launch_bwd_t<7, ASRC, HIER>(a, st);
+    case 13: return launch_bwd_t<13, ASRC, HIER>(a, st);
+    case 16: return launch_bwd_t<16, ASRC, HIER>(a, st);
     default: return hipErrorInvalidValue;
   }
 }
@@ -253,22 +307,25 @@ static bool plan_bwd(Geo& g, const BwdRequest& r) {
   if (r.w > 16) return false;
   const bool cached = r.M != nullptr;
   const bool mix = r.mixw != nullptr;
-  if (!plan_geo(g, r.B, r.C, r.H, r.W, r.w, r.layout, false, cached, mix, 1)) {
-    if (!plan_geo(g, r.B, r.C, r.H, r.W, r.w, r.layout, false, cached, false, 1)) return false;
+  const int s = r.Tsub ? r.s : 0;
+  if (!plan_geo(g, r.B, r.C, r.H, r.W, r.w, r.layout, false, cached, mix, 1, s)) {
+    if (!plan_geo(g, r.B, r.C, r.H, r.W, r.w, r.layout, false, cached, false, 1, s)) return false;
   }
   return g.WR == 1;
 }
 
 namespace {
 struct BwdWs {
-  size_t partT, partW, dz, total;
+  size_t partT, partW, partTs, dz, total;
 };
 BwdWs bwd_ws_layout(const Geo& g, const BwdRequest& r) {
   auto al = [](size_t v) { return (v + 255) / 256 * 256; };
   BwdWs w{};
   w.partT = 0;
   w.partW = w.partT + al((size_t)g.C * g.col_groups * g.L * sizeof(double));
-  w.dz = w.partW + al((size_t)g.C * g.col_groups * 9 * sizeof(double));
+  w.partTs = w.partW + al((size_t)g.C * g.col_groups * 9 * sizeof(double));
+  const size_t ls = g.s ? (size_t)(2 * g.s - 1) * (2 * g.s - 1) : 0;
+  w.dz = w.partTs + al((size_t)g.C * g.col_groups * ls * sizeof(double));
   const bool need_dz = r.mixw && !g.image_mode;
   w.total = w.dz + (need_dz ? al((size_t)r.B * r.C * r.H * r.W * sizeof(float)) : 0);
   return w;
@@ -284,18 +341,22 @@ size_t backward_workspace(const BwdRequest& r) {
   Geo g;
   if (!plan_bwd(g, r)) return 0;
   const size_t generic = bwd_ws_layout(g, r).total;
-  const size_t fast = fast_backward_workspace(r);
+  const size_t fast = r.Tsub ? 0 : fast_backward_workspace(r);
   return generic > fast ? generic : fast;
 }
 
 hipError_t launch_backward(const BwdRequest& r, hipStream_t st) {
-  if (fast_backward_ok(r)) return launch_backward_fast(r, st);
+  // the fast paths have no on-chip fold: a sub-table takes the general path
+  if (!r.Tsub && fast_backward_ok(r)) return launch_backward_fast(r, st);
   BwdArgs a{};
   if (!plan_bwd(a.g, r)) return hipErrorInvalidValue;
   const BwdWs wl = bwd_ws_layout(a.g, r);
   unsigned char* ws = (unsigned char*)r.ws;
   a.x = r.x;
   a.tab = r.T;
+  a.tsub = r.Tsub;
+  a.partTs = (double*)(ws + wl.partTs);
+  a.want_dTs = r.Tsub && r.dTsub;
   a.mat = r.M;
   a.mixw = r.mixw;
   a.zsaved = r.zsaved;
@@ -324,11 +385,16 @@ hipError_t launch_backward(const BwdRequest& r, hipStream_t st) {
     a.mix_here = mix ? 1 : 0;
     a.want_dW = (mix && r.dmixw) ? 1 : 0;
   }
+  if (a.want_dTs) a.want_dT = 1;  // the sub-table gradient comes out of the table-gradient pass
   if (!a.want_dx && !a.want_dT && !a.want_dW) return hipSuccess;
-  e = r.M ? launch_bwd_tiles<1>(a, st) : launch_bwd_tiles<0>(a, st);
+  if (r.Tsub) e = launch_bwd_tiles<0, true>(a, st);  // fp32 table path only (planned so)
+  else e = r.M ? launch_bwd_tiles<1>(a, st) : launch_bwd_tiles<0>(a, st);
   if (e != hipSuccess || (!a.want_dT && !a.want_dW)) return e;
-  return launch_bwd_reduce(a.partT, a.want_dW ? a.partW : nullptr, a.g.col_groups, r.C, a.g.L,
-                           a.want_dT ? r.dT : nullptr, a.want_dW ? r.dmixw : nullptr, st);
+  e = launch_bwd_reduce(a.partT, a.want_dW ? a.partW : nullptr, a.g.col_groups, r.C, a.g.L,
+                        r.dT, a.want_dW ? r.dmixw : nullptr, st);
+  if (e != hipSuccess || !a.want_dTs) return e;
+  return launch_bwd_reduce(a.partTs, nullptr, a.g.col_groups, r.C,
+                           (2 * a.g.s - 1) * (2 * a.g.s - 1), r.dTsub, nullptr, st);
 }
 
 }  // namespace wbmm

@@ -107,14 +107,38 @@ __device__ __forceinline__ void load_xtile(const Geo& g, const TIn* __restrict__
 //                       y_k*RP + x_k      (X-tile slot; the zero slot w*RP when k >= d) }.
 // With base(i) = y_i*(2w-1) + x_i + 2w(w-1), the table entry of M[i][k] is base(i) - offset and
 // that of the transposed matrix (M^T, used for dX) is L-1 - base(i) + offset.
+// With a sub-window side g.s (w = 2s) the hierarchical fold happens here
+// [gecl.asia reading notes, "Method" point 4]: a second copy of the table at Ts + round_up(L, 4)
+// holds T[q] + T_sub[q'] (one fp32 add, RNE, the same value an explicit fold stores) for the
+// offsets a same-sub-window pair can have (|dy|, |dx| < s; q' is that offset in the sub-table),
+// and K is walked by quadrants (lane group gq takes quadrant (gq >> 1, gq & 1)), which for
+// w = 2s are exactly the sub-windows. A pair (i, k) is then inside one sub-window exactly when
+// output pixel i lies in quadrant gq, so contract_f32 picks the copy per lane and tile.
 __device__ __forceinline__ void load_table_f32(const Geo& g, const float* __restrict__ T, int c, float* Ts,
-                               int2* Offs) {
+                               int2* Offs, const float* __restrict__ Tsub = nullptr) {
   if (T) {
     const float* Tc = T + (size_t)c * g.L;
     for (int q = threadIdx.x; q < g.L; q += kThreads) Ts[q] = Tc[q];
+    if (g.s) {
+      const int s = g.s, s2m1 = 2 * g.s - 1;
+      const float* Sc = Tsub + (size_t)c * s2m1 * s2m1;
+      float* Tf = Ts + (g.L + 3) / 4 * 4;
+      for (int q = threadIdx.x; q < g.L; q += kThreads) {
+        const int oy = q / g.w2m1 - (g.w - 1), ox = q % g.w2m1 - (g.w - 1);
+        float v = Tc[q];
+        if (oy > -s && oy < s && ox > -s && ox < s) v = v + Sc[(oy + s - 1) * s2m1 + ox + s - 1];
+        Tf[q] = v;
+      }
+    }
   }
   for (int e = threadIdx.x; e < 4 * g.KQ; e += kThreads) {
-    const int k = e;  // e = gq*KQ + s is exactly the pixel index
+    int k;
+    if (g.s) {  // quadrant order; 4 KQ = d for even w
+      const int gq = e / g.KQ, sq = e - gq * g.KQ;
+      k = ((gq >> 1) * g.s + sq / g.s) * g.w + (gq & 1) * g.s + sq % g.s;
+    } else {
+      k = e;  // e = gq*KQ + s is exactly the pixel index
+    }
     const int kc = k > g.d - 1 ? g.d - 1 : k;
     uint32_t y, xx;
     fdivmod((uint32_t)kc, g.fd_w, y, xx);
@@ -159,7 +183,9 @@ __device__ __forceinline__ int row_base(const Geo& g, int rt, int lane) {
 // acc[t] (16 x 16, rows of tile wr*RPW + t, columns ct*16..ct*16+15) = sum_k A[i][k] * X[k][n].
 // ASRC 0: A from the table in LDS; ASRC 1: A staged chunk by chunk from the cached M in memory.
 // FLIP: use M^T (the adjoint, for dX).
-template <int RPW, int WR, int ASRC, bool FLIP>
+// HIER: the table path with the on-chip fold (see load_table_f32): each tile reads the folded
+// copy in the lane groups whose quadrant holds the tile row's output pixel.
+template <int RPW, int WR, int ASRC, bool FLIP, bool HIER = false>
 __device__ __forceinline__ void contract_f32(const Geo& g, int c, const float* __restrict__ M,
                                              const float* Xs, float* Ms, const float* Ts,
                                              const int2* Offs, int wr, int ct, v4f (&acc)[RPW]) {
@@ -172,10 +198,20 @@ __device__ __forceinline__ void contract_f32(const Geo& g, int c, const float* _
 
   if constexpr (ASRC == 0) {
     int abase[RPW];
+    const float* tp[RPW];
 #pragma unroll
     for (int t = 0; t < RPW; ++t) {
       const int b = row_base(g, wr * RPW + t, lane);
       abase[t] = FLIP ? (g.L - 1 - b) : b;
+      tp[t] = Ts;
+      if constexpr (HIER) {
+        int i = (wr * RPW + t) * 16 + (lane & 15);
+        if (i > g.d - 1) i = g.d - 1;
+        uint32_t yi, xi;
+        fdivmod((uint32_t)i, g.fd_w, yi, xi);
+        const int sub = ((int)yi / g.s) * 2 + (int)xi / g.s;
+        if (sub == gq) tp[t] = Ts + (g.L + 3) / 4 * 4;
+      }
     }
     for (int s = 0; s < g.KQ; ++s) {
       const int2 o = oc[s];
@@ -183,7 +219,7 @@ __device__ __forceinline__ void contract_f32(const Geo& g, int c, const float* _
 #pragma unroll
       for (int t = 0; t < RPW; ++t) {
         if ((wr * RPW + t) * 16 < g.d) {
-          const float av = Ts[FLIP ? abase[t] + o.x : abase[t] - o.x];
+          const float av = tp[t][FLIP ? abase[t] + o.x : abase[t] - o.x];
           acc[t] = mfma_f32(av, bv, acc[t]);
         }
       }

@@ -16,9 +16,10 @@ struct FwdArgs {
   void* y;         // layer output (window mode with a mix: the pre-mix buffer)
   int out_bf16;
   int mix_here;    // apply the 3x3 mix in this kernel (image mode only)
+  const float* tsub;  // sub-window tables folded on chip (HIER), or null
 };
 
-template <typename TIn, int RPW, int WR, int ASRC>
+template <typename TIn, int RPW, int WR, int ASRC, bool HIER = false>
 __global__ void __launch_bounds__(kThreads) k_wbmm_fwd(FwdArgs a) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   const Geo& g = a.g;
@@ -37,7 +38,8 @@ __global__ void __launch_bounds__(kThreads) k_wbmm_fwd(FwdArgs a) {
   if constexpr (kBf16) {
     if constexpr (ASRC == 0) load_table_bf16(g, (const uint16_t*)a.tab, c, (uint16_t*)tab, offs);
   } else {
-    load_table_f32(g, ASRC == 0 ? (const float*)a.tab : nullptr, c, (float*)tab, (int2*)offs);
+    load_table_f32(g, ASRC == 0 ? (const float*)a.tab : nullptr, c, (float*)tab, (int2*)offs,
+                   a.tsub);
   }
   load_xtile<TIn>(g, (const TIn*)a.x, c, colgrp, big);  // ends with a barrier
 
@@ -46,9 +48,9 @@ __global__ void __launch_bounds__(kThreads) k_wbmm_fwd(FwdArgs a) {
     contract_bf16<RPW, WR, ASRC>(g, c, (const uint16_t*)a.mat, (const uint16_t*)big,
                                  (uint16_t*)mchunk, (const uint16_t*)tab, offs, wr, ct, acc);
   } else {
-    contract_f32<RPW, WR, ASRC, false>(g, c, (const float*)a.mat, (const float*)big,
-                                       (float*)mchunk, (const float*)tab, (const int2*)offs, wr,
-                                       ct, acc);
+    contract_f32<RPW, WR, ASRC, false, HIER>(g, c, (const float*)a.mat, (const float*)big,
+                                             (float*)mchunk, (const float*)tab, (const int2*)offs,
+                                             wr, ct, acc);
   }
 
   if (!g.image_mode) {
@@ -94,26 +96,26 @@ __global__ void __launch_bounds__(kThreads) k_wbmm_fwd(FwdArgs a) {
 }
 
 // ---------------------------------------------------------------------------- dispatch
-template <typename TIn, int RPW, int WR, int ASRC>
+template <typename TIn, int RPW, int WR, int ASRC, bool HIER = false>
 static hipError_t launch_fwd_t(const FwdArgs& a, hipStream_t st) {
-  auto fn = k_wbmm_fwd<TIn, RPW, WR, ASRC>;
+  auto fn = k_wbmm_fwd<TIn, RPW, WR, ASRC, HIER>;
   hipError_t e = hipFuncSetAttribute((const void*)fn, hipFuncAttributeMaxDynamicSharedMemorySize,
                                      a.g.lds_total);
   if (e != hipSuccess) return e;
   return launch_main(fn, dim3(a.g.col_groups, a.g.C, 1), dim3(kThreads), a.g.lds_total, st, a);
 }
 
-template <typename TIn, int ASRC>
+template <typename TIn, int ASRC, bool HIER = false>
 static hipError_t launch_fwd_tiles(const FwdArgs& a, hipStream_t st) {
   const int RPW = a.g.RPW, WR = a.g.WR;
   if (WR == 1) {
-    if (RPW == 4) return launch_fwd_t<TIn, 4, 1, ASRC>(a, st);
-    if (RPW == 7) return launch_fwd_t<TIn, 7, 1, ASRC>(a, st);
-    if (RPW == 13) return launch_fwd_t<TIn, 13, 1, ASRC>(a, st);
-    if (RPW == 16) return launch_fwd_t<TIn, 16, 1, ASRC>(a, st);
+    if (RPW == 4) return launch_fwd_t<TIn, 4, 1, ASRC, HIER>(a, st);
+    if (RPW == 7) return launch_fwd_t<TIn, 7, 1, ASRC, HIER>(a, st);
+    if (RPW == 13) return launch_fwd_t<TIn, 13, 1, ASRC, HIER>(a, st);
+    if (RPW == 16) return launch_fwd_t<TIn, 16, 1, ASRC, HIER>(a, st);
   } else {
-    if (RPW == 13) return launch_fwd_t<TIn, 13, 4, ASRC>(a, st);
-    if (RPW == 16) return launch_fwd_t<TIn, 16, 4, ASRC>(a, st);
+    if (RPW == 13) return launch_fwd_t<TIn, 13, 4, ASRC, HIER>(a, st);
+    if (RPW == 16) return launch_fwd_t<TIn, 16, 4, ASRC, HIER>(a, st);
   }
   return hipErrorInvalidValue;
 }
@@ -123,11 +125,12 @@ static hipError_t launch_fwd_tiles(const FwdArgs& a, hipStream_t st) {
 static bool plan_fwd(Geo& g, const FwdRequest& r) {
   const bool cached = r.M != nullptr;
   const bool mix = r.mixw != nullptr;
-  if (!plan_geo(g, r.B, r.C, r.H, r.W, r.w, r.layout, r.in_bf16, cached, true, 0)) {
-    if (!plan_geo(g, r.B, r.C, r.H, r.W, r.w, r.layout, r.in_bf16, cached, false, 0)) return false;
+  const int s = r.Tsub ? r.s : 0;
+  if (!plan_geo(g, r.B, r.C, r.H, r.W, r.w, r.layout, r.in_bf16, cached, true, 0, s)) {
+    if (!plan_geo(g, r.B, r.C, r.H, r.W, r.w, r.layout, r.in_bf16, cached, false, 0, s)) return false;
   }
   if (g.image_mode && !mix && 4 * g.ipw * g.nWin < 3 * g.NT) {
-    if (!plan_geo(g, r.B, r.C, r.H, r.W, r.w, r.layout, r.in_bf16, cached, false, 0)) return false;
+    if (!plan_geo(g, r.B, r.C, r.H, r.W, r.w, r.layout, r.in_bf16, cached, false, 0, s)) return false;
   }
   return true;
 }
@@ -145,12 +148,14 @@ size_t forward_workspace(const FwdRequest& r) {
 }
 
 hipError_t launch_forward(const FwdRequest& r, hipStream_t st) {
-  if (fast_forward_ok(r)) return launch_forward_fast(r, st);
-  if (fast_bf16_forward_ok(r)) return launch_forward_fast_bf16(r, st);
+  // the fast paths have no on-chip fold: a sub-table takes the general path
+  if (!r.Tsub && fast_forward_ok(r)) return launch_forward_fast(r, st);
+  if (!r.Tsub && fast_bf16_forward_ok(r)) return launch_forward_fast_bf16(r, st);
   FwdArgs a{};
   if (!plan_fwd(a.g, r)) return hipErrorInvalidValue;
   a.x = r.x;
   a.tab = r.T;
+  a.tsub = r.Tsub;
   a.mat = r.M;
   a.mixw = r.mixw;
   a.out_bf16 = r.out_bf16;
@@ -174,7 +179,8 @@ hipError_t launch_forward(const FwdRequest& r, hipStream_t st) {
   }
   const bool cached = r.M != nullptr;
   hipError_t e;
-  if (r.in_bf16) e = cached ? launch_fwd_tiles<uint16_t, 1>(a, st) : launch_fwd_tiles<uint16_t, 0>(a, st);
+  if (r.Tsub) e = launch_fwd_tiles<float, 0, true>(a, st);  // fp32 table path only (planned so)
+  else if (r.in_bf16) e = cached ? launch_fwd_tiles<uint16_t, 1>(a, st) : launch_fwd_tiles<uint16_t, 0>(a, st);
   else e = cached ? launch_fwd_tiles<float, 1>(a, st) : launch_fwd_tiles<float, 0>(a, st);
   if (e != hipSuccess) return e;
   if (!a.g.image_mode && mix)

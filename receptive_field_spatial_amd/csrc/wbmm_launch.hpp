@@ -19,6 +19,8 @@ struct FwdRequest {
   void* y;
   void* ws;
   size_t ws_bytes;
+  const float* Tsub;  // s x s sub-window tables folded on chip (fp32 table path, w = 2s), or null
+  int s;
 };
 
 struct BwdRequest {
@@ -34,6 +36,9 @@ struct BwdRequest {
   float* dmixw;
   void* ws;
   size_t ws_bytes;
+  const float* Tsub;  // as in FwdRequest; with it, dTsub (or null) receives the sub-table gradient
+  int s;
+  float* dTsub;
 };
 
 hipError_t launch_build_index(int w, int32_t* idx, hipStream_t st);

@@ -24,6 +24,7 @@ struct Geo {
   int B, C, H, W, w, d, L, w2m1;  // L = (2w-1)^2, w2m1 = 2w-1
   int Hp, Wp, nH, nW, nWin, N;    // padded map, window grid, windows per image, per channel
   int layout;
+  int s;            // hierarchical sub-window side folded on chip (w = 2s), or 0
   // fp32 K mapping
   int KQ, RP, XR;   // K-steps, window row pitch, X-tile stride per window (floats)
   // bf16 K mapping
@@ -66,9 +67,12 @@ constexpr int kMaxLds = 160 * 1024;
 // bf16: element type of x/T/M; cached: M read from memory (else formed from T in LDS);
 // want_image: ask for image mode (needed for an in-kernel 3x3 mix);
 // extra_big: bytes the caller needs in the big region beyond the X tile (backward's G tile).
+// hier_s: fold an s x s sub-window table on chip (fp32 table path, w = 2s only).
 inline bool plan_geo(Geo& g, int B, int C, int H, int W, int w, int layout, bool bf16,
-                     bool cached, bool want_image, int big_extra_tiles) {
+                     bool cached, bool want_image, int big_extra_tiles, int hier_s = 0) {
   g = Geo{};
+  if (hier_s && (bf16 || cached || 2 * hier_s != w)) return false;
+  g.s = hier_s;
   g.B = B; g.C = C; g.H = H; g.W = W; g.w = w; g.d = w * w;
   g.w2m1 = 2 * w - 1; g.L = g.w2m1 * g.w2m1;
   g.Hp = (H + w - 1) / w * w; g.Wp = (W + w - 1) / w * w;
@@ -89,8 +93,9 @@ inline bool plan_geo(Geo& g, int B, int C, int H, int W, int w, int layout, bool
   while (g.XSB % 64 != 8) g.XSB += 8;                // 8 lanes x 16 B cover all 32 banks
   g.CS = round_up(g.L + 24, 8) + 8;
 
-  // table region: fp32 -> L floats + offset table; bf16 -> 8 shifted copies + offsets
-  const int tab_bytes = bf16 ? 8 * g.CS * 2 : round_up(g.L, 4) * 4;
+  // table region: fp32 -> L floats (then the folded copy with a sub-table) + offset table;
+  // bf16 -> 8 shifted copies + offsets
+  const int tab_bytes = bf16 ? 8 * g.CS * 2 : (hier_s ? 2 : 1) * round_up(g.L, 4) * 4;
   const int off_bytes = bf16 ? round_up(g.KS * 4, 4) * 4 : 4 * g.KQ * 8;
 
   // X tile (+ cached-M chunk) bytes

@@ -153,6 +153,50 @@ def test_backward_validation(lib):
     assert lib.wbmm_backward_workspace_bytes(1, 2, 8, 8, 17, 0, 0) == 0
 
 
+def hier_fwd(lib, **kw):
+    a = dict(B=1, C=2, H=28, W=28, w=14, s=7, layout=0, x=FAKE, T=FAKE2, Ts=0x300000, mix=None,
+             z=None, y=0x40000000, ws=None, wsb=0)
+    a.update(kw)
+    return lib.wbmm_forward_hier(a["B"], a["C"], a["H"], a["W"], a["w"], a["s"], a["layout"],
+                                 a["x"], a["T"], a["Ts"], a["mix"], a["z"], a["y"], a["ws"],
+                                 a["wsb"], None)
+
+
+def hier_bwd(lib, **kw):
+    a = dict(B=1, C=2, H=28, W=28, w=14, s=7, layout=0, x=FAKE, T=FAKE2, Ts=0x300000, mix=None,
+             z=None, dy=0x380000, dx=0x400000, dT=0x500000, dTs=0x580000, dW=None, ws=None, wsb=0)
+    a.update(kw)
+    return lib.wbmm_backward_hier(a["B"], a["C"], a["H"], a["W"], a["w"], a["s"], a["layout"],
+                                  a["x"], a["T"], a["Ts"], a["mix"], a["z"], a["dy"], a["dx"],
+                                  a["dT"], a["dTs"], a["dW"], a["ws"], a["wsb"], None)
+
+
+def test_hier_validation(lib):
+    """The on-chip fold entry points: w = 2s only, both tables required, fp32 maps checked like
+    the plain calls, workspace sizes reported and enforced."""
+    for w, s in [(14, 2), (12, 4), (14, 14), (14, 0)]:
+        assert hier_fwd(lib, w=w, s=s) == R.WBMM_E_UNSUPPORTED, (w, s)
+        assert hier_bwd(lib, w=w, s=s) == R.WBMM_E_UNSUPPORTED, (w, s)
+        assert lib.wbmm_forward_hier_workspace_bytes(1, 2, 28, 28, w, s, 0, 1, 0) == 0
+        assert lib.wbmm_backward_hier_workspace_bytes(1, 2, 28, 28, w, s, 0, 0) == 0
+    assert "w = 2s" in err(lib)
+    assert hier_fwd(lib, Ts=None) == R.WBMM_E_INVALID
+    assert hier_fwd(lib, T=None) == R.WBMM_E_INVALID
+    assert hier_fwd(lib, y=FAKE) == R.WBMM_E_INVALID             # y aliases x
+    assert hier_fwd(lib, y=0x300000) == R.WBMM_E_INVALID         # y overlaps T_sub
+    assert hier_bwd(lib, w=18, s=9) == R.WBMM_E_UNSUPPORTED       # backward w <= 16
+    assert hier_bwd(lib, Ts=None) == R.WBMM_E_INVALID
+    assert hier_bwd(lib, mix=0x900000) == R.WBMM_E_INVALID       # mix without z_saved
+    assert hier_bwd(lib, dTs=0x300000) == R.WBMM_E_INVALID       # dT_sub aliases T_sub
+    assert hier_bwd(lib, dTs=0x500000) == R.WBMM_E_INVALID       # dT_sub aliases dT
+    need = lib.wbmm_backward_hier_workspace_bytes(1, 2, 28, 28, 14, 7, 0, 0)
+    plain = lib.wbmm_backward_workspace_bytes(1, 2, 28, 28, 14, 0, 0)
+    assert need > 0 and plain > 0
+    assert hier_bwd(lib) == R.WBMM_E_WORKSPACE
+    assert hier_bwd(lib, ws=0xA00000, wsb=need - 1) == R.WBMM_E_WORKSPACE
+    assert lib.wbmm_forward_hier_workspace_bytes(1, 2, 128, 128, 14, 7, 0, 1, 0) > 0  # window-mode mix
+
+
 def test_last_error_is_per_thread(lib):
     import threading
     assert lib.wbmm_build_index(0, FAKE, None) == R.WBMM_E_INVALID

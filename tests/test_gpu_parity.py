@@ -485,3 +485,95 @@ def test_errors_enqueue_nothing():
     assert e.value.status == Rm.WBMM_E_UNSUPPORTED
     torch.cuda.synchronize()
     assert torch.all(y == 7.0)
+
+
+# ----------------------------------------------------------------------------- hierarchical fold
+def hier_inputs(B, C, H, W, w, s, seed, mix):
+    x = synth.normal_f32((B, C, H, W), 1.0, seed=seed)
+    T = synth.normal_f32((C, 2 * w - 1, 2 * w - 1), 0.02, seed=seed + 1)
+    Ts = synth.normal_f32((C, 2 * s - 1, 2 * s - 1), 0.02, seed=seed + 2)
+    Wm = synth.normal_f32((C, 3, 3), 0.1, seed=seed + 3) if mix else None
+    return x, T, Ts, Wm
+
+
+@pytest.mark.parametrize("B,C,H,W,w,s", [(2, 3, 28, 28, 14, 7), (1, 2, 30, 25, 14, 7),
+                                         (2, 3, 8, 8, 4, 2), (1, 2, 12, 18, 6, 3),
+                                         (2, 2, 16, 16, 8, 4), (1, 2, 128, 128, 14, 7)])
+@pytest.mark.parametrize("mix", [False, True])
+def test_forward_hier(B, C, H, W, w, s, mix):
+    """The fold on chip (image and window mode, ragged maps) against the oracle's explicit fold."""
+    say(f"forward hier B={B} C={C} H={H} W={W} w={w} s={s} mix={mix}")
+    x, T, Ts, Wm = hier_inputs(B, C, H, W, w, s, 70, mix)
+    zs = torch.empty((B, C, H, W), device="cuda")
+    y = R().wbmm_forward_hier(dev(x), w, s, dev(T), dev(Ts), mix_w=dev(Wm) if mix else None,
+                              z_save=zs)
+    want_y, want_z = O.layer_forward_hier(x.astype(np.float64), w, s, T, Ts, Wmix=Wm)
+    assert_f32(host(y), want_y, "y")
+    assert_f32(host(zs), want_z, "z")
+
+
+@pytest.mark.parametrize("w,s", [(14, 7), (4, 2)])
+def test_forward_hier_one_hot_bitwise(w, s):
+    """One-hot T and T_sub at different offsets per channel: every output is a sum of at most two
+    input pixels with weight 1 (or one with weight 2), exact in fp32, so the on-chip fold must
+    match the oracle's explicit fold bit for bit."""
+    B, C, H, W = 3, 5, 2 * w, 3 * w
+    say(f"forward hier one-hot w={w} s={s}")
+    x = synth.normal_f32((B, C, H, W), 1.0, seed=75)
+    L1, Ls = 2 * w - 1, 2 * s - 1
+    T = np.zeros((C, L1, L1), np.float32)
+    Ts = np.zeros((C, Ls, Ls), np.float32)
+    c = np.arange(1, C)
+    T[c, (c * 3) % L1, (c * 7 + 1) % L1] = 1.0
+    Ts[c, (c * 2 + 1) % Ls, (c * 5) % Ls] = 1.0
+    T[0, w - 1, w - 1] = 1.0  # channel 0: both at offset 0 -> z = 2 x
+    Ts[0, s - 1, s - 1] = 1.0
+    y = R().wbmm_forward_hier(dev(x), w, s, dev(T), dev(Ts))
+    want, _ = O.layer_forward_hier(x.astype(np.float64), w, s, T, Ts)
+    assert np.array_equal(host(y), want.astype(np.float32))
+
+
+@pytest.mark.parametrize("B,C,H,W,w,s", [(2, 3, 28, 28, 14, 7), (1, 2, 30, 25, 14, 7),
+                                         (2, 3, 8, 8, 4, 2), (1, 2, 12, 18, 6, 3),
+                                         (2, 2, 16, 16, 8, 4), (1, 2, 128, 128, 14, 7)])
+@pytest.mark.parametrize("mix", [False, True])
+def test_backward_hier(B, C, H, W, w, s, mix):
+    """dx, dT, dT_sub (and dWmix) of the folded layer against the oracle; image mode fuses the mix
+    adjoint, window mode (128x128) runs it as separate passes. Determinism: a second call is
+    bitwise identical."""
+    say(f"backward hier B={B} C={C} H={H} W={W} w={w} s={s} mix={mix}")
+    x, T, Ts, Wm = hier_inputs(B, C, H, W, w, s, 80, mix)
+    dy = synth.normal_f32((B, C, H, W), 1.0, seed=85)
+    xd, Td, Tsd, dyd = dev(x), dev(T), dev(Ts), dev(dy)
+    Wd = dev(Wm) if mix else None
+    zs = None
+    if mix:
+        zs = torch.empty_like(xd)
+        R().wbmm_forward_hier(xd, w, s, Td, Tsd, mix_w=Wd, z_save=zs)
+    dx, dT, dTs, dW = R().wbmm_backward_hier(xd, dyd, w, s, Td, Tsd, mix_w=Wd, z_saved=zs)
+    z64 = host(zs).astype(np.float64) if mix else None
+    wdx, wdT, wdTs, wdW = O.layer_backward_hier(x.astype(np.float64), dy.astype(np.float64), w, s,
+                                                T, Ts, Wmix=Wm, z=z64)
+    assert_f32(host(dx), wdx, "dx")
+    assert_f32(host(dT), wdT, "dT")
+    assert_f32(host(dTs), wdTs, "dT_sub")
+    if mix:
+        assert_f32(host(dW), wdW, "dWmix")
+    dx2, dT2, dTs2, _ = R().wbmm_backward_hier(xd, dyd, w, s, Td, Tsd, mix_w=Wd, z_saved=zs)
+    assert torch.equal(dx, dx2) and torch.equal(dT, dT2) and torch.equal(dTs, dTs2)
+
+
+def test_backward_hier_partial_outputs():
+    """Only dT_sub, or only dx: the skipped outputs stay untouched and the others match."""
+    B, C, H, W, w, s = 2, 3, 28, 28, 14, 7
+    say("backward hier partial outputs")
+    x, T, Ts, _ = hier_inputs(B, C, H, W, w, s, 90, False)
+    dy = synth.normal_f32((B, C, H, W), 1.0, seed=95)
+    xd, Td, Tsd, dyd = dev(x), dev(T), dev(Ts), dev(dy)
+    _, dT0, dTs, _ = R().wbmm_backward_hier(xd, dyd, w, s, Td, Tsd, dx=False, dT=False)
+    assert dT0 is None
+    dx, _, dTs0, _ = R().wbmm_backward_hier(xd, dyd, w, s, Td, Tsd, dT=False, dT_sub=False)
+    assert dTs0 is None
+    wdx, _, wdTs, _ = O.layer_backward_hier(x.astype(np.float64), dy.astype(np.float64), w, s, T, Ts)
+    assert_f32(host(dTs), wdTs, "dT_sub")
+    assert_f32(host(dx), wdx, "dx")
