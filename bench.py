@@ -81,13 +81,16 @@ def accounting(wl):
 
     flops: 2d per output element for the window contraction, 4d for its backward (dX + dT),
     18 per element for the 3x3 mix and 36 for its backward (data + weight).
-    bytes: every input read once, every output written once, plus the per-channel table.
+    bytes: every input read once, every output written once, plus the per-channel table (and
+    the sub-window table when the fold is on; its gradient in the backward).
     """
     d = wl.w * wl.w
     E = wl.B * wl.C * wl.H * wl.W
     esz = 2 if wl.dtype == "bf16" else 4
     L = (2 * wl.w - 1) ** 2
     tab = wl.C * L * esz
+    if wl.s is not None:
+        tab += wl.C * (2 * wl.s - 1) ** 2 * esz
     fwd_flops = E * (2 * d + (18 if wl.mix else 0))
     fwd_bytes = E * esz * (2 + (1 if wl.backward else 0)) + tab + (wl.C * 36 if wl.mix else 0)
     acc = {"E": E, "d": d, "fwd_flops": fwd_flops, "fwd_bytes": fwd_bytes}
@@ -111,14 +114,20 @@ def cpu_baseline(wl, budget_s: float = 10.0):
     x = inp["x"].astype(np.float64)
     T = inp["T"].astype(np.float64)
     Wm = inp.get("Wmix")
+    Ts = inp["T_sub"].astype(np.float64) if wl.s is not None else None
     dy = inp["dY"].astype(np.float64) if wl.backward else None
     times = []
     t_start = time.perf_counter()
     while True:
         t0 = time.perf_counter()
-        y, z = O.layer_forward(x, wl.w, T=T, Wmix=Wm)
-        if wl.backward:
-            O.layer_backward(x, dy, wl.w, T=T, Wmix=Wm, z=z)
+        if Ts is not None:
+            y, z = O.layer_forward_hier(x, wl.w, wl.s, T, Ts, Wmix=Wm)
+            if wl.backward:
+                O.layer_backward_hier(x, dy, wl.w, wl.s, T, Ts, Wmix=Wm, z=z)
+        else:
+            y, z = O.layer_forward(x, wl.w, T=T, Wmix=Wm)
+            if wl.backward:
+                O.layer_backward(x, dy, wl.w, T=T, Wmix=Wm, z=z)
         times.append(time.perf_counter() - t0)
         if time.perf_counter() - t_start >= budget_s and len(times) >= 3:
             break
@@ -212,26 +221,48 @@ def run(args):
     T = to_dev(inp["T"])
     Wm = to_dev(inp["Wmix"]) if wl.mix else None
     M = None
-    if wl.s is not None:  # inference caching + hierarchical fold, built once
-        M = R.wbmm_fold_hier(R.wbmm_build_matrix(T, wl.w), to_dev(inp["T_sub"]), wl.w, wl.s)
+    Tsub = to_dev(inp["T_sub"]) if wl.s is not None else None
+    hier_train = wl.s is not None and wl.backward  # fold on chip, dT_sub in the backward
+    if wl.s is not None and not wl.backward:  # inference: folded M built once and cached
+        M = R.wbmm_fold_hier(R.wbmm_build_matrix(T, wl.w), Tsub, wl.w, wl.s)
     L = 2 * wl.w - 1
     dT = torch.empty((wl.C, L, L), dtype=torch.float32, device=dev)
     dW = torch.empty((wl.C, 3, 3), dtype=torch.float32, device=dev) if wl.mix else None
+    dTs = (torch.empty((wl.C, 2 * wl.s - 1, 2 * wl.s - 1), dtype=torch.float32, device=dev)
+           if hier_train else None)
     ws_b = None
     if wl.backward:
-        nb = R.wbmm_backward_workspace_bytes(wl.B, wl.C, wl.H, wl.W, wl.w, has_mix=wl.mix)
+        if hier_train:
+            nb = R.wbmm_backward_hier_workspace_bytes(wl.B, wl.C, wl.H, wl.W, wl.w, wl.s,
+                                                      has_mix=wl.mix)
+        else:
+            nb = R.wbmm_backward_workspace_bytes(wl.B, wl.C, wl.H, wl.W, wl.w, has_mix=wl.mix)
         ws_b = torch.zeros(nb, dtype=torch.uint8, device=dev)
-    nf = R.wbmm_forward_workspace_bytes(wl.B, wl.C, wl.H, wl.W, wl.w, has_mix=wl.mix,
-                                        has_z_save=wl.backward)
+    if hier_train:
+        nf = R.wbmm_forward_hier_workspace_bytes(wl.B, wl.C, wl.H, wl.W, wl.w, wl.s,
+                                                 has_mix=wl.mix, has_z_save=True)
+    else:
+        nf = R.wbmm_forward_workspace_bytes(wl.B, wl.C, wl.H, wl.W, wl.w, has_mix=wl.mix,
+                                            has_z_save=wl.backward)
     ws_f = torch.empty(max(nf, 1), dtype=torch.uint8, device=dev) if nf else None
     stream = torch.cuda.current_stream()
     kw_tab = {"M": M} if M is not None else {"T": T}
 
     def fwd(s):
+        if hier_train:
+            R.wbmm_forward_hier(s["x"], wl.w, wl.s, T, Tsub, mix_w=Wm, y=s["y"], z_save=s["z"],
+                                workspace=ws_f, stream=stream)
+            return
         R.wbmm_forward(s["x"], wl.w, mix_w=Wm, y=s["y"], z_save=s.get("z"), workspace=ws_f,
                        stream=stream, **kw_tab)
 
     def bwd(s):
+        if hier_train:
+            R.wbmm_backward_hier(s["x"], s["dy"], wl.w, wl.s, T, Tsub, mix_w=Wm,
+                                 z_saved=s["z"] if wl.mix else None, dx=s["dx"], dT=dT,
+                                 dT_sub=dTs, dmix_w=dW if wl.mix else False, workspace=ws_b,
+                                 stream=stream)
+            return
         R.wbmm_backward(s["x"], s["dy"], wl.w, mix_w=Wm, z_saved=s["z"] if wl.mix else None,
                         dx=s["dx"], dT=dT, dmix_w=dW if wl.mix else False, workspace=ws_b,
                         stream=stream, **kw_tab)
@@ -311,7 +342,9 @@ def run(args):
         "data": "synthetic",
         "config": {"workload": wl.name, "B": wl.B, "C": wl.C, "H": wl.H, "W": wl.W, "w": wl.w,
                    "mix": wl.mix, "fold_s": wl.s, "pass": "fwd+bwd" if wl.backward else "fwd",
-                   "matrix": "cached M" if M is not None else "formed on chip from T",
+                   "matrix": ("cached M" if M is not None else
+                              "formed and folded on chip from T, T_sub" if hier_train else
+                              "formed on chip from T"),
                    "rotating_batches": nsets},
         "out_elems_per_s": round(acc["E"] / (ms_step / 1e3), 1),
         "roofline": roof,

@@ -341,13 +341,12 @@ size_t backward_workspace(const BwdRequest& r) {
   Geo g;
   if (!plan_bwd(g, r)) return 0;
   const size_t generic = bwd_ws_layout(g, r).total;
-  const size_t fast = r.Tsub ? 0 : fast_backward_workspace(r);
+  const size_t fast = fast_backward_ok(r) ? fast_backward_workspace(r) : 0;
   return generic > fast ? generic : fast;
 }
 
 hipError_t launch_backward(const BwdRequest& r, hipStream_t st) {
-  // the fast paths have no on-chip fold: a sub-table takes the general path
-  if (!r.Tsub && fast_backward_ok(r)) return launch_backward_fast(r, st);
+  if (fast_backward_ok(r)) return launch_backward_fast(r, st);  // folds a sub-table when w = 2s
   BwdArgs a{};
   if (!plan_bwd(a.g, r)) return hipErrorInvalidValue;
   const BwdWs wl = bwd_ws_layout(a.g, r);

@@ -19,6 +19,15 @@
 //     lane group, so for every K-step the table offset splits into a per-lane base plus a
 //     compile-time constant: every A operand is one LDS read with an immediate offset;
 //   * 3x3 mixes walk image columns with a sliding 3x3 register window (3 LDS reads per pixel).
+//
+// Hierarchical fold (WS = 2s): the s x s sub-windows of a window are exactly its four quadrants,
+// so a pair (i, j) shares a sub-window iff quadrant(i) == quadrant(j) [gecl.asia reading notes,
+// "Method", point 4]. Beside T_c the LDS holds a folded copy Tf_c = T_c + T_sub,c (the sub-table
+// added at offsets |dy|, |dx| < s, one fp32 add), and an MFMA A operand comes from the copy iff
+// the output pixel's quadrant equals the lane group's K quadrant: a per-lane, per-tile choice of
+// base address, so the inner loops are unchanged. The backward's table-gradient pass keeps the
+// row pairs of one sub-window band in chains of their own; their diagonals restricted to one
+// column half give dT_sub.
 #include "wbmm_core.hpp"
 #include "wbmm_launch.hpp"
 
@@ -42,6 +51,9 @@ struct FastArgs {
   double* partT;        // [C * groups][L]: one fp64 table-gradient partial per unit
   double* partW;        // [C * groups][9]
   int want_dx, want_dT, want_dW;
+  const float* Tsub;    // (C, 2s-1, 2s-1) sub-window tables, s = WS / 2 (hierarchical kernels)
+  double* partTs;       // [C * groups][(2s-1)^2]: sub-table gradient partials (backward)
+  int want_dTs;
 };
 
 constexpr int kWsThreads = 12 * 64;  // 8 consumer waves + 4 producer waves
@@ -79,13 +91,14 @@ struct Shape {
   static constexpr int C0 = 2 * WS * (WS - 1); // table index of offset (0,0) relative shift
   static constexpr int LP = (L + 3) / 4 * 4;   // padded table size (floats)
   static constexpr int XP = (D + 15) / 32 * 32 + 16;  // X-chunk window pitch: lane groups on disjoint banks
-  static constexpr int TSZ = LP + 72 > 4 * XP ? LP + 72 : 4 * XP;  // table (+ 36 doubles), later X chunks
   static constexpr int NWY = IH / WS, NWX = IW / WS, NWIN = NWY * NWX;
   static constexpr int IPW = 16 / NWIN;        // images per wave
   static constexpr int WPITCH = D;             // floats per window in LDS
   static constexpr int RSZ = 16 * WPITCH;      // floats per wave region
   static constexpr int PLANE = IH * IW;
   static constexpr int CMAX = (QW - 1) * L1 + (QW - 1);  // largest in-quadrant table offset
+  static constexpr int LS1 = 2 * QW - 1;       // sub-window table side (s = QW)
+  static constexpr int LS = LS1 * LS1;
   static_assert(WS % 2 == 0 && IH % WS == 0 && IW % WS == 0 && 16 % NWIN == 0, "shape");
   static constexpr int COLS = IPW * IW;                   // image columns per wave
   static constexpr int CHUNK_IMGS = IW <= 64 ? (64 / IW < IPW ? 64 / IW : IPW) : 1;
@@ -157,23 +170,73 @@ struct PlaneLoad {
   }
 };
 
-// One table (C, L) row into registers (producer threads ptid = 0..255) and then into LDS.
+// Offset (dy, dx) = (q / L1, q % L1) - (WS-1) of table entry q lies in the sub-table's range.
 template <class S>
+__host__ __device__ constexpr bool central(int q) {
+  return q / S::L1 - (S::WS - 1) > -S::QW && q / S::L1 - (S::WS - 1) < S::QW &&
+         q % S::L1 - (S::WS - 1) > -S::QW && q % S::L1 - (S::WS - 1) < S::QW;
+}
+// Sub-table index of a central table entry q.
+template <class S>
+__device__ __forceinline__ int sub_index(int q) {
+  return (q / S::L1 - (S::WS - 1) + S::QW - 1) * S::LS1 + (q % S::L1 - (S::WS - 1) + S::QW - 1);
+}
+// Sub-table entry folded into table entry q: the entry at the same offset when q is central,
+// else 0. The load index is clamped, not guarded.
+template <class S>
+__device__ __forceinline__ float sub_entry(const float* __restrict__ Tsub, int c, int q) {
+  const bool in = central<S>(q);
+  const float v = Tsub[(size_t)c * S::LS + (in ? sub_index<S>(q) : 0)];
+  return in ? v : 0.f;
+}
+// Producer thread p loads table entries p + 256 j; at most one of them is central.
+template <class S>
+constexpr bool one_central_per_thread() {
+  for (int p = 0; p < 256; ++p) {
+    int n = 0;
+    for (int q = p; q < S::L; q += 256) n += central<S>(q) ? 1 : 0;
+    if (n > 1) return false;
+  }
+  return true;
+}
+
+// One table (C, L) row into registers (producer threads ptid = 0..255) and then into LDS; with
+// HIER also the central entries of the folded copy at Ts + LP (the only ones ever read there:
+// pairs inside one sub-window have offsets |dy|, |dx| < s).
+template <class S, bool HIER>
 struct TableLoad {
   static constexpr int NT = (S::L + 255) / 256;
+  static_assert(!HIER || one_central_per_thread<S>(), "one folded entry per producer thread");
   float v[NT];
-  __device__ __forceinline__ void issue(const float* __restrict__ T, int c, int ptid) {
+  float f;  // HIER: sub-table entry of this thread's central table entry (0 if it has none)
+  __device__ __forceinline__ void issue(const float* __restrict__ T,
+                                        const float* __restrict__ Tsub, int c, int ptid) {
 #pragma unroll
     for (int j = 0; j < NT; ++j) {
       const int q = ptid + 256 * j;
       v[j] = q < S::L ? T[(size_t)c * S::L + q] : 0.f;
+    }
+    if constexpr (HIER) {
+      int qc = -1;
+#pragma unroll
+      for (int j = 0; j < NT; ++j) {
+        const int q = ptid + 256 * j;
+        if (q < S::L && central<S>(q)) qc = q;
+      }
+      const float t = Tsub[(size_t)c * S::LS + (qc >= 0 ? sub_index<S>(qc) : 0)];
+      f = qc >= 0 ? t : 0.f;
     }
   }
   __device__ __forceinline__ void commit(float* Ts, int ptid) const {
 #pragma unroll
     for (int j = 0; j < NT; ++j) {
       const int q = ptid + 256 * j;
-      if (q < S::L) Ts[q] = v[j];
+      if (q < S::L) {
+        Ts[q] = v[j];
+        if constexpr (HIER) {
+          if (central<S>(q)) Ts[S::LP + q] = v[j] + f;
+        }
+      }
     }
   }
 };
@@ -203,7 +266,8 @@ __device__ constexpr int ktab(int s) { return (s / S::QW) * S::L1 + (s % S::QW);
 // at T0, with A from the table in LDS and B from the wave-unit's region (window n = lane % 16);
 // both are single LDS reads with immediate offsets.
 // Non-flipped A entry: base(i) - (qoff + ktab(s)); flipped (M^T): L-1-base(i) + qoff + ktab(s).
-template <class S, bool FLIP, int T0, int NT>
+// HIER: rows i in the lane group's own quadrant read the folded copy at Ts + LP.
+template <class S, bool FLIP, int T0, int NT, bool HIER = false>
 __device__ __forceinline__ void contract(const float* Ts, const float* R, int lane,
                                          v4f (&acc)[NT]) {
   const LaneGeo<S> lg(lane);
@@ -216,6 +280,10 @@ __device__ __forceinline__ void contract(const float* Ts, const float* R, int la
     const int base = (i / S::WS) * S::L1 + (i % S::WS) + S::C0;
     // non-flipped address = (base - qoff - CMAX) + (CMAX - ktab(s)), both parts >= 0
     abase[t] = FLIP ? Ts + (S::L - 1 - base + lg.qoff()) : Ts + (base - lg.qoff() - S::CMAX);
+    if constexpr (HIER) {
+      const int qi = ((i / S::WS) / S::QW) * 2 + (i % S::WS) / S::QW;
+      if (qi == lg.gq) abase[t] += S::LP;
+    }
     acc[t] = v4f{0.f, 0.f, 0.f, 0.f};
   }
 #pragma unroll
@@ -322,20 +390,24 @@ __device__ __forceinline__ void sweep_column(const float* R, const Col& col, F&&
 
 // ---------------------------------------------------------------------------- forward
 // 12 waves: 8 consumers (2 per SIMD; consumer c contracts row tiles half c >> 2 of wave-unit
-// c & 3) and 4 producers (wave-unit p). LDS: tables [2][LP] (by step parity) and regions
+// c & 3) and 4 producers (wave-unit p). LDS: tables [2][TP] (by step parity; TP = LP, or 2 LP
+// with the folded copy) and regions
 // [3][4][RSZ] (unit k in k % 3). Step k:
 //   consumers: contract unit k | barrier | accumulators -> region (z over X) | barrier
 //   producers: issue loads of unit k+1, epilogue (mix, stores) of unit k-1 | barrier |
 //              commit the loads | barrier
 // The mid-step barrier keeps a half from overwriting X while the other half still reads it.
-template <class S, int T0, int NT>
+template <class S, bool HIER>
+constexpr int table_pitch() { return HIER ? 2 * S::LP : S::LP; }
+
+template <class S, int T0, int NT, bool HIER>
 __device__ __forceinline__ void fwd_consumer(const FastArgs& a, const float* Tb, float* Rg, int wi,
                                              int nmine, int lane) {
   for (int k = -1; k <= nmine; ++k) {
     const bool work = k >= 0 && k < nmine;
     v4f acc[NT];
     float* R = Rg + (((k < 0 ? 0 : k) % 3) * 4 + wi) * S::RSZ;
-    if (work) contract<S, false, T0, NT>(Tb + (k & 1) * S::LP, R, lane, acc);
+    if (work) contract<S, false, T0, NT, HIER>(Tb + (k & 1) * table_pitch<S, HIER>(), R, lane, acc);
     __syncthreads();
     if (work) write_acc<S, T0, NT>(R, lane, acc);
     __syncthreads();
@@ -369,7 +441,7 @@ __device__ __forceinline__ void fwd_epilogue(const FastArgs& a, const float* R, 
   }
 }
 
-template <class S, bool MIX, bool ZS>
+template <class S, bool MIX, bool ZS, bool HIER>
 __device__ __forceinline__ void fwd_producer(const FastArgs& a, float* Tb, float* Rg, int wi,
                                              int nmine, int lane, int ptid) {
   for (int k = -1; k <= nmine; ++k) {
@@ -384,10 +456,10 @@ __device__ __forceinline__ void fwd_producer(const FastArgs& a, float* Tb, float
       }
     }
     PlaneLoad<S> pl;
-    TableLoad<S> tl;
+    TableLoad<S, HIER> tl;
     if (next) {
       const Unit Un = unit_of<S>(a, blockIdx.x + (k + 1) * gridDim.x);
-      tl.issue(a.T, Un.c, ptid);
+      tl.issue(a.T, a.Tsub, Un.c, ptid);
       pl.issue(a.x + Un.base, Un, wi * S::IPW, lane);
     }
     if (k >= 1)
@@ -395,35 +467,38 @@ __device__ __forceinline__ void fwd_producer(const FastArgs& a, float* Tb, float
                                lane);
     __syncthreads();
     if (next) {
-      tl.commit(Tb + ((k + 1) & 1) * S::LP, ptid);
-      pl.commit(Rg + (((k + 1) % 3) * 4 + wi) * S::RSZ, lane);
+      // with the fold's extra registers, the commit's address math is redone each step rather
+      // than held across the loop
+      const int tp = HIER ? opaque_lane(ptid) : ptid, pp = HIER ? opaque_lane(lane) : lane;
+      tl.commit(Tb + ((k + 1) & 1) * table_pitch<S, HIER>(), tp);
+      pl.commit(Rg + (((k + 1) % 3) * 4 + wi) * S::RSZ, pp);
     }
     __syncthreads();
   }
 }
 
-template <class S>
+template <class S, bool HIER>
 __global__ void __launch_bounds__(kWsThreads) k_fwd_ws(FastArgs a) {
   extern __shared__ __attribute__((aligned(16))) float smem_f[];
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   float* Tb = smem_f;
-  float* Rg = smem_f + 2 * S::LP;
+  float* Rg = smem_f + 2 * table_pitch<S, HIER>();
   const int NU = a.C * a.groups;
   const int nmine = (NU - (int)blockIdx.x + (int)gridDim.x - 1) / (int)gridDim.x;
   // Role loops run separately, each with the same barriers per step (a workgroup barrier counts
   // wave arrivals, not program locations), so each keeps only its own registers live.
   constexpr int H0 = (S::RT + 1) / 2;
   if (wave < 4) {
-    fwd_consumer<S, 0, H0>(a, Tb, Rg, wave, nmine, lane);
+    fwd_consumer<S, 0, H0, HIER>(a, Tb, Rg, wave, nmine, lane);
   } else if (wave < 8) {
-    fwd_consumer<S, H0, S::RT - H0>(a, Tb, Rg, wave - 4, nmine, lane);
+    fwd_consumer<S, H0, S::RT - H0, HIER>(a, Tb, Rg, wave - 4, nmine, lane);
   } else {
     const int wi = wave - 8, ptid = threadIdx.x - 8 * 64;
     const bool mix = a.mixw != nullptr, zs = a.zsave != nullptr;
-    if (mix && zs) fwd_producer<S, true, true>(a, Tb, Rg, wi, nmine, lane, ptid);
-    else if (mix) fwd_producer<S, true, false>(a, Tb, Rg, wi, nmine, lane, ptid);
-    else if (zs) fwd_producer<S, false, true>(a, Tb, Rg, wi, nmine, lane, ptid);
-    else fwd_producer<S, false, false>(a, Tb, Rg, wi, nmine, lane, ptid);
+    if (mix && zs) fwd_producer<S, true, true, HIER>(a, Tb, Rg, wi, nmine, lane, ptid);
+    else if (mix) fwd_producer<S, true, false, HIER>(a, Tb, Rg, wi, nmine, lane, ptid);
+    else if (zs) fwd_producer<S, false, true, HIER>(a, Tb, Rg, wi, nmine, lane, ptid);
+    else fwd_producer<S, false, false, HIER>(a, Tb, Rg, wi, nmine, lane, ptid);
   }
 }
 
@@ -447,10 +522,12 @@ __device__ constexpr bool slot_valid(int j) {
 //   acc_j[x1][x2] += sum_{y1 - y2 = dy_j} G_n[y1][x1] * X_n[y2][x2]
 // G rows from the LDS regions (any wave's), X rows from the workgroup's LDS chunk buffer (4
 // windows at pitch XP). Lanes with x1 or x2 >= WS produce rows/columns of acc never read.
-template <class S, int Q>
+// HIER: pairs with y1, y2 in one sub-window band (y1 / s == y2 / s, possible only for |dy| < s,
+// i.e. slots j < 4) accumulate in b32[j] instead; at each flush they go to both acc64 and accs64.
+template <class S, int Q, bool HIER>
 __device__ __forceinline__ void dt_chunk(const float* regions, const float* xbuf, int n0, int kn,
                                          int xc, v4f (&a32)[8], double (&acc64)[8][4],
-                                         bool flush) {
+                                         v4f (&b32)[4], double (&accs64)[4][4], bool flush) {
   constexpr int WS = S::WS;
   const int n = n0 + kn;
   const float* g = regions + (n >> 4) * S::RSZ + (n & 15) * S::WPITCH + xc;
@@ -466,7 +543,13 @@ __device__ __forceinline__ void dt_chunk(const float* regions, const float* xbuf
 #define WBMM_DT_STEP(J)                                                             \
   if constexpr (Slot<WS, Q, J>::valid) {                                            \
     const int y2 = y1 - Slot<WS, Q, J>::dy;                                         \
-    if (y2 >= 0 && y2 < WS) a32[J] = mfma_f32(Av[y1], Bv[y2 < 0 ? 0 : (y2 < WS ? y2 : WS - 1)], a32[J]); \
+    const float bv = Bv[y2 < 0 ? 0 : (y2 < WS ? y2 : WS - 1)];                      \
+    if (y2 >= 0 && y2 < WS) {                                                       \
+      if (HIER && J < 4 && y1 / S::QW == y2 / S::QW)                                \
+        b32[J & 3] = mfma_f32(Av[y1], bv, b32[J & 3]);                              \
+      else                                                                          \
+        a32[J] = mfma_f32(Av[y1], bv, a32[J]);                                      \
+    }                                                                               \
   }
     WBMM_DT_STEP(0) WBMM_DT_STEP(1) WBMM_DT_STEP(2) WBMM_DT_STEP(3)
     WBMM_DT_STEP(4) WBMM_DT_STEP(5) WBMM_DT_STEP(6) WBMM_DT_STEP(7)
@@ -479,6 +562,17 @@ __device__ __forceinline__ void dt_chunk(const float* regions, const float* xbuf
 #pragma unroll
       for (int r = 0; r < 4; ++r) acc64[j][r] += (double)a32[j][r];
       a32[j] = v4f{0.f, 0.f, 0.f, 0.f};
+      if constexpr (HIER) {
+        if (j < 4) {
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const double b = (double)b32[j & 3][r];
+            acc64[j][r] += b;
+            accs64[j & 3][r] += b;
+          }
+          b32[j & 3] = v4f{0.f, 0.f, 0.f, 0.f};
+        }
+      }
     }
   }
 }
@@ -523,6 +617,48 @@ __device__ __forceinline__ void dt_partial_write(double* scr, const double (&acc
   WBMM_DT_SUM(0) WBMM_DT_SUM(1) WBMM_DT_SUM(2) WBMM_DT_SUM(3)
   WBMM_DT_SUM(4) WBMM_DT_SUM(5) WBMM_DT_SUM(6) WBMM_DT_SUM(7)
 #undef WBMM_DT_SUM
+}
+
+// Sub-table gradient partial from the band tiles (slots j < 4 with |dy_j| < s):
+//   pTs[dy_j + s-1][dx + s-1] = sum over x1 - x2 = dx, x1 / s == x2 / s of accs_j[x1][x2]
+// The two lane halves (x1 < s, x1 >= s) are exactly the two column halves of a window; they
+// are added in a fixed order as in dt_partial_write, whose LDS scratch this reuses.
+template <class S, int Q>
+__device__ __forceinline__ void dts_partial_write(double* scr, const double (&accs64)[4][4],
+                                                  double* pTs, int lane) {
+  constexpr int WS = S::WS, QW = S::QW, DD = WS * WS;
+  static_assert((WS + 1) / 2 == QW, "lane halves are the column halves");
+  const int x2 = lane & 15, g = lane >> 4;
+  const int dump = 7 * DD + lane;
+  wave_sync_lds();  // every read of the table-gradient tiles has been issued
+#define WBMM_DTS_ON(J) \
+  (Slot<WS, Q, J>::valid && Slot<WS, Q, J>::dy < QW && Slot<WS, Q, J>::dy > -QW)
+#define WBMM_DTS_PUT(J)                                                       \
+  if constexpr (WBMM_DTS_ON(J)) {                                             \
+    _Pragma("unroll") for (int r = 0; r < 4; ++r) {                           \
+      const int x1 = 4 * g + r;                                               \
+      scr[(x1 < WS && x2 < WS) ? J * DD + x1 * WS + x2 : dump] = accs64[J][r]; \
+    }                                                                         \
+  }
+  WBMM_DTS_PUT(0) WBMM_DTS_PUT(1) WBMM_DTS_PUT(2) WBMM_DTS_PUT(3)
+#undef WBMM_DTS_PUT
+  wave_sync_lds();
+  const int h = lane >> 5, dd = lane & 31, dxv = dd - (QW - 1);
+#define WBMM_DTS_SUM(J)                                                        \
+  if constexpr (WBMM_DTS_ON(J)) {                                              \
+    double s = 0.0;                                                            \
+    _Pragma("unroll") for (int k = 0; k < QW; ++k) {                           \
+      const int x1 = h * QW + k, xb = x1 - dxv;                                \
+      const bool ok = dd < S::LS1 && xb >= h * QW && xb < (h + 1) * QW;        \
+      const double v = scr[ok ? J * DD + x1 * WS + xb : J * DD];               \
+      s += ok ? v : 0.0;                                                       \
+    }                                                                          \
+    const double o = __shfl_down(s, 32, 64);                                   \
+    if (lane < S::LS1) pTs[(Slot<WS, Q, J>::dy + QW - 1) * S::LS1 + lane] = s + o; \
+  }
+  WBMM_DTS_SUM(0) WBMM_DTS_SUM(1) WBMM_DTS_SUM(2) WBMM_DTS_SUM(3)
+#undef WBMM_DTS_SUM
+#undef WBMM_DTS_ON
 }
 
 template <class S>
@@ -593,14 +729,22 @@ __device__ __forceinline__ void dx_store(const FastArgs& a, const Unit& U, int i
 //   dy -> G regions (mix adjoint in place, dWmix sums) | dX from the accumulators | table
 //   gradient: X streamed in 4-window chunks through the table region (loads of the next chunk
 //   in flight in registers), row-pair MFMAs per slot set, fp64 partial of the unit.
-template <class S>
-__global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3, 8))) k_bwd_ls(FastArgs a) {
+// Table region (floats): the table, with HIER its folded copy, then 36 doubles of dWmix sums;
+// later the X chunks.
+template <class S, bool HIER>
+constexpr int bwd_tsz() {
+  return table_pitch<S, HIER>() + 72 > 4 * S::XP ? table_pitch<S, HIER>() + 72 : 4 * S::XP;
+}
+
+template <class S, bool HIER>
+__global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(HIER ? 2 : 3, 8)))
+k_bwd_ls(FastArgs a) {
   extern __shared__ __attribute__((aligned(16))) float smem_f[];
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   float* Ts = smem_f;
   // per-wave dWmix sums, [4][9] doubles, in the table region's tail (free until the X chunks)
-  double* s_wred = (double*)(smem_f + S::LP);
-  float* regions = smem_f + S::TSZ;
+  double* s_wred = (double*)(smem_f + table_pitch<S, HIER>());
+  float* regions = smem_f + bwd_tsz<S, HIER>();
   float* R = regions + wave * S::RSZ;
   const int u = blockIdx.x;
   const Unit U = unit_of<S>(a, u);
@@ -623,7 +767,11 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3
   {
     PlaneLoad<S> pl;
     pl.issue(a.dy + U.base, U, ir0, lane);
-    for (int q = threadIdx.x; q < S::L; q += kThreads) Ts[q] = a.T[(size_t)U.c * S::L + q];
+    for (int q = threadIdx.x; q < S::L; q += kThreads) {
+      const float v = a.T[(size_t)U.c * S::L + q];
+      Ts[q] = v;
+      if constexpr (HIER) Ts[S::LP + q] = v + sub_entry<S>(a.Tsub, U.c, q);
+    }
     pl.commit(R, lane);
   }
   wave_sync_lds();
@@ -655,7 +803,7 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3
   // ---- dX = M^T . G, stored straight from the accumulators (G stays in LDS for dT)
   if (a.want_dx) {
     v4f acc[S::RT];
-    contract<S, true, 0, S::RT>(Ts, R, lane, acc);
+    contract<S, true, 0, S::RT, HIER>(Ts, R, lane, acc);
     dx_store<S>(a, U, ir0, acc, lane);
   }
 
@@ -671,6 +819,14 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3
     v4f a32[8];
 #pragma unroll
     for (int j = 0; j < 8; ++j) a32[j] = v4f{0.f, 0.f, 0.f, 0.f};
+    v4f b32[4];           // HIER: sub-window band chains of slots 0..3
+    double accs64[4][4];  // HIER: their fp64 sums (the sub-table gradient tiles)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      b32[j] = v4f{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int r = 0; r < 4; ++r) accs64[j][r] = 0.0;
+    }
     constexpr int CH_E = 4 * S::D;
     constexpr int EPT = (CH_E + kThreads - 1) / kThreads;
     int goff[EPT], loff[EPT], ekn[EPT];
@@ -713,10 +869,10 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3
       // max-abs bound)
       const bool flush = (ci & 3) == 3;
       switch (wave) {
-        case 0: dt_chunk<S, 0>(regions, xbuf, 4 * ci, kn, xc, a32, acc64, flush); break;
-        case 1: dt_chunk<S, 1>(regions, xbuf, 4 * ci, kn, xc, a32, acc64, flush); break;
-        case 2: dt_chunk<S, 2>(regions, xbuf, 4 * ci, kn, xc, a32, acc64, flush); break;
-        default: dt_chunk<S, 3>(regions, xbuf, 4 * ci, kn, xc, a32, acc64, flush); break;
+        case 0: dt_chunk<S, 0, HIER>(regions, xbuf, 4 * ci, kn, xc, a32, acc64, b32, accs64, flush); break;
+        case 1: dt_chunk<S, 1, HIER>(regions, xbuf, 4 * ci, kn, xc, a32, acc64, b32, accs64, flush); break;
+        case 2: dt_chunk<S, 2, HIER>(regions, xbuf, 4 * ci, kn, xc, a32, acc64, b32, accs64, flush); break;
+        default: dt_chunk<S, 3, HIER>(regions, xbuf, 4 * ci, kn, xc, a32, acc64, b32, accs64, flush); break;
       }
     }
     double* pT = a.partT + (size_t)u * S::L;
@@ -727,6 +883,17 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3
       case 1: dt_partial_write<S, 1>(scr, acc64, pT, lane); break;
       case 2: dt_partial_write<S, 2>(scr, acc64, pT, lane); break;
       default: dt_partial_write<S, 3>(scr, acc64, pT, lane); break;
+    }
+    if constexpr (HIER) {
+      if (a.want_dTs) {
+        double* pTs = a.partTs + (size_t)u * S::LS;
+        switch (wave) {
+          case 0: dts_partial_write<S, 0>(scr, accs64, pTs, lane); break;
+          case 1: dts_partial_write<S, 1>(scr, accs64, pTs, lane); break;
+          case 2: dts_partial_write<S, 2>(scr, accs64, pTs, lane); break;
+          default: dts_partial_write<S, 3>(scr, accs64, pTs, lane); break;
+        }
+      }
     }
   }
 }
@@ -751,10 +918,10 @@ constexpr bool lds_fits(int bytes, int wgs) {
   return (bytes + kLdsGranule - 1) / kLdsGranule * kLdsGranule * wgs <= kLdsPerCu;
 }
 
-template <class S>
-constexpr int fwd_lds() { return (2 * S::LP + 12 * S::RSZ) * 4; }
-template <class S>
-constexpr int bwd_lds() { return (S::TSZ + 4 * S::RSZ) * 4; }
+template <class S, bool HIER = false>
+constexpr int fwd_lds() { return (2 * table_pitch<S, HIER>() + 12 * S::RSZ) * 4; }
+template <class S, bool HIER = false>
+constexpr int bwd_lds() { return (bwd_tsz<S, HIER>() + 4 * S::RSZ) * 4; }
 
 template <class S>
 int groups(int B) { return (B + 4 * S::IPW - 1) / (4 * S::IPW); }
@@ -793,6 +960,13 @@ static_assert(lds_fits(fwd_lds<S14>(), 1) && lds_fits(fwd_lds<S28>(), 1) &&
 static_assert(lds_fits(bwd_lds<S14>(), 3) && lds_fits(bwd_lds<S28>(), 3) &&
                   lds_fits(bwd_lds<S56>(), 3),
               "three backward workgroups per CU");
+// with the folded table copy: still one persistent forward workgroup, two backward per CU
+static_assert(lds_fits(fwd_lds<S14, true>(), 1) && lds_fits(fwd_lds<S28, true>(), 1) &&
+                  lds_fits(fwd_lds<S56, true>(), 1),
+              "one persistent hierarchical forward workgroup per CU");
+static_assert(lds_fits(bwd_lds<S14, true>(), 2) && lds_fits(bwd_lds<S28, true>(), 2) &&
+                  lds_fits(bwd_lds<S56, true>(), 2),
+              "two hierarchical backward workgroups per CU");
 
 // Backward: one workgroup of 4 waves per unit.
 template <class S, class Fn>
@@ -809,14 +983,15 @@ hipError_t launch_ls(Fn fn, int lds, FastArgs a, hipStream_t st) {
 // Per-lane offsets within a unit are ints: ir * C * plane + pixel, ir < 16 images.
 bool offsets_fit(int C, int H, int W) { return (size_t)16 * C * H * W < ((size_t)1 << 31); }
 
+// A sub-table is folded on chip when its sub-windows are the quadrants (w = 2s).
 bool fast_forward_ok(const FwdRequest& r) {
-  return !r.in_bf16 && !r.out_bf16 && r.T && !r.M &&
+  return !r.in_bf16 && !r.out_bf16 && r.T && !r.M && (!r.Tsub || 2 * r.s == r.w) &&
          fast_shape(r.H, r.W, r.w, r.layout) != FS_NONE && offsets_fit(r.C, r.H, r.W);
 }
 
 bool fast_backward_ok(const BwdRequest& r) {
-  return r.T && !r.M && fast_shape(r.H, r.W, r.w, r.layout) != FS_NONE &&
-         offsets_fit(r.C, r.H, r.W);
+  return r.T && !r.M && (!r.Tsub || 2 * r.s == r.w) &&
+         fast_shape(r.H, r.W, r.w, r.layout) != FS_NONE && offsets_fit(r.C, r.H, r.W);
 }
 
 hipError_t launch_forward_fast(const FwdRequest& r, hipStream_t st) {
@@ -828,10 +1003,18 @@ hipError_t launch_forward_fast(const FwdRequest& r, hipStream_t st) {
   a.mixw = r.mixw;
   a.zsave = (float*)r.zsave;
   a.y = (float*)r.y;
+  a.Tsub = r.Tsub;
+  const bool h = r.Tsub != nullptr;
   switch (fast_shape(r.H, r.W, r.w, r.layout)) {
-    case FS_14_14_14: return launch_ws<S14>(k_fwd_ws<S14>, fwd_lds<S14>(), a, st);
-    case FS_14_28_28: return launch_ws<S28>(k_fwd_ws<S28>, fwd_lds<S28>(), a, st);
-    case FS_14_56_56: return launch_ws<S56>(k_fwd_ws<S56>, fwd_lds<S56>(), a, st);
+    case FS_14_14_14:
+      return h ? launch_ws<S14>(k_fwd_ws<S14, true>, fwd_lds<S14, true>(), a, st)
+               : launch_ws<S14>(k_fwd_ws<S14, false>, fwd_lds<S14>(), a, st);
+    case FS_14_28_28:
+      return h ? launch_ws<S28>(k_fwd_ws<S28, true>, fwd_lds<S28, true>(), a, st)
+               : launch_ws<S28>(k_fwd_ws<S28, false>, fwd_lds<S28>(), a, st);
+    case FS_14_56_56:
+      return h ? launch_ws<S56>(k_fwd_ws<S56, true>, fwd_lds<S56, true>(), a, st)
+               : launch_ws<S56>(k_fwd_ws<S56, false>, fwd_lds<S56>(), a, st);
     default: return hipErrorInvalidValue;
   }
 }
@@ -846,7 +1029,8 @@ size_t fast_backward_workspace(const BwdRequest& r) {
   }
   auto al = [](size_t v) { return (v + 255) / 256 * 256; };
   const size_t L = (size_t)(2 * r.w - 1) * (2 * r.w - 1);
-  return al((size_t)r.C * g * L * 8) + al((size_t)r.C * g * 9 * 8);
+  const size_t Ls = r.Tsub ? (size_t)(2 * r.s - 1) * (2 * r.s - 1) : 0;
+  return al((size_t)r.C * g * L * 8) + al((size_t)r.C * g * 9 * 8) + al((size_t)r.C * g * Ls * 8);
 }
 
 hipError_t launch_backward_fast(const BwdRequest& r, hipStream_t st) {
@@ -866,6 +1050,8 @@ hipError_t launch_backward_fast(const BwdRequest& r, hipStream_t st) {
   unsigned char* ws = (unsigned char*)r.ws;
   a.partT = (double*)ws;
   a.partW = (double*)(ws + al((size_t)r.C * g * L * 8));
+  a.partTs = (double*)(ws + al((size_t)r.C * g * L * 8) + al((size_t)r.C * g * 9 * 8));
+  a.Tsub = r.Tsub;
   a.x = r.x;
   a.T = r.T;
   a.mixw = r.mixw;
@@ -877,15 +1063,31 @@ hipError_t launch_backward_fast(const BwdRequest& r, hipStream_t st) {
   a.want_dx = r.dx != nullptr;
   a.want_dT = r.dT != nullptr;
   a.want_dW = (r.mixw && r.dmixw) ? 1 : 0;
+  a.want_dTs = (r.Tsub && r.dTsub) ? 1 : 0;
+  if (a.want_dTs) a.want_dT = 1;  // the sub-table gradient comes out of the table-gradient pass
+  if (!a.want_dx && !a.want_dT && !a.want_dW) return hipSuccess;
+  const bool h = r.Tsub != nullptr;
   hipError_t e;
   switch (fs) {
-    case FS_14_14_14: e = launch_ls<S14>(k_bwd_ls<S14>, bwd_lds<S14>(), a, st); break;
-    case FS_14_28_28: e = launch_ls<S28>(k_bwd_ls<S28>, bwd_lds<S28>(), a, st); break;
-    default: e = launch_ls<S56>(k_bwd_ls<S56>, bwd_lds<S56>(), a, st); break;
+    case FS_14_14_14:
+      e = h ? launch_ls<S14>(k_bwd_ls<S14, true>, bwd_lds<S14, true>(), a, st)
+            : launch_ls<S14>(k_bwd_ls<S14, false>, bwd_lds<S14>(), a, st);
+      break;
+    case FS_14_28_28:
+      e = h ? launch_ls<S28>(k_bwd_ls<S28, true>, bwd_lds<S28, true>(), a, st)
+            : launch_ls<S28>(k_bwd_ls<S28, false>, bwd_lds<S28>(), a, st);
+      break;
+    default:
+      e = h ? launch_ls<S56>(k_bwd_ls<S56, true>, bwd_lds<S56, true>(), a, st)
+            : launch_ls<S56>(k_bwd_ls<S56, false>, bwd_lds<S56>(), a, st);
+      break;
   }
   if (e != hipSuccess || (!a.want_dT && !a.want_dW)) return e;
-  return launch_bwd_reduce(a.partT, a.want_dW ? a.partW : nullptr, g, r.C, (int)L,
-                           a.want_dT ? r.dT : nullptr, a.want_dW ? r.dmixw : nullptr, st);
+  e = launch_bwd_reduce(a.partT, a.want_dW ? a.partW : nullptr, g, r.C, (int)L,
+                        r.dT, a.want_dW ? r.dmixw : nullptr, st);
+  if (e != hipSuccess || !a.want_dTs) return e;
+  return launch_bwd_reduce(a.partTs, nullptr, g, r.C, (2 * r.s - 1) * (2 * r.s - 1), r.dTsub,
+                           nullptr, st);
 }
 
 }  // namespace wbmm

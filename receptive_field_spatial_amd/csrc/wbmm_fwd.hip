@@ -148,8 +148,7 @@ size_t forward_workspace(const FwdRequest& r) {
 }
 
 hipError_t launch_forward(const FwdRequest& r, hipStream_t st) {
-  // the fast paths have no on-chip fold: a sub-table takes the general path
-  if (!r.Tsub && fast_forward_ok(r)) return launch_forward_fast(r, st);
+  if (fast_forward_ok(r)) return launch_forward_fast(r, st);  // folds a sub-table when w = 2s
   if (!r.Tsub && fast_bf16_forward_ok(r)) return launch_forward_fast_bf16(r, st);
   FwdArgs a{};
   if (!plan_fwd(a.g, r)) return hipErrorInvalidValue;

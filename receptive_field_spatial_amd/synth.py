@@ -79,6 +79,10 @@ WORKLOADS: Dict[str, Workload] = {
                             note="dense-prediction map padded 128->140, fold + 3x3 mix"),
     "train_w14": Workload("train_w14", B=64, C=192, H=28, W=28, w=14, mix=True, backward=True,
                           note="fp32 training step: forward + backward with 3x3 mix"),
+    "train_w14_hier": Workload("train_w14_hier", B=64, C=192, H=28, W=28, w=14, s=7, mix=True,
+                               backward=True,
+                               note="fp32 training step with the 7x7 sub-window table folded on "
+                                    "chip and its gradient"),
 }
 
 

@@ -577,3 +577,73 @@ def test_backward_hier_partial_outputs():
     wdx, _, wdTs, _ = O.layer_backward_hier(x.astype(np.float64), dy.astype(np.float64), w, s, T, Ts)
     assert_f32(host(dTs), wdTs, "dT_sub")
     assert_f32(host(dx), wdx, "dx")
+
+
+@pytest.mark.parametrize("B,C,H", [(5, 3, 14), (18, 2, 28), (5, 2, 56)])
+@pytest.mark.parametrize("mix", [False, True])
+def test_hier_fast_shapes(B, C, H, mix):
+    """w = 14, s = 7 on the whole-image shapes (14², 28², 56² NCHW), where the fold runs in the
+    fast kernels: the folded copy picked per output quadrant and the sub-window band chains of
+    the table gradient. Ragged batches leave the last unit part empty."""
+    w, s = 14, 7
+    say(f"hier fast shapes B={B} C={C} H=W={H} mix={mix}")
+    x, T, Ts, Wm = hier_inputs(B, C, H, H, w, s, 100, mix)
+    dy = synth.normal_f32((B, C, H, H), 1.0, seed=105)
+    xd, Td, Tsd, dyd = dev(x), dev(T), dev(Ts), dev(dy)
+    Wd = dev(Wm) if mix else None
+    zs = torch.empty_like(xd)
+    y = R().wbmm_forward_hier(xd, w, s, Td, Tsd, mix_w=Wd, z_save=zs)
+    want_y, want_z = O.layer_forward_hier(x.astype(np.float64), w, s, T, Ts, Wmix=Wm)
+    assert_f32(host(y), want_y, "y")
+    assert_f32(host(zs), want_z, "z")
+    dx, dT, dTs, dW = R().wbmm_backward_hier(xd, dyd, w, s, Td, Tsd, mix_w=Wd,
+                                             z_saved=zs if mix else None)
+    z64 = host(zs).astype(np.float64) if mix else None
+    wdx, wdT, wdTs, wdW = O.layer_backward_hier(x.astype(np.float64), dy.astype(np.float64), w, s,
+                                                T, Ts, Wmix=Wm, z=z64)
+    assert_f32(host(dx), wdx, "dx")
+    assert_f32(host(dT), wdT, "dT")
+    assert_f32(host(dTs), wdTs, "dT_sub")
+    if mix:
+        assert_f32(host(dW), wdW, "dWmix")
+
+
+def test_hier_fast_one_hot_bitwise():
+    """Fast-kernel fold on 28² images: one-hot T and T_sub per channel make every output a sum of
+    at most two inputs with weight 1 (channel 0: one input with weight 2), exact in fp32."""
+    w, s, B, C, H = 14, 7, 6, 5, 28
+    say("hier fast one-hot")
+    x = synth.normal_f32((B, C, H, H), 1.0, seed=110)
+    T = np.zeros((C, 27, 27), np.float32)
+    Ts = np.zeros((C, 13, 13), np.float32)
+    c = np.arange(1, C)
+    T[c, (c * 5) % 27, (c * 11 + 2) % 27] = 1.0
+    Ts[c, (c * 3 + 2) % 13, (c * 4) % 13] = 1.0
+    T[0, 13, 13] = 1.0
+    Ts[0, 6, 6] = 1.0
+    y = R().wbmm_forward_hier(dev(x), w, s, dev(T), dev(Ts))
+    want, _ = O.layer_forward_hier(x.astype(np.float64), w, s, T, Ts)
+    assert np.array_equal(host(y), want.astype(np.float32))
+
+
+def test_hier_fast_zero_sub_table_matches_plain():
+    """With T_sub = 0 the folded copy equals T, so the hierarchical fast forward and dX are bitwise
+    the plain kernels' results; dT (its sub-window band pairs summed in chains of their own) and
+    dT_sub (the plain layer's gradient summed over same-sub-window pairs) match the oracle."""
+    w, s, B, C, H = 14, 7, 20, 3, 28
+    say("hier fast zero sub-table")
+    x, T, _, Wm = hier_inputs(B, C, H, H, w, s, 120, True)
+    Ts = np.zeros((C, 13, 13), np.float32)
+    dy = synth.normal_f32((B, C, H, H), 1.0, seed=125)
+    xd, Td, Tsd, dyd, Wd = dev(x), dev(T), dev(Ts), dev(dy), dev(Wm)
+    zh, zp = torch.empty_like(xd), torch.empty_like(xd)
+    yh = R().wbmm_forward_hier(xd, w, s, Td, Tsd, mix_w=Wd, z_save=zh)
+    yp = R().wbmm_forward(xd, w, T=Td, mix_w=Wd, z_save=zp)
+    assert torch.equal(yh, yp) and torch.equal(zh, zp)
+    dxh, dTh, dTsh, dWh = R().wbmm_backward_hier(xd, dyd, w, s, Td, Tsd, mix_w=Wd, z_saved=zh)
+    dxp, dTp, dWp = R().wbmm_backward(xd, dyd, w, T=Td, mix_w=Wd, z_saved=zp)
+    assert torch.equal(dxh, dxp) and torch.equal(dWh, dWp)
+    _, wdT, wdTs, _ = O.layer_backward_hier(x.astype(np.float64), dy.astype(np.float64), w, s, T,
+                                            Ts, Wmix=Wm, z=host(zh).astype(np.float64))
+    assert_f32(host(dTh), wdT, "dT")
+    assert_f32(host(dTsh), wdTs, "dT_sub")
