@@ -279,11 +279,12 @@ __device__ __forceinline__ void contract(const float* Ts, const float* R, int la
     if (i > S::D - 1) i = S::D - 1;
     const int base = (i / S::WS) * S::L1 + (i % S::WS) + S::C0;
     // non-flipped address = (base - qoff - CMAX) + (CMAX - ktab(s)), both parts >= 0
-    abase[t] = FLIP ? Ts + (S::L - 1 - base + lg.qoff()) : Ts + (base - lg.qoff() - S::CMAX);
-    if constexpr (HIER) {
+    int off = FLIP ? S::L - 1 - base + lg.qoff() : base - lg.qoff() - S::CMAX;
+    if constexpr (HIER) {  // an integer offset, so the pointer stays a plain LDS address
       const int qi = ((i / S::WS) / S::QW) * 2 + (i % S::WS) / S::QW;
-      if (qi == lg.gq) abase[t] += S::LP;
+      off += qi == lg.gq ? S::LP : 0;
     }
+    abase[t] = Ts + off;
     acc[t] = v4f{0.f, 0.f, 0.f, 0.f};
   }
 #pragma unroll
