@@ -38,7 +38,7 @@ __all__ = [
     "padded_hw", "build_index", "build_matrix", "fold_hier", "sub_index",
     "pad_map", "partition", "reverse", "wbmm_forward", "mix_forward", "mix_backward",
     "wbmm_backward", "layer_forward", "layer_backward", "wbmm_backward_hier",
-    "layer_forward_hier", "layer_backward_hier",
+    "layer_forward_hier", "layer_backward_hier", "dw_conv_forward",
 ]
 
 
@@ -176,6 +176,29 @@ def mix_forward(z: np.ndarray, Wmix: np.ndarray) -> np.ndarray:
     for u in range(3):
         for t in range(3):
             y += Wd[None, :, u, t, None, None] * zp[:, :, u:u + H, t:t + W]
+    return y
+
+
+def dw_conv_forward(x: np.ndarray, Wdw: np.ndarray) -> np.ndarray:
+    """Standard k x k depthwise convolution (the pages' DW-Std baseline, reading R18).
+
+    Every output gathers the k*k neighbours around its own position from its own channel
+    [pith page, Fig. 1 and Fig. 2 captions]; it is the operator the pages time WBMM against
+    [pith page, Fig. 3 caption]. Written as the deep-learning frameworks define it:
+    y[b,c,h,v] = sum_{u,t} W[c,u,t] * x_pad[b,c,h+u,v+t], x_pad = x with p = k // 2 zero pixels
+    on every side, odd k, stride 1, no bias.
+    """
+    B, C, H, W = x.shape
+    k = Wdw.shape[-1]
+    assert Wdw.shape == (C, k, k) and k % 2 == 1
+    p = k // 2
+    xp = np.zeros((B, C, H + 2 * p, W + 2 * p), dtype=np.float64)
+    xp[:, :, p:p + H, p:p + W] = x
+    Wd = Wdw.astype(np.float64)
+    y = np.zeros((B, C, H, W), dtype=np.float64)
+    for u in range(k):
+        for t in range(k):
+            y += Wd[None, :, u, t, None, None] * xp[:, :, u:u + H, t:t + W]
     return y
 
 

@@ -10,7 +10,10 @@ Each test ties an oracle function to something the pages or the mathematics fix:
     real pixels per window, the dT of all-ones data counts pairs per offset;
   * the adjoint identity, torch autograd of the closed form, and finite differences for the
     backward;
-  * torch's conv2d for the 3x3 depthwise mix and its gradients.
+  * torch's conv2d for the 3x3 depthwise mix and its gradients;
+  * for the k x k depthwise convolution (the pages' DW-Std baseline): torch's conv2d, a pure-loop
+    brute force, one-hot kernels as exact shifts, and its two exact relations to the rest of the
+    oracle (k = 3 is the 3x3 mix; on a single-window image with k = 2w-1 it is WBMM).
 A plausible slip in the oracle (a flipped sign, a transposed matrix, a dropped term, a wrong
 crop/pad) fails at least one of these.
 """
@@ -519,3 +522,75 @@ def test_inputs_are_seeded_and_ordered():
     x = (rng.standard_normal((1, 8, 28, 28)) * 1.0).astype(np.float32)
     assert np.array_equal(a["x"], x)
     assert a["T"].shape == (8, 13, 13) and abs(float(a["T"].std()) - 0.02) < 0.004
+
+
+# ----------------------------------------------------------------------------- DW-Std (k x k)
+def dw_brute_force(x, Wd):
+    """Per-output sum over the k x k neighbours inside the image (pure Python loops)."""
+    B, C, H, W = x.shape
+    k = Wd.shape[-1]
+    p = k // 2
+    out = np.zeros((B, C, H, W))
+    for b in range(B):
+        for c in range(C):
+            for h in range(H):
+                for v in range(W):
+                    acc = 0.0
+                    for u in range(k):
+                        for t in range(k):
+                            hh, vv = h + u - p, v + t - p
+                            if 0 <= hh < H and 0 <= vv < W:
+                                acc += Wd[c, u, t] * x[b, c, hh, vv]
+                    out[b, c, h, v] = acc
+    return out
+
+
+@pytest.mark.parametrize("k,H,W", [(3, 9, 11), (5, 14, 14), (9, 12, 7), (13, 20, 17), (13, 5, 6)])
+def test_dw_conv_matches_torch_conv2d(k, H, W):
+    x = rnd((2, 4, H, W), seed=130 + k)
+    Wd = rnd((4, k, k), 0.05, seed=131 + k)
+    want = F.conv2d(torch.from_numpy(x), torch.from_numpy(Wd)[:, None], padding=k // 2,
+                    groups=4).numpy()
+    got = O.dw_conv_forward(x, Wd)
+    assert np.abs(got - want).max() <= 1e-12 * max(1.0, np.abs(want).max())
+
+
+@pytest.mark.parametrize("k,H,W", [(5, 7, 6), (7, 9, 9), (13, 6, 15)])
+def test_dw_conv_brute_force(k, H, W):
+    x = rnd((1, 2, H, W), seed=140 + k)
+    Wd = rnd((2, k, k), 0.05, seed=141 + k)
+    assert np.allclose(O.dw_conv_forward(x, Wd), dw_brute_force(x, Wd), rtol=0, atol=1e-12)
+
+
+@pytest.mark.parametrize("k,u,t", [(5, 0, 4), (7, 3, 3), (13, 12, 1), (9, 2, 6)])
+def test_dw_conv_one_hot_is_shift(k, u, t):
+    """A single 1 at (u, t) copies x shifted by (u - p, t - p), zeros where it leaves the image."""
+    x = rnd((2, 3, 16, 18), seed=150)
+    Wd = np.zeros((3, k, k))
+    Wd[:, u, t] = 1.0
+    p = k // 2
+    dy, dx = u - p, t - p
+    want = np.zeros_like(x)
+    H, W = x.shape[2:]
+    for h in range(H):
+        for v in range(W):
+            if 0 <= h + dy < H and 0 <= v + dx < W:
+                want[:, :, h, v] = x[:, :, h + dy, v + dx]
+    assert np.array_equal(O.dw_conv_forward(x, Wd), want)
+
+
+def test_dw_conv_k3_is_the_mix():
+    z = rnd((2, 5, 9, 13), seed=160)
+    Wm = rnd((5, 3, 3), 0.1, seed=161)
+    assert np.allclose(O.dw_conv_forward(z, Wm), O.mix_forward(z, Wm), rtol=0, atol=1e-14)
+
+
+@pytest.mark.parametrize("w", [2, 5, 7])
+def test_dw_conv_on_one_window_is_wbmm(w):
+    """An image that is exactly one window: WBMM with table T equals DW-Std with k = 2w-1 and the
+    180-degree rotated table as its kernel (the zero padding of the convolution stands in for the
+    window edge)."""
+    x = rnd((3, 4, w, w), seed=170 + w)
+    T = rnd((4, 2 * w - 1, 2 * w - 1), 0.05, seed=171 + w)
+    dw = O.dw_conv_forward(x, np.ascontiguousarray(T[:, ::-1, ::-1]))
+    assert np.allclose(dw, O.wbmm_forward(x, w, T=T), rtol=0, atol=1e-12)
