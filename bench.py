@@ -11,6 +11,7 @@ Prints ONE JSON line on stdout; diagnostics go to stderr.
 
   python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
   python bench.py --copy-calibration        # plain device copy for HBM counter scaling
+  python bench.py --fig3-sweep              # WBMM w=7/14/28 vs DW-Std k=5..13, one line each
   python bench.py --summarize-pmc DIR ...   # turn rocprofv3 --pmc output into profiles/ json
 """
 from __future__ import annotations
@@ -31,6 +32,9 @@ sys.path.insert(0, ROOT)
 FP32_MFMA_PEAK_TFLOPS = 157.3     # MI355X dense fp32 matrix
 BF16_MFMA_PEAK_TFLOPS = 2516.6    # MI355X dense bf16 matrix
 HBM_PEAK_GBS = 8000.0             # MI355X HBM3E
+# fp32 FMA on the vector ALUs without packed (two-wide) instructions, which these kernels do not
+# use: 256 CUs x 4 SIMDs x 16 lanes x 2 flops x 2.4 GHz
+FP32_VALU_PEAK_TFLOPS = 256 * 4 * 16 * 2 * 2.4e9 / 1e12
 METRIC = "WBMM fwd+bwd GFLOP/s & out-elems/s at w=14; % of MFMA/HBM roofline"
 CSRC = os.path.join(ROOT, "receptive_field_spatial_amd", "csrc")
 
@@ -437,6 +441,76 @@ def summarize_pmc(workload, fetch_dir, write_dir, copy_fetch_dir, copy_write_dir
     log(f"[pmc] wrote {out}")
 
 
+# ----------------------------------------------------------------------------- DW-Std comparison
+FIG3 = {"B": 128, "C": 256, "H": 56, "W": 56}
+
+
+def fig3_sweep(args):
+    """The pages' operator comparison on this GPU: one layer call at batch 128, 256 channels,
+    56x56, fp32, for WBMM (w = 7, 14, 28; table input, no mix) and the k x k depthwise convolution
+    (k = 5 .. 13). Each line: main-kernel time from HIP events on its dispatch (inputs rotate over
+    4 batches), output elements/s (the same output for every operator), algorithmic GFLOP/s and
+    the roofline of the binding resource."""
+    import numpy as np
+    import torch
+
+    import receptive_field_spatial_amd as R
+    from receptive_field_spatial_amd import synth
+
+    R.load_library()
+    B, C, H, W = FIG3["B"], FIG3["C"], FIG3["H"], FIG3["W"]
+    E = B * C * H * W
+    nsets = max(1, args.rotate)
+    xs = [torch.from_numpy(synth.normal_f32((B, C, H, W), 1.0, seed=i)).cuda() for i in range(nsets)]
+    ys = [torch.empty_like(xs[0]) for _ in range(nsets)]
+    hev = HipEvents()
+    stream = torch.cuda.current_stream()
+
+    def timed(call):
+        for i in range(args.warmup):
+            call(i % nsets)
+        torch.cuda.synchronize()
+        evs = [(hev.create(), hev.create()) for _ in range(args.steps)]
+        for i in range(args.steps):
+            R.wbmm_set_launch_events(evs[i][0], evs[i][1])
+            call(i % nsets)
+        torch.cuda.synchronize()
+        ms = [hev.elapsed_ms(a, b) for a, b in evs]
+        for a, b in evs:
+            hev.destroy(a)
+            hev.destroy(b)
+        return statistics.mean(ms) / 1e3
+
+    lines = []
+    for w in (7, 14, 28):
+        T = torch.from_numpy(synth.normal_f32((C, 2 * w - 1, 2 * w - 1), 0.02, seed=50 + w)).cuda()
+        sec = timed(lambda i: R.wbmm_forward(xs[i], w, T=T, y=ys[i], stream=stream))
+        Hp, Wp = -(-H // w) * w, -(-W // w) * w
+        flops = B * C * Hp * Wp * 2 * w * w
+        lines.append({"op": "wbmm", "w": w, "receptive_field": w * w, "us": round(sec * 1e6, 2),
+                      "out_elems_per_s": round(E / sec, 1), "gflops": round(flops / sec / 1e9, 1),
+                      "roofline": {"bound": "mfma", "peak_tflops": FP32_MFMA_PEAK_TFLOPS,
+                                   "frac": round(flops / sec / 1e12 / FP32_MFMA_PEAK_TFLOPS, 4)}})
+    for k in (5, 7, 9, 11, 13):
+        Wd = torch.from_numpy(synth.normal_f32((C, k, k), 0.05, seed=60 + k)).cuda()
+        sec = timed(lambda i: R.wbmm_dwconv_forward(xs[i], Wd, y=ys[i], stream=stream))
+        flops = E * 2 * k * k
+        nbytes = E * 8 + C * k * k * 4
+        t_alu = flops / (FP32_VALU_PEAK_TFLOPS * 1e12)
+        t_hbm = nbytes / (HBM_PEAK_GBS * 1e9)
+        roof = ({"bound": "alu", "peak_tflops": round(FP32_VALU_PEAK_TFLOPS, 1),
+                 "frac": round(t_alu / sec, 4)} if t_alu >= t_hbm else
+                {"bound": "hbm", "peak_gbs": HBM_PEAK_GBS, "frac": round(t_hbm / sec, 4)})
+        lines.append({"op": "dw_std", "k": k, "receptive_field": k * k, "us": round(sec * 1e6, 2),
+                      "out_elems_per_s": round(E / sec, 1), "gflops": round(flops / sec / 1e9, 1),
+                      "roofline": roof})
+    base = next(l for l in lines if l["op"] == "dw_std" and l["k"] == 5)["us"]
+    for l in lines:
+        l["speed_vs_dw5"] = round(base / l["us"], 3)
+        l["config"] = dict(FIG3, dtype="f32", data="synthetic", rotating_batches=nsets)
+        print(json.dumps(l), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -447,6 +521,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", dest="cpu_baseline", action="store_false")
     ap.add_argument("--cpu-budget", type=float, default=10.0, help="seconds of oracle CPU work")
     ap.add_argument("--copy-calibration", action="store_true")
+    ap.add_argument("--fig3-sweep", action="store_true",
+                    help="WBMM vs DW-Std at batch 128, 256 channels, 56x56, fp32")
     ap.add_argument("--summarize-pmc", nargs=4, metavar=("FETCH", "WRITE", "COPY_FETCH", "COPY_WRITE"))
     args = ap.parse_args()
 
@@ -460,6 +536,9 @@ def main():
         return
     if args.copy_calibration:
         copy_calibration()
+        return
+    if args.fig3_sweep:
+        fig3_sweep(args)
         return
     line = run(args)
     print(json.dumps(line), flush=True)

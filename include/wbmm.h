@@ -214,8 +214,28 @@ wbmm_status wbmm_backward_hier(int B, int C, int H, int W, int w, int s, int lay
                                void* workspace, size_t workspace_bytes, void* stream);
 
 /*
- * wbmm_set_launch_events — measurement aid, not part of the method. The next wbmm_forward or
- * wbmm_backward call made on the calling thread attaches `before` and `after` (hipEvent_t
+ * wbmm_dwconv_forward — the standard k x k depthwise convolution (DW-Std) that the pages time
+ * WBMM against: every output gathers the k*k neighbours around its own position in its own
+ * channel [pith page, Fig. 1 and Fig. 2 captions; operator benchmark, Fig. 3 caption]. Not part of
+ * a WBMM layer; provided so the comparison runs on the same hardware.
+ *   y[b,c,h,v] = sum_{u,t in 0..k-1} w_dw[c,u,t] * x[b,c,h+u-p,v+t-p],  p = k / 2,
+ *   x taken as 0 outside the map (cross-correlation, stride 1, no bias: the frameworks' form).
+ * Sizes: B, C, H, W >= 1; k odd, 3 <= k <= 13 (WBMM_E_UNSUPPORTED otherwise, and for rows too
+ *         long for one workgroup's staging buffer, about 600 pixels).
+ * x:    device fp32 NCHW [B][C][H][W].
+ * w_dw: device fp32 [C][k][k].
+ * y:    device fp32 NCHW [B][C][H][W], written; must not overlap x or w_dw.
+ * Accumulates in fp32 (one fma per tap, taps in row-major order). Enqueued on `stream`; no
+ * workspace. Errors: WBMM_E_INVALID (sizes, even k, NULL, overlap), WBMM_E_UNSUPPORTED (k or
+ * row length out of range, misaligned pointers), WBMM_E_HIP (launch failure).
+ */
+wbmm_status wbmm_dwconv_forward(int B, int C, int H, int W, int k, const float* x,
+                                const float* w_dw, float* y, void* stream);
+
+/*
+ * wbmm_set_launch_events — measurement aid, not part of the method. The next wbmm_forward,
+ * wbmm_backward (or their _hier forms) or wbmm_dwconv_forward call made on the calling thread
+ * attaches `before` and `after` (hipEvent_t
  * handles passed as void*) to the dispatch of its main contraction kernel (hipExtLaunchKernel's
  * start and stop events), so their elapsed time is that kernel's execution; the pair is then
  * cleared. Both NULL clears a pending pair. The caller owns the events. Errors: WBMM_E_INVALID

@@ -18,7 +18,7 @@ __all__ = [
     "wbmm_forward", "wbmm_forward_workspace_bytes",
     "wbmm_backward", "wbmm_backward_workspace_bytes", "wbmm_set_launch_events",
     "wbmm_forward_hier", "wbmm_forward_hier_workspace_bytes",
-    "wbmm_backward_hier", "wbmm_backward_hier_workspace_bytes",
+    "wbmm_backward_hier", "wbmm_backward_hier_workspace_bytes", "wbmm_dwconv_forward",
     "WBMM_OK", "WBMM_E_INVALID", "WBMM_E_UNSUPPORTED", "WBMM_E_WORKSPACE", "WBMM_E_HIP",
 ]
 
@@ -58,6 +58,7 @@ def _declare(lib):
         "wbmm_forward_hier": (c_int, [c_int] * 7 + [vp] * 7 + [c_size, vp]),
         "wbmm_backward_hier_workspace_bytes": (c_size, [c_int] * 8),
         "wbmm_backward_hier": (c_int, [c_int] * 7 + [vp] * 11 + [c_size, vp]),
+        "wbmm_dwconv_forward": (c_int, [c_int] * 5 + [vp] * 4),
     }
     for name, (res, args) in sigs.items():
         fn = getattr(lib, name)
@@ -292,3 +293,20 @@ def wbmm_set_launch_events(before, after):
     """Attach two HIP events (raw handles) to the dispatch of the next forward/backward call's
     main kernel: their elapsed time is that kernel's execution."""
     _check(_lib().wbmm_set_launch_events(before, after))
+
+
+def wbmm_dwconv_forward(x, w_dw, *, y=None, stream=None):
+    """k x k depthwise convolution (DW-Std, the pages' comparison operator): fp32 NCHW x
+    (B, C, H, W), weights w_dw (C, k, k), zero padding k // 2, stride 1. Returns y."""
+    torch = _torch()
+    B, C, H, W = _bchw(x, "NCHW")
+    k = int(w_dw.shape[-1])
+    if tuple(w_dw.shape) != (C, k, k):
+        raise WbmmError(WBMM_E_INVALID, f"w_dw must be (C, k, k), got {tuple(w_dw.shape)}")
+    if x.dtype != torch.float32 or w_dw.dtype != torch.float32:
+        raise WbmmError(WBMM_E_INVALID, "the depthwise convolution is fp32")
+    if y is None:
+        y = torch.empty_like(x)
+    _check(_lib().wbmm_dwconv_forward(B, C, H, W, k, _ptr(x), _ptr(w_dw), _ptr(y),
+                                      _stream(stream)))
+    return y

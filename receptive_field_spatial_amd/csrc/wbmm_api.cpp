@@ -372,3 +372,22 @@ WBMM_API wbmm_status wbmm_backward_hier(int B, int C, int H, int W, int w, int s
     return fail(WBMM_E_UNSUPPORTED, "workspace not 256-byte aligned");
   return hip_status(wbmm::launch_backward(r, (hipStream_t)stream), "wbmm_backward_hier");
 }
+
+WBMM_API wbmm_status wbmm_dwconv_forward(int B, int C, int H, int W, int k, const float* x,
+                                         const float* w_dw, float* y, void* stream) {
+  if (B < 1 || C < 1 || H < 1 || W < 1)
+    return fail(WBMM_E_INVALID, "sizes must be >= 1 (B=%d C=%d H=%d W=%d)", B, C, H, W);
+  if (k < 1 || k % 2 == 0) return fail(WBMM_E_INVALID, "kernel size k=%d must be odd and >= 1", k);
+  if (!x || !w_dw || !y) return fail(WBMM_E_INVALID, "x, w_dw and y must be non-NULL");
+  if (!aligned(x, 4) || !aligned(w_dw, 4) || !aligned(y, 4))
+    return fail(WBMM_E_UNSUPPORTED, "pointer not 4-byte aligned");
+  if (!wbmm::dwconv_supported(B, C, H, W, k))
+    return fail(WBMM_E_UNSUPPORTED,
+                "the depthwise convolution is provided for odd k in 3..13 and rows up to ~600 "
+                "pixels (k=%d, W=%d)", k, W);
+  const size_t mb = (size_t)B * C * H * W * 4;
+  if (overlaps(y, mb, x, mb)) return fail(WBMM_E_INVALID, "y overlaps x");
+  if (overlaps(y, mb, w_dw, (size_t)C * k * k * 4)) return fail(WBMM_E_INVALID, "y overlaps w_dw");
+  return hip_status(wbmm::launch_dwconv(B, C, H, W, k, x, w_dw, y, (hipStream_t)stream),
+                    "wbmm_dwconv_forward");
+}

@@ -88,6 +88,11 @@ hipError_t launch_main(K kernel, dim3 grid, dim3 block, unsigned lds, hipStream_
   return hipGetLastError();
 }
 
+// k x k depthwise convolution (DW-Std), fp32 NCHW, odd k in 3..13.
+bool dwconv_supported(int B, int C, int H, int W, int k);
+hipError_t launch_dwconv(int B, int C, int H, int W, int k, const float* x, const float* w,
+                         float* y, hipStream_t st);
+
 // 3x3 depthwise mix kernels (used by the window-mode paths).
 hipError_t launch_mix_fwd(const float* z, const float* w9, void* y, int out_bf16, int B, int C,
                           int H, int W, int layout, hipStream_t st);

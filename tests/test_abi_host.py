@@ -41,7 +41,8 @@ def test_header_declares_the_entry_points():
     fns = header_functions()
     for name in ["wbmm_build_index", "wbmm_build_matrix", "wbmm_fold_hier", "wbmm_forward",
                  "wbmm_backward", "wbmm_forward_workspace_bytes", "wbmm_backward_workspace_bytes",
-                 "wbmm_last_error", "wbmm_abi_version"]:
+                 "wbmm_last_error", "wbmm_abi_version", "wbmm_forward_hier", "wbmm_backward_hier",
+                 "wbmm_dwconv_forward"]:
         assert name in fns, name
 
 
@@ -195,6 +196,25 @@ def test_hier_validation(lib):
     assert hier_bwd(lib) == R.WBMM_E_WORKSPACE
     assert hier_bwd(lib, ws=0xA00000, wsb=need - 1) == R.WBMM_E_WORKSPACE
     assert lib.wbmm_forward_hier_workspace_bytes(1, 2, 128, 128, 14, 7, 0, 1, 0) > 0  # window-mode mix
+
+
+def test_dwconv_validation(lib):
+    """The DW-Std comparison kernel: odd k in 3..13, rows it can stage, non-overlapping output;
+    all rejected on the host."""
+    def call(B=2, C=3, H=56, W=56, k=5, x=FAKE, w=0x300000, y=FAKE2):
+        return lib.wbmm_dwconv_forward(B, C, H, W, k, x, w, y, None)
+    assert call(k=4) == R.WBMM_E_INVALID
+    assert call(k=0) == R.WBMM_E_INVALID
+    assert call(k=1) == R.WBMM_E_UNSUPPORTED
+    assert call(k=15) == R.WBMM_E_UNSUPPORTED
+    assert "odd k in 3..13" in err(lib)
+    assert call(W=1100) == R.WBMM_E_UNSUPPORTED          # a row too long to stage
+    assert call(B=0) == R.WBMM_E_INVALID
+    assert call(x=None) == R.WBMM_E_INVALID
+    assert call(w=None) == R.WBMM_E_INVALID
+    assert call(y=FAKE) == R.WBMM_E_INVALID              # y aliases x
+    assert call(y=0x300000) == R.WBMM_E_INVALID          # y overlaps the weights
+    assert call(x=FAKE + 2) == R.WBMM_E_UNSUPPORTED      # misaligned
 
 
 def test_last_error_is_per_thread(lib):

@@ -647,3 +647,56 @@ def test_hier_fast_zero_sub_table_matches_plain():
                                             Ts, Wmix=Wm, z=host(zh).astype(np.float64))
     assert_f32(host(dTh), wdT, "dT")
     assert_f32(host(dTsh), wdTs, "dT_sub")
+
+
+# ----------------------------------------------------------------------------- DW-Std comparison
+@pytest.mark.parametrize("k", [3, 5, 7, 9, 11, 13])
+@pytest.mark.parametrize("B,C,H,W", [(2, 3, 56, 56), (2, 5, 28, 28), (1, 2, 13, 17),
+                                     (1, 3, 5, 3), (1, 2, 150, 64), (3, 2, 14, 14)])
+def test_dwconv_parity(k, B, C, H, W):
+    """The k x k depthwise convolution against the oracle: whole 56² / 28² planes (16-byte
+    staging and stores, 7- and 4-row tiles), ragged odd widths, maps smaller than the kernel,
+    several row bands per plane, several planes per workgroup."""
+    say(f"dwconv k={k} B={B} C={C} H={H} W={W}")
+    x = synth.normal_f32((B, C, H, W), 1.0, seed=200 + k)
+    Wd = synth.normal_f32((C, k, k), 0.05, seed=201 + k)
+    y = R().wbmm_dwconv_forward(dev(x), dev(Wd))
+    assert_f32(host(y), O.dw_conv_forward(x.astype(np.float64), Wd), "y")
+
+
+@pytest.mark.parametrize("k", [5, 13])
+def test_dwconv_one_hot_is_exact_shift(k):
+    """One tap per channel (a different one in each): y is x shifted, bit for bit."""
+    B, C, H, W = 2, 6, 28, 36
+    say(f"dwconv one-hot k={k}")
+    x = synth.normal_f32((B, C, H, W), 1.0, seed=210)
+    Wd = np.zeros((C, k, k), np.float32)
+    for c in range(C):
+        Wd[c, (c * 3) % k, (c * 5 + 1) % k] = 1.0
+    y = R().wbmm_dwconv_forward(dev(x), dev(Wd))
+    assert np.array_equal(host(y), O.dw_conv_forward(x.astype(np.float64), Wd).astype(np.float32))
+
+
+@pytest.mark.parametrize("w", [3, 5, 7])
+def test_dwconv_on_one_window_matches_wbmm(w):
+    """On maps that are exactly one window, DW-Std with k = 2w-1 and the rotated table is WBMM:
+    the two GPU operators agree (to rounding) on the same inputs."""
+    B, C = 4, 3
+    say(f"dwconv vs wbmm on one window w={w}")
+    x = synth.normal_f32((B, C, w, w), 1.0, seed=220 + w)
+    T = synth.normal_f32((C, 2 * w - 1, 2 * w - 1), 0.05, seed=221 + w)
+    y_dw = R().wbmm_dwconv_forward(dev(x), dev(np.ascontiguousarray(T[:, ::-1, ::-1])))
+    y_wb = R().wbmm_forward(dev(x), w, T=dev(T))
+    assert_f32(host(y_dw), host(y_wb).astype(np.float64), "dw vs wbmm")
+
+
+def test_dwconv_full_size_sampled():
+    """The comparison shape (B=128, C=256, 56², k=13): sampled planes against the oracle."""
+    B, C, H, W, k = 128, 256, 56, 56, 13
+    say("dwconv full size k=13")
+    xn = synth.normal_f32((B, C, H, W), 1.0, seed=230)
+    wn = synth.normal_f32((C, k, k), 0.05, seed=231)
+    y = host(R().wbmm_dwconv_forward(dev(xn), dev(wn)))
+    for b, c in [(0, 0), (127, 255), (64, 3), (5, 200), (100, 129)]:
+        want = O.dw_conv_forward(xn[b:b + 1, c:c + 1].astype(np.float64), wn[c:c + 1])
+        assert_f32(y[b:b + 1, c:c + 1], want, f"plane ({b},{c})")
