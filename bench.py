@@ -491,6 +491,24 @@ def fig3_sweep(args):
                       "out_elems_per_s": round(E / sec, 1), "gflops": round(flops / sec / 1e9, 1),
                       "roofline": {"bound": "mfma", "peak_tflops": FP32_MFMA_PEAK_TFLOPS,
                                    "frac": round(flops / sec / 1e12 / FP32_MFMA_PEAK_TFLOPS, 4)}})
+    # context beyond the pages' fp32 comparison: the same layers with bf16 maps and tables
+    xb = [x.to(torch.bfloat16) for x in xs]
+    yb = [torch.empty_like(x) for x in xb]
+    for w in (7, 14, 28):
+        T = torch.from_numpy(synth.normal_f32((C, 2 * w - 1, 2 * w - 1), 0.02, seed=50 + w)).cuda()
+        Tb = T.to(torch.bfloat16)
+        sec = timed(lambda i: R.wbmm_forward(xb[i], w, T=Tb, y=yb[i], stream=stream))
+        flops = B * C * H * W * 2 * w * w
+        nbytes = E * 4 + C * (2 * w - 1) ** 2 * 2
+        t_mfma = flops / (BF16_MFMA_PEAK_TFLOPS * 1e12)
+        t_hbm = nbytes / (HBM_PEAK_GBS * 1e9)
+        roof = ({"bound": "mfma", "peak_tflops": BF16_MFMA_PEAK_TFLOPS,
+                 "frac": round(t_mfma / sec, 4)} if t_mfma >= t_hbm else
+                {"bound": "hbm", "peak_gbs": HBM_PEAK_GBS, "frac": round(t_hbm / sec, 4)})
+        lines.append({"op": "wbmm_bf16", "w": w, "receptive_field": w * w,
+                      "us": round(sec * 1e6, 2), "out_elems_per_s": round(E / sec, 1),
+                      "gflops": round(flops / sec / 1e9, 1), "roofline": roof})
+    del xb, yb
     for k in (5, 7, 9, 11, 13):
         Wd = torch.from_numpy(synth.normal_f32((C, k, k), 0.05, seed=60 + k)).cuda()
         sec = timed(lambda i: R.wbmm_dwconv_forward(xs[i], Wd, y=ys[i], stream=stream))
@@ -507,7 +525,8 @@ def fig3_sweep(args):
     base = next(l for l in lines if l["op"] == "dw_std" and l["k"] == 5)["us"]
     for l in lines:
         l["speed_vs_dw5"] = round(base / l["us"], 3)
-        l["config"] = dict(FIG3, dtype="f32", data="synthetic", rotating_batches=nsets)
+        l["config"] = dict(FIG3, dtype="bf16" if l["op"] == "wbmm_bf16" else "f32",
+                           data="synthetic", rotating_batches=nsets)
         print(json.dumps(l), flush=True)
 
 

@@ -59,36 +59,59 @@ __global__ void __launch_bounds__(kThreads) k_dw_conv(DwArgs a) {
   const float* xp = a.x + (size_t)plane * g.H * g.W;
 
   // ---- stage LDS rows r = 0 .. ph-1 (image row h0 - P + r); LDS column P + v holds image
-  //      column v, zero outside the image. Four columns per step.
-  const int gpr = g.pw / 4;
-  for (int e = pt; e < g.ph * gpr; e += nt) {
-    const int r = e / gpr, q = e - r * gpr;
-    const int hh = h0 - P + r;
-    const bool row_in = live && hh >= 0 && hh < g.H;
-    float v[4];
-    if (g.vec4) {  // image columns 4q' .. 4q'+3 -> LDS columns 4q'+P .. (one 16-byte load)
-      const int v0 = 4 * q;
-      const bool in = row_in && v0 < g.W;
-      const v4f t = *(const v4f*)(xp + (in ? (size_t)hh * g.W + v0 : 0));
+  //      column v, zero outside the image. Four columns per group; each lane takes groups in
+  //      batches of SB with every load of a batch in flight before its LDS writes.
+  constexpr int SB = 8;
+  const int gpr = g.pw / 4, total = g.ph * gpr;
+  for (int e0 = 0; e0 < total; e0 += SB * nt) {
+    float v[SB][4];
+    if (g.vec4) {  // group q: image columns 4q .. 4q+3 (one 16-byte load) -> LDS 4q+P ..
 #pragma unroll
-      for (int j = 0; j < 4; ++j) v[j] = in ? t[j] : 0.f;  // zeros past the image's right edge
-      float* dst = slab + r * g.pw + P + v0;
+      for (int s = 0; s < SB; ++s) {
+        const int e = e0 + s * nt + pt;
+        const int r = e / gpr, q = e - r * gpr;
+        const int hh = h0 - P + r, v0 = 4 * q;
+        const bool in = live && e < total && hh >= 0 && hh < g.H && v0 < g.W;
+        const v4f t4 = *(const v4f*)(xp + (in ? (size_t)hh * g.W + v0 : 0));
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
-        if (v0 + P + j < g.pw) dst[j] = v[j];
-      if (q == 0) {
-#pragma unroll
-        for (int j = 0; j < P; ++j) slab[r * g.pw + j] = 0.f;
+        for (int j = 0; j < 4; ++j) v[s][j] = in ? t4[j] : 0.f;
       }
-    } else {  // LDS columns 4q .. 4q+3 one by one
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int vv = 4 * q + j - P;
-        const bool in = row_in && vv >= 0 && vv < g.W;
-        const float t = xp[in ? (size_t)hh * g.W + vv : 0];
-        v[j] = in ? t : 0.f;
+      for (int s = 0; s < SB; ++s) {
+        const int e = e0 + s * nt + pt;
+        if (e >= total) break;
+        const int r = e / gpr, q = e - r * gpr;
+        float* dst = slab + r * g.pw + P + 4 * q;
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          if (4 * q + P + j < g.pw) dst[j] = v[s][j];
+        if (q == 0) {
+#pragma unroll
+          for (int j = 0; j < P; ++j) slab[r * g.pw + j] = 0.f;
+        }
       }
-      *(v4f*)(slab + r * g.pw + 4 * q) = v4f{v[0], v[1], v[2], v[3]};
+    } else {  // group q: LDS columns 4q .. 4q+3, image columns 4q - P .., one load each
+#pragma unroll
+      for (int s = 0; s < SB; ++s) {
+        const int e = e0 + s * nt + pt;
+        const int r = e / gpr, q = e - r * gpr;
+        const int hh = h0 - P + r;
+        const bool row_in = live && e < total && hh >= 0 && hh < g.H;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int vv = 4 * q + j - P;
+          const bool in = row_in && vv >= 0 && vv < g.W;
+          const float t = xp[in ? (size_t)hh * g.W + vv : 0];
+          v[s][j] = in ? t : 0.f;
+        }
+      }
+#pragma unroll
+      for (int s = 0; s < SB; ++s) {
+        const int e = e0 + s * nt + pt;
+        if (e >= total) break;
+        const int r = e / gpr, q = e - r * gpr;
+        *(v4f*)(slab + r * g.pw + 4 * q) = v4f{v[s][0], v[s][1], v[s][2], v[s][3]};
+      }
     }
   }
   __syncthreads();
