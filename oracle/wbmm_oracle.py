@@ -39,6 +39,8 @@ __all__ = [
     "pad_map", "partition", "reverse", "wbmm_forward", "mix_forward", "mix_backward",
     "wbmm_backward", "layer_forward", "layer_backward", "wbmm_backward_hier",
     "layer_forward_hier", "layer_backward_hier", "dw_conv_forward",
+    "wbmm_forward_shifted", "wbmm_backward_shifted", "layer_forward_shifted",
+    "layer_backward_shifted",
 ]
 
 
@@ -296,6 +298,55 @@ def layer_backward(x, dy, w, T=None, M=None, Wmix=None, z=None):
     else:
         dz, dW = dy.astype(np.float64), None
     dx, dT = wbmm_backward(x, dz, w, T=T, M=M)
+    return dx, dT, dW
+
+
+# ----------------------------------------------------------------------------- shifted grid
+def _shift_pad(x: np.ndarray, oy: int, ox: int) -> np.ndarray:
+    B, C, H, W = x.shape
+    out = np.zeros((B, C, H + oy, W + ox), dtype=np.float64)
+    out[:, :, oy:, ox:] = x
+    return out
+
+
+def wbmm_forward_shifted(x: np.ndarray, w: int, oy: int, ox: int, T=None, M=None) -> np.ndarray:
+    """WBMM on a window grid offset by (oy, ox), 0 <= oy, ox < w (reading R19).
+
+    The pages list interleaving the window grid between layers as a way to let information cross
+    window borders, without defining it [gecl.asia reading notes, "Limitations"]. Taken: the
+    windows of such a layer cover map rows [k w - oy, (k+1) w - oy) and columns likewise; pixels
+    of a border window that fall outside the map are zeros (as for ragged maps, reading R3).
+    Written as: oy zero rows on top and ox zero columns on the left, the plain forward, then the
+    added rows and columns removed.
+    """
+    H, W = x.shape[2:]
+    return wbmm_forward(_shift_pad(x, oy, ox), w, T=T, M=M)[:, :, oy:oy + H, ox:ox + W]
+
+
+def wbmm_backward_shifted(x, dz, w, oy, ox, T=None, M=None):
+    """Gradients of ``wbmm_forward_shifted``: (dx, dT). The padding pixels are constants, so dx is
+    the padded problem's dx without them and dT is the padded problem's dT (zeros add nothing)."""
+    H, W = x.shape[2:]
+    dx, dT = wbmm_backward(_shift_pad(x, oy, ox), _shift_pad(dz, oy, ox), w, T=T, M=M)
+    return dx[:, :, oy:oy + H, ox:ox + W], dT
+
+
+def layer_forward_shifted(x, w, oy, ox, T=None, M=None, Wmix=None):
+    """Shifted-grid WBMM, then the optional 3x3 mix on the map. Returns (y, z)."""
+    z = wbmm_forward_shifted(x, w, oy, ox, T=T, M=M)
+    y = mix_forward(z, Wmix) if Wmix is not None else z
+    return y, z
+
+
+def layer_backward_shifted(x, dy, w, oy, ox, T=None, M=None, Wmix=None, z=None):
+    """Backward of ``layer_forward_shifted``: (dx, dT, dWmix-or-None)."""
+    if Wmix is not None:
+        if z is None:
+            z = wbmm_forward_shifted(x, w, oy, ox, T=T, M=M)
+        dz, dW = mix_backward(dy, z, Wmix)
+    else:
+        dz, dW = dy.astype(np.float64), None
+    dx, dT = wbmm_backward_shifted(x, dz, w, oy, ox, T=T, M=M)
     return dx, dT, dW
 
 

@@ -594,3 +594,73 @@ def test_dw_conv_on_one_window_is_wbmm(w):
     T = rnd((4, 2 * w - 1, 2 * w - 1), 0.05, seed=171 + w)
     dw = O.dw_conv_forward(x, np.ascontiguousarray(T[:, ::-1, ::-1]))
     assert np.allclose(dw, O.wbmm_forward(x, w, T=T), rtol=0, atol=1e-12)
+
+
+# ----------------------------------------------------------------------------- shifted grid
+def brute_force_shifted(x, T, w, oy, ox):
+    """Per-output sum over the positions of the output's own window, windows starting at
+    k*w - oy (rows) and k*w - ox (columns), pure Python loops."""
+    B, C, H, W = x.shape
+    out = np.zeros((B, C, H, W))
+    for b in range(B):
+        for c in range(C):
+            for py in range(H):
+                for px in range(W):
+                    wy0 = ((py + oy) // w) * w - oy
+                    wx0 = ((px + ox) // w) * w - ox
+                    acc = 0.0
+                    for qy in range(max(wy0, 0), min(wy0 + w, H)):
+                        for qx in range(max(wx0, 0), min(wx0 + w, W)):
+                            acc += T[c, py - qy + w - 1, px - qx + w - 1] * x[b, c, qy, qx]
+                    out[b, c, py, px] = acc
+    return out
+
+
+@pytest.mark.parametrize("B,C,H,W,w,oy,ox", [(1, 2, 9, 11, 4, 2, 2), (2, 1, 7, 7, 7, 3, 3),
+                                              (1, 2, 10, 6, 3, 1, 2), (1, 1, 5, 9, 5, 0, 4)])
+def test_shifted_brute_force(B, C, H, W, w, oy, ox):
+    x = rnd((B, C, H, W), seed=300 + w)
+    T = rnd((C, 2 * w - 1, 2 * w - 1), 0.1, seed=301 + w)
+    assert np.allclose(O.wbmm_forward_shifted(x, w, oy, ox, T=T),
+                       brute_force_shifted(x, T, w, oy, ox), rtol=0, atol=1e-12)
+
+
+def test_shifted_zero_offset_is_plain():
+    x = rnd((2, 3, 13, 10), seed=310)
+    T = rnd((3, 9, 9), 0.1, seed=311)
+    assert np.array_equal(O.wbmm_forward_shifted(x, 5, 0, 0, T=T), O.wbmm_forward(x, 5, T=T))
+
+
+def test_shifted_window_borders_move():
+    """With a one-hot table that copies the left neighbour, a pixel whose left neighbour lies in
+    another window gets 0: at columns k*w - ox, not at the plain grid's k*w."""
+    w, ox = 4, 2
+    x = rnd((1, 1, 4, 12), seed=320)
+    T = np.zeros((1, 7, 7))
+    T[0, 3, 4] = 1.0      # offset (0, +1): out[px] = x[px - 1] inside the window
+    y = O.wbmm_forward_shifted(x, w, 0, ox, T=T)
+    for px in range(12):
+        starts_window = (px + ox) % w == 0
+        want = 0.0 if starts_window or px == 0 else x[0, 0, :, px - 1]  # px 0: neighbour off-map
+        assert np.array_equal(y[0, 0, :, px], np.broadcast_to(want, (4,)))
+
+
+@pytest.mark.parametrize("oy,ox", [(2, 3), (3, 0)])
+def test_shifted_backward_adjoint_and_fd(oy, ox):
+    """dx by the adjoint identity <WBMM_s(x), g> = <x, dX_s(g)>; dT by central differences of
+    L(T) = sum(g * WBMM_s(x; T)) (linear in T, so exact up to rounding)."""
+    w = 5
+    x = rnd((2, 2, 11, 8), seed=330)
+    g = rnd((2, 2, 11, 8), seed=331)
+    T = rnd((2, 9, 9), 0.1, seed=332)
+    dx, dT = O.wbmm_backward_shifted(x, g, w, oy, ox, T=T)
+    y = O.wbmm_forward_shifted(x, w, oy, ox, T=T)
+    assert abs(np.sum(y * g) - np.sum(dx * x)) < 1e-9
+    eps = 1e-3
+    for c, i, j in [(0, 4, 4), (1, 0, 8), (0, 7, 2), (1, 3, 6)]:
+        Tp, Tm = T.copy(), T.copy()
+        Tp[c, i, j] += eps
+        Tm[c, i, j] -= eps
+        fd = (np.sum(g * O.wbmm_forward_shifted(x, w, oy, ox, T=Tp)) -
+              np.sum(g * O.wbmm_forward_shifted(x, w, oy, ox, T=Tm))) / (2 * eps)
+        assert abs(fd - dT[c, i, j]) < 1e-8 * max(1.0, abs(fd))
