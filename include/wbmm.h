@@ -214,6 +214,37 @@ wbmm_status wbmm_backward_hier(int B, int C, int H, int W, int w, int s, int lay
                                void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * wbmm_forward_shifted_workspace_bytes / wbmm_forward_shifted — wbmm_forward on a window grid
+ * offset by (oy, ox), 0 <= oy, ox < w: the interleaved grid that alternate layers can use so
+ * that information crosses window borders [gecl.asia reading notes, "Limitations": interleaving
+ * windows between layers]. Window (wy, wx) covers map rows wy*w - oy .. wy*w - oy + w - 1 and
+ * columns wx*w - ox .. wx*w - ox + w - 1; the pixels of a border window that lie outside the map
+ * are zeros (no cyclic roll), and only positions inside the map are written. (0, 0) is exactly
+ * wbmm_forward. Every other argument, layout, dtype and error as in wbmm_forward; an offset
+ * outside [0, w) is WBMM_E_INVALID.
+ */
+size_t wbmm_forward_shifted_workspace_bytes(int B, int C, int H, int W, int w, int oy, int ox,
+                                            int layout, int has_mix, int has_z_save);
+wbmm_status wbmm_forward_shifted(int B, int C, int H, int W, int w, int oy, int ox, int layout,
+                                 int in_dtype, int out_dtype, const void* x, const void* T,
+                                 const void* M, const float* mix_w, void* z_save, void* y,
+                                 void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * wbmm_backward_shifted_workspace_bytes / wbmm_backward_shifted — the gradients of
+ * wbmm_forward_shifted (dx, dT, dmix_w), with the arguments, outputs and errors of wbmm_backward
+ * plus the grid offset (oy, ox) of the forward. The padding pixels are constants: dT sums the
+ * pair products of the map's own pixels only.
+ */
+size_t wbmm_backward_shifted_workspace_bytes(int B, int C, int H, int W, int w, int oy, int ox,
+                                             int layout, int has_mix);
+wbmm_status wbmm_backward_shifted(int B, int C, int H, int W, int w, int oy, int ox, int layout,
+                                  const float* x, const float* T, const float* M,
+                                  const float* mix_w, const float* z_saved, const float* dy,
+                                  float* dx, float* dT, float* dmix_w, void* workspace,
+                                  size_t workspace_bytes, void* stream);
+
+/*
  * wbmm_dwconv_forward — the standard k x k depthwise convolution (DW-Std) that the pages time
  * WBMM against: every output gathers the k*k neighbours around its own position in its own
  * channel [pith page, Fig. 1 and Fig. 2 captions; operator benchmark, Fig. 3 caption]. Not part of
@@ -234,7 +265,7 @@ wbmm_status wbmm_dwconv_forward(int B, int C, int H, int W, int k, const float* 
 
 /*
  * wbmm_set_launch_events — measurement aid, not part of the method. The next wbmm_forward,
- * wbmm_backward (or their _hier forms) or wbmm_dwconv_forward call made on the calling thread
+ * wbmm_backward (or their _hier and _shifted forms) or wbmm_dwconv_forward call made on the calling thread
  * attaches `before` and `after` (hipEvent_t
  * handles passed as void*) to the dispatch of its main contraction kernel (hipExtLaunchKernel's
  * start and stop events), so their elapsed time is that kernel's execution; the pair is then

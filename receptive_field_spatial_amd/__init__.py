@@ -19,6 +19,8 @@ __all__ = [
     "wbmm_backward", "wbmm_backward_workspace_bytes", "wbmm_set_launch_events",
     "wbmm_forward_hier", "wbmm_forward_hier_workspace_bytes",
     "wbmm_backward_hier", "wbmm_backward_hier_workspace_bytes", "wbmm_dwconv_forward",
+    "wbmm_forward_shifted", "wbmm_forward_shifted_workspace_bytes", "wbmm_backward_shifted",
+    "wbmm_backward_shifted_workspace_bytes",
     "WBMM_OK", "WBMM_E_INVALID", "WBMM_E_UNSUPPORTED", "WBMM_E_WORKSPACE", "WBMM_E_HIP",
 ]
 
@@ -59,6 +61,10 @@ def _declare(lib):
         "wbmm_backward_hier_workspace_bytes": (c_size, [c_int] * 8),
         "wbmm_backward_hier": (c_int, [c_int] * 7 + [vp] * 11 + [c_size, vp]),
         "wbmm_dwconv_forward": (c_int, [c_int] * 5 + [vp] * 4),
+        "wbmm_forward_shifted_workspace_bytes": (c_size, [c_int] * 10),
+        "wbmm_forward_shifted": (c_int, [c_int] * 10 + [vp] * 7 + [c_size, vp]),
+        "wbmm_backward_shifted_workspace_bytes": (c_size, [c_int] * 9),
+        "wbmm_backward_shifted": (c_int, [c_int] * 8 + [vp] * 10 + [c_size, vp]),
     }
     for name, (res, args) in sigs.items():
         fn = getattr(lib, name)
@@ -184,18 +190,47 @@ def wbmm_forward_workspace_bytes(B, C, H, W, w, layout="NCHW", has_mix=False, ha
 def wbmm_forward(x, w: int, T=None, M=None, mix_w=None, *, layout: str = "NCHW", out_dtype=None,
                  y=None, z_save=None, workspace=None, stream=None):
     """Layer forward. Returns y (and z_save, when given, holds the pre-mix output)."""
+    return _forward(x, w, None, T, M, mix_w, layout, out_dtype, y, z_save, workspace, stream)
+
+
+def wbmm_forward_shifted_workspace_bytes(B, C, H, W, w, oy, ox, layout="NCHW", has_mix=False,
+                                         has_z_save=False) -> int:
+    return int(_lib().wbmm_forward_shifted_workspace_bytes(B, C, H, W, int(w), int(oy), int(ox),
+                                                           _layout_code(layout),
+                                                           int(bool(has_mix)),
+                                                           int(bool(has_z_save))))
+
+
+def wbmm_forward_shifted(x, w: int, oy: int, ox: int, T=None, M=None, mix_w=None, *,
+                         layout: str = "NCHW", out_dtype=None, y=None, z_save=None,
+                         workspace=None, stream=None):
+    """Layer forward on the window grid offset by (oy, ox) (interleaved windows). Returns y."""
+    return _forward(x, w, (int(oy), int(ox)), T, M, mix_w, layout, out_dtype, y, z_save,
+                    workspace, stream)
+
+
+def _forward(x, w, shift, T, M, mix_w, layout, out_dtype, y, z_save, workspace, stream):
     torch = _torch()
     B, C, H, W = _bchw(x, layout)
     out_dtype = out_dtype or x.dtype
     if y is None:
         y = torch.empty(x.shape, dtype=out_dtype, device=x.device)
-    need = wbmm_forward_workspace_bytes(B, C, H, W, w, layout, mix_w is not None, z_save is not None)
+    if shift is None:
+        need = wbmm_forward_workspace_bytes(B, C, H, W, w, layout, mix_w is not None,
+                                            z_save is not None)
+    else:
+        need = wbmm_forward_shifted_workspace_bytes(B, C, H, W, w, shift[0], shift[1], layout,
+                                                    mix_w is not None, z_save is not None)
     if need and (workspace is None or workspace.numel() * workspace.element_size() < need):
         workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    _check(_lib().wbmm_forward(B, C, H, W, int(w), _layout_code(layout), _dtype_code(x.dtype),
-                               _dtype_code(out_dtype), _ptr(x), _ptr(T), _ptr(M), _ptr(mix_w),
-                               _ptr(z_save), _ptr(y), _ptr(workspace), ws_bytes, _stream(stream)))
+    args = (_layout_code(layout), _dtype_code(x.dtype), _dtype_code(out_dtype), _ptr(x), _ptr(T),
+            _ptr(M), _ptr(mix_w), _ptr(z_save), _ptr(y), _ptr(workspace), ws_bytes,
+            _stream(stream))
+    if shift is None:
+        _check(_lib().wbmm_forward(B, C, H, W, int(w), *args))
+    else:
+        _check(_lib().wbmm_forward_shifted(B, C, H, W, int(w), shift[0], shift[1], *args))
     return y
 
 
@@ -210,6 +245,26 @@ def wbmm_backward(x, dy, w: int, T=None, M=None, mix_w=None, z_saved=None, *, la
 
     ``workspace`` (uint8, at least wbmm_backward_workspace_bytes); one is allocated when None.
     """
+    return _backward(x, dy, w, None, T, M, mix_w, z_saved, layout, dx, dT, dmix_w, workspace,
+                     stream)
+
+
+def wbmm_backward_shifted_workspace_bytes(B, C, H, W, w, oy, ox, layout="NCHW",
+                                          has_mix=False) -> int:
+    return int(_lib().wbmm_backward_shifted_workspace_bytes(B, C, H, W, int(w), int(oy), int(ox),
+                                                            _layout_code(layout),
+                                                            int(bool(has_mix))))
+
+
+def wbmm_backward_shifted(x, dy, w: int, oy: int, ox: int, T=None, M=None, mix_w=None,
+                          z_saved=None, *, layout: str = "NCHW", dx=True, dT=True, dmix_w=True,
+                          workspace=None, stream=None):
+    """Backward of wbmm_forward_shifted (fp32). Returns (dx, dT, dmix_w)."""
+    return _backward(x, dy, w, (int(oy), int(ox)), T, M, mix_w, z_saved, layout, dx, dT, dmix_w,
+                     workspace, stream)
+
+
+def _backward(x, dy, w, shift, T, M, mix_w, z_saved, layout, dx, dT, dmix_w, workspace, stream):
     torch = _torch()
     B, C, H, W = _bchw(x, layout)
     L = 2 * w - 1
@@ -220,13 +275,20 @@ def wbmm_backward(x, dy, w: int, T=None, M=None, mix_w=None, z_saved=None, *, la
         dW_t = None
     else:
         dW_t = torch.empty((C, 3, 3), dtype=torch.float32, device=dev) if dmix_w is True else (dmix_w if dmix_w is not False else None)
-    need = wbmm_backward_workspace_bytes(B, C, H, W, w, layout, mix_w is not None)
+    if shift is None:
+        need = wbmm_backward_workspace_bytes(B, C, H, W, w, layout, mix_w is not None)
+    else:
+        need = wbmm_backward_shifted_workspace_bytes(B, C, H, W, w, shift[0], shift[1], layout,
+                                                     mix_w is not None)
     if need and (workspace is None or workspace.numel() * workspace.element_size() < need):
         workspace = torch.empty(need, dtype=torch.uint8, device=dev)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    _check(_lib().wbmm_backward(B, C, H, W, int(w), _layout_code(layout), _ptr(x), _ptr(T), _ptr(M),
-                                _ptr(mix_w), _ptr(z_saved), _ptr(dy), _ptr(dx_t), _ptr(dT_t),
-                                _ptr(dW_t), _ptr(workspace), ws_bytes, _stream(stream)))
+    args = (_layout_code(layout), _ptr(x), _ptr(T), _ptr(M), _ptr(mix_w), _ptr(z_saved), _ptr(dy),
+            _ptr(dx_t), _ptr(dT_t), _ptr(dW_t), _ptr(workspace), ws_bytes, _stream(stream))
+    if shift is None:
+        _check(_lib().wbmm_backward(B, C, H, W, int(w), *args))
+    else:
+        _check(_lib().wbmm_backward_shifted(B, C, H, W, int(w), shift[0], shift[1], *args))
     return dx_t, dT_t, dW_t
 
 

@@ -180,23 +180,35 @@ wbmm::FwdRequest make_fwd(int B, int C, int H, int W, int w, int layout, int in_
 
 }  // namespace
 
-WBMM_API size_t wbmm_forward_workspace_bytes(int B, int C, int H, int W, int w, int layout,
-                                             int has_mix, int has_z_save) {
-  if (check_map(B, C, H, W, w, layout) != WBMM_OK) return 0;
+namespace {
+
+bool offsets_ok(int w, int oy, int ox) { return oy >= 0 && ox >= 0 && oy < w && ox < w; }
+
+size_t forward_ws_bytes(int B, int C, int H, int W, int w, int oy, int ox, int layout, int has_mix,
+                        int has_z_save) {
+  if (check_map(B, C, H + oy, W + ox, w, layout) != WBMM_OK || !offsets_ok(w, oy, ox)) return 0;
   static const float dummy = 0.f;
   wbmm::FwdRequest r = make_fwd(B, C, H, W, w, layout, WBMM_F32, WBMM_F32, &dummy, &dummy, nullptr,
                                 has_mix ? &dummy : nullptr, has_z_save ? (void*)&dummy : nullptr,
                                 (void*)&dummy, nullptr, 0);
+  r.oy = oy;
+  r.ox = ox;
   if (!wbmm::forward_plan_ok(r)) return 0;
   return wbmm::forward_workspace(r);
 }
 
-WBMM_API wbmm_status wbmm_forward(int B, int C, int H, int W, int w, int layout, int in_dtype,
-                                  int out_dtype, const void* x, const void* T, const void* M,
-                                  const float* mix_w, void* z_save, void* y, void* workspace,
-                                  size_t workspace_bytes, void* stream) {
+wbmm_status forward_call(int B, int C, int H, int W, int w, int oy, int ox, int layout,
+                         int in_dtype, int out_dtype, const void* x, const void* T, const void* M,
+                         const float* mix_w, void* z_save, void* y, void* workspace,
+                         size_t workspace_bytes, void* stream, const char* name) {
+  if (!offsets_ok(w, oy, ox))
+    return fail(WBMM_E_INVALID, "grid offset (%d, %d) outside [0, w=%d)", oy, ox, w);
+  const wbmm_status sm = check_map(B, C, H + oy, W + ox, w, layout);
+  if (sm != WBMM_OK) return sm;
   wbmm::FwdRequest r = make_fwd(B, C, H, W, w, layout, in_dtype, out_dtype, x, T, M, mix_w, z_save,
                                 y, workspace, workspace_bytes);
+  r.oy = oy;
+  r.ox = ox;
   wbmm_status st = check_forward(r, in_dtype, out_dtype);
   if (st != WBMM_OK) return st;
   const size_t need = wbmm::forward_workspace(r);
@@ -205,7 +217,37 @@ WBMM_API wbmm_status wbmm_forward(int B, int C, int H, int W, int w, int layout,
                 workspace ? workspace_bytes : (size_t)0);
   if (need > 0 && !aligned(workspace, 16))
     return fail(WBMM_E_UNSUPPORTED, "workspace not 16-byte aligned");
-  return hip_status(wbmm::launch_forward(r, (hipStream_t)stream), "wbmm_forward");
+  return hip_status(wbmm::launch_forward(r, (hipStream_t)stream), name);
+}
+
+}  // namespace
+
+WBMM_API size_t wbmm_forward_workspace_bytes(int B, int C, int H, int W, int w, int layout,
+                                             int has_mix, int has_z_save) {
+  return forward_ws_bytes(B, C, H, W, w, 0, 0, layout, has_mix, has_z_save);
+}
+
+WBMM_API wbmm_status wbmm_forward(int B, int C, int H, int W, int w, int layout, int in_dtype,
+                                  int out_dtype, const void* x, const void* T, const void* M,
+                                  const float* mix_w, void* z_save, void* y, void* workspace,
+                                  size_t workspace_bytes, void* stream) {
+  return forward_call(B, C, H, W, w, 0, 0, layout, in_dtype, out_dtype, x, T, M, mix_w, z_save, y,
+                      workspace, workspace_bytes, stream, "wbmm_forward");
+}
+
+WBMM_API size_t wbmm_forward_shifted_workspace_bytes(int B, int C, int H, int W, int w, int oy,
+                                                     int ox, int layout, int has_mix,
+                                                     int has_z_save) {
+  return forward_ws_bytes(B, C, H, W, w, oy, ox, layout, has_mix, has_z_save);
+}
+
+WBMM_API wbmm_status wbmm_forward_shifted(int B, int C, int H, int W, int w, int oy, int ox,
+                                          int layout, int in_dtype, int out_dtype, const void* x,
+                                          const void* T, const void* M, const float* mix_w,
+                                          void* z_save, void* y, void* workspace,
+                                          size_t workspace_bytes, void* stream) {
+  return forward_call(B, C, H, W, w, oy, ox, layout, in_dtype, out_dtype, x, T, M, mix_w, z_save,
+                      y, workspace, workspace_bytes, stream, "wbmm_forward_shifted");
 }
 
 namespace {
@@ -224,23 +266,30 @@ wbmm::BwdRequest make_bwd(int B, int C, int H, int W, int w, int layout, const f
 
 }  // namespace
 
-WBMM_API size_t wbmm_backward_workspace_bytes(int B, int C, int H, int W, int w, int layout,
-                                              int has_mix) {
-  if (check_map(B, C, H, W, w, layout) != WBMM_OK || w > 16) return 0;
+namespace {
+
+size_t backward_ws_bytes(int B, int C, int H, int W, int w, int oy, int ox, int layout,
+                         int has_mix) {
+  if (check_map(B, C, H + oy, W + ox, w, layout) != WBMM_OK || w > 16 || !offsets_ok(w, oy, ox))
+    return 0;
   static const float dummy = 0.f;
   wbmm::BwdRequest r = make_bwd(B, C, H, W, w, layout, &dummy, &dummy, nullptr,
                                 has_mix ? &dummy : nullptr, has_mix ? &dummy : nullptr, &dummy,
                                 nullptr, nullptr, nullptr, nullptr, 0);
+  r.oy = oy;
+  r.ox = ox;
   if (!wbmm::backward_plan_ok(r)) return 0;
   return wbmm::backward_workspace(r);
 }
 
-WBMM_API wbmm_status wbmm_backward(int B, int C, int H, int W, int w, int layout, const float* x,
-                                   const float* T, const float* M, const float* mix_w,
-                                   const float* z_saved, const float* dy, float* dx, float* dT,
-                                   float* dmix_w, void* workspace, size_t workspace_bytes,
-                                   void* stream) {
-  wbmm_status st = check_map(B, C, H, W, w, layout);
+wbmm_status backward_call(int B, int C, int H, int W, int w, int oy, int ox, int layout,
+                          const float* x, const float* T, const float* M, const float* mix_w,
+                          const float* z_saved, const float* dy, float* dx, float* dT,
+                          float* dmix_w, void* workspace, size_t workspace_bytes, void* stream,
+                          const char* name) {
+  if (!offsets_ok(w, oy, ox))
+    return fail(WBMM_E_INVALID, "grid offset (%d, %d) outside [0, w=%d)", oy, ox, w);
+  wbmm_status st = check_map(B, C, H + oy, W + ox, w, layout);
   if (st != WBMM_OK) return st;
   if (w > 16) return fail(WBMM_E_UNSUPPORTED, "the backward is provided for w <= 16 (w=%d)", w);
   if (!x || !dy) return fail(WBMM_E_INVALID, "x and dy must be non-NULL");
@@ -259,6 +308,8 @@ WBMM_API wbmm_status wbmm_backward(int B, int C, int H, int W, int w, int layout
     return fail(WBMM_E_INVALID, "dT overlaps T or dx");
   wbmm::BwdRequest r = make_bwd(B, C, H, W, w, layout, x, T, M, mix_w, z_saved, dy, dx, dT, dmix_w,
                                 workspace, workspace_bytes);
+  r.oy = oy;
+  r.ox = ox;
   if (!wbmm::backward_plan_ok(r))
     return fail(WBMM_E_UNSUPPORTED, "no launch shape fits this problem (w=%d)", w);
   const size_t need = wbmm::backward_workspace(r);
@@ -267,7 +318,38 @@ WBMM_API wbmm_status wbmm_backward(int B, int C, int H, int W, int w, int layout
                 workspace ? workspace_bytes : (size_t)0);
   if (need > 0 && !aligned(workspace, 256))
     return fail(WBMM_E_UNSUPPORTED, "workspace not 256-byte aligned");
-  return hip_status(wbmm::launch_backward(r, (hipStream_t)stream), "wbmm_backward");
+  return hip_status(wbmm::launch_backward(r, (hipStream_t)stream), name);
+}
+
+}  // namespace
+
+WBMM_API size_t wbmm_backward_workspace_bytes(int B, int C, int H, int W, int w, int layout,
+                                              int has_mix) {
+  return backward_ws_bytes(B, C, H, W, w, 0, 0, layout, has_mix);
+}
+
+WBMM_API wbmm_status wbmm_backward(int B, int C, int H, int W, int w, int layout, const float* x,
+                                   const float* T, const float* M, const float* mix_w,
+                                   const float* z_saved, const float* dy, float* dx, float* dT,
+                                   float* dmix_w, void* workspace, size_t workspace_bytes,
+                                   void* stream) {
+  return backward_call(B, C, H, W, w, 0, 0, layout, x, T, M, mix_w, z_saved, dy, dx, dT, dmix_w,
+                       workspace, workspace_bytes, stream, "wbmm_backward");
+}
+
+WBMM_API size_t wbmm_backward_shifted_workspace_bytes(int B, int C, int H, int W, int w, int oy,
+                                                      int ox, int layout, int has_mix) {
+  return backward_ws_bytes(B, C, H, W, w, oy, ox, layout, has_mix);
+}
+
+WBMM_API wbmm_status wbmm_backward_shifted(int B, int C, int H, int W, int w, int oy, int ox,
+                                           int layout, const float* x, const float* T,
+                                           const float* M, const float* mix_w,
+                                           const float* z_saved, const float* dy, float* dx,
+                                           float* dT, float* dmix_w, void* workspace,
+                                           size_t workspace_bytes, void* stream) {
+  return backward_call(B, C, H, W, w, oy, ox, layout, x, T, M, mix_w, z_saved, dy, dx, dT, dmix_w,
+                       workspace, workspace_bytes, stream, "wbmm_backward_shifted");
 }
 namespace {
 // Shared checks of the hierarchical entry points: fp32 table path with the s x s sub-window

@@ -100,8 +100,8 @@ __global__ void __launch_bounds__(kThreads) k_wbmm_bwd(BwdArgs a) {
 #pragma unroll
         for (int t = 0; t < 3; ++t) dz = fmaf(w9[u * 3 + t], P[(p - u + 2) * g.PW + (q - t + 2)], dz);
       uint32_t wy, y, wx, xx;
-      fdivmod(p, g.fd_w, wy, y);
-      fdivmod(q, g.fd_w, wx, xx);
+      fdivmod(p + g.oy, g.fd_w, wy, y);
+      fdivmod(q + g.ox, g.fd_w, wx, xx);
       const int n = (int)img * g.nWin + (int)wy * g.nW + (int)wx;
       Gt[xs_slot_f32(g, n, (int)y, (int)xx)] = dz;
       if (a.want_dW) {
@@ -308,8 +308,8 @@ static bool plan_bwd(Geo& g, const BwdRequest& r) {
   const bool cached = r.M != nullptr;
   const bool mix = r.mixw != nullptr;
   const int s = r.Tsub ? r.s : 0;
-  if (!plan_geo(g, r.B, r.C, r.H, r.W, r.w, r.layout, false, cached, mix, 1, s)) {
-    if (!plan_geo(g, r.B, r.C, r.H, r.W, r.w, r.layout, false, cached, false, 1, s)) return false;
+  if (!plan_geo(g, r.B, r.C, r.H, r.W, r.w, r.layout, false, cached, mix, 1, s, r.oy, r.ox)) {
+    if (!plan_geo(g, r.B, r.C, r.H, r.W, r.w, r.layout, false, cached, false, 1, s, r.oy, r.ox)) return false;
   }
   return g.WR == 1;
 }

@@ -78,8 +78,8 @@ __device__ __forceinline__ void load_xtile(const Geo& g, const TIn* __restrict__
       const int b = colgrp * g.ipw + (int)img;
       if (b >= g.B) continue;
       uint32_t wy, y, wx, xx;
-      fdivmod(h, g.fd_w, wy, y);
-      fdivmod(v, g.fd_w, wx, xx);
+      fdivmod(h + g.oy, g.fd_w, wy, y);
+      fdivmod(v + g.ox, g.fd_w, wx, xx);
       const int n = (int)img * g.nWin + (int)wy * g.nW + (int)wx;
       put_tile<TIn>(g, tile, n, (int)y, (int)xx, x,
                     map_off(g.layout, b, c, (int)h, (int)v, g.C, g.H, g.W));
@@ -92,8 +92,8 @@ __device__ __forceinline__ void load_xtile(const Geo& g, const TIn* __restrict__
       int b, wy, wx;
       if (!wg_window(g, colgrp, (int)n, b, wy, wx)) continue;
       fdivmod(k, g.fd_w, y, xx);
-      const int h = wy * g.w + (int)y, v = wx * g.w + (int)xx;
-      if (h >= g.H || v >= g.W) continue;
+      const int h = wy * g.w + (int)y - g.oy, v = wx * g.w + (int)xx - g.ox;
+      if (h < 0 || v < 0 || h >= g.H || v >= g.W) continue;
       put_tile<TIn>(g, tile, (int)n, (int)y, (int)xx, x,
                     map_off(g.layout, b, c, h, v, g.C, g.H, g.W));
     }
@@ -350,8 +350,8 @@ __device__ __forceinline__ void stage_acc(const Geo& g, int colgrp, int wr, int 
       if (i >= g.d) continue;
       uint32_t yi, xi;
       fdivmod((uint32_t)i, g.fd_w, yi, xi);
-      const int h = (int)wy * g.w + (int)yi, v = (int)wx * g.w + (int)xi;
-      if (h < g.H && v < g.W) P[(h + 1) * g.PW + v + 1] = acc[t][r];
+      const int h = (int)wy * g.w + (int)yi - g.oy, v = (int)wx * g.w + (int)xi - g.ox;
+      if (h >= 0 && v >= 0 && h < g.H && v < g.W) P[(h + 1) * g.PW + v + 1] = acc[t][r];
     }
   }
 }
@@ -374,8 +374,8 @@ __device__ __forceinline__ void store_acc_direct(const Geo& g, int colgrp, int w
       if (i >= g.d) continue;
       uint32_t yi, xi;
       fdivmod((uint32_t)i, g.fd_w, yi, xi);
-      const int h = wy * g.w + (int)yi, v = wx * g.w + (int)xi;
-      if (h >= g.H || v >= g.W) continue;
+      const int h = wy * g.w + (int)yi - g.oy, v = wx * g.w + (int)xi - g.ox;
+      if (h < 0 || v < 0 || h >= g.H || v >= g.W) continue;
       const size_t off = map_off(g.layout, b, c, h, v, g.C, g.H, g.W);
       store_out(out, off, acc[t][r], out_bf16);
       if (out2) store_out(out2, off, acc[t][r], out_bf16);

@@ -987,11 +987,12 @@ bool offsets_fit(int C, int H, int W) { return (size_t)16 * C * H * W < ((size_t
 // A sub-table is folded on chip when its sub-windows are the quadrants (w = 2s).
 bool fast_forward_ok(const FwdRequest& r) {
   return !r.in_bf16 && !r.out_bf16 && r.T && !r.M && (!r.Tsub || 2 * r.s == r.w) &&
+         r.oy == 0 && r.ox == 0 &&
          fast_shape(r.H, r.W, r.w, r.layout) != FS_NONE && offsets_fit(r.C, r.H, r.W);
 }
 
 bool fast_backward_ok(const BwdRequest& r) {
-  return r.T && !r.M && (!r.Tsub || 2 * r.s == r.w) &&
+  return r.T && !r.M && (!r.Tsub || 2 * r.s == r.w) && r.oy == 0 && r.ox == 0 &&
          fast_shape(r.H, r.W, r.w, r.layout) != FS_NONE && offsets_fit(r.C, r.H, r.W);
 }
 

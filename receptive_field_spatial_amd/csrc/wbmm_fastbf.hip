@@ -704,7 +704,8 @@ static_assert(2 * ((bf28_lds_bytes<Bf28Shape<56>>() + kLdsGranule - 1) / kLdsGra
 
 bool fast_bf16_forward_ok(const FwdRequest& r) {
   // unit indices (C * groups) are ints
-  return r.in_bf16 && r.out_bf16 && r.T && !r.M && !r.mixw && r.B > 0 && r.C > 0 &&
+  return r.in_bf16 && r.out_bf16 && r.T && !r.M && !r.mixw && !r.Tsub && r.oy == 0 &&
+         r.ox == 0 && r.B > 0 && r.C > 0 &&
          (long long)r.C * ((r.B + 3) / 4 + 1) < ((long long)1 << 31) && bf_shape(r) != BF_NONE;
 }
 

@@ -126,11 +126,11 @@ static bool plan_fwd(Geo& g, const FwdRequest& r) {
   const bool cached = r.M != nullptr;
   const bool mix = r.mixw != nullptr;
   const int s = r.Tsub ? r.s : 0;
-  if (!plan_geo(g, r.B, r.C, r.H, r.W, r.w, r.layout, r.in_bf16, cached, true, 0, s)) {
-    if (!plan_geo(g, r.B, r.C, r.H, r.W, r.w, r.layout, r.in_bf16, cached, false, 0, s)) return false;
+  if (!plan_geo(g, r.B, r.C, r.H, r.W, r.w, r.layout, r.in_bf16, cached, true, 0, s, r.oy, r.ox)) {
+    if (!plan_geo(g, r.B, r.C, r.H, r.W, r.w, r.layout, r.in_bf16, cached, false, 0, s, r.oy, r.ox)) return false;
   }
   if (g.image_mode && !mix && 4 * g.ipw * g.nWin < 3 * g.NT) {
-    if (!plan_geo(g, r.B, r.C, r.H, r.W, r.w, r.layout, r.in_bf16, cached, false, 0, s)) return false;
+    if (!plan_geo(g, r.B, r.C, r.H, r.W, r.w, r.layout, r.in_bf16, cached, false, 0, s, r.oy, r.ox)) return false;
   }
   return true;
 }

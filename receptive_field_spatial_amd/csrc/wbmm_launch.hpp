@@ -21,6 +21,7 @@ struct FwdRequest {
   size_t ws_bytes;
   const float* Tsub;  // s x s sub-window tables folded on chip (fp32 table path, w = 2s), or null
   int s;
+  int oy, ox;         // window grid offset (0 <= oy, ox < w); the fast paths take 0, 0 only
 };
 
 struct BwdRequest {
@@ -39,6 +40,7 @@ struct BwdRequest {
   const float* Tsub;  // as in FwdRequest; with it, dTsub (or null) receives the sub-table gradient
   int s;
   float* dTsub;
+  int oy, ox;         // as in FwdRequest
 };
 
 hipError_t launch_build_index(int w, int32_t* idx, hipStream_t st);

@@ -25,6 +25,8 @@ struct Geo {
   int Hp, Wp, nH, nW, nWin, N;    // padded map, window grid, windows per image, per channel
   int layout;
   int s;            // hierarchical sub-window side folded on chip (w = 2s), or 0
+  int oy, ox;       // window grid offset: window (wy, wx) covers map rows wy*w - oy .. and
+                    // columns wx*w - ox .. (0 for the plain grid)
   // fp32 K mapping
   int KQ, RP, XR;   // K-steps, window row pitch, X-tile stride per window (floats)
   // bf16 K mapping
@@ -68,14 +70,19 @@ constexpr int kMaxLds = 160 * 1024;
 // want_image: ask for image mode (needed for an in-kernel 3x3 mix);
 // extra_big: bytes the caller needs in the big region beyond the X tile (backward's G tile).
 // hier_s: fold an s x s sub-window table on chip (fp32 table path, w = 2s only).
+// oy, ox: window grid offset, 0 <= oy, ox < w.
 inline bool plan_geo(Geo& g, int B, int C, int H, int W, int w, int layout, bool bf16,
-                     bool cached, bool want_image, int big_extra_tiles, int hier_s = 0) {
+                     bool cached, bool want_image, int big_extra_tiles, int hier_s = 0,
+                     int oy = 0, int ox = 0) {
   g = Geo{};
   if (hier_s && (bf16 || cached || 2 * hier_s != w)) return false;
+  if (oy < 0 || ox < 0 || oy >= w || ox >= w) return false;
   g.s = hier_s;
+  g.oy = oy;
+  g.ox = ox;
   g.B = B; g.C = C; g.H = H; g.W = W; g.w = w; g.d = w * w;
   g.w2m1 = 2 * w - 1; g.L = g.w2m1 * g.w2m1;
-  g.Hp = (H + w - 1) / w * w; g.Wp = (W + w - 1) / w * w;
+  g.Hp = (H + oy + w - 1) / w * w; g.Wp = (W + ox + w - 1) / w * w;
   g.nH = g.Hp / w; g.nW = g.Wp / w; g.nWin = g.nH * g.nW; g.N = B * g.nWin;
   g.layout = layout;
   pick_tiles(g.d, g.RPW, g.WR);

@@ -42,7 +42,7 @@ def test_header_declares_the_entry_points():
     for name in ["wbmm_build_index", "wbmm_build_matrix", "wbmm_fold_hier", "wbmm_forward",
                  "wbmm_backward", "wbmm_forward_workspace_bytes", "wbmm_backward_workspace_bytes",
                  "wbmm_last_error", "wbmm_abi_version", "wbmm_forward_hier", "wbmm_backward_hier",
-                 "wbmm_dwconv_forward"]:
+                 "wbmm_dwconv_forward", "wbmm_forward_shifted", "wbmm_backward_shifted"]:
         assert name in fns, name
 
 
@@ -196,6 +196,26 @@ def test_hier_validation(lib):
     assert hier_bwd(lib) == R.WBMM_E_WORKSPACE
     assert hier_bwd(lib, ws=0xA00000, wsb=need - 1) == R.WBMM_E_WORKSPACE
     assert lib.wbmm_forward_hier_workspace_bytes(1, 2, 128, 128, 14, 7, 0, 1, 0) > 0  # window-mode mix
+
+
+def test_shifted_validation(lib):
+    """Window-grid offsets must lie in [0, w); the rest is checked as in the plain calls."""
+    for oy, ox in [(-1, 0), (0, 14), (14, 3), (2, -3)]:
+        assert lib.wbmm_forward_shifted(2, 3, 28, 28, 14, oy, ox, 0, 0, 0, FAKE, 0x300000, None,
+                                        None, None, FAKE2, None, 0, None) == R.WBMM_E_INVALID
+        assert lib.wbmm_backward_shifted(2, 3, 28, 28, 14, oy, ox, 0, FAKE, 0x300000, None, None,
+                                         None, 0x400000, FAKE2, None, None, None, 0,
+                                         None) == R.WBMM_E_INVALID
+        assert lib.wbmm_forward_shifted_workspace_bytes(2, 3, 28, 28, 14, oy, ox, 0, 1, 0) == 0
+        assert lib.wbmm_backward_shifted_workspace_bytes(2, 3, 28, 28, 14, oy, ox, 0, 0) == 0
+    assert "grid offset" in err(lib)
+    # y aliasing x is still caught with a valid offset; backward w <= 16
+    assert lib.wbmm_forward_shifted(2, 3, 28, 28, 14, 7, 7, 0, 0, 0, FAKE, 0x300000, None, None,
+                                    None, FAKE, None, 0, None) == R.WBMM_E_INVALID
+    assert lib.wbmm_backward_shifted(2, 3, 40, 40, 20, 10, 10, 0, FAKE, 0x300000, None, None,
+                                     None, 0x400000, FAKE2, None, None, None, 0,
+                                     None) == R.WBMM_E_UNSUPPORTED
+    assert lib.wbmm_backward_shifted_workspace_bytes(2, 3, 28, 28, 14, 7, 7, 0, 0) > 0
 
 
 def test_dwconv_validation(lib):

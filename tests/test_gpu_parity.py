@@ -700,3 +700,78 @@ def test_dwconv_full_size_sampled():
     for b, c in [(0, 0), (127, 255), (64, 3), (5, 200), (100, 129)]:
         want = O.dw_conv_forward(xn[b:b + 1, c:c + 1].astype(np.float64), wn[c:c + 1])
         assert_f32(y[b:b + 1, c:c + 1], want, f"plane ({b},{c})")
+
+
+# ----------------------------------------------------------------------------- shifted window grid
+SHIFT_CASES = [(2, 3, 28, 28, 14, 7, 7), (1, 2, 30, 25, 14, 3, 11), (2, 3, 17, 13, 4, 2, 1),
+               (1, 2, 128, 128, 14, 7, 7), (2, 2, 9, 9, 7, 0, 3)]
+
+
+@pytest.mark.parametrize("B,C,H,W,w,oy,ox", SHIFT_CASES)
+@pytest.mark.parametrize("mix", [False, True])
+@pytest.mark.parametrize("src", ["T", "M"])
+def test_forward_shifted(B, C, H, W, w, oy, ox, mix, src):
+    """Interleaved grid (offset windows, zero border pixels) against the oracle: image and window
+    mode, ragged maps, table and cached matrix, with and without the 3x3 mix."""
+    say(f"forward shifted B={B} C={C} H={H} W={W} w={w} o=({oy},{ox}) mix={mix} src={src}")
+    x = synth.normal_f32((B, C, H, W), 1.0, seed=240)
+    T = synth.normal_f32((C, 2 * w - 1, 2 * w - 1), 0.05, seed=241)
+    Wm = synth.normal_f32((C, 3, 3), 0.1, seed=242) if mix else None
+    kw = {"T": dev(T)} if src == "T" else {"M": R().wbmm_build_matrix(dev(T), w)}
+    zs = torch.empty((B, C, H, W), device="cuda")
+    y = R().wbmm_forward_shifted(dev(x), w, oy, ox, mix_w=dev(Wm) if mix else None, z_save=zs,
+                                 **kw)
+    want_y, want_z = O.layer_forward_shifted(x.astype(np.float64), w, oy, ox, T=T, Wmix=Wm)
+    assert_f32(host(y), want_y, "y")
+    assert_f32(host(zs), want_z, "z")
+
+
+@pytest.mark.parametrize("B,C,H,W,w,oy,ox", [(2, 3, 28, 28, 14, 7, 7), (1, 2, 17, 13, 4, 2, 1),
+                                             (1, 2, 56, 56, 14, 5, 9)])
+def test_forward_shifted_bf16(B, C, H, W, w, oy, ox):
+    say(f"forward shifted bf16 B={B} C={C} H={H} W={W} w={w} o=({oy},{ox})")
+    x = synth.round_to_bf16(synth.normal_f32((B, C, H, W), 1.0, seed=245))
+    T = synth.round_to_bf16(synth.normal_f32((C, 2 * w - 1, 2 * w - 1), 0.05, seed=246))
+    y = R().wbmm_forward_shifted(dev_bf16(x), w, oy, ox, T=dev_bf16(T))
+    want = O.wbmm_forward_shifted(x.astype(np.float64), w, oy, ox, T=T)
+    assert_bf16(host(y.float()), want, "y")
+
+
+@pytest.mark.parametrize("B,C,H,W,w,oy,ox", SHIFT_CASES)
+@pytest.mark.parametrize("mix", [False, True])
+def test_backward_shifted(B, C, H, W, w, oy, ox, mix):
+    """dx, dT (and dWmix) on the interleaved grid against the oracle; run twice, bitwise equal."""
+    say(f"backward shifted B={B} C={C} H={H} W={W} w={w} o=({oy},{ox}) mix={mix}")
+    x = synth.normal_f32((B, C, H, W), 1.0, seed=250)
+    T = synth.normal_f32((C, 2 * w - 1, 2 * w - 1), 0.05, seed=251)
+    dy = synth.normal_f32((B, C, H, W), 1.0, seed=252)
+    Wm = synth.normal_f32((C, 3, 3), 0.1, seed=253) if mix else None
+    xd, Td, dyd = dev(x), dev(T), dev(dy)
+    Wd = dev(Wm) if mix else None
+    zs = None
+    if mix:
+        zs = torch.empty_like(xd)
+        R().wbmm_forward_shifted(xd, w, oy, ox, T=Td, mix_w=Wd, z_save=zs)
+    dx, dT, dW = R().wbmm_backward_shifted(xd, dyd, w, oy, ox, T=Td, mix_w=Wd, z_saved=zs)
+    z64 = host(zs).astype(np.float64) if mix else None
+    wdx, wdT, wdW = O.layer_backward_shifted(x.astype(np.float64), dy.astype(np.float64), w, oy,
+                                             ox, T=T, Wmix=Wm, z=z64)
+    assert_f32(host(dx), wdx, "dx")
+    assert_f32(host(dT), wdT, "dT")
+    if mix:
+        assert_f32(host(dW), wdW, "dWmix")
+    dx2, dT2, _ = R().wbmm_backward_shifted(xd, dyd, w, oy, ox, T=Td, mix_w=Wd, z_saved=zs)
+    assert torch.equal(dx, dx2) and torch.equal(dT, dT2)
+
+
+def test_shifted_zero_offset_is_the_plain_call():
+    """(0, 0) through the shifted entry points is the plain call, bit for bit."""
+    B, C, H, W, w = 4, 3, 28, 28, 14
+    say("shifted zero offset")
+    x = dev(synth.normal_f32((B, C, H, W), 1.0, seed=260))
+    T = dev(synth.normal_f32((C, 27, 27), 0.05, seed=261))
+    dy = dev(synth.normal_f32((B, C, H, W), 1.0, seed=262))
+    assert torch.equal(R().wbmm_forward_shifted(x, w, 0, 0, T=T), R().wbmm_forward(x, w, T=T))
+    a = R().wbmm_backward_shifted(x, dy, w, 0, 0, T=T)
+    b = R().wbmm_backward(x, dy, w, T=T)
+    assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
