@@ -22,6 +22,7 @@ import glob
 import hashlib
 import json
 import os
+import re
 import statistics
 import sys
 import time
@@ -43,19 +44,31 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-# kernel -> the source file that defines it. A kernel's hash covers that file and the headers
-# with device code; wbmm_launch.hpp (host-side request structs and launcher declarations) and
-# the other kernels' files do not change it.
+# kernel -> the source file that defines it. A kernel's hash covers that file and the device
+# headers it includes (directly or through another header); wbmm_launch.hpp (host-side request
+# structs and launcher declarations) and the other kernels' files do not change it.
 KERNEL_FILES = {"k_fwd_ws": "wbmm_fast.hip", "k_bwd_ls": "wbmm_fast.hip",
                 "k_fwd_bf16_w7": "wbmm_fastbf.hip",
                 "k_fwd_bf16_w28": "wbmm_fastbf.hip", "k_fwd_bf16": "wbmm_fastbf.hip",
                 "k_wbmm_fwd": "wbmm_fwd.hip", "k_wbmm_bwd": "wbmm_bwd.hip"}
-DEVICE_HEADERS = ("wbmm_device.hpp", "wbmm_core.hpp", "wbmm_plan.hpp")
+HOST_HEADERS = ("wbmm_launch.hpp",)
+
+
+def _device_sources(name: str, seen=None):
+    """`name` and the local headers it includes, transitively, minus the host-side ones."""
+    seen = [] if seen is None else seen
+    if name in seen or name in HOST_HEADERS:
+        return seen
+    seen.append(name)
+    with open(os.path.join(CSRC, name), encoding="utf-8") as f:
+        for inc in re.findall(r'^\s*#include\s+"([^"]+)"', f.read(), flags=re.M):
+            _device_sources(inc, seen)
+    return seen
 
 
 def kernel_source_hash(kernel: str) -> str:
     h = hashlib.sha256()
-    for name in (KERNEL_FILES[kernel],) + DEVICE_HEADERS:
+    for name in sorted(_device_sources(KERNEL_FILES[kernel])):
         with open(os.path.join(CSRC, name), encoding="utf-8") as f:
             h.update(name.encode())
             h.update(_code_only(f.read()).encode())
@@ -124,7 +137,11 @@ def cpu_baseline(wl, budget_s: float = 10.0):
     t_start = time.perf_counter()
     while True:
         t0 = time.perf_counter()
-        if Ts is not None:
+        if wl.shift:
+            y, z = O.layer_forward_shifted(x, wl.w, wl.shift, wl.shift, T=T, Wmix=Wm)
+            if wl.backward:
+                O.layer_backward_shifted(x, dy, wl.w, wl.shift, wl.shift, T=T, Wmix=Wm, z=z)
+        elif Ts is not None:
             y, z = O.layer_forward_hier(x, wl.w, wl.s, T, Ts, Wmix=Wm)
             if wl.backward:
                 O.layer_backward_hier(x, dy, wl.w, wl.s, T, Ts, Wmix=Wm, z=z)
@@ -191,6 +208,46 @@ class HipEvents:
         self.hip.hipEventDestroy(self.ct.c_void_p(ev))
 
 
+# ----------------------------------------------------------------------------- measured peaks
+def measure_peaks(R, torch, hev):
+    """Peaks measured in the same session, beside the datasheet ones: the matrix-core probe
+    (wbmm_probe_mfma: 8 independent MFMA chains per wave, 4096 waves, no memory traffic) for fp32
+    and bf16, and a 1 GiB device-to-device copy (read + write bytes / time) for HBM. Best of 3."""
+    out = torch.empty(1024 * 256, dtype=torch.float32, device="cuda")
+    peaks = {}
+    for name, dt, iters in (("fp32_mfma_tflops", torch.float32, 2000),
+                            ("bf16_mfma_tflops", torch.bfloat16, 2048)):
+        best = 0.0
+        for _ in range(3):
+            a, b = hev.create(), hev.create()
+            R.wbmm_set_launch_events(a, b)
+            flops = R.wbmm_probe_mfma(dt, 1024, iters, out=out)
+            torch.cuda.synchronize()
+            best = max(best, flops / (hev.elapsed_ms(a, b) / 1e3) / 1e12)
+            hev.destroy(a)
+            hev.destroy(b)
+        peaks[name] = round(best, 1)
+    n = (1 << 30) // 4
+    src = torch.ones(n, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    best = 0.0
+    for _ in range(3):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        dst.copy_(src)
+        e1.record()
+        torch.cuda.synchronize()
+        best = max(best, 2 * n * 4 / (e0.elapsed_time(e1) / 1e3) / 1e9)
+    peaks["hbm_copy_gbs"] = round(best, 1)
+    del src, dst
+    return peaks
+
+
+def _pct(xs, q):
+    xs = sorted(xs)
+    return xs[min(len(xs) - 1, max(0, int(round(q * (len(xs) - 1)))))]
+
+
 # ----------------------------------------------------------------------------- GPU run
 def run(args):
     import numpy as np
@@ -236,13 +293,20 @@ def run(args):
            if hier_train else None)
     ws_b = None
     if wl.backward:
-        if hier_train:
+        if wl.shift:
+            nb = R.wbmm_backward_shifted_workspace_bytes(wl.B, wl.C, wl.H, wl.W, wl.w, wl.shift,
+                                                         wl.shift, has_mix=wl.mix)
+        elif hier_train:
             nb = R.wbmm_backward_hier_workspace_bytes(wl.B, wl.C, wl.H, wl.W, wl.w, wl.s,
                                                       has_mix=wl.mix)
         else:
             nb = R.wbmm_backward_workspace_bytes(wl.B, wl.C, wl.H, wl.W, wl.w, has_mix=wl.mix)
         ws_b = torch.zeros(nb, dtype=torch.uint8, device=dev)
-    if hier_train:
+    if wl.shift:
+        nf = R.wbmm_forward_shifted_workspace_bytes(wl.B, wl.C, wl.H, wl.W, wl.w, wl.shift,
+                                                    wl.shift, has_mix=wl.mix,
+                                                    has_z_save=wl.backward)
+    elif hier_train:
         nf = R.wbmm_forward_hier_workspace_bytes(wl.B, wl.C, wl.H, wl.W, wl.w, wl.s,
                                                  has_mix=wl.mix, has_z_save=True)
     else:
@@ -253,6 +317,10 @@ def run(args):
     kw_tab = {"M": M} if M is not None else {"T": T}
 
     def fwd(s):
+        if wl.shift:
+            R.wbmm_forward_shifted(s["x"], wl.w, wl.shift, wl.shift, mix_w=Wm, y=s["y"],
+                                   z_save=s.get("z"), workspace=ws_f, stream=stream, **kw_tab)
+            return
         if hier_train:
             R.wbmm_forward_hier(s["x"], wl.w, wl.s, T, Tsub, mix_w=Wm, y=s["y"], z_save=s["z"],
                                 workspace=ws_f, stream=stream)
@@ -261,6 +329,12 @@ def run(args):
                        stream=stream, **kw_tab)
 
     def bwd(s):
+        if wl.shift:
+            R.wbmm_backward_shifted(s["x"], s["dy"], wl.w, wl.shift, wl.shift, mix_w=Wm,
+                                    z_saved=s["z"] if wl.mix else None, dx=s["dx"], dT=dT,
+                                    dmix_w=dW if wl.mix else False, workspace=ws_b,
+                                    stream=stream, **kw_tab)
+            return
         if hier_train:
             R.wbmm_backward_hier(s["x"], s["dy"], wl.w, wl.s, T, Tsub, mix_w=Wm,
                                  z_saved=s["z"] if wl.mix else None, dx=s["dx"], dT=dT,
@@ -304,6 +378,18 @@ def run(args):
     for e in kev:
         for h in e:
             hev.destroy(h)
+    # warm: the same input set every step (resident in the 256 MB last-level cache when it fits)
+    torch.cuda.synchronize()
+    w0, w1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    w0.record(stream)
+    for i in range(K):
+        fwd(sets[0])
+        if wl.backward:
+            bwd(sets[0])
+    w1.record(stream)
+    torch.cuda.synchronize()
+    warm_ms = w0.elapsed_time(w1) / K
+    peaks = measure_peaks(R, torch, hev)
     log(f"[bench] {wl.name}: {K} steps in {total_ms:.3f} ms GPU ({wall*1e3:.1f} ms wall); "
         f"fwd kernel avg {statistics.mean(fwd_ms)*1e3:.1f} us"
         + (f", bwd kernel avg {statistics.mean(bwd_ms)*1e3:.1f} us" if bwd_ms else ""))
@@ -325,6 +411,10 @@ def run(args):
         achieved = kbytes / ksec / 1e9
         roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBS, 4)}
+    meas = (peaks["hbm_copy_gbs"] if roof["bound"] == "hbm" else
+            peaks["bf16_mfma_tflops"] if bf16 else peaks["fp32_mfma_tflops"])
+    roof["peak_measured"] = meas
+    roof["frac_of_measured"] = round(roof["achieved"] / meas, 4)
     roof["traffic"] = load_traffic(wl.name, kname)
     roof["kernel"] = kname
     roof["kernel_us"] = round(ksec * 1e6, 2)
@@ -345,7 +435,8 @@ def run(args):
         "dtype": "bf16" if bf16 else "f32",
         "data": "synthetic",
         "config": {"workload": wl.name, "B": wl.B, "C": wl.C, "H": wl.H, "W": wl.W, "w": wl.w,
-                   "mix": wl.mix, "fold_s": wl.s, "pass": "fwd+bwd" if wl.backward else "fwd",
+                   "mix": wl.mix, "fold_s": wl.s, "grid_offset": wl.shift,
+                   "pass": "fwd+bwd" if wl.backward else "fwd",
                    "matrix": ("cached M" if M is not None else
                               "formed and folded on chip from T, T_sub" if hier_train else
                               "formed on chip from T"),
@@ -355,6 +446,11 @@ def run(args):
     }
     if wl.backward:
         line["kernels_us"] = {k: round(v[0] * 1e6, 2) for k, v in kernels.items()}
+    kl = bwd_ms if kname == "k_wbmm_bwd" else fwd_ms
+    roof["kernel_us_median_p10_p90"] = [round(statistics.median(kl) * 1e3, 2),
+                                        round(_pct(kl, 0.1) * 1e3, 2), round(_pct(kl, 0.9) * 1e3, 2)]
+    line["ms_per_step_warm"] = round(warm_ms, 4)
+    line["peaks_measured"] = peaks
     if args.cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(wl, args.cpu_budget)
     return line

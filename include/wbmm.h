@@ -264,8 +264,21 @@ wbmm_status wbmm_dwconv_forward(int B, int C, int H, int W, int k, const float* 
                                 const float* w_dw, float* y, void* stream);
 
 /*
+ * wbmm_probe_mfma — measurement aid, not part of the method: a matrix-core peak probe. Launches
+ * `blocks` workgroups of 4 waves; every wave runs `iters` rounds of 8 independent MFMA
+ * accumulation chains on register operands (dtype WBMM_F32: v_mfma_f32_16x16x4f32, WBMM_BF16:
+ * v_mfma_f32_16x16x32_bf16) and writes one float per lane to out (device, blocks * 256 floats),
+ * so the sustained matrix rate on this part and clock can be set beside the datasheet peak.
+ * wbmm_probe_mfma_flops returns the flops of such a launch (0 for invalid arguments).
+ * wbmm_set_launch_events attaches to it like to the main kernel of the other calls.
+ * Errors: WBMM_E_INVALID (dtype, blocks or iters < 1, NULL or misaligned out), WBMM_E_HIP.
+ */
+double wbmm_probe_mfma_flops(int dtype, int blocks, int iters);
+wbmm_status wbmm_probe_mfma(int dtype, int blocks, int iters, float* out, void* stream);
+
+/*
  * wbmm_set_launch_events — measurement aid, not part of the method. The next wbmm_forward,
- * wbmm_backward (or their _hier and _shifted forms) or wbmm_dwconv_forward call made on the calling thread
+ * wbmm_backward (or their _hier and _shifted forms), wbmm_dwconv_forward or wbmm_probe_mfma call made on the calling thread
  * attaches `before` and `after` (hipEvent_t
  * handles passed as void*) to the dispatch of its main contraction kernel (hipExtLaunchKernel's
  * start and stop events), so their elapsed time is that kernel's execution; the pair is then

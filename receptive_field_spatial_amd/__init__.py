@@ -20,7 +20,7 @@ __all__ = [
     "wbmm_forward_hier", "wbmm_forward_hier_workspace_bytes",
     "wbmm_backward_hier", "wbmm_backward_hier_workspace_bytes", "wbmm_dwconv_forward",
     "wbmm_forward_shifted", "wbmm_forward_shifted_workspace_bytes", "wbmm_backward_shifted",
-    "wbmm_backward_shifted_workspace_bytes",
+    "wbmm_backward_shifted_workspace_bytes", "wbmm_probe_mfma",
     "WBMM_OK", "WBMM_E_INVALID", "WBMM_E_UNSUPPORTED", "WBMM_E_WORKSPACE", "WBMM_E_HIP",
 ]
 
@@ -61,6 +61,8 @@ def _declare(lib):
         "wbmm_backward_hier_workspace_bytes": (c_size, [c_int] * 8),
         "wbmm_backward_hier": (c_int, [c_int] * 7 + [vp] * 11 + [c_size, vp]),
         "wbmm_dwconv_forward": (c_int, [c_int] * 5 + [vp] * 4),
+        "wbmm_probe_mfma_flops": (ctypes.c_double, [c_int] * 3),
+        "wbmm_probe_mfma": (c_int, [c_int] * 3 + [vp, vp]),
         "wbmm_forward_shifted_workspace_bytes": (c_size, [c_int] * 10),
         "wbmm_forward_shifted": (c_int, [c_int] * 10 + [vp] * 7 + [c_size, vp]),
         "wbmm_backward_shifted_workspace_bytes": (c_size, [c_int] * 9),
@@ -372,3 +374,14 @@ def wbmm_dwconv_forward(x, w_dw, *, y=None, stream=None):
     _check(_lib().wbmm_dwconv_forward(B, C, H, W, k, _ptr(x), _ptr(w_dw), _ptr(y),
                                       _stream(stream)))
     return y
+
+
+def wbmm_probe_mfma(dtype, blocks: int, iters: int, *, out=None, stream=None) -> float:
+    """Matrix-core peak probe (measurement aid): launches it and returns the launch's flops.
+    dtype: torch.float32 or torch.bfloat16 (the MFMA operand type)."""
+    torch = _torch()
+    if out is None:
+        out = torch.empty(blocks * 256, dtype=torch.float32, device="cuda")
+    code = _dtype_code(dtype)
+    _check(_lib().wbmm_probe_mfma(code, int(blocks), int(iters), _ptr(out), _stream(stream)))
+    return float(_lib().wbmm_probe_mfma_flops(code, int(blocks), int(iters)))

@@ -473,3 +473,19 @@ WBMM_API wbmm_status wbmm_dwconv_forward(int B, int C, int H, int W, int k, cons
   return hip_status(wbmm::launch_dwconv(B, C, H, W, k, x, w_dw, y, (hipStream_t)stream),
                     "wbmm_dwconv_forward");
 }
+
+WBMM_API double wbmm_probe_mfma_flops(int dtype, int blocks, int iters) {
+  if (!valid_dtype(dtype) || blocks < 1 || iters < 1) return 0.0;
+  return wbmm::probe_mfma_flops(dtype == WBMM_BF16, blocks, iters);
+}
+
+WBMM_API wbmm_status wbmm_probe_mfma(int dtype, int blocks, int iters, float* out, void* stream) {
+  if (!valid_dtype(dtype)) return fail(WBMM_E_INVALID, "unknown dtype %d", dtype);
+  if (blocks < 1 || iters < 1 || blocks > 1 << 20)
+    return fail(WBMM_E_INVALID, "blocks=%d and iters=%d must be >= 1 (blocks <= 2^20)", blocks,
+                iters);
+  if (!out || !aligned(out, 4)) return fail(WBMM_E_INVALID, "out must be a 4-byte aligned pointer");
+  return hip_status(wbmm::launch_probe_mfma(dtype == WBMM_BF16, blocks, iters, out,
+                                            (hipStream_t)stream),
+                    "wbmm_probe_mfma");
+}

@@ -90,6 +90,10 @@ hipError_t launch_main(K kernel, dim3 grid, dim3 block, unsigned lds, hipStream_
   return hipGetLastError();
 }
 
+// Matrix-core peak probe (measurement aid): flops of one launch, and the launch.
+double probe_mfma_flops(int bf16, int blocks, int iters);
+hipError_t launch_probe_mfma(int bf16, int blocks, int iters, float* out, hipStream_t st);
+
 // k x k depthwise convolution (DW-Std), fp32 NCHW, odd k in 3..13.
 bool dwconv_supported(int B, int C, int H, int W, int k);
 hipError_t launch_dwconv(int B, int C, int H, int W, int k, const float* x, const float* w,

@@ -57,6 +57,7 @@ class Workload:
     mix: bool = False             # 3x3 depthwise inter-block mix after the window mixer
     sigma_mix: float = 0.1
     backward: bool = False        # draw dY and run the backward pass
+    shift: int = 0                # window grid offset (shift, shift) of an interleaved layer
     note: str = ""
 
     @property
@@ -79,6 +80,9 @@ WORKLOADS: Dict[str, Workload] = {
                             note="dense-prediction map padded 128->140, fold + 3x3 mix"),
     "train_w14": Workload("train_w14", B=64, C=192, H=28, W=28, w=14, mix=True, backward=True,
                           note="fp32 training step: forward + backward with 3x3 mix"),
+    "train_w14_shift": Workload("train_w14_shift", B=64, C=192, H=28, W=28, w=14, mix=True,
+                                backward=True, shift=7,
+                                note="fp32 training step of an interleaved layer (grid offset 7)"),
     "train_w14_hier": Workload("train_w14_hier", B=64, C=192, H=28, W=28, w=14, s=7, mix=True,
                                backward=True,
                                note="fp32 training step with the 7x7 sub-window table folded on "

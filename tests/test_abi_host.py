@@ -28,7 +28,7 @@ def lib():
 def header_functions():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    decls = re.findall(r"^\s*(?:wbmm_status|int|size_t|const char\*)\s+(wbmm_\w+)\s*\(([^;]*?)\)\s*;",
+    decls = re.findall(r"^\s*(?:wbmm_status|int|size_t|double|const char\*)\s+(wbmm_\w+)\s*\(([^;]*?)\)\s*;",
                        text, flags=re.M | re.S)
     out = {}
     for name, params in decls:
@@ -216,6 +216,18 @@ def test_shifted_validation(lib):
                                      None, 0x400000, FAKE2, None, None, None, 0,
                                      None) == R.WBMM_E_UNSUPPORTED
     assert lib.wbmm_backward_shifted_workspace_bytes(2, 3, 28, 28, 14, 7, 7, 0, 0) > 0
+
+
+def test_probe_validation(lib):
+    assert lib.wbmm_probe_mfma(7, 4, 10, FAKE, None) == R.WBMM_E_INVALID
+    assert lib.wbmm_probe_mfma(0, 0, 10, FAKE, None) == R.WBMM_E_INVALID
+    assert lib.wbmm_probe_mfma(0, 4, 0, FAKE, None) == R.WBMM_E_INVALID
+    assert lib.wbmm_probe_mfma(0, 4, 10, None, None) == R.WBMM_E_INVALID
+    # flops: blocks x 4 waves x iters x 8 chains x (2*16*16*K), K = 4 (fp32) or 32 (bf16)
+    assert lib.wbmm_probe_mfma_flops(0, 3, 5) == 3 * 4 * 5 * 8 * 2048
+    assert lib.wbmm_probe_mfma_flops(1, 3, 5) == 3 * 4 * 128 * 8 * 16384   # whole rounds of 128
+    assert lib.wbmm_probe_mfma_flops(1, 3, 256) == 3 * 4 * 256 * 8 * 16384
+    assert lib.wbmm_probe_mfma_flops(0, 0, 5) == 0.0
 
 
 def test_dwconv_validation(lib):

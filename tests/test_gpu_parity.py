@@ -775,3 +775,15 @@ def test_shifted_zero_offset_is_the_plain_call():
     a = R().wbmm_backward_shifted(x, dy, w, 0, 0, T=T)
     b = R().wbmm_backward(x, dy, w, T=T)
     assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
+
+
+def test_probe_mfma_runs():
+    """The matrix-core peak probe (a measurement aid) runs for both operand types and writes
+    finite sums."""
+    say("probe mfma")
+    out = torch.zeros(8 * 256, device="cuda")
+    for dt in (torch.float32, torch.bfloat16):
+        flops = R().wbmm_probe_mfma(dt, 8, 256, out=out)
+        torch.cuda.synchronize()
+        o = host(out)
+        assert flops > 0 and np.isfinite(o).all() and np.abs(o).max() > 0
