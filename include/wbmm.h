@@ -264,6 +264,27 @@ wbmm_status wbmm_dwconv_forward(int B, int C, int H, int W, int k, const float* 
                                 const float* w_dw, float* y, void* stream);
 
 /*
+ * wbmm_backward_bf16_workspace_bytes / wbmm_backward_bf16 — the layer backward with bf16 maps
+ * (mixed-precision training): x, dy, z_saved and dx in bf16, T in bf16 (the forward's table),
+ * dT and dmix_w in fp32. Same gradients as wbmm_backward (derived by the chain rule; the pages
+ * train with the operator [arxivdaily abstract]):
+ *   G = mix adjoint of dy (kept as a bf16 map, RNE), or dy itself without a mix;
+ *   dx = M_c^T G per window (bf16 matrix cores, fp32 accumulation, RNE to bf16);
+ *   dT_c[k] = sum over pairs with idx = k of (G X^T)[i][j] (bf16 products, fp32 sums over a
+ *   unit of 64 windows, fp64 across units in a fixed order); dmix_w as in wbmm_backward.
+ * Provided for w = 14 on NCHW maps of 28x28 or 56x56 images (WBMM_E_UNSUPPORTED otherwise).
+ * mix_w / z_saved: both or neither. dx, dT, dmix_w may each be NULL (skipped). bf16 maps and T
+ * must be 16-byte aligned. workspace: at least wbmm_backward_bf16_workspace_bytes(...) bytes,
+ * 256-byte aligned (never NULL: the dT partials live there). Errors as in wbmm_backward.
+ */
+size_t wbmm_backward_bf16_workspace_bytes(int B, int C, int H, int W, int w, int layout,
+                                          int has_mix);
+wbmm_status wbmm_backward_bf16(int B, int C, int H, int W, int w, int layout, const void* x,
+                               const void* T, const float* mix_w, const void* z_saved,
+                               const void* dy, void* dx, float* dT, float* dmix_w,
+                               void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * wbmm_probe_mfma — measurement aid, not part of the method: a matrix-core peak probe. Launches
  * `blocks` workgroups of 4 waves; every wave runs `iters` rounds of 8 independent MFMA
  * accumulation chains on register operands (dtype WBMM_F32: v_mfma_f32_16x16x4f32, WBMM_BF16:
@@ -278,7 +299,8 @@ wbmm_status wbmm_probe_mfma(int dtype, int blocks, int iters, float* out, void* 
 
 /*
  * wbmm_set_launch_events — measurement aid, not part of the method. The next wbmm_forward,
- * wbmm_backward (or their _hier and _shifted forms), wbmm_dwconv_forward or wbmm_probe_mfma call made on the calling thread
+ * wbmm_backward (or their _hier, _shifted and _bf16 forms), wbmm_dwconv_forward or wbmm_probe_mfma
+ * call made on the calling thread
  * attaches `before` and `after` (hipEvent_t
  * handles passed as void*) to the dispatch of its main contraction kernel (hipExtLaunchKernel's
  * start and stop events), so their elapsed time is that kernel's execution; the pair is then

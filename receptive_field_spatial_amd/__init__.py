@@ -20,7 +20,8 @@ __all__ = [
     "wbmm_forward_hier", "wbmm_forward_hier_workspace_bytes",
     "wbmm_backward_hier", "wbmm_backward_hier_workspace_bytes", "wbmm_dwconv_forward",
     "wbmm_forward_shifted", "wbmm_forward_shifted_workspace_bytes", "wbmm_backward_shifted",
-    "wbmm_backward_shifted_workspace_bytes", "wbmm_probe_mfma",
+    "wbmm_backward_shifted_workspace_bytes", "wbmm_probe_mfma", "wbmm_backward_bf16",
+    "wbmm_backward_bf16_workspace_bytes",
     "WBMM_OK", "WBMM_E_INVALID", "WBMM_E_UNSUPPORTED", "WBMM_E_WORKSPACE", "WBMM_E_HIP",
 ]
 
@@ -62,6 +63,8 @@ def _declare(lib):
         "wbmm_backward_hier": (c_int, [c_int] * 7 + [vp] * 11 + [c_size, vp]),
         "wbmm_dwconv_forward": (c_int, [c_int] * 5 + [vp] * 4),
         "wbmm_probe_mfma_flops": (ctypes.c_double, [c_int] * 3),
+        "wbmm_backward_bf16_workspace_bytes": (c_size, [c_int] * 7),
+        "wbmm_backward_bf16": (c_int, [c_int] * 6 + [vp] * 9 + [c_size, vp]),
         "wbmm_probe_mfma": (c_int, [c_int] * 3 + [vp, vp]),
         "wbmm_forward_shifted_workspace_bytes": (c_size, [c_int] * 10),
         "wbmm_forward_shifted": (c_int, [c_int] * 10 + [vp] * 7 + [c_size, vp]),
@@ -385,3 +388,32 @@ def wbmm_probe_mfma(dtype, blocks: int, iters: int, *, out=None, stream=None) ->
     code = _dtype_code(dtype)
     _check(_lib().wbmm_probe_mfma(code, int(blocks), int(iters), _ptr(out), _stream(stream)))
     return float(_lib().wbmm_probe_mfma_flops(code, int(blocks), int(iters)))
+
+
+def wbmm_backward_bf16_workspace_bytes(B, C, H, W, w, layout="NCHW", has_mix=False) -> int:
+    return int(_lib().wbmm_backward_bf16_workspace_bytes(B, C, H, W, int(w), _layout_code(layout),
+                                                         int(bool(has_mix))))
+
+
+def wbmm_backward_bf16(x, dy, w: int, T, mix_w=None, z_saved=None, *, dx=True, dT=True,
+                       dmix_w=True, workspace=None, stream=None):
+    """Layer backward with bf16 maps (x, dy, z_saved bf16; T bf16). Returns (dx bf16, dT fp32,
+    dmix_w fp32); an output passed as False is skipped."""
+    torch = _torch()
+    B, C, H, W = _bchw(x, "NCHW")
+    L = 2 * w - 1
+    dev = x.device
+    dx_t = torch.empty_like(x) if dx is True else (dx if dx is not False else None)
+    dT_t = torch.empty((C, L, L), dtype=torch.float32, device=dev) if dT is True else (dT if dT is not False else None)
+    if mix_w is None:
+        dW_t = None
+    else:
+        dW_t = torch.empty((C, 3, 3), dtype=torch.float32, device=dev) if dmix_w is True else (dmix_w if dmix_w is not False else None)
+    need = wbmm_backward_bf16_workspace_bytes(B, C, H, W, w, "NCHW", mix_w is not None)
+    if workspace is None or workspace.numel() * workspace.element_size() < need:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    ws_bytes = workspace.numel() * workspace.element_size()
+    _check(_lib().wbmm_backward_bf16(B, C, H, W, int(w), WBMM_NCHW, _ptr(x), _ptr(T), _ptr(mix_w),
+                                     _ptr(z_saved), _ptr(dy), _ptr(dx_t), _ptr(dT_t), _ptr(dW_t),
+                                     _ptr(workspace), ws_bytes, _stream(stream)))
+    return dx_t, dT_t, dW_t

@@ -489,3 +489,51 @@ WBMM_API wbmm_status wbmm_probe_mfma(int dtype, int blocks, int iters, float* ou
                                             (hipStream_t)stream),
                     "wbmm_probe_mfma");
 }
+
+WBMM_API size_t wbmm_backward_bf16_workspace_bytes(int B, int C, int H, int W, int w, int layout,
+                                                   int has_mix) {
+  if (!wbmm::bf16_backward_ok(B, C, H, W, w, layout)) return 0;
+  return wbmm::bf16_backward_workspace(B, C, H, W, w, has_mix);
+}
+
+WBMM_API wbmm_status wbmm_backward_bf16(int B, int C, int H, int W, int w, int layout,
+                                        const void* x, const void* T, const float* mix_w,
+                                        const void* z_saved, const void* dy, void* dx, float* dT,
+                                        float* dmix_w, void* workspace, size_t workspace_bytes,
+                                        void* stream) {
+  wbmm_status st = check_map(B, C, H, W, w, layout);
+  if (st != WBMM_OK) return st;
+  if (!wbmm::bf16_backward_ok(B, C, H, W, w, layout))
+    return fail(WBMM_E_UNSUPPORTED,
+                "the bf16 backward is provided for w = 14 on NCHW 28x28 and 56x56 images "
+                "(w=%d, %dx%d)", w, H, W);
+  if (!x || !T || !dy) return fail(WBMM_E_INVALID, "x, T and dy must be non-NULL");
+  if ((mix_w == nullptr) != (z_saved == nullptr))
+    return fail(WBMM_E_INVALID, "z_saved is required exactly when mix_w is given");
+  const void* ptrs[] = {x, T, z_saved, dy, dx};
+  for (const void* p : ptrs)
+    if (p && !aligned(p, 16)) return fail(WBMM_E_UNSUPPORTED, "bf16 maps and T must be 16-byte aligned");
+  const void* fptrs[] = {mix_w, dT, dmix_w};
+  for (const void* p : fptrs)
+    if (p && !aligned(p, 4)) return fail(WBMM_E_UNSUPPORTED, "pointer not 4-byte aligned");
+  const size_t mb = (size_t)B * C * H * W * 2;
+  const size_t tb = (size_t)C * (2 * w - 1) * (2 * w - 1);
+  if (dx && (overlaps(dx, mb, x, mb) || overlaps(dx, mb, dy, mb) || overlaps(dx, mb, z_saved, mb) ||
+             overlaps(dx, mb, T, tb * 2)))
+    return fail(WBMM_E_INVALID, "dx overlaps an input");
+  if (dT && (overlaps(dT, tb * 4, T, tb * 2) || overlaps(dT, tb * 4, dx, mb)))
+    return fail(WBMM_E_INVALID, "dT overlaps T or dx");
+  if (dmix_w && mix_w && overlaps(dmix_w, (size_t)C * 36, mix_w, (size_t)C * 36))
+    return fail(WBMM_E_INVALID, "dmix_w overlaps mix_w");
+  const size_t need = wbmm::bf16_backward_workspace(B, C, H, W, w, mix_w != nullptr);
+  if (!workspace || workspace_bytes < need)
+    return fail(WBMM_E_WORKSPACE, "workspace of %zu bytes required, %zu given", need,
+                workspace ? workspace_bytes : (size_t)0);
+  if (!aligned(workspace, 256)) return fail(WBMM_E_UNSUPPORTED, "workspace not 256-byte aligned");
+  wbmm::BwdBf16Request r{};
+  r.B = B; r.C = C; r.H = H; r.W = W; r.w = w;
+  r.x = (const uint16_t*)x; r.T = (const uint16_t*)T; r.mixw = mix_w;
+  r.zsaved = (const uint16_t*)z_saved; r.dy = (const uint16_t*)dy; r.dx = (uint16_t*)dx;
+  r.dT = dT; r.dmixw = mix_w ? dmix_w : nullptr; r.ws = workspace;
+  return hip_status(wbmm::launch_backward_bf16(r, (hipStream_t)stream), "wbmm_backward_bf16");
+}

@@ -160,10 +160,12 @@ __global__ void __launch_bounds__(kThreads) k_mix_fwd(const float* __restrict__ 
   }
 }
 
-// dz[b,c,p,q] = sum_{u,t} w9[c][u][t] * dy[b,c,p-u+1,q-t+1]  (adjoint of k_mix_fwd)
-__global__ void __launch_bounds__(kThreads) k_mix_bwd_data(const float* __restrict__ dy,
+// dz[b,c,p,q] = sum_{u,t} w9[c][u][t] * dy[b,c,p-u+1,q-t+1]  (adjoint of k_mix_fwd); bf16
+// maps (TM = uint16_t) are read and written as bf16 (RNE), the sums run in fp32.
+template <typename TM>
+__global__ void __launch_bounds__(kThreads) k_mix_bwd_data(const TM* __restrict__ dy,
                                                            const float* __restrict__ w9,
-                                                           float* __restrict__ dz, int B, int C,
+                                                           TM* __restrict__ dz, int B, int C,
                                                            int H, int W, int layout) {
   const size_t total = (size_t)B * C * H * W;
   for (size_t e = (size_t)blockIdx.x * kThreads + threadIdx.x; e < total;
@@ -178,18 +180,20 @@ __global__ void __launch_bounds__(kThreads) k_mix_bwd_data(const float* __restri
       for (int t = 0; t < 3; ++t) {
         const int vv = v - t + 1;
         const float g = (hh >= 0 && hh < H && vv >= 0 && vv < W)
-                            ? dy[map_off(layout, b, c, hh, vv, C, H, W)] : 0.f;
+                            ? load_f32<TM>(dy, map_off(layout, b, c, hh, vv, C, H, W)) : 0.f;
         acc = fmaf(w9[c * 9 + u * 3 + t], g, acc);
       }
     }
-    dz[e] = acc;
+    if constexpr (sizeof(TM) == 2) dz[e] = f2bf(acc);
+    else dz[e] = acc;
   }
 }
 
 // dw9[c][u][t] = sum_{b,h,v} dy[b,c,h,v] * z[b,c,h+u-1,v+t-1]; one workgroup per channel,
 // fp64 partial sums per thread, then a fixed-order tree: bitwise reproducible.
-__global__ void __launch_bounds__(kThreads) k_mix_bwd_weight(const float* __restrict__ dy,
-                                                             const float* __restrict__ z,
+template <typename TM>
+__global__ void __launch_bounds__(kThreads) k_mix_bwd_weight(const TM* __restrict__ dy,
+                                                             const TM* __restrict__ z,
                                                              float* __restrict__ dw9, int B,
                                                              int C, int H, int W, int layout) {
   __shared__ double red[9][kThreads];
@@ -202,7 +206,7 @@ __global__ void __launch_bounds__(kThreads) k_mix_bwd_weight(const float* __rest
     const int v = (int)(e % W);
     const int h = (int)((e / W) % H);
     const int b = (int)(e / ((size_t)W * H));
-    const double g = dy[map_off(layout, b, c, h, v, C, H, W)];
+    const double g = load_f32<TM>(dy, map_off(layout, b, c, h, v, C, H, W));
 #pragma unroll
     for (int u = 0; u < 3; ++u) {
       const int hh = h + u - 1;
@@ -210,7 +214,7 @@ __global__ void __launch_bounds__(kThreads) k_mix_bwd_weight(const float* __rest
       for (int t = 0; t < 3; ++t) {
         const int vv = v + t - 1;
         if (hh >= 0 && hh < H && vv >= 0 && vv < W)
-          acc[u * 3 + t] += g * (double)z[map_off(layout, b, c, hh, vv, C, H, W)];
+          acc[u * 3 + t] += g * (double)load_f32<TM>(z, map_off(layout, b, c, hh, vv, C, H, W));
       }
     }
   }
@@ -267,15 +271,30 @@ hipError_t launch_mix_fwd(const float* z, const float* w9, void* y, int out_bf16
 hipError_t launch_mix_bwd_data(const float* dy, const float* w9, float* dz, int B, int C, int H,
                                int W, int layout, hipStream_t st) {
   const size_t n = (size_t)B * C * H * W;
-  hipLaunchKernelGGL(k_mix_bwd_data, dim3(grid_for(n)), dim3(kThreads), 0, st, dy, w9, dz, B, C,
-                     H, W, layout);
+  hipLaunchKernelGGL(k_mix_bwd_data<float>, dim3(grid_for(n)), dim3(kThreads), 0, st, dy, w9, dz,
+                     B, C, H, W, layout);
   return hipGetLastError();
 }
 
 hipError_t launch_mix_bwd_weight(const float* dy, const float* z, float* dw9, int B, int C, int H,
                                  int W, int layout, hipStream_t st) {
-  hipLaunchKernelGGL(k_mix_bwd_weight, dim3(C), dim3(kThreads), 0, st, dy, z, dw9, B, C, H, W,
-                     layout);
+  hipLaunchKernelGGL(k_mix_bwd_weight<float>, dim3(C), dim3(kThreads), 0, st, dy, z, dw9, B, C, H,
+                     W, layout);
+  return hipGetLastError();
+}
+
+hipError_t launch_mix_bwd_data_bf16(const uint16_t* dy, const float* w9, uint16_t* dz, int B,
+                                    int C, int H, int W, hipStream_t st) {
+  const size_t n = (size_t)B * C * H * W;
+  hipLaunchKernelGGL(k_mix_bwd_data<uint16_t>, dim3(grid_for(n)), dim3(kThreads), 0, st, dy, w9,
+                     dz, B, C, H, W, 0);
+  return hipGetLastError();
+}
+
+hipError_t launch_mix_bwd_weight_bf16(const uint16_t* dy, const uint16_t* z, float* dw9, int B,
+                                      int C, int H, int W, hipStream_t st) {
+  hipLaunchKernelGGL(k_mix_bwd_weight<uint16_t>, dim3(C), dim3(kThreads), 0, st, dy, z, dw9, B, C,
+                     H, W, 0);
   return hipGetLastError();
 }
 

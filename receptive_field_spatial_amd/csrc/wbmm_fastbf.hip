@@ -104,8 +104,10 @@ __device__ __forceinline__ int opaque(int v) {
 // past every read; threads past CS - 8 repeat entry CS - 8 (same value to the same places), so
 // every write is unconditional. All threads of the workgroup take part. Split in two so that a
 // caller can put other loads in flight between them: the memory counter completes in order, so
-// waiting for the table entries never waits for loads issued after them.
-template <class S, int NTH>
+// waiting for the table entries never waits for loads issued after them. ROT stages the table
+// rotated by 180 degrees (entry L-1-q for q), whose matrix is M^T: the contraction then computes
+// the backward's dX = M^T G.
+template <class S, int NTH, bool ROT = false>
 struct TableStage {
   static constexpr int NQ = (S::CS + NTH - 1) / NTH;
   uint16_t tv[NQ];
@@ -123,7 +125,7 @@ struct TableStage {
       const int p = S::PT - 1 - q;  // padded table index
       const bool in = p >= 0 && (p % S::TP) < S::L1;
       const int ti = in ? (p / S::TP) * S::L1 + (p % S::TP) : 0;
-      tv[j] = Tc[ti];
+      tv[j] = Tc[ROT ? S::L1 * S::L1 - 1 - ti : ti];
       pad |= in ? 0u : 1u << j;
     }
   }
@@ -140,9 +142,9 @@ struct TableStage {
     __syncthreads();
   }
 };
-template <class S, int NTH = kThreads>
+template <class S, int NTH = kThreads, bool ROT = false>
 __device__ __forceinline__ void stage_table(uint16_t* copies, const uint16_t* T, int c) {
-  TableStage<S, NTH> ts;
+  TableStage<S, NTH, ROT> ts;
   ts.load(T, c);
   ts.write(copies);
 }
@@ -153,7 +155,7 @@ __device__ __forceinline__ void stage_table(uint16_t* copies, const uint16_t* T,
 // contracts and stores the current one.
 constexpr int kWgPerCu = 4;  // resident workgroups per CU (kWgPerCu waves per SIMD)
 
-template <class S, bool ZS>
+template <class S, bool ZS, bool ROT = false>
 __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWgPerCu, 8)))
 k_fwd_bf16(BfArgs a) {
   extern __shared__ __attribute__((aligned(16))) uint16_t smem_h[];
@@ -212,7 +214,7 @@ k_fwd_bf16(BfArgs a) {
   auto unit = [&](auto more, const UnitPos& pos, int u_next, u32x4 (&into)[7],
                   const u32x4 (&conv)[7]) {
     if (pos.c != table_c) {  // uniform over the workgroup
-      stage_table<S>(copies, a.T, pos.c);
+      stage_table<S, kThreads, ROT>(copies, a.T, pos.c);
       table_c = pos.c;
     }
     constexpr bool MORE = decltype(more)::value;
@@ -707,6 +709,21 @@ bool fast_bf16_forward_ok(const FwdRequest& r) {
   return r.in_bf16 && r.out_bf16 && r.T && !r.M && !r.mixw && !r.Tsub && r.oy == 0 &&
          r.ox == 0 && r.B > 0 && r.C > 0 &&
          (long long)r.C * ((r.B + 3) / 4 + 1) < ((long long)1 << 31) && bf_shape(r) != BF_NONE;
+}
+
+// dX = M_c^T G_c of the bf16 backward (w = 14, NCHW 28x28 or 56x56 images): the forward
+// contraction on G with the table staged rotated, written as bf16.
+hipError_t launch_bf16_transposed_contraction(const uint16_t* g, const uint16_t* T, uint16_t* out,
+                                              int B, int C, int H, hipStream_t st) {
+  FwdRequest r{};
+  r.B = B; r.C = C; r.H = H; r.W = H; r.w = 14; r.layout = 0;
+  r.in_bf16 = 1; r.out_bf16 = 1;
+  r.x = g; r.T = T; r.y = out;
+  switch (bf_shape(r)) {
+    case BF_28: return launch_bf<BfShape<28>>(r, st, k_fwd_bf16<BfShape<28>, false, true>, k_fwd_bf16<BfShape<28>, false, true>);
+    case BF_56: return launch_bf<BfShape<56>>(r, st, k_fwd_bf16<BfShape<56>, false, true>, k_fwd_bf16<BfShape<56>, false, true>);
+    default: return hipErrorInvalidValue;
+  }
 }
 
 hipError_t launch_forward_fast_bf16(const FwdRequest& r, hipStream_t st) {

@@ -90,6 +90,30 @@ hipError_t launch_main(K kernel, dim3 grid, dim3 block, unsigned lds, hipStream_
   return hipGetLastError();
 }
 
+// bf16 backward (w = 14, NCHW 28x28 / 56x56 images, table input): maps and table in bf16,
+// dT and dWmix in fp32.
+struct BwdBf16Request {
+  int B, C, H, W, w;
+  const uint16_t* x;
+  const uint16_t* T;
+  const float* mixw;
+  const uint16_t* zsaved;
+  const uint16_t* dy;
+  uint16_t* dx;
+  float* dT;
+  float* dmixw;
+  void* ws;
+};
+bool bf16_backward_ok(int B, int C, int H, int W, int w, int layout);
+size_t bf16_backward_workspace(int B, int C, int H, int W, int w, int has_mix);
+hipError_t launch_backward_bf16(const BwdBf16Request& r, hipStream_t st);
+hipError_t launch_bf16_transposed_contraction(const uint16_t* g, const uint16_t* T, uint16_t* out,
+                                              int B, int C, int H, hipStream_t st);
+hipError_t launch_mix_bwd_data_bf16(const uint16_t* dy, const float* w9, uint16_t* dz, int B,
+                                    int C, int H, int W, hipStream_t st);
+hipError_t launch_mix_bwd_weight_bf16(const uint16_t* dy, const uint16_t* z, float* dw9, int B,
+                                      int C, int H, int W, hipStream_t st);
+
 // Matrix-core peak probe (measurement aid): flops of one launch, and the launch.
 double probe_mfma_flops(int bf16, int blocks, int iters);
 hipError_t launch_probe_mfma(int bf16, int blocks, int iters, float* out, hipStream_t st);

@@ -42,7 +42,8 @@ def test_header_declares_the_entry_points():
     for name in ["wbmm_build_index", "wbmm_build_matrix", "wbmm_fold_hier", "wbmm_forward",
                  "wbmm_backward", "wbmm_forward_workspace_bytes", "wbmm_backward_workspace_bytes",
                  "wbmm_last_error", "wbmm_abi_version", "wbmm_forward_hier", "wbmm_backward_hier",
-                 "wbmm_dwconv_forward", "wbmm_forward_shifted", "wbmm_backward_shifted"]:
+                 "wbmm_dwconv_forward", "wbmm_forward_shifted", "wbmm_backward_shifted",
+                 "wbmm_backward_bf16", "wbmm_probe_mfma"]:
         assert name in fns, name
 
 
@@ -216,6 +217,25 @@ def test_shifted_validation(lib):
                                      None, 0x400000, FAKE2, None, None, None, 0,
                                      None) == R.WBMM_E_UNSUPPORTED
     assert lib.wbmm_backward_shifted_workspace_bytes(2, 3, 28, 28, 14, 7, 7, 0, 0) > 0
+
+
+def test_backward_bf16_validation(lib):
+    """bf16 backward: w = 14 on NCHW 28² / 56² only, mix and z_saved together, workspace needed."""
+    def call(B=2, C=3, H=28, W=28, w=14, layout=0, mix=None, z=None, dx=0x500000, ws=0x900000,
+             wsb=1 << 30):
+        return lib.wbmm_backward_bf16(B, C, H, W, w, layout, FAKE, 0x300000, mix, z, FAKE2, dx,
+                                      0x600000, None, ws, wsb, None)
+    assert call(H=30, W=30) == R.WBMM_E_UNSUPPORTED
+    assert call(w=7) == R.WBMM_E_UNSUPPORTED
+    assert call(layout=1) == R.WBMM_E_UNSUPPORTED
+    assert "bf16 backward" in err(lib)
+    assert call(mix=0x700000) == R.WBMM_E_INVALID            # mix without z_saved
+    assert call(dx=FAKE) == R.WBMM_E_INVALID                  # dx aliases x
+    assert call(ws=None) == R.WBMM_E_WORKSPACE
+    need = lib.wbmm_backward_bf16_workspace_bytes(2, 3, 28, 28, 14, 0, 1)
+    assert need > lib.wbmm_backward_bf16_workspace_bytes(2, 3, 28, 28, 14, 0, 0) > 0
+    assert call(mix=0x700000, z=0x800000, wsb=need - 1) == R.WBMM_E_WORKSPACE
+    assert lib.wbmm_backward_bf16_workspace_bytes(2, 3, 30, 30, 14, 0, 0) == 0
 
 
 def test_probe_validation(lib):

@@ -787,3 +787,52 @@ def test_probe_mfma_runs():
         torch.cuda.synchronize()
         o = host(out)
         assert flops > 0 and np.isfinite(o).all() and np.abs(o).max() > 0
+
+
+# ----------------------------------------------------------------------------- bf16 backward
+@pytest.mark.parametrize("B,C,H", [(5, 3, 28), (18, 2, 28), (3, 2, 56), (6, 3, 56)])
+@pytest.mark.parametrize("mix", [False, True])
+def test_backward_bf16(B, C, H, mix):
+    """bf16 maps and table (mixed-precision training) against the oracle on the same bf16 values:
+    dx (bf16) and, with a mix, dT within the bf16 bar (G is kept as a bf16 map); without a mix G
+    is dy itself, every product is exact and dT meets the fp32 bar; dWmix (fp64 sums of bf16
+    values) meets the fp32 bar. Ragged batches leave units part empty; run twice, bitwise."""
+    w = 14
+    say(f"backward bf16 B={B} C={C} H=W={H} mix={mix}")
+    x = synth.round_to_bf16(synth.normal_f32((B, C, H, H), 1.0, seed=270))
+    T = synth.round_to_bf16(synth.normal_f32((C, 27, 27), 0.02, seed=271))
+    dy = synth.round_to_bf16(synth.normal_f32((B, C, H, H), 1.0, seed=272))
+    Wm = synth.normal_f32((C, 3, 3), 0.1, seed=273) if mix else None
+    z = (synth.round_to_bf16(O.wbmm_forward(x.astype(np.float64), w, T=T).astype(np.float32))
+         if mix else None)
+    xd, Td, dyd = dev_bf16(x), dev_bf16(T), dev_bf16(dy)
+    zd = dev_bf16(z) if mix else None
+    Wd = dev(Wm) if mix else None
+    dx, dT, dW = R().wbmm_backward_bf16(xd, dyd, w, Td, mix_w=Wd, z_saved=zd)
+    wdx, wdT, wdW = O.layer_backward(x.astype(np.float64), dy.astype(np.float64), w, T=T, Wmix=Wm,
+                                     z=z.astype(np.float64) if mix else None)
+    assert_bf16(host(dx.float()), wdx, "dx")
+    if mix:
+        assert_bf16(host(dT), wdT, "dT")
+        assert_f32(host(dW), wdW, "dWmix")
+    else:
+        assert_f32(host(dT), wdT, "dT")
+    dx2, dT2, _ = R().wbmm_backward_bf16(xd, dyd, w, Td, mix_w=Wd, z_saved=zd)
+    assert torch.equal(dx, dx2) and torch.equal(dT, dT2)
+
+
+def test_backward_bf16_partial_outputs():
+    """Only dT, or only dx: the skipped outputs are not written and the others match."""
+    B, C, H, w = 4, 2, 28, 14
+    say("backward bf16 partial outputs")
+    x = synth.round_to_bf16(synth.normal_f32((B, C, H, H), 1.0, seed=280))
+    T = synth.round_to_bf16(synth.normal_f32((C, 27, 27), 0.02, seed=281))
+    dy = synth.round_to_bf16(synth.normal_f32((B, C, H, H), 1.0, seed=282))
+    xd, Td, dyd = dev_bf16(x), dev_bf16(T), dev_bf16(dy)
+    dx0, dT, _ = R().wbmm_backward_bf16(xd, dyd, w, Td, dx=False)
+    assert dx0 is None
+    dx, dT0, _ = R().wbmm_backward_bf16(xd, dyd, w, Td, dT=False)
+    assert dT0 is None
+    wdx, wdT, _ = O.layer_backward(x.astype(np.float64), dy.astype(np.float64), w, T=T)
+    assert_f32(host(dT), wdT, "dT")
+    assert_bf16(host(dx.float()), wdx, "dx")
