@@ -114,7 +114,8 @@ def accounting(wl):
     if wl.backward:
         acc["bwd_flops"] = E * (4 * d + (36 if wl.mix else 0))
         # reads x, dy, z (mix), table; writes dx, dT, dWmix
-        acc["bwd_bytes"] = E * 4 * (3 + (1 if wl.mix else 0)) + 2 * tab + (wl.C * 72 if wl.mix else 0)
+        acc["bwd_bytes"] = E * esz * (3 + (1 if wl.mix else 0)) + tab + wl.C * L * 4 + \
+            (wl.C * 72 if wl.mix else 0)
     acc["step_flops"] = fwd_flops + acc.get("bwd_flops", 0)
     return acc
 
@@ -198,6 +199,10 @@ class HipEvents:
             raise RuntimeError("hipEventCreate failed")
         return ev.value
 
+    def record(self, ev, stream):
+        if self.hip.hipEventRecord(self.ct.c_void_p(ev), self.ct.c_void_p(stream.cuda_stream)) != 0:
+            raise RuntimeError("hipEventRecord failed")
+
     def elapsed_ms(self, a, b):
         ms = self.ct.c_float()
         if self.hip.hipEventElapsedTime(self.ct.byref(ms), self.ct.c_void_p(a), self.ct.c_void_p(b)) != 0:
@@ -276,7 +281,8 @@ def run(args):
         s["y"] = torch.empty_like(s["x"])
         if wl.backward:
             s["dy"] = to_dev(inp["dY"])
-            s["z"] = torch.empty_like(s["x"])
+            if wl.mix:
+                s["z"] = torch.empty_like(s["x"])
             s["dx"] = torch.empty_like(s["x"])
         sets.append(s)
     T = to_dev(inp["T"])
@@ -292,8 +298,11 @@ def run(args):
     dTs = (torch.empty((wl.C, 2 * wl.s - 1, 2 * wl.s - 1), dtype=torch.float32, device=dev)
            if hier_train else None)
     ws_b = None
+    bf16_bwd = bf16 and wl.backward
     if wl.backward:
-        if wl.shift:
+        if bf16_bwd:
+            nb = R.wbmm_backward_bf16_workspace_bytes(wl.B, wl.C, wl.H, wl.W, wl.w, has_mix=wl.mix)
+        elif wl.shift:
             nb = R.wbmm_backward_shifted_workspace_bytes(wl.B, wl.C, wl.H, wl.W, wl.w, wl.shift,
                                                          wl.shift, has_mix=wl.mix)
         elif hier_train:
@@ -305,13 +314,13 @@ def run(args):
     if wl.shift:
         nf = R.wbmm_forward_shifted_workspace_bytes(wl.B, wl.C, wl.H, wl.W, wl.w, wl.shift,
                                                     wl.shift, has_mix=wl.mix,
-                                                    has_z_save=wl.backward)
+                                                    has_z_save=wl.backward and wl.mix)
     elif hier_train:
         nf = R.wbmm_forward_hier_workspace_bytes(wl.B, wl.C, wl.H, wl.W, wl.w, wl.s,
                                                  has_mix=wl.mix, has_z_save=True)
     else:
         nf = R.wbmm_forward_workspace_bytes(wl.B, wl.C, wl.H, wl.W, wl.w, has_mix=wl.mix,
-                                            has_z_save=wl.backward)
+                                            has_z_save=wl.backward and wl.mix)
     ws_f = torch.empty(max(nf, 1), dtype=torch.uint8, device=dev) if nf else None
     stream = torch.cuda.current_stream()
     kw_tab = {"M": M} if M is not None else {"T": T}
@@ -329,6 +338,11 @@ def run(args):
                        stream=stream, **kw_tab)
 
     def bwd(s):
+        if bf16_bwd:
+            R.wbmm_backward_bf16(s["x"], s["dy"], wl.w, T, mix_w=Wm,
+                                 z_saved=s["z"] if wl.mix else None, dx=s["dx"], dT=dT,
+                                 dmix_w=dW if wl.mix else False, workspace=ws_b, stream=stream)
+            return
         if wl.shift:
             R.wbmm_backward_shifted(s["x"], s["dy"], wl.w, wl.shift, wl.shift, mix_w=Wm,
                                     z_saved=s["z"] if wl.mix else None, dx=s["dx"], dT=dT,
@@ -365,8 +379,13 @@ def run(args):
         R.wbmm_set_launch_events(kev[i][0], kev[i][1])
         fwd(s)
         if wl.backward:
-            R.wbmm_set_launch_events(kev[i][2], kev[i][3])
-            bwd(s)
+            if bf16_bwd:  # several kernels (dX contraction, row-pair dT, reduction): time them all
+                hev.record(kev[i][2], stream)
+                bwd(s)
+                hev.record(kev[i][3], stream)
+            else:
+                R.wbmm_set_launch_events(kev[i][2], kev[i][3])
+                bwd(s)
     stop.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0

@@ -80,6 +80,9 @@ WORKLOADS: Dict[str, Workload] = {
                             note="dense-prediction map padded 128->140, fold + 3x3 mix"),
     "train_w14": Workload("train_w14", B=64, C=192, H=28, W=28, w=14, mix=True, backward=True,
                           note="fp32 training step: forward + backward with 3x3 mix"),
+    "train_w14_bf16": Workload("train_w14_bf16", B=64, C=192, H=28, W=28, w=14, dtype="bf16",
+                               backward=True,
+                               note="bf16 (mixed-precision) training step of the operator"),
     "train_w14_shift": Workload("train_w14_shift", B=64, C=192, H=28, W=28, w=14, mix=True,
                                 backward=True, shift=7,
                                 note="fp32 training step of an interleaved layer (grid offset 7)"),
@@ -118,6 +121,8 @@ def draw_inputs(wl: Workload, seed: int = 0, *, B: Optional[int] = None,
     if wl.dtype == "bf16":
         out["x"] = round_to_bf16(out["x"])
         out["T"] = round_to_bf16(out["T"])
+        if wl.backward:
+            out["dY"] = round_to_bf16(out["dY"])
     return out
 
 
