@@ -9,7 +9,8 @@
 //        whose diagonals x1 - x2 = dx are dT[dy][dx].
 // The row-pair kernel stages a unit's 64 windows of G and X transposed in LDS (pixel-major,
 // window-minor), so an MFMA operand (8 consecutive windows of one pixel) is one 16-byte read;
-// each unit leaves one fp64 partial, summed in a fixed order by k_bwd_reduce.
+// eight waves share a unit's tiles (27 row offsets over 8 waves); each unit leaves one fp64
+// partial, summed in a fixed order by k_bwd_reduce.
 #include "wbmm_device.hpp"
 #include "wbmm_launch.hpp"
 
@@ -25,7 +26,7 @@ struct DtShape {
   static constexpr int IPU = 4 * IPW;       // images per unit of 64 windows
   static constexpr int PLANE = IH * IW;
   static constexpr int NP = 72;             // bf16 per pixel row of a transposed tile (64 + 8)
-  static constexpr int PAIRS = 64 * WS * (WS / 2);  // pixel pairs of a unit
+  static constexpr int ITEMS = 32 * WS * (WS / 2);  // (window pair, row, pixel pair) of a unit
   static_assert(IW == 28 || IW == 56, "shape");
   static_assert(NP * 2 % 16 == 0, "16-byte operand reads");
 };
@@ -33,11 +34,15 @@ struct DtShape {
 template <class S>
 constexpr int dt_lds_bytes() { return 2 * S::D * S::NP * 2; }
 
+constexpr int kDtWaves = 8;                 // waves per unit
+constexpr int kDtThreads = 64 * kDtWaves;
+constexpr int kDtSlots = 4;                 // row offsets per wave (27 over 8 waves)
+
 // Row-offset slots of wave Q: offsets ordered 0, +1, -1, +2, -2, ... dealt in a snake so the
-// four waves get near-equal MFMA counts (WS - |dy| row pairs per offset).
+// eight waves get near-equal MFMA counts (WS - |dy| row pairs per offset).
 template <int WS, int Q, int J>
 struct DtSlot {
-  static constexpr int T = 4 * J + ((J & 1) ? 3 - Q : Q);
+  static constexpr int T = kDtWaves * J + ((J & 1) ? kDtWaves - 1 - Q : Q);
   static constexpr bool valid = T < 2 * WS - 1;
   static constexpr int dy = T == 0 ? 0 : ((T & 1) ? (T + 1) / 2 : -(T / 2));
 };
@@ -56,9 +61,9 @@ __device__ __forceinline__ void dt_wave(const uint16_t* Gt, const uint16_t* Xt, 
   constexpr int WS = S::WS, DD = WS * WS;
   const int m = lane & 15, grp = lane >> 4;
   const int mc = m < WS ? m : WS - 1;  // MFMA rows/columns 14, 15 are never read
-  v4f acc[8];
+  v4f acc[kDtSlots];
 #pragma unroll
-  for (int j = 0; j < 8; ++j) acc[j] = v4f{0.f, 0.f, 0.f, 0.f};
+  for (int j = 0; j < kDtSlots; ++j) acc[j] = v4f{0.f, 0.f, 0.f, 0.f};
   // A[x1][n] = G_n[y1][x1] (row x1 = m), B[n][x2] = X_n[y2][x2] (column x2 = m): lane group grp
   // feeds windows k0 + 8 grp .. + 7 of K step k0
   const uint16_t* ga = Gt + mc * S::NP + 8 * grp;
@@ -76,13 +81,12 @@ __device__ __forceinline__ void dt_wave(const uint16_t* Gt, const uint16_t* Xt, 
     }                                                                               \
   }
   WBMM_DTB_SLOT(0) WBMM_DTB_SLOT(1) WBMM_DTB_SLOT(2) WBMM_DTB_SLOT(3)
-  WBMM_DTB_SLOT(4) WBMM_DTB_SLOT(5) WBMM_DTB_SLOT(6) WBMM_DTB_SLOT(7)
 #undef WBMM_DTB_SLOT
   __syncthreads();  // every wave is done with the tiles: the scratch reuses them
   // acc[J][r] is element (x1 = 4 grp + r, x2 = m) of slot J's tile; elements outside the WS x WS
   // tile go to a per-lane dump slot, so no store is conditional
-  const int dump = 7 * DD + lane;
-  static_assert(!DtSlot<WS, Q, 7>::valid, "at most 7 slots per wave: 7 tiles + dump in scratch");
+  const int dump = kDtSlots * DD + lane;
+  static_assert(!DtSlot<WS, Q, kDtSlots>::valid, "every row offset has a slot");
 #define WBMM_DTB_PUT(J)                                                            \
   if constexpr (DtSlot<WS, Q, J>::valid) {                                         \
     _Pragma("unroll") for (int r = 0; r < 4; ++r) {                                \
@@ -91,7 +95,6 @@ __device__ __forceinline__ void dt_wave(const uint16_t* Gt, const uint16_t* Xt, 
     }                                                                              \
   }
   WBMM_DTB_PUT(0) WBMM_DTB_PUT(1) WBMM_DTB_PUT(2) WBMM_DTB_PUT(3)
-  WBMM_DTB_PUT(4) WBMM_DTB_PUT(5) WBMM_DTB_PUT(6)
 #undef WBMM_DTB_PUT
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
   __builtin_amdgcn_wave_barrier();
@@ -113,13 +116,12 @@ __device__ __forceinline__ void dt_wave(const uint16_t* Gt, const uint16_t* Xt, 
     if (lane < S::L1) pT[(DtSlot<WS, Q, J>::dy + WS - 1) * S::L1 + lane] = s + o; \
   }
   WBMM_DTB_SUM(0) WBMM_DTB_SUM(1) WBMM_DTB_SUM(2) WBMM_DTB_SUM(3)
-  WBMM_DTB_SUM(4) WBMM_DTB_SUM(5) WBMM_DTB_SUM(6) WBMM_DTB_SUM(7)
 #undef WBMM_DTB_SUM
 }
 
-// One workgroup (4 waves) per unit of 64 windows (whole images) of one channel.
+// One workgroup (8 waves) per unit of 64 windows (whole images) of one channel.
 template <class S>
-__global__ void __launch_bounds__(kThreads) k_dt_bf16(DtArgs a) {
+__global__ void __launch_bounds__(kDtThreads) k_dt_bf16(DtArgs a) {
   extern __shared__ __attribute__((aligned(16))) uint16_t smem_h[];
   uint16_t* Gt = smem_h;             // [D][NP]: G of pixel p, window n at p * NP + n
   uint16_t* Xt = smem_h + S::D * S::NP;
@@ -128,54 +130,66 @@ __global__ void __launch_bounds__(kThreads) k_dt_bf16(DtArgs a) {
   const int c = u / a.groups;
   const int img0 = (u - c * a.groups) * S::IPU;
 
-  // ---- stage: pixel pairs (2 bf16, 4 bytes) of every window row; windows past the batch are 0
-  constexpr int SB = 8;
-  for (int e0 = 0; e0 < S::PAIRS; e0 += SB * kThreads) {
-    uint32_t gv[SB], xv[SB];
+  // ---- stage: item (window pair wp, row y, pixel pair xp) loads pixels 2xp, 2xp+1 of row y of
+  //      windows 2wp and 2wp+1 (4 bytes each) and writes each pixel's two windows as one 4-byte
+  //      LDS word; windows past the batch are 0. All loads of a lane are in flight before its
+  //      writes.
+  constexpr int SB = (S::ITEMS + kDtThreads - 1) / kDtThreads;
+  uint32_t gv[SB][2], xv[SB][2];
 #pragma unroll
-    for (int s = 0; s < SB; ++s) {
-      const int e = e0 + s * kThreads + threadIdx.x;
-      const int n = e / (S::WS * S::WS / 2), rem = e - n * (S::WS * S::WS / 2);
-      const int y = rem / (S::WS / 2), xp = rem - y * (S::WS / 2);
+  for (int s = 0; s < SB; ++s) {
+    const int e = s * kDtThreads + threadIdx.x;
+    const int wp = e / (S::WS * S::WS / 2), rem = e - wp * (S::WS * S::WS / 2);
+    const int y = rem / (S::WS / 2), xp = rem - y * (S::WS / 2);
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int n = 2 * wp + h;
       const int im = n / S::NWIN, k = n - im * S::NWIN;
-      const bool in = e < S::PAIRS && img0 + im < a.B;
+      const bool in = e < S::ITEMS && img0 + im < a.B;
       const size_t off = in ? ((size_t)(img0 + im) * a.C + c) * S::PLANE +
                                   ((k / S::NWX) * S::WS + y) * S::IW + (k % S::NWX) * S::WS + 2 * xp
                             : 0;
       const uint32_t g2 = *(const uint32_t*)(a.g + off);
       const uint32_t x2 = *(const uint32_t*)(a.x + off);
-      gv[s] = in ? g2 : 0u;
-      xv[s] = in ? x2 : 0u;
+      gv[s][h] = in ? g2 : 0u;
+      xv[s][h] = in ? x2 : 0u;
     }
+  }
 #pragma unroll
-    for (int s = 0; s < SB; ++s) {
-      const int e = e0 + s * kThreads + threadIdx.x;
-      if (e >= S::PAIRS) break;
-      const int n = e / (S::WS * S::WS / 2), rem = e - n * (S::WS * S::WS / 2);
-      const int y = rem / (S::WS / 2), xp = rem - y * (S::WS / 2);
-      const int p = y * S::WS + 2 * xp;
-      Gt[p * S::NP + n] = (uint16_t)(gv[s] & 0xffffu);
-      Gt[(p + 1) * S::NP + n] = (uint16_t)(gv[s] >> 16);
-      Xt[p * S::NP + n] = (uint16_t)(xv[s] & 0xffffu);
-      Xt[(p + 1) * S::NP + n] = (uint16_t)(xv[s] >> 16);
-    }
+  for (int s = 0; s < SB; ++s) {
+    const int e = s * kDtThreads + threadIdx.x;
+    if (e >= S::ITEMS) break;
+    const int wp = e / (S::WS * S::WS / 2), rem = e - wp * (S::WS * S::WS / 2);
+    const int y = rem / (S::WS / 2), xp = rem - y * (S::WS / 2);
+    const int p = y * S::WS + 2 * xp;
+    // pixel p: (window 2wp, window 2wp+1) = the low halves; pixel p+1: the high halves
+    uint32_t* g32 = (uint32_t*)(Gt + p * S::NP + 2 * wp);
+    uint32_t* x32 = (uint32_t*)(Xt + p * S::NP + 2 * wp);
+    g32[0] = (gv[s][0] & 0xffffu) | (gv[s][1] << 16);
+    g32[S::NP / 2] = (gv[s][0] >> 16) | (gv[s][1] & 0xffff0000u);
+    x32[0] = (xv[s][0] & 0xffffu) | (xv[s][1] << 16);
+    x32[S::NP / 2] = (xv[s][0] >> 16) | (xv[s][1] & 0xffff0000u);
   }
   __syncthreads();
 
-  double* scr = (double*)smem_h + wave * (7 * S::D + 64);
+  double* scr = (double*)smem_h + wave * (kDtSlots * S::D + 64);
   double* pT = a.partT + (size_t)u * S::L;
   switch (wave) {
     case 0: dt_wave<S, 0>(Gt, Xt, scr, pT, lane); break;
     case 1: dt_wave<S, 1>(Gt, Xt, scr, pT, lane); break;
     case 2: dt_wave<S, 2>(Gt, Xt, scr, pT, lane); break;
-    default: dt_wave<S, 3>(Gt, Xt, scr, pT, lane); break;
+    case 3: dt_wave<S, 3>(Gt, Xt, scr, pT, lane); break;
+    case 4: dt_wave<S, 4>(Gt, Xt, scr, pT, lane); break;
+    case 5: dt_wave<S, 5>(Gt, Xt, scr, pT, lane); break;
+    case 6: dt_wave<S, 6>(Gt, Xt, scr, pT, lane); break;
+    default: dt_wave<S, 7>(Gt, Xt, scr, pT, lane); break;
   }
 }
 
 using D28 = DtShape<28>;
 using D56 = DtShape<56>;
-// the diagonal-sum scratch (4 waves x (7 tiles + a dump row) of doubles) fits in the tiles
-static_assert(4 * (7 * 196 + 64) * 8 <= dt_lds_bytes<D28>(), "scratch");
+// the diagonal-sum scratch (8 waves x (4 tiles + a dump row) of doubles) fits in the tiles
+static_assert(kDtWaves * (kDtSlots * 196 + 64) * 8 <= dt_lds_bytes<D28>(), "scratch");
 
 template <class S>
 int dt_groups(int B) { return (B + S::IPU - 1) / S::IPU; }
@@ -194,7 +208,7 @@ hipError_t launch_dt(const uint16_t* g, const uint16_t* x, double* partT, int B,
   hipError_t e = hipFuncSetAttribute((const void*)k_dt_bf16<S>,
                                      hipFuncAttributeMaxDynamicSharedMemorySize, lds);
   if (e != hipSuccess) return e;
-  return launch_main(k_dt_bf16<S>, dim3(C * a.groups), dim3(kThreads), lds, st, a);
+  return launch_main(k_dt_bf16<S>, dim3(C * a.groups), dim3(kDtThreads), lds, st, a);
 }
 
 size_t al256(size_t v) { return (v + 255) / 256 * 256; }
