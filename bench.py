@@ -286,7 +286,7 @@ def run(args):
             s["dx"] = torch.empty_like(s["x"])
         sets.append(s)
     T = to_dev(inp["T"])
-    Wm = to_dev(inp["Wmix"]) if wl.mix else None
+    Wm = torch.from_numpy(inp["Wmix"]).to(dev) if wl.mix else None  # the mix weights stay fp32
     M = None
     Tsub = to_dev(inp["T_sub"]) if wl.s is not None else None
     hier_train = wl.s is not None and wl.backward  # fold on chip, dT_sub in the backward

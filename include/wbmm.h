@@ -93,7 +93,10 @@ wbmm_status wbmm_fold_hier(const void* M_in, const void* T_sub, int C, int w, in
 
 /*
  * wbmm_forward_workspace_bytes — device workspace wbmm_forward needs for these arguments
- * (0 when none). Returns 0 for invalid arguments as well; wbmm_forward reports those.
+ * (0 when none), the largest need over fp32 and bf16 inputs and outputs (a bf16 z_save with the
+ * mix in window mode takes the fp32 pre-mix map through the workspace; bf16 maps with the mix
+ * on the fast bf16 shapes keep z there when no z_save is given). Returns 0 for invalid
+ * arguments as well; wbmm_forward reports those.
  */
 size_t wbmm_forward_workspace_bytes(int B, int C, int H, int W, int w, int layout, int has_mix,
                                     int has_z_save);
@@ -113,7 +116,8 @@ size_t wbmm_forward_workspace_bytes(int B, int C, int H, int W, int w, int layou
  * x:      device map, in_dtype.
  * T, M:   exactly one non-NULL. T: device [C][2w-1][2w-1] — M_c is formed on chip from T_c.
  *         M: device [C][d][d] — the cached (possibly folded) matrices are read from memory.
- * mix_w:  device fp32 [C][3][3] or NULL.
+ * mix_w:  device fp32 [C][3][3] or NULL. The mix runs in fp32 on the fp32 pre-mix map; with
+ *         bf16 output, y and z_save are rounded from it (RNE).
  * z_save: device map in out_dtype receiving the pre-mix output z (for the backward), or NULL.
  * y:      device map in out_dtype, written; must not overlap x, T, M, mix_w or z_save.
  * workspace / workspace_bytes: device scratch of at least wbmm_forward_workspace_bytes(...)

@@ -143,8 +143,6 @@ wbmm_status check_forward(const wbmm::FwdRequest& r, int in_dtype, int out_dtype
   if (!r.x || !r.y) return fail(WBMM_E_INVALID, "x and y must be non-NULL");
   if ((r.T == nullptr) == (r.M == nullptr))
     return fail(WBMM_E_INVALID, "exactly one of T (table) and M (cached matrix) must be given");
-  if (r.mixw && out_dtype != WBMM_F32)
-    return fail(WBMM_E_UNSUPPORTED, "the 3x3 mix is provided with fp32 output only");
   const size_t ies = dtype_size(in_dtype), oes = dtype_size(out_dtype);
   if (!aligned(r.x, ies) || (r.T && !aligned(r.T, ies)) || (r.M && !aligned(r.M, ies)) ||
       !aligned(r.y, oes) || (r.zsave && !aligned(r.zsave, oes)) || (r.mixw && !aligned(r.mixw, 4)))
@@ -194,7 +192,16 @@ size_t forward_ws_bytes(int B, int C, int H, int W, int w, int oy, int ox, int l
   r.oy = oy;
   r.ox = ox;
   if (!wbmm::forward_plan_ok(r)) return 0;
-  return wbmm::forward_workspace(r);
+  // the dtypes are not arguments: the largest need over fp32 / bf16 inputs and outputs
+  size_t need = 0;
+  for (int ib = 0; ib < 2; ++ib)
+    for (int ob = 0; ob < 2; ++ob) {
+      r.in_bf16 = ib;
+      r.out_bf16 = ob;
+      const size_t n = wbmm::forward_workspace(r);
+      if (n > need) need = n;
+    }
+  return need;
 }
 
 wbmm_status forward_call(int B, int C, int H, int W, int w, int oy, int ox, int layout,

@@ -134,10 +134,11 @@ __device__ __forceinline__ void map_coords(size_t e, int layout, int C, int H, i
 
 // y[b,c,h,v] = sum_{u,t} w9[c][u][t] * z[b,c,h+u-1,v+t-1]  (zero outside the map)
 // [gecl.asia reading notes, "Method" point 3: cross-block 3x3 depthwise mixing]
+// zcopy (bf16, or null): the pre-mix map z rounded to bf16, for a bf16 z_save.
 __global__ void __launch_bounds__(kThreads) k_mix_fwd(const float* __restrict__ z,
                                                       const float* __restrict__ w9, void* y,
                                                       int out_bf16, int B, int C, int H, int W,
-                                                      int layout) {
+                                                      int layout, uint16_t* zcopy) {
   const size_t total = (size_t)B * C * H * W;
   for (size_t e = (size_t)blockIdx.x * kThreads + threadIdx.x; e < total;
        e += (size_t)gridDim.x * kThreads) {
@@ -157,6 +158,7 @@ __global__ void __launch_bounds__(kThreads) k_mix_fwd(const float* __restrict__ 
     }
     if (out_bf16) ((uint16_t*)y)[e] = f2bf(acc);
     else ((float*)y)[e] = acc;
+    if (zcopy) zcopy[e] = f2bf(z[e]);
   }
 }
 
@@ -261,10 +263,10 @@ hipError_t launch_bwd_reduce(const double* partT, const double* partW, int parts
 }
 
 hipError_t launch_mix_fwd(const float* z, const float* w9, void* y, int out_bf16, int B, int C,
-                          int H, int W, int layout, hipStream_t st) {
+                          int H, int W, int layout, hipStream_t st, uint16_t* zcopy) {
   const size_t n = (size_t)B * C * H * W;
   hipLaunchKernelGGL(k_mix_fwd, dim3(grid_for(n)), dim3(kThreads), 0, st, z, w9, y, out_bf16, B,
-                     C, H, W, layout);
+                     C, H, W, layout, zcopy);
   return hipGetLastError();
 }
 
@@ -280,6 +282,146 @@ hipError_t launch_mix_bwd_weight(const float* dy, const float* z, float* dw9, in
                                  int W, int layout, hipStream_t st) {
   hipLaunchKernelGGL(k_mix_bwd_weight<float>, dim3(C), dim3(kThreads), 0, st, dy, z, dw9, B, C, H,
                      W, layout);
+  return hipGetLastError();
+}
+
+// Stage one bf16 plane into LDS as fp32 with a one-pixel zero halo (pitch W + 2): the halo is
+// zeroed, then the interior is filled from 4-byte pixel pairs (W even) or single pixels.
+__device__ __forceinline__ void stage_plane_bf16(const uint16_t* __restrict__ src, float* P,
+                                                 int H, int W) {
+  const int PW = W + 2;
+  for (int e = threadIdx.x; e < PW; e += kThreads) {
+    P[e] = 0.f;
+    P[(H + 1) * PW + e] = 0.f;
+  }
+  for (int r = threadIdx.x; r < H; r += kThreads) {
+    P[(r + 1) * PW] = 0.f;
+    P[(r + 1) * PW + W + 1] = 0.f;
+  }
+  if ((W & 1) == 0) {
+    const int hw = W / 2;
+    for (int e = threadIdx.x; e < H * hw; e += kThreads) {
+      const int h = e / hw, v2 = e - h * hw;
+      const uint32_t pr = *(const uint32_t*)(src + (size_t)h * W + 2 * v2);
+      P[(h + 1) * PW + 2 * v2 + 1] = __uint_as_float(pr << 16);
+      P[(h + 1) * PW + 2 * v2 + 2] = __uint_as_float(pr & 0xffff0000u);
+    }
+  } else {
+    for (int e = threadIdx.x; e < H * W; e += kThreads) {
+      const int h = e / W, v = e - h * W;
+      P[(h + 1) * PW + v + 1] = bf2f(src[(size_t)h * W + v]);
+    }
+  }
+}
+
+// Mix adjoint and dWmix partials of whole planes: workgroup (c, q) takes planes (b, c) for
+// b = q*PB .. q*PB + PB - 1 in turn; each is staged in LDS with a one-pixel zero halo (dy and z),
+// then every pixel does the 9 neighbour reads once for both g[h,v] = sum_{u,t} W[u][t]
+// dy[h-u+1, v-t+1] (written as bf16) and the dWmix terms z[h,v] dy[h-u+1, v-t+1] (fp64 per
+// thread over all its planes). The 9 sums are then reduced over the wave by shuffles and over the
+// 4 waves in a fixed order into the workgroup's partial partW[c][q][9] (z may be null: no
+// partials). Several planes per workgroup keep the reduction's cost off each plane.
+__global__ void __launch_bounds__(kThreads) k_mix_bwd_planes_bf16(
+    const uint16_t* __restrict__ dy, const uint16_t* __restrict__ z, const float* __restrict__ w9,
+    uint16_t* __restrict__ g, double* __restrict__ partW, int B, int C, int H, int W, int PB) {
+  extern __shared__ __attribute__((aligned(16))) float smem_f[];
+  __shared__ double wsum[4][9];
+  const int c = blockIdx.x, q = blockIdx.y;
+  const int PW = W + 2, plane = (H + 2) * PW;
+  float* Dp = smem_f;
+  float* Zp = smem_f + plane;
+  float w[9];
+#pragma unroll
+  for (int k = 0; k < 9; ++k) w[k] = w9[c * 9 + k];
+  double acc[9];
+#pragma unroll
+  for (int k = 0; k < 9; ++k) acc[k] = 0.0;
+  const int b1 = min(B, (q + 1) * PB);
+  for (int b = q * PB; b < b1; ++b) {
+    const size_t base = ((size_t)b * C + c) * H * W;
+    if (b > q * PB) __syncthreads();  // every thread is done with the previous plane
+    stage_plane_bf16(dy + base, Dp, H, W);
+    if (z) stage_plane_bf16(z + base, Zp, H, W);
+    __syncthreads();
+    for (int e = threadIdx.x; e < H * W; e += kThreads) {
+      const int h = e / W, v = e - h * W;
+      float nb[9];  // nb[u][t] = dy[h-u+1][v-t+1]
+#pragma unroll
+      for (int u = 0; u < 3; ++u)
+#pragma unroll
+        for (int t = 0; t < 3; ++t) nb[u * 3 + t] = Dp[(h - u + 2) * PW + (v - t + 2)];
+      float gv = 0.f;
+#pragma unroll
+      for (int k = 0; k < 9; ++k) gv = fmaf(w[k], nb[k], gv);
+      g[base + e] = f2bf(gv);
+      if (z) {
+        const double zv = Zp[(h + 1) * PW + v + 1];
+#pragma unroll
+        for (int k = 0; k < 9; ++k) acc[k] += zv * (double)nb[k];
+      }
+    }
+  }
+  if (!z) return;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+#pragma unroll
+  for (int k = 0; k < 9; ++k) {
+    double v = acc[k];
+    for (int off = 32; off > 0; off >>= 1) v += __shfl_down(v, off, 64);
+    if (lane == 0) wsum[wave][k] = v;
+  }
+  __syncthreads();
+  if (threadIdx.x < 9) {
+    const int k = threadIdx.x;
+    partW[((size_t)c * gridDim.y + q) * 9 + k] = ((wsum[0][k] + wsum[1][k]) + wsum[2][k]) + wsum[3][k];
+  }
+}
+
+// y = mix3x3(z) of whole bf16 planes (fp32 sums, RNE), one workgroup per (b, c) plane: the
+// stand-alone mix pass after a bf16 forward that wrote z.
+__global__ void __launch_bounds__(kThreads) k_mix_fwd_planes_bf16(
+    const uint16_t* __restrict__ z, const float* __restrict__ w9, uint16_t* __restrict__ y, int C,
+    int H, int W) {
+  extern __shared__ __attribute__((aligned(16))) float smem_f[];
+  const int pl = blockIdx.x, c = pl % C;
+  const int PW = W + 2;
+  const size_t base = (size_t)pl * H * W;
+  stage_plane_bf16(z + base, smem_f, H, W);
+  __syncthreads();
+  float w[9];
+#pragma unroll
+  for (int q = 0; q < 9; ++q) w[q] = w9[c * 9 + q];
+  for (int e = threadIdx.x; e < H * W; e += kThreads) {
+    const int h = e / W, v = e - h * W;
+    float acc = 0.f;
+#pragma unroll
+    for (int u = 0; u < 3; ++u)
+#pragma unroll
+      for (int t = 0; t < 3; ++t) acc = fmaf(w[u * 3 + t], smem_f[(h + u) * PW + v + t], acc);
+    y[base + e] = f2bf(acc);
+  }
+}
+
+hipError_t launch_mix_fwd_planes_bf16(const uint16_t* z, const float* w9, uint16_t* y, int B,
+                                      int C, int H, int W, hipStream_t st) {
+  const size_t lds = (size_t)(H + 2) * (W + 2) * sizeof(float);
+  if (lds > 64 * 1024) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(k_mix_fwd_planes_bf16, dim3(B * C), dim3(kThreads), (unsigned)lds, st, z, w9,
+                     y, C, H, W);
+  return hipGetLastError();
+}
+
+size_t mix_planes_lds_bytes(int H, int W) { return (size_t)2 * (H + 2) * (W + 2) * sizeof(float); }
+
+int mix_planes_per_group(int B) { return B < 8 ? B : 8; }
+
+hipError_t launch_mix_bwd_planes_bf16(const uint16_t* dy, const uint16_t* z, const float* w9,
+                                      uint16_t* g, double* partW, int B, int C, int H, int W,
+                                      hipStream_t st) {
+  const size_t lds = mix_planes_lds_bytes(H, W);
+  if (lds > 64 * 1024) return hipErrorInvalidValue;
+  const int pb = mix_planes_per_group(B);
+  hipLaunchKernelGGL(k_mix_bwd_planes_bf16, dim3(C, (B + pb - 1) / pb), dim3(kThreads),
+                     (unsigned)lds, st, dy, z, w9, g, partW, B, C, H, W, pb);
   return hipGetLastError();
 }
 

@@ -220,12 +220,12 @@ bool bf16_backward_ok(int B, int C, int H, int W, int w, int layout) {
          (long long)C * ((B + 3) / 4 + 1) < (1LL << 31);
 }
 
-// [G map (bf16, with a mix)] [dT partials (fp64)]
+// [G map (bf16), dWmix partials (fp64, per plane): with a mix] [dT partials (fp64)]
 size_t bf16_backward_workspace(int B, int C, int H, int W, int w, int has_mix) {
   if (!bf16_backward_ok(B, C, H, W, w, 0)) return 0;
   const int groups = H == 28 ? dt_groups<D28>(B) : dt_groups<D56>(B);
-  const size_t gmap = has_mix ? al256((size_t)B * C * H * W * 2) : 0;
-  return gmap + al256((size_t)C * groups * 729 * 8);
+  const size_t mixpart = has_mix ? al256((size_t)B * C * H * W * 2) + al256((size_t)C * B * 9 * 8) : 0;
+  return mixpart + al256((size_t)C * groups * 729 * 8);
 }
 
 hipError_t launch_backward_bf16(const BwdBf16Request& r, hipStream_t st) {
@@ -234,12 +234,17 @@ hipError_t launch_backward_bf16(const BwdBf16Request& r, hipStream_t st) {
   const bool mix = r.mixw != nullptr;
   const uint16_t* g = r.dy;
   hipError_t e = hipSuccess;
-  if (mix) {
+  const size_t gmap = mix ? al256((size_t)r.B * r.C * r.H * r.W * 2) : 0;
+  const size_t mixpart = mix ? gmap + al256((size_t)r.C * r.B * 9 * 8) : 0;
+  if (mix) {  // G and the per-plane dWmix partials in one pass over dy and z
     uint16_t* gm = (uint16_t*)ws;
-    e = launch_mix_bwd_data_bf16(r.dy, r.mixw, gm, r.B, r.C, r.H, r.W, st);
+    double* partW = (double*)(ws + gmap);
+    e = launch_mix_bwd_planes_bf16(r.dy, r.dmixw ? r.zsaved : nullptr, r.mixw, gm, partW, r.B,
+                                   r.C, r.H, r.W, st);
     if (e != hipSuccess) return e;
     if (r.dmixw) {
-      e = launch_mix_bwd_weight_bf16(r.dy, r.zsaved, r.dmixw, r.B, r.C, r.H, r.W, st);
+      const int pb = mix_planes_per_group(r.B);
+      e = launch_bwd_reduce(nullptr, partW, (r.B + pb - 1) / pb, r.C, 0, nullptr, r.dmixw, st);
       if (e != hipSuccess) return e;
     }
     g = gm;
@@ -249,7 +254,7 @@ hipError_t launch_backward_bf16(const BwdBf16Request& r, hipStream_t st) {
     if (e != hipSuccess) return e;
   }
   if (r.dT) {
-    double* partT = (double*)(ws + (mix ? al256((size_t)r.B * r.C * r.H * r.W * 2) : 0));
+    double* partT = (double*)(ws + mixpart);
     const int groups = r.H == 28 ? dt_groups<D28>(r.B) : dt_groups<D56>(r.B);
     e = r.H == 28 ? launch_dt<D28>(g, r.x, partT, r.B, r.C, st)
                   : launch_dt<D56>(g, r.x, partT, r.B, r.C, st);

@@ -140,16 +140,39 @@ bool forward_plan_ok(const FwdRequest& r) {
   return plan_fwd(g, r);
 }
 
+// bf16 maps with the mix on a fast bf16 shape: the fast forward writes z (bf16) to z_save or the
+// workspace, then a plane-staged pass applies the mix (y = bf16(mix(bf16 z))).
+static bool fast_bf16_mix_ok(const FwdRequest& r) {
+  if (!r.mixw || r.Tsub || !r.in_bf16 || !r.out_bf16) return false;
+  FwdRequest q = r;
+  q.mixw = nullptr;
+  q.zsave = nullptr;
+  return fast_bf16_forward_ok(q) && (size_t)(r.H + 2) * (r.W + 2) * 4 <= 64 * 1024;
+}
+
 size_t forward_workspace(const FwdRequest& r) {
+  if (fast_bf16_mix_ok(r)) return r.zsave ? 0 : (size_t)r.B * r.C * r.H * r.W * 2;
   Geo g;
   if (!plan_fwd(g, r)) return 0;
-  if (r.mixw && !g.image_mode && !r.zsave) return (size_t)r.B * r.C * r.H * r.W * sizeof(float);
+  // window mode with a mix: the fp32 pre-mix map goes to z_save when that is fp32, else here
+  if (r.mixw && !g.image_mode && (!r.zsave || r.out_bf16))
+    return (size_t)r.B * r.C * r.H * r.W * sizeof(float);
   return 0;
 }
 
 hipError_t launch_forward(const FwdRequest& r, hipStream_t st) {
   if (fast_forward_ok(r)) return launch_forward_fast(r, st);  // folds a sub-table when w = 2s
   if (!r.Tsub && fast_bf16_forward_ok(r)) return launch_forward_fast_bf16(r, st);
+  if (fast_bf16_mix_ok(r)) {
+    FwdRequest q = r;
+    uint16_t* zb = (uint16_t*)(r.zsave ? r.zsave : r.ws);
+    q.mixw = nullptr;
+    q.zsave = nullptr;
+    q.y = zb;
+    hipError_t e = launch_forward_fast_bf16(q, st);
+    if (e != hipSuccess) return e;
+    return launch_mix_fwd_planes_bf16(zb, r.mixw, (uint16_t*)r.y, r.B, r.C, r.H, r.W, st);
+  }
   FwdArgs a{};
   if (!plan_fwd(a.g, r)) return hipErrorInvalidValue;
   a.x = r.x;
@@ -165,8 +188,9 @@ hipError_t launch_forward(const FwdRequest& r, hipStream_t st) {
     a.y = r.y;
     a.mix_here = mix ? 1 : 0;
   } else if (mix) {
-    // pre-mix output goes to z_save (fp32 only, checked by the API) or the workspace
-    zbuf = r.zsave ? (float*)r.zsave : (float*)r.ws;
+    // pre-mix output goes to an fp32 z_save or to the workspace (a bf16 z_save is written from it
+    // by the mix pass)
+    zbuf = (r.zsave && !r.out_bf16) ? (float*)r.zsave : (float*)r.ws;
     a.zsave = nullptr;
     a.y = zbuf;
     a.out_bf16 = 0;
@@ -183,7 +207,8 @@ hipError_t launch_forward(const FwdRequest& r, hipStream_t st) {
   else e = cached ? launch_fwd_tiles<float, 1>(a, st) : launch_fwd_tiles<float, 0>(a, st);
   if (e != hipSuccess) return e;
   if (!a.g.image_mode && mix)
-    e = launch_mix_fwd(zbuf, r.mixw, r.y, r.out_bf16, r.B, r.C, r.H, r.W, r.layout, st);
+    e = launch_mix_fwd(zbuf, r.mixw, r.y, r.out_bf16, r.B, r.C, r.H, r.W, r.layout, st,
+                       (r.zsave && r.out_bf16) ? (uint16_t*)r.zsave : nullptr);
   return e;
 }
 

@@ -109,6 +109,13 @@ size_t bf16_backward_workspace(int B, int C, int H, int W, int w, int has_mix);
 hipError_t launch_backward_bf16(const BwdBf16Request& r, hipStream_t st);
 hipError_t launch_bf16_transposed_contraction(const uint16_t* g, const uint16_t* T, uint16_t* out,
                                               int B, int C, int H, hipStream_t st);
+hipError_t launch_mix_fwd_planes_bf16(const uint16_t* z, const float* w9, uint16_t* y, int B,
+                                      int C, int H, int W, hipStream_t st);
+// dWmix partials of launch_mix_bwd_planes_bf16: [C][ceil(B / mix_planes_per_group(B))][9]
+int mix_planes_per_group(int B);
+hipError_t launch_mix_bwd_planes_bf16(const uint16_t* dy, const uint16_t* z, const float* w9,
+                                      uint16_t* g, double* partW, int B, int C, int H, int W,
+                                      hipStream_t st);
 hipError_t launch_mix_bwd_data_bf16(const uint16_t* dy, const float* w9, uint16_t* dz, int B,
                                     int C, int H, int W, hipStream_t st);
 hipError_t launch_mix_bwd_weight_bf16(const uint16_t* dy, const uint16_t* z, float* dw9, int B,
@@ -125,7 +132,7 @@ hipError_t launch_dwconv(int B, int C, int H, int W, int k, const float* x, cons
 
 // 3x3 depthwise mix kernels (used by the window-mode paths).
 hipError_t launch_mix_fwd(const float* z, const float* w9, void* y, int out_bf16, int B, int C,
-                          int H, int W, int layout, hipStream_t st);
+                          int H, int W, int layout, hipStream_t st, uint16_t* zcopy = nullptr);
 hipError_t launch_mix_bwd_data(const float* dy, const float* w9, float* dz, int B, int C, int H,
                                int W, int layout, hipStream_t st);
 hipError_t launch_mix_bwd_weight(const float* dy, const float* z, float* dw9, int B, int C, int H,

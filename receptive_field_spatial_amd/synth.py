@@ -83,6 +83,9 @@ WORKLOADS: Dict[str, Workload] = {
     "train_w14_bf16": Workload("train_w14_bf16", B=64, C=192, H=28, W=28, w=14, dtype="bf16",
                                backward=True,
                                note="bf16 (mixed-precision) training step of the operator"),
+    "train_w14_bf16_mix": Workload("train_w14_bf16_mix", B=64, C=192, H=28, W=28, w=14,
+                                   dtype="bf16", mix=True, backward=True,
+                                   note="bf16 training step of the layer with the 3x3 mix"),
     "train_w14_shift": Workload("train_w14_shift", B=64, C=192, H=28, W=28, w=14, mix=True,
                                 backward=True, shift=7,
                                 note="fp32 training step of an interleaved layer (grid offset 7)"),

@@ -836,3 +836,44 @@ def test_backward_bf16_partial_outputs():
     wdx, wdT, _ = O.layer_backward(x.astype(np.float64), dy.astype(np.float64), w, T=T)
     assert_f32(host(dT), wdT, "dT")
     assert_bf16(host(dx.float()), wdx, "dx")
+
+
+@pytest.mark.parametrize("B,C,H,W,w", [(4, 3, 28, 28, 14), (2, 2, 128, 128, 14), (3, 2, 20, 17, 6),
+                                       (5, 2, 56, 56, 14), (3, 2, 56, 56, 7), (2, 2, 56, 56, 28)])
+@pytest.mark.parametrize("zsave", [True, False])
+def test_forward_bf16_with_mix(B, C, H, W, w, zsave):
+    """bf16 maps with the 3x3 mix: y and z_save in bf16, against the oracle on bf16 values. Fast
+    bf16 shapes run the fast forward into z (z_save or the workspace) and a plane-staged mix pass;
+    the general kernel fuses the mix in image mode and runs it as a pass in window mode."""
+    say(f"forward bf16 mix B={B} C={C} H={H} W={W} w={w} zsave={zsave}")
+    x = synth.round_to_bf16(synth.normal_f32((B, C, H, W), 1.0, seed=290))
+    T = synth.round_to_bf16(synth.normal_f32((C, 2 * w - 1, 2 * w - 1), 0.02, seed=291))
+    Wm = synth.normal_f32((C, 3, 3), 0.1, seed=292)
+    zs = torch.empty((B, C, H, W), dtype=torch.bfloat16, device="cuda") if zsave else None
+    y = R().wbmm_forward(dev_bf16(x), w, T=dev_bf16(T), mix_w=dev(Wm), z_save=zs)
+    want_y, want_z = O.layer_forward(x.astype(np.float64), w, T=T, Wmix=Wm)
+    assert y.dtype == torch.bfloat16
+    assert_bf16(host(y.float()), want_y, "y")
+    if zsave:
+        assert_bf16(host(zs.float()), want_z, "z")
+
+
+def test_bf16_training_step_with_mix():
+    """A bf16 layer training step with the mix: the bf16 forward's z_save feeds the bf16
+    backward; all gradients against the oracle on the same bf16 values."""
+    B, C, H, w = 8, 3, 28, 14
+    say("bf16 training step with mix")
+    x = synth.round_to_bf16(synth.normal_f32((B, C, H, H), 1.0, seed=300))
+    T = synth.round_to_bf16(synth.normal_f32((C, 27, 27), 0.02, seed=301))
+    Wm = synth.normal_f32((C, 3, 3), 0.1, seed=302)
+    dy = synth.round_to_bf16(synth.normal_f32((B, C, H, H), 1.0, seed=303))
+    xd, Td, Wd = dev_bf16(x), dev_bf16(T), dev(Wm)
+    zs = torch.empty((B, C, H, H), dtype=torch.bfloat16, device="cuda")
+    R().wbmm_forward(xd, w, T=Td, mix_w=Wd, z_save=zs)
+    dx, dT, dW = R().wbmm_backward_bf16(xd, dev_bf16(dy), w, Td, mix_w=Wd, z_saved=zs)
+    z = host(zs.float()).astype(np.float64)
+    wdx, wdT, wdW = O.layer_backward(x.astype(np.float64), dy.astype(np.float64), w, T=T,
+                                     Wmix=Wm, z=z)
+    assert_bf16(host(dx.float()), wdx, "dx")
+    assert_bf16(host(dT), wdT, "dT")
+    assert_f32(host(dW), wdW, "dWmix")
