@@ -314,13 +314,47 @@ __device__ __forceinline__ void stage_plane_bf16(const uint16_t* __restrict__ sr
   }
 }
 
+// Column strips over halo-padded LDS planes (pitch W + 2): a task is (plane slot, column v,
+// strip of kStrip rows); walking down the strip with a sliding 3x3 register window
+// win[a][b] = P[(h + a) * PW + v + b] = input (h + a - 1, v + b - 1) reads 3 LDS values per row.
+constexpr int kStrip = 7;
+
+template <class F>
+__device__ __forceinline__ void walk_strip(const float* P, int PW, int v, int h0, int h1, F&& f) {
+  float win[3][3];
+#pragma unroll
+  for (int a = 0; a < 2; ++a)
+#pragma unroll
+    for (int b = 0; b < 3; ++b) win[a][b] = P[(h0 + a) * PW + v + b];
+  for (int h = h0; h < h1; ++h) {
+#pragma unroll
+    for (int b = 0; b < 3; ++b) win[2][b] = P[(h + 2) * PW + v + b];
+    f(h, win);
+#pragma unroll
+    for (int b = 0; b < 3; ++b) {
+      win[0][b] = win[1][b];
+      win[1][b] = win[2][b];
+    }
+  }
+}
+
+// Planes staged together so that a plane's strips (W * ceil(H / kStrip) tasks) fill the block.
+__host__ __device__ inline int mix_tasks_per_plane(int H, int W) {
+  return W * ((H + kStrip - 1) / kStrip);
+}
+__host__ __device__ inline int mix_planes_together(int H, int W) {
+  const int t = mix_tasks_per_plane(H, W);
+  const int sp = t >= kThreads ? 1 : kThreads / t;
+  return sp > 4 ? 4 : sp;
+}
+
 // Mix adjoint and dWmix partials of whole planes: workgroup (c, q) takes planes (b, c) for
-// b = q*PB .. q*PB + PB - 1 in turn; each is staged in LDS with a one-pixel zero halo (dy and z),
-// then every pixel does the 9 neighbour reads once for both g[h,v] = sum_{u,t} W[u][t]
-// dy[h-u+1, v-t+1] (written as bf16) and the dWmix terms z[h,v] dy[h-u+1, v-t+1] (fp64 per
-// thread over all its planes). The 9 sums are then reduced over the wave by shuffles and over the
-// 4 waves in a fixed order into the workgroup's partial partW[c][q][9] (z may be null: no
-// partials). Several planes per workgroup keep the reduction's cost off each plane.
+// b = q*PB .. q*PB + PB - 1, SP at a time; each is staged in LDS with a one-pixel zero halo (dy and
+// z), then every pixel's 9 neighbours (from the strip's register window) give both
+// g[h,v] = sum_{u,t} W[u][t] dy[h-u+1, v-t+1] (written as bf16) and the dWmix terms
+// z[h,v] dy[h-u+1, v-t+1] (fp64 per thread over all its planes). The 9 sums are then reduced over
+// the wave by shuffles and over the 4 waves in a fixed order into the workgroup's partial
+// partW[c][q][9] (z may be null: no partials).
 __global__ void __launch_bounds__(kThreads) k_mix_bwd_planes_bf16(
     const uint16_t* __restrict__ dy, const uint16_t* __restrict__ z, const float* __restrict__ w9,
     uint16_t* __restrict__ g, double* __restrict__ partW, int B, int C, int H, int W, int PB) {
@@ -328,37 +362,43 @@ __global__ void __launch_bounds__(kThreads) k_mix_bwd_planes_bf16(
   __shared__ double wsum[4][9];
   const int c = blockIdx.x, q = blockIdx.y;
   const int PW = W + 2, plane = (H + 2) * PW;
-  float* Dp = smem_f;
-  float* Zp = smem_f + plane;
+  const int SP = mix_planes_together(H, W), tpp = mix_tasks_per_plane(H, W);
+  const int nstrip = (H + kStrip - 1) / kStrip;
   float w[9];
 #pragma unroll
   for (int k = 0; k < 9; ++k) w[k] = w9[c * 9 + k];
   double acc[9];
 #pragma unroll
   for (int k = 0; k < 9; ++k) acc[k] = 0.0;
-  const int b1 = min(B, (q + 1) * PB);
-  for (int b = q * PB; b < b1; ++b) {
-    const size_t base = ((size_t)b * C + c) * H * W;
-    if (b > q * PB) __syncthreads();  // every thread is done with the previous plane
-    stage_plane_bf16(dy + base, Dp, H, W);
-    if (z) stage_plane_bf16(z + base, Zp, H, W);
+  const int b0 = q * PB, b1 = min(B, (q + 1) * PB);
+  for (int bs = b0; bs < b1; bs += SP) {
+    if (bs > b0) __syncthreads();  // every thread is done with the previous planes
+    const int np = min(SP, b1 - bs);
+    for (int j = 0; j < np; ++j) {
+      const size_t base = ((size_t)(bs + j) * C + c) * H * W;
+      stage_plane_bf16(dy + base, smem_f + (2 * j) * plane, H, W);
+      if (z) stage_plane_bf16(z + base, smem_f + (2 * j + 1) * plane, H, W);
+    }
     __syncthreads();
-    for (int e = threadIdx.x; e < H * W; e += kThreads) {
-      const int h = e / W, v = e - h * W;
-      float nb[9];  // nb[u][t] = dy[h-u+1][v-t+1]
+    for (int task = threadIdx.x; task < np * tpp; task += kThreads) {
+      const int j = task / tpp, r = task - j * tpp;
+      const int sidx = r / W, v = r - sidx * W;
+      const float* Dp = smem_f + (2 * j) * plane;
+      const float* Zp = smem_f + (2 * j + 1) * plane;
+      uint16_t* gp = g + ((size_t)(bs + j) * C + c) * H * W;
+      const int h0 = sidx * kStrip, h1 = min(H, h0 + kStrip);
+      walk_strip(Dp, PW, v, h0, h1, [&](int h, const float (&win)[3][3]) {
+        // dy[h-u+1][v-t+1] = win[2-u][2-t]
+        float gv = 0.f;
 #pragma unroll
-      for (int u = 0; u < 3; ++u)
+        for (int k = 0; k < 9; ++k) gv = fmaf(w[k], win[2 - k / 3][2 - k % 3], gv);
+        gp[(size_t)h * W + v] = f2bf(gv);
+        if (z) {
+          const double zv = Zp[(h + 1) * PW + v + 1];
 #pragma unroll
-        for (int t = 0; t < 3; ++t) nb[u * 3 + t] = Dp[(h - u + 2) * PW + (v - t + 2)];
-      float gv = 0.f;
-#pragma unroll
-      for (int k = 0; k < 9; ++k) gv = fmaf(w[k], nb[k], gv);
-      g[base + e] = f2bf(gv);
-      if (z) {
-        const double zv = Zp[(h + 1) * PW + v + 1];
-#pragma unroll
-        for (int k = 0; k < 9; ++k) acc[k] += zv * (double)nb[k];
-      }
+          for (int k = 0; k < 9; ++k) acc[k] += zv * (double)win[2 - k / 3][2 - k % 3];
+        }
+      });
     }
   }
   if (!z) return;
@@ -376,41 +416,50 @@ __global__ void __launch_bounds__(kThreads) k_mix_bwd_planes_bf16(
   }
 }
 
-// y = mix3x3(z) of whole bf16 planes (fp32 sums, RNE), one workgroup per (b, c) plane: the
-// stand-alone mix pass after a bf16 forward that wrote z.
+// y = mix3x3(z) of whole bf16 planes (fp32 sums, RNE): workgroup q takes planes q*SP .. + SP - 1
+// (the stand-alone mix pass after a bf16 forward that wrote z).
 __global__ void __launch_bounds__(kThreads) k_mix_fwd_planes_bf16(
     const uint16_t* __restrict__ z, const float* __restrict__ w9, uint16_t* __restrict__ y, int C,
-    int H, int W) {
+    int H, int W, int planes) {
   extern __shared__ __attribute__((aligned(16))) float smem_f[];
-  const int pl = blockIdx.x, c = pl % C;
-  const int PW = W + 2;
-  const size_t base = (size_t)pl * H * W;
-  stage_plane_bf16(z + base, smem_f, H, W);
+  const int PW = W + 2, plane = (H + 2) * PW;
+  const int SP = mix_planes_together(H, W), tpp = mix_tasks_per_plane(H, W);
+  const int p0 = blockIdx.x * SP, np = min(SP, planes - p0);
+  for (int j = 0; j < np; ++j)
+    stage_plane_bf16(z + (size_t)(p0 + j) * H * W, smem_f + j * plane, H, W);
   __syncthreads();
-  float w[9];
+  for (int task = threadIdx.x; task < np * tpp; task += kThreads) {
+    const int j = task / tpp, r = task - j * tpp;
+    const int sidx = r / W, v = r - sidx * W;
+    const int c = (p0 + j) % C;
+    float w[9];
 #pragma unroll
-  for (int q = 0; q < 9; ++q) w[q] = w9[c * 9 + q];
-  for (int e = threadIdx.x; e < H * W; e += kThreads) {
-    const int h = e / W, v = e - h * W;
-    float acc = 0.f;
+    for (int k = 0; k < 9; ++k) w[k] = w9[c * 9 + k];
+    uint16_t* yp = y + (size_t)(p0 + j) * H * W;
+    const int h0 = sidx * kStrip, h1 = min(H, h0 + kStrip);
+    walk_strip(smem_f + j * plane, PW, v, h0, h1, [&](int h, const float (&win)[3][3]) {
+      float acc = 0.f;
 #pragma unroll
-    for (int u = 0; u < 3; ++u)
-#pragma unroll
-      for (int t = 0; t < 3; ++t) acc = fmaf(w[u * 3 + t], smem_f[(h + u) * PW + v + t], acc);
-    y[base + e] = f2bf(acc);
+      for (int k = 0; k < 9; ++k) acc = fmaf(w[k], win[k / 3][k % 3], acc);
+      yp[(size_t)h * W + v] = f2bf(acc);
+    });
   }
 }
 
 hipError_t launch_mix_fwd_planes_bf16(const uint16_t* z, const float* w9, uint16_t* y, int B,
                                       int C, int H, int W, hipStream_t st) {
-  const size_t lds = (size_t)(H + 2) * (W + 2) * sizeof(float);
+  const int sp = mix_planes_together(H, W);
+  const size_t lds = (size_t)sp * (H + 2) * (W + 2) * sizeof(float);
   if (lds > 64 * 1024) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(k_mix_fwd_planes_bf16, dim3(B * C), dim3(kThreads), (unsigned)lds, st, z, w9,
-                     y, C, H, W);
+  const int planes = B * C;
+  hipLaunchKernelGGL(k_mix_fwd_planes_bf16, dim3((planes + sp - 1) / sp), dim3(kThreads),
+                     (unsigned)lds, st, z, w9, y, C, H, W, planes);
   return hipGetLastError();
 }
 
-size_t mix_planes_lds_bytes(int H, int W) { return (size_t)2 * (H + 2) * (W + 2) * sizeof(float); }
+size_t mix_planes_lds_bytes(int H, int W) {
+  return (size_t)2 * mix_planes_together(H, W) * (H + 2) * (W + 2) * sizeof(float);
+}
 
 int mix_planes_per_group(int B) { return B < 8 ? B : 8; }
 
