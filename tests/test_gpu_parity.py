@@ -877,3 +877,42 @@ def test_bf16_training_step_with_mix():
     assert_bf16(host(dx.float()), wdx, "dx")
     assert_bf16(host(dT), wdT, "dT")
     assert_f32(host(dW), wdW, "dWmix")
+
+
+@pytest.mark.parametrize("kind", ["hier", "shift"])
+def test_nhwc_hier_and_shifted(kind):
+    """Channels-last maps through the on-chip fold and the interleaved grid (general kernels):
+    forward with the mix and backward, against the oracle on the transposed maps."""
+    B, C, H, W, w = 2, 3, 28, 28, 14
+    say(f"nhwc {kind}")
+    x = synth.normal_f32((B, C, H, W), 1.0, seed=310)
+    T = synth.normal_f32((C, 27, 27), 0.05, seed=311)
+    Ts = synth.normal_f32((C, 13, 13), 0.05, seed=312)
+    Wm = synth.normal_f32((C, 3, 3), 0.1, seed=313)
+    dy = synth.normal_f32((B, C, H, W), 1.0, seed=314)
+    nhwc = lambda a: dev(np.ascontiguousarray(a.transpose(0, 2, 3, 1)))
+    back = lambda t: host(t).transpose(0, 3, 1, 2)
+    xd, dyd, Td, Wd = nhwc(x), nhwc(dy), dev(T), dev(Wm)
+    zs = torch.empty_like(xd)
+    if kind == "hier":
+        y = R().wbmm_forward_hier(xd, w, 7, Td, dev(Ts), mix_w=Wd, layout="NHWC", z_save=zs)
+        dx, dT, dTs, dW = R().wbmm_backward_hier(xd, dyd, w, 7, Td, dev(Ts), mix_w=Wd, z_saved=zs,
+                                                 layout="NHWC")
+        wy, wz = O.layer_forward_hier(x.astype(np.float64), w, 7, T, Ts, Wmix=Wm)
+        wdx, wdT, wdTs, wdW = O.layer_backward_hier(x.astype(np.float64), dy.astype(np.float64),
+                                                    w, 7, T, Ts, Wmix=Wm,
+                                                    z=back(zs).astype(np.float64))
+        assert_f32(host(dTs), wdTs, "dT_sub")
+    else:
+        y = R().wbmm_forward_shifted(xd, w, 7, 7, T=Td, mix_w=Wd, layout="NHWC", z_save=zs)
+        dx, dT, dW = R().wbmm_backward_shifted(xd, dyd, w, 7, 7, T=Td, mix_w=Wd, z_saved=zs,
+                                               layout="NHWC")
+        wy, wz = O.layer_forward_shifted(x.astype(np.float64), w, 7, 7, T=T, Wmix=Wm)
+        wdx, wdT, wdW = O.layer_backward_shifted(x.astype(np.float64), dy.astype(np.float64), w,
+                                                 7, 7, T=T, Wmix=Wm,
+                                                 z=back(zs).astype(np.float64))
+    assert_f32(back(y), wy, "y")
+    assert_f32(back(zs), wz, "z")
+    assert_f32(back(dx), wdx, "dx")
+    assert_f32(host(dT), wdT, "dT")
+    assert_f32(host(dW), wdW, "dWmix")
