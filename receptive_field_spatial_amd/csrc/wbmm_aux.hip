@@ -474,19 +474,4 @@ hipError_t launch_mix_bwd_planes_bf16(const uint16_t* dy, const uint16_t* z, con
   return hipGetLastError();
 }
 
-hipError_t launch_mix_bwd_data_bf16(const uint16_t* dy, const float* w9, uint16_t* dz, int B,
-                                    int C, int H, int W, hipStream_t st) {
-  const size_t n = (size_t)B * C * H * W;
-  hipLaunchKernelGGL(k_mix_bwd_data<uint16_t>, dim3(grid_for(n)), dim3(kThreads), 0, st, dy, w9,
-                     dz, B, C, H, W, 0);
-  return hipGetLastError();
-}
-
-hipError_t launch_mix_bwd_weight_bf16(const uint16_t* dy, const uint16_t* z, float* dw9, int B,
-                                      int C, int H, int W, hipStream_t st) {
-  hipLaunchKernelGGL(k_mix_bwd_weight<uint16_t>, dim3(C), dim3(kThreads), 0, st, dy, z, dw9, B, C,
-                     H, W, 0);
-  return hipGetLastError();
-}
-
 }  // namespace wbmm

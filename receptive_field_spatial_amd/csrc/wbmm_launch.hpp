@@ -116,10 +116,6 @@ int mix_planes_per_group(int B);
 hipError_t launch_mix_bwd_planes_bf16(const uint16_t* dy, const uint16_t* z, const float* w9,
                                       uint16_t* g, double* partW, int B, int C, int H, int W,
                                       hipStream_t st);
-hipError_t launch_mix_bwd_data_bf16(const uint16_t* dy, const float* w9, uint16_t* dz, int B,
-                                    int C, int H, int W, hipStream_t st);
-hipError_t launch_mix_bwd_weight_bf16(const uint16_t* dy, const uint16_t* z, float* dw9, int B,
-                                      int C, int H, int W, hipStream_t st);
 
 // Matrix-core peak probe (measurement aid): flops of one launch, and the launch.
 double probe_mfma_flops(int bf16, int blocks, int iters);
