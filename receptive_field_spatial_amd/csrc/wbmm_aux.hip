@@ -239,20 +239,25 @@ __global__ void __launch_bounds__(kThreads) k_bwd_reduce(const double* __restric
                                                          int parts, int L, float* __restrict__ dT,
                                                          float* __restrict__ dmixw) {
   const int c = blockIdx.x;
-  if (dT) {
-    for (int q = threadIdx.x; q < L; q += kThreads) {
-      const double* p = partT + (size_t)c * parts * L + q;
-      double s = 0.0;
-      for (int k = 0; k < parts; ++k) s += p[(size_t)k * L];
-      dT[(size_t)c * L + q] = (float)s;
-    }
-  }
-  if (dmixw && threadIdx.x < 9) {
-    const double* p = partW + (size_t)c * parts * 9 + threadIdx.x;
+  // partials are loaded 8 at a time (all in flight together) and added in order k = 0, 1, ...
+  auto sum = [](const double* p, size_t stride, int parts) {
     double s = 0.0;
-    for (int k = 0; k < parts; ++k) s += p[(size_t)k * 9];
-    dmixw[c * 9 + threadIdx.x] = (float)s;
+    for (int k0 = 0; k0 < parts; k0 += 8) {
+      double v[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) v[j] = k0 + j < parts ? p[(size_t)(k0 + j) * stride] : 0.0;
+#pragma unroll
+      for (int j = 0; j < 8; ++j)
+        if (k0 + j < parts) s += v[j];
+    }
+    return s;
+  };
+  if (dT) {
+    for (int q = threadIdx.x; q < L; q += kThreads)
+      dT[(size_t)c * L + q] = (float)sum(partT + (size_t)c * parts * L + q, (size_t)L, parts);
   }
+  if (dmixw && threadIdx.x < 9)
+    dmixw[c * 9 + threadIdx.x] = (float)sum(partW + (size_t)c * parts * 9 + threadIdx.x, 9, parts);
 }
 
 hipError_t launch_bwd_reduce(const double* partT, const double* partW, int parts, int C, int L,
