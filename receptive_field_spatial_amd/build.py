@@ -16,7 +16,7 @@ OBJ_DIR = os.path.join(PKG_DIR, "_build")
 LIB_PATH = os.path.join(PKG_DIR, "libwbmm.so")
 SOURCES = ["wbmm_api.cpp", "wbmm_aux.hip", "wbmm_fwd.hip", "wbmm_bwd.hip", "wbmm_fast.hip",
            "wbmm_fastbf.hip", "wbmm_dw.hip",
-           "wbmm_probe.hip", "wbmm_bwdbf.hip"]
+           "wbmm_probe.hip", "wbmm_bwdbf.hip", "wbmm_repack.hip"]
 
 ARCH = "gfx950"
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

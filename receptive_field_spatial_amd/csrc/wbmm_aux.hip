@@ -290,10 +290,14 @@ hipError_t launch_mix_bwd_weight(const float* dy, const float* z, float* dw9, in
   return hipGetLastError();
 }
 
-// Stage one bf16 plane into LDS as fp32 with a one-pixel zero halo (pitch W + 2): the halo is
-// zeroed, then the interior is filled from 4-byte pixel pairs (W even) or single pixels.
-__device__ __forceinline__ void stage_plane_bf16(const uint16_t* __restrict__ src, float* P,
-                                                 int H, int W) {
+// Stage one plane (bf16 or fp32) into LDS as fp32 with a one-pixel zero halo (pitch W + 2): the
+// halo is zeroed, then the interior is filled from pixel pairs (W even) or single pixels.
+template <typename TM>
+__device__ __forceinline__ void stage_plane(const TM* __restrict__ src, float* P, int H, int W);
+
+template <>
+__device__ __forceinline__ void stage_plane<uint16_t>(const uint16_t* __restrict__ src, float* P,
+                                                      int H, int W) {
   const int PW = W + 2;
   for (int e = threadIdx.x; e < PW; e += kThreads) {
     P[e] = 0.f;
@@ -318,6 +322,37 @@ __device__ __forceinline__ void stage_plane_bf16(const uint16_t* __restrict__ sr
     }
   }
 }
+
+template <>
+__device__ __forceinline__ void stage_plane<float>(const float* __restrict__ src, float* P, int H,
+                                                   int W) {
+  const int PW = W + 2;
+  for (int e = threadIdx.x; e < PW; e += kThreads) {
+    P[e] = 0.f;
+    P[(H + 1) * PW + e] = 0.f;
+  }
+  for (int r = threadIdx.x; r < H; r += kThreads) {
+    P[(r + 1) * PW] = 0.f;
+    P[(r + 1) * PW + W + 1] = 0.f;
+  }
+  if ((W & 1) == 0) {  // planes start at even pixel offsets: 8-byte pairs
+    const int hw = W / 2;
+    for (int e = threadIdx.x; e < H * hw; e += kThreads) {
+      const int h = e / hw, v2 = e - h * hw;
+      const float2 pr = *(const float2*)(src + (size_t)h * W + 2 * v2);
+      P[(h + 1) * PW + 2 * v2 + 1] = pr.x;
+      P[(h + 1) * PW + 2 * v2 + 2] = pr.y;
+    }
+  } else {
+    for (int e = threadIdx.x; e < H * W; e += kThreads) {
+      const int h = e / W, v = e - h * W;
+      P[(h + 1) * PW + v + 1] = src[(size_t)h * W + v];
+    }
+  }
+}
+
+__device__ __forceinline__ void put_map(uint16_t* p, float v) { *p = f2bf(v); }
+__device__ __forceinline__ void put_map(float* p, float v) { *p = v; }
 
 // Column strips over halo-padded LDS planes (pitch W + 2): a task is (plane slot, column v,
 // strip of kStrip rows); walking down the strip with a sliding 3x3 register window
@@ -359,10 +394,11 @@ __host__ __device__ inline int mix_planes_together(int H, int W) {
 // g[h,v] = sum_{u,t} W[u][t] dy[h-u+1, v-t+1] (written as bf16) and the dWmix terms
 // z[h,v] dy[h-u+1, v-t+1] (fp64 per thread over all its planes). The 9 sums are then reduced over
 // the wave by shuffles and over the 4 waves in a fixed order into the workgroup's partial
-// partW[c][q][9] (z may be null: no partials).
-__global__ void __launch_bounds__(kThreads) k_mix_bwd_planes_bf16(
-    const uint16_t* __restrict__ dy, const uint16_t* __restrict__ z, const float* __restrict__ w9,
-    uint16_t* __restrict__ g, double* __restrict__ partW, int B, int C, int H, int W, int PB) {
+// partW[c][q][9] (z may be null: no partials). Maps are bf16 or fp32 (TM); g has their type.
+template <typename TM>
+__global__ void __launch_bounds__(kThreads) k_mix_bwd_planes(
+    const TM* __restrict__ dy, const TM* __restrict__ z, const float* __restrict__ w9,
+    TM* __restrict__ g, double* __restrict__ partW, int B, int C, int H, int W, int PB) {
   extern __shared__ __attribute__((aligned(16))) float smem_f[];
   __shared__ double wsum[4][9];
   const int c = blockIdx.x, q = blockIdx.y;
@@ -381,8 +417,8 @@ __global__ void __launch_bounds__(kThreads) k_mix_bwd_planes_bf16(
     const int np = min(SP, b1 - bs);
     for (int j = 0; j < np; ++j) {
       const size_t base = ((size_t)(bs + j) * C + c) * H * W;
-      stage_plane_bf16(dy + base, smem_f + (2 * j) * plane, H, W);
-      if (z) stage_plane_bf16(z + base, smem_f + (2 * j + 1) * plane, H, W);
+      stage_plane<TM>(dy + base, smem_f + (2 * j) * plane, H, W);
+      if (z) stage_plane<TM>(z + base, smem_f + (2 * j + 1) * plane, H, W);
     }
     __syncthreads();
     for (int task = threadIdx.x; task < np * tpp; task += kThreads) {
@@ -390,14 +426,14 @@ __global__ void __launch_bounds__(kThreads) k_mix_bwd_planes_bf16(
       const int sidx = r / W, v = r - sidx * W;
       const float* Dp = smem_f + (2 * j) * plane;
       const float* Zp = smem_f + (2 * j + 1) * plane;
-      uint16_t* gp = g + ((size_t)(bs + j) * C + c) * H * W;
+      TM* gp = g + ((size_t)(bs + j) * C + c) * H * W;
       const int h0 = sidx * kStrip, h1 = min(H, h0 + kStrip);
       walk_strip(Dp, PW, v, h0, h1, [&](int h, const float (&win)[3][3]) {
         // dy[h-u+1][v-t+1] = win[2-u][2-t]
         float gv = 0.f;
 #pragma unroll
         for (int k = 0; k < 9; ++k) gv = fmaf(w[k], win[2 - k / 3][2 - k % 3], gv);
-        gp[(size_t)h * W + v] = f2bf(gv);
+        put_map(gp + (size_t)h * W + v, gv);
         if (z) {
           const double zv = Zp[(h + 1) * PW + v + 1];
 #pragma unroll
@@ -421,17 +457,18 @@ __global__ void __launch_bounds__(kThreads) k_mix_bwd_planes_bf16(
   }
 }
 
-// y = mix3x3(z) of whole bf16 planes (fp32 sums, RNE): workgroup q takes planes q*SP .. + SP - 1
-// (the stand-alone mix pass after a bf16 forward that wrote z).
-__global__ void __launch_bounds__(kThreads) k_mix_fwd_planes_bf16(
-    const uint16_t* __restrict__ z, const float* __restrict__ w9, uint16_t* __restrict__ y, int C,
+// y = mix3x3(z) of whole planes (fp32 sums; bf16 maps rounded to nearest even): workgroup q takes
+// planes q*SP .. + SP - 1 (the stand-alone mix pass after a forward that wrote z).
+template <typename TM>
+__global__ void __launch_bounds__(kThreads) k_mix_fwd_planes(
+    const TM* __restrict__ z, const float* __restrict__ w9, TM* __restrict__ y, int C,
     int H, int W, int planes) {
   extern __shared__ __attribute__((aligned(16))) float smem_f[];
   const int PW = W + 2, plane = (H + 2) * PW;
   const int SP = mix_planes_together(H, W), tpp = mix_tasks_per_plane(H, W);
   const int p0 = blockIdx.x * SP, np = min(SP, planes - p0);
   for (int j = 0; j < np; ++j)
-    stage_plane_bf16(z + (size_t)(p0 + j) * H * W, smem_f + j * plane, H, W);
+    stage_plane<TM>(z + (size_t)(p0 + j) * H * W, smem_f + j * plane, H, W);
   __syncthreads();
   for (int task = threadIdx.x; task < np * tpp; task += kThreads) {
     const int j = task / tpp, r = task - j * tpp;
@@ -440,26 +477,37 @@ __global__ void __launch_bounds__(kThreads) k_mix_fwd_planes_bf16(
     float w[9];
 #pragma unroll
     for (int k = 0; k < 9; ++k) w[k] = w9[c * 9 + k];
-    uint16_t* yp = y + (size_t)(p0 + j) * H * W;
+    TM* yp = y + (size_t)(p0 + j) * H * W;
     const int h0 = sidx * kStrip, h1 = min(H, h0 + kStrip);
     walk_strip(smem_f + j * plane, PW, v, h0, h1, [&](int h, const float (&win)[3][3]) {
       float acc = 0.f;
 #pragma unroll
       for (int k = 0; k < 9; ++k) acc = fmaf(w[k], win[k / 3][k % 3], acc);
-      yp[(size_t)h * W + v] = f2bf(acc);
+      put_map(yp + (size_t)h * W + v, acc);
     });
   }
 }
 
-hipError_t launch_mix_fwd_planes_bf16(const uint16_t* z, const float* w9, uint16_t* y, int B,
-                                      int C, int H, int W, hipStream_t st) {
+template <typename TM>
+hipError_t launch_mix_fwd_planes(const TM* z, const float* w9, TM* y, int B, int C, int H, int W,
+                                 hipStream_t st) {
   const int sp = mix_planes_together(H, W);
   const size_t lds = (size_t)sp * (H + 2) * (W + 2) * sizeof(float);
   if (lds > 64 * 1024) return hipErrorInvalidValue;
   const int planes = B * C;
-  hipLaunchKernelGGL(k_mix_fwd_planes_bf16, dim3((planes + sp - 1) / sp), dim3(kThreads),
+  hipLaunchKernelGGL(k_mix_fwd_planes<TM>, dim3((planes + sp - 1) / sp), dim3(kThreads),
                      (unsigned)lds, st, z, w9, y, C, H, W, planes);
   return hipGetLastError();
+}
+
+hipError_t launch_mix_fwd_planes_bf16(const uint16_t* z, const float* w9, uint16_t* y, int B,
+                                      int C, int H, int W, hipStream_t st) {
+  return launch_mix_fwd_planes<uint16_t>(z, w9, y, B, C, H, W, st);
+}
+
+hipError_t launch_mix_fwd_planes_f32(const float* z, const float* w9, float* y, int B, int C,
+                                     int H, int W, hipStream_t st) {
+  return launch_mix_fwd_planes<float>(z, w9, y, B, C, H, W, st);
 }
 
 size_t mix_planes_lds_bytes(int H, int W) {
@@ -468,15 +516,26 @@ size_t mix_planes_lds_bytes(int H, int W) {
 
 int mix_planes_per_group(int B) { return B < 8 ? B : 8; }
 
-hipError_t launch_mix_bwd_planes_bf16(const uint16_t* dy, const uint16_t* z, const float* w9,
-                                      uint16_t* g, double* partW, int B, int C, int H, int W,
-                                      hipStream_t st) {
+template <typename TM>
+hipError_t launch_mix_bwd_planes(const TM* dy, const TM* z, const float* w9, TM* g, double* partW,
+                                 int B, int C, int H, int W, hipStream_t st) {
   const size_t lds = mix_planes_lds_bytes(H, W);
   if (lds > 64 * 1024) return hipErrorInvalidValue;
   const int pb = mix_planes_per_group(B);
-  hipLaunchKernelGGL(k_mix_bwd_planes_bf16, dim3(C, (B + pb - 1) / pb), dim3(kThreads),
+  hipLaunchKernelGGL(k_mix_bwd_planes<TM>, dim3(C, (B + pb - 1) / pb), dim3(kThreads),
                      (unsigned)lds, st, dy, z, w9, g, partW, B, C, H, W, pb);
   return hipGetLastError();
+}
+
+hipError_t launch_mix_bwd_planes_bf16(const uint16_t* dy, const uint16_t* z, const float* w9,
+                                      uint16_t* g, double* partW, int B, int C, int H, int W,
+                                      hipStream_t st) {
+  return launch_mix_bwd_planes<uint16_t>(dy, z, w9, g, partW, B, C, H, W, st);
+}
+
+hipError_t launch_mix_bwd_planes_f32(const float* dy, const float* z, const float* w9, float* g,
+                                     double* partW, int B, int C, int H, int W, hipStream_t st) {
+  return launch_mix_bwd_planes<float>(dy, z, w9, g, partW, B, C, H, W, st);
 }
 
 }  // namespace wbmm

@@ -316,8 +316,13 @@ static bool plan_bwd(Geo& g, const BwdRequest& r) {
 
 namespace {
 struct BwdWs {
-  size_t partT, partW, partTs, dz, total;
+  size_t partT, partW, partTs, dz, mixp, total;
 };
+// Window mode with the mix on fp32 NCHW maps: the mix's data and weight gradients come from one
+// plane-staged pass (G, and dWmix partials per group of planes) when its planes fit in LDS.
+bool mix_planes_route(const Geo& g, const BwdRequest& r) {
+  return r.mixw && !g.image_mode && r.layout == 0 && mix_planes_lds_bytes(r.H, r.W) <= 64 * 1024;
+}
 BwdWs bwd_ws_layout(const Geo& g, const BwdRequest& r) {
   auto al = [](size_t v) { return (v + 255) / 256 * 256; };
   BwdWs w{};
@@ -327,7 +332,9 @@ BwdWs bwd_ws_layout(const Geo& g, const BwdRequest& r) {
   const size_t ls = g.s ? (size_t)(2 * g.s - 1) * (2 * g.s - 1) : 0;
   w.dz = w.partTs + al((size_t)g.C * g.col_groups * ls * sizeof(double));
   const bool need_dz = r.mixw && !g.image_mode;
-  w.total = w.dz + (need_dz ? al((size_t)r.B * r.C * r.H * r.W * sizeof(float)) : 0);
+  w.mixp = w.dz + (need_dz ? al((size_t)r.B * r.C * r.H * r.W * sizeof(float)) : 0);
+  const int pb = mix_planes_per_group(r.B);
+  w.total = w.mixp + (mix_planes_route(g, r) ? al((size_t)r.C * ((r.B + pb - 1) / pb) * 9 * 8) : 0);
   return w;
 }
 }  // namespace
@@ -340,6 +347,7 @@ bool backward_plan_ok(const BwdRequest& r) {
 size_t backward_workspace(const BwdRequest& r) {
   Geo g;
   if (!plan_bwd(g, r)) return 0;
+  if (repack_backward_ok(r)) return repack_backward_workspace(r);
   const size_t generic = bwd_ws_layout(g, r).total;
   const size_t fast = fast_backward_ok(r) ? fast_backward_workspace(r) : 0;
   return generic > fast ? generic : fast;
@@ -347,6 +355,7 @@ size_t backward_workspace(const BwdRequest& r) {
 
 hipError_t launch_backward(const BwdRequest& r, hipStream_t st) {
   if (fast_backward_ok(r)) return launch_backward_fast(r, st);  // folds a sub-table when w = 2s
+  if (repack_backward_ok(r)) return launch_backward_repacked(r, st);  // offset grid, w = 14
   BwdArgs a{};
   if (!plan_bwd(a.g, r)) return hipErrorInvalidValue;
   const BwdWs wl = bwd_ws_layout(a.g, r);
@@ -370,11 +379,23 @@ hipError_t launch_backward(const BwdRequest& r, hipStream_t st) {
   hipError_t e = hipSuccess;
   if (mix && !a.g.image_mode) {
     float* dz = (float*)(ws + wl.dz);
-    e = launch_mix_bwd_data(r.dy, r.mixw, dz, r.B, r.C, r.H, r.W, r.layout, st);
-    if (e != hipSuccess) return e;
-    if (r.dmixw) {
-      e = launch_mix_bwd_weight(r.dy, r.zsaved, r.dmixw, r.B, r.C, r.H, r.W, r.layout, st);
+    if (mix_planes_route(a.g, r)) {
+      double* partM = (double*)(ws + wl.mixp);
+      e = launch_mix_bwd_planes_f32(r.dy, r.dmixw ? r.zsaved : nullptr, r.mixw, dz, partM, r.B,
+                                    r.C, r.H, r.W, st);
       if (e != hipSuccess) return e;
+      if (r.dmixw) {
+        const int pb = mix_planes_per_group(r.B);
+        e = launch_bwd_reduce(nullptr, partM, (r.B + pb - 1) / pb, r.C, 0, nullptr, r.dmixw, st);
+        if (e != hipSuccess) return e;
+      }
+    } else {
+      e = launch_mix_bwd_data(r.dy, r.mixw, dz, r.B, r.C, r.H, r.W, r.layout, st);
+      if (e != hipSuccess) return e;
+      if (r.dmixw) {
+        e = launch_mix_bwd_weight(r.dy, r.zsaved, r.dmixw, r.B, r.C, r.H, r.W, r.layout, st);
+        if (e != hipSuccess) return e;
+      }
     }
     a.gsrc = dz;
     a.mix_here = 0;

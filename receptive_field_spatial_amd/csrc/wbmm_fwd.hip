@@ -151,6 +151,7 @@ static bool fast_bf16_mix_ok(const FwdRequest& r) {
 }
 
 size_t forward_workspace(const FwdRequest& r) {
+  if (repack_forward_ok(r)) return repack_forward_workspace(r);
   if (fast_bf16_mix_ok(r)) return r.zsave ? 0 : (size_t)r.B * r.C * r.H * r.W * 2;
   Geo g;
   if (!plan_fwd(g, r)) return 0;
@@ -163,6 +164,7 @@ size_t forward_workspace(const FwdRequest& r) {
 hipError_t launch_forward(const FwdRequest& r, hipStream_t st) {
   if (fast_forward_ok(r)) return launch_forward_fast(r, st);  // folds a sub-table when w = 2s
   if (!r.Tsub && fast_bf16_forward_ok(r)) return launch_forward_fast_bf16(r, st);
+  if (repack_forward_ok(r)) return launch_forward_repacked(r, st);  // offset grid, w = 14
   if (fast_bf16_mix_ok(r)) {
     FwdRequest q = r;
     uint16_t* zb = (uint16_t*)(r.zsave ? r.zsave : r.ws);
@@ -206,9 +208,12 @@ hipError_t launch_forward(const FwdRequest& r, hipStream_t st) {
   else if (r.in_bf16) e = cached ? launch_fwd_tiles<uint16_t, 1>(a, st) : launch_fwd_tiles<uint16_t, 0>(a, st);
   else e = cached ? launch_fwd_tiles<float, 1>(a, st) : launch_fwd_tiles<float, 0>(a, st);
   if (e != hipSuccess) return e;
-  if (!a.g.image_mode && mix)
+  if (!a.g.image_mode && mix) {
+    if (!r.out_bf16 && r.layout == 0 && mix_planes_lds_bytes(r.H, r.W) <= 64 * 1024)
+      return launch_mix_fwd_planes_f32(zbuf, r.mixw, (float*)r.y, r.B, r.C, r.H, r.W, st);
     e = launch_mix_fwd(zbuf, r.mixw, r.y, r.out_bf16, r.B, r.C, r.H, r.W, r.layout, st,
                        (r.zsave && r.out_bf16) ? (uint16_t*)r.zsave : nullptr);
+  }
   return e;
 }
 

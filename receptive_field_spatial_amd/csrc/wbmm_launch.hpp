@@ -63,6 +63,17 @@ hipError_t launch_forward_fast(const FwdRequest& r, hipStream_t st);
 bool fast_backward_ok(const BwdRequest& r);
 size_t fast_backward_workspace(const BwdRequest& r);
 hipError_t launch_backward_fast(const BwdRequest& r, hipStream_t st);
+// Per-image element offsets of the fast kernels stay in 32 bits.
+bool offsets_fit(int C, int H, int W);
+
+// Offset window grids (w = 14, NCHW, fp32 table path, no sub-table) on the fast kernels: the
+// grid's windows are gathered into whole 28x28 images in the workspace and the results put back.
+bool repack_forward_ok(const FwdRequest& r);
+size_t repack_forward_workspace(const FwdRequest& r);
+hipError_t launch_forward_repacked(const FwdRequest& r, hipStream_t st);
+bool repack_backward_ok(const BwdRequest& r);
+size_t repack_backward_workspace(const BwdRequest& r);
+hipError_t launch_backward_repacked(const BwdRequest& r, hipStream_t st);
 
 // Fast bf16 forwards for NCHW table input, bf16 output, no mix: w = 14 on 28x28 and 56x56
 // images, w = 7 and w = 28 on 56x56 images.
@@ -116,6 +127,13 @@ int mix_planes_per_group(int B);
 hipError_t launch_mix_bwd_planes_bf16(const uint16_t* dy, const uint16_t* z, const float* w9,
                                       uint16_t* g, double* partW, int B, int C, int H, int W,
                                       hipStream_t st);
+// The same plane-staged mix passes on fp32 NCHW maps (both need mix_planes_lds_bytes(H, W) and
+// (H + 2) (W + 2) 4 bytes per staged plane within 64 KB; they return hipErrorInvalidValue else).
+size_t mix_planes_lds_bytes(int H, int W);
+hipError_t launch_mix_fwd_planes_f32(const float* z, const float* w9, float* y, int B, int C,
+                                     int H, int W, hipStream_t st);
+hipError_t launch_mix_bwd_planes_f32(const float* dy, const float* z, const float* w9, float* g,
+                                     double* partW, int B, int C, int H, int W, hipStream_t st);
 
 // Matrix-core peak probe (measurement aid): flops of one launch, and the launch.
 double probe_mfma_flops(int bf16, int blocks, int iters);

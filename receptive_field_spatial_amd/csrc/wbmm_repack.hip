@@ -1,0 +1,240 @@
+// Offset (interleaved) window grids on the fast kernels.
+//
+// WBMM acts on each window of a channel on its own, with that channel's table (WBMM paper, the
+// windowed product and its matrix M built from the table T), so the windows of an offset grid
+// (first window at (-oy, -ox), pixels outside the image zero) can be moved anywhere before the
+// product and moved back after it. This path copies the grid's windows of every channel into
+// whole 28 x 28 images of 2 x 2 windows (w = 14) in the workspace, runs the fast kernels there
+// without the mix, and copies the result back to image coordinates, where the 3 x 3 mix runs
+// on the whole map as its own pass. The backward does the same with the mix's data gradient G
+// and X; the table gradient is a sum over windows, whose zero pixels add nothing.
+//
+// Global window n = b * nW + wy * nwx + wx of image b sits in repacked image q = n / 4 at
+// window slot n % 4 (row-major 2 x 2); windows past B * nW are zero.
+#include "wbmm_device.hpp"
+#include "wbmm_launch.hpp"
+
+namespace wbmm {
+namespace {
+
+constexpr int kW = 14;          // window side of this path
+constexpr int kP = 2 * kW;      // repacked image side
+constexpr int kQ = kP * kP / 4; // float4 per repacked plane
+
+struct RepackGeo {
+  int B, C, H, W, oy, ox, nwx, nW, Bp;
+};
+
+RepackGeo repack_geo(int B, int C, int H, int W, int oy, int ox) {
+  RepackGeo g{};
+  g.B = B;
+  g.C = C;
+  g.H = H;
+  g.W = W;
+  g.oy = oy;
+  g.ox = ox;
+  g.nwx = (W + ox + kW - 1) / kW;
+  g.nW = ((H + oy + kW - 1) / kW) * g.nwx;
+  g.Bp = (int)(((long long)B * g.nW + 3) / 4);
+  return g;
+}
+
+bool repack_fits(int B, int C, int H, int W, int w, int layout, int oy, int ox) {
+  if (w != kW || layout != 0 || (oy == 0 && ox == 0) || B < 1 || C < 1 || H < 1 || W < 1)
+    return false;
+  const long long nW = (long long)((H + oy + kW - 1) / kW) * ((W + ox + kW - 1) / kW);
+  const long long Bp = ((long long)B * nW + 3) / 4;
+  return Bp * C * kQ < (1LL << 31) && (long long)C * H * W < (1LL << 31) &&
+         (long long)B * C < (1LL << 31) && offsets_fit(C, kP, kP);
+}
+
+size_t al256(size_t v) { return (v + 255) / 256 * 256; }
+size_t repacked_bytes(const RepackGeo& g) { return al256((size_t)g.Bp * g.C * kP * kP * 4); }
+bool mix_planes_fit(int H, int W) { return mix_planes_lds_bytes(H, W) <= 64 * 1024; }
+size_t mix_partials_bytes(int B, int C) {
+  const int pb = mix_planes_per_group(B);
+  return al256((size_t)C * ((B + pb - 1) / pb) * 9 * sizeof(double));
+}
+
+// Repacked map <- image map: one float4 of a repacked row per thread (4 pixels, which may lie in
+// two windows); pixels outside the image or past the last window are 0.
+__global__ void __launch_bounds__(256) k_gather_windows(RepackGeo g, const float* __restrict__ src,
+                                                        float* __restrict__ dst) {
+  const int id = blockIdx.x * 256 + threadIdx.x;
+  if (id >= g.Bp * g.C * kQ) return;
+  const int plane = id / kQ, j = id - plane * kQ;
+  const int q = plane / g.C, c = plane - q * g.C;
+  const int py = j / (kP / 4), px0 = (j - py * (kP / 4)) * 4;
+  const int ky = py / kW, y = py - ky * kW;
+  const int nlast = g.B * g.nW;  // 4 Bp < 2^31: window numbers fit in 32 bits
+  float v[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const int px = px0 + e, kx = px / kW, x = px - kx * kW;
+    const int n = 4 * q + 2 * ky + kx;
+    v[e] = 0.f;
+    if (n < nlast) {
+      const int b = n / g.nW, k = n - b * g.nW;
+      const int wy = k / g.nwx, wx = k - wy * g.nwx;
+      const int iy = wy * kW - g.oy + y, ix = wx * kW - g.ox + x;
+      if (iy >= 0 && iy < g.H && ix >= 0 && ix < g.W)
+        v[e] = src[(((size_t)b * g.C + c) * g.H + iy) * g.W + ix];
+    }
+  }
+  *(float4*)(dst + (size_t)id * 4) = make_float4(v[0], v[1], v[2], v[3]);
+}
+
+// Image map <- repacked map: every image pixel lies in exactly one window of the grid. One
+// workgroup per (image, channel) plane; dst2 (may be null) receives a second copy.
+__global__ void __launch_bounds__(256) k_scatter_windows(RepackGeo g, const float* __restrict__ src,
+                                                         float* __restrict__ dst,
+                                                         float* __restrict__ dst2) {
+  const int plane = blockIdx.x;
+  const int b = plane / g.C, c = plane - b * g.C;
+  const int HW = g.H * g.W;
+  const size_t base = (size_t)plane * HW;
+  for (int i = threadIdx.x; i < HW; i += 256) {
+    const int iy = i / g.W, ix = i - iy * g.W;
+    const int wy = (iy + g.oy) / kW, y = iy + g.oy - wy * kW;
+    const int wx = (ix + g.ox) / kW, x = ix + g.ox - wx * kW;
+    const int n = b * g.nW + wy * g.nwx + wx;
+    const int q = n >> 2, k = n & 3;
+    const float v = src[((size_t)q * g.C + c) * (kP * kP) + ((k >> 1) * kW + y) * kP +
+                        (k & 1) * kW + x];
+    dst[base + i] = v;
+    if (dst2) dst2[base + i] = v;
+  }
+}
+
+hipError_t gather(const RepackGeo& g, const float* src, float* dst, hipStream_t st) {
+  const int n = g.Bp * g.C * kQ;
+  hipLaunchKernelGGL(k_gather_windows, dim3((n + 255) / 256), dim3(256), 0, st, g, src, dst);
+  return hipGetLastError();
+}
+
+hipError_t scatter(const RepackGeo& g, const float* src, float* dst, float* dst2, hipStream_t st) {
+  hipLaunchKernelGGL(k_scatter_windows, dim3(g.B * g.C), dim3(256), 0, st, g, src, dst, dst2);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+bool repack_forward_ok(const FwdRequest& r) {
+  return !r.in_bf16 && !r.out_bf16 && r.T && !r.M && !r.Tsub &&
+         repack_fits(r.B, r.C, r.H, r.W, r.w, r.layout, r.oy, r.ox);
+}
+
+// [repacked X] [repacked z] [image-space z: with the mix and no fp32 z_save]
+size_t repack_forward_workspace(const FwdRequest& r) {
+  if (!repack_forward_ok(r)) return 0;
+  const RepackGeo g = repack_geo(r.B, r.C, r.H, r.W, r.oy, r.ox);
+  const bool zb = r.mixw && !r.zsave;
+  return 2 * repacked_bytes(g) + (zb ? al256((size_t)r.B * r.C * r.H * r.W * 4) : 0);
+}
+
+hipError_t launch_forward_repacked(const FwdRequest& r, hipStream_t st) {
+  if (!repack_forward_ok(r)) return hipErrorInvalidValue;
+  const RepackGeo g = repack_geo(r.B, r.C, r.H, r.W, r.oy, r.ox);
+  unsigned char* ws = (unsigned char*)r.ws;
+  float* xr = (float*)ws;
+  float* zr = (float*)(ws + repacked_bytes(g));
+  hipError_t e = gather(g, (const float*)r.x, xr, st);
+  if (e != hipSuccess) return e;
+  FwdRequest q = r;
+  q.B = g.Bp;
+  q.H = q.W = kP;
+  q.oy = q.ox = 0;
+  q.x = xr;
+  q.mixw = nullptr;
+  q.zsave = nullptr;
+  q.y = zr;
+  if (!fast_forward_ok(q)) return hipErrorInvalidValue;
+  e = launch_forward_fast(q, st);
+  if (e != hipSuccess) return e;
+  if (!r.mixw) return scatter(g, zr, (float*)r.y, (float*)r.zsave, st);
+  float* z = r.zsave ? (float*)r.zsave : (float*)(ws + 2 * repacked_bytes(g));
+  e = scatter(g, zr, z, nullptr, st);
+  if (e != hipSuccess) return e;
+  if (mix_planes_fit(r.H, r.W))
+    return launch_mix_fwd_planes_f32(z, r.mixw, (float*)r.y, r.B, r.C, r.H, r.W, st);
+  return launch_mix_fwd(z, r.mixw, r.y, 0, r.B, r.C, r.H, r.W, 0, st);
+}
+
+bool repack_backward_ok(const BwdRequest& r) {
+  return r.T && !r.M && !r.Tsub && repack_fits(r.B, r.C, r.H, r.W, r.w, r.layout, r.oy, r.ox);
+}
+
+namespace {
+BwdRequest repacked_request(const BwdRequest& r, const RepackGeo& g) {
+  BwdRequest q = r;
+  q.B = g.Bp;
+  q.H = q.W = kP;
+  q.oy = q.ox = 0;
+  q.mixw = nullptr;
+  q.zsaved = nullptr;
+  q.dmixw = nullptr;
+  return q;
+}
+}  // namespace
+
+// [fast backward partials] [repacked G] [repacked X] [repacked dX]
+// [with the mix: image-space G, dWmix partials of the plane-staged pass]
+size_t repack_backward_workspace(const BwdRequest& r) {
+  if (!repack_backward_ok(r)) return 0;
+  const RepackGeo g = repack_geo(r.B, r.C, r.H, r.W, r.oy, r.ox);
+  const size_t fast = al256(fast_backward_workspace(repacked_request(r, g)));
+  const size_t mix =
+      r.mixw ? al256((size_t)r.B * r.C * r.H * r.W * 4) + mix_partials_bytes(r.B, r.C) : 0;
+  return fast + 3 * repacked_bytes(g) + mix;
+}
+
+hipError_t launch_backward_repacked(const BwdRequest& r, hipStream_t st) {
+  if (!repack_backward_ok(r)) return hipErrorInvalidValue;
+  const RepackGeo g = repack_geo(r.B, r.C, r.H, r.W, r.oy, r.ox);
+  BwdRequest q = repacked_request(r, g);
+  if (!fast_backward_ok(q)) return hipErrorInvalidValue;
+  unsigned char* ws = (unsigned char*)r.ws;
+  const size_t fast = al256(fast_backward_workspace(q));
+  const size_t rb = repacked_bytes(g);
+  float* gr = (float*)(ws + fast);
+  float* xr = (float*)(ws + fast + rb);
+  float* dxr = (float*)(ws + fast + 2 * rb);
+  const float* gsrc = r.dy;
+  hipError_t e = hipSuccess;
+  if (r.mixw) {  // the mix's data gradient (and its weight gradient) on the whole map
+    float* gz = (float*)(ws + fast + 3 * rb);
+    if (mix_planes_fit(r.H, r.W)) {  // one plane-staged pass: G and per-group dWmix partials
+      double* partW = (double*)(ws + fast + 3 * rb + al256((size_t)r.B * r.C * r.H * r.W * 4));
+      e = launch_mix_bwd_planes_f32(r.dy, r.dmixw ? r.zsaved : nullptr, r.mixw, gz, partW, r.B,
+                                    r.C, r.H, r.W, st);
+      if (e != hipSuccess) return e;
+      if (r.dmixw) {
+        const int pb = mix_planes_per_group(r.B);
+        e = launch_bwd_reduce(nullptr, partW, (r.B + pb - 1) / pb, r.C, 0, nullptr, r.dmixw, st);
+        if (e != hipSuccess) return e;
+      }
+    } else {
+      e = launch_mix_bwd_data(r.dy, r.mixw, gz, r.B, r.C, r.H, r.W, 0, st);
+      if (e != hipSuccess) return e;
+      if (r.dmixw) {
+        e = launch_mix_bwd_weight(r.dy, r.zsaved, r.dmixw, r.B, r.C, r.H, r.W, 0, st);
+        if (e != hipSuccess) return e;
+      }
+    }
+    gsrc = gz;
+  }
+  if (!r.dx && !r.dT) return hipSuccess;
+  e = gather(g, gsrc, gr, st);
+  if (e != hipSuccess) return e;
+  e = gather(g, r.x, xr, st);
+  if (e != hipSuccess) return e;
+  q.x = xr;
+  q.dy = gr;
+  q.dx = r.dx ? dxr : nullptr;
+  q.ws = ws;
+  e = launch_backward_fast(q, st);
+  if (e != hipSuccess || !r.dx) return e;
+  return scatter(g, dxr, r.dx, nullptr, st);
+}
+
+}  // namespace wbmm

@@ -703,8 +703,11 @@ def test_dwconv_full_size_sampled():
 
 
 # ----------------------------------------------------------------------------- shifted window grid
+# w = 14 with a table runs the repacked fast kernels (a cached matrix, other w: general kernels);
+# B = 5 at 28x28 leaves 45 windows: 12 repacked images, the last with 3 zero windows
 SHIFT_CASES = [(2, 3, 28, 28, 14, 7, 7), (1, 2, 30, 25, 14, 3, 11), (2, 3, 17, 13, 4, 2, 1),
-               (1, 2, 128, 128, 14, 7, 7), (2, 2, 9, 9, 7, 0, 3)]
+               (1, 2, 128, 128, 14, 7, 7), (2, 2, 9, 9, 7, 0, 3), (5, 4, 28, 28, 14, 7, 7),
+               (3, 2, 5, 40, 14, 13, 0)]
 
 
 @pytest.mark.parametrize("B,C,H,W,w,oy,ox", SHIFT_CASES)
@@ -762,6 +765,35 @@ def test_backward_shifted(B, C, H, W, w, oy, ox, mix):
         assert_f32(host(dW), wdW, "dWmix")
     dx2, dT2, _ = R().wbmm_backward_shifted(xd, dyd, w, oy, ox, T=Td, mix_w=Wd, z_saved=zs)
     assert torch.equal(dx, dx2) and torch.equal(dT, dT2)
+
+
+def test_shifted_step_full_size_sampled_channels():
+    """The interleaved training step at its full size (B=64, C=192, 28x28, w=14, offset (7, 7),
+    mix) in the launch configuration the benchmark times: y, z, dx, dT and dWmix of sampled
+    channels against the oracle run on those channels alone (the product and the mix act on each
+    channel by itself)."""
+    B, C, H, W, w, o = 64, 192, 28, 28, 14, 7
+    say("shifted step full size")
+    x = synth.normal_f32((B, C, H, W), 1.0, seed=260)
+    T = synth.normal_f32((C, 2 * w - 1, 2 * w - 1), 0.05, seed=261)
+    dy = synth.normal_f32((B, C, H, W), 1.0, seed=262)
+    Wm = synth.normal_f32((C, 3, 3), 0.1, seed=263)
+    xd, Td, dyd, Wd = dev(x), dev(T), dev(dy), dev(Wm)
+    zs = torch.empty_like(xd)
+    y = R().wbmm_forward_shifted(xd, w, o, o, T=Td, mix_w=Wd, z_save=zs)
+    dx, dT, dW = R().wbmm_backward_shifted(xd, dyd, w, o, o, T=Td, mix_w=Wd, z_saved=zs)
+    y, zs, dx, dT, dW = host(y), host(zs), host(dx), host(dT), host(dW)
+    for c in (0, 77, 191):
+        xc = x[:, c:c + 1].astype(np.float64)
+        wy, wz = O.layer_forward_shifted(xc, w, o, o, T=T[c:c + 1], Wmix=Wm[c:c + 1])
+        assert_f32(y[:, c:c + 1], wy, f"y c={c}")
+        assert_f32(zs[:, c:c + 1], wz, f"z c={c}")
+        wdx, wdT, wdW = O.layer_backward_shifted(xc, dy[:, c:c + 1].astype(np.float64), w, o, o,
+                                                 T=T[c:c + 1], Wmix=Wm[c:c + 1],
+                                                 z=zs[:, c:c + 1].astype(np.float64))
+        assert_f32(dx[:, c:c + 1], wdx, f"dx c={c}")
+        assert_f32(dT[c:c + 1], wdT, f"dT c={c}")
+        assert_f32(dW[c:c + 1], wdW, f"dWmix c={c}")
 
 
 def test_shifted_zero_offset_is_the_plain_call():
