@@ -56,64 +56,108 @@ size_t mix_partials_bytes(int B, int C) {
   return al256((size_t)C * ((B + pb - 1) / pb) * 9 * sizeof(double));
 }
 
-// Repacked map <- image map: one float4 of a repacked row per thread (4 pixels, which may lie in
-// two windows); pixels outside the image or past the last window are 0.
+// Repacked map <- image map: workgroup (qg, c) takes repacked planes (q, c) for
+// q = kGQ qg .. kGQ qg + kGQ - 1 (consecutive windows of a channel: their source rows share cache
+// lines). Each plane's 4 windows are located once (uniform); each thread then loads one float4
+// of a repacked row (4 pixels, which may lie in two windows) of every plane, all loads in flight
+// before the stores. Pixels outside the image or past the last window are 0.
+constexpr int kGQ = 4;
+
 __global__ void __launch_bounds__(256) k_gather_windows(RepackGeo g, const float* __restrict__ src,
                                                         float* __restrict__ dst) {
-  const int id = blockIdx.x * 256 + threadIdx.x;
-  if (id >= g.Bp * g.C * kQ) return;
-  const int plane = id / kQ, j = id - plane * kQ;
-  const int q = plane / g.C, c = plane - q * g.C;
+  const int qg = blockIdx.x / g.C, c = blockIdx.x - qg * g.C;
+  const int nlast = g.B * g.nW;  // 4 Bp < 2^31: window numbers fit in 32 bits
+  const int j = threadIdx.x;
   const int py = j / (kP / 4), px0 = (j - py * (kP / 4)) * 4;
   const int ky = py / kW, y = py - ky * kW;
-  const int nlast = g.B * g.nW;  // 4 Bp < 2^31: window numbers fit in 32 bits
-  float v[4];
+  float v[kGQ][4];
 #pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    const int px = px0 + e, kx = px / kW, x = px - kx * kW;
-    const int n = 4 * q + 2 * ky + kx;
-    v[e] = 0.f;
-    if (n < nlast) {
-      const int b = n / g.nW, k = n - b * g.nW;
-      const int wy = k / g.nwx, wx = k - wy * g.nwx;
-      const int iy = wy * kW - g.oy + y, ix = wx * kW - g.ox + x;
-      if (iy >= 0 && iy < g.H && ix >= 0 && ix < g.W)
-        v[e] = src[(((size_t)b * g.C + c) * g.H + iy) * g.W + ix];
+  for (int i = 0; i < kGQ; ++i) {
+    const int q = kGQ * qg + i;
+    // the row's two window slots 2 ky (left) and 2 ky + 1 (right): source plane offset (-1: past
+    // the last window) and the image position of the window's first pixel
+    long long sb[2];
+    int oy2[2], ox2[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int n = 4 * q + 2 * ky + h;
+      const int b = n / g.nW, kk = n - b * g.nW;
+      const int wy = kk / g.nwx, wx = kk - wy * g.nwx;
+      sb[h] = (q < g.Bp && n < nlast) ? ((long long)b * g.C + c) * g.H * g.W : -1;
+      oy2[h] = wy * kW - g.oy + y;
+      ox2[h] = wx * kW - g.ox;
+    }
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int px = px0 + e;
+      const int h = px >= kW ? 1 : 0;
+      const long long base = h ? sb[1] : sb[0];
+      const int iy = h ? oy2[1] : oy2[0], ix = (h ? ox2[1] : ox2[0]) + px - h * kW;
+      v[i][e] = 0.f;
+      if (j < kQ && base >= 0 && iy >= 0 && iy < g.H && ix >= 0 && ix < g.W)
+        v[i][e] = src[(size_t)base + (size_t)iy * g.W + ix];
     }
   }
-  *(float4*)(dst + (size_t)id * 4) = make_float4(v[0], v[1], v[2], v[3]);
+  if (j >= kQ) return;
+#pragma unroll
+  for (int i = 0; i < kGQ; ++i) {
+    const int q = kGQ * qg + i;
+    if (q < g.Bp)
+      *(float4*)(dst + (((size_t)q * g.C + c) * kQ + j) * 4) =
+          make_float4(v[i][0], v[i][1], v[i][2], v[i][3]);
+  }
 }
 
-// Image map <- repacked map: every image pixel lies in exactly one window of the grid. One
-// workgroup per (image, channel) plane; dst2 (may be null) receives a second copy.
+// Image map <- repacked map: every image pixel lies in exactly one window of the grid. Workgroup
+// (bg, c) takes the planes (b, c) for b = kSB bg .. kSB bg + kSB - 1, a row by 32 lanes (W <= 32)
+// or by a wave, a pixel's kSB planes loaded before they are stored. dst2 (may be null) receives
+// a second copy.
+constexpr int kSB = 4;
+
 __global__ void __launch_bounds__(256) k_scatter_windows(RepackGeo g, const float* __restrict__ src,
                                                          float* __restrict__ dst,
                                                          float* __restrict__ dst2) {
-  const int plane = blockIdx.x;
-  const int b = plane / g.C, c = plane - b * g.C;
-  const int HW = g.H * g.W;
-  const size_t base = (size_t)plane * HW;
-  for (int i = threadIdx.x; i < HW; i += 256) {
-    const int iy = i / g.W, ix = i - iy * g.W;
+  const int bg = blockIdx.x / g.C, c = blockIdx.x - bg * g.C;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const bool half = g.W <= 32;
+  const int rows_per_pass = half ? 8 : 4, step = half ? 32 : 64;
+  const int r0 = half ? 2 * wave + (lane >> 5) : wave, l0 = half ? (lane & 31) : lane;
+  for (int iy = r0; iy < g.H; iy += rows_per_pass) {
     const int wy = (iy + g.oy) / kW, y = iy + g.oy - wy * kW;
-    const int wx = (ix + g.ox) / kW, x = ix + g.ox - wx * kW;
-    const int n = b * g.nW + wy * g.nwx + wx;
-    const int q = n >> 2, k = n & 3;
-    const float v = src[((size_t)q * g.C + c) * (kP * kP) + ((k >> 1) * kW + y) * kP +
-                        (k & 1) * kW + x];
-    dst[base + i] = v;
-    if (dst2) dst2[base + i] = v;
+    for (int ix = l0; ix < g.W; ix += step) {
+      const int wx = (ix + g.ox) / kW, x = ix + g.ox - wx * kW;
+      float v[kSB];
+#pragma unroll
+      for (int i = 0; i < kSB; ++i) {
+        const int b = kSB * bg + i;
+        const int n = b * g.nW + wy * g.nwx + wx;
+        const int q = n >> 2, k = n & 3;
+        v[i] = b < g.B ? src[((size_t)q * g.C + c) * (kP * kP) + ((k >> 1) * kW + y) * kP +
+                             (k & 1) * kW + x]
+                       : 0.f;
+      }
+#pragma unroll
+      for (int i = 0; i < kSB; ++i) {
+        const int b = kSB * bg + i;
+        if (b >= g.B) break;
+        const size_t o = (((size_t)b * g.C + c) * g.H + iy) * g.W + ix;
+        dst[o] = v[i];
+        if (dst2) dst2[o] = v[i];
+      }
+    }
   }
 }
 
 hipError_t gather(const RepackGeo& g, const float* src, float* dst, hipStream_t st) {
-  const int n = g.Bp * g.C * kQ;
-  hipLaunchKernelGGL(k_gather_windows, dim3((n + 255) / 256), dim3(256), 0, st, g, src, dst);
+  static_assert(kQ <= 256, "a repacked row's float4s per thread");
+  const int groups = (g.Bp + kGQ - 1) / kGQ;
+  hipLaunchKernelGGL(k_gather_windows, dim3(groups * g.C), dim3(256), 0, st, g, src, dst);
   return hipGetLastError();
 }
 
 hipError_t scatter(const RepackGeo& g, const float* src, float* dst, float* dst2, hipStream_t st) {
-  hipLaunchKernelGGL(k_scatter_windows, dim3(g.B * g.C), dim3(256), 0, st, g, src, dst, dst2);
+  const int groups = (g.B + kSB - 1) / kSB;
+  hipLaunchKernelGGL(k_scatter_windows, dim3(groups * g.C), dim3(256), 0, st, g, src, dst, dst2);
   return hipGetLastError();
 }
 
