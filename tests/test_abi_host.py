@@ -224,6 +224,25 @@ def test_shifted_validation(lib):
     assert lib.wbmm_backward_shifted_workspace_bytes(2, 3, 28, 28, 14, 7, 7, 0, 0) > 0
 
 
+def test_shifted_workspace_covers_the_repacked_maps(lib):
+    """w = 14 offset grids on NCHW fp32 maps run on whole 28x28 images of 2x2 windows: B=64 at
+    28x28 with offset (7, 7) has 9 windows per image, 576 windows = 144 repacked images. The
+    forward holds repacked X and z (and the image-space z without a z_save buffer, with the mix);
+    the backward repacked G, X and dX, and with the mix the image-space G."""
+    B, C = 64, 192
+    rep = 144 * C * 28 * 28 * 4
+    img = B * C * 28 * 28 * 4
+    fwd = lib.wbmm_forward_shifted_workspace_bytes(B, C, 28, 28, 14, 7, 7, 0, 0, 0)
+    assert fwd >= 2 * rep
+    assert lib.wbmm_forward_shifted_workspace_bytes(B, C, 28, 28, 14, 7, 7, 0, 1, 0) >= fwd + img
+    bwd = lib.wbmm_backward_shifted_workspace_bytes(B, C, 28, 28, 14, 7, 7, 0, 0)
+    assert bwd >= 3 * rep
+    assert lib.wbmm_backward_shifted_workspace_bytes(B, C, 28, 28, 14, 7, 7, 0, 1) >= bwd + img
+    # a partial last repacked image: 5 images x 9 windows = 45 windows -> 12 repacked images
+    assert lib.wbmm_backward_shifted_workspace_bytes(5, 2, 28, 28, 14, 7, 7, 0, 0) >= \
+        3 * 12 * 2 * 28 * 28 * 4
+
+
 def test_backward_bf16_validation(lib):
     """bf16 backward: w = 14 on NCHW 28² / 56² only, mix and z_saved together, workspace needed."""
     def call(B=2, C=3, H=28, W=28, w=14, layout=0, mix=None, z=None, dx=0x500000, ws=0x900000,
