@@ -66,8 +66,9 @@ hipError_t launch_backward_fast(const BwdRequest& r, hipStream_t st);
 // Per-image element offsets of the fast kernels stay in 32 bits.
 bool offsets_fit(int C, int H, int W);
 
-// Offset window grids (w = 14, NCHW, fp32 table path, no sub-table) on the fast kernels: the
-// grid's windows are gathered into whole 28x28 images in the workspace and the results put back.
+// Offset window grids (w = 14, NCHW, table input, no sub-table; fp32 maps, or bf16 maps without
+// the mix in the forward) on the fast kernels: the grid's windows are gathered into whole 28x28
+// images in the workspace and the results put back.
 bool repack_forward_ok(const FwdRequest& r);
 size_t repack_forward_workspace(const FwdRequest& r);
 hipError_t launch_forward_repacked(const FwdRequest& r, hipStream_t st);

@@ -5,7 +5,8 @@
 // (first window at (-oy, -ox), pixels outside the image zero) can be moved anywhere before the
 // product and moved back after it. This path copies the grid's windows of every channel into
 // whole 28 x 28 images of 2 x 2 windows (w = 14) in the workspace, runs the fast kernels there
-// without the mix, and copies the result back to image coordinates, where the 3 x 3 mix runs
+// without the mix (fp32 maps; bf16 maps without the mix go to the fast bf16 forward), and
+// copies the result back to image coordinates, where the 3 x 3 mix runs
 // on the whole map as its own pass. The backward does the same with the mix's data gradient G
 // and X; the table gradient is a sum over windows, whose zero pixels add nothing.
 //
@@ -49,7 +50,17 @@ bool repack_fits(int B, int C, int H, int W, int w, int layout, int oy, int ox) 
 }
 
 size_t al256(size_t v) { return (v + 255) / 256 * 256; }
-size_t repacked_bytes(const RepackGeo& g) { return al256((size_t)g.Bp * g.C * kP * kP * 4); }
+size_t repacked_bytes(const RepackGeo& g, size_t esz = 4) {
+  return al256((size_t)g.Bp * g.C * kP * kP * esz);
+}
+
+// four map elements as one store: float4 (fp32) or 4 x 16 bits (bf16)
+__device__ __forceinline__ void put4(float* p, const float (&v)[4]) {
+  *(float4*)p = make_float4(v[0], v[1], v[2], v[3]);
+}
+__device__ __forceinline__ void put4(uint16_t* p, const uint16_t (&v)[4]) {
+  *(uint2*)p = make_uint2(v[0] | ((uint32_t)v[1] << 16), v[2] | ((uint32_t)v[3] << 16));
+}
 bool mix_planes_fit(int H, int W) { return mix_planes_lds_bytes(H, W) <= 64 * 1024; }
 size_t mix_partials_bytes(int B, int C) {
   const int pb = mix_planes_per_group(B);
@@ -63,14 +74,15 @@ size_t mix_partials_bytes(int B, int C) {
 // before the stores. Pixels outside the image or past the last window are 0.
 constexpr int kGQ = 4;
 
-__global__ void __launch_bounds__(256) k_gather_windows(RepackGeo g, const float* __restrict__ src,
-                                                        float* __restrict__ dst) {
+template <typename TE>
+__global__ void __launch_bounds__(256) k_gather_windows(RepackGeo g, const TE* __restrict__ src,
+                                                        TE* __restrict__ dst) {
   const int qg = blockIdx.x / g.C, c = blockIdx.x - qg * g.C;
   const int nlast = g.B * g.nW;  // 4 Bp < 2^31: window numbers fit in 32 bits
   const int j = threadIdx.x;
   const int py = j / (kP / 4), px0 = (j - py * (kP / 4)) * 4;
   const int ky = py / kW, y = py - ky * kW;
-  float v[kGQ][4];
+  TE v[kGQ][4];
 #pragma unroll
   for (int i = 0; i < kGQ; ++i) {
     const int q = kGQ * qg + i;
@@ -93,7 +105,7 @@ __global__ void __launch_bounds__(256) k_gather_windows(RepackGeo g, const float
       const int h = px >= kW ? 1 : 0;
       const long long base = h ? sb[1] : sb[0];
       const int iy = h ? oy2[1] : oy2[0], ix = (h ? ox2[1] : ox2[0]) + px - h * kW;
-      v[i][e] = 0.f;
+      v[i][e] = TE(0);  // +0 in both types
       if (j < kQ && base >= 0 && iy >= 0 && iy < g.H && ix >= 0 && ix < g.W)
         v[i][e] = src[(size_t)base + (size_t)iy * g.W + ix];
     }
@@ -102,9 +114,7 @@ __global__ void __launch_bounds__(256) k_gather_windows(RepackGeo g, const float
 #pragma unroll
   for (int i = 0; i < kGQ; ++i) {
     const int q = kGQ * qg + i;
-    if (q < g.Bp)
-      *(float4*)(dst + (((size_t)q * g.C + c) * kQ + j) * 4) =
-          make_float4(v[i][0], v[i][1], v[i][2], v[i][3]);
+    if (q < g.Bp) put4(dst + (((size_t)q * g.C + c) * kQ + j) * 4, v[i]);
   }
 }
 
@@ -114,9 +124,10 @@ __global__ void __launch_bounds__(256) k_gather_windows(RepackGeo g, const float
 // a second copy.
 constexpr int kSB = 4;
 
-__global__ void __launch_bounds__(256) k_scatter_windows(RepackGeo g, const float* __restrict__ src,
-                                                         float* __restrict__ dst,
-                                                         float* __restrict__ dst2) {
+template <typename TE>
+__global__ void __launch_bounds__(256) k_scatter_windows(RepackGeo g, const TE* __restrict__ src,
+                                                         TE* __restrict__ dst,
+                                                         TE* __restrict__ dst2) {
   const int bg = blockIdx.x / g.C, c = blockIdx.x - bg * g.C;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const bool half = g.W <= 32;
@@ -126,7 +137,7 @@ __global__ void __launch_bounds__(256) k_scatter_windows(RepackGeo g, const floa
     const int wy = (iy + g.oy) / kW, y = iy + g.oy - wy * kW;
     for (int ix = l0; ix < g.W; ix += step) {
       const int wx = (ix + g.ox) / kW, x = ix + g.ox - wx * kW;
-      float v[kSB];
+      TE v[kSB];
 #pragma unroll
       for (int i = 0; i < kSB; ++i) {
         const int b = kSB * bg + i;
@@ -134,7 +145,7 @@ __global__ void __launch_bounds__(256) k_scatter_windows(RepackGeo g, const floa
         const int q = n >> 2, k = n & 3;
         v[i] = b < g.B ? src[((size_t)q * g.C + c) * (kP * kP) + ((k >> 1) * kW + y) * kP +
                              (k & 1) * kW + x]
-                       : 0.f;
+                       : TE(0);
       }
 #pragma unroll
       for (int i = 0; i < kSB; ++i) {
@@ -148,23 +159,27 @@ __global__ void __launch_bounds__(256) k_scatter_windows(RepackGeo g, const floa
   }
 }
 
-hipError_t gather(const RepackGeo& g, const float* src, float* dst, hipStream_t st) {
+template <typename TE>
+hipError_t gather(const RepackGeo& g, const TE* src, TE* dst, hipStream_t st) {
   static_assert(kQ <= 256, "a repacked row's float4s per thread");
   const int groups = (g.Bp + kGQ - 1) / kGQ;
-  hipLaunchKernelGGL(k_gather_windows, dim3(groups * g.C), dim3(256), 0, st, g, src, dst);
+  hipLaunchKernelGGL(k_gather_windows<TE>, dim3(groups * g.C), dim3(256), 0, st, g, src, dst);
   return hipGetLastError();
 }
 
-hipError_t scatter(const RepackGeo& g, const float* src, float* dst, float* dst2, hipStream_t st) {
+template <typename TE>
+hipError_t scatter(const RepackGeo& g, const TE* src, TE* dst, TE* dst2, hipStream_t st) {
   const int groups = (g.B + kSB - 1) / kSB;
-  hipLaunchKernelGGL(k_scatter_windows, dim3(groups * g.C), dim3(256), 0, st, g, src, dst, dst2);
+  hipLaunchKernelGGL(k_scatter_windows<TE>, dim3(groups * g.C), dim3(256), 0, st, g, src, dst,
+                     dst2);
   return hipGetLastError();
 }
 
 }  // namespace
 
 bool repack_forward_ok(const FwdRequest& r) {
-  return !r.in_bf16 && !r.out_bf16 && r.T && !r.M && !r.Tsub &&
+  const bool f32 = !r.in_bf16 && !r.out_bf16, bf16 = r.in_bf16 && r.out_bf16 && !r.mixw;
+  return (f32 || bf16) && r.T && !r.M && !r.Tsub &&
          repack_fits(r.B, r.C, r.H, r.W, r.w, r.layout, r.oy, r.ox);
 }
 
@@ -173,31 +188,44 @@ size_t repack_forward_workspace(const FwdRequest& r) {
   if (!repack_forward_ok(r)) return 0;
   const RepackGeo g = repack_geo(r.B, r.C, r.H, r.W, r.oy, r.ox);
   const bool zb = r.mixw && !r.zsave;
-  return 2 * repacked_bytes(g) + (zb ? al256((size_t)r.B * r.C * r.H * r.W * 4) : 0);
+  return 2 * repacked_bytes(g, r.in_bf16 ? 2 : 4) +
+         (zb ? al256((size_t)r.B * r.C * r.H * r.W * 4) : 0);
 }
 
 hipError_t launch_forward_repacked(const FwdRequest& r, hipStream_t st) {
   if (!repack_forward_ok(r)) return hipErrorInvalidValue;
   const RepackGeo g = repack_geo(r.B, r.C, r.H, r.W, r.oy, r.ox);
   unsigned char* ws = (unsigned char*)r.ws;
-  float* xr = (float*)ws;
-  float* zr = (float*)(ws + repacked_bytes(g));
-  hipError_t e = gather(g, (const float*)r.x, xr, st);
-  if (e != hipSuccess) return e;
   FwdRequest q = r;
   q.B = g.Bp;
   q.H = q.W = kP;
   q.oy = q.ox = 0;
+  q.zsave = nullptr;
+  if (r.in_bf16) {  // bf16 maps, no mix: the fast bf16 forward on the repacked images
+    uint16_t* xr = (uint16_t*)ws;
+    uint16_t* zr = (uint16_t*)(ws + repacked_bytes(g, 2));
+    q.x = xr;
+    q.y = zr;
+    if (!fast_bf16_forward_ok(q)) return hipErrorInvalidValue;
+    hipError_t e = gather(g, (const uint16_t*)r.x, xr, st);
+    if (e != hipSuccess) return e;
+    e = launch_forward_fast_bf16(q, st);
+    if (e != hipSuccess) return e;
+    return scatter(g, (const uint16_t*)zr, (uint16_t*)r.y, (uint16_t*)r.zsave, st);
+  }
+  float* xr = (float*)ws;
+  float* zr = (float*)(ws + repacked_bytes(g));
+  hipError_t e = gather(g, (const float*)r.x, xr, st);
+  if (e != hipSuccess) return e;
   q.x = xr;
   q.mixw = nullptr;
-  q.zsave = nullptr;
   q.y = zr;
   if (!fast_forward_ok(q)) return hipErrorInvalidValue;
   e = launch_forward_fast(q, st);
   if (e != hipSuccess) return e;
-  if (!r.mixw) return scatter(g, zr, (float*)r.y, (float*)r.zsave, st);
+  if (!r.mixw) return scatter(g, (const float*)zr, (float*)r.y, (float*)r.zsave, st);
   float* z = r.zsave ? (float*)r.zsave : (float*)(ws + 2 * repacked_bytes(g));
-  e = scatter(g, zr, z, nullptr, st);
+  e = scatter(g, (const float*)zr, z, (float*)nullptr, st);
   if (e != hipSuccess) return e;
   if (mix_planes_fit(r.H, r.W))
     return launch_mix_fwd_planes_f32(z, r.mixw, (float*)r.y, r.B, r.C, r.H, r.W, st);
@@ -268,9 +296,9 @@ hipError_t launch_backward_repacked(const BwdRequest& r, hipStream_t st) {
     gsrc = gz;
   }
   if (!r.dx && !r.dT) return hipSuccess;
-  e = gather(g, gsrc, gr, st);
+  e = gather<float>(g, gsrc, gr, st);
   if (e != hipSuccess) return e;
-  e = gather(g, r.x, xr, st);
+  e = gather<float>(g, r.x, xr, st);
   if (e != hipSuccess) return e;
   q.x = xr;
   q.dy = gr;
@@ -278,7 +306,7 @@ hipError_t launch_backward_repacked(const BwdRequest& r, hipStream_t st) {
   q.ws = ws;
   e = launch_backward_fast(q, st);
   if (e != hipSuccess || !r.dx) return e;
-  return scatter(g, dxr, r.dx, nullptr, st);
+  return scatter(g, (const float*)dxr, r.dx, (float*)nullptr, st);
 }
 
 }  // namespace wbmm

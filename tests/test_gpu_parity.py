@@ -730,14 +730,19 @@ def test_forward_shifted(B, C, H, W, w, oy, ox, mix, src):
 
 
 @pytest.mark.parametrize("B,C,H,W,w,oy,ox", [(2, 3, 28, 28, 14, 7, 7), (1, 2, 17, 13, 4, 2, 1),
-                                             (1, 2, 56, 56, 14, 5, 9)])
+                                             (1, 2, 56, 56, 14, 5, 9), (5, 4, 28, 28, 14, 7, 7),
+                                             (3, 2, 5, 40, 14, 13, 0)])
 def test_forward_shifted_bf16(B, C, H, W, w, oy, ox):
+    """bf16 maps on the offset grid (w = 14: repacked windows on the fast bf16 forward); z_save,
+    without the mix, holds y."""
     say(f"forward shifted bf16 B={B} C={C} H={H} W={W} w={w} o=({oy},{ox})")
     x = synth.round_to_bf16(synth.normal_f32((B, C, H, W), 1.0, seed=245))
     T = synth.round_to_bf16(synth.normal_f32((C, 2 * w - 1, 2 * w - 1), 0.05, seed=246))
-    y = R().wbmm_forward_shifted(dev_bf16(x), w, oy, ox, T=dev_bf16(T))
+    zs = torch.empty((B, C, H, W), device="cuda", dtype=torch.bfloat16)
+    y = R().wbmm_forward_shifted(dev_bf16(x), w, oy, ox, T=dev_bf16(T), z_save=zs)
     want = O.wbmm_forward_shifted(x.astype(np.float64), w, oy, ox, T=T)
     assert_bf16(host(y.float()), want, "y")
+    assert torch.equal(zs, y)
 
 
 @pytest.mark.parametrize("B,C,H,W,w,oy,ox", SHIFT_CASES)
