@@ -13,6 +13,7 @@ Prints ONE JSON line on stdout; diagnostics go to stderr.
       NAME: train_w14 (default), train_w14_hier (sub-window fold + dT_sub), train_w14_shift
       (interleaved window grid), train_w14_bf16 / train_w14_bf16_mix (bf16 maps), stage1_w14,
       bf16_w7 / bf16_w14 / bf16_w28, highres_w14, tiny_w7 (see receptive_field_spatial_amd/synth.py)
+  python bench.py --workload stage1_w14 --cached   # forward on M cached in HBM
   python bench.py --copy-calibration        # plain device copy for HBM counter scaling
   python bench.py --fig3-sweep              # WBMM w=7/14/28 vs DW-Std k=5..13, one line each
   python bench.py --summarize-pmc DIR ...   # turn rocprofv3 --pmc output into profiles/ json
@@ -96,26 +97,34 @@ def _code_only(src: str) -> str:
 
 
 # ----------------------------------------------------------------------------- accounting
-def accounting(wl):
+def accounting(wl, cached=False):
     """Algorithmic flops and bytes (the method's minimum), per kernel and per step.
 
-    flops: 2d per output element for the window contraction, 4d for its backward (dX + dT),
-    18 per element for the 3x3 mix and 36 for its backward (data + weight).
+    flops: 2d per element of the window grid for the window contraction (a map whose sides are
+    not multiples of w is computed on the zero-padded grid), 4d for its backward (dX + dT),
+    18 per output element for the 3x3 mix and 36 for its backward (data + weight).
     bytes: every input read once, every output written once, plus the per-channel table (and
     the sub-window table when the fold is on; its gradient in the backward).
     """
     d = wl.w * wl.w
     E = wl.B * wl.C * wl.H * wl.W
+    # the window grid the method computes: the map zero-padded up to whole windows. (The extra
+    # border windows of an interleaved grid are counted as overhead, not work.)
+    Hp = -(-wl.H // wl.w) * wl.w
+    Wp = -(-wl.W // wl.w) * wl.w
+    Eg = wl.B * wl.C * Hp * Wp
     esz = 2 if wl.dtype == "bf16" else 4
     L = (2 * wl.w - 1) ** 2
     tab = wl.C * L * esz
     if wl.s is not None:
         tab += wl.C * (2 * wl.s - 1) ** 2 * esz
-    fwd_flops = E * (2 * d + (18 if wl.mix else 0))
+    if cached or (wl.s is not None and not wl.backward):
+        tab = wl.C * d * d * esz  # the cached (folded) matrices are read instead of the tables
+    fwd_flops = Eg * 2 * d + E * (18 if wl.mix else 0)
     fwd_bytes = E * esz * (2 + (1 if wl.backward else 0)) + tab + (wl.C * 36 if wl.mix else 0)
-    acc = {"E": E, "d": d, "fwd_flops": fwd_flops, "fwd_bytes": fwd_bytes}
+    acc = {"E": E, "E_grid": Eg, "d": d, "fwd_flops": fwd_flops, "fwd_bytes": fwd_bytes}
     if wl.backward:
-        acc["bwd_flops"] = E * (4 * d + (36 if wl.mix else 0))
+        acc["bwd_flops"] = Eg * 4 * d + E * (36 if wl.mix else 0)
         # reads x, dy, z (mix), table; writes dx, dT, dWmix
         acc["bwd_bytes"] = E * esz * (3 + (1 if wl.mix else 0)) + tab + wl.C * L * 4 + \
             (wl.C * 72 if wl.mix else 0)
@@ -124,7 +133,18 @@ def accounting(wl):
 
 
 # ----------------------------------------------------------------------------- CPU baseline
-def cpu_baseline(wl, budget_s: float = 10.0):
+def host_cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_baseline(wl, budget_s: float = 10.0, cached: bool = False):
     """Time the oracle (as it is) on the same step, repeated until ~budget_s of CPU work."""
     import numpy as np
     from threadpoolctl import threadpool_info
@@ -141,7 +161,12 @@ def cpu_baseline(wl, budget_s: float = 10.0):
     t_start = time.perf_counter()
     while True:
         t0 = time.perf_counter()
-        if wl.shift:
+        if cached or (Ts is not None and not wl.backward):  # inference with the cached matrix
+            M = O.build_matrix(T, wl.w)
+            if Ts is not None:
+                M = O.fold_hier(M, Ts, wl.w, wl.s)
+            O.layer_forward(x, wl.w, M=M, Wmix=Wm)
+        elif wl.shift:
             y, z = O.layer_forward_shifted(x, wl.w, wl.shift, wl.shift, T=T, Wmix=Wm)
             if wl.backward:
                 O.layer_backward_shifted(x, dy, wl.w, wl.shift, wl.shift, T=T, Wmix=Wm, z=z)
@@ -158,13 +183,15 @@ def cpu_baseline(wl, budget_s: float = 10.0):
             break
     med = statistics.median(times)
     threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
-    acc = accounting(wl)
+    acc = accounting(wl, cached)
+    what = "fwd+bwd" if wl.backward else "fwd"
     return {
         "value": round(acc["step_flops"] / med / 1e9, 3),
         "unit": "GFLOP/s",
         "cores": threads,
         "kind": "oracle",
-        "sample": f"full {wl.name} step (fwd+bwd, all {wl.C} channels), {len(times)} runs, median "
+        "cpu_model": host_cpu_model(),
+        "sample": f"full {wl.name} step ({what}, all {wl.C} channels), {len(times)} runs, median "
                   f"{med:.3f} s; fp64 numpy/OpenBLAS on {len(os.sched_getaffinity(0))} host CPUs",
     }
 
@@ -266,7 +293,9 @@ def run(args):
 
     R.load_library()
     wl = synth.WORKLOADS[args.workload]
-    acc = accounting(wl)
+    if args.cached and (wl.backward or wl.shift):
+        raise SystemExit("--cached applies to the forward-only workloads on the plain grid")
+    acc = accounting(wl, args.cached)
     dev = torch.device("cuda:0")
     inp = synth.draw_inputs(wl)
     bf16 = wl.dtype == "bf16"
@@ -295,6 +324,8 @@ def run(args):
     hier_train = wl.s is not None and wl.backward  # fold on chip, dT_sub in the backward
     if wl.s is not None and not wl.backward:  # inference: folded M built once and cached
         M = R.wbmm_fold_hier(R.wbmm_build_matrix(T, wl.w), Tsub, wl.w, wl.s)
+    elif args.cached:  # inference caching: M built once from the table, then read every step
+        M = R.wbmm_build_matrix(T, wl.w)
     L = 2 * wl.w - 1
     dT = torch.empty((wl.C, L, L), dtype=torch.float32, device=dev)
     dW = torch.empty((wl.C, 3, 3), dtype=torch.float32, device=dev) if wl.mix else None
@@ -464,6 +495,7 @@ def run(args):
                               "formed on chip from T"),
                    "rotating_batches": nsets},
         "out_elems_per_s": round(acc["E"] / (ms_step / 1e3), 1),
+        "grid_elems_per_s": round(acc["E_grid"] / (ms_step / 1e3), 1),
         "roofline": roof,
     }
     if wl.backward:
@@ -474,7 +506,7 @@ def run(args):
     line["ms_per_step_warm"] = round(warm_ms, 4)
     line["peaks_measured"] = peaks
     if args.cpu_baseline:
-        line["cpu_baseline"] = cpu_baseline(wl, args.cpu_budget)
+        line["cpu_baseline"] = cpu_baseline(wl, args.cpu_budget, args.cached)
     return line
 
 
@@ -654,6 +686,9 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="train_w14")
+    ap.add_argument("--cached", action="store_true",
+                    help="forward-only workloads: read M built once by wbmm_build_matrix "
+                         "(inference caching) instead of forming it on chip from T")
     ap.add_argument("--rotate", type=int, default=4, help="independent batches cycled per step")
     ap.add_argument("--no-cpu-baseline", dest="cpu_baseline", action="store_false")
     ap.add_argument("--cpu-budget", type=float, default=10.0, help="seconds of oracle CPU work")

@@ -137,6 +137,8 @@ def test_forward_tiny_workload(cached):
     (1, 2, 33, 47, 8),
     (2, 2, 20, 21, 10),
     (1, 3, 28, 42, 14),
+    (5, 3, 14, 14, 14),   # fast 14x14 kernel: one unit of 64 images, part empty
+    (3, 2, 56, 56, 14),   # fast 56x56 kernel: last unit part empty
     (2, 2, 30, 30, 15),
     (1, 2, 32, 48, 16),
     (1, 2, 40, 37, 20),   # w > 16: rows split over waves
@@ -186,6 +188,34 @@ def test_forward_f32_28x28_w14_shift_bitwise(B, C, mix):
     W9 = np.zeros((C, 3, 3), np.float32)
     W9[:, 1, 1] = 1.0
     xd = dev(x)
+    z = torch.empty_like(xd)
+    y = R().wbmm_forward(xd, w, T=dev(T), mix_w=dev(W9), z_save=z)
+    assert np.array_equal(host(z), want)
+    assert np.array_equal(host(y), want)
+
+
+@pytest.mark.parametrize("hw,B,C,mix", [(56, 4, 700, False), (56, 5, 300, True),
+                                         (56, 13, 256, True), (14, 70, 600, True),
+                                         (14, 64, 300, False)])
+def test_forward_f32_w14_shift_bitwise_all_channels(hw, B, C, mix):
+    """As the 28x28 case, on the fast fp32 kernels for 56x56 and 14x14 images: one-hot tables at
+    a different offset in every channel (and the identity mix with z_save), so that every
+    channel's output is the input shifted inside each window, bit for bit. With more units than
+    resident workgroups, this checks the units' walk over channels and images at full width."""
+    w = 14
+    say(f"forward f32 {hw}x{hw} shift all channels B={B} C={C} mix={mix}")
+    x = synth.normal_f32((B, C, hw, hw), 1.0, seed=36)
+    dy = (np.arange(C) * 7 + 1) % 27 - 13
+    dx = (np.arange(C) * 3 + 5) % 27 - 13
+    T = np.zeros((C, 27, 27), np.float32)
+    T[np.arange(C), dy + 13, dx + 13] = 1.0
+    want = _window_shift(x, w, dy, dx)
+    xd = dev(x)
+    if not mix:
+        assert np.array_equal(host(R().wbmm_forward(xd, w, T=dev(T))), want)
+        return
+    W9 = np.zeros((C, 3, 3), np.float32)
+    W9[:, 1, 1] = 1.0
     z = torch.empty_like(xd)
     y = R().wbmm_forward(xd, w, T=dev(T), mix_w=dev(W9), z_save=z)
     assert np.array_equal(host(z), want)
@@ -404,6 +434,9 @@ def bwd_case(B, C, H, W, w, *, mix, cached=False, layout="NCHW", seed=0):
     (1, 2, 30, 30, 15, False), (1, 2, 32, 32, 16, True), (1, 2, 100, 100, 14, True),
     (1, 2, 128, 128, 14, True), (2, 2, 128, 120, 14, False),
     (2, 2, 17, 23, 5, False),
+    # the fast fp32 kernels on 56x56 and 14x14 images (ragged batches: last unit part empty)
+    (2, 3, 56, 56, 14, True), (2, 3, 56, 56, 14, False), (5, 3, 56, 56, 14, True),
+    (5, 3, 14, 14, 14, True), (5, 3, 14, 14, 14, False), (70, 2, 14, 14, 14, True),
 ])
 @pytest.mark.parametrize("cached", [False, True])
 def test_backward_shapes(B, C, H, W, w, mix, cached):
@@ -713,54 +746,64 @@ SHIFT_CASES = [(2, 3, 28, 28, 14, 7, 7), (1, 2, 30, 25, 14, 3, 11), (2, 3, 17, 1
 @pytest.mark.parametrize("B,C,H,W,w,oy,ox", SHIFT_CASES)
 @pytest.mark.parametrize("mix", [False, True])
 @pytest.mark.parametrize("src", ["T", "M"])
-def test_forward_shifted(B, C, H, W, w, oy, ox, mix, src):
+@pytest.mark.parametrize("zsave", [True, False])
+def test_forward_shifted(B, C, H, W, w, oy, ox, mix, src, zsave):
     """Interleaved grid (offset windows, zero border pixels) against the oracle: image and window
-    mode, ragged maps, table and cached matrix, with and without the 3x3 mix."""
-    say(f"forward shifted B={B} C={C} H={H} W={W} w={w} o=({oy},{ox}) mix={mix} src={src}")
+    mode, ragged maps, table and cached matrix, with and without the 3x3 mix; without z_save
+    the pre-mix map goes through the workspace."""
+    say(f"forward shifted B={B} C={C} H={H} W={W} w={w} o=({oy},{ox}) mix={mix} src={src} "
+        f"zsave={zsave}")
     x = synth.normal_f32((B, C, H, W), 1.0, seed=240)
     T = synth.normal_f32((C, 2 * w - 1, 2 * w - 1), 0.05, seed=241)
     Wm = synth.normal_f32((C, 3, 3), 0.1, seed=242) if mix else None
     kw = {"T": dev(T)} if src == "T" else {"M": R().wbmm_build_matrix(dev(T), w)}
-    zs = torch.empty((B, C, H, W), device="cuda")
+    zs = torch.empty((B, C, H, W), device="cuda") if zsave else None
     y = R().wbmm_forward_shifted(dev(x), w, oy, ox, mix_w=dev(Wm) if mix else None, z_save=zs,
                                  **kw)
     want_y, want_z = O.layer_forward_shifted(x.astype(np.float64), w, oy, ox, T=T, Wmix=Wm)
     assert_f32(host(y), want_y, "y")
-    assert_f32(host(zs), want_z, "z")
+    if zsave:
+        assert_f32(host(zs), want_z, "z")
 
 
 @pytest.mark.parametrize("B,C,H,W,w,oy,ox", [(2, 3, 28, 28, 14, 7, 7), (1, 2, 17, 13, 4, 2, 1),
                                              (1, 2, 56, 56, 14, 5, 9), (5, 4, 28, 28, 14, 7, 7),
                                              (3, 2, 5, 40, 14, 13, 0)])
-def test_forward_shifted_bf16(B, C, H, W, w, oy, ox):
+@pytest.mark.parametrize("zsave", [True, False])
+def test_forward_shifted_bf16(B, C, H, W, w, oy, ox, zsave):
     """bf16 maps on the offset grid (w = 14: repacked windows on the fast bf16 forward); z_save,
-    without the mix, holds y."""
-    say(f"forward shifted bf16 B={B} C={C} H={H} W={W} w={w} o=({oy},{ox})")
+    without the mix, holds y; without z_save only y is scattered back."""
+    say(f"forward shifted bf16 B={B} C={C} H={H} W={W} w={w} o=({oy},{ox}) zsave={zsave}")
     x = synth.round_to_bf16(synth.normal_f32((B, C, H, W), 1.0, seed=245))
     T = synth.round_to_bf16(synth.normal_f32((C, 2 * w - 1, 2 * w - 1), 0.05, seed=246))
-    zs = torch.empty((B, C, H, W), device="cuda", dtype=torch.bfloat16)
+    zs = torch.empty((B, C, H, W), device="cuda", dtype=torch.bfloat16) if zsave else None
     y = R().wbmm_forward_shifted(dev_bf16(x), w, oy, ox, T=dev_bf16(T), z_save=zs)
     want = O.wbmm_forward_shifted(x.astype(np.float64), w, oy, ox, T=T)
     assert_bf16(host(y.float()), want, "y")
-    assert torch.equal(zs, y)
+    if zsave:
+        assert torch.equal(zs, y)
 
 
 @pytest.mark.parametrize("B,C,H,W,w,oy,ox", SHIFT_CASES)
 @pytest.mark.parametrize("mix", [False, True])
-def test_backward_shifted(B, C, H, W, w, oy, ox, mix):
-    """dx, dT (and dWmix) on the interleaved grid against the oracle; run twice, bitwise equal."""
-    say(f"backward shifted B={B} C={C} H={H} W={W} w={w} o=({oy},{ox}) mix={mix}")
+@pytest.mark.parametrize("src", ["T", "M"])
+def test_backward_shifted(B, C, H, W, w, oy, ox, mix, src):
+    """dx, dT (and dWmix) on the interleaved grid against the oracle, from the table or from a
+    cached matrix (dT is then the gradient of the table M was gathered from); run twice,
+    bitwise equal."""
+    say(f"backward shifted B={B} C={C} H={H} W={W} w={w} o=({oy},{ox}) mix={mix} src={src}")
     x = synth.normal_f32((B, C, H, W), 1.0, seed=250)
     T = synth.normal_f32((C, 2 * w - 1, 2 * w - 1), 0.05, seed=251)
     dy = synth.normal_f32((B, C, H, W), 1.0, seed=252)
     Wm = synth.normal_f32((C, 3, 3), 0.1, seed=253) if mix else None
     xd, Td, dyd = dev(x), dev(T), dev(dy)
+    kw = {"T": Td} if src == "T" else {"M": R().wbmm_build_matrix(Td, w)}
     Wd = dev(Wm) if mix else None
     zs = None
     if mix:
         zs = torch.empty_like(xd)
-        R().wbmm_forward_shifted(xd, w, oy, ox, T=Td, mix_w=Wd, z_save=zs)
-    dx, dT, dW = R().wbmm_backward_shifted(xd, dyd, w, oy, ox, T=Td, mix_w=Wd, z_saved=zs)
+        R().wbmm_forward_shifted(xd, w, oy, ox, mix_w=Wd, z_save=zs, **kw)
+    dx, dT, dW = R().wbmm_backward_shifted(xd, dyd, w, oy, ox, mix_w=Wd, z_saved=zs, **kw)
     z64 = host(zs).astype(np.float64) if mix else None
     wdx, wdT, wdW = O.layer_backward_shifted(x.astype(np.float64), dy.astype(np.float64), w, oy,
                                              ox, T=T, Wmix=Wm, z=z64)
@@ -768,7 +811,7 @@ def test_backward_shifted(B, C, H, W, w, oy, ox, mix):
     assert_f32(host(dT), wdT, "dT")
     if mix:
         assert_f32(host(dW), wdW, "dWmix")
-    dx2, dT2, _ = R().wbmm_backward_shifted(xd, dyd, w, oy, ox, T=Td, mix_w=Wd, z_saved=zs)
+    dx2, dT2, _ = R().wbmm_backward_shifted(xd, dyd, w, oy, ox, mix_w=Wd, z_saved=zs, **kw)
     assert torch.equal(dx, dx2) and torch.equal(dT, dT2)
 
 

@@ -664,3 +664,79 @@ def test_shifted_backward_adjoint_and_fd(oy, ox):
         fd = (np.sum(g * O.wbmm_forward_shifted(x, w, oy, ox, T=Tp)) -
               np.sum(g * O.wbmm_forward_shifted(x, w, oy, ox, T=Tm))) / (2 * eps)
         assert abs(fd - dT[c, i, j]) < 1e-8 * max(1.0, abs(fd))
+
+
+def mix_brute_force(z, Wm):
+    """3x3 depthwise cross-correlation with zero padding 1, pure Python loops."""
+    B, C, H, W = z.shape
+    out = np.zeros_like(z, dtype=np.float64)
+    for b in range(B):
+        for c in range(C):
+            for py in range(H):
+                for px in range(W):
+                    acc = 0.0
+                    for u in range(3):
+                        for t in range(3):
+                            qy, qx = py + u - 1, px + t - 1
+                            if 0 <= qy < H and 0 <= qx < W:
+                                acc += Wm[c, u, t] * z[b, c, qy, qx]
+                    out[b, c, py, px] = acc
+    return out
+
+
+@pytest.mark.parametrize("B,C,H,W,w,oy,ox", [(1, 2, 9, 11, 4, 2, 2), (2, 1, 10, 7, 5, 4, 1)])
+def test_shifted_layer_with_mix_brute_force(B, C, H, W, w, oy, ox):
+    """The interleaved layer is the offset-grid WBMM followed by the 3x3 mix on the map itself
+    (zero padding at the map border, not at the padded grid's): both stages as pure loops."""
+    x = rnd((B, C, H, W), seed=340 + w)
+    T = rnd((C, 2 * w - 1, 2 * w - 1), 0.1, seed=341 + w)
+    Wm = rnd((C, 3, 3), 0.1, seed=342 + w)
+    y, z = O.layer_forward_shifted(x, w, oy, ox, T=T, Wmix=Wm)
+    zb = brute_force_shifted(x, T, w, oy, ox)
+    assert np.allclose(z, zb, rtol=0, atol=1e-12)
+    assert np.allclose(y, mix_brute_force(zb, Wm), rtol=0, atol=1e-12)
+    # the cached-matrix form gives the same layer
+    y2, z2 = O.layer_forward_shifted(x, w, oy, ox, M=O.build_matrix(T, w), Wmix=Wm)
+    assert np.array_equal(y2, y) and np.array_equal(z2, z)
+
+
+@pytest.mark.parametrize("oy,ox", [(2, 3), (4, 0)])
+def test_shifted_layer_with_mix_finite_differences(oy, ox):
+    """Central differences of L = sum(dY * y) through the offset grid and the mix, for entries of
+    x, T and the mix weights: L is linear in each, so the differences are exact up to rounding.
+    A mix applied on the padded grid, or dY used in place of the mix adjoint, fails this."""
+    w = 5
+    x = rnd((2, 2, 11, 8), seed=350)
+    T = rnd((2, 9, 9), 0.1, seed=351)
+    Wm = rnd((2, 3, 3), 0.2, seed=352)
+    dY = rnd((2, 2, 11, 8), seed=353)
+    dx, dT, dW = O.layer_backward_shifted(x, dY, w, oy, ox, T=T, Wmix=Wm)
+    # z passed in (as the GPU backward gets it) or recomputed: the same gradients
+    _, z = O.layer_forward_shifted(x, w, oy, ox, T=T, Wmix=Wm)
+    dx2, dT2, dW2 = O.layer_backward_shifted(x, dY, w, oy, ox, T=T, Wmix=Wm, z=z)
+    assert np.array_equal(dx, dx2) and np.array_equal(dT, dT2) and np.array_equal(dW, dW2)
+    dx3, dT3, dW3 = O.layer_backward_shifted(x, dY, w, oy, ox, M=O.build_matrix(T, w), Wmix=Wm,
+                                             z=z)
+    assert np.allclose(dx3, dx, rtol=0, atol=1e-12) and np.allclose(dT3, dT, rtol=0, atol=1e-12)
+
+    def L(x_=x, T_=T, W_=Wm):
+        return np.sum(dY * brute_force_layer_shifted(x_, T_, W_, w, oy, ox))
+
+    h = 1e-3
+
+    def fd(arr, k, key):
+        P, Mn = arr.copy().reshape(-1), arr.copy().reshape(-1)
+        P[k] += h
+        Mn[k] -= h
+        return (L(**{key: P.reshape(arr.shape)}) - L(**{key: Mn.reshape(arr.shape)})) / (2 * h)
+
+    for k in (0, 17, 40, 80, 161):
+        assert abs(fd(T, k, "T_") - dT.reshape(-1)[k]) <= 1e-8
+    for k in range(Wm.size):
+        assert abs(fd(Wm, k, "W_") - dW.reshape(-1)[k]) <= 1e-8
+    for k in (0, 9, 50, 87, 200, 351):
+        assert abs(fd(x, k, "x_") - dx.reshape(-1)[k]) <= 1e-8
+
+
+def brute_force_layer_shifted(x, T, Wm, w, oy, ox):
+    return mix_brute_force(brute_force_shifted(x, T, w, oy, ox), Wm)
