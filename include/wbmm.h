@@ -165,6 +165,23 @@ wbmm_status wbmm_backward(int B, int C, int H, int W, int w, int layout, const f
                           float* dmix_w, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * wbmm_backward_noalloc — wbmm_backward for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving or training loops, harnesses that forbid hipMalloc):
+ * the same gradients, arguments and errors, minus the workspace. The scratch that the backward
+ * needs (per-workgroup fp64 partials, a dz map) is a fixed device array inside the library, one
+ * copy per GPU, held until the process ends: WBMM_NOALLOC_SCRATCH_BYTES bytes. A problem whose
+ * wbmm_backward_workspace_bytes(...) exceeds that is rejected with WBMM_E_UNSUPPORTED. The call
+ * allocates and frees nothing and needs no initial contents in the scratch. Every call on one
+ * GPU shares that GPU's scratch: calls that may overlap on one GPU (other streams, other host
+ * threads) race and must be ordered by the caller; calls on one stream are ordered.
+ */
+#define WBMM_NOALLOC_SCRATCH_BYTES ((size_t)32 << 20)
+wbmm_status wbmm_backward_noalloc(int B, int C, int H, int W, int w, int layout, const float* x,
+                                  const float* T, const float* M, const float* mix_w,
+                                  const float* z_saved, const float* dy, float* dx, float* dT,
+                                  float* dmix_w, void* stream);
+
+/*
  * wbmm_forward_hier_workspace_bytes — device workspace wbmm_forward_hier needs (0 when none, and
  * 0 for invalid arguments, which wbmm_forward_hier reports).
  */

@@ -21,13 +21,14 @@ __all__ = [
     "wbmm_backward_hier", "wbmm_backward_hier_workspace_bytes", "wbmm_dwconv_forward",
     "wbmm_forward_shifted", "wbmm_forward_shifted_workspace_bytes", "wbmm_backward_shifted",
     "wbmm_backward_shifted_workspace_bytes", "wbmm_probe_mfma", "wbmm_backward_bf16",
-    "wbmm_backward_bf16_workspace_bytes",
+    "wbmm_backward_bf16_workspace_bytes", "wbmm_backward_noalloc", "WBMM_NOALLOC_SCRATCH_BYTES",
     "WBMM_OK", "WBMM_E_INVALID", "WBMM_E_UNSUPPORTED", "WBMM_E_WORKSPACE", "WBMM_E_HIP",
 ]
 
 WBMM_OK, WBMM_E_INVALID, WBMM_E_UNSUPPORTED, WBMM_E_WORKSPACE, WBMM_E_HIP = range(5)
 WBMM_F32, WBMM_BF16 = 0, 1
 WBMM_NCHW, WBMM_NHWC = 0, 1
+WBMM_NOALLOC_SCRATCH_BYTES = 32 << 20  # the library's fixed scratch for wbmm_backward_noalloc
 
 _PKG_DIR = os.path.dirname(os.path.abspath(__file__))
 _LIB = None
@@ -70,6 +71,7 @@ def _declare(lib):
         "wbmm_forward_shifted": (c_int, [c_int] * 10 + [vp] * 7 + [c_size, vp]),
         "wbmm_backward_shifted_workspace_bytes": (c_size, [c_int] * 9),
         "wbmm_backward_shifted": (c_int, [c_int] * 8 + [vp] * 10 + [c_size, vp]),
+        "wbmm_backward_noalloc": (c_int, [c_int] * 6 + [vp] * 10),
     }
     for name, (res, args) in sigs.items():
         fn = getattr(lib, name)
@@ -252,6 +254,28 @@ def wbmm_backward(x, dy, w: int, T=None, M=None, mix_w=None, z_saved=None, *, la
     """
     return _backward(x, dy, w, None, T, M, mix_w, z_saved, layout, dx, dT, dmix_w, workspace,
                      stream)
+
+
+def wbmm_backward_noalloc(x, dy, w: int, T=None, M=None, mix_w=None, z_saved=None, *,
+                          layout: str = "NCHW", dx=True, dT=True, dmix_w=True, stream=None):
+    """wbmm_backward without a workspace: the library's own fixed scratch (one per GPU,
+    WBMM_NOALLOC_SCRATCH_BYTES) holds what the backward needs, and the C call allocates nothing.
+    Outputs passed as tensors are written in place (pass them all to keep the whole call free of
+    allocations); True allocates one here, False skips it. Returns (dx, dT, dmix_w)."""
+    torch = _torch()
+    B, C, H, W = _bchw(x, layout)
+    L = 2 * w - 1
+    dev = x.device
+    dx_t = torch.empty_like(x) if dx is True else (dx if dx is not False else None)
+    dT_t = torch.empty((C, L, L), dtype=torch.float32, device=dev) if dT is True else (dT if dT is not False else None)
+    if mix_w is None:
+        dW_t = None
+    else:
+        dW_t = torch.empty((C, 3, 3), dtype=torch.float32, device=dev) if dmix_w is True else (dmix_w if dmix_w is not False else None)
+    _check(_lib().wbmm_backward_noalloc(B, C, H, W, int(w), _layout_code(layout), _ptr(x), _ptr(T),
+                                        _ptr(M), _ptr(mix_w), _ptr(z_saved), _ptr(dy), _ptr(dx_t),
+                                        _ptr(dT_t), _ptr(dW_t), _stream(stream)))
+    return dx_t, dT_t, dW_t
 
 
 def wbmm_backward_shifted_workspace_bytes(B, C, H, W, w, oy, ox, layout="NCHW",

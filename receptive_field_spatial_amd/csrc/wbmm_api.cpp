@@ -5,6 +5,7 @@
 #include <cstdarg>
 #include <cstdint>
 #include <cstdio>
+#include <mutex>
 #include <string>
 
 #include "../../include/wbmm.h"
@@ -289,11 +290,43 @@ size_t backward_ws_bytes(int B, int C, int H, int W, int w, int oy, int ox, int 
   return wbmm::backward_workspace(r);
 }
 
+}  // namespace
+
+// Scratch of the allocation-free backward: one copy per GPU, in the library's code object, held
+// until the process ends. Host code never passes `scratch` itself to a kernel (on the host it is
+// only a stand-in for the symbol); it asks for the device address once per device.
+static __device__ __align__(256) unsigned char scratch[WBMM_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+constexpr size_t kScratchBytes = WBMM_NOALLOC_SCRATCH_BYTES;
+std::mutex g_scratch_mu;
+void* g_scratch_dev[64];  // device address of `scratch` per device id, once looked up
+
+// The current device's copy of `scratch` (looked up on first use with that device current).
+wbmm_status scratch_ptr(void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_status(e, "hipGetDevice");
+  if (dev < 0 || dev >= 64) return fail(WBMM_E_UNSUPPORTED, "device id %d out of range", dev);
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if (!g_scratch_dev[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_status(e, "hipGetSymbolAddress(scratch)");
+    if (!p) return fail(WBMM_E_HIP, "hipGetSymbolAddress(scratch) returned NULL");
+    g_scratch_dev[dev] = p;
+  }
+  *out = g_scratch_dev[dev];
+  return WBMM_OK;
+}
+
+// no_alloc: the workspace is the current device's `scratch` (workspace arguments ignored).
 wbmm_status backward_call(int B, int C, int H, int W, int w, int oy, int ox, int layout,
                           const float* x, const float* T, const float* M, const float* mix_w,
                           const float* z_saved, const float* dy, float* dx, float* dT,
                           float* dmix_w, void* workspace, size_t workspace_bytes, void* stream,
-                          const char* name) {
+                          const char* name, bool no_alloc = false) {
   if (!offsets_ok(w, oy, ox))
     return fail(WBMM_E_INVALID, "grid offset (%d, %d) outside [0, w=%d)", oy, ox, w);
   wbmm_status st = check_map(B, C, H + oy, W + ox, w, layout);
@@ -320,6 +353,16 @@ wbmm_status backward_call(int B, int C, int H, int W, int w, int oy, int ox, int
   if (!wbmm::backward_plan_ok(r))
     return fail(WBMM_E_UNSUPPORTED, "no launch shape fits this problem (w=%d)", w);
   const size_t need = wbmm::backward_workspace(r);
+  if (no_alloc) {
+    if (need > kScratchBytes)
+      return fail(WBMM_E_UNSUPPORTED,
+                  "this problem needs %zu bytes of scratch; the allocation-free backward holds "
+                  "%zu (use wbmm_backward with a workspace)", need, kScratchBytes);
+    const wbmm_status sp = scratch_ptr(&r.ws);
+    if (sp != WBMM_OK) return sp;
+    r.ws_bytes = kScratchBytes;
+    return hip_status(wbmm::launch_backward(r, (hipStream_t)stream), name);
+  }
   if (need > 0 && (!workspace || workspace_bytes < need))
     return fail(WBMM_E_WORKSPACE, "workspace of %zu bytes required, %zu given", need,
                 workspace ? workspace_bytes : (size_t)0);
@@ -342,6 +385,15 @@ WBMM_API wbmm_status wbmm_backward(int B, int C, int H, int W, int w, int layout
                                    void* stream) {
   return backward_call(B, C, H, W, w, 0, 0, layout, x, T, M, mix_w, z_saved, dy, dx, dT, dmix_w,
                        workspace, workspace_bytes, stream, "wbmm_backward");
+}
+
+WBMM_API wbmm_status wbmm_backward_noalloc(int B, int C, int H, int W, int w, int layout,
+                                           const float* x, const float* T, const float* M,
+                                           const float* mix_w, const float* z_saved,
+                                           const float* dy, float* dx, float* dT, float* dmix_w,
+                                           void* stream) {
+  return backward_call(B, C, H, W, w, 0, 0, layout, x, T, M, mix_w, z_saved, dy, dx, dT, dmix_w,
+                       nullptr, 0, stream, "wbmm_backward_noalloc", true);
 }
 
 WBMM_API size_t wbmm_backward_shifted_workspace_bytes(int B, int C, int H, int W, int w, int oy,
