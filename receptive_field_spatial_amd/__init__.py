@@ -419,12 +419,12 @@ def wbmm_backward_bf16_workspace_bytes(B, C, H, W, w, layout="NCHW", has_mix=Fal
                                                          int(bool(has_mix))))
 
 
-def wbmm_backward_bf16(x, dy, w: int, T, mix_w=None, z_saved=None, *, dx=True, dT=True,
-                       dmix_w=True, workspace=None, stream=None):
+def wbmm_backward_bf16(x, dy, w: int, T, mix_w=None, z_saved=None, *, layout: str = "NCHW",
+                       dx=True, dT=True, dmix_w=True, workspace=None, stream=None):
     """Layer backward with bf16 maps (x, dy, z_saved bf16; T bf16). Returns (dx bf16, dT fp32,
     dmix_w fp32); an output passed as False is skipped."""
     torch = _torch()
-    B, C, H, W = _bchw(x, "NCHW")
+    B, C, H, W = _bchw(x, layout)
     L = 2 * w - 1
     dev = x.device
     dx_t = torch.empty_like(x) if dx is True else (dx if dx is not False else None)
@@ -433,11 +433,12 @@ def wbmm_backward_bf16(x, dy, w: int, T, mix_w=None, z_saved=None, *, dx=True, d
         dW_t = None
     else:
         dW_t = torch.empty((C, 3, 3), dtype=torch.float32, device=dev) if dmix_w is True else (dmix_w if dmix_w is not False else None)
-    need = wbmm_backward_bf16_workspace_bytes(B, C, H, W, w, "NCHW", mix_w is not None)
+    need = wbmm_backward_bf16_workspace_bytes(B, C, H, W, w, layout, mix_w is not None)
     if workspace is None or workspace.numel() * workspace.element_size() < need:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
     ws_bytes = workspace.numel() * workspace.element_size()
-    _check(_lib().wbmm_backward_bf16(B, C, H, W, int(w), WBMM_NCHW, _ptr(x), _ptr(T), _ptr(mix_w),
+    _check(_lib().wbmm_backward_bf16(B, C, H, W, int(w), _layout_code(layout), _ptr(x), _ptr(T),
+                                     _ptr(mix_w),
                                      _ptr(z_saved), _ptr(dy), _ptr(dx_t), _ptr(dT_t), _ptr(dW_t),
                                      _ptr(workspace), ws_bytes, _stream(stream)))
     return dx_t, dT_t, dW_t

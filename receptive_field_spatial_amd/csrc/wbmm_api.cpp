@@ -551,8 +551,10 @@ WBMM_API wbmm_status wbmm_probe_mfma(int dtype, int blocks, int iters, float* ou
 
 WBMM_API size_t wbmm_backward_bf16_workspace_bytes(int B, int C, int H, int W, int w, int layout,
                                                    int has_mix) {
-  if (!wbmm::bf16_backward_ok(B, C, H, W, w, layout)) return 0;
-  return wbmm::bf16_backward_workspace(B, C, H, W, w, has_mix);
+  if (check_map(B, C, H, W, w, layout) != WBMM_OK || w > 16 ||
+      !wbmm::bf16_backward_plan_ok(B, C, H, W, w, layout))
+    return 0;
+  return wbmm::bf16_backward_workspace(B, C, H, W, w, layout, has_mix);
 }
 
 WBMM_API wbmm_status wbmm_backward_bf16(int B, int C, int H, int W, int w, int layout,
@@ -562,10 +564,9 @@ WBMM_API wbmm_status wbmm_backward_bf16(int B, int C, int H, int W, int w, int l
                                         void* stream) {
   wbmm_status st = check_map(B, C, H, W, w, layout);
   if (st != WBMM_OK) return st;
-  if (!wbmm::bf16_backward_ok(B, C, H, W, w, layout))
-    return fail(WBMM_E_UNSUPPORTED,
-                "the bf16 backward is provided for w = 14 on NCHW 28x28 and 56x56 images "
-                "(w=%d, %dx%d)", w, H, W);
+  if (w > 16) return fail(WBMM_E_UNSUPPORTED, "the backward is provided for w <= 16 (w=%d)", w);
+  if (!wbmm::bf16_backward_plan_ok(B, C, H, W, w, layout))
+    return fail(WBMM_E_UNSUPPORTED, "no launch shape fits this problem (w=%d)", w);
   if (!x || !T || !dy) return fail(WBMM_E_INVALID, "x, T and dy must be non-NULL");
   if ((mix_w == nullptr) != (z_saved == nullptr))
     return fail(WBMM_E_INVALID, "z_saved is required exactly when mix_w is given");
@@ -584,13 +585,13 @@ WBMM_API wbmm_status wbmm_backward_bf16(int B, int C, int H, int W, int w, int l
     return fail(WBMM_E_INVALID, "dT overlaps T or dx");
   if (dmix_w && mix_w && overlaps(dmix_w, (size_t)C * 36, mix_w, (size_t)C * 36))
     return fail(WBMM_E_INVALID, "dmix_w overlaps mix_w");
-  const size_t need = wbmm::bf16_backward_workspace(B, C, H, W, w, mix_w != nullptr);
+  const size_t need = wbmm::bf16_backward_workspace(B, C, H, W, w, layout, mix_w != nullptr);
   if (!workspace || workspace_bytes < need)
     return fail(WBMM_E_WORKSPACE, "workspace of %zu bytes required, %zu given", need,
                 workspace ? workspace_bytes : (size_t)0);
   if (!aligned(workspace, 256)) return fail(WBMM_E_UNSUPPORTED, "workspace not 256-byte aligned");
   wbmm::BwdBf16Request r{};
-  r.B = B; r.C = C; r.H = H; r.W = W; r.w = w;
+  r.B = B; r.C = C; r.H = H; r.W = W; r.w = w; r.layout = layout;
   r.x = (const uint16_t*)x; r.T = (const uint16_t*)T; r.mixw = mix_w;
   r.zsaved = (const uint16_t*)z_saved; r.dy = (const uint16_t*)dy; r.dx = (uint16_t*)dx;
   r.dT = dT; r.dmixw = mix_w ? dmix_w : nullptr; r.ws = workspace;

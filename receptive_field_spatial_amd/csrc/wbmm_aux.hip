@@ -290,6 +290,32 @@ hipError_t launch_mix_bwd_weight(const float* dy, const float* z, float* dw9, in
   return hipGetLastError();
 }
 
+template <typename TM>
+hipError_t launch_mix_bwd_data_t(const TM* dy, const float* w9, TM* dz, int B, int C, int H,
+                                 int W, int layout, hipStream_t st) {
+  const size_t n = (size_t)B * C * H * W;
+  hipLaunchKernelGGL(k_mix_bwd_data<TM>, dim3(grid_for(n)), dim3(kThreads), 0, st, dy, w9, dz, B,
+                     C, H, W, layout);
+  return hipGetLastError();
+}
+
+template <typename TM>
+hipError_t launch_mix_bwd_weight_t(const TM* dy, const TM* z, float* dw9, int B, int C, int H,
+                                   int W, int layout, hipStream_t st) {
+  hipLaunchKernelGGL(k_mix_bwd_weight<TM>, dim3(C), dim3(kThreads), 0, st, dy, z, dw9, B, C, H, W,
+                     layout);
+  return hipGetLastError();
+}
+
+template hipError_t launch_mix_bwd_data_t<float>(const float*, const float*, float*, int, int, int,
+                                                 int, int, hipStream_t);
+template hipError_t launch_mix_bwd_data_t<uint16_t>(const uint16_t*, const float*, uint16_t*, int,
+                                                    int, int, int, int, hipStream_t);
+template hipError_t launch_mix_bwd_weight_t<float>(const float*, const float*, float*, int, int,
+                                                   int, int, int, hipStream_t);
+template hipError_t launch_mix_bwd_weight_t<uint16_t>(const uint16_t*, const uint16_t*, float*,
+                                                      int, int, int, int, int, hipStream_t);
+
 // Stage one plane (bf16 or fp32) into LDS as fp32 with a one-pixel zero halo (pitch W + 2): the
 // halo is zeroed, then the interior is filled from pixel pairs (W even) or single pixels.
 template <typename TM>
@@ -508,6 +534,24 @@ hipError_t launch_mix_fwd_planes_bf16(const uint16_t* z, const float* w9, uint16
 hipError_t launch_mix_fwd_planes_f32(const float* z, const float* w9, float* y, int B, int C,
                                      int H, int W, hipStream_t st) {
   return launch_mix_fwd_planes<float>(z, w9, y, B, C, H, W, st);
+}
+
+// fp32 NCHW mix pass after a forward that wrote z: whole planes staged in LDS when they fit (up to
+// 150 KB for one plane, so 128 x 128 planes stage too), else the per-pixel kernel.
+hipError_t launch_mix_fwd_f32_route(const float* z, const float* w9, float* y, int B, int C,
+                                    int H, int W, hipStream_t st) {
+  const int sp = mix_planes_together(H, W);
+  const size_t lds = (size_t)sp * (H + 2) * (W + 2) * sizeof(float);
+  if (lds > 150 * 1024) return launch_mix_fwd(z, w9, y, 0, B, C, H, W, 0, st);
+  if (lds > 64 * 1024) {
+    hipError_t e = hipFuncSetAttribute((const void*)k_mix_fwd_planes<float>,
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return e;
+  }
+  const int planes = B * C;
+  hipLaunchKernelGGL(k_mix_fwd_planes<float>, dim3((planes + sp - 1) / sp), dim3(kThreads),
+                     (unsigned)lds, st, z, w9, y, C, H, W, planes);
+  return hipGetLastError();
 }
 
 size_t mix_planes_lds_bytes(int H, int W) {

@@ -13,15 +13,18 @@
 
 namespace wbmm {
 
+// Maps (x, dy or dz, z, dx) and the table are fp32, or bf16 (TM = uint16_t: mixed-precision
+// training on the general shapes); the tiles and MFMAs are fp32 either way (bf16 values widen
+// exactly, their products are exact in fp32), dx is rounded to the map type.
 struct BwdArgs {
   Geo g;
-  const float* x;
-  const float* tab;
+  const void* x;
+  const void* tab;
   const float* mat;
   const float* mixw;
-  const float* zsaved;
-  const float* gsrc;    // dy (mix applied here, or no mix) or dz (mix applied by a prior pass)
-  float* dx;
+  const void* zsaved;
+  const void* gsrc;     // dy (mix applied here, or no mix) or dz (mix applied by a prior pass)
+  void* dx;
   float* dT;
   float* dmixw;
   double* partT;        // [C][col_groups][L]
@@ -45,8 +48,11 @@ __device__ __forceinline__ int slot_dy(int j, int wave, int nd, bool& valid) {
 // i.e. row pairs in one band of s rows (y1 / s == y2 / s) and, within them, column pairs in one
 // band of s columns. Row offsets |dy| < s keep those row pairs in a second fp32 chain; dT takes
 // both chains, dT_sub the second one's band-restricted diagonals.
-template <int RPW, int ASRC, bool HIER = false>
+template <int RPW, int ASRC, bool HIER = false, typename TM = float>
 __global__ void __launch_bounds__(kThreads) k_wbmm_bwd(BwdArgs a) {
+  constexpr int kBf16 = sizeof(TM) == 2;
+  const TM* gsrc = (const TM*)a.gsrc;
+  const TM* zsaved = (const TM*)a.zsaved;
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   __shared__ double s_wred[4][9];
   const Geo& g = a.g;
@@ -60,7 +66,7 @@ __global__ void __launch_bounds__(kThreads) k_wbmm_bwd(BwdArgs a) {
   int2* Offs = (int2*)(smem + g.lds_off);
   const int plane = g.PH * g.PW;
 
-  load_table_f32(g, ASRC == 0 ? a.tab : nullptr, c, Ts, Offs, a.tsub);
+  load_table_f32<TM>(g, ASRC == 0 ? (const TM*)a.tab : nullptr, c, Ts, Offs, a.tsub);
 
   double wacc[9];
 #pragma unroll
@@ -80,7 +86,7 @@ __global__ void __launch_bounds__(kThreads) k_wbmm_bwd(BwdArgs a) {
       const int b = colgrp * g.ipw + (int)img;
       if (b >= g.B) continue;
       Hs[(int)img * plane + (h + 1) * g.PW + v + 1] =
-          a.gsrc[map_off(g.layout, b, c, (int)h, (int)v, g.C, g.H, g.W)];
+          load_f32<TM>(gsrc, map_off(g.layout, b, c, (int)h, (int)v, g.C, g.H, g.W));
     }
     __syncthreads();
     float w9[9];
@@ -106,7 +112,7 @@ __global__ void __launch_bounds__(kThreads) k_wbmm_bwd(BwdArgs a) {
       Gt[xs_slot_f32(g, n, (int)y, (int)xx)] = dz;
       if (a.want_dW) {
         // dWmix[u][t] = sum_{p,q} z[p][q] * dy[p-u+1][q-t+1]
-        const double zv = a.zsaved[map_off(g.layout, b, c, (int)p, (int)q, g.C, g.H, g.W)];
+        const double zv = load_f32<TM>(zsaved, map_off(g.layout, b, c, (int)p, (int)q, g.C, g.H, g.W));
 #pragma unroll
         for (int u = 0; u < 3; ++u)
 #pragma unroll
@@ -116,7 +122,7 @@ __global__ void __launch_bounds__(kThreads) k_wbmm_bwd(BwdArgs a) {
     }
     __syncthreads();
   } else {
-    load_xtile<float>(g, a.gsrc, c, colgrp, Gt);
+    load_xtile<TM, float>(g, gsrc, c, colgrp, Gt);
   }
 
   // ---------------------------------------------------------------- dX = M^T . G
@@ -137,11 +143,11 @@ __global__ void __launch_bounds__(kThreads) k_wbmm_bwd(BwdArgs a) {
         fdivmod(rem, g.fd_W, h, v);
         const int b = colgrp * g.ipw + (int)img;
         if (b >= g.B) continue;
-        a.dx[map_off(g.layout, b, c, (int)h, (int)v, g.C, g.H, g.W)] =
-            St[(int)img * plane + (h + 1) * g.PW + v + 1];
+        store_out(a.dx, map_off(g.layout, b, c, (int)h, (int)v, g.C, g.H, g.W),
+                  St[(int)img * plane + (h + 1) * g.PW + v + 1], kBf16);
       }
     } else {
-      store_acc_direct<RPW>(g, colgrp, 0, wave, acc, c, a.dx, nullptr, 0);
+      store_acc_direct<RPW>(g, colgrp, 0, wave, acc, c, a.dx, nullptr, kBf16);
     }
   }
   __syncthreads();
@@ -149,7 +155,7 @@ __global__ void __launch_bounds__(kThreads) k_wbmm_bwd(BwdArgs a) {
   // ---------------------------------------------------------------- dT partial (row pairs)
   if (a.want_dT) {
     float* Xt = (float*)RA;
-    load_xtile<float>(g, a.x, c, colgrp, Xt);
+    load_xtile<TM, float>(g, (const TM*)a.x, c, colgrp, Xt);
     int nvalid;
     if (g.image_mode) {
       int imgs = g.B - colgrp * g.ipw;
@@ -283,22 +289,22 @@ __global__ void __launch_bounds__(kThreads) k_wbmm_bwd(BwdArgs a) {
 }
 
 // ---------------------------------------------------------------------------- dispatch
-template <int RPW, int ASRC, bool HIER = false>
+template <int RPW, int ASRC, bool HIER = false, typename TM = float>
 static hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t st) {
-  auto fn = k_wbmm_bwd<RPW, ASRC, HIER>;
+  auto fn = k_wbmm_bwd<RPW, ASRC, HIER, TM>;
   hipError_t e = hipFuncSetAttribute((const void*)fn, hipFuncAttributeMaxDynamicSharedMemorySize,
                                      a.g.lds_total);
   if (e != hipSuccess) return e;
   return launch_main(fn, dim3(a.g.col_groups, a.g.C, 1), dim3(kThreads), a.g.lds_total, st, a);
 }
 
-template <int ASRC, bool HIER = false>
+template <int ASRC, bool HIER = false, typename TM = float>
 static hipError_t launch_bwd_tiles(const BwdArgs& a, hipStream_t st) {
   switch (a.g.RPW) {
-    case 4: return launch_bwd_t<4, ASRC, HIER>(a, st);
-    case 7: return launch_bwd_t<7, ASRC, HIER>(a, st);
-    case 13: return launch_bwd_t<13, ASRC, HIER>(a, st);
-    case 16: return launch_bwd_t<16, ASRC, HIER>(a, st);
+    case 4: return launch_bwd_t<4, ASRC, HIER, TM>(a, st);
+    case 7: return launch_bwd_t<7, ASRC, HIER, TM>(a, st);
+    case 13: return launch_bwd_t<13, ASRC, HIER, TM>(a, st);
+    case 16: return launch_bwd_t<16, ASRC, HIER, TM>(a, st);
     default: return hipErrorInvalidValue;
   }
 }
@@ -353,9 +359,11 @@ size_t backward_workspace(const BwdRequest& r) {
   return generic > fast ? generic : fast;
 }
 
-hipError_t launch_backward(const BwdRequest& r, hipStream_t st) {
-  if (fast_backward_ok(r)) return launch_backward_fast(r, st);  // folds a sub-table when w = 2s
-  if (repack_backward_ok(r)) return launch_backward_repacked(r, st);  // offset grid, w = 14
+// The general kernels for any w <= 16, layout and map size. TM is the map type: float, or
+// uint16_t for bf16 maps and table (the request's map pointers then point at bf16 data).
+template <typename TM>
+static hipError_t launch_backward_general(const BwdRequest& r, hipStream_t st) {
+  constexpr bool kBf16 = sizeof(TM) == 2;
   BwdArgs a{};
   if (!plan_bwd(a.g, r)) return hipErrorInvalidValue;
   const BwdWs wl = bwd_ws_layout(a.g, r);
@@ -376,13 +384,20 @@ hipError_t launch_backward(const BwdRequest& r, hipStream_t st) {
   a.want_dx = r.dx != nullptr;
   a.want_dT = r.dT != nullptr;
   const bool mix = r.mixw != nullptr;
+  const TM* dy = (const TM*)r.dy;
+  const TM* zs = (const TM*)r.zsaved;
   hipError_t e = hipSuccess;
   if (mix && !a.g.image_mode) {
-    float* dz = (float*)(ws + wl.dz);
+    // dz (in the map type) from a separate pass, dWmix with it
+    TM* dz = (TM*)(ws + wl.dz);
     if (mix_planes_route(a.g, r)) {
       double* partM = (double*)(ws + wl.mixp);
-      e = launch_mix_bwd_planes_f32(r.dy, r.dmixw ? r.zsaved : nullptr, r.mixw, dz, partM, r.B,
-                                    r.C, r.H, r.W, st);
+      if constexpr (kBf16)
+        e = launch_mix_bwd_planes_bf16(dy, r.dmixw ? zs : nullptr, r.mixw, dz, partM, r.B, r.C,
+                                       r.H, r.W, st);
+      else
+        e = launch_mix_bwd_planes_f32(dy, r.dmixw ? zs : nullptr, r.mixw, dz, partM, r.B, r.C,
+                                      r.H, r.W, st);
       if (e != hipSuccess) return e;
       if (r.dmixw) {
         const int pb = mix_planes_per_group(r.B);
@@ -390,10 +405,10 @@ hipError_t launch_backward(const BwdRequest& r, hipStream_t st) {
         if (e != hipSuccess) return e;
       }
     } else {
-      e = launch_mix_bwd_data(r.dy, r.mixw, dz, r.B, r.C, r.H, r.W, r.layout, st);
+      e = launch_mix_bwd_data_t<TM>(dy, r.mixw, dz, r.B, r.C, r.H, r.W, r.layout, st);
       if (e != hipSuccess) return e;
       if (r.dmixw) {
-        e = launch_mix_bwd_weight(r.dy, r.zsaved, r.dmixw, r.B, r.C, r.H, r.W, r.layout, st);
+        e = launch_mix_bwd_weight_t<TM>(dy, zs, r.dmixw, r.B, r.C, r.H, r.W, r.layout, st);
         if (e != hipSuccess) return e;
       }
     }
@@ -401,20 +416,42 @@ hipError_t launch_backward(const BwdRequest& r, hipStream_t st) {
     a.mix_here = 0;
     a.want_dW = 0;
   } else {
-    a.gsrc = r.dy;
+    a.gsrc = dy;
     a.mix_here = mix ? 1 : 0;
     a.want_dW = (mix && r.dmixw) ? 1 : 0;
   }
   if (a.want_dTs) a.want_dT = 1;  // the sub-table gradient comes out of the table-gradient pass
   if (!a.want_dx && !a.want_dT && !a.want_dW) return hipSuccess;
-  if (r.Tsub) e = launch_bwd_tiles<0, true>(a, st);  // fp32 table path only (planned so)
-  else e = r.M ? launch_bwd_tiles<1>(a, st) : launch_bwd_tiles<0>(a, st);
+  if constexpr (kBf16) {
+    e = launch_bwd_tiles<0, false, uint16_t>(a, st);  // bf16 maps: table input only
+  } else {
+    if (r.Tsub) e = launch_bwd_tiles<0, true>(a, st);  // fp32 table path only (planned so)
+    else e = r.M ? launch_bwd_tiles<1>(a, st) : launch_bwd_tiles<0>(a, st);
+  }
   if (e != hipSuccess || (!a.want_dT && !a.want_dW)) return e;
   e = launch_bwd_reduce(a.partT, a.want_dW ? a.partW : nullptr, a.g.col_groups, r.C, a.g.L,
                         r.dT, a.want_dW ? r.dmixw : nullptr, st);
   if (e != hipSuccess || !a.want_dTs) return e;
   return launch_bwd_reduce(a.partTs, nullptr, a.g.col_groups, r.C,
                            (2 * a.g.s - 1) * (2 * a.g.s - 1), r.dTsub, nullptr, st);
+}
+
+hipError_t launch_backward(const BwdRequest& r, hipStream_t st) {
+  if (fast_backward_ok(r)) return launch_backward_fast(r, st);  // folds a sub-table when w = 2s
+  if (repack_backward_ok(r)) return launch_backward_repacked(r, st);  // offset grid, w = 14
+  return launch_backward_general<float>(r, st);
+}
+
+// bf16 maps and table on the general kernels (the shapes the fast bf16 backward does not cover).
+size_t backward_bf16_general_workspace(const BwdRequest& r) {
+  Geo g;
+  if (r.M || r.Tsub || r.oy || r.ox || !plan_bwd(g, r)) return 0;
+  return bwd_ws_layout(g, r).total;
+}
+
+hipError_t launch_backward_bf16_general(const BwdRequest& r, hipStream_t st) {
+  if (r.M || r.Tsub || r.oy || r.ox) return hipErrorInvalidValue;
+  return launch_backward_general<uint16_t>(r, st);
 }
 
 }  // namespace wbmm

@@ -220,16 +220,47 @@ bool bf16_backward_ok(int B, int C, int H, int W, int w, int layout) {
          (long long)C * ((B + 3) / 4 + 1) < (1LL << 31);
 }
 
-// [G map (bf16), dWmix partials (fp64, per plane): with a mix] [dT partials (fp64)]
-size_t bf16_backward_workspace(int B, int C, int H, int W, int w, int has_mix) {
-  if (!bf16_backward_ok(B, C, H, W, w, 0)) return 0;
+namespace {
+// The request for the general kernels (bf16 data behind the map and table pointers).
+BwdRequest general_request(const BwdBf16Request& q) {
+  BwdRequest r{};
+  r.B = q.B; r.C = q.C; r.H = q.H; r.W = q.W; r.w = q.w; r.layout = q.layout;
+  r.x = (const float*)q.x; r.T = (const float*)q.T; r.mixw = q.mixw;
+  r.zsaved = (const float*)q.zsaved; r.dy = (const float*)q.dy; r.dx = (float*)q.dx;
+  r.dT = q.dT; r.dmixw = q.dmixw; r.ws = q.ws;
+  return r;
+}
+}  // namespace
+
+bool bf16_backward_plan_ok(int B, int C, int H, int W, int w, int layout) {
+  if (bf16_backward_ok(B, C, H, W, w, layout)) return true;
+  static const float dummy = 0.f;
+  BwdRequest r{};
+  r.B = B; r.C = C; r.H = H; r.W = W; r.w = w; r.layout = layout;
+  r.x = r.T = r.dy = &dummy;
+  return backward_plan_ok(r);
+}
+
+// Fast shapes: [G map (bf16), dWmix partials (fp64, per plane): with a mix] [dT partials (fp64)];
+// other shapes: the general kernels' layout.
+size_t bf16_backward_workspace(int B, int C, int H, int W, int w, int layout, int has_mix) {
+  if (!bf16_backward_ok(B, C, H, W, w, layout)) {
+    static const float dummy = 0.f;
+    BwdRequest r{};
+    r.B = B; r.C = C; r.H = H; r.W = W; r.w = w; r.layout = layout;
+    r.x = r.T = r.dy = &dummy;
+    r.mixw = has_mix ? &dummy : nullptr;
+    r.zsaved = has_mix ? &dummy : nullptr;
+    return backward_bf16_general_workspace(r);
+  }
   const int groups = H == 28 ? dt_groups<D28>(B) : dt_groups<D56>(B);
   const size_t mixpart = has_mix ? al256((size_t)B * C * H * W * 2) + al256((size_t)C * B * 9 * 8) : 0;
   return mixpart + al256((size_t)C * groups * 729 * 8);
 }
 
 hipError_t launch_backward_bf16(const BwdBf16Request& r, hipStream_t st) {
-  if (!bf16_backward_ok(r.B, r.C, r.H, r.W, r.w, 0)) return hipErrorInvalidValue;
+  if (!bf16_backward_ok(r.B, r.C, r.H, r.W, r.w, r.layout))
+    return launch_backward_bf16_general(general_request(r), st);
   unsigned char* ws = (unsigned char*)r.ws;
   const bool mix = r.mixw != nullptr;
   const uint16_t* g = r.dy;

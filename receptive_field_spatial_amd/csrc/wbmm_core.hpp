@@ -44,13 +44,15 @@ __device__ __forceinline__ int xs_slot_bf16(const Geo& g, int n, int y, int x) {
   return n * g.XSB + y * g.WP + x;
 }
 
-template <typename TIn>
+// TTile: the tile's element type (bf16 tiles feed bf16 MFMAs; a bf16 map may also be widened
+// exactly into an fp32 tile).
+template <typename TIn, typename TTile>
 __device__ __forceinline__ void put_tile(const Geo& g, void* tile, int n, int y, int x,
                                          const TIn* __restrict__ src, size_t off) {
-  if constexpr (sizeof(TIn) == 2) {
+  if constexpr (sizeof(TTile) == 2) {
     ((uint16_t*)tile)[xs_slot_bf16(g, n, y, x)] = src[off];
   } else {
-    ((float*)tile)[xs_slot_f32(g, n, y, x)] = src[off];
+    ((float*)tile)[xs_slot_f32(g, n, y, x)] = load_f32<TIn>(src, off);
   }
 }
 
@@ -59,10 +61,10 @@ __device__ __forceinline__ void put_tile(const Geo& g, void* tile, int n, int y,
 // padded K slots and empty columns stay zero). Image mode walks whole image planes so that
 // global reads are contiguous rows [pith page, Fig. 2 caption: a window is one contiguous block].
 // Ends with a barrier.
-template <typename TIn>
+template <typename TIn, typename TTile = TIn>
 __device__ __forceinline__ void load_xtile(const Geo& g, const TIn* __restrict__ x, int c, int colgrp,
                            void* tile) {
-  constexpr bool kBf16 = sizeof(TIn) == 2;
+  constexpr bool kBf16 = sizeof(TTile) == 2;
   {
     const int words = kBf16 ? g.NT * g.XSB / 2 : g.NT * g.XR;
     uint32_t* t32 = (uint32_t*)tile;
@@ -81,8 +83,8 @@ __device__ __forceinline__ void load_xtile(const Geo& g, const TIn* __restrict__
       fdivmod(h + g.oy, g.fd_w, wy, y);
       fdivmod(v + g.ox, g.fd_w, wx, xx);
       const int n = (int)img * g.nWin + (int)wy * g.nW + (int)wx;
-      put_tile<TIn>(g, tile, n, (int)y, (int)xx, x,
-                    map_off(g.layout, b, c, (int)h, (int)v, g.C, g.H, g.W));
+      put_tile<TIn, TTile>(g, tile, n, (int)y, (int)xx, x,
+                           map_off(g.layout, b, c, (int)h, (int)v, g.C, g.H, g.W));
     }
   } else {
     const int total = g.NT * g.d;
@@ -94,8 +96,8 @@ __device__ __forceinline__ void load_xtile(const Geo& g, const TIn* __restrict__
       fdivmod(k, g.fd_w, y, xx);
       const int h = wy * g.w + (int)y - g.oy, v = wx * g.w + (int)xx - g.ox;
       if (h < 0 || v < 0 || h >= g.H || v >= g.W) continue;
-      put_tile<TIn>(g, tile, (int)n, (int)y, (int)xx, x,
-                    map_off(g.layout, b, c, h, v, g.C, g.H, g.W));
+      put_tile<TIn, TTile>(g, tile, (int)n, (int)y, (int)xx, x,
+                           map_off(g.layout, b, c, h, v, g.C, g.H, g.W));
     }
   }
   __syncthreads();
@@ -114,18 +116,20 @@ __device__ __forceinline__ void load_xtile(const Geo& g, const TIn* __restrict__
 // and K is walked by quadrants (lane group gq takes quadrant (gq >> 1, gq & 1)), which for
 // w = 2s are exactly the sub-windows. A pair (i, k) is then inside one sub-window exactly when
 // output pixel i lies in quadrant gq, so contract_f32 picks the copy per lane and tile.
-__device__ __forceinline__ void load_table_f32(const Geo& g, const float* __restrict__ T, int c, float* Ts,
+// TT: the table's element type (a bf16 table is widened exactly; the fold is fp32 only).
+template <typename TT = float>
+__device__ __forceinline__ void load_table_f32(const Geo& g, const TT* __restrict__ T, int c, float* Ts,
                                int2* Offs, const float* __restrict__ Tsub = nullptr) {
   if (T) {
-    const float* Tc = T + (size_t)c * g.L;
-    for (int q = threadIdx.x; q < g.L; q += kThreads) Ts[q] = Tc[q];
+    const TT* Tc = T + (size_t)c * g.L;
+    for (int q = threadIdx.x; q < g.L; q += kThreads) Ts[q] = load_f32<TT>(Tc, q);
     if (g.s) {
       const int s = g.s, s2m1 = 2 * g.s - 1;
       const float* Sc = Tsub + (size_t)c * s2m1 * s2m1;
       float* Tf = Ts + (g.L + 3) / 4 * 4;
       for (int q = threadIdx.x; q < g.L; q += kThreads) {
         const int oy = q / g.w2m1 - (g.w - 1), ox = q % g.w2m1 - (g.w - 1);
-        float v = Tc[q];
+        float v = load_f32<TT>(Tc, q);
         if (oy > -s && oy < s && ox > -s && ox < s) v = v + Sc[(oy + s - 1) * s2m1 + ox + s - 1];
         Tf[q] = v;
       }

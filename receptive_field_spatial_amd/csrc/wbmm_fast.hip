@@ -830,41 +830,50 @@ k_bwd_ls(FastArgs a) {
     }
     constexpr int CH_E = 4 * S::D;
     constexpr int EPT = (CH_E + kThreads - 1) / kThreads;
-    int goff[EPT], loff[EPT], ekn[EPT];
+    // Window n = 4 ci + kn of the unit (kn = element / D) lies in image ir and window wnd with
+    // ir * cp + window origin = chunk part (uniform) + element part: NWIN = 1: ir = 4 ci + kn;
+    // NWIN = 4: ir = ci, wnd = kn; NWIN = 16: ir = ci / 4, window row ci % 4, column kn.
+    static_assert(S::NWIN == 1 || S::NWIN == 4 || (S::NWIN == 16 && S::NWX == 4), "chunk map");
+    int eoff[EPT], loff[EPT];
 #pragma unroll
     for (int j = 0; j < EPT; ++j) {
       const int e = threadIdx.x + j * kThreads;
       const int ee = e < CH_E ? e : 0;
-      ekn[j] = ee / S::D;
-      const int p = ee % S::D;
-      goff[j] = (p / S::WS) * S::IW + (p % S::WS);
-      loff[j] = e < CH_E ? ekn[j] * S::XP + p : -1;
+      const int kn = ee / S::D, p = ee % S::D;
+      const int pix = (p / S::WS) * S::IW + (p % S::WS);
+      if constexpr (S::NWIN == 1) eoff[j] = kn * U.cp + pix;
+      else if constexpr (S::NWIN == 4) eoff[j] = (kn / S::NWX) * S::WS * S::IW + (kn % S::NWX) * S::WS + pix;
+      else eoff[j] = kn * S::WS + pix;
+      loff[j] = e < CH_E ? kn * S::XP + p : -1;
     }
     const float* xu = a.x + U.base;
-    float stg[EPT];
-    auto load_chunk = [&](int ci) {
+    // windows past the batch have G = 0: their loads read within the last image instead
+    const int maxoff = (U.nimg - 1) * U.cp + S::PLANE - 1;
+    // two register buffers: chunk ci + 2 is loaded while chunk ci is contracted, so a global
+    // load has two chunks of matrix work to land (one was not enough once a CU runs only one
+    // workgroup, at the end of the kernel); the loads past the last chunk repeat it (no
+    // conditional loads)
+    float stgA[EPT], stgB[EPT];
+    auto load_chunk = [&](float (&stg)[EPT], int ci) {
+      const int cbase = S::NWIN == 1 ? 4 * ci * U.cp
+                        : S::NWIN == 4 ? ci * U.cp
+                                       : (ci >> 2) * U.cp + (ci & 3) * S::WS * S::IW;
 #pragma unroll
       for (int j = 0; j < EPT; ++j) {
-        const int n = 4 * ci + ekn[j];
-        const int q = n >> 4, nl = n & 15;
-        const int im = nl / S::NWIN, wnd = nl % S::NWIN;
-        int ir = q * S::IPW + im;
-        ir = ir < U.nimg ? ir : U.nimg - 1;  // windows past the batch have G = 0
-        stg[j] = xu[ir * U.cp + (wnd / S::NWX) * S::WS * S::IW + (wnd % S::NWX) * S::WS + goff[j]];
+        const int o = cbase + eoff[j];
+        stg[j] = xu[o < maxoff ? o : maxoff];
       }
     };
     const int kn = lane >> 4, x1 = lane & 15;
     const int xc = x1 < S::WS ? x1 : S::WS - 1;
     float* xbuf = Ts;
-    load_chunk(0);
-    __syncthreads();  // every wave is done with the table (dX) and the dWmix sums
-    for (int ci = 0; ci < 16; ++ci) {
+    auto step = [&](float (&stg)[EPT], int ci) {
       if (ci > 0) __syncthreads();  // chunk ci-1 consumed by every wave
 #pragma unroll
       for (int j = 0; j < EPT; ++j)
         if (loff[j] >= 0) xbuf[loff[j]] = stg[j];
       __syncthreads();
-      if (ci + 1 < 16) load_chunk(ci + 1);
+      load_chunk(stg, ci + 2 < 16 ? ci + 2 : 15);
       // fp32 chains over 4 chunks (16 windows, at most 224 products each) before each
       // promotion to fp64 (over 8 chunks the full training shape came within 7% of the
       // max-abs bound)
@@ -875,6 +884,13 @@ k_bwd_ls(FastArgs a) {
         case 2: dt_chunk<S, 2, HIER>(regions, xbuf, 4 * ci, kn, xc, a32, acc64, b32, accs64, flush); break;
         default: dt_chunk<S, 3, HIER>(regions, xbuf, 4 * ci, kn, xc, a32, acc64, b32, accs64, flush); break;
       }
+    };
+    load_chunk(stgA, 0);
+    load_chunk(stgB, 1);
+    __syncthreads();  // every wave is done with the table (dX) and the dWmix sums
+    for (int ci = 0; ci < 16; ci += 2) {
+      step(stgA, ci);
+      step(stgB, ci + 1);
     }
     double* pT = a.partT + (size_t)u * S::L;
     __syncthreads();  // every wave is done reading the G regions and the last chunk

@@ -152,6 +152,8 @@ static bool fast_bf16_mix_ok(const FwdRequest& r) {
 
 size_t forward_workspace(const FwdRequest& r) {
   if (repack_forward_ok(r)) return repack_forward_workspace(r);
+  // cached matrix on the fast path: with the mix, the pre-mix map goes to z_save or here
+  if (fast_cm_forward_ok(r)) return r.mixw && !r.zsave ? (size_t)r.B * r.C * r.H * r.W * 4 : 0;
   if (fast_bf16_mix_ok(r)) return r.zsave ? 0 : (size_t)r.B * r.C * r.H * r.W * 2;
   Geo g;
   if (!plan_fwd(g, r)) return 0;
@@ -165,6 +167,13 @@ hipError_t launch_forward(const FwdRequest& r, hipStream_t st) {
   if (fast_forward_ok(r)) return launch_forward_fast(r, st);  // folds a sub-table when w = 2s
   if (!r.Tsub && fast_bf16_forward_ok(r)) return launch_forward_fast_bf16(r, st);
   if (repack_forward_ok(r)) return launch_forward_repacked(r, st);  // offset grid, w = 14
+  if (fast_cm_forward_ok(r)) {  // cached matrix, fp32, w = 14: the contraction, then the mix pass
+    if (!r.mixw) return launch_forward_fast_cm(r, (float*)r.y, (float*)r.zsave, st);
+    float* z = (float*)(r.zsave ? r.zsave : r.ws);
+    hipError_t e = launch_forward_fast_cm(r, z, nullptr, st);
+    if (e != hipSuccess) return e;
+    return launch_mix_fwd_f32_route(z, r.mixw, (float*)r.y, r.B, r.C, r.H, r.W, st);
+  }
   if (fast_bf16_mix_ok(r)) {
     FwdRequest q = r;
     uint16_t* zb = (uint16_t*)(r.zsave ? r.zsave : r.ws);
@@ -209,8 +218,8 @@ hipError_t launch_forward(const FwdRequest& r, hipStream_t st) {
   else e = cached ? launch_fwd_tiles<float, 1>(a, st) : launch_fwd_tiles<float, 0>(a, st);
   if (e != hipSuccess) return e;
   if (!a.g.image_mode && mix) {
-    if (!r.out_bf16 && r.layout == 0 && mix_planes_lds_bytes(r.H, r.W) <= 64 * 1024)
-      return launch_mix_fwd_planes_f32(zbuf, r.mixw, (float*)r.y, r.B, r.C, r.H, r.W, st);
+    if (!r.out_bf16 && r.layout == 0)
+      return launch_mix_fwd_f32_route(zbuf, r.mixw, (float*)r.y, r.B, r.C, r.H, r.W, st);
     e = launch_mix_fwd(zbuf, r.mixw, r.y, r.out_bf16, r.B, r.C, r.H, r.W, r.layout, st,
                        (r.zsave && r.out_bf16) ? (uint16_t*)r.zsave : nullptr);
   }

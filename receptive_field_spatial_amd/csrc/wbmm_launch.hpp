@@ -76,6 +76,11 @@ bool repack_backward_ok(const BwdRequest& r);
 size_t repack_backward_workspace(const BwdRequest& r);
 hipError_t launch_backward_repacked(const BwdRequest& r, hipStream_t st);
 
+// Fast fp32 forward on a cached matrix (w = 14, NCHW, any H and W, no sub-table, plain grid):
+// the contraction's result goes to `out` (and a copy to `out2` when not null).
+bool fast_cm_forward_ok(const FwdRequest& r);
+hipError_t launch_forward_fast_cm(const FwdRequest& r, float* out, float* out2, hipStream_t st);
+
 // Fast bf16 forwards for NCHW table input, bf16 output, no mix: w = 14 on 28x28 and 56x56
 // images, w = 7 and w = 28 on 56x56 images.
 bool fast_bf16_forward_ok(const FwdRequest& r);
@@ -105,7 +110,7 @@ hipError_t launch_main(K kernel, dim3 grid, dim3 block, unsigned lds, hipStream_
 // bf16 backward (w = 14, NCHW 28x28 / 56x56 images, table input): maps and table in bf16,
 // dT and dWmix in fp32.
 struct BwdBf16Request {
-  int B, C, H, W, w;
+  int B, C, H, W, w, layout;
   const uint16_t* x;
   const uint16_t* T;
   const float* mixw;
@@ -117,7 +122,13 @@ struct BwdBf16Request {
   void* ws;
 };
 bool bf16_backward_ok(int B, int C, int H, int W, int w, int layout);
-size_t bf16_backward_workspace(int B, int C, int H, int W, int w, int has_mix);
+// The fast bf16 shapes above, or any shape the general kernels plan (w <= 16, any layout).
+bool bf16_backward_plan_ok(int B, int C, int H, int W, int w, int layout);
+size_t bf16_backward_workspace(int B, int C, int H, int W, int w, int layout, int has_mix);
+// bf16 maps and table through the general kernels (fp32 tiles and matrix cores, exact widening;
+// the request's map and table pointers point at bf16 data).
+size_t backward_bf16_general_workspace(const BwdRequest& r);
+hipError_t launch_backward_bf16_general(const BwdRequest& r, hipStream_t st);
 hipError_t launch_backward_bf16(const BwdBf16Request& r, hipStream_t st);
 hipError_t launch_bf16_transposed_contraction(const uint16_t* g, const uint16_t* T, uint16_t* out,
                                               int B, int C, int H, hipStream_t st);
@@ -131,6 +142,9 @@ hipError_t launch_mix_bwd_planes_bf16(const uint16_t* dy, const uint16_t* z, con
 // The same plane-staged mix passes on fp32 NCHW maps (both need mix_planes_lds_bytes(H, W) and
 // (H + 2) (W + 2) 4 bytes per staged plane within 64 KB; they return hipErrorInvalidValue else).
 size_t mix_planes_lds_bytes(int H, int W);
+// fp32 NCHW forward mix pass: the plane-staged pass when a plane fits in LDS, else launch_mix_fwd.
+hipError_t launch_mix_fwd_f32_route(const float* z, const float* w9, float* y, int B, int C,
+                                    int H, int W, hipStream_t st);
 hipError_t launch_mix_fwd_planes_f32(const float* z, const float* w9, float* y, int B, int C,
                                      int H, int W, hipStream_t st);
 hipError_t launch_mix_bwd_planes_f32(const float* dy, const float* z, const float* w9, float* g,
@@ -152,5 +166,12 @@ hipError_t launch_mix_bwd_data(const float* dy, const float* w9, float* dz, int 
                                int W, int layout, hipStream_t st);
 hipError_t launch_mix_bwd_weight(const float* dy, const float* z, float* dw9, int B, int C, int H,
                                  int W, int layout, hipStream_t st);
+// The same two passes on fp32 or bf16 maps (TM = float or uint16_t; dz in the map type).
+template <typename TM>
+hipError_t launch_mix_bwd_data_t(const TM* dy, const float* w9, TM* dz, int B, int C, int H,
+                                 int W, int layout, hipStream_t st);
+template <typename TM>
+hipError_t launch_mix_bwd_weight_t(const TM* dy, const TM* z, float* dw9, int B, int C, int H,
+                                   int W, int layout, hipStream_t st);
 
 }  // namespace wbmm

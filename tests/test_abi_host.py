@@ -244,22 +244,27 @@ def test_shifted_workspace_covers_the_repacked_maps(lib):
 
 
 def test_backward_bf16_validation(lib):
-    """bf16 backward: w = 14 on NCHW 28² / 56² only, mix and z_saved together, workspace needed."""
+    """bf16 backward: w <= 16 (any layout and map size), mix and z_saved together, workspace
+    needed (the fast w = 14 NCHW 28² / 56² shapes and the general ones have their own layouts)."""
     def call(B=2, C=3, H=28, W=28, w=14, layout=0, mix=None, z=None, dx=0x500000, ws=0x900000,
              wsb=1 << 30):
         return lib.wbmm_backward_bf16(B, C, H, W, w, layout, FAKE, 0x300000, mix, z, FAKE2, dx,
                                       0x600000, None, ws, wsb, None)
-    assert call(H=30, W=30) == R.WBMM_E_UNSUPPORTED
-    assert call(w=7) == R.WBMM_E_UNSUPPORTED
-    assert call(layout=1) == R.WBMM_E_UNSUPPORTED
-    assert "bf16 backward" in err(lib)
+    assert call(w=17) == R.WBMM_E_UNSUPPORTED
+    assert "w <= 16" in err(lib)
+    assert call(w=0) == R.WBMM_E_INVALID
+    for kw in ({"H": 30, "W": 30}, {"w": 7}, {"layout": 1}):   # general shapes: workspace sized
+        need = lib.wbmm_backward_bf16_workspace_bytes(2, 3, kw.get("H", 28), kw.get("W", 28),
+                                                      kw.get("w", 14), kw.get("layout", 0), 0)
+        assert need > 0
+        assert call(ws=0x900000, wsb=need - 1, **kw) == R.WBMM_E_WORKSPACE
     assert call(mix=0x700000) == R.WBMM_E_INVALID            # mix without z_saved
     assert call(dx=FAKE) == R.WBMM_E_INVALID                  # dx aliases x
     assert call(ws=None) == R.WBMM_E_WORKSPACE
     need = lib.wbmm_backward_bf16_workspace_bytes(2, 3, 28, 28, 14, 0, 1)
     assert need > lib.wbmm_backward_bf16_workspace_bytes(2, 3, 28, 28, 14, 0, 0) > 0
     assert call(mix=0x700000, z=0x800000, wsb=need - 1) == R.WBMM_E_WORKSPACE
-    assert lib.wbmm_backward_bf16_workspace_bytes(2, 3, 30, 30, 14, 0, 0) == 0
+    assert lib.wbmm_backward_bf16_workspace_bytes(2, 3, 30, 30, 17, 0, 0) == 0
 
 
 def test_probe_validation(lib):

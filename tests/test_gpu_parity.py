@@ -901,6 +901,46 @@ def test_backward_bf16(B, C, H, mix):
     assert torch.equal(dx, dx2) and torch.equal(dT, dT2)
 
 
+@pytest.mark.parametrize("B,C,H,W,w,layout,mix", [
+    (2, 3, 30, 25, 14, "NCHW", True),    # ragged map, image mode (mix adjoint fused)
+    (3, 2, 21, 14, 7, "NCHW", False),
+    (2, 3, 28, 28, 14, "NHWC", True),    # channels-last
+    (1, 2, 56, 56, 7, "NCHW", True),
+    (2, 2, 17, 23, 5, "NHWC", False),
+    (1, 2, 32, 32, 16, "NCHW", True),
+    (2, 2, 128, 128, 14, "NCHW", True),  # window mode: plane-staged mix adjoint (bf16 G)
+    (1, 2, 100, 100, 14, "NHWC", True),  # window mode, channels-last: per-pixel mix passes
+])
+def test_backward_bf16_general(B, C, H, W, w, layout, mix):
+    """bf16 maps and table on the shapes the fast bf16 backward does not cover (any w <= 16,
+    ragged maps, NHWC): the general kernels widen bf16 to fp32 tiles exactly. dx within the
+    bf16 bar; dT within the fp32 bar without a mix (G = dy, exact products), the bf16 bar with
+    one (G may be rounded to bf16); dWmix within the fp32 bar."""
+    say(f"backward bf16 general B={B} C={C} H={H} W={W} w={w} {layout} mix={mix}")
+    x = synth.round_to_bf16(synth.normal_f32((B, C, H, W), 1.0, seed=275))
+    T = synth.round_to_bf16(synth.normal_f32((C, 2 * w - 1, 2 * w - 1), 0.02, seed=276))
+    dy = synth.round_to_bf16(synth.normal_f32((B, C, H, W), 1.0, seed=277))
+    Wm = synth.normal_f32((C, 3, 3), 0.1, seed=278) if mix else None
+    z = (synth.round_to_bf16(O.wbmm_forward(x.astype(np.float64), w, T=T).astype(np.float32))
+         if mix else None)
+    tl = (lambda a: a) if layout == "NCHW" else (lambda a: np.ascontiguousarray(a.transpose(0, 2, 3, 1)))
+    fl = (lambda a: a) if layout == "NCHW" else (lambda a: a.transpose(0, 3, 1, 2))
+    xd, Td, dyd = dev_bf16(tl(x)), dev_bf16(T), dev_bf16(tl(dy))
+    zd = dev_bf16(tl(z)) if mix else None
+    Wd = dev(Wm) if mix else None
+    dx, dT, dW = R().wbmm_backward_bf16(xd, dyd, w, Td, mix_w=Wd, z_saved=zd, layout=layout)
+    wdx, wdT, wdW = O.layer_backward(x.astype(np.float64), dy.astype(np.float64), w, T=T, Wmix=Wm,
+                                     z=z.astype(np.float64) if mix else None)
+    assert_bf16(fl(host(dx.float())), wdx, "dx")
+    if mix:
+        assert_bf16(host(dT), wdT, "dT")
+        assert_f32(host(dW), wdW, "dWmix")
+    else:
+        assert_f32(host(dT), wdT, "dT")
+    dx2, dT2, _ = R().wbmm_backward_bf16(xd, dyd, w, Td, mix_w=Wd, z_saved=zd, layout=layout)
+    assert torch.equal(dx, dx2) and torch.equal(dT, dT2)
+
+
 def test_backward_bf16_partial_outputs():
     """Only dT, or only dx: the skipped outputs are not written and the others match."""
     B, C, H, w = 4, 2, 28, 14
