@@ -362,12 +362,28 @@ __device__ __forceinline__ void stage_plane<float>(const float* __restrict__ src
     P[(r + 1) * PW + W + 1] = 0.f;
   }
   if ((W & 1) == 0) {  // planes start at even pixel offsets: 8-byte pairs
-    const int hw = W / 2;
-    for (int e = threadIdx.x; e < H * hw; e += kThreads) {
-      const int h = e / hw, v2 = e - h * hw;
-      const float2 pr = *(const float2*)(src + (size_t)h * W + 2 * v2);
-      P[(h + 1) * PW + 2 * v2 + 1] = pr.x;
-      P[(h + 1) * PW + 2 * v2 + 2] = pr.y;
+    // eight pairs per thread in flight before their LDS writes (large planes would otherwise
+    // pay one memory latency per pass); the loads are clamped, not guarded
+    const int hw = W / 2, n = H * hw;
+    constexpr int KB = 8;
+    for (int e0 = threadIdx.x; e0 < n; e0 += KB * kThreads) {
+      float2 pr[KB];
+#pragma unroll
+      for (int k = 0; k < KB; ++k) {
+        const int e = e0 + k * kThreads;
+        const int ec = e < n ? e : n - 1;
+        const int h = ec / hw, v2 = ec - h * hw;
+        pr[k] = *(const float2*)(src + (size_t)h * W + 2 * v2);
+      }
+#pragma unroll
+      for (int k = 0; k < KB; ++k) {
+        const int e = e0 + k * kThreads;
+        if (e < n) {
+          const int h = e / hw, v2 = e - h * hw;
+          P[(h + 1) * PW + 2 * v2 + 1] = pr[k].x;
+          P[(h + 1) * PW + 2 * v2 + 2] = pr[k].y;
+        }
+      }
     }
   } else {
     for (int e = threadIdx.x; e < H * W; e += kThreads) {

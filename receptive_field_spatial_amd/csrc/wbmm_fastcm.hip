@@ -32,7 +32,7 @@ constexpr int CW = 14, CD = CW * CW, CRT = (CD + 15) / 16;  // window, pixels, r
 constexpr int CQ = 7, CKQ = CQ * CQ;                        // quadrant side, K-steps
 constexpr int SEGP = 50;                                    // LDS floats per quadrant segment
 constexpr int MP = 4 * SEGP + 2;                            // LDS row pitch (floats)
-constexpr int kCmLds = CD * MP * 4;
+constexpr int kCmLds = CD * MP * 4 + CD * 4;  // the matrix, then the column-slot table
 static_assert(kCmLds <= 160 * 1024, "one channel's matrix fits in LDS");
 
 struct CmArgs {
@@ -82,32 +82,54 @@ struct XLoad {
   }
 };
 
-// Stage M_c (row-major (196, 196) in HBM) into LDS: thread j < 196 owns column j (quadrant
-// segment g(j), slot s(j)) and walks the rows, so each row is one contiguous 784-byte read over
-// the threads; eight rows' loads are in flight before their LDS writes.
-__device__ __forceinline__ void stage_matrix(const float* __restrict__ M, int c, float* Ms) {
-  const int j = threadIdx.x;
-  if (j >= CD) return;
-  const int y = j / CW, xx = j - (j / CW) * CW;
-  float* dst = Ms + ((y / 7) * 2 + xx / 7) * SEGP + (y % 7) * 7 + xx % 7;
-  const float* src = M + (size_t)c * CD * CD + j;
-  constexpr int RB = 7;  // 196 = 28 x 7 rows
-  for (int i0 = 0; i0 < CD; i0 += RB) {
-    float v[RB];
+// Stage M_c (row-major (196, 196) in HBM) into LDS: each thread moves 16-byte pieces (rows of 49
+// pieces), thirteen of them in flight before their LDS writes; column j goes to quadrant
+// segment g(j), slot s(j), whose offsets come from a 196-entry table in LDS (`segs`).
+__device__ __forceinline__ void stage_matrix(const float* __restrict__ M, int c, float* Ms,
+                                             const int* segs) {
+  const float4* src = (const float4*)(M + (size_t)c * CD * CD);
+  constexpr int N4 = CD * CD / 4;  // 9604 pieces
+  constexpr int KB = 13;
+  for (int e0 = threadIdx.x; e0 < N4; e0 += KB * kCmThreads) {
+    float4 v[KB];
 #pragma unroll
-    for (int k = 0; k < RB; ++k) v[k] = src[(i0 + k) * CD];
+    for (int k = 0; k < KB; ++k) {
+      const int e = e0 + k * kCmThreads;
+      v[k] = src[e < N4 ? e : N4 - 1];
+    }
 #pragma unroll
-    for (int k = 0; k < RB; ++k) dst[(i0 + k) * MP] = v[k];
+    for (int k = 0; k < KB; ++k) {
+      const int e = e0 + k * kCmThreads;
+      if (e < N4) {
+        const int i = e / 49, j0 = (e - i * 49) * 4;
+        float* row = Ms + i * MP;
+        row[segs[j0]] = v[k].x;
+        row[segs[j0 + 1]] = v[k].y;
+        row[segs[j0 + 2]] = v[k].z;
+        row[segs[j0 + 3]] = v[k].w;
+      }
+    }
   }
 }
 
 __global__ void __launch_bounds__(kCmThreads) k_fwd_cm(CmArgs a) {
   extern __shared__ __attribute__((aligned(16))) float smem_f[];
   float* Ms = smem_f;
+  int* segs = (int*)(smem_f + CD * MP);  // LDS slot of column j within a row
+  for (int j = threadIdx.x; j < CD; j += kCmThreads) {
+    const int y = j / CW, xx = j - (j / CW) * CW;
+    segs[j] = ((y / 7) * 2 + xx / 7) * SEGP + (y % 7) * 7 + xx % 7;
+  }
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int n = lane & 15, g = lane >> 4;
-  const long long lo = a.total * blockIdx.x / gridDim.x;
-  const long long hi = a.total * (blockIdx.x + 1) / gridDim.x;
+  // XCD-aware ranges: workgroups are dealt to the 8 XCDs round-robin (workgroup b runs on XCD
+  // b % 8), so range r = (b % 8) (G / 8) + b / 8 gives each XCD a contiguous run of ranges; the
+  // ranges that share a channel then mostly share an L2, and a matrix staged by one CU is read
+  // from that L2 by its neighbours
+  const int G = gridDim.x;
+  const int rg = G % 8 == 0 ? (int)(blockIdx.x % 8) * (G / 8) + (int)(blockIdx.x / 8) : (int)blockIdx.x;
+  const long long lo = a.total * rg / G;
+  const long long hi = a.total * (rg + 1) / G;
 
   // Per-lane output offsets within a window for r = 0 of each tile (pixel p0 = 16 t + 4 g) and
   // the column p0 % 14 that decides whether p0 + r wraps to the next window row.
@@ -143,7 +165,7 @@ __global__ void __launch_bounds__(kCmThreads) k_fwd_cm(CmArgs a) {
     const int c = (int)(r0 / a.wupc);
     if (c != staged) {
       __syncthreads();  // every wave is done with the previous channel's matrix
-      stage_matrix(a.M, c, Ms);
+      stage_matrix(a.M, c, Ms, segs);
       __syncthreads();
       staged = c;
     }
