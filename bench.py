@@ -51,7 +51,7 @@ def log(*a):
 # kernel -> the source file that defines it. A kernel's hash covers that file and the device
 # headers it includes (directly or through another header); wbmm_launch.hpp (host-side request
 # structs and launcher declarations) and the other kernels' files do not change it.
-KERNEL_FILES = {"k_fwd_ws": "wbmm_fast.hip", "k_bwd_ls": "wbmm_fast.hip",
+KERNEL_FILES = {"k_fwd_ws": "wbmm_fast.hip", "k_bwd_ls": "wbmm_fast.hip", "k_fwd_cm": "wbmm_fastcm.hip",
                 "k_fwd_bf16_w7": "wbmm_fastbf.hip",
                 "k_fwd_bf16_w28": "wbmm_fastbf.hip", "k_fwd_bf16": "wbmm_fastbf.hip",
                 "k_wbmm_fwd": "wbmm_fwd.hip", "k_wbmm_bwd": "wbmm_bwd.hip"}
@@ -468,7 +468,7 @@ def run(args):
             peaks["bf16_mfma_tflops"] if bf16 else peaks["fp32_mfma_tflops"])
     roof["peak_measured"] = meas
     roof["frac_of_measured"] = round(roof["achieved"] / meas, 4)
-    roof["traffic"] = load_traffic(wl.name, kname)
+    roof["traffic"] = load_traffic(wl.name + ("_cached" if args.cached else ""), kname)
     roof["kernel"] = kname
     roof["kernel_us"] = round(ksec * 1e6, 2)
     roof["algorithmic_per_launch"] = kflops if mfma_bound else kbytes
@@ -543,7 +543,8 @@ def _pmc_rows(d):
 
 
 # bench label -> names of the kernels that can be that call's main kernel (fast or general path)
-MAIN_KERNELS = {"k_wbmm_fwd": ("k_fwd_ws", "k_fwd_bf16_w7", "k_fwd_bf16_w28", "k_fwd_bf16", "k_wbmm_fwd"),
+MAIN_KERNELS = {"k_wbmm_fwd": ("k_fwd_ws", "k_fwd_cm", "k_fwd_bf16_w7", "k_fwd_bf16_w28", "k_fwd_bf16",
+                               "k_wbmm_fwd"),
                 "k_wbmm_bwd": ("k_bwd_ls", "k_wbmm_bwd")}
 
 
@@ -704,7 +705,7 @@ def main():
               f"(asked for --gpus {args.gpus}, WORLD_SIZE={world}).", file=sys.stderr)
         sys.exit(2)
     if args.summarize_pmc:
-        summarize_pmc(args.workload, *args.summarize_pmc)
+        summarize_pmc(args.workload + ("_cached" if args.cached else ""), *args.summarize_pmc)
         return
     if args.copy_calibration:
         copy_calibration()

@@ -362,9 +362,18 @@ __device__ __forceinline__ void stage_plane<float>(const float* __restrict__ src
     P[(r + 1) * PW + W + 1] = 0.f;
   }
   if ((W & 1) == 0) {  // planes start at even pixel offsets: 8-byte pairs
-    // eight pairs per thread in flight before their LDS writes (large planes would otherwise
-    // pay one memory latency per pass); the loads are clamped, not guarded
+    // large planes: eight pairs per thread in flight before their LDS writes (they would
+    // otherwise pay one memory latency per pass); the loads are clamped, not guarded
     const int hw = W / 2, n = H * hw;
+    if (n <= 4 * kThreads) {  // small planes: one or a few pairs per thread
+      for (int e = threadIdx.x; e < n; e += kThreads) {
+        const int h = e / hw, v2 = e - h * hw;
+        const float2 pr = *(const float2*)(src + (size_t)h * W + 2 * v2);
+        P[(h + 1) * PW + 2 * v2 + 1] = pr.x;
+        P[(h + 1) * PW + 2 * v2 + 2] = pr.y;
+      }
+      return;
+    }
     constexpr int KB = 8;
     for (int e0 = threadIdx.x; e0 < n; e0 += KB * kThreads) {
       float2 pr[KB];

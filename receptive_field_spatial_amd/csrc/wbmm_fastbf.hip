@@ -49,6 +49,7 @@ struct BfArgs {
   const uint16_t* T;
   uint16_t* y;
   uint16_t* z;  // optional copy of the output (the pre-mix map equals y without a mix)
+  const float* mixw;  // (C, 3, 3) weights of the fused 3x3 mix (MIX kernels), else null
 };
 
 template <int IW_>
@@ -66,10 +67,21 @@ struct BfShape {
   static constexpr int C0 = PT - 1 - (WS - 1) * TP - (WS - 1);
   static_assert(IW == 28 || IW == 56, "shape");
   static_assert(CS % 8 == 0 && CS >= PT + 16, "copies");
+  // fused 3x3 mix: each wave stages the pre-mix map of its images as bf16 planes with a zero
+  // halo, image column v at plane column v + 2 (so 2-pixel runs are 4-byte aligned), pitch ZP
+  static constexpr int ZP = IW + 4, ZPLANE = (IH + 2) * ZP;
+  static constexpr int ZWAVE = IPW * ZPLANE;      // bf16 per wave
+  static constexpr int CPAIR = IW / 2;            // column pairs per image row
+  static constexpr int RSEG = 64 / (IPW * CPAIR); // row segments per column pair (1 or 2)
+  static constexpr int RLEN = IH / RSEG;
+  static_assert(RSEG >= 1 && IH % RSEG == 0 && IPW * CPAIR * RSEG <= 64, "mix tasks");
 };
 
 template <class S>
 constexpr int bf_lds_bytes() { return 8 * S::CS * 2; }
+// with the fused mix: the table copies, then 4 waves' staging planes
+template <class S>
+constexpr int bf_mix_lds_bytes() { return 8 * S::CS * 2 + 4 * S::ZWAVE * 2; }
 
 // Pixel offset of window n's first pixel within its image plane (window n of a wave-unit lies in
 // image n / NWIN of it).
@@ -154,9 +166,22 @@ __device__ __forceinline__ void stage_table(uint16_t* copies, const uint16_t* T,
 // one wave-unit (16 windows) of every unit and has the next unit's pixels in flight while it
 // contracts and stores the current one.
 constexpr int kWgPerCu = 4;  // resident workgroups per CU (kWgPerCu waves per SIMD)
+constexpr int kWgPerCuMix = 3;  // with the fused mix's staging planes
 
-template <class S, bool ZS, bool ROT = false>
-__global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWgPerCu, 8)))
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// MIX: the 3x3 inter-block mix is fused [gecl.asia reading notes, "Method" point 3]: the output
+// tiles (z, rounded to bf16) go to the wave's staging planes instead of memory (z_save still
+// gets them), and once the wave has contracted its images it computes
+// y[h][v] = sum_{u,t} W[u][t] z[h+u-1][v+t-1] (fp32 sums of the bf16 z, zero outside the image,
+// RNE to bf16) from the planes: a lane walks a pair of columns down its image with a sliding
+// 3 x 4 register window (three 4-byte LDS reads per row) and stores the pair as 4 bytes.
+template <class S, bool ZS, bool ROT = false, bool MIX = false>
+__global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(MIX ? kWgPerCuMix : kWgPerCu, 8)))
 k_fwd_bf16(BfArgs a) {
   extern __shared__ __attribute__((aligned(16))) uint16_t smem_h[];
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -183,6 +208,19 @@ k_fwd_bf16(BfArgs a) {
   const int bi0 = S::C0 - xi;          // row t subtracts TP t, which keeps the copy index
   const int rc = (-bi0) & 7;           // copy whose runs from bi (mod 8) are 16-byte aligned
   const int ab = rc * S::CS + bi0 + rc + S::TP * kq + 8 * kh - S::TP * (S::WS - 1);
+
+  // MIX: this wave's staging planes, zeroed once (the halo stays zero: tiles only write the
+  // interior); zoff: where this lane's 8 output pixels of tile 0 go
+  uint16_t* zst = copies + 8 * S::CS + wave * S::ZWAVE;
+  int zoff = 0;
+  if constexpr (MIX) {
+    for (int e = lane; e < S::ZWAVE / 2; e += 64) ((uint32_t*)zst)[e] = 0u;
+    const int k = n % S::NWIN;
+    const int row0 = (k / S::NWX) * S::WS + (gq & 1);
+    const int col0 = (k % S::NWX) * S::WS + (gq < 2 ? 0 : S::WS - 8);
+    zoff = (n / S::NWIN) * S::ZPLANE + (row0 + 1) * S::ZP + col0 + 2;
+    wave_lds_sync();
+  }
 
   auto plane = [&](const UnitPos& p) {  // element offset of this lane's image plane
     const int ic = min(im, p.nimg - 1);  // images past the batch read its last image
@@ -261,12 +299,69 @@ k_fwd_bf16(BfArgs a) {
         const auto hi = __builtin_amdgcn_permlane16_swap(pk[0][1], pk[1][1], false, false);
         const u32x4 v = u32x4{lo[0], hi[0], lo[1], hi[1]};
         const size_t o = obase + (size_t)(T0 + t) * S::IW;
-        *(u32x4a*)(a.y + o) = v;
+        if constexpr (MIX) {
+          uint32_t* zp = (uint32_t*)(zst + zoff + (T0 + t) * S::ZP);
+          zp[0] = v.x;
+          zp[1] = v.y;
+          zp[2] = v.z;
+          zp[3] = v.w;
+        } else {
+          *(u32x4a*)(a.y + o) = v;
+        }
         if constexpr (ZS) *(u32x4a*)(a.z + o) = v;
       }
     };
     half(std::integral_constant<int, 0>{}, std::integral_constant<int, 8>{});
     half(std::integral_constant<int, 8>{}, std::integral_constant<int, 6>{});
+    if constexpr (MIX) {
+      wave_lds_sync();  // every lane's tiles are in the planes
+      if (lane < S::IPW * S::CPAIR * S::RSEG) {
+        const int i = lane / (S::CPAIR * S::RSEG), rem = lane - i * (S::CPAIR * S::RSEG);
+        const int cp = rem / S::RSEG, h0 = (rem - cp * S::RSEG) * S::RLEN;
+        float w9[9];
+#pragma unroll
+        for (int q = 0; q < 9; ++q) w9[q] = a.mixw[pos.c * 9 + q];
+        // plane column of image column 2 cp - 2 (the word holding columns 2cp-1 .. 2cp+2 starts
+        // one pixel earlier, at an even plane column)
+        const uint32_t* zr = (const uint32_t*)(zst + i * S::ZPLANE + 2 * cp);
+        // win[a][0..3] = z(h + a - 1, 2cp - 1 .. 2cp + 2): words 0..2 hold columns 2cp-2 .. 2cp+3
+        auto row = [&](int hp, float (&r4)[4]) {  // hp: plane row
+          const uint32_t w0 = zr[hp * (S::ZP / 2)], w1 = zr[hp * (S::ZP / 2) + 1],
+                         w2 = zr[hp * (S::ZP / 2) + 2];
+          r4[0] = __uint_as_float(w0 & 0xffff0000u);
+          r4[1] = __uint_as_float(w1 << 16);
+          r4[2] = __uint_as_float(w1 & 0xffff0000u);
+          r4[3] = __uint_as_float(w2 << 16);
+        };
+        float win[3][4];
+        row(h0, win[0]);
+        row(h0 + 1, win[1]);
+        const int ii = wave * S::IPW + i;  // image of the unit (past the batch: not stored)
+        const bool real = ii < pos.nimg;
+        uint16_t* yrow = a.y + ((size_t)(pos.img0 + (real ? ii : 0)) * a.C + pos.c) * S::PLANE + 2 * cp;
+#pragma unroll 4
+        for (int h = h0; h < h0 + S::RLEN; ++h) {
+          row(h + 2, win[2]);
+          float y0 = 0.f, y1 = 0.f;
+#pragma unroll
+          for (int u = 0; u < 3; ++u)
+#pragma unroll
+            for (int t = 0; t < 3; ++t) {
+              y0 = fmaf(w9[u * 3 + t], win[u][t], y0);
+              y1 = fmaf(w9[u * 3 + t], win[u][t + 1], y1);
+            }
+          if (real)
+            *(uint32_t*)(yrow + (size_t)h * S::IW) =
+                __builtin_bit_cast(uint32_t, __builtin_convertvector((v2f{y0, y1}), v2bf));
+#pragma unroll
+          for (int t = 0; t < 4; ++t) {
+            win[0][t] = win[1][t];
+            win[1][t] = win[2][t];
+          }
+        }
+      }
+      wave_lds_sync();  // the planes are read before the next unit's tiles overwrite them
+    }
     if constexpr (MORE) convert(conv);
     return nxt;
   };
@@ -652,7 +747,13 @@ static_assert(fits(bf_lds_bytes<BfShape<28>>()) && fits(bf_lds_bytes<BfShape<56>
                   fits(bf_lds_bytes<Bf7Shape<56>>()),
               "resident workgroups per CU");
 
-template <class S, class K>
+static_assert((bf_mix_lds_bytes<BfShape<28>>() + kLdsGranule - 1) / kLdsGranule * kLdsGranule *
+                      kWgPerCuMix <= kLdsPerCu &&
+                  (bf_mix_lds_bytes<BfShape<56>>() + kLdsGranule - 1) / kLdsGranule * kLdsGranule *
+                      kWgPerCuMix <= kLdsPerCu,
+              "resident workgroups per CU with the fused mix");
+
+template <class S, bool MIX = false, class K>
 hipError_t launch_bf(const FwdRequest& r, hipStream_t st, K with_z, K without_z) {
   BfArgs a{};
   a.B = r.B;
@@ -662,7 +763,11 @@ hipError_t launch_bf(const FwdRequest& r, hipStream_t st, K with_z, K without_z)
   a.T = (const uint16_t*)r.T;
   a.y = (uint16_t*)r.y;
   a.z = (uint16_t*)r.zsave;
-  const int lds = bf_lds_bytes<S>();
+  a.mixw = MIX ? r.mixw : nullptr;
+  int lds;
+  if constexpr (MIX) lds = bf_mix_lds_bytes<S>();
+  else lds = bf_lds_bytes<S>();
+  const int per_cu = MIX ? kWgPerCuMix : kWgPerCu;
   const K fn = a.z ? with_z : without_z;
   hipError_t e = hipFuncSetAttribute((const void*)fn, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
   if (e != hipSuccess) return e;
@@ -671,7 +776,7 @@ hipError_t launch_bf(const FwdRequest& r, hipStream_t st, K with_z, K without_z)
       hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
     cus = 256;
   const int units = a.C * a.groups;
-  const int grid = units < kWgPerCu * cus ? units : kWgPerCu * cus;
+  const int grid = units < per_cu * cus ? units : per_cu * cus;
   return launch_main(fn, dim3(grid), dim3(kThreads), lds, st, a);
 }
 
@@ -703,6 +808,27 @@ static_assert(2 * ((bf28_lds_bytes<Bf28Shape<56>>() + kLdsGranule - 1) / kLdsGra
               "two w = 28 workgroups per CU");
 
 }  // namespace
+
+// bf16 maps with the 3x3 mix, w = 14 on 28x28 / 56x56 images: the mix fused into the fast
+// forward (y and z_save bf16).
+bool fast_bf16_fused_mix_ok(const FwdRequest& r) {
+  if (!r.mixw) return false;
+  FwdRequest q = r;
+  q.mixw = nullptr;
+  return fast_bf16_forward_ok(q) && (bf_shape(q) == BF_28 || bf_shape(q) == BF_56);
+}
+
+hipError_t launch_forward_fast_bf16_mix(const FwdRequest& r, hipStream_t st) {
+  switch (bf_shape(r)) {
+    case BF_28:
+      return launch_bf<BfShape<28>, true>(r, st, k_fwd_bf16<BfShape<28>, true, false, true>,
+                                          k_fwd_bf16<BfShape<28>, false, false, true>);
+    case BF_56:
+      return launch_bf<BfShape<56>, true>(r, st, k_fwd_bf16<BfShape<56>, true, false, true>,
+                                          k_fwd_bf16<BfShape<56>, false, false, true>);
+    default: return hipErrorInvalidValue;
+  }
+}
 
 bool fast_bf16_forward_ok(const FwdRequest& r) {
   // unit indices (C * groups) are ints

@@ -143,7 +143,7 @@ bool forward_plan_ok(const FwdRequest& r) {
 // bf16 maps with the mix on a fast bf16 shape: the fast forward writes z (bf16) to z_save or the
 // workspace, then a plane-staged pass applies the mix (y = bf16(mix(bf16 z))).
 static bool fast_bf16_mix_ok(const FwdRequest& r) {
-  if (!r.mixw || r.Tsub || !r.in_bf16 || !r.out_bf16) return false;
+  if (!r.mixw || r.Tsub || !r.in_bf16 || !r.out_bf16 || fast_bf16_fused_mix_ok(r)) return false;
   FwdRequest q = r;
   q.mixw = nullptr;
   q.zsave = nullptr;
@@ -174,6 +174,7 @@ hipError_t launch_forward(const FwdRequest& r, hipStream_t st) {
     if (e != hipSuccess) return e;
     return launch_mix_fwd_f32_route(z, r.mixw, (float*)r.y, r.B, r.C, r.H, r.W, st);
   }
+  if (fast_bf16_fused_mix_ok(r)) return launch_forward_fast_bf16_mix(r, st);  // w = 14
   if (fast_bf16_mix_ok(r)) {
     FwdRequest q = r;
     uint16_t* zb = (uint16_t*)(r.zsave ? r.zsave : r.ws);

@@ -85,6 +85,9 @@ hipError_t launch_forward_fast_cm(const FwdRequest& r, float* out, float* out2, 
 // images, w = 7 and w = 28 on 56x56 images.
 bool fast_bf16_forward_ok(const FwdRequest& r);
 hipError_t launch_forward_fast_bf16(const FwdRequest& r, hipStream_t st);
+// The same w = 14 kernel with the 3x3 mix fused (bf16 y and z_save).
+bool fast_bf16_fused_mix_ok(const FwdRequest& r);
+hipError_t launch_forward_fast_bf16_mix(const FwdRequest& r, hipStream_t st);
 
 // Fixed-order sum of per-workgroup fp64 partials: dT[c][q] = sum_k partT[c][k][q] (and dWmix).
 hipError_t launch_bwd_reduce(const double* partT, const double* partW, int parts, int C, int L,

@@ -43,7 +43,7 @@ struct Geo {
   FastDiv fd_w, fd_nW, fd_nWin, fd_W, fd_HW, fd_KQ, fd_WP, fd_d;
 };
 
-inline FastDiv make_fastdiv(uint32_t d) {
+__host__ __device__ inline FastDiv make_fastdiv(uint32_t d) {
   FastDiv f{};
   f.d = d;
   f.m = d <= 1 ? 0ull : UINT64_MAX / d + 1;

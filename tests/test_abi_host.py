@@ -125,8 +125,10 @@ def test_forward_workspace_rules(lib):
     # workspace: the query (which has no dtype argument) reports the larger need
     assert lib.wbmm_forward_workspace_bytes(1, 2, 128, 128, 14, 0, 1, 1) == need
     assert lib.wbmm_forward_workspace_bytes(1, 2, 100, 100, 14, 0, 1, 0) == 0  # 64 windows: fused
-    # fused in-kernel for fp32; bf16 maps on this fast bf16 shape keep z in the workspace
-    assert lib.wbmm_forward_workspace_bytes(64, 192, 28, 28, 14, 0, 1, 0) == 64 * 192 * 28 * 28 * 2
+    # fused in-kernel for fp32 and, on this fast bf16 shape, for bf16 maps: no workspace; the
+    # bf16 w = 7 fast shape keeps z in the workspace for its separate mix pass
+    assert lib.wbmm_forward_workspace_bytes(64, 192, 28, 28, 14, 0, 1, 0) == 0
+    assert lib.wbmm_forward_workspace_bytes(8, 4, 56, 56, 7, 0, 1, 0) == 8 * 4 * 56 * 56 * 2
     assert lib.wbmm_forward_workspace_bytes(64, 192, 28, 28, 14, 0, 1, 1) == 0
     assert lib.wbmm_forward_workspace_bytes(1, 2, 8, 8, 0, 0, 0, 0) == 0       # invalid -> 0
     st = fwd(lib, B=1, C=2, H=128, W=128, w=14, mix=0x900000, y=0x40000000, ws=None, wsb=0)

@@ -345,18 +345,40 @@ def _window_shift(x, w, dy, dx):
 @pytest.mark.parametrize("w,hw,B,C", [(14, 56, 4, 800), (14, 56, 7, 300), (14, 28, 16, 1100),
                                       (7, 56, 4, 900), (7, 56, 5, 300), (28, 56, 17, 40)])
 def test_forward_bf16_fast_shift_bitwise(w, hw, B, C):
+    _bf16_shift_case(w, hw, B, C, mix=False)
+
+
+@pytest.mark.parametrize("hw,B,C", [(28, 16, 700), (28, 37, 300), (56, 5, 400)])
+def test_forward_bf16_fused_mix_shift_bitwise(hw, B, C):
+    """The w = 14 bf16 forward with the 3x3 mix fused: one-hot tables per channel and the identity
+    mix make y and z_save the window-shifted input bit for bit, which pins the staging of the
+    output tiles, the halo and the column-pair sweep over many units and ragged batches."""
+    _bf16_shift_case(14, hw, B, C, mix=True)
+
+
+def _bf16_shift_case(w, hw, B, C, mix):
     """One-hot tables at a different offset in every channel: the output is the input shifted
     inside each window (exact in bf16). More units than resident workgroups, so workgroups walk
     several units and rebuild the staged table when the channel changes."""
-    say(f"forward bf16 fast shift w={w} {hw}x{hw} B={B} C={C}")
+    say(f"forward bf16 fast shift w={w} {hw}x{hw} B={B} C={C} mix={mix}")
     x = synth.round_to_bf16(synth.normal_f32((B, C, hw, hw), 1.0, seed=34))
     L1 = 2 * w - 1
     dy = (np.arange(C) * 5) % L1 - (w - 1)
     dx = (np.arange(C) * 11 + 3) % L1 - (w - 1)
     T = np.zeros((C, L1, L1), np.float32)
     T[np.arange(C), dy + w - 1, dx + w - 1] = 1.0
-    y = R().wbmm_forward(dev_bf16(x), w, T=dev_bf16(T), out_dtype=torch.bfloat16)
-    assert np.array_equal(host(y), _window_shift(x, w, dy, dx))
+    want = _window_shift(x, w, dy, dx)
+    if not mix:
+        y = R().wbmm_forward(dev_bf16(x), w, T=dev_bf16(T), out_dtype=torch.bfloat16)
+        assert np.array_equal(host(y), want)
+        return
+    W9 = np.zeros((C, 3, 3), np.float32)
+    W9[:, 1, 1] = 1.0
+    z = torch.empty((B, C, hw, hw), dtype=torch.bfloat16, device="cuda")
+    y = R().wbmm_forward(dev_bf16(x), w, T=dev_bf16(T), mix_w=dev(W9), z_save=z,
+                         out_dtype=torch.bfloat16)
+    assert np.array_equal(host(z), want)
+    assert np.array_equal(host(y), want)
 
 
 # ----------------------------------------------------------------------------- workloads
