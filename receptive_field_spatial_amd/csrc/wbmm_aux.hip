@@ -233,10 +233,14 @@ __global__ void __launch_bounds__(kThreads) k_mix_bwd_weight(const TM* __restric
   if (threadIdx.x < 9) dw9[c * 9 + threadIdx.x] = (float)red[threadIdx.x][0];
 }
 
-// dT[c][q] = sum over workgroups k (in order) of partT[c][k][q]; the same for the 9 dWmix values.
+// dT[c][q] = sum over partials k (in order) of partT[c][k][q]; the same for the 9 dWmix values
+// over their own partials. Workgroup (c, j) takes entries q = 256 j .. 256 j + 255 of channel c
+// (one per thread, so each thread waits for one batch of loads); workgroups with j = 0 also sum
+// dWmix.
 __global__ void __launch_bounds__(kThreads) k_bwd_reduce(const double* __restrict__ partT,
+                                                         int partsT,
                                                          const double* __restrict__ partW,
-                                                         int parts, int L, float* __restrict__ dT,
+                                                         int partsW, int L, float* __restrict__ dT,
                                                          float* __restrict__ dmixw) {
   const int c = blockIdx.x;
   // partials are loaded 8 at a time (all in flight together) and added in order k = 0, 1, ...
@@ -252,19 +256,25 @@ __global__ void __launch_bounds__(kThreads) k_bwd_reduce(const double* __restric
     }
     return s;
   };
-  if (dT) {
-    for (int q = threadIdx.x; q < L; q += kThreads)
-      dT[(size_t)c * L + q] = (float)sum(partT + (size_t)c * parts * L + q, (size_t)L, parts);
-  }
-  if (dmixw && threadIdx.x < 9)
-    dmixw[c * 9 + threadIdx.x] = (float)sum(partW + (size_t)c * parts * 9 + threadIdx.x, 9, parts);
+  const int q = blockIdx.y * kThreads + threadIdx.x;
+  if (dT && q < L)
+    dT[(size_t)c * L + q] = (float)sum(partT + (size_t)c * partsT * L + q, (size_t)L, partsT);
+  if (dmixw && blockIdx.y == 0 && threadIdx.x < 9)
+    dmixw[c * 9 + threadIdx.x] =
+        (float)sum(partW + (size_t)c * partsW * 9 + threadIdx.x, 9, partsW);
+}
+
+hipError_t launch_bwd_reduce2(const double* partT, int partsT, const double* partW, int partsW,
+                              int C, int L, float* dT, float* dmixw, hipStream_t st) {
+  const int gy = dT && L > 0 ? (L + kThreads - 1) / kThreads : 1;
+  hipLaunchKernelGGL(k_bwd_reduce, dim3(C, gy), dim3(kThreads), 0, st, partT, partsT, partW,
+                     partsW, L, dT, dmixw);
+  return hipGetLastError();
 }
 
 hipError_t launch_bwd_reduce(const double* partT, const double* partW, int parts, int C, int L,
                              float* dT, float* dmixw, hipStream_t st) {
-  hipLaunchKernelGGL(k_bwd_reduce, dim3(C), dim3(kThreads), 0, st, partT, partW, parts, L, dT,
-                     dmixw);
-  return hipGetLastError();
+  return launch_bwd_reduce2(partT, parts, partW, parts, C, L, dT, dmixw, st);
 }
 
 hipError_t launch_mix_fwd(const float* z, const float* w9, void* y, int out_bf16, int B, int C,
@@ -539,9 +549,309 @@ __global__ void __launch_bounds__(kThreads) k_mix_fwd_planes(
   }
 }
 
+// Direct 3x3 mix passes for NCHW planes of even width (any height): no staging and no barrier
+// before the arithmetic. A lane takes a column pair (2cp, 2cp + 1) and a run of kMixRun rows
+// h0 .. h0 + kMixRun - 1 of one plane and loads its own pixel pair of the kMixRun + 2 rows
+// h0 - 1 .. h0 + kMixRun (a 4-byte word for bf16, a float2 for fp32) through a buffer resource
+// spanning the plane: the rows above and below the plane fall outside it and read as zero, which
+// is the mix's zero padding, and stores outside it are dropped, so no access needs a branch. The
+// lanes of a wave hold consecutive column pairs of whole row runs, so the neighbouring pixels
+// 2cp - 1 and 2cp + 2 come from the lanes beside it by DPP wave shifts (lanes at a row's ends take
+// zero); rows wider than 64 pairs are split over waves and the two lanes at a wave's ends load the
+// pixel beyond it themselves. n[r][j] below is pixel (h0 - 1 + r, 2cp - 1 + j), j = 0..3. A wave
+// takes kMixNpw small planes (one wave unit each) of one channel with all their loads in flight at
+// once; larger planes are split into chunks of four wave units, one workgroup per chunk.
+//   forward: y[h][v] = sum_{u,t} W[u][t] z[h+u-1][v+t-1]            [gecl.asia reading notes,
+//   adjoint: g[h][v] = sum_{u,t} W[u][t] dy[h-u+1][v-t+1]             "Method" point 3: the
+//   weights: dW[u][t] = sum_{h,v} z[h][v] dy[h-u+1][v-t+1]            inter-block 3x3 mix]
+// (k = 3u + t in a fixed fmaf order per output, the same order as the plane-staged kernels, so the
+// two give equal bits; bf16 outputs round to nearest even). dW: fp32 sums over a lane's pixels of
+// one plane (at most 2 kMixRun products of map values per weight), then fp64 over its planes and
+// over the wave in a fixed order (through LDS: four lanes per weight add 16 lanes' values each,
+// then the four sums are paired); a wave of small planes leaves partial partW[c][q][9] (planes
+// b = q kMixNpw ..), a chunk the sum of its four waves in order, partW[c][b][chunk][9];
+// k_bwd_reduce adds them per channel in order.
+constexpr int kMixRun = 7;
+constexpr int kMixNpw = 2;  // small planes of one channel per wave
+
+// Wave units per plane: a wave holds 64 / CP whole row runs (CP = W / 2 <= 64 pairs per row) or
+// 64 pairs of one run.
+__host__ __device__ inline int mix_direct_wpp(int H, int W) {
+  const int CP = W / 2, nseg = (H + kMixRun - 1) / kMixRun;
+  if (CP <= 64) {
+    const int spw = 64 / CP;
+    return (nseg + spw - 1) / spw;
+  }
+  return nseg * ((CP + 63) / 64);
+}
+__host__ __device__ inline int mix_direct_chunks(int H, int W) {
+  const int wpp = mix_direct_wpp(H, W);
+  return wpp == 1 ? 1 : (wpp + 3) / 4;
+}
+
+// Planes the direct passes take: even width, byte offsets (rows above included) below 2^31.
+inline bool mix_direct_ok(int H, int W) {
+  return (W & 1) == 0 && (long long)(H + 2) * W * 4 < (1LL << 30);
+}
+
+typedef float mix_v2f __attribute__((ext_vector_type(2)));
+typedef __bf16 mix_v2bf __attribute__((ext_vector_type(2)));
+
+// A plane as a raw buffer of `bytes` bytes: loads past it read 0, stores past it are dropped.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t plane_rsrc(const void* base, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, bytes, 0x00020000);
+}
+
+template <typename TM>
+struct MixPair;
+template <>
+struct MixPair<uint16_t> {  // two bf16 pixels as one word
+  typedef uint32_t T;
+  static __device__ __forceinline__ T load(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+    return __builtin_amdgcn_raw_buffer_load_b32(r, (int)off, 0, 0);
+  }
+  static __device__ __forceinline__ float lo(T w) { return __uint_as_float(w << 16); }
+  static __device__ __forceinline__ float hi(T w) { return __uint_as_float(w & 0xffff0000u); }
+  static __device__ __forceinline__ void store(__amdgpu_buffer_rsrc_t r, uint32_t off, float a,
+                                               float b) {
+    const uint32_t v = __builtin_bit_cast(uint32_t, __builtin_convertvector((mix_v2f{a, b}), mix_v2bf));
+    __builtin_amdgcn_raw_buffer_store_b32(v, r, (int)off, 0, 0);
+  }
+};
+template <>
+struct MixPair<float> {
+  typedef float2 T;
+  static __device__ __forceinline__ T load(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+    return __builtin_bit_cast(float2, __builtin_amdgcn_raw_buffer_load_b64(r, (int)off, 0, 0));
+  }
+  static __device__ __forceinline__ float lo(T w) { return w.x; }
+  static __device__ __forceinline__ float hi(T w) { return w.y; }
+  static __device__ __forceinline__ void store(__amdgpu_buffer_rsrc_t r, uint32_t off, float a,
+                                               float b) {
+    typedef uint32_t u32x2v __attribute__((ext_vector_type(2)));
+    __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2v, make_float2(a, b)), r,
+                                          (int)off, 0, 0);
+  }
+};
+
+// x of lane i - 1 (CTRL 0x138, wave_shr:1) or i + 1 (0x130, wave_shl:1); 0 past the wave's ends
+template <int CTRL>
+__device__ __forceinline__ float dpp_wave_f32(float x) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), CTRL, 0xf, 0xf, true));
+}
+// x + (x of the lane given by a quad permutation)
+template <int CTRL>
+__device__ __forceinline__ double add_quad_f64(double x) {
+  const uint64_t b = (uint64_t)__double_as_longlong(x);
+  const int lo = __builtin_amdgcn_mov_dpp((int)(uint32_t)b, CTRL, 0xf, 0xf, true);
+  const int hi = __builtin_amdgcn_mov_dpp((int)(uint32_t)(b >> 32), CTRL, 0xf, 0xf, true);
+  return x + __longlong_as_double((long long)(((uint64_t)(uint32_t)hi << 32) | (uint32_t)lo));
+}
+
+struct MixDirectArgs {
+  const void* src;   // z (forward) or dy (adjoint)
+  const void* zs;    // adjoint: saved z for the weight partials, or null
+  const float* w9;   // (C, 3, 3)
+  void* dst;         // y or g
+  double* partW;     // adjoint with zs: see above
+  int B, C, H, W, wpp, chunks;
+};
+
+template <typename TM, bool ADJ>
+__global__ void __launch_bounds__(kThreads) k_mix_direct(MixDirectArgs a) {
+  typedef MixPair<TM> MP;
+  typedef typename MP::T PT;
+  constexpr int R = kMixRun, NPW = kMixNpw, PS = (int)sizeof(PT);
+  __shared__ __attribute__((aligned(16))) double red[ADJ ? 4 * 9 * 64 : 1];
+  __shared__ double wsum[4][9];
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int CP = a.W >> 1, nseg = (a.H + R - 1) / R;
+  const bool small = a.wpp == 1;  // uniform
+  const int groups = (a.B + NPW - 1) / NPW;
+  // this wave (all uniform): planes (b0 + j, c), j < nb, and wave unit wu of each
+  int c, b0, nb, wu, chunk = 0, wi = 0;
+  bool wlive;
+  if (small) {
+    wi = blockIdx.x * 4 + wave;
+    wlive = wi < a.C * groups;
+    c = wlive ? wi / groups : 0;
+    b0 = wlive ? (wi - c * groups) * NPW : 0;
+    nb = min(NPW, a.B - b0);
+    wu = 0;
+  } else {
+    const int p = blockIdx.x / a.chunks;
+    chunk = blockIdx.x - p * a.chunks;
+    wu = chunk * 4 + wave;
+    wlive = wu < a.wpp;
+    b0 = p / a.C;
+    c = p - b0 * a.C;
+    nb = 1;
+  }
+  int seg, cp;
+  bool task;
+  if (CP <= 64) {
+    const int spw = 64 / CP, s = lane / CP;
+    seg = wu * spw + s;
+    cp = lane - s * CP;
+    task = wlive && s < spw && seg < nseg;
+  } else {
+    const int wpr = (CP + 63) / 64;
+    seg = wu / wpr;
+    cp = (wu - seg * wpr) * 64 + lane;
+    task = wlive && cp < CP;
+  }
+  if (!task) cp = 0;
+  const int h0 = seg * R;
+  const uint32_t rowb = (uint32_t)a.W * sizeof(TM);
+  const int pbytes = a.H * (int)rowb;
+  // byte offset of this lane's pair in row h0 - 1 + r: a row above the plane wraps to an offset
+  // >= 2^31, past the plane; lanes without a task start at 2^31
+  const uint32_t off0 = task ? (uint32_t)(h0 - 1) * rowb + (uint32_t)(cp * PS) : 0x80000000u;
+  float w[9];
+#pragma unroll
+  for (int k = 0; k < 9; ++k) w[k] = a.w9[c * 9 + k];
+  const size_t pstride = (size_t)a.C * a.H * a.W;  // elements from image b to b + 1
+  const size_t pbase = ((size_t)b0 * a.C + c) * a.H * a.W;
+  // every load of the wave's planes in flight before the first sum
+  PT own[NPW][R + 2];
+  PT zr[NPW][R];
+#pragma unroll
+  for (int j = 0; j < NPW; ++j) {
+    if (j >= nb) break;  // uniform
+    const __amdgpu_buffer_rsrc_t rs = plane_rsrc((const TM*)a.src + pbase + j * pstride, pbytes);
+#pragma unroll
+    for (int r = 0; r < R + 2; ++r) own[j][r] = MP::load(rs, off0 + r * rowb);
+    if constexpr (ADJ) {
+      if (a.zs) {
+        const __amdgpu_buffer_rsrc_t rz = plane_rsrc((const TM*)a.zs + pbase + j * pstride, pbytes);
+#pragma unroll
+        for (int i = 0; i < R; ++i) zr[j][i] = MP::load(rz, off0 + (i + 1) * rowb);
+      }
+    }
+  }
+  double dacc[9];
+#pragma unroll
+  for (int k = 0; k < 9; ++k) dacc[k] = 0.0;
+#pragma unroll
+  for (int j = 0; j < NPW; ++j) {
+    if (j >= nb) break;  // uniform
+    float n[R + 2][4];
+#pragma unroll
+    for (int r = 0; r < R + 2; ++r) {
+      n[r][1] = MP::lo(own[j][r]);
+      n[r][2] = MP::hi(own[j][r]);
+      // the pixels beside the pair: the neighbouring lanes' pairs
+      const float lft = dpp_wave_f32<0x138>(n[r][2]);
+      const float rgt = dpp_wave_f32<0x130>(n[r][1]);
+      n[r][0] = cp > 0 ? lft : 0.f;
+      n[r][3] = cp < CP - 1 ? rgt : 0.f;
+    }
+    if (CP > 64) {  // uniform: rows split over waves; the end lanes load across the split
+      const __amdgpu_buffer_rsrc_t rs = plane_rsrc((const TM*)a.src + pbase + j * pstride, pbytes);
+#pragma unroll
+      for (int r = 0; r < R + 2; ++r) {
+        if (task && lane == 0 && cp > 0) n[r][0] = MP::hi(MP::load(rs, off0 + r * rowb - PS));
+        if (task && lane == 63 && cp < CP - 1) n[r][3] = MP::lo(MP::load(rs, off0 + r * rowb + PS));
+      }
+    }
+    const __amdgpu_buffer_rsrc_t rd = plane_rsrc((const TM*)a.dst + pbase + j * pstride, pbytes);
+    float fw[9];
+#pragma unroll
+    for (int k = 0; k < 9; ++k) fw[k] = 0.f;
+#pragma unroll
+    for (int i = 0; i < R; ++i) {
+      float o0 = 0.f, o1 = 0.f;
+#pragma unroll
+      for (int k = 0; k < 9; ++k) {
+        const int u = k / 3, tt = k % 3;
+        if constexpr (ADJ) {  // dy[h-u+1][v-t+1]: row i + 2 - u, column (of pixel 2cp) 2 - t
+          o0 = fmaf(w[k], n[i + 2 - u][2 - tt], o0);
+          o1 = fmaf(w[k], n[i + 2 - u][3 - tt], o1);
+        } else {              // z[h+u-1][v+t-1]: row i + u, column t
+          o0 = fmaf(w[k], n[i + u][tt], o0);
+          o1 = fmaf(w[k], n[i + u][tt + 1], o1);
+        }
+      }
+      MP::store(rd, off0 + (i + 1) * rowb, o0, o1);  // rows past the plane are dropped
+      if constexpr (ADJ) {
+        if (a.zs) {
+          const float z0 = MP::lo(zr[j][i]), z1 = MP::hi(zr[j][i]);
+#pragma unroll
+          for (int k = 0; k < 9; ++k) {
+            const int u = k / 3, tt = k % 3;
+            fw[k] = fmaf(z0, n[i + 2 - u][2 - tt], fw[k]);
+            fw[k] = fmaf(z1, n[i + 2 - u][3 - tt], fw[k]);
+          }
+        }
+      }
+    }
+#pragma unroll
+    for (int k = 0; k < 9; ++k) dacc[k] += (double)fw[k];
+  }
+  if constexpr (ADJ) {
+    if (!a.zs) return;  // uniform
+    // wave sums: red[wave][k][lane]; lane 4k + q adds lanes 16q .. 16q + 15 of weight k in order,
+    // then (q0 + q1) + (q2 + q3) by quad permutations, left in lane 4k
+    double* rw = red + wave * 9 * 64;
+#pragma unroll
+    for (int k = 0; k < 9; ++k) rw[k * 64 + lane] = dacc[k];
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    const int kk = min(lane >> 2, 8), q = lane & 3;
+    const double* rp = rw + kk * 64 + 16 * q;
+    double sum = 0.0;
+#pragma unroll
+    for (int i = 0; i < 16; i += 2) {
+      const double2 v = *(const double2*)(rp + i);
+      sum += v.x;
+      sum += v.y;
+    }
+    sum = add_quad_f64<0xB1>(sum);  // quad_perm [1, 0, 3, 2]
+    sum = add_quad_f64<0x4E>(sum);  // quad_perm [2, 3, 0, 1]
+    const bool holder = lane < 36 && q == 0;
+    if (small) {
+      if (holder && wlive) a.partW[(size_t)wi * 9 + kk] = sum;
+      return;
+    }
+    if (holder) wsum[wave][kk] = sum;
+    __syncthreads();
+    if (threadIdx.x < 9) {
+      const int k = threadIdx.x;
+      a.partW[(((size_t)c * a.B + b0) * a.chunks + chunk) * 9 + k] =
+          ((wsum[0][k] + wsum[1][k]) + wsum[2][k]) + wsum[3][k];
+    }
+  }
+}
+
+template <typename TM, bool ADJ>
+hipError_t launch_mix_direct(const TM* src, const TM* zs, const float* w9, TM* dst, double* partW,
+                             int B, int C, int H, int W, hipStream_t st) {
+  if (!mix_direct_ok(H, W) || B < 1 || C < 1 || H < 1) return hipErrorInvalidValue;
+  MixDirectArgs a{};
+  a.src = src;
+  a.zs = zs;
+  a.w9 = w9;
+  a.dst = dst;
+  a.partW = partW;
+  a.B = B;
+  a.C = C;
+  a.H = H;
+  a.W = W;
+  a.wpp = mix_direct_wpp(H, W);
+  a.chunks = mix_direct_chunks(H, W);
+  const long long waves = (long long)C * ((B + kMixNpw - 1) / kMixNpw);
+  const long long grid = a.wpp == 1 ? (waves + 3) / 4 : (long long)B * C * a.chunks;
+  if (grid > 0x7fffffffLL) return hipErrorInvalidValue;
+  hipLaunchKernelGGL((k_mix_direct<TM, ADJ>), dim3((unsigned)grid), dim3(kThreads), 0, st, a);
+  return hipGetLastError();
+}
+
 template <typename TM>
 hipError_t launch_mix_fwd_planes(const TM* z, const float* w9, TM* y, int B, int C, int H, int W,
                                  hipStream_t st) {
+  if (mix_direct_ok(H, W)) return launch_mix_direct<TM, false>(z, nullptr, w9, y, nullptr, B, C, H, W, st);
   const int sp = mix_planes_together(H, W);
   const size_t lds = (size_t)sp * (H + 2) * (W + 2) * sizeof(float);
   if (lds > 64 * 1024) return hipErrorInvalidValue;
@@ -565,6 +875,8 @@ hipError_t launch_mix_fwd_planes_f32(const float* z, const float* w9, float* y, 
 // 150 KB for one plane, so 128 x 128 planes stage too), else the per-pixel kernel.
 hipError_t launch_mix_fwd_f32_route(const float* z, const float* w9, float* y, int B, int C,
                                     int H, int W, hipStream_t st) {
+  if (mix_direct_ok(H, W))
+    return launch_mix_direct<float, false>(z, nullptr, w9, y, nullptr, B, C, H, W, st);
   const int sp = mix_planes_together(H, W);
   const size_t lds = (size_t)sp * (H + 2) * (W + 2) * sizeof(float);
   if (lds > 150 * 1024) return launch_mix_fwd(z, w9, y, 0, B, C, H, W, 0, st);
@@ -583,11 +895,23 @@ size_t mix_planes_lds_bytes(int H, int W) {
   return (size_t)2 * mix_planes_together(H, W) * (H + 2) * (W + 2) * sizeof(float);
 }
 
-int mix_planes_per_group(int B) { return B < 8 ? B : 8; }
+static int mix_planes_per_group(int B) { return B < 8 ? B : 8; }
+
+bool mix_bwd_pass_ok(int H, int W) {
+  return mix_direct_ok(H, W) || mix_planes_lds_bytes(H, W) <= 64 * 1024;
+}
+
+int mix_bwd_parts(int B, int H, int W) {
+  if (mix_direct_ok(H, W))
+    return mix_direct_wpp(H, W) == 1 ? (B + kMixNpw - 1) / kMixNpw : B * mix_direct_chunks(H, W);
+  const int pb = mix_planes_per_group(B);
+  return (B + pb - 1) / pb;
+}
 
 template <typename TM>
 hipError_t launch_mix_bwd_planes(const TM* dy, const TM* z, const float* w9, TM* g, double* partW,
                                  int B, int C, int H, int W, hipStream_t st) {
+  if (mix_direct_ok(H, W)) return launch_mix_direct<TM, true>(dy, z, w9, g, partW, B, C, H, W, st);
   const size_t lds = mix_planes_lds_bytes(H, W);
   if (lds > 64 * 1024) return hipErrorInvalidValue;
   const int pb = mix_planes_per_group(B);

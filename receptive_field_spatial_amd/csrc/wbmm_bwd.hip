@@ -324,10 +324,10 @@ namespace {
 struct BwdWs {
   size_t partT, partW, partTs, dz, mixp, total;
 };
-// Window mode with the mix on fp32 NCHW maps: the mix's data and weight gradients come from one
-// plane-staged pass (G, and dWmix partials per group of planes) when its planes fit in LDS.
+// Window mode with the mix on NCHW maps: the mix's data and weight gradients come from one pass
+// over dy and z (G, and dWmix partials) for even widths, or odd ones whose planes fit in LDS.
 bool mix_planes_route(const Geo& g, const BwdRequest& r) {
-  return r.mixw && !g.image_mode && r.layout == 0 && mix_planes_lds_bytes(r.H, r.W) <= 64 * 1024;
+  return r.mixw && !g.image_mode && r.layout == 0 && mix_bwd_pass_ok(r.H, r.W);
 }
 BwdWs bwd_ws_layout(const Geo& g, const BwdRequest& r) {
   auto al = [](size_t v) { return (v + 255) / 256 * 256; };
@@ -339,8 +339,8 @@ BwdWs bwd_ws_layout(const Geo& g, const BwdRequest& r) {
   w.dz = w.partTs + al((size_t)g.C * g.col_groups * ls * sizeof(double));
   const bool need_dz = r.mixw && !g.image_mode;
   w.mixp = w.dz + (need_dz ? al((size_t)r.B * r.C * r.H * r.W * sizeof(float)) : 0);
-  const int pb = mix_planes_per_group(r.B);
-  w.total = w.mixp + (mix_planes_route(g, r) ? al((size_t)r.C * ((r.B + pb - 1) / pb) * 9 * 8) : 0);
+  w.total = w.mixp +
+            (mix_planes_route(g, r) ? al((size_t)r.C * mix_bwd_parts(r.B, r.H, r.W) * 9 * 8) : 0);
   return w;
 }
 }  // namespace
@@ -400,8 +400,8 @@ static hipError_t launch_backward_general(const BwdRequest& r, hipStream_t st) {
                                       r.H, r.W, st);
       if (e != hipSuccess) return e;
       if (r.dmixw) {
-        const int pb = mix_planes_per_group(r.B);
-        e = launch_bwd_reduce(nullptr, partM, (r.B + pb - 1) / pb, r.C, 0, nullptr, r.dmixw, st);
+        e = launch_bwd_reduce(nullptr, partM, mix_bwd_parts(r.B, r.H, r.W), r.C, 0, nullptr,
+                              r.dmixw, st);
         if (e != hipSuccess) return e;
       }
     } else {

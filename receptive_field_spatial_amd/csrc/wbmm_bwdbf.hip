@@ -254,7 +254,9 @@ size_t bf16_backward_workspace(int B, int C, int H, int W, int w, int layout, in
     return backward_bf16_general_workspace(r);
   }
   const int groups = H == 28 ? dt_groups<D28>(B) : dt_groups<D56>(B);
-  const size_t mixpart = has_mix ? al256((size_t)B * C * H * W * 2) + al256((size_t)C * B * 9 * 8) : 0;
+  const size_t mixpart =
+      has_mix ? al256((size_t)B * C * H * W * 2) + al256((size_t)C * mix_bwd_parts(B, H, W) * 9 * 8)
+              : 0;
   return mixpart + al256((size_t)C * groups * 729 * 8);
 }
 
@@ -266,18 +268,15 @@ hipError_t launch_backward_bf16(const BwdBf16Request& r, hipStream_t st) {
   const uint16_t* g = r.dy;
   hipError_t e = hipSuccess;
   const size_t gmap = mix ? al256((size_t)r.B * r.C * r.H * r.W * 2) : 0;
-  const size_t mixpart = mix ? gmap + al256((size_t)r.C * r.B * 9 * 8) : 0;
-  if (mix) {  // G and the per-plane dWmix partials in one pass over dy and z
+  const int partsW = mix ? mix_bwd_parts(r.B, r.H, r.W) : 0;
+  const size_t mixpart = mix ? gmap + al256((size_t)r.C * partsW * 9 * 8) : 0;
+  double* partW = mix ? (double*)(ws + gmap) : nullptr;
+  float* dmixw = mix ? r.dmixw : nullptr;
+  if (mix) {  // G and the dWmix partials in one pass over dy and z
     uint16_t* gm = (uint16_t*)ws;
-    double* partW = (double*)(ws + gmap);
-    e = launch_mix_bwd_planes_bf16(r.dy, r.dmixw ? r.zsaved : nullptr, r.mixw, gm, partW, r.B,
-                                   r.C, r.H, r.W, st);
+    e = launch_mix_bwd_planes_bf16(r.dy, dmixw ? r.zsaved : nullptr, r.mixw, gm, partW, r.B, r.C,
+                                   r.H, r.W, st);
     if (e != hipSuccess) return e;
-    if (r.dmixw) {
-      const int pb = mix_planes_per_group(r.B);
-      e = launch_bwd_reduce(nullptr, partW, (r.B + pb - 1) / pb, r.C, 0, nullptr, r.dmixw, st);
-      if (e != hipSuccess) return e;
-    }
     g = gm;
   }
   if (r.dx) {
@@ -290,8 +289,10 @@ hipError_t launch_backward_bf16(const BwdBf16Request& r, hipStream_t st) {
     e = r.H == 28 ? launch_dt<D28>(g, r.x, partT, r.B, r.C, st)
                   : launch_dt<D56>(g, r.x, partT, r.B, r.C, st);
     if (e != hipSuccess) return e;
-    e = launch_bwd_reduce(partT, nullptr, groups, r.C, 729, r.dT, nullptr, st);
+    // dT and dWmix partials summed in one launch
+    return launch_bwd_reduce2(partT, groups, partW, partsW, r.C, 729, r.dT, dmixw, st);
   }
+  if (dmixw) e = launch_bwd_reduce2(nullptr, 0, partW, partsW, r.C, 0, nullptr, dmixw, st);
   return e;
 }
 

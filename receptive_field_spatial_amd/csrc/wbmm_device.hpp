@@ -65,4 +65,29 @@ __device__ __forceinline__ v4f mfma_bf16(u32x4 a, u32x4 b, v4f c) {
                                                  __builtin_bit_cast(v8bf, b), c, 0, 0, 0);
 }
 
+// ---------------------------------------------------------------------------- wave sums
+// x of lane (i - n) within the lane's row of 16 (ROW_SHR), or of the broadcast source lane; 0
+// where there is none or the row is masked off. Both 32-bit halves move the same way.
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ double dpp_f64(double x) {
+  const uint64_t b = (uint64_t)__double_as_longlong(x);
+  const int lo = __builtin_amdgcn_update_dpp(0, (int)(uint32_t)b, CTRL, ROW_MASK, 0xf, true);
+  const int hi = __builtin_amdgcn_update_dpp(0, (int)(uint32_t)(b >> 32), CTRL, ROW_MASK, 0xf, true);
+  return __longlong_as_double((long long)(((uint64_t)(uint32_t)hi << 32) | (uint32_t)lo));
+}
+
+// Sum of x over the 64 lanes of a wave, in a fixed order, left in lane 63: within each row of 16
+// lanes, shifted copies are added (row_shr 1, 2, 4, 8: lane 15 then holds its row's sum); the sum
+// of row 0 is added into row 1 and that of row 2 into row 3 (row_bcast 15), then lane 31's into
+// rows 2 and 3 (row_bcast 31). VALU moves only (no LDS traffic, unlike lane shuffles).
+__device__ __forceinline__ double wave_sum_f64_last(double x) {
+  x += dpp_f64<0x111, 0xf>(x);
+  x += dpp_f64<0x112, 0xf>(x);
+  x += dpp_f64<0x114, 0xf>(x);
+  x += dpp_f64<0x118, 0xf>(x);
+  x += dpp_f64<0x142, 0xa>(x);
+  x += dpp_f64<0x143, 0xc>(x);
+  return x;
+}
+
 }  // namespace wbmm

@@ -92,6 +92,9 @@ hipError_t launch_forward_fast_bf16_mix(const FwdRequest& r, hipStream_t st);
 // Fixed-order sum of per-workgroup fp64 partials: dT[c][q] = sum_k partT[c][k][q] (and dWmix).
 hipError_t launch_bwd_reduce(const double* partT, const double* partW, int parts, int C, int L,
                              float* dT, float* dmixw, hipStream_t st);
+// The same with separate partial counts for dT and dWmix (one launch for both).
+hipError_t launch_bwd_reduce2(const double* partT, int partsT, const double* partW, int partsW,
+                              int C, int L, float* dT, float* dmixw, hipStream_t st);
 
 // Hands out the caller's timing events (null if none were set for this thread); a pair is used
 // by one launch only.
@@ -137,15 +140,19 @@ hipError_t launch_bf16_transposed_contraction(const uint16_t* g, const uint16_t*
                                               int B, int C, int H, hipStream_t st);
 hipError_t launch_mix_fwd_planes_bf16(const uint16_t* z, const float* w9, uint16_t* y, int B,
                                       int C, int H, int W, hipStream_t st);
-// dWmix partials of launch_mix_bwd_planes_bf16: [C][ceil(B / mix_planes_per_group(B))][9]
-int mix_planes_per_group(int B);
+// The mix adjoint passes below (G and dWmix partials in one pass over dy and z): planes of even
+// width take the direct pass (any size), odd widths the plane-staged one when a plane fits in
+// LDS. Their dWmix partials: [C][mix_bwd_parts(B, H, W)][9].
+bool mix_bwd_pass_ok(int H, int W);
+int mix_bwd_parts(int B, int H, int W);
 hipError_t launch_mix_bwd_planes_bf16(const uint16_t* dy, const uint16_t* z, const float* w9,
                                       uint16_t* g, double* partW, int B, int C, int H, int W,
                                       hipStream_t st);
-// The same plane-staged mix passes on fp32 NCHW maps (both need mix_planes_lds_bytes(H, W) and
+// The same mix passes on fp32 NCHW maps (odd widths need mix_planes_lds_bytes(H, W) and
 // (H + 2) (W + 2) 4 bytes per staged plane within 64 KB; they return hipErrorInvalidValue else).
 size_t mix_planes_lds_bytes(int H, int W);
-// fp32 NCHW forward mix pass: the plane-staged pass when a plane fits in LDS, else launch_mix_fwd.
+// fp32 NCHW forward mix pass: the direct pass for even widths, else the plane-staged pass when a
+// plane fits in LDS, else launch_mix_fwd.
 hipError_t launch_mix_fwd_f32_route(const float* z, const float* w9, float* y, int B, int C,
                                     int H, int W, hipStream_t st);
 hipError_t launch_mix_fwd_planes_f32(const float* z, const float* w9, float* y, int B, int C,

@@ -61,10 +61,9 @@ __device__ __forceinline__ void put4(float* p, const float (&v)[4]) {
 __device__ __forceinline__ void put4(uint16_t* p, const uint16_t (&v)[4]) {
   *(uint2*)p = make_uint2(v[0] | ((uint32_t)v[1] << 16), v[2] | ((uint32_t)v[3] << 16));
 }
-bool mix_planes_fit(int H, int W) { return mix_planes_lds_bytes(H, W) <= 64 * 1024; }
-size_t mix_partials_bytes(int B, int C) {
-  const int pb = mix_planes_per_group(B);
-  return al256((size_t)C * ((B + pb - 1) / pb) * 9 * sizeof(double));
+bool mix_planes_fit(int H, int W) { return mix_bwd_pass_ok(H, W); }
+size_t mix_partials_bytes(int B, int C, int H, int W) {
+  return al256((size_t)C * mix_bwd_parts(B, H, W) * 9 * sizeof(double));
 }
 
 // Repacked map <- image map: workgroup (qg, c) takes repacked planes (q, c) for
@@ -256,7 +255,7 @@ size_t repack_backward_workspace(const BwdRequest& r) {
   const RepackGeo g = repack_geo(r.B, r.C, r.H, r.W, r.oy, r.ox);
   const size_t fast = al256(fast_backward_workspace(repacked_request(r, g)));
   const size_t mix =
-      r.mixw ? al256((size_t)r.B * r.C * r.H * r.W * 4) + mix_partials_bytes(r.B, r.C) : 0;
+      r.mixw ? al256((size_t)r.B * r.C * r.H * r.W * 4) + mix_partials_bytes(r.B, r.C, r.H, r.W) : 0;
   return fast + 3 * repacked_bytes(g) + mix;
 }
 
@@ -281,8 +280,8 @@ hipError_t launch_backward_repacked(const BwdRequest& r, hipStream_t st) {
                                     r.C, r.H, r.W, st);
       if (e != hipSuccess) return e;
       if (r.dmixw) {
-        const int pb = mix_planes_per_group(r.B);
-        e = launch_bwd_reduce(nullptr, partW, (r.B + pb - 1) / pb, r.C, 0, nullptr, r.dmixw, st);
+        e = launch_bwd_reduce(nullptr, partW, mix_bwd_parts(r.B, r.H, r.W), r.C, 0, nullptr,
+                              r.dmixw, st);
         if (e != hipSuccess) return e;
       }
     } else {

@@ -222,7 +222,8 @@ def test_forward_f32_w14_shift_bitwise_all_channels(hw, B, C, mix):
     assert np.array_equal(host(y), want)
 
 
-@pytest.mark.parametrize("B,C,H,W,w", [(2, 3, 28, 28, 14), (1, 4, 10, 13, 4), (3, 2, 56, 56, 7)])
+@pytest.mark.parametrize("B,C,H,W,w", [(2, 3, 28, 28, 14), (1, 4, 10, 13, 4), (3, 2, 56, 56, 7),
+                                       (1, 3, 150, 74, 14)])
 @pytest.mark.parametrize("cached", [False, True])
 def test_forward_mix_and_zsave(B, C, H, W, w, cached):
     say(f"forward mix+zsave B={B} C={C} H={H} W={W} w={w} cached={cached}")
@@ -459,6 +460,9 @@ def bwd_case(B, C, H, W, w, *, mix, cached=False, layout="NCHW", seed=0):
     # the fast fp32 kernels on 56x56 and 14x14 images (ragged batches: last unit part empty)
     (2, 3, 56, 56, 14, True), (2, 3, 56, 56, 14, False), (5, 3, 56, 56, 14, True),
     (5, 3, 14, 14, 14, True), (5, 3, 14, 14, 14, False), (70, 2, 14, 14, 14, True),
+    # the direct mix adjoint pass on ragged plane heights (last row run part empty), several
+    # chunks per plane
+    (1, 2, 150, 74, 14, True), (3, 2, 26, 30, 5, True),
 ])
 @pytest.mark.parametrize("cached", [False, True])
 def test_backward_shapes(B, C, H, W, w, mix, cached):
