@@ -9,18 +9,22 @@
 // image, row-major), so the window pixels never pass through LDS:
 //   * B operand (window pixels) straight from HBM into registers: lane (n, g) holds the 49 pixels
 //     of quadrant g of window n, the next wave-unit's pixels in flight during the contraction;
-//     pixels outside the map (the zero padding of a map whose sides are not multiples of 14)
-//     read as zero;
+//     the loads address x as one raw buffer (a 32-bit per-lane offset, the window row as a
+//     uniform offset, the column as an immediate); pixels outside the map (the zero padding of
+//     a map whose sides are not multiples of 14) read as zero;
 //   * A operand (M_c[i][j]) from LDS, quadrant-major within each row (quadrant g's 49 columns at
 //     offset 50 g), so two consecutive K-steps of a lane are one 8-byte read;
 //   * v_mfma_f32_16x16x4f32: 13 row tiles x 49 K-steps per wave-unit;
 //   * outputs stored from the accumulators (reverse + crop fused), to y or, with the 3x3 mix,
 //     to the pre-mix map that a mix pass then reads.
-// A workgroup walks a contiguous range of the (channel, wave-unit) list in rounds of 8
-// wave-units of one channel; the matrix is restaged when the channel changes.
+// A workgroup walks a contiguous range of the (channel, wave-unit) list in rounds of 4
+// wave-units of one channel; the matrix is restaged when the channel changes. With few channels
+// of many wave-units each, every channel is split into equal parts instead, one workgroup (and one
+// matrix staging) per part.
 #include "wbmm_device.hpp"
 #include "wbmm_launch.hpp"
 
+#include <algorithm>
 #include <atomic>
 
 namespace wbmm {
@@ -32,7 +36,7 @@ constexpr int CW = 14, CD = CW * CW, CRT = (CD + 15) / 16;  // window, pixels, r
 constexpr int CQ = 7, CKQ = CQ * CQ;                        // quadrant side, K-steps
 constexpr int SEGP = 50;                                    // LDS floats per quadrant segment
 constexpr int MP = 4 * SEGP + 2;                            // LDS row pitch (floats)
-constexpr int kCmLds = CD * MP * 4 + CD * 4;  // the matrix, then the column-slot table
+constexpr int kCmLds = CD * MP * 4;  // the matrix
 static_assert(kCmLds <= 160 * 1024, "one channel's matrix fits in LDS");
 
 struct CmArgs {
@@ -40,6 +44,7 @@ struct CmArgs {
   int nWx, nWin;       // windows per image row, per image
   int wupc;            // wave-units per channel: ceil(B * nWin / 16)
   long long total;     // C * wupc
+  int parts;           // > 0: workgroup rg takes part rg % parts of channel rg / parts
   const float* x;
   const float* M;      // (C, 196, 196)
   float* out;          // y, or the pre-mix map when the mix runs as its own pass
@@ -51,62 +56,86 @@ __device__ __forceinline__ int quad_col(int g, int s) {
   return (7 * (g >> 1) + s / 7) * CW + 7 * (g & 1) + s % 7;
 }
 
+// The x tensor as a raw buffer (the host takes this path only below 2^31 bytes): loads address it
+// by a per-lane 32-bit byte offset, a uniform row offset and an immediate column offset.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t x_rsrc(const CmArgs& a) {
+  const long long bytes = (long long)a.B * a.C * a.H * a.W * 4;
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(a.x), (short)0, (int)bytes,
+                                           0x00020000);
+}
+
 // The window pixels of one lane (window n of the wave-unit, quadrant g), 49 registers.
 struct XLoad {
   float v[CKQ];
   // win: the lane's window index in the channel (>= B * nWin: no window, zeros)
-  __device__ __forceinline__ void issue(const CmArgs& a, int c, int win, int g) {
+  __device__ __forceinline__ void issue(const CmArgs& a, __amdgpu_buffer_rsrc_t xr, int c, int win,
+                                        int g) {
     const int nwin_ch = a.B * a.nWin;
     const bool valid = win < nwin_ch;
     const int wn = valid ? win : 0;
     const int b = wn / a.nWin, wi = wn - b * a.nWin;
     const int wy = wi / a.nWx, wx = wi - wy * a.nWx;
     const int r0 = wy * CW + 7 * (g >> 1), c0 = wx * CW + 7 * (g & 1);
-    const float* base = a.x + ((size_t)b * a.C + c) * a.H * a.W + (size_t)r0 * a.W + c0;
+    // byte offset of the quadrant origin
+    const int vo = (int)((((size_t)b * a.C + c) * a.H * a.W + (size_t)r0 * a.W + c0) * 4);
+    const int rowb = a.W * 4;
     const bool inside = valid && r0 + 7 <= a.H && c0 + 7 <= a.W;
     if (__builtin_amdgcn_ballot_w64(!inside) == 0) {  // the whole wave is inside the map
 #pragma unroll
-      for (int s = 0; s < CKQ; ++s) v[s] = base[(s / 7) * a.W + s % 7];
+      for (int s = 0; s < CKQ; ++s)
+        v[s] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
+                                             xr, vo + (s % 7) * 4, (s / 7) * rowb, 0));
     } else {
-      // rows / columns of the quadrant inside the map; out-of-map pixels read the quadrant
-      // origin (clamped address) and are replaced by zero
+      // rows / columns of the quadrant inside the map; out-of-map pixels read the tensor's
+      // first element and are replaced by zero
       const int nr = valid ? min(7, a.H - r0) : 0, nc = valid ? min(7, a.W - c0) : 0;
-      const float* safe = valid && nr > 0 && nc > 0 ? base : a.x;
 #pragma unroll
       for (int s = 0; s < CKQ; ++s) {
         const bool ok = s / 7 < nr && s % 7 < nc;
-        const float t = safe[ok ? (s / 7) * a.W + s % 7 : 0];
+        const float t = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
+            xr, ok ? vo + (s / 7) * rowb + (s % 7) * 4 : 0, 0, 0));
         v[s] = ok ? t : 0.f;
       }
     }
   }
 };
 
-// Stage M_c (row-major (196, 196) in HBM) into LDS: each thread moves 16-byte pieces (rows of 49
-// pieces), thirteen of them in flight before their LDS writes; column j goes to quadrant
-// segment g(j), slot s(j), whose offsets come from a 196-entry table in LDS (`segs`).
-__device__ __forceinline__ void stage_matrix(const float* __restrict__ M, int c, float* Ms,
-                                             const int* segs) {
-  const float4* src = (const float4*)(M + (size_t)c * CD * CD);
-  constexpr int N4 = CD * CD / 4;  // 9604 pieces
-  constexpr int KB = 13;
-  for (int e0 = threadIdx.x; e0 < N4; e0 += KB * kCmThreads) {
+// LDS slot of matrix column j within a row: quadrant segment g(j), then the column's place in it.
+__device__ __forceinline__ int col_slot(int j) {
+  const int y = j / CW, xx = j - (j / CW) * CW;
+  return ((y / 7) * 2 + xx / 7) * SEGP + (y % 7) * 7 + xx % 7;
+}
+
+// Stage M_c (row-major (196, 196) in HBM) into LDS: thread t < 245 moves the 16-byte pieces of
+// column group cg = t % 49 (columns 4 cg .. 4 cg + 3, whose four LDS slots it computes once) in
+// rows t / 49 + 5 m, eight pieces in flight before their LDS writes.
+__device__ __forceinline__ void stage_matrix(const float* __restrict__ M, int c, float* Ms) {
+  constexpr int NG = CD / 4, RS = kCmThreads / NG, NR = (CD + RS - 1) / RS;  // 49, 5, 40
+  constexpr int KB = 8;
+  const int t = threadIdx.x;
+  if (t >= NG * RS) return;
+  const int cg = t % NG, r0 = t / NG;
+  int slot[4];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) slot[k] = col_slot(4 * cg + k);
+  const float4* src = (const float4*)(M + (size_t)c * CD * CD) + cg;
+#pragma unroll 1
+  for (int m0 = 0; m0 < NR; m0 += KB) {
     float4 v[KB];
 #pragma unroll
     for (int k = 0; k < KB; ++k) {
-      const int e = e0 + k * kCmThreads;
-      v[k] = src[e < N4 ? e : N4 - 1];
+      const int i = min(r0 + RS * (m0 + k), CD - 1);
+      v[k] = src[i * NG];
     }
 #pragma unroll
     for (int k = 0; k < KB; ++k) {
-      const int e = e0 + k * kCmThreads;
-      if (e < N4) {
-        const int i = e / 49, j0 = (e - i * 49) * 4;
+      const int i = r0 + RS * (m0 + k);
+      if (i < CD) {
         float* row = Ms + i * MP;
-        row[segs[j0]] = v[k].x;
-        row[segs[j0 + 1]] = v[k].y;
-        row[segs[j0 + 2]] = v[k].z;
-        row[segs[j0 + 3]] = v[k].w;
+        row[slot[0]] = v[k].x;
+        row[slot[1]] = v[k].y;
+        row[slot[2]] = v[k].z;
+        row[slot[3]] = v[k].w;
       }
     }
   }
@@ -115,11 +144,6 @@ __device__ __forceinline__ void stage_matrix(const float* __restrict__ M, int c,
 __global__ void __launch_bounds__(kCmThreads) k_fwd_cm(CmArgs a) {
   extern __shared__ __attribute__((aligned(16))) float smem_f[];
   float* Ms = smem_f;
-  int* segs = (int*)(smem_f + CD * MP);  // LDS slot of column j within a row
-  for (int j = threadIdx.x; j < CD; j += kCmThreads) {
-    const int y = j / CW, xx = j - (j / CW) * CW;
-    segs[j] = ((y / 7) * 2 + xx / 7) * SEGP + (y % 7) * 7 + xx % 7;
-  }
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int n = lane & 15, g = lane >> 4;
   // XCD-aware ranges: workgroups are dealt to the 8 XCDs round-robin (workgroup b runs on XCD
@@ -128,18 +152,16 @@ __global__ void __launch_bounds__(kCmThreads) k_fwd_cm(CmArgs a) {
   // from that L2 by its neighbours
   const int G = gridDim.x;
   const int rg = G % 8 == 0 ? (int)(blockIdx.x % 8) * (G / 8) + (int)(blockIdx.x / 8) : (int)blockIdx.x;
-  const long long lo = a.total * rg / G;
-  const long long hi = a.total * (rg + 1) / G;
-
-  // Per-lane output offsets within a window for r = 0 of each tile (pixel p0 = 16 t + 4 g) and
-  // the column p0 % 14 that decides whether p0 + r wraps to the next window row.
-  int ooff[CRT], ocol[CRT];
-#pragma unroll
-  for (int t = 0; t < CRT; ++t) {
-    const int p0 = 16 * t + 4 * g;
-    ocol[t] = p0 % CW;
-    ooff[t] = (p0 / CW) * a.W + p0 % CW;
+  long long lo, hi;
+  if (a.parts > 0) {  // channel-aligned: each workgroup stages one matrix
+    const int c = rg / a.parts, q = rg - c * a.parts;
+    lo = (long long)c * a.wupc + (long long)a.wupc * q / a.parts;
+    hi = (long long)c * a.wupc + (long long)a.wupc * (q + 1) / a.parts;
+  } else {
+    lo = a.total * rg / G;
+    hi = a.total * (rg + 1) / G;
   }
+
   // A operand base of this lane: row m of tile 0, quadrant g's segment
   const float* abase = Ms + n * MP + g * SEGP;
 
@@ -149,11 +171,12 @@ __global__ void __launch_bounds__(kCmThreads) k_fwd_cm(CmArgs a) {
     const long long cend = (r / a.wupc + 1) * (long long)a.wupc;
     return min(min(r + kCmWaves, cend), hi);
   };
+  const __amdgpu_buffer_rsrc_t xr = x_rsrc(a);
   auto issue = [&](XLoad& xl, long long r, long long rend) {
     const long long wu = r + wave;
     if (r < hi && wu < rend) {
       const int c = (int)(wu / a.wupc), k = (int)(wu - (long long)c * a.wupc);
-      xl.issue(a, c, 16 * k + n, g);
+      xl.issue(a, xr, c, 16 * k + n, g);
     }
   };
   int staged = -1;
@@ -165,7 +188,7 @@ __global__ void __launch_bounds__(kCmThreads) k_fwd_cm(CmArgs a) {
     const int c = (int)(r0 / a.wupc);
     if (c != staged) {
       __syncthreads();  // every wave is done with the previous channel's matrix
-      stage_matrix(a.M, c, Ms, segs);
+      stage_matrix(a.M, c, Ms);
       __syncthreads();
       staged = c;
     }
@@ -229,16 +252,19 @@ __global__ void __launch_bounds__(kCmThreads) k_fwd_cm(CmArgs a) {
 #pragma unroll
           for (int t = 0; t < CRT; ++t) {
             if (16 * t + 4 * g >= CD) continue;
+            // pixel p0 = 16 t + 4 g of the window: its offset and window column
+            const int p0 = 16 * t + 4 * g;
+            const int ocol = p0 % CW, ooff = (p0 / CW) * a.W + ocol;
             const v4f v = acc[t];
-            if (ocol[t] <= CW - 4) {
-              *(f4u*)(o + ooff[t]) = f4u{v[0], v[1], v[2], v[3]};
-              if (o2) *(f4u*)(o2 + ooff[t]) = f4u{v[0], v[1], v[2], v[3]};
+            if (ocol <= CW - 4) {
+              *(f4u*)(o + ooff) = f4u{v[0], v[1], v[2], v[3]};
+              if (o2) *(f4u*)(o2 + ooff) = f4u{v[0], v[1], v[2], v[3]};
             } else {
-              *(f2u*)(o + ooff[t]) = f2u{v[0], v[1]};
-              *(f2u*)(o + ooff[t] + a.W - (CW - 2)) = f2u{v[2], v[3]};
+              *(f2u*)(o + ooff) = f2u{v[0], v[1]};
+              *(f2u*)(o + ooff + a.W - (CW - 2)) = f2u{v[2], v[3]};
               if (o2) {
-                *(f2u*)(o2 + ooff[t]) = f2u{v[0], v[1]};
-                *(f2u*)(o2 + ooff[t] + a.W - (CW - 2)) = f2u{v[2], v[3]};
+                *(f2u*)(o2 + ooff) = f2u{v[0], v[1]};
+                *(f2u*)(o2 + ooff + a.W - (CW - 2)) = f2u{v[2], v[3]};
               }
             }
           }
@@ -283,7 +309,7 @@ int cm_cu_count() {
 
 bool fast_cm_forward_ok(const FwdRequest& r) {
   return !r.in_bf16 && !r.out_bf16 && r.M && !r.T && !r.Tsub && r.w == CW && r.layout == 0 &&
-         r.oy == 0 && r.ox == 0;
+         r.oy == 0 && r.ox == 0 && (long long)r.B * r.C * r.H * r.W * 4 < (1LL << 31);
 }
 
 // out: where the contraction's result goes (y, or the pre-mix map); out2: a second copy or null.
@@ -303,7 +329,22 @@ hipError_t launch_forward_fast_cm(const FwdRequest& r, float* out, float* out2, 
   a.out2 = out2;
   const long long rounds = (a.total + kCmWaves - 1) / kCmWaves;
   const int cus = cm_cu_count();
-  const int grid = (int)(rounds < cus ? rounds : cus);
+  int grid = (int)(rounds < cus ? rounds : cus);
+  // Few channels with many wave-units each: splitting every channel into `parts` workgroups
+  // (one matrix staging each) beats contiguous ranges, whose workgroups straddle a channel
+  // boundary (a second staging and a partial round), when it needs no more rounds per workgroup.
+  a.parts = 0;
+  if (r.C <= cus) {
+    const int parts = (int)std::min<long long>(cus / r.C, a.wupc);
+    const long long per = (a.wupc + parts - 1) / parts;
+    const long long rounds_split = (per + kCmWaves - 1) / kCmWaves;
+    const long long per_range = (a.total + grid - 1) / grid;
+    const long long rounds_range = (per_range + kCmWaves - 1) / kCmWaves + 1;  // + a straddle
+    if (rounds_split <= rounds_range && (long long)r.C * parts <= 0x7fffffffLL) {
+      a.parts = parts;
+      grid = r.C * parts;
+    }
+  }
   hipError_t e = hipFuncSetAttribute((const void*)k_fwd_cm,
                                      hipFuncAttributeMaxDynamicSharedMemorySize, kCmLds);
   if (e != hipSuccess) return e;
