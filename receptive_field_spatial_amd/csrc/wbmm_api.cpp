@@ -193,15 +193,20 @@ size_t forward_ws_bytes(int B, int C, int H, int W, int w, int oy, int ox, int l
   r.oy = oy;
   r.ox = ox;
   if (!wbmm::forward_plan_ok(r)) return 0;
-  // the dtypes are not arguments: the largest need over fp32 / bf16 inputs and outputs
+  // the dtypes and the operand kind are not arguments: the largest need over fp32 / bf16 inputs
+  // and outputs, with a table or a cached matrix
   size_t need = 0;
-  for (int ib = 0; ib < 2; ++ib)
-    for (int ob = 0; ob < 2; ++ob) {
-      r.in_bf16 = ib;
-      r.out_bf16 = ob;
-      const size_t n = wbmm::forward_workspace(r);
-      if (n > need) need = n;
-    }
+  for (int cached = 0; cached < 2; ++cached)
+    for (int ib = 0; ib < 2; ++ib)
+      for (int ob = 0; ob < 2; ++ob) {
+        r.T = cached ? nullptr : (const void*)&dummy;
+        r.M = cached ? (const void*)&dummy : nullptr;
+        r.in_bf16 = ib;
+        r.out_bf16 = ob;
+        if (cached && !wbmm::forward_plan_ok(r)) continue;
+        const size_t n = wbmm::forward_workspace(r);
+        if (n > need) need = n;
+      }
   return need;
 }
 

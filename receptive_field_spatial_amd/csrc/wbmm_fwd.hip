@@ -153,7 +153,8 @@ static bool fast_bf16_mix_ok(const FwdRequest& r) {
 size_t forward_workspace(const FwdRequest& r) {
   if (repack_forward_ok(r)) return repack_forward_workspace(r);
   // cached matrix on the fast path: with the mix, the pre-mix map goes to z_save or here
-  if (fast_cm_forward_ok(r)) return r.mixw && !r.zsave ? (size_t)r.B * r.C * r.H * r.W * 4 : 0;
+  if (fast_cm_forward_ok(r) || fast_f32_w28_forward_ok(r))
+    return r.mixw && !r.zsave ? (size_t)r.B * r.C * r.H * r.W * 4 : 0;
   if (fast_bf16_mix_ok(r)) return r.zsave ? 0 : (size_t)r.B * r.C * r.H * r.W * 2;
   Geo g;
   if (!plan_fwd(g, r)) return 0;
@@ -171,6 +172,13 @@ hipError_t launch_forward(const FwdRequest& r, hipStream_t st) {
     if (!r.mixw) return launch_forward_fast_cm(r, (float*)r.y, (float*)r.zsave, st);
     float* z = (float*)(r.zsave ? r.zsave : r.ws);
     hipError_t e = launch_forward_fast_cm(r, z, nullptr, st);
+    if (e != hipSuccess) return e;
+    return launch_mix_fwd_f32_route(z, r.mixw, (float*)r.y, r.B, r.C, r.H, r.W, st);
+  }
+  if (fast_f32_w28_forward_ok(r)) {  // fp32, w = 28, 56x56: the contraction, then the mix pass
+    if (!r.mixw) return launch_forward_fast_f32_w28(r, (float*)r.y, (float*)r.zsave, st);
+    float* z = (float*)(r.zsave ? r.zsave : r.ws);
+    hipError_t e = launch_forward_fast_f32_w28(r, z, nullptr, st);
     if (e != hipSuccess) return e;
     return launch_mix_fwd_f32_route(z, r.mixw, (float*)r.y, r.B, r.C, r.H, r.W, st);
   }

@@ -124,12 +124,18 @@ def test_forward_workspace_rules(lib):
     # with z_save the fp32 call writes z there, but a bf16 z_save takes the fp32 map through the
     # workspace: the query (which has no dtype argument) reports the larger need
     assert lib.wbmm_forward_workspace_bytes(1, 2, 128, 128, 14, 0, 1, 1) == need
-    assert lib.wbmm_forward_workspace_bytes(1, 2, 100, 100, 14, 0, 1, 0) == 0  # 64 windows: fused
-    # fused in-kernel for fp32 and, on this fast bf16 shape, for bf16 maps: no workspace; the
-    # bf16 w = 7 fast shape keeps z in the workspace for its separate mix pass
-    assert lib.wbmm_forward_workspace_bytes(64, 192, 28, 28, 14, 0, 1, 0) == 0
+    # with a table the mix is fused in-kernel here (64 windows per image; the fast fp32 and bf16
+    # w = 14 kernels), but the query also covers a cached matrix, whose fast fp32 kernel writes
+    # the pre-mix map to the workspace for a separate mix pass
+    assert lib.wbmm_forward_workspace_bytes(1, 2, 100, 100, 14, 0, 1, 0) == 1 * 2 * 100 * 100 * 4
+    assert lib.wbmm_forward_workspace_bytes(64, 192, 28, 28, 14, 0, 1, 0) == 64 * 192 * 28 * 28 * 4
+    # the bf16 w = 7 fast shape keeps z (bf16) in the workspace for its separate mix pass
     assert lib.wbmm_forward_workspace_bytes(8, 4, 56, 56, 7, 0, 1, 0) == 8 * 4 * 56 * 56 * 2
+    # with z_save the fp32 pre-mix map goes there
     assert lib.wbmm_forward_workspace_bytes(64, 192, 28, 28, 14, 0, 1, 1) == 0
+    # the fast fp32 w = 28 kernel (56x56 maps) runs the mix as its own pass too
+    assert lib.wbmm_forward_workspace_bytes(3, 2, 56, 56, 28, 0, 1, 0) == 3 * 2 * 56 * 56 * 4
+    assert lib.wbmm_forward_workspace_bytes(3, 2, 56, 56, 28, 0, 0, 0) == 0
     assert lib.wbmm_forward_workspace_bytes(1, 2, 8, 8, 0, 0, 0, 0) == 0       # invalid -> 0
     st = fwd(lib, B=1, C=2, H=128, W=128, w=14, mix=0x900000, y=0x40000000, ws=None, wsb=0)
     assert st == R.WBMM_E_WORKSPACE

@@ -357,6 +357,37 @@ def test_forward_bf16_fused_mix_shift_bitwise(hw, B, C):
     _bf16_shift_case(14, hw, B, C, mix=True)
 
 
+@pytest.mark.parametrize("B,C", [(1, 1), (3, 2), (9, 3), (17, 2)])
+@pytest.mark.parametrize("mix,zsave", [(False, False), (False, True), (True, False), (True, True)])
+def test_forward_f32_w28_fast(B, C, mix, zsave):
+    """The fast fp32 w = 28 kernel (56x56 maps, 32-window blocks of 8 images): ragged batches
+    (blocks part past the batch), several channels, z_save and the 3x3 mix (a separate pass on
+    the kernel's z) against the oracle."""
+    say(f"forward f32 w=28 fast B={B} C={C} mix={mix} zsave={zsave}")
+    yh, want_y, zh, want_z = fwd_case(B, C, 56, 56, 28, mix=mix, zsave=zsave)
+    assert_f32(yh, want_y, "y")
+    if zsave:
+        assert_f32(zh, want_z, "z")
+
+
+@pytest.mark.parametrize("B,C", [(10, 300), (8, 129), (3, 520)])
+def test_forward_f32_w28_shift_bitwise_all_channels(B, C):
+    """One-hot tables at a different offset in every channel: the fast fp32 w = 28 kernel's
+    output is the input shifted inside each window, bit for bit, in every channel. More blocks
+    than resident workgroups, so workgroups walk several blocks and restage the table when the
+    channel changes."""
+    w, hw = 28, 56
+    say(f"forward f32 w=28 shift all channels B={B} C={C}")
+    x = synth.normal_f32((B, C, hw, hw), 1.0, seed=37)
+    L1 = 2 * w - 1
+    dy = (np.arange(C) * 7 + 2) % L1 - (w - 1)
+    dx = (np.arange(C) * 13 + 5) % L1 - (w - 1)
+    T = np.zeros((C, L1, L1), np.float32)
+    T[np.arange(C), dy + w - 1, dx + w - 1] = 1.0
+    want = _window_shift(x, w, dy, dx)
+    assert np.array_equal(host(R().wbmm_forward(dev(x), w, T=dev(T))), want)
+
+
 def _bf16_shift_case(w, hw, B, C, mix):
     """One-hot tables at a different offset in every channel: the output is the input shifted
     inside each window (exact in bf16). More units than resident workgroups, so workgroups walk
