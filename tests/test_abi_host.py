@@ -129,8 +129,9 @@ def test_forward_workspace_rules(lib):
     # the pre-mix map to the workspace for a separate mix pass
     assert lib.wbmm_forward_workspace_bytes(1, 2, 100, 100, 14, 0, 1, 0) == 1 * 2 * 100 * 100 * 4
     assert lib.wbmm_forward_workspace_bytes(64, 192, 28, 28, 14, 0, 1, 0) == 64 * 192 * 28 * 28 * 4
-    # the bf16 w = 7 fast shape keeps z (bf16) in the workspace for its separate mix pass
-    assert lib.wbmm_forward_workspace_bytes(8, 4, 56, 56, 7, 0, 1, 0) == 8 * 4 * 56 * 56 * 2
+    # the fast w = 7 shape (bf16 and fp32 kernels) keeps z in the workspace for its separate mix
+    # pass: the fp32 map is the larger need
+    assert lib.wbmm_forward_workspace_bytes(8, 4, 56, 56, 7, 0, 1, 0) == 8 * 4 * 56 * 56 * 4
     # with z_save the fp32 pre-mix map goes there
     assert lib.wbmm_forward_workspace_bytes(64, 192, 28, 28, 14, 0, 1, 1) == 0
     # the fast fp32 w = 28 kernel (56x56 maps) runs the mix as its own pass too

@@ -370,6 +370,36 @@ def test_forward_f32_w28_fast(B, C, mix, zsave):
         assert_f32(zh, want_z, "z")
 
 
+@pytest.mark.parametrize("B,C", [(1, 1), (3, 2), (5, 7)])
+@pytest.mark.parametrize("mix,zsave", [(False, False), (False, True), (True, False), (True, True)])
+def test_forward_f32_w7_fast(B, C, mix, zsave):
+    """The fast fp32 w = 7 kernel (56x56 maps; persistent waves over (channel, image) planes,
+    the table operand in registers per channel): batches and channel counts that leave waves with
+    one, several or no planes, z_save and the mix (a separate pass) against the oracle."""
+    say(f"forward f32 w=7 fast B={B} C={C} mix={mix} zsave={zsave}")
+    yh, want_y, zh, want_z = fwd_case(B, C, 56, 56, 7, mix=mix, zsave=zsave)
+    assert_f32(yh, want_y, "y")
+    if zsave:
+        assert_f32(zh, want_z, "z")
+
+
+@pytest.mark.parametrize("B,C", [(4, 900), (9, 300), (1, 2050)])
+def test_forward_f32_w7_shift_bitwise_all_channels(B, C):
+    """One-hot tables at a different offset in every channel: the fast fp32 w = 7 kernel's output
+    is the input shifted inside each window, bit for bit. More planes than waves, so waves walk
+    several planes and re-form the table operand when the channel changes."""
+    w, hw = 7, 56
+    say(f"forward f32 w=7 shift all channels B={B} C={C}")
+    x = synth.normal_f32((B, C, hw, hw), 1.0, seed=38)
+    L1 = 2 * w - 1
+    dy = (np.arange(C) * 5 + 1) % L1 - (w - 1)
+    dx = (np.arange(C) * 3 + 4) % L1 - (w - 1)
+    T = np.zeros((C, L1, L1), np.float32)
+    T[np.arange(C), dy + w - 1, dx + w - 1] = 1.0
+    want = _window_shift(x, w, dy, dx)
+    assert np.array_equal(host(R().wbmm_forward(dev(x), w, T=dev(T))), want)
+
+
 @pytest.mark.parametrize("B,C", [(10, 300), (8, 129), (3, 520)])
 def test_forward_f32_w28_shift_bitwise_all_channels(B, C):
     """One-hot tables at a different offset in every channel: the fast fp32 w = 28 kernel's
