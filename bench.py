@@ -54,7 +54,9 @@ def log(*a):
 KERNEL_FILES = {"k_fwd_ws": "wbmm_fast.hip", "k_bwd_ls": "wbmm_fast.hip", "k_fwd_cm": "wbmm_fastcm.hip",
                 "k_fwd_bf16_w7": "wbmm_fastbf.hip",
                 "k_fwd_bf16_w28": "wbmm_fastbf.hip", "k_fwd_bf16": "wbmm_fastbf.hip",
-                "k_wbmm_fwd": "wbmm_fwd.hip", "k_wbmm_bwd": "wbmm_bwd.hip"}
+                "k_wbmm_fwd": "wbmm_fwd.hip", "k_wbmm_bwd": "wbmm_bwd.hip",
+                "k_fwd_f32_w7": "wbmm_fast7.hip", "k_fwd_f32_w28": "wbmm_fast28.hip",
+                "k_mix_direct": "wbmm_aux.hip"}
 HOST_HEADERS = ("wbmm_launch.hpp",)
 
 
@@ -561,7 +563,7 @@ def _pmc_rows(d):
 
 # bench label -> names of the kernels that can be that call's main kernel (fast or general path)
 MAIN_KERNELS = {"k_wbmm_fwd": ("k_fwd_ws", "k_fwd_cm", "k_fwd_bf16_w7", "k_fwd_bf16_w28", "k_fwd_bf16",
-                               "k_wbmm_fwd"),
+                               "k_fwd_f32_w7", "k_fwd_f32_w28", "k_wbmm_fwd"),
                 "k_wbmm_bwd": ("k_bwd_ls", "k_wbmm_bwd")}
 
 
@@ -655,10 +657,15 @@ def fig3_sweep(args):
         sec = timed(lambda i: R.wbmm_forward(xs[i], w, T=T, y=ys[i], stream=stream))
         Hp, Wp = -(-H // w) * w, -(-W // w) * w
         flops = B * C * Hp * Wp * 2 * w * w
+        nbytes = E * 8 + C * (2 * w - 1) ** 2 * 4
+        t_mfma = flops / (FP32_MFMA_PEAK_TFLOPS * 1e12)
+        t_hbm = nbytes / (HBM_PEAK_GBS * 1e9)
+        roof = ({"bound": "mfma", "peak_tflops": FP32_MFMA_PEAK_TFLOPS,
+                 "frac": round(t_mfma / sec, 4)} if t_mfma >= t_hbm else
+                {"bound": "hbm", "peak_gbs": HBM_PEAK_GBS, "frac": round(t_hbm / sec, 4)})
         lines.append({"op": "wbmm", "w": w, "receptive_field": w * w, "us": round(sec * 1e6, 2),
                       "out_elems_per_s": round(E / sec, 1), "gflops": round(flops / sec / 1e9, 1),
-                      "roofline": {"bound": "mfma", "peak_tflops": FP32_MFMA_PEAK_TFLOPS,
-                                   "frac": round(flops / sec / 1e12 / FP32_MFMA_PEAK_TFLOPS, 4)}})
+                      "roofline": roof})
     # context beyond the pages' fp32 comparison: the same layers with bf16 maps and tables
     xb = [x.to(torch.bfloat16) for x in xs]
     yb = [torch.empty_like(x) for x in xb]
