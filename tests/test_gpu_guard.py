@@ -131,6 +131,40 @@ def test_guard_fp32_layer(B, C, H, W, w, mix):
         assert_f32(host(dW.t), wdW, "dWmix")
 
 
+# forward-only fast fp32 kernels: w = 7 and w = 28 on 56x56 maps (ragged batches against the
+# w = 28 kernel's 8-image blocks), and the cached-matrix kernel (whole and border windows)
+F32_FWD_CASES = [(5, 2, 56, 56, 7, False), (9, 2, 56, 56, 28, False), (3, 2, 56, 56, 28, False),
+                 (5, 3, 56, 56, 14, True), (3, 3, 28, 28, 14, True), (2, 2, 100, 100, 14, True)]
+
+
+@pytest.mark.parametrize("B,C,H,W,w,cached", F32_FWD_CASES)
+@pytest.mark.parametrize("mix", [False, True])
+def test_guard_fp32_forward_fast(B, C, H, W, w, cached, mix):
+    """y, z_save and the workspace of the forward-only fast kernels in guarded buffers."""
+    say(f"guard fp32 forward B={B} C={C} H={H} W={W} w={w} cached={cached} mix={mix}")
+    x = synth.normal_f32((B, C, H, W), 1.0, seed=410)
+    T = synth.normal_f32((C, 2 * w - 1, 2 * w - 1), 0.02, seed=411)
+    Wm = synth.normal_f32((C, 3, 3), 0.1, seed=412) if mix else None
+    xd, Td = dev(x), dev(T)
+    kw = {"M": R().wbmm_build_matrix(Td, w)} if cached else {"T": Td}
+    for zsave in (False, True):
+        y = Guarded(x.shape)
+        z = Guarded(x.shape) if zsave else None
+        wsf = guarded_ws(R().wbmm_forward_workspace_bytes(B, C, H, W, w, has_mix=mix,
+                                                          has_z_save=zsave))
+        R().wbmm_forward(xd, w, mix_w=dev(Wm) if mix else None, y=y.t,
+                         z_save=z.t if zsave else None, workspace=wsf.t if wsf else None, **kw)
+        y.check("y")
+        if zsave:
+            z.check("z_save")
+        if wsf:
+            wsf.check("forward workspace")
+        wy, wz = O.layer_forward(x.astype(np.float64), w, T=T, Wmix=Wm)
+        assert_f32(host(y.t), wy, "y")
+        if zsave:
+            assert_f32(host(z.t), wz, "z")
+
+
 @pytest.mark.parametrize("B,C,H", [(5, 3, 14), (18, 2, 28), (5, 2, 56)])
 @pytest.mark.parametrize("mix", [False, True])
 def test_guard_hier(B, C, H, mix):
