@@ -155,8 +155,10 @@ size_t wbmm_backward_workspace_bytes(int B, int C, int H, int W, int w, int layo
  *          workspace must be ordered on one stream.
  * dT and dmix_w are reduced in a fixed order (fp64 per-workgroup partials summed by a second,
  * small kernel; no floating-point atomics): results are bitwise reproducible run to run.
- * This build supports the backward for 1 <= w <= 16.
- * Errors: WBMM_E_INVALID, WBMM_E_UNSUPPORTED (w > 16, misaligned pointer), WBMM_E_WORKSPACE,
+ * Windows 1 <= w <= 32 (16 < w <= 32: dx through the forward contraction with the table
+ * rotated by 180 degrees or the matrix transposed, whose matrix is M^T; dT from row-pair tiles
+ * of 32 x 32, with the windows as the sum dimension).
+ * Errors: WBMM_E_INVALID, WBMM_E_UNSUPPORTED (misaligned pointer), WBMM_E_WORKSPACE,
  *         WBMM_E_HIP.
  */
 wbmm_status wbmm_backward(int B, int C, int H, int W, int w, int layout, const float* x,
@@ -292,8 +294,10 @@ wbmm_status wbmm_dwconv_forward(int B, int C, int H, int W, int k, const float* 
  *   G = mix adjoint of dy (kept as a bf16 map, RNE), or dy itself without a mix;
  *   dx = M_c^T G per window (bf16 matrix cores, fp32 accumulation, RNE to bf16);
  *   dT_c[k] = sum over pairs with idx = k of (G X^T)[i][j] (bf16 products, fp32 sums over a
- *   unit of 64 windows, fp64 across units in a fixed order); dmix_w as in wbmm_backward.
- * Provided for w = 14 on NCHW maps of 28x28 or 56x56 images (WBMM_E_UNSUPPORTED otherwise).
+ *   group of windows, fp64 across groups in a fixed order); dmix_w as in wbmm_backward.
+ * Any 1 <= w <= 32, NCHW or NHWC (`layout`), any map size; w = 14 on NCHW 28x28 or 56x56 maps
+ * runs the bf16 matrix-core kernels, other shapes the fp32 kernels on the bf16 values (widened
+ * exactly), with dx rounded to bf16 (RNE).
  * mix_w / z_saved: both or neither. dx, dT, dmix_w may each be NULL (skipped). bf16 maps and T
  * must be 16-byte aligned. workspace: at least wbmm_backward_bf16_workspace_bytes(...) bytes,
  * 256-byte aligned (never NULL: the dT partials live there). Errors as in wbmm_backward.

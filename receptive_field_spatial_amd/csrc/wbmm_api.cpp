@@ -283,8 +283,7 @@ namespace {
 
 size_t backward_ws_bytes(int B, int C, int H, int W, int w, int oy, int ox, int layout,
                          int has_mix) {
-  if (check_map(B, C, H + oy, W + ox, w, layout) != WBMM_OK || w > 16 || !offsets_ok(w, oy, ox))
-    return 0;
+  if (check_map(B, C, H + oy, W + ox, w, layout) != WBMM_OK || !offsets_ok(w, oy, ox)) return 0;
   static const float dummy = 0.f;
   wbmm::BwdRequest r = make_bwd(B, C, H, W, w, layout, &dummy, &dummy, nullptr,
                                 has_mix ? &dummy : nullptr, has_mix ? &dummy : nullptr, &dummy,
@@ -336,7 +335,6 @@ wbmm_status backward_call(int B, int C, int H, int W, int w, int oy, int ox, int
     return fail(WBMM_E_INVALID, "grid offset (%d, %d) outside [0, w=%d)", oy, ox, w);
   wbmm_status st = check_map(B, C, H + oy, W + ox, w, layout);
   if (st != WBMM_OK) return st;
-  if (w > 16) return fail(WBMM_E_UNSUPPORTED, "the backward is provided for w <= 16 (w=%d)", w);
   if (!x || !dy) return fail(WBMM_E_INVALID, "x and dy must be non-NULL");
   if ((T == nullptr) == (M == nullptr))
     return fail(WBMM_E_INVALID, "exactly one of T (table) and M (cached matrix) must be given");
@@ -556,7 +554,7 @@ WBMM_API wbmm_status wbmm_probe_mfma(int dtype, int blocks, int iters, float* ou
 
 WBMM_API size_t wbmm_backward_bf16_workspace_bytes(int B, int C, int H, int W, int w, int layout,
                                                    int has_mix) {
-  if (check_map(B, C, H, W, w, layout) != WBMM_OK || w > 16 ||
+  if (check_map(B, C, H, W, w, layout) != WBMM_OK ||
       !wbmm::bf16_backward_plan_ok(B, C, H, W, w, layout))
     return 0;
   return wbmm::bf16_backward_workspace(B, C, H, W, w, layout, has_mix);
@@ -569,7 +567,6 @@ WBMM_API wbmm_status wbmm_backward_bf16(int B, int C, int H, int W, int w, int l
                                         void* stream) {
   wbmm_status st = check_map(B, C, H, W, w, layout);
   if (st != WBMM_OK) return st;
-  if (w > 16) return fail(WBMM_E_UNSUPPORTED, "the backward is provided for w <= 16 (w=%d)", w);
   if (!wbmm::bf16_backward_plan_ok(B, C, H, W, w, layout))
     return fail(WBMM_E_UNSUPPORTED, "no launch shape fits this problem (w=%d)", w);
   if (!x || !T || !dy) return fail(WBMM_E_INVALID, "x, T and dy must be non-NULL");

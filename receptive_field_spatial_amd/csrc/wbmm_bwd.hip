@@ -346,11 +346,13 @@ BwdWs bwd_ws_layout(const Geo& g, const BwdRequest& r) {
 }  // namespace
 
 bool backward_plan_ok(const BwdRequest& r) {
+  if (wide_backward_ok(r)) return true;
   Geo g;
   return plan_bwd(g, r);
 }
 
 size_t backward_workspace(const BwdRequest& r) {
+  if (wide_backward_ok(r)) return backward_wide_workspace(r, sizeof(float));
   Geo g;
   if (!plan_bwd(g, r)) return 0;
   if (repack_backward_ok(r)) return repack_backward_workspace(r);
@@ -437,6 +439,7 @@ static hipError_t launch_backward_general(const BwdRequest& r, hipStream_t st) {
 }
 
 hipError_t launch_backward(const BwdRequest& r, hipStream_t st) {
+  if (wide_backward_ok(r)) return launch_backward_wide(r, false, st);  // 16 < w <= 32
   if (fast_backward_ok(r)) return launch_backward_fast(r, st);  // folds a sub-table when w = 2s
   if (repack_backward_ok(r)) return launch_backward_repacked(r, st);  // offset grid, w = 14
   return launch_backward_general<float>(r, st);
@@ -444,12 +447,14 @@ hipError_t launch_backward(const BwdRequest& r, hipStream_t st) {
 
 // bf16 maps and table on the general kernels (the shapes the fast bf16 backward does not cover).
 size_t backward_bf16_general_workspace(const BwdRequest& r) {
+  if (!r.M && !r.Tsub && wide_backward_ok(r)) return backward_wide_workspace(r, 2);
   Geo g;
   if (r.M || r.Tsub || r.oy || r.ox || !plan_bwd(g, r)) return 0;
   return bwd_ws_layout(g, r).total;
 }
 
 hipError_t launch_backward_bf16_general(const BwdRequest& r, hipStream_t st) {
+  if (!r.M && !r.Tsub && wide_backward_ok(r)) return launch_backward_wide(r, true, st);
   if (r.M || r.Tsub || r.oy || r.ox) return hipErrorInvalidValue;
   return launch_backward_general<uint16_t>(r, st);
 }

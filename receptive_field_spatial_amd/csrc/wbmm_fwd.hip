@@ -19,7 +19,8 @@ struct FwdArgs {
   const float* tsub;  // sub-window tables folded on chip (HIER), or null
 };
 
-template <typename TIn, int RPW, int WR, int ASRC, bool HIER = false>
+// FLIP: contract with M^T instead of M (the backward's dX of a cached matrix, fp32).
+template <typename TIn, int RPW, int WR, int ASRC, bool HIER = false, bool FLIP = false>
 __global__ void __launch_bounds__(kThreads) k_wbmm_fwd(FwdArgs a) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   const Geo& g = a.g;
@@ -48,7 +49,7 @@ __global__ void __launch_bounds__(kThreads) k_wbmm_fwd(FwdArgs a) {
     contract_bf16<RPW, WR, ASRC>(g, c, (const uint16_t*)a.mat, (const uint16_t*)big,
                                  (uint16_t*)mchunk, (const uint16_t*)tab, offs, wr, ct, acc);
   } else {
-    contract_f32<RPW, WR, ASRC, false, HIER>(g, c, (const float*)a.mat, (const float*)big,
+    contract_f32<RPW, WR, ASRC, FLIP, HIER>(g, c, (const float*)a.mat, (const float*)big,
                                              (float*)mchunk, (const float*)tab, (const int2*)offs,
                                              wr, ct, acc);
   }
@@ -96,26 +97,27 @@ __global__ void __launch_bounds__(kThreads) k_wbmm_fwd(FwdArgs a) {
 }
 
 // ---------------------------------------------------------------------------- dispatch
-template <typename TIn, int RPW, int WR, int ASRC, bool HIER = false>
+template <typename TIn, int RPW, int WR, int ASRC, bool HIER = false, bool FLIP = false>
 static hipError_t launch_fwd_t(const FwdArgs& a, hipStream_t st) {
-  auto fn = k_wbmm_fwd<TIn, RPW, WR, ASRC, HIER>;
+  static_assert(!FLIP || sizeof(TIn) == 4, "M^T contraction: fp32 only");
+  auto fn = k_wbmm_fwd<TIn, RPW, WR, ASRC, HIER, FLIP>;
   hipError_t e = hipFuncSetAttribute((const void*)fn, hipFuncAttributeMaxDynamicSharedMemorySize,
                                      a.g.lds_total);
   if (e != hipSuccess) return e;
   return launch_main(fn, dim3(a.g.col_groups, a.g.C, 1), dim3(kThreads), a.g.lds_total, st, a);
 }
 
-template <typename TIn, int ASRC, bool HIER = false>
+template <typename TIn, int ASRC, bool HIER = false, bool FLIP = false>
 static hipError_t launch_fwd_tiles(const FwdArgs& a, hipStream_t st) {
   const int RPW = a.g.RPW, WR = a.g.WR;
   if (WR == 1) {
-    if (RPW == 4) return launch_fwd_t<TIn, 4, 1, ASRC, HIER>(a, st);
-    if (RPW == 7) return launch_fwd_t<TIn, 7, 1, ASRC, HIER>(a, st);
-    if (RPW == 13) return launch_fwd_t<TIn, 13, 1, ASRC, HIER>(a, st);
-    if (RPW == 16) return launch_fwd_t<TIn, 16, 1, ASRC, HIER>(a, st);
+    if (RPW == 4) return launch_fwd_t<TIn, 4, 1, ASRC, HIER, FLIP>(a, st);
+    if (RPW == 7) return launch_fwd_t<TIn, 7, 1, ASRC, HIER, FLIP>(a, st);
+    if (RPW == 13) return launch_fwd_t<TIn, 13, 1, ASRC, HIER, FLIP>(a, st);
+    if (RPW == 16) return launch_fwd_t<TIn, 16, 1, ASRC, HIER, FLIP>(a, st);
   } else {
-    if (RPW == 13) return launch_fwd_t<TIn, 13, 4, ASRC, HIER>(a, st);
-    if (RPW == 16) return launch_fwd_t<TIn, 16, 4, ASRC, HIER>(a, st);
+    if (RPW == 13) return launch_fwd_t<TIn, 13, 4, ASRC, HIER, FLIP>(a, st);
+    if (RPW == 16) return launch_fwd_t<TIn, 16, 4, ASRC, HIER, FLIP>(a, st);
   }
   return hipErrorInvalidValue;
 }
@@ -165,6 +167,16 @@ size_t forward_workspace(const FwdRequest& r) {
 }
 
 hipError_t launch_forward(const FwdRequest& r, hipStream_t st) {
+  if (r.flip) {  // Z = M^T X on the general kernel (fp32 cached matrix, no mix)
+    FwdArgs a{};
+    if (!r.M || r.T || r.in_bf16 || r.out_bf16 || r.mixw || r.Tsub || !plan_fwd(a.g, r))
+      return hipErrorInvalidValue;
+    a.x = r.x;
+    a.mat = r.M;
+    a.zsave = r.zsave;
+    a.y = r.y;
+    return launch_fwd_tiles<float, 1, false, true>(a, st);
+  }
   if (fast_forward_ok(r)) return launch_forward_fast(r, st);  // folds a sub-table when w = 2s
   if (!r.Tsub && fast_bf16_forward_ok(r)) return launch_forward_fast_bf16(r, st);
   if (repack_forward_ok(r)) return launch_forward_repacked(r, st);  // offset grid, w = 14

@@ -22,6 +22,7 @@ struct FwdRequest {
   const float* Tsub;  // s x s sub-window tables folded on chip (fp32 table path, w = 2s), or null
   int s;
   int oy, ox;         // window grid offset (0 <= oy, ox < w); the fast paths take 0, 0 only
+  int flip;           // contract with M^T (fp32 cached matrix, no mix; the backward's dX)
 };
 
 struct BwdRequest {
@@ -52,6 +53,11 @@ hipError_t launch_fold(const void* Min, const void* Tsub, int C, int w, int s, i
 bool forward_plan_ok(const FwdRequest& r);
 size_t forward_workspace(const FwdRequest& r);
 hipError_t launch_forward(const FwdRequest& r, hipStream_t st);
+// Backward for 16 < w <= 32 (fp32 or bf16 maps: map_bytes 4 or 2; the request's map and table
+// pointers point at data of that type).
+bool wide_backward_ok(const BwdRequest& r);
+size_t backward_wide_workspace(const BwdRequest& r, size_t map_bytes);
+hipError_t launch_backward_wide(const BwdRequest& r, bool bf16, hipStream_t st);
 
 bool backward_plan_ok(const BwdRequest& r);
 size_t backward_workspace(const BwdRequest& r);

@@ -154,8 +154,10 @@ def bwd(lib, **kw):
 
 
 def test_backward_validation(lib):
-    assert bwd(lib, w=17) == R.WBMM_E_UNSUPPORTED
-    assert "w <= 16" in err(lib)
+    assert bwd(lib, w=33) == R.WBMM_E_INVALID
+    assert "w=33" in err(lib)
+    # 16 < w <= 32: the wide-window backward, which needs a workspace
+    assert bwd(lib, w=17) == R.WBMM_E_WORKSPACE
     assert bwd(lib, T=None) == R.WBMM_E_INVALID
     assert bwd(lib, mix=0x900000) == R.WBMM_E_INVALID           # mix without z_saved
     assert bwd(lib, z=0x900000) == R.WBMM_E_INVALID             # z_saved without mix
@@ -166,7 +168,8 @@ def test_backward_validation(lib):
     assert bwd(lib) == R.WBMM_E_WORKSPACE
     assert bwd(lib, ws=0xA00000, wsb=need - 1) == R.WBMM_E_WORKSPACE
     assert bwd(lib, ws=0xA00010, wsb=need) == R.WBMM_E_UNSUPPORTED  # not 256-byte aligned
-    assert lib.wbmm_backward_workspace_bytes(1, 2, 8, 8, 17, 0, 0) == 0
+    assert lib.wbmm_backward_workspace_bytes(1, 2, 8, 8, 17, 0, 0) > 0
+    assert lib.wbmm_backward_workspace_bytes(1, 2, 8, 8, 33, 0, 0) == 0
 
 
 def hier_fwd(lib, **kw):
@@ -224,12 +227,14 @@ def test_shifted_validation(lib):
         assert lib.wbmm_forward_shifted_workspace_bytes(2, 3, 28, 28, 14, oy, ox, 0, 1, 0) == 0
         assert lib.wbmm_backward_shifted_workspace_bytes(2, 3, 28, 28, 14, oy, ox, 0, 0) == 0
     assert "grid offset" in err(lib)
-    # y aliasing x is still caught with a valid offset; backward w <= 16
+    # y aliasing x is still caught with a valid offset; the wide-window backward (w = 20) takes
+    # offsets too, and needs a workspace
     assert lib.wbmm_forward_shifted(2, 3, 28, 28, 14, 7, 7, 0, 0, 0, FAKE, 0x300000, None, None,
                                     None, FAKE, None, 0, None) == R.WBMM_E_INVALID
     assert lib.wbmm_backward_shifted(2, 3, 40, 40, 20, 10, 10, 0, FAKE, 0x300000, None, None,
                                      None, 0x400000, FAKE2, None, None, None, 0,
-                                     None) == R.WBMM_E_UNSUPPORTED
+                                     None) == R.WBMM_E_WORKSPACE
+    assert lib.wbmm_backward_shifted_workspace_bytes(2, 3, 40, 40, 20, 10, 10, 0, 0) > 0
     assert lib.wbmm_backward_shifted_workspace_bytes(2, 3, 28, 28, 14, 7, 7, 0, 0) > 0
 
 
@@ -253,16 +258,17 @@ def test_shifted_workspace_covers_the_repacked_maps(lib):
 
 
 def test_backward_bf16_validation(lib):
-    """bf16 backward: w <= 16 (any layout and map size), mix and z_saved together, workspace
-    needed (the fast w = 14 NCHW 28² / 56² shapes and the general ones have their own layouts)."""
+    """bf16 backward: 1 <= w <= 32 (any layout and map size), mix and z_saved together, workspace
+    needed (the fast w = 14 NCHW 28² / 56² shapes, the general and the wide-window ones have
+    their own layouts)."""
     def call(B=2, C=3, H=28, W=28, w=14, layout=0, mix=None, z=None, dx=0x500000, ws=0x900000,
              wsb=1 << 30):
         return lib.wbmm_backward_bf16(B, C, H, W, w, layout, FAKE, 0x300000, mix, z, FAKE2, dx,
                                       0x600000, None, ws, wsb, None)
-    assert call(w=17) == R.WBMM_E_UNSUPPORTED
-    assert "w <= 16" in err(lib)
+    assert call(w=33) == R.WBMM_E_INVALID
     assert call(w=0) == R.WBMM_E_INVALID
-    for kw in ({"H": 30, "W": 30}, {"w": 7}, {"layout": 1}):   # general shapes: workspace sized
+    for kw in ({"H": 30, "W": 30}, {"w": 7}, {"layout": 1}, {"w": 17}, {"w": 28, "layout": 1}):
+        # general and wide-window shapes: workspace sized
         need = lib.wbmm_backward_bf16_workspace_bytes(2, 3, kw.get("H", 28), kw.get("W", 28),
                                                       kw.get("w", 14), kw.get("layout", 0), 0)
         assert need > 0
@@ -273,7 +279,8 @@ def test_backward_bf16_validation(lib):
     need = lib.wbmm_backward_bf16_workspace_bytes(2, 3, 28, 28, 14, 0, 1)
     assert need > lib.wbmm_backward_bf16_workspace_bytes(2, 3, 28, 28, 14, 0, 0) > 0
     assert call(mix=0x700000, z=0x800000, wsb=need - 1) == R.WBMM_E_WORKSPACE
-    assert lib.wbmm_backward_bf16_workspace_bytes(2, 3, 30, 30, 17, 0, 0) == 0
+    assert lib.wbmm_backward_bf16_workspace_bytes(2, 3, 30, 30, 17, 0, 0) > 0
+    assert lib.wbmm_backward_bf16_workspace_bytes(2, 3, 30, 30, 33, 0, 0) == 0
 
 
 def test_probe_validation(lib):

@@ -535,6 +535,28 @@ def test_backward_shapes(B, C, H, W, w, mix, cached):
         assert_f32(dW, wdW, "dWmix")
 
 
+@pytest.mark.parametrize("B,C,H,W,w,mix,layout", [
+    (2, 2, 28, 28, 28, True, "NCHW"), (2, 2, 28, 28, 28, False, "NCHW"),
+    (3, 2, 56, 56, 28, True, "NCHW"),    # dx on the fast fp32 w = 28 kernel
+    (1, 3, 40, 37, 20, True, "NCHW"),    # ragged, padded map
+    (2, 2, 64, 64, 32, False, "NCHW"), (3, 2, 30, 45, 17, True, "NCHW"),
+    (2, 2, 28, 28, 28, True, "NHWC"), (1, 2, 33, 21, 19, False, "NHWC"),
+])
+@pytest.mark.parametrize("cached", [False, True])
+def test_backward_wide(B, C, H, W, w, mix, layout, cached):
+    """The backward for windows wider than 16 (dx through the forward with M^T: the rotated table,
+    or the transposed cached matrix; dT on 32x32 row-pair tiles) against the oracle, with the mix
+    and without, padded and ragged maps, NHWC; run twice, bitwise equal."""
+    say(f"backward wide B={B} C={C} H={H} W={W} w={w} mix={mix} {layout} cached={cached}")
+    (dx, dT, dW), (wdx, wdT, wdW) = bwd_case(B, C, H, W, w, mix=mix, cached=cached, layout=layout)
+    assert_f32(dx, wdx, "dx")
+    assert_f32(dT, wdT, "dT")
+    if mix:
+        assert_f32(dW, wdW, "dWmix")
+    (dx2, dT2, _), _ = bwd_case(B, C, H, W, w, mix=mix, cached=cached, layout=layout)
+    assert np.array_equal(dx, dx2) and np.array_equal(dT, dT2)
+
+
 def test_backward_nhwc():
     say("backward NHWC B=2 C=3 28x28 w=14 mix")
     (dx, dT, dW), (wdx, wdT, wdW) = bwd_case(2, 3, 28, 28, 14, mix=True, layout="NHWC")
@@ -601,8 +623,8 @@ def test_errors_enqueue_nothing():
         Rm.wbmm_forward(x, 4, T=T, y=x)  # y aliases x
     assert e.value.status == Rm.WBMM_E_INVALID
     with pytest.raises(Rm.WbmmError) as e:
-        Rm.wbmm_backward(x, x, 20, T=torch.zeros((2, 39, 39), device="cuda"))
-    assert e.value.status == Rm.WBMM_E_UNSUPPORTED
+        Rm.wbmm_backward(x, x, 33, T=torch.zeros((2, 65, 65), device="cuda"))
+    assert e.value.status == Rm.WBMM_E_INVALID
     torch.cuda.synchronize()
     assert torch.all(y == 7.0)
 
@@ -827,7 +849,7 @@ def test_dwconv_full_size_sampled():
 # B = 5 at 28x28 leaves 45 windows: 12 repacked images, the last with 3 zero windows
 SHIFT_CASES = [(2, 3, 28, 28, 14, 7, 7), (1, 2, 30, 25, 14, 3, 11), (2, 3, 17, 13, 4, 2, 1),
                (1, 2, 128, 128, 14, 7, 7), (2, 2, 9, 9, 7, 0, 3), (5, 4, 28, 28, 14, 7, 7),
-               (3, 2, 5, 40, 14, 13, 0)]
+               (3, 2, 5, 40, 14, 13, 0), (1, 2, 40, 40, 20, 10, 10)]
 
 
 @pytest.mark.parametrize("B,C,H,W,w,oy,ox", SHIFT_CASES)
@@ -855,7 +877,7 @@ def test_forward_shifted(B, C, H, W, w, oy, ox, mix, src, zsave):
 
 @pytest.mark.parametrize("B,C,H,W,w,oy,ox", [(2, 3, 28, 28, 14, 7, 7), (1, 2, 17, 13, 4, 2, 1),
                                              (1, 2, 56, 56, 14, 5, 9), (5, 4, 28, 28, 14, 7, 7),
-                                             (3, 2, 5, 40, 14, 13, 0)])
+                                             (3, 2, 5, 40, 14, 13, 0), (1, 2, 40, 40, 20, 10, 10)])
 @pytest.mark.parametrize("zsave", [True, False])
 def test_forward_shifted_bf16(B, C, H, W, w, oy, ox, zsave):
     """bf16 maps on the offset grid (w = 14: repacked windows on the fast bf16 forward); z_save,
@@ -997,6 +1019,10 @@ def test_backward_bf16(B, C, H, mix):
     (1, 2, 32, 32, 16, "NCHW", True),
     (2, 2, 128, 128, 14, "NCHW", True),  # window mode: plane-staged mix adjoint (bf16 G)
     (1, 2, 100, 100, 14, "NHWC", True),  # window mode, channels-last: per-pixel mix passes
+    # windows wider than 16: dx through the bf16 forward with the rotated table (the fast bf16
+    # w = 28 kernel on 56x56 maps), dT on 32x32 row-pair tiles
+    (2, 2, 56, 56, 28, "NCHW", True), (1, 2, 40, 37, 20, "NCHW", False),
+    (2, 2, 34, 30, 17, "NHWC", True),
 ])
 def test_backward_bf16_general(B, C, H, W, w, layout, mix):
     """bf16 maps and table on the shapes the fast bf16 backward does not cover (any w <= 16,
