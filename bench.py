@@ -56,7 +56,7 @@ KERNEL_FILES = {"k_fwd_ws": "wbmm_fast.hip", "k_bwd_ls": "wbmm_fast.hip", "k_fwd
                 "k_fwd_bf16_w28": "wbmm_fastbf.hip", "k_fwd_bf16": "wbmm_fastbf.hip",
                 "k_wbmm_fwd": "wbmm_fwd.hip", "k_wbmm_bwd": "wbmm_bwd.hip",
                 "k_fwd_f32_w7": "wbmm_fast7.hip", "k_fwd_f32_w28": "wbmm_fast28.hip",
-                "k_mix_direct": "wbmm_aux.hip"}
+                "k_fwd_tab": "wbmm_fasttab.hip", "k_mix_direct": "wbmm_aux.hip"}
 HOST_HEADERS = ("wbmm_launch.hpp",)
 
 
@@ -120,7 +120,7 @@ def accounting(wl, cached=False):
     tab = wl.C * L * esz
     if wl.s is not None:
         tab += wl.C * (2 * wl.s - 1) ** 2 * esz
-    if cached or (wl.s is not None and not wl.backward):
+    if cached:
         tab = wl.C * d * d * esz  # the cached (folded) matrices are read instead of the tables
     fwd_flops = Eg * 2 * d + E * (18 if wl.mix else 0)
     fwd_bytes = E * esz * (2 + (1 if wl.backward else 0)) + tab + (wl.C * 36 if wl.mix else 0)
@@ -132,6 +132,14 @@ def accounting(wl, cached=False):
             (wl.C * 72 if wl.mix else 0)
     acc["step_flops"] = fwd_flops + acc.get("bwd_flops", 0)
     return acc
+
+
+def mix_in_main_kernel(wl, cached=False):
+    """Whether the main forward and backward kernels apply the 3x3 mix (and its adjoint)
+    themselves: the w = 14 kernels on whole 14/28/56 images of the plain grid. Elsewhere the mix
+    runs as a pass of its own."""
+    whole = wl.w == 14 and wl.H == wl.W and wl.H in (14, 28, 56)
+    return wl.mix and whole and not wl.shift and not cached
 
 
 # ----------------------------------------------------------------------------- CPU baseline
@@ -163,7 +171,7 @@ def cpu_baseline(wl, budget_s: float = 10.0, cached: bool = False):
     t_start = time.perf_counter()
     while True:
         t0 = time.perf_counter()
-        if cached or (Ts is not None and not wl.backward):  # inference with the cached matrix
+        if cached:  # inference with the cached (folded) matrix
             M = O.build_matrix(T, wl.w)
             if Ts is not None:
                 M = O.fold_hier(M, Ts, wl.w, wl.s)
@@ -324,10 +332,11 @@ def run(args):
     M = None
     Tsub = to_dev(inp["T_sub"]) if wl.s is not None else None
     hier_train = wl.s is not None and wl.backward  # fold on chip, dT_sub in the backward
-    if wl.s is not None and not wl.backward:  # inference: folded M built once and cached
-        M = R.wbmm_fold_hier(R.wbmm_build_matrix(T, wl.w), Tsub, wl.w, wl.s)
-    elif args.cached:  # inference caching: M built once from the table, then read every step
+    hier_chip = wl.s is not None and not args.cached  # the forward folds T_sub on chip
+    if args.cached:  # inference caching: M (folded: M') built once, then read every step
         M = R.wbmm_build_matrix(T, wl.w)
+        if wl.s is not None:
+            M = R.wbmm_fold_hier(M, Tsub, wl.w, wl.s)
     L = 2 * wl.w - 1
     dT = torch.empty((wl.C, L, L), dtype=torch.float32, device=dev)
     dW = torch.empty((wl.C, 3, 3), dtype=torch.float32, device=dev) if wl.mix else None
@@ -351,9 +360,9 @@ def run(args):
         nf = R.wbmm_forward_shifted_workspace_bytes(wl.B, wl.C, wl.H, wl.W, wl.w, wl.shift,
                                                     wl.shift, has_mix=wl.mix,
                                                     has_z_save=wl.backward and wl.mix)
-    elif hier_train:
+    elif hier_chip:
         nf = R.wbmm_forward_hier_workspace_bytes(wl.B, wl.C, wl.H, wl.W, wl.w, wl.s,
-                                                 has_mix=wl.mix, has_z_save=True)
+                                                 has_mix=wl.mix, has_z_save=wl.backward and wl.mix)
     else:
         nf = R.wbmm_forward_workspace_bytes(wl.B, wl.C, wl.H, wl.W, wl.w, has_mix=wl.mix,
                                             has_z_save=wl.backward and wl.mix)
@@ -366,8 +375,8 @@ def run(args):
             R.wbmm_forward_shifted(s["x"], wl.w, wl.shift, wl.shift, mix_w=Wm, y=s["y"],
                                    z_save=s.get("z"), workspace=ws_f, stream=stream, **kw_tab)
             return
-        if hier_train:
-            R.wbmm_forward_hier(s["x"], wl.w, wl.s, T, Tsub, mix_w=Wm, y=s["y"], z_save=s["z"],
+        if hier_chip:
+            R.wbmm_forward_hier(s["x"], wl.w, wl.s, T, Tsub, mix_w=Wm, y=s["y"], z_save=s.get("z"),
                                 workspace=ws_f, stream=stream)
             return
         R.wbmm_forward(s["x"], wl.w, mix_w=Wm, y=s["y"], z_save=s.get("z"), workspace=ws_f,
@@ -467,9 +476,15 @@ def run(args):
 
     # dominant kernel and its roofline
     fwd_avg = statistics.mean(fwd_ms) / 1e3
-    kernels = {"k_wbmm_fwd": (fwd_avg, acc["fwd_flops"], acc["fwd_bytes"])}
+    # the mix's flops count for the main kernel only where it applies the mix itself (the bf16
+    # backward's bracket holds all of its kernels, the mix pass included)
+    mixf = acc["E"] * 18 if wl.mix else 0
+    fused = mix_in_main_kernel(wl, args.cached)
+    kernels = {"k_wbmm_fwd": (fwd_avg, acc["fwd_flops"] - (0 if fused else mixf), acc["fwd_bytes"])}
     if wl.backward:
-        kernels["k_wbmm_bwd"] = (statistics.mean(bwd_ms) / 1e3, acc["bwd_flops"], acc["bwd_bytes"])
+        kernels["k_wbmm_bwd"] = (statistics.mean(bwd_ms) / 1e3,
+                                 acc["bwd_flops"] - (0 if fused or bf16_bwd else 2 * mixf),
+                                 acc["bwd_bytes"])
     kname = max(kernels, key=lambda k: kernels[k][0])
     ksec, kflops, kbytes = kernels[kname]
     mfma_bound = not (bf16 and wl.w <= 14)
@@ -509,7 +524,7 @@ def run(args):
                    "mix": wl.mix, "fold_s": wl.s, "grid_offset": wl.shift,
                    "pass": "fwd+bwd" if wl.backward else "fwd",
                    "matrix": ("cached M" if M is not None else
-                              "formed and folded on chip from T, T_sub" if hier_train else
+                              "formed and folded on chip from T, T_sub" if hier_chip else
                               "formed on chip from T"),
                    "rotating_batches": nsets},
         "out_elems_per_s": round(acc["E"] / (ms_step / 1e3), 1),
@@ -563,7 +578,7 @@ def _pmc_rows(d):
 
 # bench label -> names of the kernels that can be that call's main kernel (fast or general path)
 MAIN_KERNELS = {"k_wbmm_fwd": ("k_fwd_ws", "k_fwd_cm", "k_fwd_bf16_w7", "k_fwd_bf16_w28", "k_fwd_bf16",
-                               "k_fwd_f32_w7", "k_fwd_f32_w28", "k_wbmm_fwd"),
+                               "k_fwd_f32_w7", "k_fwd_f32_w28", "k_fwd_tab", "k_wbmm_fwd"),
                 "k_wbmm_bwd": ("k_bwd_ls", "k_wbmm_bwd")}
 
 

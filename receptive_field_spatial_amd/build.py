@@ -17,7 +17,7 @@ LIB_PATH = os.path.join(PKG_DIR, "libwbmm.so")
 SOURCES = ["wbmm_api.cpp", "wbmm_aux.hip", "wbmm_fwd.hip", "wbmm_bwd.hip", "wbmm_fast.hip",
            "wbmm_fastbf.hip", "wbmm_dw.hip",
            "wbmm_probe.hip", "wbmm_bwdbf.hip", "wbmm_repack.hip", "wbmm_fastcm.hip",
-           "wbmm_fast28.hip", "wbmm_fast7.hip",
+           "wbmm_fast28.hip", "wbmm_fast7.hip", "wbmm_fasttab.hip",
            "wbmm_bwdwide.hip"]
 
 ARCH = "gfx950"

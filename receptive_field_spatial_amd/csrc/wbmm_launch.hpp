@@ -85,6 +85,10 @@ hipError_t launch_backward_repacked(const BwdRequest& r, hipStream_t st);
 // Fast fp32 forward on a cached matrix (w = 14, NCHW, any H and W, no sub-table, plain grid):
 // the contraction's result goes to `out` (and a copy to `out2` when not null).
 bool fast_cm_forward_ok(const FwdRequest& r);
+// Fast fp32 forward from the table (w = 14, NCHW, any H and W, plain grid; a 7 x 7 sub-table
+// folded on chip when Tsub is set): the contraction into out (and out2 when not null).
+bool fast_tab_forward_ok(const FwdRequest& r);
+hipError_t launch_forward_fast_tab(const FwdRequest& r, float* out, float* out2, hipStream_t st);
 // fp32 w = 7 and w = 28 on NCHW 56x56 maps, table input: the contraction into out (and out2
 // when not null).
 bool fast_f32_w7_forward_ok(const FwdRequest& r);

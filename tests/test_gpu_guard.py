@@ -134,7 +134,8 @@ def test_guard_fp32_layer(B, C, H, W, w, mix):
 # forward-only fast fp32 kernels: w = 7 and w = 28 on 56x56 maps (ragged batches against the
 # w = 28 kernel's 8-image blocks), and the cached-matrix kernel (whole and border windows)
 F32_FWD_CASES = [(5, 2, 56, 56, 7, False), (9, 2, 56, 56, 28, False), (3, 2, 56, 56, 28, False),
-                 (5, 3, 56, 56, 14, True), (3, 3, 28, 28, 14, True), (2, 2, 100, 100, 14, True)]
+                 (5, 3, 56, 56, 14, True), (3, 3, 28, 28, 14, True), (2, 2, 100, 100, 14, True),
+                 (2, 3, 100, 100, 14, False), (3, 2, 30, 44, 14, False)]
 
 
 @pytest.mark.parametrize("B,C,H,W,w,cached", F32_FWD_CASES)
@@ -165,10 +166,11 @@ def test_guard_fp32_forward_fast(B, C, H, W, w, cached, mix):
             assert_f32(host(z.t), wz, "z")
 
 
-@pytest.mark.parametrize("B,C,H", [(5, 3, 14), (18, 2, 28), (5, 2, 56)])
+@pytest.mark.parametrize("B,C,H", [(5, 3, 14), (18, 2, 28), (5, 2, 56), (2, 3, 30)])
 @pytest.mark.parametrize("mix", [False, True])
 def test_guard_hier(B, C, H, mix):
-    """The fast kernels with the fold on chip: y, z_save, dx, dT, dT_sub, dWmix guarded."""
+    """The kernels with the fold on chip (whole images; a padded map: the table kernel forward,
+    the general backward): y, z_save, dx, dT, dT_sub, dWmix guarded."""
     w, s = 14, 7
     say(f"guard hier B={B} C={C} H=W={H} mix={mix}")
     x = synth.normal_f32((B, C, H, H), 1.0, seed=410)

@@ -418,6 +418,65 @@ def test_forward_f32_w28_shift_bitwise_all_channels(B, C):
     assert np.array_equal(host(R().wbmm_forward(dev(x), w, T=dev(T))), want)
 
 
+def _window_shift_padded(x, w, dy, dx):
+    """_window_shift on a map zero-padded up to whole windows, cropped back."""
+    B, C, H, W = x.shape
+    Hp, Wp = -(-H // w) * w, -(-W // w) * w
+    xp = np.zeros((B, C, Hp, Wp), x.dtype)
+    xp[:, :, :H, :W] = x
+    return _window_shift(xp, w, dy, dx)[:, :, :H, :W]
+
+
+@pytest.mark.parametrize("B,C,H,W", [(2, 3, 128, 128), (1, 2, 30, 25), (3, 2, 14, 20),
+                                     (1, 1, 140, 140), (5, 2, 42, 14), (1, 3, 17, 150)])
+@pytest.mark.parametrize("mix,zsave", [(False, False), (False, True), (True, False), (True, True)])
+def test_forward_f32_tab_fast(B, C, H, W, mix, zsave):
+    """The fp32 w = 14 table kernel for maps that are not whole 14/28/56 images (padded, ragged,
+    one window wide): z_save and the mix (a separate pass) against the oracle."""
+    say(f"forward f32 table fast B={B} C={C} H={H} W={W} mix={mix} zsave={zsave}")
+    yh, want_y, zh, want_z = fwd_case(B, C, H, W, 14, mix=mix, zsave=zsave)
+    assert_f32(yh, want_y, "y")
+    if zsave:
+        assert_f32(zh, want_z, "z")
+
+
+@pytest.mark.parametrize("B,C,H,W", [(2, 300, 128, 128), (3, 129, 30, 44), (1, 520, 60, 70)])
+def test_forward_f32_tab_shift_bitwise_all_channels(B, C, H, W):
+    """One-hot tables at a different offset in every channel on padded maps: the fp32 w = 14
+    table kernel's output is the input shifted inside each window, bit for bit, in every channel.
+    More work items than waves, so waves walk several wave-units and thirds and restage their
+    table when the channel changes."""
+    w = 14
+    say(f"forward f32 table shift all channels B={B} C={C} H={H} W={W}")
+    x = synth.normal_f32((B, C, H, W), 1.0, seed=39)
+    L1 = 2 * w - 1
+    dy = (np.arange(C) * 5 + 2) % L1 - (w - 1)
+    dx = (np.arange(C) * 11 + 1) % L1 - (w - 1)
+    T = np.zeros((C, L1, L1), np.float32)
+    T[np.arange(C), dy + w - 1, dx + w - 1] = 1.0
+    want = _window_shift_padded(x, w, dy, dx)
+    assert np.array_equal(host(R().wbmm_forward(dev(x), w, T=dev(T))), want)
+
+
+@pytest.mark.parametrize("B,C,H,W", [(2, 300, 128, 128), (1, 130, 45, 33)])
+def test_forward_hier_tab_shift_bitwise_all_channels(B, C, H, W):
+    """Zero window tables and one-hot 7 x 7 sub-tables at a different offset in every channel:
+    the fold on chip of the fp32 table kernel makes the output the input shifted inside each
+    7 x 7 sub-window, bit for bit, on padded maps."""
+    w, s = 14, 7
+    say(f"forward hier table shift all channels B={B} C={C} H={H} W={W}")
+    x = synth.normal_f32((B, C, H, W), 1.0, seed=40)
+    S1 = 2 * s - 1
+    dy = (np.arange(C) * 3 + 1) % S1 - (s - 1)
+    dx = (np.arange(C) * 7 + 4) % S1 - (s - 1)
+    T = np.zeros((C, 2 * w - 1, 2 * w - 1), np.float32)
+    Ts = np.zeros((C, S1, S1), np.float32)
+    Ts[np.arange(C), dy + s - 1, dx + s - 1] = 1.0
+    want = _window_shift_padded(x, s, dy, dx)
+    y = R().wbmm_forward_hier(dev(x), w, s, dev(T), dev(Ts))
+    assert np.array_equal(host(y), want)
+
+
 def _bf16_shift_case(w, hw, B, C, mix):
     """One-hot tables at a different offset in every channel: the output is the input shifted
     inside each window (exact in bf16). More units than resident workgroups, so workgroups walk
