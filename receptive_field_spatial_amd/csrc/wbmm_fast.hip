@@ -314,12 +314,13 @@ __device__ __forceinline__ void write_acc(float* R, int lane, const v4f (&acc)[N
 }
 
 // One image column of a wave-unit region, as seen by the 3x3 stencils: lane `lane` of pass p owns
-// column col = PW*p + lane (image im, column v); the neighbour columns' LDS bases are clamped to
-// the own column at the image border and the values read there are selected away. A sweep that
-// overwrites its input in place needs image-aligned passes (PW = S::CHUNK_COLS), so that no
-// column's neighbour is rewritten by an earlier pass.
-template <class S, int PW = 64>
+// column col = PW*p + lane (image im, column v). Passes are image-aligned (PW = S::CHUNK_COLS):
+// the neighbour columns of an image are neighbour lanes, and a sweep that overwrites its input in
+// place never rewrites a column another pass still reads. The neighbour columns' LDS bases are
+// clamped to the own column at the image border and the values read there are selected away.
+template <class S, int PW_ = S::CHUNK_COLS>
 struct Column {
+  static constexpr int PW = PW_;
   static constexpr int NP = (S::COLS + PW - 1) / PW;
   int im, v;
   bool active, hasL, hasR;
@@ -336,33 +337,35 @@ struct Column {
     pl = col_part<S>(im, hasL ? v - 1 : v);
     pr = col_part<S>(im, hasR ? v + 1 : v);
   }
-  // 3 values of image row h (zero outside the image)
-  __device__ __forceinline__ void row(const float* R, int h, float (&w)[3]) const {
+};
+
+// Walk one column top to bottom with a window w[u][t] = value at (h+u-1, v+t-1) read from LDS
+// (three reads per row; zero outside the image), calling f(h, w) for every row. Rows are read in blocks of RB, the next
+// block's reads in flight while the current one is processed. f may overwrite row h of the
+// column in LDS: every read of rows <= h+1 has been issued by then, and later blocks only read
+// rows below. This form spends no VALU on the neighbours, for sweeps whose arithmetic is the
+// limit; sweep_column_lanes below trades two of the reads for two DPP moves.
+template <class S, int RB, class Col, class F>
+__device__ __forceinline__ void sweep_column_lds(const float* R, const Col& col, F&& f) {
+  static_assert(Col::PW == S::CHUNK_COLS, "image-aligned passes");
+  static_assert(S::IH % RB == 0, "row block");
+  auto row = [&](int h, float (&w)[3]) {
     if (h < 0 || h >= S::IH) {
       w[0] = w[1] = w[2] = 0.f;
       return;
     }
-    const float l = R[pl + row_part<S>(h)], c = R[pc + row_part<S>(h)], r = R[pr + row_part<S>(h)];
-    w[0] = hasL ? l : 0.f;
+    const float l = R[col.pl + row_part<S>(h)], c = R[col.pc + row_part<S>(h)];
+    const float r = R[col.pr + row_part<S>(h)];
+    w[0] = col.hasL ? l : 0.f;
     w[1] = c;
-    w[2] = hasR ? r : 0.f;
-  }
-};
-
-// Walk one column top to bottom with a sliding 3x3 window w[u][t] = value at (h+u-1, v+t-1),
-// calling f(h, w) for every row. Rows are read from LDS in blocks of RB, the next block's reads in
-// flight while the current one is processed, so LDS latency is paid about once per column. f may
-// overwrite row h of the column in LDS: every read of rows <= h+1 has been issued by then, and
-// later blocks only read rows below.
-template <class S, int RB, class Col, class F>
-__device__ __forceinline__ void sweep_column(const float* R, const Col& col, F&& f) {
-  static_assert(S::IH % RB == 0, "row block");
+    w[2] = col.hasR ? r : 0.f;
+  };
   float w[3][3];
-  col.row(R, -1, w[0]);
-  col.row(R, 0, w[1]);
+  row(-1, w[0]);
+  row(0, w[1]);
   float nxt[RB][3];
 #pragma unroll
-  for (int j = 0; j < RB; ++j) col.row(R, j + 1, nxt[j]);
+  for (int j = 0; j < RB; ++j) row(j + 1, nxt[j]);
 #pragma unroll
   for (int hb = 0; hb < S::IH; hb += RB) {
     float cur[RB][3];
@@ -372,13 +375,66 @@ __device__ __forceinline__ void sweep_column(const float* R, const Col& col, F&&
       for (int t = 0; t < 3; ++t) cur[j][t] = nxt[j][t];
     if (hb + RB < S::IH) {
 #pragma unroll
-      for (int j = 0; j < RB; ++j) col.row(R, hb + RB + j + 1, nxt[j]);
+      for (int j = 0; j < RB; ++j) row(hb + RB + j + 1, nxt[j]);
     }
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int j = 0; j < RB; ++j) {
 #pragma unroll
       for (int t = 0; t < 3; ++t) w[2][t] = cur[j][t];
+      f(hb + j, w);
+#pragma unroll
+      for (int t = 0; t < 3; ++t) {
+        w[0][t] = w[1][t];
+        w[1][t] = w[2][t];
+      }
+    }
+  }
+}
+
+// Walk one column top to bottom with a sliding 3x3 window w[u][t] = value at (h+u-1, v+t-1),
+// calling f(h, w) for every row. Passes are image-aligned (PW = S::CHUNK_COLS), so the neighbour
+// columns of a lane's column are the neighbour lanes' columns: each row costs one LDS read, the
+// column's own value, and the neighbours come by wave-wide DPP shifts (a lane at an image border
+// selects zero instead). Rows are read in blocks of RB, the next block's reads in flight while
+// the current one is processed. f may overwrite row h of the column in LDS: every lane's reads of
+// rows <= h+1 have been issued by then, and later blocks only read rows below.
+__device__ __forceinline__ float lane_left(float x) {  // x of lane - 1 (wave_shr:1)
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x138, 0xf, 0xf, true));
+}
+__device__ __forceinline__ float lane_right(float x) {  // x of lane + 1 (wave_shl:1)
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x130, 0xf, 0xf, true));
+}
+template <class S, int RB, class Col, class F>
+__device__ __forceinline__ void sweep_column_lanes(const float* R, const Col& col, F&& f) {
+  static_assert(Col::PW == S::CHUNK_COLS, "image-aligned passes");
+  static_assert(S::IH % RB == 0, "row block");
+  auto ctr = [&](int h) { return (h < 0 || h >= S::IH) ? 0.f : R[col.pc + row_part<S>(h)]; };
+  auto expand = [&](float c, float (&w)[3]) {
+    const float l = lane_left(c), r = lane_right(c);
+    w[0] = col.hasL ? l : 0.f;
+    w[1] = c;
+    w[2] = col.hasR ? r : 0.f;
+  };
+  float w[3][3];
+  w[0][0] = w[0][1] = w[0][2] = 0.f;  // row -1
+  expand(ctr(0), w[1]);
+  float nxt[RB];
+#pragma unroll
+  for (int j = 0; j < RB; ++j) nxt[j] = ctr(j + 1);
+#pragma unroll
+  for (int hb = 0; hb < S::IH; hb += RB) {
+    float cur[RB];
+#pragma unroll
+    for (int j = 0; j < RB; ++j) cur[j] = nxt[j];
+    if (hb + RB < S::IH) {
+#pragma unroll
+      for (int j = 0; j < RB; ++j) nxt[j] = ctr(hb + RB + j + 1);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int j = 0; j < RB; ++j) {
+      expand(cur[j], w[2]);
       f(hb + j, w);
 #pragma unroll
       for (int t = 0; t < 3; ++t) {
@@ -426,7 +482,7 @@ __device__ __forceinline__ void fwd_epilogue(const FastArgs& a, const float* R, 
     const Column<S> col(p, lane);
     if (!col.active || ir0 + col.im >= U.nimg) continue;
     const int o = (ir0 + col.im) * U.cp + col.v;
-    sweep_column<S, 7>(R, col, [&](int h, const float (&w)[3][3]) {
+    sweep_column_lanes<S, 7>(R, col, [&](int h, const float (&w)[3][3]) {
       const float z = w[1][1];
       if constexpr (ZS) zu[o + h * S::IW] = z;
       float yv = z;
@@ -681,7 +737,7 @@ __device__ __forceinline__ void bwd_mix_sweep(float* R, const float (&w9r)[9],
     float wcol[9];
 #pragma unroll
     for (int q = 0; q < 9; ++q) wcol[q] = 0.f;
-    sweep_column<S, 7>(R, col, [&](int h, const float (&w)[3][3]) {
+    sweep_column_lds<S, 7>(R, col, [&](int h, const float (&w)[3][3]) {
       // w[u][t] = dy(h+u-1, v+t-1); dz(h,v) = sum_{u,t} W[2-u][2-t] w[u][t]
       float gsum = 0.f;
 #pragma unroll
