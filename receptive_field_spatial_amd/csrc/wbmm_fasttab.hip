@@ -25,6 +25,7 @@
 #include "wbmm_device.hpp"
 #include "wbmm_launch.hpp"
 
+#include <algorithm>
 #include <atomic>
 
 namespace wbmm {
@@ -48,7 +49,9 @@ static_assert(kTabWaves * 2 * TPITCH * 4 <= kTabLdsReserve, "per-wave tables fit
 
 struct TabArgs {
   int B, C, H, W;
-  int nWx, nWin;     // windows per image row, per image
+  int oy, ox;        // window grid offset: window (wy, wx) starts at map pixel (14 wy - oy, 14 wx - ox)
+  int nWx, nWy, nWin;  // windows per image row, per image column, per image
+  int ix0, iy0;      // first whole window column, row
   int nIx, nIy;      // whole windows per image row, per image column
   int nIn;           // whole windows per image (nIx * nIy)
   int wupc;          // wave-units per channel: ceil(B * nWin / 16)
@@ -68,26 +71,33 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t tab_x_rsrc(const TabArgs& a) {
 }
 
 // Window order within a channel: the whole windows of every image first (image by image,
-// row-major), then the partial ones of a padded map (per image: the right column, then the bottom
-// row), so that most wave-units hold only whole windows and take the vector loads below.
+// row-major over the whole-window block), then the partial ones at the map border (per image,
+// row-major over the frame around that block), so that most wave-units hold only whole windows
+// and take the vector loads below.
 __device__ __forceinline__ void tab_window(const TabArgs& a, int win, int& b, int& wy, int& wx) {
   const int nin_all = a.B * a.nIn;
   if (win < nin_all) {
     b = win / a.nIn;
     const int i = win - b * a.nIn;
-    wy = i / a.nIx;
-    wx = i - wy * a.nIx;
+    const int ry = i / a.nIx;
+    wy = a.iy0 + ry;
+    wx = a.ix0 + (i - ry * a.nIx);
   } else {
     const int nbd = a.nWin - a.nIn, j = win - nin_all;
     b = j / nbd;
     const int i = j - b * nbd;
-    const int ncol = a.nWx > a.nIx ? a.nIy : 0;  // right-column windows per image
-    if (i < ncol) {
-      wy = i;
-      wx = a.nIx;
-    } else {
-      wy = a.nIy;
-      wx = i - ncol;
+    const int top = a.iy0 * a.nWx, per = a.nWx - a.nIx, mid = a.nIy * per;
+    if (i < top) {  // rows above the whole-window block
+      wy = i / a.nWx;
+      wx = i - wy * a.nWx;
+    } else if (i < top + mid) {  // the block's rows: columns left and right of it
+      const int k = i - top, ry = k / per, e = k - ry * per;
+      wy = a.iy0 + ry;
+      wx = e < a.ix0 ? e : e + a.nIx;
+    } else {  // rows below it
+      const int k = i - top - mid, ry = k / a.nWx;
+      wy = a.iy0 + a.nIy + ry;
+      wx = k - ry * a.nWx;
     }
   }
 }
@@ -100,7 +110,8 @@ typedef float tab_f4 __attribute__((ext_vector_type(4)));
 // The lane's window coordinates and output origin ride along for the stores.
 struct TabXLoad {
   float v[TKQ];
-  size_t wbase;      // element offset of the window's origin in the map
+  long long wbase;   // element offset of the window's origin in the map (negative above or left
+                     // of a plane's origin on an offset grid: only its in-map pixels are used)
   int wy, wx;        // window row and column
   bool valid;        // a window of the batch (not past the last one)
   bool whole;        // the window lies inside the map
@@ -110,12 +121,13 @@ struct TabXLoad {
     valid = win < nwin_ch;
     int b;
     tab_window(a, valid ? win : 0, b, wy, wx);
-    wbase = ((size_t)b * a.C + c) * a.H * a.W + (size_t)(wy * TW) * a.W + wx * TW;
-    whole = wy * TW + TW <= a.H && wx * TW + TW <= a.W;
-    const int r0 = wy * TW + TQ * (g >> 1), c0 = wx * TW + TQ * (g & 1);
-    const int vo = (int)((((size_t)b * a.C + c) * a.H * a.W + (size_t)r0 * a.W + c0) * 4);
+    const int y0 = wy * TW - a.oy, x0 = wx * TW - a.ox;  // map pixel of the window origin
+    wbase = ((long long)b * a.C + c) * a.H * a.W + (long long)y0 * a.W + x0;
+    whole = y0 >= 0 && x0 >= 0 && y0 + TW <= a.H && x0 + TW <= a.W;
+    const int r0 = y0 + TQ * (g >> 1), c0 = x0 + TQ * (g & 1);
+    const int vo = (int)((wbase + (long long)(TQ * (g >> 1)) * a.W + TQ * (g & 1)) * 4);
     const int rowb = a.W * 4;
-    const bool inside = valid && r0 + TQ <= a.H && c0 + TQ <= a.W;
+    const bool inside = valid && r0 >= 0 && c0 >= 0 && r0 + TQ <= a.H && c0 + TQ <= a.W;
     if (__builtin_amdgcn_ballot_w64(!inside) == 0) {
       // each quadrant row as a 16-byte and a 12-byte load (4-byte aligned)
 #pragma unroll
@@ -137,12 +149,12 @@ struct TabXLoad {
     } else {
       // pixels outside the map get a row or column offset of kTabOob, which puts the sum past
       // the buffer's end: the hardware returns zero, so no select waits on the loads
-      const int nr = valid ? min(TQ, a.H - r0) : 0, nc = valid ? min(TQ, a.W - c0) : 0;
       int rowo[TQ], colo[TQ];
 #pragma unroll
-      for (int r = 0; r < TQ; ++r) rowo[r] = r < nr ? vo + r * rowb : kTabOob;
+      for (int r = 0; r < TQ; ++r)
+        rowo[r] = valid && r0 + r >= 0 && r0 + r < a.H ? vo + r * rowb : kTabOob;
 #pragma unroll
-      for (int q = 0; q < TQ; ++q) colo[q] = q < nc ? q * 4 : kTabOob;
+      for (int q = 0; q < TQ; ++q) colo[q] = c0 + q >= 0 && c0 + q < a.W ? q * 4 : kTabOob;
 #pragma unroll
       for (int s = 0; s < TKQ; ++s)
         v[s] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
@@ -225,8 +237,12 @@ __device__ __forceinline__ void tab_contract(const TabArgs& a, const float* Tw, 
   // at 32-bit offsets; an offset of kTabOob (past the end) drops a store, which covers the
   // padding rows of tile 12 and, in border windows, the pixels outside the map.
   const bool valid = xl.valid, whole = xl.whole;
-  const unsigned ob = (unsigned)xl.wbase * 4u;  // byte offset of the window origin (< 2^31)
-  const int rows = a.H - xl.wy * TW, cols = a.W - xl.wx * TW;  // of this window in the map
+  // byte offset of the window origin, modulo 2^32: the offset of every in-map pixel from it is
+  // exact (the map is < 2^31 bytes)
+  const unsigned ob = (unsigned)(unsigned long long)xl.wbase * 4u;
+  // the window rows [rlo, rhi) and columns [clo, chi) that lie in the map
+  const int y0 = xl.wy * TW - a.oy, x0 = xl.wx * TW - a.ox;
+  const int rlo = -y0, rhi = a.H - y0, clo = -x0, chi = a.W - x0;
   if (!valid) return;
   typedef uint32_t tab_u2 __attribute__((ext_vector_type(2)));
   auto put2 = [&](unsigned off, float v0, float v1) {
@@ -247,24 +263,25 @@ __device__ __forceinline__ void tab_contract(const TabArgs& a, const float* Tw, 
       put2(ob + (unsigned)tl.po[T0 + i], v[0], v[1]);
       put2(ob + (unsigned)tl.po2[T0 + i], v[2], v[3]);
     }
-  } else if ((a.W & 1) == 0) {
-    // a border window of a map of even width: a pixel pair is inside or outside as a whole
+  } else if (((a.W | a.ox) & 1) == 0) {
+    // a border window, map width and column offset even: a pixel pair (even map column first)
+    // is inside or outside as a whole
 #pragma unroll
     for (int i = 0; i < NT; ++i) {
       const int p0 = 16 * (T0 + i) + 4 * g, p2 = p0 + 2;
-      const bool in0 = p0 / TW < rows && p0 % TW < cols;
-      const bool in2 = p2 / TW < rows && p2 % TW < cols;
+      const bool in0 = p0 < TD && p0 / TW >= rlo && p0 / TW < rhi && p0 % TW >= clo && p0 % TW < chi;
+      const bool in2 = p0 < TD && p2 / TW >= rlo && p2 / TW < rhi && p2 % TW >= clo && p2 % TW < chi;
       const v4f v = acc[i];
       put2(in0 ? ob + (unsigned)tl.po[T0 + i] : (unsigned)kTabOob, v[0], v[1]);
       put2(in2 ? ob + (unsigned)tl.po2[T0 + i] : (unsigned)kTabOob, v[2], v[3]);
     }
-  } else {  // a border window of a map of odd width: pixel by pixel, inside the map only
+  } else {  // a border window otherwise: pixel by pixel, inside the map only
 #pragma unroll
     for (int i = 0; i < NT; ++i)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int p = 16 * (T0 + i) + 4 * g + r;
-        const bool in = p < TD && p / TW < rows && p % TW < cols;
+        const bool in = p < TD && p / TW >= rlo && p / TW < rhi && p % TW >= clo && p % TW < chi;
         put1(in ? ob + 4u * (unsigned)((p / TW) * a.W + p % TW) : (unsigned)kTabOob, acc[i][r]);
       }
   }
@@ -373,9 +390,9 @@ int tab_cu_count() {
 }  // namespace
 
 bool fast_tab_forward_ok(const FwdRequest& r) {
-  return !r.in_bf16 && !r.out_bf16 && r.T && !r.M && r.w == TW && r.layout == 0 && r.oy == 0 &&
-         r.ox == 0 && (!r.Tsub || r.s == TQ) && r.B >= 1 && r.C >= 1 &&
-         (long long)r.B * r.C * r.H * r.W * 4 < kTabOob;
+  return !r.in_bf16 && !r.out_bf16 && r.T && !r.M && r.w == TW && r.layout == 0 && r.oy >= 0 &&
+         r.oy < TW && r.ox >= 0 && r.ox < TW && (!r.Tsub || r.s == TQ) && r.B >= 1 && r.C >= 1 &&
+         (long long)r.B * r.C * r.H * r.W * 4 < kTabOob - (1 << 16);
 }
 
 // out: where the contraction's result goes (y, or the pre-mix map); out2: a second copy or null.
@@ -385,10 +402,15 @@ hipError_t launch_forward_fast_tab(const FwdRequest& r, float* out, float* out2,
   a.C = r.C;
   a.H = r.H;
   a.W = r.W;
-  a.nWx = (r.W + TW - 1) / TW;
-  a.nWin = a.nWx * ((r.H + TW - 1) / TW);
-  a.nIx = r.W / TW;
-  a.nIy = r.H / TW;
+  a.oy = r.oy;
+  a.ox = r.ox;
+  a.nWx = (r.W + r.ox + TW - 1) / TW;
+  a.nWy = (r.H + r.oy + TW - 1) / TW;
+  a.nWin = a.nWx * a.nWy;
+  a.ix0 = (r.ox + TW - 1) / TW;  // 1 when the grid is offset, else 0
+  a.iy0 = (r.oy + TW - 1) / TW;
+  a.nIx = std::max(0, (r.W + r.ox) / TW - a.ix0);
+  a.nIy = std::max(0, (r.H + r.oy) / TW - a.iy0);
   a.nIn = a.nIx * a.nIy;
   a.wupc = (int)(((long long)r.B * a.nWin + 15) / 16);
   a.items = (long long)r.C * a.wupc * 3;

@@ -153,11 +153,12 @@ static bool fast_bf16_mix_ok(const FwdRequest& r) {
 }
 
 size_t forward_workspace(const FwdRequest& r) {
-  if (repack_forward_ok(r)) return repack_forward_workspace(r);
-  // cached matrix on the fast path: with the mix, the pre-mix map goes to z_save or here
+  // the fast kernels that leave the mix to a pass of its own: with the mix, the pre-mix map goes
+  // to z_save or here
   if (fast_cm_forward_ok(r) || fast_f32_w28_forward_ok(r) || fast_f32_w7_forward_ok(r) ||
       (!fast_forward_ok(r) && fast_tab_forward_ok(r)))
     return r.mixw && !r.zsave ? (size_t)r.B * r.C * r.H * r.W * 4 : 0;
+  if (repack_forward_ok(r)) return repack_forward_workspace(r);
   if (fast_bf16_mix_ok(r)) return r.zsave ? 0 : (size_t)r.B * r.C * r.H * r.W * 2;
   Geo g;
   if (!plan_fwd(g, r)) return 0;
@@ -180,6 +181,13 @@ hipError_t launch_forward(const FwdRequest& r, hipStream_t st) {
   }
   if (fast_forward_ok(r)) return launch_forward_fast(r, st);  // folds a sub-table when w = 2s
   if (!r.Tsub && fast_bf16_forward_ok(r)) return launch_forward_fast_bf16(r, st);
+  if (fast_tab_forward_ok(r)) {  // fp32 w = 14 from the table, any map and grid offset
+    if (!r.mixw) return launch_forward_fast_tab(r, (float*)r.y, (float*)r.zsave, st);
+    float* z = (float*)(r.zsave ? r.zsave : r.ws);
+    hipError_t e = launch_forward_fast_tab(r, z, nullptr, st);
+    if (e != hipSuccess) return e;
+    return launch_mix_fwd_f32_route(z, r.mixw, (float*)r.y, r.B, r.C, r.H, r.W, st);
+  }
   if (repack_forward_ok(r)) return launch_forward_repacked(r, st);  // offset grid, w = 14
   if (fast_cm_forward_ok(r)) {  // cached matrix, fp32, w = 14: the contraction, then the mix pass
     if (!r.mixw) return launch_forward_fast_cm(r, (float*)r.y, (float*)r.zsave, st);
@@ -188,15 +196,12 @@ hipError_t launch_forward(const FwdRequest& r, hipStream_t st) {
     if (e != hipSuccess) return e;
     return launch_mix_fwd_f32_route(z, r.mixw, (float*)r.y, r.B, r.C, r.H, r.W, st);
   }
-  // fp32: w = 7 or 28 on 56x56 maps, or w = 14 from the table on other maps (the fold on chip):
-  // the contraction, then the mix pass
+  // fp32, w = 7 or 28, 56x56: the contraction, then the mix pass
   const bool f7 = fast_f32_w7_forward_ok(r), f28 = fast_f32_w28_forward_ok(r);
-  const bool ftab = fast_tab_forward_ok(r);
-  if (f7 || f28 || ftab) {
+  if (f7 || f28) {
     auto contract = [&](float* out, float* out2) {
-      return f7    ? launch_forward_fast_f32_w7(r, out, out2, st)
-             : f28 ? launch_forward_fast_f32_w28(r, out, out2, st)
-                   : launch_forward_fast_tab(r, out, out2, st);
+      return f7 ? launch_forward_fast_f32_w7(r, out, out2, st)
+                : launch_forward_fast_f32_w28(r, out, out2, st);
     };
     if (!r.mixw) return contract((float*)r.y, (float*)r.zsave);
     float* z = (float*)(r.zsave ? r.zsave : r.ws);

@@ -239,16 +239,18 @@ def test_shifted_validation(lib):
 
 
 def test_shifted_workspace_covers_the_repacked_maps(lib):
-    """w = 14 offset grids on NCHW fp32 maps run on whole 28x28 images of 2x2 windows: B=64 at
-    28x28 with offset (7, 7) has 9 windows per image, 576 windows = 144 repacked images. The
-    forward holds repacked X and z (and the image-space z without a z_save buffer, with the mix);
-    the backward repacked G, X and dX, and with the mix the image-space G."""
+    """w = 14 offset grids on NCHW maps: B=64 at 28x28 with offset (7, 7) has 9 windows per image,
+    576 windows = 144 repacked 28x28 images of 2x2 windows. The fp32 forward reads the offset
+    grid directly (with the mix and no z_save buffer it needs the image-space z); the bf16 forward
+    without the mix runs on repacked X and z (bf16: together the bytes of one fp32 repacked map);
+    the backward holds repacked G, X and dX, and with the mix the image-space G."""
     B, C = 64, 192
     rep = 144 * C * 28 * 28 * 4
     img = B * C * 28 * 28 * 4
     fwd = lib.wbmm_forward_shifted_workspace_bytes(B, C, 28, 28, 14, 7, 7, 0, 0, 0)
-    assert fwd >= 2 * rep
-    assert lib.wbmm_forward_shifted_workspace_bytes(B, C, 28, 28, 14, 7, 7, 0, 1, 0) >= fwd + img
+    assert fwd >= rep
+    assert lib.wbmm_forward_shifted_workspace_bytes(B, C, 28, 28, 14, 7, 7, 0, 1, 0) >= img
+    assert lib.wbmm_forward_shifted_workspace_bytes(B, C, 28, 28, 14, 7, 7, 0, 1, 1) < img
     bwd = lib.wbmm_backward_shifted_workspace_bytes(B, C, 28, 28, 14, 7, 7, 0, 0)
     assert bwd >= 3 * rep
     assert lib.wbmm_backward_shifted_workspace_bytes(B, C, 28, 28, 14, 7, 7, 0, 1) >= bwd + img

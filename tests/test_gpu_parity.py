@@ -908,7 +908,37 @@ def test_dwconv_full_size_sampled():
 # B = 5 at 28x28 leaves 45 windows: 12 repacked images, the last with 3 zero windows
 SHIFT_CASES = [(2, 3, 28, 28, 14, 7, 7), (1, 2, 30, 25, 14, 3, 11), (2, 3, 17, 13, 4, 2, 1),
                (1, 2, 128, 128, 14, 7, 7), (2, 2, 9, 9, 7, 0, 3), (5, 4, 28, 28, 14, 7, 7),
-               (3, 2, 5, 40, 14, 13, 0), (1, 2, 40, 40, 20, 10, 10)]
+               (3, 2, 5, 40, 14, 13, 0), (1, 2, 40, 40, 20, 10, 10), (2, 3, 42, 36, 14, 6, 4),
+               (1, 2, 14, 14, 14, 1, 13)]
+
+
+def _window_shift_grid(x, w, oy, ox, dy, dx):
+    """_window_shift on the offset grid: the map placed at (oy, ox) in a zero canvas of whole
+    windows, shifted inside each window, cropped back."""
+    B, C, H, W = x.shape
+    Hp, Wp = -(-(H + oy) // w) * w, -(-(W + ox) // w) * w
+    xp = np.zeros((B, C, Hp, Wp), x.dtype)
+    xp[:, :, oy:oy + H, ox:ox + W] = x
+    return _window_shift(xp, w, dy, dx)[:, :, oy:oy + H, ox:ox + W]
+
+
+@pytest.mark.parametrize("B,C,H,W,oy,ox", [(4, 300, 28, 28, 7, 7), (3, 129, 30, 44, 5, 9),
+                                           (2, 130, 40, 36, 6, 4), (1, 260, 17, 13, 13, 0),
+                                           (2, 140, 128, 128, 7, 7)])
+def test_forward_shifted_tab_bitwise_all_channels(B, C, H, W, oy, ox):
+    """One-hot tables at a different offset in every channel on an offset window grid: the fp32
+    w = 14 table kernel's output is the input shifted inside each window of that grid, bit for
+    bit, in every channel (whole and border windows, even and odd column offsets)."""
+    w = 14
+    say(f"forward shifted table shift all channels B={B} C={C} H={H} W={W} o=({oy},{ox})")
+    x = synth.normal_f32((B, C, H, W), 1.0, seed=41)
+    L1 = 2 * w - 1
+    dy = (np.arange(C) * 5 + 3) % L1 - (w - 1)
+    dx = (np.arange(C) * 11 + 2) % L1 - (w - 1)
+    T = np.zeros((C, L1, L1), np.float32)
+    T[np.arange(C), dy + w - 1, dx + w - 1] = 1.0
+    want = _window_shift_grid(x, w, oy, ox, dy, dx)
+    assert np.array_equal(host(R().wbmm_forward_shifted(dev(x), w, oy, ox, T=dev(T))), want)
 
 
 @pytest.mark.parametrize("B,C,H,W,w,oy,ox", SHIFT_CASES)
