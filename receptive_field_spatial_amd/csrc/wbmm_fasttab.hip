@@ -12,10 +12,10 @@
 // the chip's SIMDs get equal shares even when a map has few wave-units per SIMD. Per item:
 //   * B operand (window pixels) straight from HBM into registers: lane (n, g) holds the 49 pixels
 //     of quadrant g of window n, kept while a wave's items stay in one wave-unit; the other wave
-//     of the SIMD computes while they load. Windows are listed whole ones first, so that most
-//     wave-units read each quadrant row as a 16-byte and a 12-byte load; wave-units with partial
-//     windows read pixel by pixel, those outside the map at an offset past the end of the
-//     buffer, which the hardware answers with zero;
+//     of the SIMD computes while they load. Windows are listed whole ones first; quadrant rows
+//     are read as a 16-byte and a 12-byte load, rows outside the map at an offset past the end
+//     of the buffer, which the hardware answers with zero; wave-units with a quadrant cut by
+//     the map's edge in columns read pixel by pixel;
 //   * A operand M_c[m][k] for K step s of quadrant g: one LDS read of the (folded) reversed table at
 //     the tile's lane base plus 27 (s / 7) + s % 7, two steps ahead of their MFMAs;
 //   * v_mfma_f32_16x16x4f32, the third's tiles as independent chains over 49 K steps;
@@ -127,12 +127,18 @@ struct TabXLoad {
     const int r0 = y0 + TQ * (g >> 1), c0 = x0 + TQ * (g & 1);
     const int vo = (int)((wbase + (long long)(TQ * (g >> 1)) * a.W + TQ * (g & 1)) * 4);
     const int rowb = a.W * 4;
-    const bool inside = valid && r0 >= 0 && c0 >= 0 && r0 + TQ <= a.H && c0 + TQ <= a.W;
-    if (__builtin_amdgcn_ballot_w64(!inside) == 0) {
-      // each quadrant row as a 16-byte and a 12-byte load (4-byte aligned)
+    // A quadrant whose columns lie all inside or all outside the map reads its rows as a
+    // 16-byte and a 12-byte load (4-byte aligned); rows outside the map, and every row of a
+    // quadrant outside in columns, take an offset past the end of the buffer and read zeros.
+    // (Quadrants of an offset grid are of this kind when the column offset is 0 or 7; a map
+    // whose width is no multiple of 7 has quadrants cut by its right edge.)
+    const bool cols_in = c0 >= 0 && c0 + TQ <= a.W, cols_out = c0 + TQ <= 0 || c0 >= a.W;
+    const bool cut = valid && !cols_in && !cols_out;
+    if (__builtin_amdgcn_ballot_w64(cut) == 0) {
 #pragma unroll
       for (int r = 0; r < TQ; ++r) {
-        const int ro = vo + r * rowb;
+        const bool rok = valid && cols_in && r0 + r >= 0 && r0 + r < a.H;
+        const int ro = rok ? vo + r * rowb : kTabOob;
         // (the loads' integer vectors are cast whole: this compiler narrows a component read of
         // them to a one-dword load)
         const tab_f4 p = __builtin_bit_cast(tab_f4, __builtin_amdgcn_raw_buffer_load_b128(xr, ro, 0, 0));
@@ -147,8 +153,9 @@ struct TabXLoad {
         v[TQ * r + 6] = q.z;
       }
     } else {
-      // pixels outside the map get a row or column offset of kTabOob, which puts the sum past
-      // the buffer's end: the hardware returns zero, so no select waits on the loads
+      // pixel by pixel: pixels outside the map get a row or column offset of kTabOob, which
+      // puts the sum past the buffer's end: the hardware returns zero, so no select waits on
+      // the loads
       int rowo[TQ], colo[TQ];
 #pragma unroll
       for (int r = 0; r < TQ; ++r)
