@@ -3,7 +3,8 @@
 // memory on every call [gecl.asia reading notes, "Method", last sentence; "Limitation" names
 // materializing M as the memory cost of the method].
 //
-// One persistent workgroup of 8 waves per CU. The workgroup holds one channel's whole matrix in
+// One persistent workgroup of 8 waves per CU (two per SIMD: one wave's loads and stores overlap
+// the other's matrix work). The workgroup holds one channel's whole matrix in
 // LDS (196 rows at a pitch of 202 floats = 154.7 KB); each wave contracts a "wave-unit" of 16
 // consecutive windows of that channel at a time (windows of a channel are numbered image by
 // image, row-major), so the window pixels never pass through LDS:
@@ -11,13 +12,14 @@
 //     of quadrant g of window n, the next wave-unit's pixels in flight during the contraction;
 //     the loads address x as one raw buffer (a 32-bit per-lane offset, the window row as a
 //     uniform offset, the column as an immediate); pixels outside the map (the zero padding of
-//     a map whose sides are not multiples of 14) read as zero;
+//     a map whose sides are not multiples of 14) are read at an offset past the end of the
+//     buffer, which the hardware answers with zero;
 //   * A operand (M_c[i][j]) from LDS, quadrant-major within each row (quadrant g's 49 columns at
 //     offset 50 g), so two consecutive K-steps of a lane are one 8-byte read;
 //   * v_mfma_f32_16x16x4f32: 13 row tiles x 49 K-steps per wave-unit;
 //   * outputs stored from the accumulators (reverse + crop fused), to y or, with the 3x3 mix,
 //     to the pre-mix map that a mix pass then reads.
-// A workgroup walks a contiguous range of the (channel, wave-unit) list in rounds of 4
+// A workgroup walks a contiguous range of the (channel, wave-unit) list in rounds of 8
 // wave-units of one channel; the matrix is restaged when the channel changes. With few channels
 // of many wave-units each, every channel is split into equal parts instead, one workgroup (and one
 // matrix staging) per part.
@@ -30,13 +32,16 @@
 namespace wbmm {
 namespace {
 
-constexpr int kCmWaves = 4;
+constexpr int kCmWaves = 8;  // two waves per SIMD
 constexpr int kCmThreads = kCmWaves * 64;
 constexpr int CW = 14, CD = CW * CW, CRT = (CD + 15) / 16;  // window, pixels, row tiles
 constexpr int CQ = 7, CKQ = CQ * CQ;                        // quadrant side, K-steps
 constexpr int SEGP = 50;                                    // LDS floats per quadrant segment
 constexpr int MP = 4 * SEGP + 2;                            // LDS row pitch (floats)
 constexpr int kCmLds = CD * MP * 4;  // the matrix
+// An offset at or past the end of x (the host takes this path below kCmOob - 2^16 bytes); two of
+// them still sum below 2^32.
+constexpr int kCmOob = 0x7fff0000;
 static_assert(kCmLds <= 160 * 1024, "one channel's matrix fits in LDS");
 
 struct CmArgs {
@@ -86,16 +91,19 @@ struct XLoad {
         v[s] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
                                              xr, vo + (s % 7) * 4, (s / 7) * rowb, 0));
     } else {
-      // rows / columns of the quadrant inside the map; out-of-map pixels read the tensor's
-      // first element and are replaced by zero
+      // rows / columns of the quadrant inside the map; out-of-map pixels take a row or column
+      // offset of kCmOob, which puts the sum past the buffer's end: the hardware returns zero,
+      // so no select waits on the loads
       const int nr = valid ? min(7, a.H - r0) : 0, nc = valid ? min(7, a.W - c0) : 0;
+      int rowo[7], colo[7];
 #pragma unroll
-      for (int s = 0; s < CKQ; ++s) {
-        const bool ok = s / 7 < nr && s % 7 < nc;
-        const float t = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
-            xr, ok ? vo + (s / 7) * rowb + (s % 7) * 4 : 0, 0, 0));
-        v[s] = ok ? t : 0.f;
-      }
+      for (int r = 0; r < 7; ++r) rowo[r] = r < nr ? vo + r * rowb : kCmOob;
+#pragma unroll
+      for (int q = 0; q < 7; ++q) colo[q] = q < nc ? q * 4 : kCmOob;
+#pragma unroll
+      for (int s = 0; s < CKQ; ++s)
+        v[s] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
+                                             xr, rowo[s / 7] + colo[s % 7], 0, 0));
     }
   }
 };
@@ -162,8 +170,6 @@ __global__ void __launch_bounds__(kCmThreads) k_fwd_cm(CmArgs a) {
     hi = a.total * (rg + 1) / G;
   }
 
-  // A operand base of this lane: row m of tile 0, quadrant g's segment
-  const float* abase = Ms + n * MP + g * SEGP;
 
   // A round is up to 8 consecutive wave-units of one channel, one per wave (waves past its end
   // idle); every wave walks the same rounds, so the barriers around a restage match.
@@ -200,6 +206,12 @@ __global__ void __launch_bounds__(kCmThreads) k_fwd_cm(CmArgs a) {
     XLoad nxt;
     issue(nxt, nr0, nrend);
     if (mine) {
+      // the lane's coordinates pass through an empty asm, so that the per-tile values derived
+      // from them are formed per wave-unit instead of being held across the loop
+      int ln = lane;
+      asm volatile("" : "+v"(ln));
+      const int n = ln & 15, g = ln >> 4;
+      const float* abase = Ms + n * MP + g * SEGP;
       v4f acc[CRT];
 #pragma unroll
       for (int t = 0; t < CRT; ++t) acc[t] = v4f{0.f, 0.f, 0.f, 0.f};
@@ -309,7 +321,7 @@ int cm_cu_count() {
 
 bool fast_cm_forward_ok(const FwdRequest& r) {
   return !r.in_bf16 && !r.out_bf16 && r.M && !r.T && !r.Tsub && r.w == CW && r.layout == 0 &&
-         r.oy == 0 && r.ox == 0 && (long long)r.B * r.C * r.H * r.W * 4 < (1LL << 31);
+         r.oy == 0 && r.ox == 0 && (long long)r.B * r.C * r.H * r.W * 4 < kCmOob - (1 << 16);
 }
 
 // out: where the contraction's result goes (y, or the pre-mix map); out2: a second copy or null.
