@@ -196,14 +196,16 @@ size_t wbmm_forward_hier_workspace_bytes(int B, int C, int H, int W, int w, int 
  * 14x14 window at no inference cost]. The matrix is
  *   M'_c[i][j] = M_c[i][j] + T_sub[c][idx_s(i, j)]   for pairs i, j in one s x s sub-window,
  *   M'_c[i][j] = M_c[i][j]                           otherwise,
- * each sum one fp32 add (RNE): exactly what wbmm_fold_hier stores, but M' is never formed in
- * memory. Then z and y as in wbmm_forward. fp32 only; this build folds on chip for w = 2s
- * (other s | w: wbmm_fold_hier + wbmm_forward with the cached matrix).
+ * each sum one fp32 add (RNE): exactly what wbmm_fold_hier stores. Then z and y as in
+ * wbmm_forward. fp32 only; s divides w and s < w. For w = 2s (the sub-windows are the window's
+ * quadrants) the fold happens on chip and M' is never formed in memory; for other s, M' is
+ * built and folded in the workspace (C w^4 floats) and read as a cached matrix.
  * x, y, z_save: device fp32 maps in `layout`; T: device fp32 [C][2w-1][2w-1];
  * T_sub: device fp32 [C][2s-1][2s-1]; mix_w, z_save, workspace as in wbmm_forward
  * (workspace size from wbmm_forward_hier_workspace_bytes).
- * Errors: WBMM_E_INVALID (sizes, NULL or overlapping pointers), WBMM_E_UNSUPPORTED (w != 2s,
- *         misaligned pointer), WBMM_E_WORKSPACE, WBMM_E_HIP.
+ * Errors: WBMM_E_INVALID (sizes, s not dividing w or not below it, NULL or overlapping
+ *         pointers), WBMM_E_UNSUPPORTED (no launch shape, misaligned pointer), WBMM_E_WORKSPACE,
+ *         WBMM_E_HIP.
  */
 wbmm_status wbmm_forward_hier(int B, int C, int H, int W, int w, int s, int layout, const float* x,
                               const float* T, const float* T_sub, const float* mix_w,
@@ -226,9 +228,12 @@ size_t wbmm_backward_hier_workspace_bytes(int B, int C, int H, int W, int w, int
  * T, T_sub: as in wbmm_forward_hier. dx, dT, dT_sub, dmix_w: written, or NULL to skip
  * (dT_sub: device fp32 [C][2s-1][2s-1]). mix_w, z_saved, dy, workspace as in wbmm_backward.
  * dT, dT_sub and dmix_w are reduced in a fixed order: bitwise reproducible run to run.
- * This build provides it for w = 2s <= 16.
- * Errors: WBMM_E_INVALID, WBMM_E_UNSUPPORTED (w != 2s, w > 16, misaligned pointer),
- *         WBMM_E_WORKSPACE, WBMM_E_HIP.
+ * Any s dividing w with s < w, 1 <= w <= 32: for w = 2s on chip; for other s with M' built in
+ * the workspace, dX and dT from the cached-matrix backward, and dT_sub as the table gradient of
+ * an s-window layer on the same G and x (a pair of one sub-window is a pair of one window of
+ * the s-grid, which the w-grid subdivides).
+ * Errors: WBMM_E_INVALID (as wbmm_forward_hier), WBMM_E_UNSUPPORTED (no launch shape,
+ *         misaligned pointer), WBMM_E_WORKSPACE, WBMM_E_HIP.
  */
 wbmm_status wbmm_backward_hier(int B, int C, int H, int W, int w, int s, int layout,
                                const float* x, const float* T, const float* T_sub,

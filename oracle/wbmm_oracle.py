@@ -16,7 +16,7 @@ What it computes (WBMM, "Windowed Batch Matrix Multiplication"):
     cross-window flow, an optional 7x7 sub-table is folded into a 14x14 window's matrix, and M
     may be cached for inference [gecl.asia reading notes, "Method" points 3-4 and last sentence].
 
-Readings taken where the pages leave a step open (each is listed in the design doc):
+Readings taken where the pages leave a step open:
   R1 offset orientation: M[i,j] = T[(y_i - y_j) + w - 1, (x_i - x_j) + w - 1], first table axis
      vertical; R2 in-window order i = y*w + x, windows ordered (b, wy, wx) row-major;
   R3 H, W not multiples of w are zero-padded at the bottom/right and the output is cropped;

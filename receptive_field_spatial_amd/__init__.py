@@ -331,7 +331,8 @@ def wbmm_forward_hier_workspace_bytes(B, C, H, W, w, s, layout="NCHW", has_mix=F
 def wbmm_forward_hier(x, w: int, s: int, T, T_sub, mix_w=None, *, layout: str = "NCHW", y=None,
                       z_save=None, workspace=None, stream=None):
     """Layer forward (fp32) with the s x s sub-window tables T_sub (C, 2s-1, 2s-1) folded into
-    the matrix on chip. Returns y (and z_save, when given, holds the pre-mix output)."""
+    the matrix (s divides w and s < w; on chip for the quadrants, w = 2s <= 16, otherwise into a
+    matrix in the workspace). Returns y (and z_save, when given, holds the pre-mix output)."""
     torch = _torch()
     B, C, H, W = _bchw(x, layout)
     if y is None:

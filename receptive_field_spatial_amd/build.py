@@ -17,12 +17,13 @@ LIB_PATH = os.path.join(PKG_DIR, "libwbmm.so")
 SOURCES = ["wbmm_api.cpp", "wbmm_aux.hip", "wbmm_fwd.hip", "wbmm_bwd.hip", "wbmm_fast.hip",
            "wbmm_fastbf.hip", "wbmm_dw.hip",
            "wbmm_probe.hip", "wbmm_bwdbf.hip", "wbmm_repack.hip", "wbmm_fastcm.hip",
-           "wbmm_fast28.hip", "wbmm_fast7.hip", "wbmm_fasttab.hip",
+           "wbmm_fast28.hip", "wbmm_fast7.hip", "wbmm_fasttab.hip", "wbmm_hiergen.cpp",
            "wbmm_bwdwide.hip"]
 
 ARCH = "gfx950"
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
-# Packed-fp32 VALU ops are disabled for every device compile ("Build").
+# Packed-fp32 VALU ops (v_pk_fma_f32 and kin) are disabled for every device compile: the code
+# keeps to scalar fp32 vector instructions, which the kernels were validated with.
 DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
 COMMON = ["-O3", "-fPIC", "-std=c++17", "-fvisibility=hidden", f"--offload-arch={ARCH}",
           "-Wall", "-Wno-unused-function", "-Wno-unused-variable", "-Wno-pass-failed"]

@@ -414,13 +414,13 @@ WBMM_API wbmm_status wbmm_backward_shifted(int B, int C, int H, int W, int w, in
                        workspace, workspace_bytes, stream, "wbmm_backward_shifted");
 }
 namespace {
-// Shared checks of the hierarchical entry points: fp32 table path with the s x s sub-window
-// tables folded on chip, which this build provides for w = 2s.
+// Shared checks of the hierarchical entry points: fp32 tables, s x s sub-windows tiling the
+// w x w window (s divides w, s < w).
+bool hier_sizes_ok(int w, int s) { return s >= 1 && s < w && w % s == 0; }
 wbmm_status check_hier(int w, int s, const float* T, const float* T_sub) {
-  if (s < 1 || 2 * s != w)
-    return fail(WBMM_E_UNSUPPORTED,
-                "the on-chip fold is provided for w = 2s (w=%d, s=%d); fold other sub-windows "
-                "with wbmm_fold_hier and pass the cached matrix", w, s);
+  if (!hier_sizes_ok(w, s))
+    return fail(WBMM_E_INVALID, "the sub-window side must divide the window side and be smaller "
+                "(w=%d, s=%d)", w, s);
   if (!T || !T_sub) return fail(WBMM_E_INVALID, "T and T_sub must be non-NULL");
   if (!aligned(T, 4) || !aligned(T_sub, 4)) return fail(WBMM_E_UNSUPPORTED, "misaligned pointer");
   return WBMM_OK;
@@ -428,7 +428,7 @@ wbmm_status check_hier(int w, int s, const float* T, const float* T_sub) {
 }  // namespace
 WBMM_API size_t wbmm_forward_hier_workspace_bytes(int B, int C, int H, int W, int w, int s,
                                                   int layout, int has_mix, int has_z_save) {
-  if (check_map(B, C, H, W, w, layout) != WBMM_OK || s < 1 || 2 * s != w) return 0;
+  if (check_map(B, C, H, W, w, layout) != WBMM_OK || !hier_sizes_ok(w, s)) return 0;
   static const float dummy = 0.f;
   wbmm::FwdRequest r = make_fwd(B, C, H, W, w, layout, WBMM_F32, WBMM_F32, &dummy, &dummy, nullptr,
                                 has_mix ? &dummy : nullptr, has_z_save ? (void*)&dummy : nullptr,
@@ -465,7 +465,7 @@ WBMM_API wbmm_status wbmm_forward_hier(int B, int C, int H, int W, int w, int s,
 }
 WBMM_API size_t wbmm_backward_hier_workspace_bytes(int B, int C, int H, int W, int w, int s,
                                                    int layout, int has_mix) {
-  if (check_map(B, C, H, W, w, layout) != WBMM_OK || w > 16 || s < 1 || 2 * s != w) return 0;
+  if (check_map(B, C, H, W, w, layout) != WBMM_OK || !hier_sizes_ok(w, s)) return 0;
   static const float dummy = 0.f;
   wbmm::BwdRequest r = make_bwd(B, C, H, W, w, layout, &dummy, &dummy, nullptr,
                                 has_mix ? &dummy : nullptr, has_mix ? &dummy : nullptr, &dummy,
@@ -482,7 +482,6 @@ WBMM_API wbmm_status wbmm_backward_hier(int B, int C, int H, int W, int w, int s
                                         void* workspace, size_t workspace_bytes, void* stream) {
   wbmm_status st = check_map(B, C, H, W, w, layout);
   if (st != WBMM_OK) return st;
-  if (w > 16) return fail(WBMM_E_UNSUPPORTED, "the backward is provided for w <= 16 (w=%d)", w);
   st = check_hier(w, s, T, T_sub);
   if (st != WBMM_OK) return st;
   if (!x || !dy) return fail(WBMM_E_INVALID, "x and dy must be non-NULL");

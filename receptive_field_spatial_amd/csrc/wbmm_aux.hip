@@ -51,8 +51,9 @@ __global__ void __launch_bounds__(kThreads) k_build_matrix(const E* __restrict__
 // Hierarchical fold: same-sub-window pairs get one added table entry (fp32 add, RNE; for bf16 the
 // two bf16 values are added in fp32 and the sum is rounded to bf16)
 // [gecl.asia reading notes, "Method" point 4].
+// Min may be Mout (each element is read, then written, by one thread).
 template <typename E>
-__global__ void __launch_bounds__(kThreads) k_fold(const E* __restrict__ Min,
+__global__ void __launch_bounds__(kThreads) k_fold(const E* Min,
                                                    const E* __restrict__ Ts, int C, int w, int s,
                                                    FastDiv fd_d, FastDiv fd_w, FastDiv fd_s,
                                                    E* Mout) {

@@ -346,12 +346,14 @@ BwdWs bwd_ws_layout(const Geo& g, const BwdRequest& r) {
 }  // namespace
 
 bool backward_plan_ok(const BwdRequest& r) {
+  if (hier_general(r)) return hier_backward_plan_ok(r);
   if (wide_backward_ok(r)) return true;
   Geo g;
   return plan_bwd(g, r);
 }
 
 size_t backward_workspace(const BwdRequest& r) {
+  if (hier_general(r)) return hier_backward_workspace(r);
   if (wide_backward_ok(r)) return backward_wide_workspace(r, sizeof(float));
   Geo g;
   if (!plan_bwd(g, r)) return 0;
@@ -439,6 +441,7 @@ static hipError_t launch_backward_general(const BwdRequest& r, hipStream_t st) {
 }
 
 hipError_t launch_backward(const BwdRequest& r, hipStream_t st) {
+  if (hier_general(r)) return launch_backward_hier_general(r, st);  // s | w, w != 2s
   if (wide_backward_ok(r)) return launch_backward_wide(r, false, st);  // 16 < w <= 32
   if (fast_backward_ok(r)) return launch_backward_fast(r, st);  // folds a sub-table when w = 2s
   if (repack_backward_ok(r)) return launch_backward_repacked(r, st);  // offset grid, w = 14

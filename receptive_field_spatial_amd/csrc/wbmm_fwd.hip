@@ -138,6 +138,7 @@ static bool plan_fwd(Geo& g, const FwdRequest& r) {
 }
 
 bool forward_plan_ok(const FwdRequest& r) {
+  if (hier_general(r)) return hier_forward_plan_ok(r);
   Geo g;
   return plan_fwd(g, r);
 }
@@ -153,6 +154,7 @@ static bool fast_bf16_mix_ok(const FwdRequest& r) {
 }
 
 size_t forward_workspace(const FwdRequest& r) {
+  if (hier_general(r)) return hier_forward_workspace(r);
   // the fast kernels that leave the mix to a pass of its own: with the mix, the pre-mix map goes
   // to z_save or here
   if (fast_cm_forward_ok(r) || fast_f32_w28_forward_ok(r) || fast_f32_w7_forward_ok(r) ||
@@ -169,6 +171,7 @@ size_t forward_workspace(const FwdRequest& r) {
 }
 
 hipError_t launch_forward(const FwdRequest& r, hipStream_t st) {
+  if (hier_general(r)) return launch_forward_hier_general(r, st);  // s | w, w != 2s
   if (r.flip) {  // Z = M^T X on the general kernel (fp32 cached matrix, no mix)
     FwdArgs a{};
     if (!r.M || r.T || r.in_bf16 || r.out_bf16 || r.mixw || r.Tsub || !plan_fwd(a.g, r))

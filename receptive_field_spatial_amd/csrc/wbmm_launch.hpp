@@ -53,6 +53,17 @@ hipError_t launch_fold(const void* Min, const void* Tsub, int C, int w, int s, i
 bool forward_plan_ok(const FwdRequest& r);
 size_t forward_workspace(const FwdRequest& r);
 hipError_t launch_forward(const FwdRequest& r, hipStream_t st);
+// The hierarchical layer for sub-windows other than the quadrants, or w = 2s > 16 (Tsub set,
+// s | w, s < w): the folded matrix built in the workspace, then the cached-matrix kernels (and for
+// the backward the s-window table gradient as dT_sub).
+bool hier_general(const FwdRequest& r);
+bool hier_general(const BwdRequest& r);
+bool hier_forward_plan_ok(const FwdRequest& r);
+size_t hier_forward_workspace(const FwdRequest& r);
+hipError_t launch_forward_hier_general(const FwdRequest& r, hipStream_t st);
+bool hier_backward_plan_ok(const BwdRequest& r);
+size_t hier_backward_workspace(const BwdRequest& r);
+hipError_t launch_backward_hier_general(const BwdRequest& r, hipStream_t st);
 // Backward for 16 < w <= 32 (fp32 or bf16 maps: map_bytes 4 or 2; the request's map and table
 // pointers point at data of that type).
 bool wide_backward_ok(const BwdRequest& r);

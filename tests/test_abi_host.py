@@ -191,19 +191,26 @@ def hier_bwd(lib, **kw):
 
 
 def test_hier_validation(lib):
-    """The on-chip fold entry points: w = 2s only, both tables required, fp32 maps checked like
-    the plain calls, workspace sizes reported and enforced."""
-    for w, s in [(14, 2), (12, 4), (14, 14), (14, 0)]:
-        assert hier_fwd(lib, w=w, s=s) == R.WBMM_E_UNSUPPORTED, (w, s)
-        assert hier_bwd(lib, w=w, s=s) == R.WBMM_E_UNSUPPORTED, (w, s)
+    """The hierarchical entry points: s divides w and s < w, both tables required, fp32 maps
+    checked like the plain calls, workspace sizes reported and enforced. Sub-windows other than
+    the quadrants (and w = 2s above 16) need the folded matrix in the workspace: C w^4 floats
+    at least."""
+    for w, s in [(14, 14), (14, 0), (14, 5), (12, 13), (14, -7)]:
+        assert hier_fwd(lib, w=w, s=s) == R.WBMM_E_INVALID, (w, s)
+        assert hier_bwd(lib, w=w, s=s) == R.WBMM_E_INVALID, (w, s)
         assert lib.wbmm_forward_hier_workspace_bytes(1, 2, 28, 28, w, s, 0, 1, 0) == 0
         assert lib.wbmm_backward_hier_workspace_bytes(1, 2, 28, 28, w, s, 0, 0) == 0
-    assert "w = 2s" in err(lib)
+    assert "divide" in err(lib)
+    for w, s in [(14, 2), (12, 4), (12, 3), (18, 9), (28, 7)]:
+        folded = 2 * w ** 4 * 4
+        assert lib.wbmm_forward_hier_workspace_bytes(1, 2, 28, 28, w, s, 0, 0, 0) >= folded, (w, s)
+        assert lib.wbmm_backward_hier_workspace_bytes(1, 2, 28, 28, w, s, 0, 1) >= folded, (w, s)
+        assert hier_fwd(lib, w=w, s=s) == R.WBMM_E_WORKSPACE, (w, s)
+        assert hier_bwd(lib, w=w, s=s) == R.WBMM_E_WORKSPACE, (w, s)
     assert hier_fwd(lib, Ts=None) == R.WBMM_E_INVALID
     assert hier_fwd(lib, T=None) == R.WBMM_E_INVALID
     assert hier_fwd(lib, y=FAKE) == R.WBMM_E_INVALID             # y aliases x
     assert hier_fwd(lib, y=0x300000) == R.WBMM_E_INVALID         # y overlaps T_sub
-    assert hier_bwd(lib, w=18, s=9) == R.WBMM_E_UNSUPPORTED       # backward w <= 16
     assert hier_bwd(lib, Ts=None) == R.WBMM_E_INVALID
     assert hier_bwd(lib, mix=0x900000) == R.WBMM_E_INVALID       # mix without z_saved
     assert hier_bwd(lib, dTs=0x300000) == R.WBMM_E_INVALID       # dT_sub aliases T_sub

@@ -206,6 +206,53 @@ def test_guard_hier(B, C, H, mix):
     assert_f32(host(dTs.t), wdTs, "dT_sub")
 
 
+@pytest.mark.parametrize("B,C,H,W,w,s", [(2, 3, 24, 24, 12, 4), (1, 2, 26, 20, 12, 3),
+                                         (1, 2, 36, 36, 18, 9)])
+@pytest.mark.parametrize("mix", [False, True])
+def test_guard_hier_general(B, C, H, W, w, s, mix):
+    """The fold for s other than w / 2 (and w = 2s above 16) goes through a folded matrix in the
+    workspace: y, z_save, both workspaces, dx, dT, dT_sub and dWmix guarded."""
+    say(f"guard hier general B={B} C={C} H={H} W={W} w={w} s={s} mix={mix}")
+    L1, Ls = 2 * w - 1, 2 * s - 1
+    x = synth.normal_f32((B, C, H, W), 1.0, seed=420)
+    T = synth.normal_f32((C, L1, L1), 0.02, seed=421)
+    Ts = synth.normal_f32((C, Ls, Ls), 0.02, seed=422)
+    Wm = synth.normal_f32((C, 3, 3), 0.1, seed=423) if mix else None
+    dy = synth.normal_f32((B, C, H, W), 1.0, seed=424)
+    xd, Td, Tsd, dyd = dev(x), dev(T), dev(Ts), dev(dy)
+    Wd = dev(Wm) if mix else None
+    y, z = Guarded(x.shape), Guarded(x.shape)
+    wsf = guarded_ws(R().wbmm_forward_hier_workspace_bytes(B, C, H, W, w, s, has_mix=mix,
+                                                            has_z_save=True))
+    assert wsf is not None
+    R().wbmm_forward_hier(xd, w, s, Td, Tsd, mix_w=Wd, y=y.t, z_save=z.t, workspace=wsf.t)
+    y.check("y")
+    z.check("z_save")
+    wsf.check("forward workspace")
+    dx, dT, dTs = Guarded(x.shape), Guarded((C, L1, L1)), Guarded((C, Ls, Ls))
+    dW = Guarded((C, 3, 3)) if mix else None
+    wsb = guarded_ws(R().wbmm_backward_hier_workspace_bytes(B, C, H, W, w, s, has_mix=mix))
+    assert wsb is not None
+    R().wbmm_backward_hier(xd, dyd, w, s, Td, Tsd, mix_w=Wd, z_saved=z.t if mix else None,
+                           dx=dx.t, dT=dT.t, dT_sub=dTs.t, dmix_w=dW.t if mix else False,
+                           workspace=wsb.t)
+    for g, n in ((dx, "dx"), (dT, "dT"), (dTs, "dT_sub")):
+        g.check(n)
+    if mix:
+        dW.check("dWmix")
+    wsb.check("backward workspace")
+    wy, _ = O.layer_forward_hier(x.astype(np.float64), w, s, T, Ts, Wmix=Wm)
+    assert_f32(host(y.t), wy, "y")
+    wdx, wdT, wdTs, wdW = O.layer_backward_hier(x.astype(np.float64), dy.astype(np.float64), w, s,
+                                                T, Ts, Wmix=Wm,
+                                                z=host(z.t).astype(np.float64) if mix else None)
+    assert_f32(host(dx.t), wdx, "dx")
+    assert_f32(host(dT.t), wdT, "dT")
+    assert_f32(host(dTs.t), wdTs, "dT_sub")
+    if mix:
+        assert_f32(host(dW.t), wdW, "dWmix")
+
+
 @pytest.mark.parametrize("w,hw,B", [(14, 28, 5), (14, 56, 3), (7, 56, 5), (28, 56, 3),
                                     (28, 56, 21), (14, 14, 3)])
 @pytest.mark.parametrize("mix", [False, True])

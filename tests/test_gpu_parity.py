@@ -780,6 +780,105 @@ def test_backward_hier_partial_outputs():
     assert_f32(host(dx), wdx, "dx")
 
 
+# Sub-windows other than the quadrants (s | w, w != 2s) and w = 2s above 16: M' is folded in the
+# workspace and the cached-matrix kernels run on it; dT_sub is the table gradient of an s-window
+# layer on the same map gradient.
+HIER_GENERAL = [(2, 3, 24, 24, 12, 4, "NCHW"), (1, 2, 26, 20, 12, 3, "NCHW"),
+                (2, 2, 28, 28, 14, 2, "NCHW"), (1, 2, 33, 30, 16, 4, "NHWC"),
+                (1, 2, 36, 36, 18, 9, "NCHW"), (1, 2, 40, 40, 20, 10, "NCHW"),
+                (1, 2, 15, 20, 10, 1, "NCHW")]
+
+
+def _to_layout(a, layout):
+    return a if layout == "NCHW" else np.ascontiguousarray(a.transpose(0, 2, 3, 1))
+
+
+def _from_layout(a, layout):
+    return a if layout == "NCHW" else a.transpose(0, 3, 1, 2)
+
+
+@pytest.mark.parametrize("B,C,H,W,w,s,layout", HIER_GENERAL)
+@pytest.mark.parametrize("mix", [False, True])
+def test_forward_hier_general(B, C, H, W, w, s, layout, mix):
+    """The fold for any s dividing w against the oracle's explicit fold (ragged and padded maps,
+    one channels-last case)."""
+    say(f"forward hier general B={B} C={C} H={H} W={W} w={w} s={s} {layout} mix={mix}")
+    x, T, Ts, Wm = hier_inputs(B, C, H, W, w, s, 170, mix)
+    xd = dev(_to_layout(x, layout))
+    zs = torch.empty_like(xd)
+    y = R().wbmm_forward_hier(xd, w, s, dev(T), dev(Ts), mix_w=dev(Wm) if mix else None,
+                              layout=layout, z_save=zs)
+    want_y, want_z = O.layer_forward_hier(x.astype(np.float64), w, s, T, Ts, Wmix=Wm)
+    assert_f32(_from_layout(host(y), layout), want_y, "y")
+    assert_f32(_from_layout(host(zs), layout), want_z, "z")
+
+
+@pytest.mark.parametrize("w,s", [(12, 3), (20, 10)])
+def test_forward_hier_general_one_hot_bitwise(w, s):
+    """One-hot T and T_sub (at offset 0 on channel 0, so that matrix entries of 2 appear): the
+    folded matrix holds 0, 1 and 2, every output is exact in fp32 and must match bit for bit."""
+    B, C, H, W = 2, 4, 2 * w, 2 * w + s
+    say(f"forward hier general one-hot w={w} s={s}")
+    x = synth.normal_f32((B, C, H, W), 1.0, seed=175)
+    L1, Ls = 2 * w - 1, 2 * s - 1
+    T = np.zeros((C, L1, L1), np.float32)
+    Ts = np.zeros((C, Ls, Ls), np.float32)
+    c = np.arange(1, C)
+    T[c, (c * 5) % L1, (c * 3 + 2) % L1] = 1.0
+    Ts[c, (c * 2) % Ls, (c + 1) % Ls] = 1.0
+    T[0, w - 1, w - 1] = 1.0
+    Ts[0, s - 1, s - 1] = 1.0
+    y = R().wbmm_forward_hier(dev(x), w, s, dev(T), dev(Ts))
+    want, _ = O.layer_forward_hier(x.astype(np.float64), w, s, T, Ts)
+    assert np.array_equal(host(y), want.astype(np.float32))
+
+
+@pytest.mark.parametrize("B,C,H,W,w,s,layout", HIER_GENERAL)
+@pytest.mark.parametrize("mix", [False, True])
+def test_backward_hier_general(B, C, H, W, w, s, layout, mix):
+    """dx, dT, dT_sub (and dWmix) for any s dividing w against the oracle; a second call is
+    bitwise identical."""
+    say(f"backward hier general B={B} C={C} H={H} W={W} w={w} s={s} {layout} mix={mix}")
+    x, T, Ts, Wm = hier_inputs(B, C, H, W, w, s, 180, mix)
+    dy = synth.normal_f32((B, C, H, W), 1.0, seed=185)
+    xd, dyd = dev(_to_layout(x, layout)), dev(_to_layout(dy, layout))
+    Td, Tsd = dev(T), dev(Ts)
+    Wd = dev(Wm) if mix else None
+    zs = None
+    if mix:
+        zs = torch.empty_like(xd)
+        R().wbmm_forward_hier(xd, w, s, Td, Tsd, mix_w=Wd, layout=layout, z_save=zs)
+    dx, dT, dTs, dW = R().wbmm_backward_hier(xd, dyd, w, s, Td, Tsd, mix_w=Wd, z_saved=zs,
+                                             layout=layout)
+    z64 = _from_layout(host(zs), layout).astype(np.float64) if mix else None
+    wdx, wdT, wdTs, wdW = O.layer_backward_hier(x.astype(np.float64), dy.astype(np.float64), w, s,
+                                                T, Ts, Wmix=Wm, z=z64)
+    assert_f32(_from_layout(host(dx), layout), wdx, "dx")
+    assert_f32(host(dT), wdT, "dT")
+    assert_f32(host(dTs), wdTs, "dT_sub")
+    if mix:
+        assert_f32(host(dW), wdW, "dWmix")
+    dx2, dT2, dTs2, _ = R().wbmm_backward_hier(xd, dyd, w, s, Td, Tsd, mix_w=Wd, z_saved=zs,
+                                               layout=layout)
+    assert torch.equal(dx, dx2) and torch.equal(dT, dT2) and torch.equal(dTs, dTs2)
+
+
+def test_backward_hier_general_partial_outputs():
+    """General s: only dT_sub (the main backward is skipped), or only dx (no sub backward)."""
+    B, C, H, W, w, s = 2, 2, 24, 24, 12, 4
+    say("backward hier general partial outputs")
+    x, T, Ts, _ = hier_inputs(B, C, H, W, w, s, 190, False)
+    dy = synth.normal_f32((B, C, H, W), 1.0, seed=195)
+    xd, Td, Tsd, dyd = dev(x), dev(T), dev(Ts), dev(dy)
+    _, dT0, dTs, _ = R().wbmm_backward_hier(xd, dyd, w, s, Td, Tsd, dx=False, dT=False)
+    assert dT0 is None
+    dx, _, dTs0, _ = R().wbmm_backward_hier(xd, dyd, w, s, Td, Tsd, dT=False, dT_sub=False)
+    assert dTs0 is None
+    wdx, _, wdTs, _ = O.layer_backward_hier(x.astype(np.float64), dy.astype(np.float64), w, s, T, Ts)
+    assert_f32(host(dTs), wdTs, "dT_sub")
+    assert_f32(host(dx), wdx, "dx")
+
+
 @pytest.mark.parametrize("B,C,H", [(5, 3, 14), (18, 2, 28), (5, 2, 56)])
 @pytest.mark.parametrize("mix", [False, True])
 def test_hier_fast_shapes(B, C, H, mix):
