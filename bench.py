@@ -56,7 +56,8 @@ KERNEL_FILES = {"k_fwd_ws": "wbmm_fast.hip", "k_bwd_ls": "wbmm_fast.hip", "k_fwd
                 "k_fwd_bf16_w28": "wbmm_fastbf.hip", "k_fwd_bf16": "wbmm_fastbf.hip",
                 "k_wbmm_fwd": "wbmm_fwd.hip", "k_wbmm_bwd": "wbmm_bwd.hip",
                 "k_fwd_f32_w7": "wbmm_fast7.hip", "k_fwd_f32_w28": "wbmm_fast28.hip",
-                "k_fwd_tab": "wbmm_fasttab.hip", "k_mix_direct": "wbmm_aux.hip"}
+                "k_fwd_tab": "wbmm_fasttab.hip", "k_mix_direct": "wbmm_aux.hip",
+                "k_roll_fwd": "wbmm_fast.hip", "k_roll_bwd": "wbmm_fast.hip"}
 HOST_HEADERS = ("wbmm_launch.hpp",)
 
 
@@ -578,8 +579,9 @@ def _pmc_rows(d):
 
 # bench label -> names of the kernels that can be that call's main kernel (fast or general path)
 MAIN_KERNELS = {"k_wbmm_fwd": ("k_fwd_ws", "k_fwd_cm", "k_fwd_bf16_w7", "k_fwd_bf16_w28", "k_fwd_bf16",
-                               "k_fwd_f32_w7", "k_fwd_f32_w28", "k_fwd_tab", "k_wbmm_fwd"),
-                "k_wbmm_bwd": ("k_bwd_ls", "k_wbmm_bwd")}
+                               "k_fwd_f32_w7", "k_fwd_f32_w28", "k_fwd_tab", "k_roll_fwd",
+                               "k_wbmm_fwd"),
+                "k_wbmm_bwd": ("k_bwd_ls", "k_roll_bwd", "k_wbmm_bwd")}
 
 
 def _per_dispatch(rows, counter, names, with_name=False):

@@ -291,7 +291,15 @@ size_t backward_ws_bytes(int B, int C, int H, int W, int w, int oy, int ox, int 
   r.oy = oy;
   r.ox = ox;
   if (!wbmm::backward_plan_ok(r)) return 0;
-  return wbmm::backward_workspace(r);
+  // the operand kind is not an argument: the larger need of a table and a cached matrix
+  size_t need = wbmm::backward_workspace(r);
+  r.T = nullptr;
+  r.M = &dummy;
+  if (wbmm::backward_plan_ok(r)) {
+    const size_t n = wbmm::backward_workspace(r);
+    if (n > need) need = n;
+  }
+  return need;
 }
 
 }  // namespace

@@ -357,6 +357,7 @@ size_t backward_workspace(const BwdRequest& r) {
   if (wide_backward_ok(r)) return backward_wide_workspace(r, sizeof(float));
   Geo g;
   if (!plan_bwd(g, r)) return 0;
+  if (roll_backward_ok(r)) return roll_backward_workspace(r);
   if (repack_backward_ok(r)) return repack_backward_workspace(r);
   const size_t generic = bwd_ws_layout(g, r).total;
   const size_t fast = fast_backward_ok(r) ? fast_backward_workspace(r) : 0;
@@ -444,6 +445,7 @@ hipError_t launch_backward(const BwdRequest& r, hipStream_t st) {
   if (hier_general(r)) return launch_backward_hier_general(r, st);  // s | w, w != 2s
   if (wide_backward_ok(r)) return launch_backward_wide(r, false, st);  // 16 < w <= 32
   if (fast_backward_ok(r)) return launch_backward_fast(r, st);  // folds a sub-table when w = 2s
+  if (roll_backward_ok(r)) return launch_backward_rolled(r, st);  // offset 0 / 7, 28 x 28
   if (repack_backward_ok(r)) return launch_backward_repacked(r, st);  // offset grid, w = 14
   return launch_backward_general<float>(r, st);
 }

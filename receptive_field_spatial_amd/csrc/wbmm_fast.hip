@@ -54,6 +54,7 @@ struct FastArgs {
   const float* Tsub;    // (C, 2s-1, 2s-1) sub-window tables, s = WS / 2 (hierarchical kernels)
   double* partTs;       // [C * groups][(2s-1)^2]: sub-table gradient partials (backward)
   int want_dTs;
+  int roy, rox;         // rolled kernels: window-grid offset, each 0 or WS / 2
 };
 
 constexpr int kWsThreads = 12 * 64;  // 8 consumer waves + 4 producer waves
@@ -581,7 +582,8 @@ __device__ constexpr bool slot_valid(int j) {
 // windows at pitch XP). Lanes with x1 or x2 >= WS produce rows/columns of acc never read.
 // HIER: pairs with y1, y2 in one sub-window band (y1 / s == y2 / s, possible only for |dy| < s,
 // i.e. slots j < 4) accumulate in b32[j] instead; at each flush they go to both acc64 and accs64.
-template <class S, int Q, bool HIER>
+// BAND: only the pairs of one band are taken (the others are not pairs of the window).
+template <class S, int Q, bool HIER, bool BAND = false>
 __device__ __forceinline__ void dt_chunk(const float* regions, const float* xbuf, int n0, int kn,
                                          int xc, v4f (&a32)[8], double (&acc64)[8][4],
                                          v4f (&b32)[4], double (&accs64)[4][4], bool flush) {
@@ -601,7 +603,7 @@ __device__ __forceinline__ void dt_chunk(const float* regions, const float* xbuf
   if constexpr (Slot<WS, Q, J>::valid) {                                            \
     const int y2 = y1 - Slot<WS, Q, J>::dy;                                         \
     const float bv = Bv[y2 < 0 ? 0 : (y2 < WS ? y2 : WS - 1)];                      \
-    if (y2 >= 0 && y2 < WS) {                                                       \
+    if (y2 >= 0 && y2 < WS && (!BAND || y1 / S::QW == y2 / S::QW)) {               \
       if (HIER && J < 4 && y1 / S::QW == y2 / S::QW)                                \
         b32[J & 3] = mfma_f32(Av[y1], bv, b32[J & 3]);                              \
       else                                                                          \
@@ -971,6 +973,325 @@ k_bwd_ls(FastArgs a) {
   }
 }
 
+// ------------------------------------------------------------------- rolled offset grid
+// The window grid offset by (oy, ox), each 0 or WS / 2, on IH x IW maps whose sides are multiples
+// of WS (the interleaved layers of the WBMM reading notes, "Limitation": windows shifted between
+// layers; pixels outside the map are zero). Rolling the map by (-oy, -ox) moves every window of
+// the offset grid, as whole quadrants at their own window positions, into one window of the plain
+// grid of the rolled map: a plain window in the last window row (oy != 0) holds the lower half of
+// an offset window above its upper half, and likewise for the last column, so a plain window
+// holds one, two or four pieces. The product keeps the pairs of one piece: the matrix is masked
+// to pairs whose quadrants agree on every split axis, and the pixels outside the map, zero in the
+// offset grid, are simply not there. The work is then that of the plain grid (4 windows of a 28 x
+// 28 map against 9 in the offset grid).
+//
+// Unit = 16 images of one channel, one workgroup of 4 waves; wave k holds the plain window k
+// (row-major 2 x 2) of every image of the unit in its region (image slot = MFMA column), so a
+// wave's windows share one mask and the MFMA table operand stays one value per lane:
+//   mask bit 1 (row split): wave's window row is the last and oy != 0; bit 0 likewise for columns;
+//   pair (i, j) is kept iff ((quadrant(i) ^ quadrant(j)) & mask) == 0.
+struct RollGeo {
+  int cy, cx;  // rolled window origin plus offset: map row of window pixel row py is (py + cy) mod IH
+  int gm;      // mask bits (2: rows split, 1: columns split)
+};
+template <class S>
+__device__ __forceinline__ RollGeo roll_geo(const FastArgs& a, int k) {
+  const int wy = k / S::NWX, wx = k % S::NWX;
+  RollGeo r;
+  r.cy = S::WS * wy + a.roy;
+  r.cx = S::WS * wx + a.rox;
+  r.gm = ((a.roy != 0 && wy == S::NWY - 1) ? 2 : 0) | ((a.rox != 0 && wx == S::NWX - 1) ? 1 : 0);
+  return r;
+}
+__device__ __forceinline__ int wrap(int v, int n) { return v >= n ? v - n : v; }
+
+typedef float f4a4 __attribute__((ext_vector_type(4), aligned(4)));
+typedef float f3a4 __attribute__((ext_vector_type(3), aligned(4)));
+typedef float f2a4 __attribute__((ext_vector_type(2), aligned(4)));
+
+// Window k of the unit's 16 images into a wave region (slot = image, window-major, row-major
+// pixels), read from the map through the roll: half-rows of QW pixels, contiguous in the map (the
+// roll moves whole quadrants), as a 16-byte and a 12-byte load. Images past the batch are zero.
+template <class S>
+struct RollLoad {
+  static_assert(S::QW == 7 && S::NWIN == 4 && S::IPW == 4, "28 x 28 maps of 14 x 14 windows");
+  static constexpr int SEG = 16 * S::WS * 2;   // half-rows per region
+  static constexpr int NS = SEG / 64;          // per lane
+  static_assert(SEG % 64 == 0, "half-rows per lane");
+  float v[NS][S::QW];
+  __device__ __forceinline__ void issue(const float* __restrict__ src, const Unit& U,
+                                        const RollGeo& g, int lane) {
+#pragma unroll
+    for (int j = 0; j < NS; ++j) {
+      const int seg = lane + 64 * j, i = seg / (2 * S::WS), rem = seg % (2 * S::WS);
+      const int py = rem >> 1, qx = rem & 1;
+      if (i < U.nimg) {
+        const float* p = src + i * U.cp + wrap(py + g.cy, S::IH) * S::IW + wrap(S::QW * qx + g.cx, S::IW);
+        const f4a4 lo = *(const f4a4*)p;
+        const f3a4 hi = *(const f3a4*)(p + 4);
+        v[j][0] = lo[0]; v[j][1] = lo[1]; v[j][2] = lo[2]; v[j][3] = lo[3];
+        v[j][4] = hi[0]; v[j][5] = hi[1]; v[j][6] = hi[2];
+      } else {
+#pragma unroll
+        for (int e = 0; e < S::QW; ++e) v[j][e] = 0.f;
+      }
+    }
+  }
+  __device__ __forceinline__ void commit(float* R, int lane) const {
+#pragma unroll
+    for (int j = 0; j < NS; ++j) {
+      const int seg = lane + 64 * j, i = seg / (2 * S::WS), rem = seg % (2 * S::WS);
+      float* d = R + i * S::WPITCH + (rem >> 1) * S::WS + S::QW * (rem & 1);
+#pragma unroll
+      for (int e = 0; e < S::QW; ++e) d[e] = v[j][e];
+    }
+  }
+};
+
+// contract() over all row tiles with the pairs across pieces removed: the table operand of a lane
+// whose output quadrant and K quadrant differ on a masked axis is replaced by zero.
+template <class S, bool FLIP>
+__device__ __forceinline__ void contract_masked(const float* Ts, const float* R, int lane, int gm,
+                                                v4f (&acc)[S::RT]) {
+  const LaneGeo<S> lg(lane);
+  const float* bsrc = R + lg.qbase();
+  const float* abase[S::RT];
+  bool keep[S::RT];
+#pragma unroll
+  for (int t = 0; t < S::RT; ++t) {
+    int i = t * 16 + (lane & 15);
+    if (i > S::D - 1) i = S::D - 1;
+    const int base = (i / S::WS) * S::L1 + (i % S::WS) + S::C0;
+    abase[t] = Ts + (FLIP ? S::L - 1 - base + lg.qoff() : base - lg.qoff() - S::CMAX);
+    const int qi = ((i / S::WS) / S::QW) * 2 + (i % S::WS) / S::QW;
+    keep[t] = ((qi ^ lg.gq) & gm) == 0;
+    acc[t] = v4f{0.f, 0.f, 0.f, 0.f};
+  }
+#pragma unroll
+  for (int s = 0; s < S::KQ; ++s) {
+    const float bv = bsrc[kpix<S>(s)];
+#pragma unroll
+    for (int t = 0; t < S::RT; ++t) {
+      const float av = FLIP ? abase[t][ktab<S>(s)] : abase[t][S::CMAX - ktab<S>(s)];
+      acc[t] = mfma_f32(keep[t] ? av : 0.f, bv, acc[t]);
+    }
+  }
+}
+
+// Accumulators of the wave's windows back to the map through the roll: lane (n, g) holds pixels
+// p = 16t + 4g + r of image slot n; pairs (r, r + 1), r even, are one window row's neighbours and
+// neighbours in the map unless the columns are split (the pair of pixels QW - 1, QW then lies at
+// both ends of a map row), where they go as two stores. o2 (may be null) gets a second copy.
+template <class S>
+__device__ __forceinline__ void roll_store(float* o, float* o2, const Unit& U, const RollGeo& g,
+                                           const v4f (&acc)[S::RT], int lane) {
+  const int n = lane & 15, g4 = 4 * (lane >> 4);
+  if (n >= U.nimg) return;
+  const size_t ob = U.base + (size_t)n * U.cp;
+  const bool split = (g.gm & 1) != 0;
+#pragma unroll
+  for (int t = 0; t < S::RT; ++t)
+#pragma unroll
+    for (int r = 0; r < 4; r += 2) {
+      const int c0 = 16 * t + r;  // p = c0 + g4
+      if (c0 + g4 >= S::D) continue;
+      const int wr = (c0 % S::WS) + g4 >= S::WS ? 1 : 0;
+      const int py = c0 / S::WS + wr, px = (c0 % S::WS) + g4 - wr * S::WS;
+      const int row = wrap(py + g.cy, S::IH) * S::IW;
+      const int e0 = row + wrap(px + g.cx, S::IW);
+      if (!split) {
+        *(f2a4*)(o + ob + e0) = f2a4{acc[t][r], acc[t][r + 1]};
+        if (o2) *(f2a4*)(o2 + ob + e0) = f2a4{acc[t][r], acc[t][r + 1]};
+      } else {
+        const int e1 = row + wrap(px + 1 + g.cx, S::IW);
+        o[ob + e0] = acc[t][r];
+        o[ob + e1] = acc[t][r + 1];
+        if (o2) {
+          o2[ob + e0] = acc[t][r];
+          o2[ob + e1] = acc[t][r + 1];
+        }
+      }
+    }
+}
+
+// Forward on the offset grid: z = masked product of each wave's windows, written to y (and
+// z_save); the 3 x 3 mix runs afterwards on the whole map.
+template <class S>
+__global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3, 8)))
+k_roll_fwd(FastArgs a) {
+  extern __shared__ __attribute__((aligned(16))) float smem_f[];
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  float* Ts = smem_f;
+  float* R = smem_f + S::LP + wave * S::RSZ;
+  const Unit U = unit_of<S>(a, blockIdx.x);
+  const RollGeo g = roll_geo<S>(a, wave);
+  {
+    RollLoad<S> rl;
+    rl.issue(a.x + U.base, U, g, lane);
+    for (int q = threadIdx.x; q < S::L; q += kThreads) Ts[q] = a.T[(size_t)U.c * S::L + q];
+    rl.commit(R, lane);
+  }
+  __syncthreads();
+  v4f acc[S::RT];
+  if (g.gm == 0)
+    contract<S, false, 0, S::RT>(Ts, R, lane, acc);
+  else
+    contract_masked<S, false>(Ts, R, lane, g.gm, acc);
+  roll_store<S>(a.y, a.zsave, U, g, acc, lane);
+}
+
+// Promote the fp32 row-pair chains of one window class to fp64; with the columns split only the
+// elements with x1, x2 in one column half are pairs of the layer.
+template <class S, int Q>
+__device__ __forceinline__ void roll_flush(v4f (&a32)[8], double (&acc64)[8][4], bool split,
+                                           int lane) {
+  const int x2 = lane & 15, g = lane >> 4;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    if (!slot_valid<S::WS, Q>(j)) continue;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int x1 = 4 * g + r;
+      const bool keep = !split || x1 / S::QW == x2 / S::QW;
+      acc64[j][r] += keep ? (double)a32[j][r] : 0.0;
+    }
+    a32[j] = v4f{0.f, 0.f, 0.f, 0.f};
+  }
+}
+
+template <class S, int Q>
+__device__ __forceinline__ void roll_dt_chunk(const float* regions, const float* xbuf, int n0,
+                                              int kn, int xc, bool band, v4f (&a32)[8],
+                                              double (&acc64)[8][4]) {
+  v4f b32[4];
+  double accs64[4][4];
+  if (band)
+    dt_chunk<S, Q, false, true>(regions, xbuf, n0, kn, xc, a32, acc64, b32, accs64, false);
+  else
+    dt_chunk<S, Q, false, false>(regions, xbuf, n0, kn, xc, a32, acc64, b32, accs64, false);
+}
+
+// Backward on the offset grid (dy is the map gradient G of the product; the mix adjoint, if any,
+// has run before): dX = masked M^T G per wave, stored through the roll; the table-gradient pass
+// walks the unit in 16 chunks of 4 windows of one class (chunk ci: window ci / 4 of images
+// 4 (ci % 4) .. +3), with the row pairs of one band only where the rows are split and the column
+// mask applied when the class's chains are promoted.
+template <class S>
+__global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3, 8)))
+k_roll_bwd(FastArgs a) {
+  extern __shared__ __attribute__((aligned(16))) float smem_f[];
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  float* Ts = smem_f;
+  float* regions = smem_f + bwd_tsz<S, false>();
+  float* R = regions + wave * S::RSZ;
+  const int u = blockIdx.x;
+  const Unit U = unit_of<S>(a, u);
+  const RollGeo g = roll_geo<S>(a, wave);
+  {
+    RollLoad<S> rl;
+    rl.issue(a.dy + U.base, U, g, lane);
+    for (int q = threadIdx.x; q < S::L; q += kThreads) Ts[q] = a.T[(size_t)U.c * S::L + q];
+    rl.commit(R, lane);
+  }
+  __syncthreads();
+
+  if (a.want_dx) {
+    v4f acc[S::RT];
+    if (g.gm == 0)
+      contract<S, true, 0, S::RT>(Ts, R, lane, acc);
+    else
+      contract_masked<S, true>(Ts, R, lane, g.gm, acc);
+    roll_store<S>(a.dx, nullptr, U, g, acc, lane);
+  }
+
+  if (a.want_dT) {
+    double acc64[8][4];
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) acc64[j][r] = 0.0;
+    v4f a32[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) a32[j] = v4f{0.f, 0.f, 0.f, 0.f};
+    constexpr int CH_E = 4 * S::D;
+    constexpr int EPT = (CH_E + kThreads - 1) / kThreads;
+    // element e = tid + 256 j of a chunk: window kn = e / D (image 4 (ci % 4) + kn), pixel
+    // p = e % D; recomputed at each use from an opaque thread index (not held across the loop)
+    const float* xu = a.x + U.base;
+    // windows past the batch have G = 0: their loads read within the last image instead
+    const int maxoff = (U.nimg - 1) * U.cp + S::PLANE - 1;
+    float stgA[EPT], stgB[EPT];
+    auto load_chunk = [&](float (&stg)[EPT], int ci) {
+      const RollGeo cg = roll_geo<S>(a, ci >> 2);
+      const int cbase = 4 * (ci & 3) * U.cp;
+      const int tid = opaque_lane(threadIdx.x);
+#pragma unroll
+      for (int j = 0; j < EPT; ++j) {
+        const int e = tid + j * kThreads;
+        const int ee = e < CH_E ? e : 0;
+        const int kn = ee / S::D, p = ee % S::D;
+        const int o = cbase + kn * U.cp + wrap(p / S::WS + cg.cy, S::IH) * S::IW +
+                      wrap(p % S::WS + cg.cx, S::IW);
+        stg[j] = xu[o < maxoff ? o : maxoff];
+      }
+    };
+    const int kn = lane >> 4, x1 = lane & 15;
+    const int xc = x1 < S::WS ? x1 : S::WS - 1;
+    float* xbuf = Ts;
+    auto step = [&](float (&stg)[EPT], int ci) {
+      if (ci > 0) __syncthreads();  // chunk ci-1 consumed by every wave
+      {
+        const int tid = opaque_lane(threadIdx.x);
+#pragma unroll
+        for (int j = 0; j < EPT; ++j) {
+          const int e = tid + j * kThreads;
+          if (e < CH_E) xbuf[(e / S::D) * S::XP + e % S::D] = stg[j];
+        }
+      }
+      __syncthreads();
+      load_chunk(stg, ci + 2 < 16 ? ci + 2 : 15);
+      const RollGeo cg = roll_geo<S>(a, ci >> 2);
+      const bool band = (cg.gm & 2) != 0, split = (cg.gm & 1) != 0;
+      const int n0 = 16 * (ci >> 2) + 4 * (ci & 3);
+      const bool flush = (ci & 3) == 3;
+      switch (wave) {
+        case 0:
+          roll_dt_chunk<S, 0>(regions, xbuf, n0, kn, xc, band, a32, acc64);
+          if (flush) roll_flush<S, 0>(a32, acc64, split, lane);
+          break;
+        case 1:
+          roll_dt_chunk<S, 1>(regions, xbuf, n0, kn, xc, band, a32, acc64);
+          if (flush) roll_flush<S, 1>(a32, acc64, split, lane);
+          break;
+        case 2:
+          roll_dt_chunk<S, 2>(regions, xbuf, n0, kn, xc, band, a32, acc64);
+          if (flush) roll_flush<S, 2>(a32, acc64, split, lane);
+          break;
+        default:
+          roll_dt_chunk<S, 3>(regions, xbuf, n0, kn, xc, band, a32, acc64);
+          if (flush) roll_flush<S, 3>(a32, acc64, split, lane);
+          break;
+      }
+    };
+    load_chunk(stgA, 0);
+    load_chunk(stgB, 1);
+    __syncthreads();  // every wave is done with the table (dX)
+    for (int ci = 0; ci < 16; ci += 2) {
+      step(stgA, ci);
+      step(stgB, ci + 1);
+    }
+    double* pT = a.partT + (size_t)u * S::L;
+    __syncthreads();  // every wave is done reading the G regions and the last chunk
+    double* scr = (double*)R;
+    switch (wave) {
+      case 0: dt_partial_write<S, 0>(scr, acc64, pT, lane); break;
+      case 1: dt_partial_write<S, 1>(scr, acc64, pT, lane); break;
+      case 2: dt_partial_write<S, 2>(scr, acc64, pT, lane); break;
+      default: dt_partial_write<S, 3>(scr, acc64, pT, lane); break;
+    }
+  }
+}
+
 // ---------------------------------------------------------------------------- dispatch
 namespace {
 
@@ -1040,6 +1361,10 @@ static_assert(lds_fits(fwd_lds<S14, true>(), 1) && lds_fits(fwd_lds<S28, true>()
 static_assert(lds_fits(bwd_lds<S14, true>(), 2) && lds_fits(bwd_lds<S28, true>(), 2) &&
                   lds_fits(bwd_lds<S56, true>(), 2),
               "two hierarchical backward workgroups per CU");
+template <class S>
+constexpr int roll_fwd_lds() { return (S::LP + 4 * S::RSZ) * 4; }
+static_assert(lds_fits(roll_fwd_lds<S28>(), 3) && lds_fits(bwd_lds<S28>(), 3),
+              "three rolled-grid workgroups per CU");
 
 // Backward: one workgroup of 4 waves per unit.
 template <class S, class Fn>
@@ -1091,6 +1416,67 @@ hipError_t launch_forward_fast(const FwdRequest& r, hipStream_t st) {
                : launch_ws<S56>(k_fwd_ws<S56, false>, fwd_lds<S56>(), a, st);
     default: return hipErrorInvalidValue;
   }
+}
+
+// The offset grid on the rolled map: fp32, w = 14, NCHW 28 x 28, offsets 0 or 7 (not both 0).
+static bool roll_shape_ok(int B, int C, int H, int W, int w, int layout, int oy, int ox) {
+  return w == 14 && layout == 0 && H == 28 && W == 28 && (oy == 0 || oy == 7) &&
+         (ox == 0 || ox == 7) && (oy != 0 || ox != 0) && B >= 1 && C >= 1 &&
+         offsets_fit(C, H, W);
+}
+
+bool fast_roll_forward_ok(const FwdRequest& r) {
+  return !r.in_bf16 && !r.out_bf16 && r.T && !r.M && !r.Tsub && !r.flip &&
+         roll_shape_ok(r.B, r.C, r.H, r.W, r.w, r.layout, r.oy, r.ox);
+}
+
+bool fast_roll_backward_ok(const BwdRequest& r) {
+  return r.T && !r.M && !r.Tsub && roll_shape_ok(r.B, r.C, r.H, r.W, r.w, r.layout, r.oy, r.ox);
+}
+
+// out: the product (y, or the pre-mix map); out2: a second copy or null.
+hipError_t launch_forward_fast_roll(const FwdRequest& r, float* out, float* out2, hipStream_t st) {
+  if (!fast_roll_forward_ok(r)) return hipErrorInvalidValue;
+  FastArgs a{};
+  a.B = r.B;
+  a.C = r.C;
+  a.x = (const float*)r.x;
+  a.T = (const float*)r.T;
+  a.y = out;
+  a.zsave = out2;
+  a.roy = r.oy;
+  a.rox = r.ox;
+  return launch_ls<S28>(k_roll_fwd<S28>, roll_fwd_lds<S28>(), a, st);
+}
+
+// Table-gradient partials of the rolled backward: one fp64 row of L per unit.
+size_t fast_roll_backward_workspace(const BwdRequest& r) {
+  if (!fast_roll_backward_ok(r)) return 0;
+  const size_t L = (size_t)(2 * r.w - 1) * (2 * r.w - 1);
+  return ((size_t)r.C * groups<S28>(r.B) * L * 8 + 255) / 256 * 256;
+}
+
+// dy: the map gradient of the product (the mix adjoint, if any, already applied).
+hipError_t launch_backward_fast_roll(const BwdRequest& r, hipStream_t st) {
+  if (!fast_roll_backward_ok(r)) return hipErrorInvalidValue;
+  FastArgs a{};
+  a.B = r.B;
+  a.C = r.C;
+  a.x = r.x;
+  a.T = r.T;
+  a.dy = r.dy;
+  a.dx = r.dx;
+  a.dT = r.dT;
+  a.partT = (double*)r.ws;
+  a.want_dx = r.dx != nullptr;
+  a.want_dT = r.dT != nullptr;
+  a.roy = r.oy;
+  a.rox = r.ox;
+  if (!a.want_dx && !a.want_dT) return hipSuccess;
+  hipError_t e = launch_ls<S28>(k_roll_bwd<S28>, bwd_lds<S28>(), a, st);
+  if (e != hipSuccess || !a.want_dT) return e;
+  const int L = (2 * r.w - 1) * (2 * r.w - 1);
+  return launch_bwd_reduce(a.partT, nullptr, groups<S28>(r.B), r.C, L, r.dT, nullptr, st);
 }
 
 size_t fast_backward_workspace(const BwdRequest& r) {

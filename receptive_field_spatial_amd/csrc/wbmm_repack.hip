@@ -231,6 +231,42 @@ hipError_t launch_forward_repacked(const FwdRequest& r, hipStream_t st) {
   return launch_mix_fwd(z, r.mixw, r.y, 0, r.B, r.C, r.H, r.W, 0, st);
 }
 
+namespace {
+// With the mix: its data gradient G (and its weight gradient) on the whole map, in `ws` (the
+// G map, then the dWmix partials); returns the map the product's backward reads (G, or dy).
+hipError_t mix_adjoint_map(const BwdRequest& r, unsigned char* ws, const float** gsrc,
+                           hipStream_t st) {
+  *gsrc = r.dy;
+  if (!r.mixw) return hipSuccess;
+  float* gz = (float*)ws;
+  hipError_t e;
+  if (mix_planes_fit(r.H, r.W)) {  // one plane-staged pass: G and per-group dWmix partials
+    double* partW = (double*)(ws + al256((size_t)r.B * r.C * r.H * r.W * 4));
+    e = launch_mix_bwd_planes_f32(r.dy, r.dmixw ? r.zsaved : nullptr, r.mixw, gz, partW, r.B,
+                                  r.C, r.H, r.W, st);
+    if (e != hipSuccess) return e;
+    if (r.dmixw) {
+      e = launch_bwd_reduce(nullptr, partW, mix_bwd_parts(r.B, r.H, r.W), r.C, 0, nullptr,
+                            r.dmixw, st);
+      if (e != hipSuccess) return e;
+    }
+  } else {
+    e = launch_mix_bwd_data(r.dy, r.mixw, gz, r.B, r.C, r.H, r.W, 0, st);
+    if (e != hipSuccess) return e;
+    if (r.dmixw) {
+      e = launch_mix_bwd_weight(r.dy, r.zsaved, r.dmixw, r.B, r.C, r.H, r.W, 0, st);
+      if (e != hipSuccess) return e;
+    }
+  }
+  *gsrc = gz;
+  return hipSuccess;
+}
+size_t mix_adjoint_bytes(const BwdRequest& r) {
+  return r.mixw ? al256((size_t)r.B * r.C * r.H * r.W * 4) + mix_partials_bytes(r.B, r.C, r.H, r.W)
+                : 0;
+}
+}  // namespace
+
 bool repack_backward_ok(const BwdRequest& r) {
   return r.T && !r.M && !r.Tsub && repack_fits(r.B, r.C, r.H, r.W, r.w, r.layout, r.oy, r.ox);
 }
@@ -254,9 +290,32 @@ size_t repack_backward_workspace(const BwdRequest& r) {
   if (!repack_backward_ok(r)) return 0;
   const RepackGeo g = repack_geo(r.B, r.C, r.H, r.W, r.oy, r.ox);
   const size_t fast = al256(fast_backward_workspace(repacked_request(r, g)));
-  const size_t mix =
-      r.mixw ? al256((size_t)r.B * r.C * r.H * r.W * 4) + mix_partials_bytes(r.B, r.C, r.H, r.W) : 0;
-  return fast + 3 * repacked_bytes(g) + mix;
+  return fast + 3 * repacked_bytes(g) + mix_adjoint_bytes(r);
+}
+
+// The rolled-map kernels for grid offsets 0 or 7 on 28 x 28 maps (fp32):
+// [table-gradient partials] [with the mix: G map, dWmix partials]
+bool roll_backward_ok(const BwdRequest& r) { return fast_roll_backward_ok(r); }
+
+size_t roll_backward_workspace(const BwdRequest& r) {
+  if (!roll_backward_ok(r)) return 0;
+  return al256(fast_roll_backward_workspace(r)) + mix_adjoint_bytes(r);
+}
+
+hipError_t launch_backward_rolled(const BwdRequest& r, hipStream_t st) {
+  if (!roll_backward_ok(r)) return hipErrorInvalidValue;
+  unsigned char* ws = (unsigned char*)r.ws;
+  const size_t part = al256(fast_roll_backward_workspace(r));
+  const float* gsrc = nullptr;
+  hipError_t e = mix_adjoint_map(r, ws + part, &gsrc, st);
+  if (e != hipSuccess || (!r.dx && !r.dT)) return e;
+  BwdRequest q = r;
+  q.dy = gsrc;
+  q.mixw = nullptr;
+  q.zsaved = nullptr;
+  q.dmixw = nullptr;
+  q.ws = ws;
+  return launch_backward_fast_roll(q, st);
 }
 
 hipError_t launch_backward_repacked(const BwdRequest& r, hipStream_t st) {
@@ -270,30 +329,9 @@ hipError_t launch_backward_repacked(const BwdRequest& r, hipStream_t st) {
   float* gr = (float*)(ws + fast);
   float* xr = (float*)(ws + fast + rb);
   float* dxr = (float*)(ws + fast + 2 * rb);
-  const float* gsrc = r.dy;
-  hipError_t e = hipSuccess;
-  if (r.mixw) {  // the mix's data gradient (and its weight gradient) on the whole map
-    float* gz = (float*)(ws + fast + 3 * rb);
-    if (mix_planes_fit(r.H, r.W)) {  // one plane-staged pass: G and per-group dWmix partials
-      double* partW = (double*)(ws + fast + 3 * rb + al256((size_t)r.B * r.C * r.H * r.W * 4));
-      e = launch_mix_bwd_planes_f32(r.dy, r.dmixw ? r.zsaved : nullptr, r.mixw, gz, partW, r.B,
-                                    r.C, r.H, r.W, st);
-      if (e != hipSuccess) return e;
-      if (r.dmixw) {
-        e = launch_bwd_reduce(nullptr, partW, mix_bwd_parts(r.B, r.H, r.W), r.C, 0, nullptr,
-                              r.dmixw, st);
-        if (e != hipSuccess) return e;
-      }
-    } else {
-      e = launch_mix_bwd_data(r.dy, r.mixw, gz, r.B, r.C, r.H, r.W, 0, st);
-      if (e != hipSuccess) return e;
-      if (r.dmixw) {
-        e = launch_mix_bwd_weight(r.dy, r.zsaved, r.dmixw, r.B, r.C, r.H, r.W, 0, st);
-        if (e != hipSuccess) return e;
-      }
-    }
-    gsrc = gz;
-  }
+  const float* gsrc = nullptr;
+  hipError_t e = mix_adjoint_map(r, ws + fast + 3 * rb, &gsrc, st);
+  if (e != hipSuccess) return e;
   if (!r.dx && !r.dT) return hipSuccess;
   e = gather<float>(g, gsrc, gr, st);
   if (e != hipSuccess) return e;

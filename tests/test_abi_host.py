@@ -246,24 +246,38 @@ def test_shifted_validation(lib):
 
 
 def test_shifted_workspace_covers_the_repacked_maps(lib):
-    """w = 14 offset grids on NCHW maps: B=64 at 28x28 with offset (7, 7) has 9 windows per image,
+    """w = 14 offset grids on NCHW maps: B=64 at 28x28 with offset (5, 9) has 9 windows per image,
     576 windows = 144 repacked 28x28 images of 2x2 windows. The fp32 forward reads the offset
     grid directly (with the mix and no z_save buffer it needs the image-space z); the bf16 forward
     without the mix runs on repacked X and z (bf16: together the bytes of one fp32 repacked map);
-    the backward holds repacked G, X and dX, and with the mix the image-space G."""
+    the backward holds repacked G, X and dX, and with the mix the image-space G. Offsets of 0 or
+    7 on 28x28 maps run on the rolled map instead: the backward from the table then holds only
+    the fp64 table-gradient partials (one row of 27 x 27 per 16 images and channel), and the
+    image-space G with the mix; the query also covers a cached matrix (general kernels), so the
+    figure is the larger of the two, far below one repacked map."""
     B, C = 64, 192
     rep = 144 * C * 28 * 28 * 4
     img = B * C * 28 * 28 * 4
-    fwd = lib.wbmm_forward_shifted_workspace_bytes(B, C, 28, 28, 14, 7, 7, 0, 0, 0)
-    assert fwd >= rep
-    assert lib.wbmm_forward_shifted_workspace_bytes(B, C, 28, 28, 14, 7, 7, 0, 1, 0) >= img
-    assert lib.wbmm_forward_shifted_workspace_bytes(B, C, 28, 28, 14, 7, 7, 0, 1, 1) < img
-    bwd = lib.wbmm_backward_shifted_workspace_bytes(B, C, 28, 28, 14, 7, 7, 0, 0)
+    for oy, ox in ((5, 9), (7, 7)):
+        fwd = lib.wbmm_forward_shifted_workspace_bytes(B, C, 28, 28, 14, oy, ox, 0, 0, 0)
+        assert fwd >= rep
+        assert lib.wbmm_forward_shifted_workspace_bytes(B, C, 28, 28, 14, oy, ox, 0, 1, 0) >= img
+        assert lib.wbmm_forward_shifted_workspace_bytes(B, C, 28, 28, 14, oy, ox, 0, 1, 1) < img
+    bwd = lib.wbmm_backward_shifted_workspace_bytes(B, C, 28, 28, 14, 5, 9, 0, 0)
     assert bwd >= 3 * rep
-    assert lib.wbmm_backward_shifted_workspace_bytes(B, C, 28, 28, 14, 7, 7, 0, 1) >= bwd + img
+    assert lib.wbmm_backward_shifted_workspace_bytes(B, C, 28, 28, 14, 5, 9, 0, 1) >= bwd + img
     # a partial last repacked image: 5 images x 9 windows = 45 windows -> 12 repacked images
-    assert lib.wbmm_backward_shifted_workspace_bytes(5, 2, 28, 28, 14, 7, 7, 0, 0) >= \
+    assert lib.wbmm_backward_shifted_workspace_bytes(5, 2, 28, 28, 14, 5, 9, 0, 0) >= \
         3 * 12 * 2 * 28 * 28 * 4
+    part = C * (B // 16) * 27 * 27 * 8
+    for oy, ox in ((7, 7), (7, 0), (0, 7)):
+        rolled = lib.wbmm_backward_shifted_workspace_bytes(B, C, 28, 28, 14, oy, ox, 0, 0)
+        assert part <= rolled < rep
+        assert lib.wbmm_backward_shifted_workspace_bytes(B, C, 28, 28, 14, oy, ox, 0, 1) >= \
+            part + img
+    # 17 images: two units of 16
+    assert lib.wbmm_backward_shifted_workspace_bytes(17, 2, 28, 28, 14, 7, 7, 0, 0) >= \
+        2 * 2 * 27 * 27 * 8
 
 
 def test_backward_bf16_validation(lib):

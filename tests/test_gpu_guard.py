@@ -309,9 +309,10 @@ def test_guard_bf16_backward(B, H, mix):
 
 
 @pytest.mark.parametrize("B,C,H,W,w,o", [(5, 3, 28, 28, 14, 7), (2, 2, 30, 25, 14, 3),
-                                         (2, 2, 17, 13, 4, 2)])
+                                         (2, 2, 17, 13, 4, 2), (17, 3, 28, 28, 14, 7)])
 def test_guard_shifted(B, C, H, W, w, o):
-    """The interleaved grid (repacked fast kernels for w = 14): outputs and workspaces guarded."""
+    """The interleaved grid (the rolled-map kernels for offset 7 on 28x28 maps, the table kernel
+    and repacked fast kernels for other w = 14 grids): outputs and workspaces guarded."""
     say(f"guard shifted B={B} C={C} H={H} W={W} w={w} o={o}")
     x = synth.normal_f32((B, C, H, W), 1.0, seed=440)
     T = synth.normal_f32((C, 2 * w - 1, 2 * w - 1), 0.05, seed=441)
