@@ -1009,72 +1009,94 @@ typedef float f4a4 __attribute__((ext_vector_type(4), aligned(4)));
 typedef float f3a4 __attribute__((ext_vector_type(3), aligned(4)));
 typedef float f2a4 __attribute__((ext_vector_type(2), aligned(4)));
 
-// Window k of the unit's 16 images into a wave region (slot = image, window-major, row-major
-// pixels), read from the map through the roll: half-rows of QW pixels, contiguous in the map (the
-// roll moves whole quadrants), as a 16-byte and a 12-byte load. Images past the batch are zero.
+// The 49 pixels of quadrant q of plain window k of image slot n (lane (n, q) = (lane % 16,
+// lane / 16)), read from the map through the roll: 7 half-rows of QW pixels, each contiguous in
+// the map (the roll moves whole quadrants), as a 16-byte and a 12-byte load. Images past the
+// batch are zero. Pixel s of the quadrant is the lane's MFMA operand of K step s.
 template <class S>
-struct RollLoad {
+struct RollQuad {
   static_assert(S::QW == 7 && S::NWIN == 4 && S::IPW == 4, "28 x 28 maps of 14 x 14 windows");
-  static constexpr int SEG = 16 * S::WS * 2;   // half-rows per region
-  static constexpr int NS = SEG / 64;          // per lane
-  static_assert(SEG % 64 == 0, "half-rows per lane");
-  float v[NS][S::QW];
-  __device__ __forceinline__ void issue(const float* __restrict__ src, const Unit& U,
-                                        const RollGeo& g, int lane) {
+  float v[S::KQ];
+  __device__ __forceinline__ void load(const float* __restrict__ src, const Unit& U,
+                                       const RollGeo& g, int lane) {
+    const int n = lane & 15, q = lane >> 4, qy = q >> 1, qx = q & 1;
+    if (n < U.nimg) {
+      const float* p = src + n * U.cp + wrap(S::QW * qx + g.cx, S::IW);
 #pragma unroll
-    for (int j = 0; j < NS; ++j) {
-      const int seg = lane + 64 * j, i = seg / (2 * S::WS), rem = seg % (2 * S::WS);
-      const int py = rem >> 1, qx = rem & 1;
-      if (i < U.nimg) {
-        const float* p = src + i * U.cp + wrap(py + g.cy, S::IH) * S::IW + wrap(S::QW * qx + g.cx, S::IW);
-        const f4a4 lo = *(const f4a4*)p;
-        const f3a4 hi = *(const f3a4*)(p + 4);
-        v[j][0] = lo[0]; v[j][1] = lo[1]; v[j][2] = lo[2]; v[j][3] = lo[3];
-        v[j][4] = hi[0]; v[j][5] = hi[1]; v[j][6] = hi[2];
-      } else {
-#pragma unroll
-        for (int e = 0; e < S::QW; ++e) v[j][e] = 0.f;
+      for (int r = 0; r < S::QW; ++r) {
+        const float* pr = p + wrap(S::QW * qy + r + g.cy, S::IH) * S::IW;
+        const f4a4 lo = *(const f4a4*)pr;
+        const f3a4 hi = *(const f3a4*)(pr + 4);
+        v[7 * r + 0] = lo[0]; v[7 * r + 1] = lo[1]; v[7 * r + 2] = lo[2]; v[7 * r + 3] = lo[3];
+        v[7 * r + 4] = hi[0]; v[7 * r + 5] = hi[1]; v[7 * r + 6] = hi[2];
       }
+    } else {
+#pragma unroll
+      for (int e = 0; e < S::KQ; ++e) v[e] = 0.f;
     }
   }
+  // into a wave region, window-major (slot n, row-major pixels)
   __device__ __forceinline__ void commit(float* R, int lane) const {
+    const LaneGeo<S> lg(lane);
+    float* d = R + lg.qbase();
 #pragma unroll
-    for (int j = 0; j < NS; ++j) {
-      const int seg = lane + 64 * j, i = seg / (2 * S::WS), rem = seg % (2 * S::WS);
-      float* d = R + i * S::WPITCH + (rem >> 1) * S::WS + S::QW * (rem & 1);
-#pragma unroll
-      for (int e = 0; e < S::QW; ++e) d[e] = v[j][e];
-    }
+    for (int e = 0; e < S::KQ; ++e) d[kpix<S>(e)] = v[e];
   }
 };
 
-// contract() over all row tiles with the pairs across pieces removed: the table operand of a lane
-// whose output quadrant and K quadrant differ on a masked axis is replaced by zero.
+// Row tiles [T0, T0 + NT) of contract() with the window operand in registers and the pairs
+// across pieces removed: a lane whose output quadrant and K quadrant differ on a masked axis
+// reads its table operands at ZOFF, where CMAX + 1 zeros lie (an integer offset, so the address
+// stays a plain LDS one; gm = 0 keeps every pair). The table operands are read two K steps
+// ahead of their MFMAs, the scheduling fenced so that the reads go out first.
 template <class S, bool FLIP>
-__device__ __forceinline__ void contract_masked(const float* Ts, const float* R, int lane, int gm,
-                                                v4f (&acc)[S::RT]) {
+__device__ constexpr int roll_koff(int s) { return FLIP ? ktab<S>(s) : S::CMAX - ktab<S>(s); }
+
+template <class S, bool FLIP, int ZOFF, int T0, int NT>
+__device__ __forceinline__ void contract_roll(const float* Ts, const float (&bq)[S::KQ], int lane,
+                                              int gm, v4f (&acc)[NT]) {
   const LaneGeo<S> lg(lane);
-  const float* bsrc = R + lg.qbase();
-  const float* abase[S::RT];
-  bool keep[S::RT];
+  int rb[NT];
 #pragma unroll
-  for (int t = 0; t < S::RT; ++t) {
-    int i = t * 16 + (lane & 15);
+  for (int t = 0; t < NT; ++t) {
+    int i = (T0 + t) * 16 + (lane & 15);
     if (i > S::D - 1) i = S::D - 1;
     const int base = (i / S::WS) * S::L1 + (i % S::WS) + S::C0;
-    abase[t] = Ts + (FLIP ? S::L - 1 - base + lg.qoff() : base - lg.qoff() - S::CMAX);
+    const int off = FLIP ? S::L - 1 - base + lg.qoff() : base - lg.qoff() - S::CMAX;
     const int qi = ((i / S::WS) / S::QW) * 2 + (i % S::WS) / S::QW;
-    keep[t] = ((qi ^ lg.gq) & gm) == 0;
+    rb[t] = (((qi ^ lg.gq) & gm) == 0) ? off : ZOFF;
     acc[t] = v4f{0.f, 0.f, 0.f, 0.f};
   }
+  float a0[NT], a1[NT];
 #pragma unroll
-  for (int s = 0; s < S::KQ; ++s) {
-    const float bv = bsrc[kpix<S>(s)];
+  for (int t = 0; t < NT; ++t) {
+    a0[t] = Ts[rb[t] + roll_koff<S, FLIP>(0)];
+    a1[t] = Ts[rb[t] + roll_koff<S, FLIP>(1)];
+  }
 #pragma unroll
-    for (int t = 0; t < S::RT; ++t) {
-      const float av = FLIP ? abase[t][ktab<S>(s)] : abase[t][S::CMAX - ktab<S>(s)];
-      acc[t] = mfma_f32(keep[t] ? av : 0.f, bv, acc[t]);
+  for (int s = 0; s < S::KQ; s += 2) {
+    float b0[NT], b1[NT];
+    if (s + 2 < S::KQ) {
+#pragma unroll
+      for (int t = 0; t < NT; ++t) b0[t] = Ts[rb[t] + roll_koff<S, FLIP>(s + 2)];
     }
+    if (s + 3 < S::KQ) {
+#pragma unroll
+      for (int t = 0; t < NT; ++t) b1[t] = Ts[rb[t] + roll_koff<S, FLIP>(s + 3)];
+    }
+    __builtin_amdgcn_sched_barrier(0);  // the reads go out before this pair's MFMAs
+#pragma unroll
+    for (int t = 0; t < NT; ++t) acc[t] = mfma_f32(a0[t], bq[s], acc[t]);
+    if (s + 1 < S::KQ) {
+#pragma unroll
+      for (int t = 0; t < NT; ++t) acc[t] = mfma_f32(a1[t], bq[s + 1], acc[t]);
+    }
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      a0[t] = b0[t];
+      a1[t] = b1[t];
+    }
+    __builtin_amdgcn_sched_barrier(0);
   }
 }
 
@@ -1082,18 +1104,18 @@ __device__ __forceinline__ void contract_masked(const float* Ts, const float* R,
 // p = 16t + 4g + r of image slot n; pairs (r, r + 1), r even, are one window row's neighbours and
 // neighbours in the map unless the columns are split (the pair of pixels QW - 1, QW then lies at
 // both ends of a map row), where they go as two stores. o2 (may be null) gets a second copy.
-template <class S>
+template <class S, int T0, int NT>
 __device__ __forceinline__ void roll_store(float* o, float* o2, const Unit& U, const RollGeo& g,
-                                           const v4f (&acc)[S::RT], int lane) {
+                                           const v4f (&acc)[NT], int lane) {
   const int n = lane & 15, g4 = 4 * (lane >> 4);
   if (n >= U.nimg) return;
   const size_t ob = U.base + (size_t)n * U.cp;
   const bool split = (g.gm & 1) != 0;
 #pragma unroll
-  for (int t = 0; t < S::RT; ++t)
+  for (int t = 0; t < NT; ++t)
 #pragma unroll
     for (int r = 0; r < 4; r += 2) {
-      const int c0 = 16 * t + r;  // p = c0 + g4
+      const int c0 = 16 * (T0 + t) + r;  // p = c0 + g4
       if (c0 + g4 >= S::D) continue;
       const int wr = (c0 % S::WS) + g4 >= S::WS ? 1 : 0;
       const int py = c0 / S::WS + wr, px = (c0 % S::WS) + g4 - wr * S::WS;
@@ -1116,28 +1138,39 @@ __device__ __forceinline__ void roll_store(float* o, float* o2, const Unit& U, c
 
 // Forward on the offset grid: z = masked product of each wave's windows, written to y (and
 // z_save); the 3 x 3 mix runs afterwards on the whole map.
+// LDS: the table, then CMAX + 1 zeros for the masked operands.
+template <class S>
+constexpr int roll_fwd_floats() { return S::LP + (S::CMAX + 4) / 4 * 4; }
+
 template <class S>
 __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3, 8)))
 k_roll_fwd(FastArgs a) {
   extern __shared__ __attribute__((aligned(16))) float smem_f[];
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   float* Ts = smem_f;
-  float* R = smem_f + S::LP + wave * S::RSZ;
   const Unit U = unit_of<S>(a, blockIdx.x);
   const RollGeo g = roll_geo<S>(a, wave);
-  {
-    RollLoad<S> rl;
-    rl.issue(a.x + U.base, U, g, lane);
-    for (int q = threadIdx.x; q < S::L; q += kThreads) Ts[q] = a.T[(size_t)U.c * S::L + q];
-    rl.commit(R, lane);
-  }
+  RollQuad<S> xq;
+  xq.load(a.x + U.base, U, g, lane);
+  for (int q = threadIdx.x; q < S::L; q += kThreads) Ts[q] = a.T[(size_t)U.c * S::L + q];
+  for (int q = threadIdx.x; q <= S::CMAX; q += kThreads) Ts[S::LP + q] = 0.f;
   __syncthreads();
-  v4f acc[S::RT];
-  if (g.gm == 0)
-    contract<S, false, 0, S::RT>(Ts, R, lane, acc);
-  else
-    contract_masked<S, false>(Ts, R, lane, g.gm, acc);
-  roll_store<S>(a.y, a.zsave, U, g, acc, lane);
+  // thirds of the row tiles (5, 4, 4): each is stored while the next one is contracted
+  {
+    v4f acc[5];
+    contract_roll<S, false, S::LP, 0, 5>(Ts, xq.v, lane, g.gm, acc);
+    roll_store<S, 0, 5>(a.y, a.zsave, U, g, acc, lane);
+  }
+  {
+    v4f acc[4];
+    contract_roll<S, false, S::LP, 5, 4>(Ts, xq.v, lane, g.gm, acc);
+    roll_store<S, 5, 4>(a.y, a.zsave, U, g, acc, lane);
+  }
+  {
+    v4f acc[4];
+    contract_roll<S, false, S::LP, 9, 4>(Ts, xq.v, lane, g.gm, acc);
+    roll_store<S, 9, 4>(a.y, a.zsave, U, g, acc, lane);
+  }
 }
 
 // Promote the fp32 row-pair chains of one window class to fp64; with the columns split only the
@@ -1187,24 +1220,38 @@ k_roll_bwd(FastArgs a) {
   const int u = blockIdx.x;
   const Unit U = unit_of<S>(a, u);
   const RollGeo g = roll_geo<S>(a, wave);
-  {
-    RollLoad<S> rl;
-    rl.issue(a.dy + U.base, U, g, lane);
-    for (int q = threadIdx.x; q < S::L; q += kThreads) Ts[q] = a.T[(size_t)U.c * S::L + q];
-    rl.commit(R, lane);
-  }
+  // G of the wave's windows in registers; during dX the zeros of the masked operands sit at the
+  // start of the regions, which take G (for the table gradient) only after dX
+  constexpr int ZOFF = bwd_tsz<S, false>();
+  static_assert(S::CMAX < S::RSZ, "zeros inside the first region");
+  RollQuad<S> gq;
+  gq.load(a.dy + U.base, U, g, lane);
+  for (int q = threadIdx.x; q < S::L; q += kThreads) Ts[q] = a.T[(size_t)U.c * S::L + q];
+  for (int q = threadIdx.x; q <= S::CMAX; q += kThreads) Ts[ZOFF + q] = 0.f;
   __syncthreads();
 
-  if (a.want_dx) {
-    v4f acc[S::RT];
-    if (g.gm == 0)
-      contract<S, true, 0, S::RT>(Ts, R, lane, acc);
-    else
-      contract_masked<S, true>(Ts, R, lane, g.gm, acc);
-    roll_store<S>(a.dx, nullptr, U, g, acc, lane);
+  if (a.want_dx) {  // thirds of the row tiles, as in the forward
+    {
+      v4f acc[5];
+      contract_roll<S, true, ZOFF, 0, 5>(Ts, gq.v, lane, g.gm, acc);
+      roll_store<S, 0, 5>(a.dx, nullptr, U, g, acc, lane);
+    }
+    {
+      v4f acc[4];
+      contract_roll<S, true, ZOFF, 5, 4>(Ts, gq.v, lane, g.gm, acc);
+      roll_store<S, 5, 4>(a.dx, nullptr, U, g, acc, lane);
+    }
+    {
+      v4f acc[4];
+      contract_roll<S, true, ZOFF, 9, 4>(Ts, gq.v, lane, g.gm, acc);
+      roll_store<S, 9, 4>(a.dx, nullptr, U, g, acc, lane);
+    }
   }
+  if (!a.want_dT) return;
+  __syncthreads();  // every wave is done with the zeros in the first region
+  gq.commit(R, lane);
 
-  if (a.want_dT) {
+  {
     double acc64[8][4];
 #pragma unroll
     for (int j = 0; j < 8; ++j)
@@ -1275,7 +1322,7 @@ k_roll_bwd(FastArgs a) {
     };
     load_chunk(stgA, 0);
     load_chunk(stgB, 1);
-    __syncthreads();  // every wave is done with the table (dX)
+    __syncthreads();  // every wave is done with the table (dX) and its G is in its region
     for (int ci = 0; ci < 16; ci += 2) {
       step(stgA, ci);
       step(stgB, ci + 1);
@@ -1362,7 +1409,7 @@ static_assert(lds_fits(bwd_lds<S14, true>(), 2) && lds_fits(bwd_lds<S28, true>()
                   lds_fits(bwd_lds<S56, true>(), 2),
               "two hierarchical backward workgroups per CU");
 template <class S>
-constexpr int roll_fwd_lds() { return (S::LP + 4 * S::RSZ) * 4; }
+constexpr int roll_fwd_lds() { return roll_fwd_floats<S>() * 4; }
 static_assert(lds_fits(roll_fwd_lds<S28>(), 3) && lds_fits(bwd_lds<S28>(), 3),
               "three rolled-grid workgroups per CU");
 
