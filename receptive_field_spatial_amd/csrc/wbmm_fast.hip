@@ -1138,39 +1138,113 @@ __device__ __forceinline__ void roll_store(float* o, float* o2, const Unit& U, c
 
 // Forward on the offset grid: z = masked product of each wave's windows, written to y (and
 // z_save); the 3 x 3 mix runs afterwards on the whole map.
-// LDS: the table, then CMAX + 1 zeros for the masked operands.
-template <class S>
-constexpr int roll_fwd_floats() { return S::LP + (S::CMAX + 4) / 4 * 4; }
+// The unit's 16 pre-mix maps in LDS (map coordinates) -> y (3 x 3 mix, or a copy) and z_save.
+// A thread walks an image column down the 28 rows with a 3 x 3 register window (3 LDS reads per
+// pixel; the neighbour columns' reads are clamped to the own column at the image border and
+// selected away); consecutive threads own consecutive columns, so the stores are row runs.
+template <class S, bool MIX>
+__device__ __forceinline__ void roll_epilogue(const FastArgs& a, const float* Z, const Unit& U) {
+  float w9[9];
+#pragma unroll
+  for (int q = 0; q < 9; ++q) w9[q] = 0.f;
+  if constexpr (MIX) {
+#pragma unroll
+    for (int q = 0; q < 9; ++q) w9[q] = a.mixw[(size_t)U.c * 9 + q];
+  }
+  for (int col = threadIdx.x; col < 16 * S::IW; col += kThreads) {
+    const int n = col / S::IW, v = col % S::IW;
+    if (n >= U.nimg) break;  // columns are image-major: the rest are past the batch too
+    const float* zc = Z + n * S::PLANE + v;
+    const int dl = v > 0 ? -1 : 0, dr = v < S::IW - 1 ? 1 : 0;
+    const size_t ob = U.base + (size_t)n * U.cp + v;
+    float up[3] = {0.f, 0.f, 0.f}, cur[3], dn[3];
+    cur[0] = dl ? zc[dl] : 0.f;
+    cur[1] = zc[0];
+    cur[2] = dr ? zc[dr] : 0.f;
+#pragma unroll
+    for (int h = 0; h < S::IH; ++h) {
+      if (h + 1 < S::IH) {
+        const float* zr = zc + (h + 1) * S::IW;
+        dn[0] = dl ? zr[dl] : 0.f;
+        dn[1] = zr[0];
+        dn[2] = dr ? zr[dr] : 0.f;
+      } else {
+        dn[0] = dn[1] = dn[2] = 0.f;
+      }
+      const size_t o = ob + (size_t)h * S::IW;
+      if constexpr (MIX) {
+        float y = 0.f;
+#pragma unroll
+        for (int t = 0; t < 3; ++t) y = fmaf(w9[t], up[t], y);
+#pragma unroll
+        for (int t = 0; t < 3; ++t) y = fmaf(w9[3 + t], cur[t], y);
+#pragma unroll
+        for (int t = 0; t < 3; ++t) y = fmaf(w9[6 + t], dn[t], y);
+        a.y[o] = y;
+      } else {
+        a.y[o] = cur[1];
+      }
+      if (a.zsave) a.zsave[o] = cur[1];
+#pragma unroll
+      for (int t = 0; t < 3; ++t) {
+        up[t] = cur[t];
+        cur[t] = dn[t];
+      }
+    }
+  }
+}
 
+// Accumulators of row tiles [T0, T0 + NT) into the unit's map staging (map coordinates).
+template <class S, int T0, int NT>
+__device__ __forceinline__ void roll_stage(float* Z, const RollGeo& g, const v4f (&acc)[NT],
+                                           int lane) {
+  const int n = lane & 15, g4 = 4 * (lane >> 4);
+  float* zb = Z + n * S::PLANE;
+#pragma unroll
+  for (int t = 0; t < NT; ++t)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int c0 = 16 * (T0 + t) + r;  // p = c0 + g4
+      if (c0 + g4 >= S::D) continue;
+      const int wr = (c0 % S::WS) + g4 >= S::WS ? 1 : 0;
+      const int py = c0 / S::WS + wr, px = (c0 % S::WS) + g4 - wr * S::WS;
+      zb[wrap(py + g.cy, S::IH) * S::IW + wrap(px + g.cx, S::IW)] = acc[t][r];
+    }
+}
+
+// LDS: the table, then the unit's 16 pre-mix maps; during the products CMAX + 1 zeros for the
+// masked operands sit at the end of the map staging, which is written only after every wave's
+// product.
 template <class S>
+constexpr int roll_fwd_floats() { return S::LP + 16 * S::PLANE; }
+
+template <class S, bool MIX>
 __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3, 8)))
 k_roll_fwd(FastArgs a) {
   extern __shared__ __attribute__((aligned(16))) float smem_f[];
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   float* Ts = smem_f;
+  float* Z = smem_f + S::LP;
+  constexpr int ZOFF = S::LP + 16 * S::PLANE - (S::CMAX + 4) / 4 * 4;
+  static_assert(ZOFF >= S::LP, "zeros inside the staging");
   const Unit U = unit_of<S>(a, blockIdx.x);
   const RollGeo g = roll_geo<S>(a, wave);
   RollQuad<S> xq;
   xq.load(a.x + U.base, U, g, lane);
   for (int q = threadIdx.x; q < S::L; q += kThreads) Ts[q] = a.T[(size_t)U.c * S::L + q];
-  for (int q = threadIdx.x; q <= S::CMAX; q += kThreads) Ts[S::LP + q] = 0.f;
+  for (int q = threadIdx.x; q <= S::CMAX; q += kThreads) Ts[ZOFF + q] = 0.f;
   __syncthreads();
-  // thirds of the row tiles (5, 4, 4): each is stored while the next one is contracted
-  {
-    v4f acc[5];
-    contract_roll<S, false, S::LP, 0, 5>(Ts, xq.v, lane, g.gm, acc);
-    roll_store<S, 0, 5>(a.y, a.zsave, U, g, acc, lane);
-  }
-  {
-    v4f acc[4];
-    contract_roll<S, false, S::LP, 5, 4>(Ts, xq.v, lane, g.gm, acc);
-    roll_store<S, 5, 4>(a.y, a.zsave, U, g, acc, lane);
-  }
-  {
-    v4f acc[4];
-    contract_roll<S, false, S::LP, 9, 4>(Ts, xq.v, lane, g.gm, acc);
-    roll_store<S, 9, 4>(a.y, a.zsave, U, g, acc, lane);
-  }
+  // thirds of the row tiles (5, 4, 4), held until every wave is past the zeros
+  v4f acc0[5], acc1[4], acc2[4];
+  contract_roll<S, false, ZOFF, 0, 5>(Ts, xq.v, lane, g.gm, acc0);
+  contract_roll<S, false, ZOFF, 5, 4>(Ts, xq.v, lane, g.gm, acc1);
+  contract_roll<S, false, ZOFF, 9, 4>(Ts, xq.v, lane, g.gm, acc2);
+  __syncthreads();
+  roll_stage<S, 0, 5>(Z, g, acc0, lane);
+  roll_stage<S, 5, 4>(Z, g, acc1, lane);
+  roll_stage<S, 9, 4>(Z, g, acc2, lane);
+  __syncthreads();
+  roll_epilogue<S, MIX>(a, Z, U);
 }
 
 // Promote the fp32 row-pair chains of one window class to fp64; with the columns split only the
@@ -1481,19 +1555,22 @@ bool fast_roll_backward_ok(const BwdRequest& r) {
   return r.T && !r.M && !r.Tsub && roll_shape_ok(r.B, r.C, r.H, r.W, r.w, r.layout, r.oy, r.ox);
 }
 
-// out: the product (y, or the pre-mix map); out2: a second copy or null.
-hipError_t launch_forward_fast_roll(const FwdRequest& r, float* out, float* out2, hipStream_t st) {
+// The layer on the offset grid: y (with the 3 x 3 mix applied on chip when there is one) and
+// z_save (the pre-mix map), both optional-free: y is always written.
+hipError_t launch_forward_fast_roll(const FwdRequest& r, hipStream_t st) {
   if (!fast_roll_forward_ok(r)) return hipErrorInvalidValue;
   FastArgs a{};
   a.B = r.B;
   a.C = r.C;
   a.x = (const float*)r.x;
   a.T = (const float*)r.T;
-  a.y = out;
-  a.zsave = out2;
+  a.mixw = r.mixw;
+  a.y = (float*)r.y;
+  a.zsave = (float*)r.zsave;
   a.roy = r.oy;
   a.rox = r.ox;
-  return launch_ls<S28>(k_roll_fwd<S28>, roll_fwd_lds<S28>(), a, st);
+  return r.mixw ? launch_ls<S28>(k_roll_fwd<S28, true>, roll_fwd_lds<S28>(), a, st)
+                : launch_ls<S28>(k_roll_fwd<S28, false>, roll_fwd_lds<S28>(), a, st);
 }
 
 // Table-gradient partials of the rolled backward: one fp64 row of L per unit.

@@ -155,10 +155,11 @@ static bool fast_bf16_mix_ok(const FwdRequest& r) {
 
 size_t forward_workspace(const FwdRequest& r) {
   if (hier_general(r)) return hier_forward_workspace(r);
+  if (fast_roll_forward_ok(r)) return 0;  // the mix on chip
   // the fast kernels that leave the mix to a pass of its own: with the mix, the pre-mix map goes
   // to z_save or here
   if (fast_cm_forward_ok(r) || fast_f32_w28_forward_ok(r) || fast_f32_w7_forward_ok(r) ||
-      fast_roll_forward_ok(r) || (!fast_forward_ok(r) && fast_tab_forward_ok(r)))
+      (!fast_forward_ok(r) && fast_tab_forward_ok(r)))
     return r.mixw && !r.zsave ? (size_t)r.B * r.C * r.H * r.W * 4 : 0;
   if (repack_forward_ok(r)) return repack_forward_workspace(r);
   if (fast_bf16_mix_ok(r)) return r.zsave ? 0 : (size_t)r.B * r.C * r.H * r.W * 2;
@@ -184,13 +185,8 @@ hipError_t launch_forward(const FwdRequest& r, hipStream_t st) {
   }
   if (fast_forward_ok(r)) return launch_forward_fast(r, st);  // folds a sub-table when w = 2s
   if (!r.Tsub && fast_bf16_forward_ok(r)) return launch_forward_fast_bf16(r, st);
-  if (fast_roll_forward_ok(r)) {  // grid offset 0 or 7 on 28 x 28 maps: the rolled map
-    if (!r.mixw) return launch_forward_fast_roll(r, (float*)r.y, (float*)r.zsave, st);
-    float* z = (float*)(r.zsave ? r.zsave : r.ws);
-    hipError_t e = launch_forward_fast_roll(r, z, nullptr, st);
-    if (e != hipSuccess) return e;
-    return launch_mix_fwd_f32_route(z, r.mixw, (float*)r.y, r.B, r.C, r.H, r.W, st);
-  }
+  // grid offset 0 or 7 on 28 x 28 maps: the rolled map, the mix on chip
+  if (fast_roll_forward_ok(r)) return launch_forward_fast_roll(r, st);
   if (fast_tab_forward_ok(r)) {  // fp32 w = 14 from the table, any map and grid offset
     if (!r.mixw) return launch_forward_fast_tab(r, (float*)r.y, (float*)r.zsave, st);
     float* z = (float*)(r.zsave ? r.zsave : r.ws);

@@ -248,7 +248,8 @@ def test_shifted_validation(lib):
 def test_shifted_workspace_covers_the_repacked_maps(lib):
     """w = 14 offset grids on NCHW maps: B=64 at 28x28 with offset (5, 9) has 9 windows per image,
     576 windows = 144 repacked 28x28 images of 2x2 windows. The fp32 forward reads the offset
-    grid directly (with the mix and no z_save buffer it needs the image-space z); the bf16 forward
+    grid directly (with the mix and no z_save buffer it needs the image-space z, except on the
+    rolled map, which applies the mix on chip); the bf16 forward
     without the mix runs on repacked X and z (bf16: together the bytes of one fp32 repacked map);
     the backward holds repacked G, X and dX, and with the mix the image-space G. Offsets of 0 or
     7 on 28x28 maps run on the rolled map instead: the backward from the table then holds only
@@ -261,8 +262,10 @@ def test_shifted_workspace_covers_the_repacked_maps(lib):
     for oy, ox in ((5, 9), (7, 7)):
         fwd = lib.wbmm_forward_shifted_workspace_bytes(B, C, 28, 28, 14, oy, ox, 0, 0, 0)
         assert fwd >= rep
-        assert lib.wbmm_forward_shifted_workspace_bytes(B, C, 28, 28, 14, oy, ox, 0, 1, 0) >= img
         assert lib.wbmm_forward_shifted_workspace_bytes(B, C, 28, 28, 14, oy, ox, 0, 1, 1) < img
+    assert lib.wbmm_forward_shifted_workspace_bytes(B, C, 28, 28, 14, 5, 9, 0, 1, 0) >= img
+    # the rolled-map forward applies the mix on chip: no image-space z without z_save
+    assert lib.wbmm_forward_shifted_workspace_bytes(B, C, 28, 28, 14, 7, 7, 0, 1, 0) < img
     bwd = lib.wbmm_backward_shifted_workspace_bytes(B, C, 28, 28, 14, 5, 9, 0, 0)
     assert bwd >= 3 * rep
     assert lib.wbmm_backward_shifted_workspace_bytes(B, C, 28, 28, 14, 5, 9, 0, 1) >= bwd + img
