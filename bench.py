@@ -57,7 +57,7 @@ KERNEL_FILES = {"k_fwd_ws": "wbmm_fast.hip", "k_bwd_ls": "wbmm_fast.hip", "k_fwd
                 "k_wbmm_fwd": "wbmm_fwd.hip", "k_wbmm_bwd": "wbmm_bwd.hip",
                 "k_fwd_f32_w7": "wbmm_fast7.hip", "k_fwd_f32_w28": "wbmm_fast28.hip",
                 "k_fwd_tab": "wbmm_fasttab.hip", "k_mix_direct": "wbmm_aux.hip",
-                "k_roll_fwd": "wbmm_fast.hip", "k_roll_bwd": "wbmm_fast.hip"}
+                "k_roll_fwd": "wbmm_fastroll.hip", "k_roll_bwd": "wbmm_fastroll.hip"}
 HOST_HEADERS = ("wbmm_launch.hpp",)
 
 

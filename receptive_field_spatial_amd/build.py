@@ -14,7 +14,7 @@ PKG_DIR = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(PKG_DIR, "csrc")
 OBJ_DIR = os.path.join(PKG_DIR, "_build")
 LIB_PATH = os.path.join(PKG_DIR, "libwbmm.so")
-SOURCES = ["wbmm_api.cpp", "wbmm_aux.hip", "wbmm_fwd.hip", "wbmm_bwd.hip", "wbmm_fast.hip",
+SOURCES = ["wbmm_api.cpp", "wbmm_aux.hip", "wbmm_fwd.hip", "wbmm_bwd.hip", "wbmm_fast.hip", "wbmm_fastroll.hip",
            "wbmm_fastbf.hip", "wbmm_dw.hip",
            "wbmm_probe.hip", "wbmm_bwdbf.hip", "wbmm_repack.hip", "wbmm_fastcm.hip",
            "wbmm_fast28.hip", "wbmm_fast7.hip", "wbmm_fasttab.hip", "wbmm_hiergen.cpp",
