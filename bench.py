@@ -10,8 +10,9 @@ fixed-order reduction kernel that finishes dT and dWmix.
 Prints ONE JSON line on stdout; diagnostics go to stderr.
 
   python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
-      NAME: train_w14 (default), train_w14_hier (sub-window fold + dT_sub), train_w14_shift
-      (interleaved window grid), train_w14_bf16 / train_w14_bf16_mix (bf16 maps), stage1_w14,
+      NAME: train_w14 (default), train_w14_hier (sub-window fold + dT_sub), train_w14_shift /
+      train_stage1_shift (interleaved window grid at 28x28 / 56x56), train_w14_bf16 /
+      train_w14_bf16_mix (bf16 maps), stage1_w14,
       bf16_w7 / bf16_w14 / bf16_w28, highres_w14, tiny_w7 (see receptive_field_spatial_amd/synth.py)
   python bench.py --workload stage1_w14 --cached   # forward on M cached in HBM
   python bench.py --copy-calibration        # plain device copy for HBM counter scaling

@@ -1,5 +1,5 @@
 // Fast fp32 WBMM forward and backward on a window grid offset by half a window (w = 14, offsets
-// 0 or 7, NCHW 28 x 28 maps), through the rolled map.
+// 0 or 7, NCHW 28 x 28 and 56 x 56 maps), through the rolled map.
 #include "wbmm_fast.hpp"
 
 namespace wbmm {
@@ -36,6 +36,30 @@ __device__ __forceinline__ RollGeo roll_geo(const FastArgs& a, int k) {
 }
 __device__ __forceinline__ int wrap(int v, int n) { return v >= n ? v - n : v; }
 
+// A unit is 16 images of one channel and 4 window positions: all of a 28 x 28 map's, a quarter
+// of a 56 x 56 map's (units per channel: ceil(B / 16) image groups x NWIN / 4 position groups,
+// in a.groups). k0: the unit's first window position; wave k holds position k0 + k.
+template <class S>
+__device__ __forceinline__ Unit roll_unit(const FastArgs& a, int u, int& k0) {
+  constexpr int NPG = S::NWIN / 4;
+  static_assert(S::NWIN % 4 == 0, "whole position groups");
+  Unit U;
+  U.c = u / a.groups;
+  const int rem = u - U.c * a.groups, ig = rem / NPG;
+  k0 = 4 * (rem - ig * NPG);
+  const int uimg0 = 16 * ig;
+  U.base = ((size_t)uimg0 * a.C + U.c) * S::PLANE;
+  U.cp = a.C * S::PLANE;
+  const int left = a.B - uimg0;
+  U.nimg = left < 16 ? left : 16;
+  return U;
+}
+template <class S>
+int roll_groups(int B) { return (B + 15) / 16 * (S::NWIN / 4); }
+// whole images in one unit: the forward applies the 3 x 3 mix on chip
+template <class S>
+constexpr bool roll_staged() { return S::NWIN == 4; }
+
 typedef float f4a4 __attribute__((ext_vector_type(4), aligned(4)));
 typedef float f3a4 __attribute__((ext_vector_type(3), aligned(4)));
 typedef float f2a4 __attribute__((ext_vector_type(2), aligned(4)));
@@ -46,7 +70,7 @@ typedef float f2a4 __attribute__((ext_vector_type(2), aligned(4)));
 // batch are zero. Pixel s of the quadrant is the lane's MFMA operand of K step s.
 template <class S>
 struct RollQuad {
-  static_assert(S::QW == 7 && S::NWIN == 4 && S::IPW == 4, "28 x 28 maps of 14 x 14 windows");
+  static_assert(S::QW == 7, "14 x 14 windows");
   float v[S::KQ];
   __device__ __forceinline__ void load(const float* __restrict__ src, const Unit& U,
                                        const RollGeo& g, int lane) {
@@ -246,8 +270,12 @@ __device__ __forceinline__ void roll_stage(float* Z, const RollGeo& g, const v4f
 // LDS: the table, then the unit's 16 pre-mix maps; during the products CMAX + 1 zeros for the
 // masked operands sit at the end of the map staging, which is written only after every wave's
 // product.
+// (56 x 56 maps: the table and the zeros only; the products are stored straight from the
+// accumulators and the mix runs as a pass of its own.)
 template <class S>
-constexpr int roll_fwd_floats() { return S::LP + 16 * S::PLANE; }
+constexpr int roll_fwd_floats() {
+  return roll_staged<S>() ? S::LP + 16 * S::PLANE : S::LP + (S::CMAX + 4) / 4 * 4;
+}
 
 template <class S, bool MIX>
 __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3, 8)))
@@ -255,27 +283,46 @@ k_roll_fwd(FastArgs a) {
   extern __shared__ __attribute__((aligned(16))) float smem_f[];
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   float* Ts = smem_f;
-  float* Z = smem_f + S::LP;
-  constexpr int ZOFF = S::LP + 16 * S::PLANE - (S::CMAX + 4) / 4 * 4;
-  static_assert(ZOFF >= S::LP, "zeros inside the staging");
-  const Unit U = unit_of<S>(a, blockIdx.x);
-  const RollGeo g = roll_geo<S>(a, wave);
+  constexpr int ZOFF = roll_staged<S>() ? S::LP + 16 * S::PLANE - (S::CMAX + 4) / 4 * 4 : S::LP;
+  static_assert(ZOFF >= S::LP && (roll_staged<S>() || !MIX), "zeros after the table");
+  int k0;
+  const Unit U = roll_unit<S>(a, blockIdx.x, k0);
+  const RollGeo g = roll_geo<S>(a, k0 + wave);
   RollQuad<S> xq;
   xq.load(a.x + U.base, U, g, lane);
   for (int q = threadIdx.x; q < S::L; q += kThreads) Ts[q] = a.T[(size_t)U.c * S::L + q];
   for (int q = threadIdx.x; q <= S::CMAX; q += kThreads) Ts[ZOFF + q] = 0.f;
   __syncthreads();
-  // thirds of the row tiles (5, 4, 4), held until every wave is past the zeros
-  v4f acc0[5], acc1[4], acc2[4];
-  contract_roll<S, false, ZOFF, 0, 5>(Ts, xq.v, lane, g.gm, acc0);
-  contract_roll<S, false, ZOFF, 5, 4>(Ts, xq.v, lane, g.gm, acc1);
-  contract_roll<S, false, ZOFF, 9, 4>(Ts, xq.v, lane, g.gm, acc2);
-  __syncthreads();
-  roll_stage<S, 0, 5>(Z, g, acc0, lane);
-  roll_stage<S, 5, 4>(Z, g, acc1, lane);
-  roll_stage<S, 9, 4>(Z, g, acc2, lane);
-  __syncthreads();
-  roll_epilogue<S, MIX>(a, Z, U);
+  if constexpr (roll_staged<S>()) {
+    // thirds of the row tiles (5, 4, 4), held until every wave is past the zeros
+    float* Z = smem_f + S::LP;
+    v4f acc0[5], acc1[4], acc2[4];
+    contract_roll<S, false, ZOFF, 0, 5>(Ts, xq.v, lane, g.gm, acc0);
+    contract_roll<S, false, ZOFF, 5, 4>(Ts, xq.v, lane, g.gm, acc1);
+    contract_roll<S, false, ZOFF, 9, 4>(Ts, xq.v, lane, g.gm, acc2);
+    __syncthreads();
+    roll_stage<S, 0, 5>(Z, g, acc0, lane);
+    roll_stage<S, 5, 4>(Z, g, acc1, lane);
+    roll_stage<S, 9, 4>(Z, g, acc2, lane);
+    __syncthreads();
+    roll_epilogue<S, MIX>(a, Z, U);
+  } else {  // each third stored while the next is contracted
+    {
+      v4f acc[5];
+      contract_roll<S, false, ZOFF, 0, 5>(Ts, xq.v, lane, g.gm, acc);
+      roll_store<S, 0, 5>(a.y, a.zsave, U, g, acc, lane);
+    }
+    {
+      v4f acc[4];
+      contract_roll<S, false, ZOFF, 5, 4>(Ts, xq.v, lane, g.gm, acc);
+      roll_store<S, 5, 4>(a.y, a.zsave, U, g, acc, lane);
+    }
+    {
+      v4f acc[4];
+      contract_roll<S, false, ZOFF, 9, 4>(Ts, xq.v, lane, g.gm, acc);
+      roll_store<S, 9, 4>(a.y, a.zsave, U, g, acc, lane);
+    }
+  }
 }
 
 // Promote the fp32 row-pair chains of one window class to fp64; with the columns split only the
@@ -323,8 +370,9 @@ k_roll_bwd(FastArgs a) {
   float* regions = smem_f + bwd_tsz<S, false>();
   float* R = regions + wave * S::RSZ;
   const int u = blockIdx.x;
-  const Unit U = unit_of<S>(a, u);
-  const RollGeo g = roll_geo<S>(a, wave);
+  int k0;
+  const Unit U = roll_unit<S>(a, u, k0);
+  const RollGeo g = roll_geo<S>(a, k0 + wave);
   // G of the wave's windows in registers; during dX the zeros of the masked operands sit at the
   // start of the regions, which take G (for the table gradient) only after dX
   constexpr int ZOFF = bwd_tsz<S, false>();
@@ -374,7 +422,7 @@ k_roll_bwd(FastArgs a) {
     const int maxoff = (U.nimg - 1) * U.cp + S::PLANE - 1;
     float stgA[EPT], stgB[EPT];
     auto load_chunk = [&](float (&stg)[EPT], int ci) {
-      const RollGeo cg = roll_geo<S>(a, ci >> 2);
+      const RollGeo cg = roll_geo<S>(a, k0 + (ci >> 2));
       const int cbase = 4 * (ci & 3) * U.cp;
       const int tid = opaque_lane(threadIdx.x);
 #pragma unroll
@@ -402,7 +450,7 @@ k_roll_bwd(FastArgs a) {
       }
       __syncthreads();
       load_chunk(stg, ci + 2 < 16 ? ci + 2 : 15);
-      const RollGeo cg = roll_geo<S>(a, ci >> 2);
+      const RollGeo cg = roll_geo<S>(a, k0 + (ci >> 2));
       const bool band = (cg.gm & 2) != 0, split = (cg.gm & 1) != 0;
       const int n0 = 16 * (ci >> 2) + 4 * (ci & 3);
       const bool flush = (ci & 3) == 3;
@@ -444,12 +492,25 @@ k_roll_bwd(FastArgs a) {
   }
 }
 
-static_assert(lds_fits((S28::LP + 16 * S28::PLANE) * 4, 3) && lds_fits(bwd_lds<S28>(), 3),
+static_assert(lds_fits(roll_fwd_floats<S28>() * 4, 3) && lds_fits(bwd_lds<S28>(), 3) &&
+                  lds_fits(roll_fwd_floats<S56>() * 4, 3) && lds_fits(bwd_lds<S56>(), 3),
               "three rolled-grid workgroups per CU");
 
-// The offset grid on the rolled map: fp32, w = 14, NCHW 28 x 28, offsets 0 or 7 (not both 0).
+namespace {
+// One workgroup of 4 waves per unit.
+template <class S, class Fn>
+hipError_t launch_roll(Fn fn, int lds, FastArgs a, hipStream_t st) {
+  a.groups = roll_groups<S>(a.B);
+  hipError_t e = hipFuncSetAttribute((const void*)fn, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+  if (e != hipSuccess) return e;
+  return launch_main(fn, dim3(a.C * a.groups), dim3(kThreads), lds, st, a);
+}
+}  // namespace
+
+// The offset grid on the rolled map: fp32, w = 14, NCHW 28 x 28 or 56 x 56, offsets 0 or 7 (not
+// both 0).
 static bool roll_shape_ok(int B, int C, int H, int W, int w, int layout, int oy, int ox) {
-  return w == 14 && layout == 0 && H == 28 && W == 28 && (oy == 0 || oy == 7) &&
+  return w == 14 && layout == 0 && H == W && (H == 28 || H == 56) && (oy == 0 || oy == 7) &&
          (ox == 0 || ox == 7) && (oy != 0 || ox != 0) && B >= 1 && C >= 1 &&
          offsets_fit(C, H, W);
 }
@@ -463,8 +524,15 @@ bool fast_roll_backward_ok(const BwdRequest& r) {
   return r.T && !r.M && !r.Tsub && roll_shape_ok(r.B, r.C, r.H, r.W, r.w, r.layout, r.oy, r.ox);
 }
 
-// The layer on the offset grid: y (with the 3 x 3 mix applied on chip when there is one) and
-// z_save (the pre-mix map), both optional-free: y is always written.
+// 56 x 56 maps with the mix and no z_save: the pre-mix map between the product and the mix pass.
+size_t fast_roll_forward_workspace(const FwdRequest& r) {
+  return fast_roll_forward_ok(r) && r.H == 56 && r.mixw && !r.zsave
+             ? (size_t)r.B * r.C * r.H * r.W * sizeof(float)
+             : 0;
+}
+
+// The layer on the offset grid: y (the 3 x 3 mix applied on chip on 28 x 28 maps, as a pass of
+// its own after the product on 56 x 56 ones) and z_save (the pre-mix map).
 hipError_t launch_forward_fast_roll(const FwdRequest& r, hipStream_t st) {
   if (!fast_roll_forward_ok(r)) return hipErrorInvalidValue;
   FastArgs a{};
@@ -477,15 +545,25 @@ hipError_t launch_forward_fast_roll(const FwdRequest& r, hipStream_t st) {
   a.zsave = (float*)r.zsave;
   a.roy = r.oy;
   a.rox = r.ox;
-  return r.mixw ? launch_ls<S28>(k_roll_fwd<S28, true>, (roll_fwd_floats<S28>() * 4), a, st)
-                : launch_ls<S28>(k_roll_fwd<S28, false>, (roll_fwd_floats<S28>() * 4), a, st);
+  if (r.H == 28)
+    return r.mixw ? launch_roll<S28>(k_roll_fwd<S28, true>, roll_fwd_floats<S28>() * 4, a, st)
+                  : launch_roll<S28>(k_roll_fwd<S28, false>, roll_fwd_floats<S28>() * 4, a, st);
+  if (!r.mixw) return launch_roll<S56>(k_roll_fwd<S56, false>, roll_fwd_floats<S56>() * 4, a, st);
+  float* z = (float*)(r.zsave ? r.zsave : r.ws);
+  a.mixw = nullptr;
+  a.y = z;
+  a.zsave = nullptr;
+  hipError_t e = launch_roll<S56>(k_roll_fwd<S56, false>, roll_fwd_floats<S56>() * 4, a, st);
+  if (e != hipSuccess) return e;
+  return launch_mix_fwd_f32_route(z, r.mixw, (float*)r.y, r.B, r.C, r.H, r.W, st);
 }
 
 // Table-gradient partials of the rolled backward: one fp64 row of L per unit.
 size_t fast_roll_backward_workspace(const BwdRequest& r) {
   if (!fast_roll_backward_ok(r)) return 0;
   const size_t L = (size_t)(2 * r.w - 1) * (2 * r.w - 1);
-  return ((size_t)r.C * groups<S28>(r.B) * L * 8 + 255) / 256 * 256;
+  const int g = r.H == 28 ? roll_groups<S28>(r.B) : roll_groups<S56>(r.B);
+  return ((size_t)r.C * g * L * 8 + 255) / 256 * 256;
 }
 
 // dy: the map gradient of the product (the mix adjoint, if any, already applied).
@@ -505,10 +583,13 @@ hipError_t launch_backward_fast_roll(const BwdRequest& r, hipStream_t st) {
   a.roy = r.oy;
   a.rox = r.ox;
   if (!a.want_dx && !a.want_dT) return hipSuccess;
-  hipError_t e = launch_ls<S28>(k_roll_bwd<S28>, bwd_lds<S28>(), a, st);
+  const bool s28 = r.H == 28;
+  hipError_t e = s28 ? launch_roll<S28>(k_roll_bwd<S28>, bwd_lds<S28>(), a, st)
+                     : launch_roll<S56>(k_roll_bwd<S56>, bwd_lds<S56>(), a, st);
   if (e != hipSuccess || !a.want_dT) return e;
   const int L = (2 * r.w - 1) * (2 * r.w - 1);
-  return launch_bwd_reduce(a.partT, nullptr, groups<S28>(r.B), r.C, L, r.dT, nullptr, st);
+  return launch_bwd_reduce(a.partT, nullptr, s28 ? roll_groups<S28>(r.B) : roll_groups<S56>(r.B),
+                           r.C, L, r.dT, nullptr, st);
 }
 
 }  // namespace wbmm

@@ -155,7 +155,7 @@ static bool fast_bf16_mix_ok(const FwdRequest& r) {
 
 size_t forward_workspace(const FwdRequest& r) {
   if (hier_general(r)) return hier_forward_workspace(r);
-  if (fast_roll_forward_ok(r)) return 0;  // the mix on chip
+  if (fast_roll_forward_ok(r)) return fast_roll_forward_workspace(r);
   // the fast kernels that leave the mix to a pass of its own: with the mix, the pre-mix map goes
   // to z_save or here
   if (fast_cm_forward_ok(r) || fast_f32_w28_forward_ok(r) || fast_f32_w7_forward_ok(r) ||
@@ -185,7 +185,7 @@ hipError_t launch_forward(const FwdRequest& r, hipStream_t st) {
   }
   if (fast_forward_ok(r)) return launch_forward_fast(r, st);  // folds a sub-table when w = 2s
   if (!r.Tsub && fast_bf16_forward_ok(r)) return launch_forward_fast_bf16(r, st);
-  // grid offset 0 or 7 on 28 x 28 maps: the rolled map, the mix on chip
+  // grid offset 0 or 7 on 28 x 28 and 56 x 56 maps: the rolled map
   if (fast_roll_forward_ok(r)) return launch_forward_fast_roll(r, st);
   if (fast_tab_forward_ok(r)) {  // fp32 w = 14 from the table, any map and grid offset
     if (!r.mixw) return launch_forward_fast_tab(r, (float*)r.y, (float*)r.zsave, st);

@@ -87,6 +87,7 @@ bool offsets_fit(int C, int H, int W);
 // the mix in the forward) on the fast kernels: the grid's windows are gathered into whole 28x28
 // images in the workspace and the results put back.
 bool fast_roll_forward_ok(const FwdRequest& r);
+size_t fast_roll_forward_workspace(const FwdRequest& r);
 hipError_t launch_forward_fast_roll(const FwdRequest& r, hipStream_t st);
 bool fast_roll_backward_ok(const BwdRequest& r);
 size_t fast_roll_backward_workspace(const BwdRequest& r);

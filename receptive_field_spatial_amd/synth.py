@@ -89,6 +89,10 @@ WORKLOADS: Dict[str, Workload] = {
     "train_w14_shift": Workload("train_w14_shift", B=64, C=192, H=28, W=28, w=14, mix=True,
                                 backward=True, shift=7,
                                 note="fp32 training step of an interleaved layer (grid offset 7)"),
+    "train_stage1_shift": Workload("train_stage1_shift", B=32, C=96, H=56, W=56, w=14, mix=True,
+                                   backward=True, shift=7,
+                                   note="fp32 training step of an interleaved layer at the stage-1 "
+                                        "map size (grid offset 7)"),
     "train_w14_hier": Workload("train_w14_hier", B=64, C=192, H=28, W=28, w=14, s=7, mix=True,
                                backward=True,
                                note="fp32 training step with the 7x7 sub-window table folded on "

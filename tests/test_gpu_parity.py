@@ -1008,7 +1008,8 @@ def test_dwconv_full_size_sampled():
 SHIFT_CASES = [(2, 3, 28, 28, 14, 7, 7), (1, 2, 30, 25, 14, 3, 11), (2, 3, 17, 13, 4, 2, 1),
                (1, 2, 128, 128, 14, 7, 7), (2, 2, 9, 9, 7, 0, 3), (5, 4, 28, 28, 14, 7, 7),
                (3, 2, 5, 40, 14, 13, 0), (1, 2, 40, 40, 20, 10, 10), (2, 3, 42, 36, 14, 6, 4),
-               (1, 2, 14, 14, 14, 1, 13), (17, 3, 28, 28, 14, 7, 0), (3, 2, 28, 28, 14, 0, 7)]
+               (1, 2, 14, 14, 14, 1, 13), (17, 3, 28, 28, 14, 7, 0), (3, 2, 28, 28, 14, 0, 7),
+               (2, 3, 56, 56, 14, 7, 7), (5, 2, 56, 56, 14, 0, 7)]
 
 
 def _window_shift_grid(x, w, oy, ox, dy, dx):
@@ -1024,7 +1025,9 @@ def _window_shift_grid(x, w, oy, ox, dy, dx):
 @pytest.mark.parametrize("B,C,H,W,oy,ox", [(4, 300, 28, 28, 7, 7), (3, 129, 30, 44, 5, 9),
                                            (2, 130, 40, 36, 6, 4), (1, 260, 17, 13, 13, 0),
                                            (2, 140, 128, 128, 7, 7), (17, 40, 28, 28, 7, 0),
-                                           (33, 24, 28, 28, 0, 7), (16, 33, 28, 28, 7, 7)])
+                                           (33, 24, 28, 28, 0, 7), (16, 33, 28, 28, 7, 7),
+                                           (3, 40, 56, 56, 7, 7), (17, 24, 56, 56, 7, 0),
+                                           (2, 33, 56, 56, 0, 7)])
 def test_forward_shifted_tab_bitwise_all_channels(B, C, H, W, oy, ox):
     """One-hot tables at a different offset in every channel on an offset window grid: the fp32
     w = 14 kernels' output (the table kernel; for offsets of 0 or 7 on 28x28 maps the rolled-map
@@ -1115,13 +1118,15 @@ def test_backward_shifted(B, C, H, W, w, oy, ox, mix, src):
     assert torch.equal(dx, dx2) and torch.equal(dT, dT2)
 
 
-@pytest.mark.parametrize("B,C,oy,ox", [(4, 150, 7, 7), (17, 40, 7, 0), (33, 24, 0, 7)])
-def test_backward_shifted_roll_dx_bitwise_all_channels(B, C, oy, ox):
-    """One-hot tables on the rolled map (offsets 0 or 7, 28x28): dX = M^T G is G shifted back
-    inside each window of the offset grid, bit for bit, in every channel, so the masked
+@pytest.mark.parametrize("B,C,H,oy,ox", [(4, 150, 28, 7, 7), (17, 40, 28, 7, 0),
+                                         (33, 24, 28, 0, 7), (3, 40, 56, 7, 7),
+                                         (17, 16, 56, 0, 7)])
+def test_backward_shifted_roll_dx_bitwise_all_channels(B, C, H, oy, ox):
+    """One-hot tables on the rolled map (offsets 0 or 7, 28x28 and 56x56): dX = M^T G is G shifted
+    back inside each window of the offset grid, bit for bit, in every channel, so the masked
     transposed product drops every pair across pieces and the stores go back through the roll."""
-    w, H = 14, 28
-    say(f"backward shifted roll dx shift all channels B={B} C={C} o=({oy},{ox})")
+    w = 14
+    say(f"backward shifted roll dx shift all channels B={B} C={C} H={H} o=({oy},{ox})")
     x = synth.normal_f32((B, C, H, H), 1.0, seed=43)
     g = synth.normal_f32((B, C, H, H), 1.0, seed=44)
     L1 = 2 * w - 1
@@ -1133,11 +1138,12 @@ def test_backward_shifted_roll_dx_bitwise_all_channels(B, C, oy, ox):
     assert np.array_equal(host(got), _window_shift_grid(g, w, oy, ox, -dy, -dx))
 
 
-def test_backward_shifted_roll_partial_outputs():
+@pytest.mark.parametrize("H", [28, 56])
+def test_backward_shifted_roll_partial_outputs(H):
     """The rolled-map backward with only dx or only dT: the other stays unwritten, the one asked
     for matches the oracle."""
-    B, C, H, W, w, o = 5, 3, 28, 28, 14, 7
-    say("backward shifted roll partial outputs")
+    B, C, W, w, o = 5, 3, H, 14, 7
+    say(f"backward shifted roll partial outputs H={H}")
     x = synth.normal_f32((B, C, H, W), 1.0, seed=255)
     T = synth.normal_f32((C, 2 * w - 1, 2 * w - 1), 0.05, seed=256)
     dy = synth.normal_f32((B, C, H, W), 1.0, seed=257)
