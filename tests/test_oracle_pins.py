@@ -645,6 +645,59 @@ def test_shifted_window_borders_move():
         assert np.array_equal(y[0, 0, :, px], np.broadcast_to(want, (4,)))
 
 
+def rolled_masked_layer(x, T, w, oy, ox):
+    """The half-window offset grid computed the way the rolled-map kernels do: roll the map by
+    (-oy, -ox), take the plain grid's windows, keep only the pairs whose pixels come from one
+    piece (quadrants that agree on every axis the roll split: the last window row when oy != 0,
+    the last window column when ox != 0), then roll the result back. Written with numpy from
+    that description, not from the oracle."""
+    B, C, H, W = x.shape
+    h = w // 2
+    xr = np.roll(x, (-oy, -ox), axis=(2, 3))
+    nwy, nwx = H // w, W // w
+    py, px = np.divmod(np.arange(w * w), w)
+    out = np.zeros_like(xr)
+    for wy in range(nwy):
+        for wx in range(nwx):
+            ry = oy != 0 and wy == nwy - 1
+            rx = ox != 0 and wx == nwx - 1
+            same = np.ones((w * w, w * w), bool)
+            if ry:
+                same &= (py[:, None] // h) == (py[None, :] // h)
+            if rx:
+                same &= (px[:, None] // h) == (px[None, :] // h)
+            for c in range(C):
+                M = T[c][py[:, None] - py[None, :] + w - 1, px[:, None] - px[None, :] + w - 1]
+                Mm = np.where(same, M, 0.0)
+                blk = xr[:, c, wy * w:(wy + 1) * w, wx * w:(wx + 1) * w].reshape(B, w * w)
+                out[:, c, wy * w:(wy + 1) * w, wx * w:(wx + 1) * w] = \
+                    (blk @ Mm.T).reshape(B, w, w)
+    return np.roll(out, (oy, ox), axis=(2, 3))
+
+
+@pytest.mark.parametrize("H,oy,ox", [(28, 7, 7), (28, 7, 0), (28, 0, 7), (56, 7, 7), (14, 7, 7)])
+def test_rolled_map_equals_offset_grid(H, oy, ox):
+    """The identity the rolled-map kernels rest on: with w = 14 and offsets of 0 or w / 2 on maps
+    whose sides are multiples of w, the layer on the offset grid (zero-padded border windows) is
+    the masked plain-grid product on the rolled map, rolled back."""
+    w = 14
+    x = rnd((2, 2, H, H), seed=340 + H)
+    T = rnd((2, 2 * w - 1, 2 * w - 1), 0.1, seed=341)
+    assert np.allclose(O.wbmm_forward_shifted(x, w, oy, ox, T=T),
+                       rolled_masked_layer(x, T, w, oy, ox), rtol=0, atol=1e-12)
+
+
+def test_rolled_map_without_mask_differs():
+    """Without the mask the rolled map's plain product mixes pixels of different offset windows:
+    the identity above depends on the mask (a check that the pin can fail)."""
+    w, H = 14, 28
+    x = rnd((1, 1, H, H), seed=350)
+    T = rnd((1, 27, 27), 0.1, seed=351)
+    plain_rolled = np.roll(O.wbmm_forward(np.roll(x, (-7, -7), axis=(2, 3)), w, T=T), (7, 7),
+                           axis=(2, 3))
+    assert not np.allclose(O.wbmm_forward_shifted(x, w, 7, 7, T=T), plain_rolled, atol=1e-6)
+
+
 @pytest.mark.parametrize("oy,ox", [(2, 3), (3, 0)])
 def test_shifted_backward_adjoint_and_fd(oy, ox):
     """dx by the adjoint identity <WBMM_s(x), g> = <x, dX_s(g)>; dT by central differences of
