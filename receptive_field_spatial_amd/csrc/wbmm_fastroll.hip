@@ -6,18 +6,18 @@ namespace wbmm {
 
 // ------------------------------------------------------------------- rolled offset grid
 // The window grid offset by (oy, ox), each 0 or WS / 2, on IH x IW maps whose sides are multiples
-// of WS (the interleaved layers of the WBMM reading notes, "Limitation": windows shifted between
-// layers; pixels outside the map are zero). Rolling the map by (-oy, -ox) moves every window of
+// of WS [gecl.asia reading notes, "Limitation": windows interleaved between layers; pixels
+// outside the map are zero, as for any ragged map]. Rolling the map by (-oy, -ox) moves every window of
 // the offset grid, as whole quadrants at their own window positions, into one window of the plain
 // grid of the rolled map: a plain window in the last window row (oy != 0) holds the lower half of
 // an offset window above its upper half, and likewise for the last column, so a plain window
 // holds one, two or four pieces. The product keeps the pairs of one piece: the matrix is masked
 // to pairs whose quadrants agree on every split axis, and the pixels outside the map, zero in the
 // offset grid, are simply not there. The work is then that of the plain grid (4 windows of a 28 x
-// 28 map against 9 in the offset grid).
+// 28 map against 9 in the offset grid, 16 of a 56 x 56 map against 25).
 //
-// Unit = 16 images of one channel, one workgroup of 4 waves; wave k holds the plain window k
-// (row-major 2 x 2) of every image of the unit in its region (image slot = MFMA column), so a
+// Unit = 16 images of one channel and 4 window positions, one workgroup of 4 waves; wave k holds
+// window position k0 + k (row-major) of every image of the unit (image slot = MFMA column), so a
 // wave's windows share one mask and the MFMA table operand stays one value per lane:
 //   mask bit 1 (row split): wave's window row is the last and oy != 0; bit 0 likewise for columns;
 //   pair (i, j) is kept iff ((quadrant(i) ^ quadrant(j)) & mask) == 0.
@@ -191,8 +191,6 @@ __device__ __forceinline__ void roll_store(float* o, float* o2, const Unit& U, c
     }
 }
 
-// Forward on the offset grid: z = masked product of each wave's windows, written to y (and
-// z_save); the 3 x 3 mix runs afterwards on the whole map.
 // The unit's 16 pre-mix maps in LDS (map coordinates) -> y (3 x 3 mix, or a copy) and z_save.
 // A thread walks an image column down the 28 rows with a 3 x 3 register window (3 LDS reads per
 // pixel; the neighbour columns' reads are clamped to the own column at the image border and
@@ -358,9 +356,9 @@ __device__ __forceinline__ void roll_dt_chunk(const float* regions, const float*
 
 // Backward on the offset grid (dy is the map gradient G of the product; the mix adjoint, if any,
 // has run before): dX = masked M^T G per wave, stored through the roll; the table-gradient pass
-// walks the unit in 16 chunks of 4 windows of one class (chunk ci: window ci / 4 of images
-// 4 (ci % 4) .. +3), with the row pairs of one band only where the rows are split and the column
-// mask applied when the class's chains are promoted.
+// walks the unit in 16 chunks of 4 windows of one position (chunk ci: position k0 + ci / 4 of
+// images 4 (ci % 4) .. +3), with the row pairs of one band only where the rows are split and the
+// column mask applied when the class's chains are promoted.
 template <class S>
 __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3, 8)))
 k_roll_bwd(FastArgs a) {
