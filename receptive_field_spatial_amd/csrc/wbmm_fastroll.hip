@@ -1,5 +1,5 @@
 // Fast fp32 WBMM forward and backward on a window grid offset by half a window (w = 14, offsets
-// 0 or 7, NCHW 28 x 28 and 56 x 56 maps), through the rolled map.
+// 0 or 7, NCHW 14 x 14, 28 x 28 and 56 x 56 maps), through the rolled map.
 #include "wbmm_fast.hpp"
 
 namespace wbmm {
@@ -16,9 +16,10 @@ namespace wbmm {
 // offset grid, are simply not there. The work is then that of the plain grid (4 windows of a 28 x
 // 28 map against 9 in the offset grid, 16 of a 56 x 56 map against 25).
 //
-// Unit = 16 images of one channel and 4 window positions, one workgroup of 4 waves; wave k holds
-// window position k0 + k (row-major) of every image of the unit (image slot = MFMA column), so a
-// wave's windows share one mask and the MFMA table operand stays one value per lane:
+// Unit = 16 images of one channel and 4 window positions (14 x 14 maps, one window per image: 64
+// images), one workgroup of 4 waves; wave k holds window position k0 + k (row-major) of every
+// image of the unit (14 x 14: the window of images 16k .. 16k + 15), image slot = MFMA column, so
+// a wave's windows share one mask and the MFMA table operand stays one value per lane:
 //   mask bit 1 (row split): wave's window row is the last and oy != 0; bit 0 likewise for columns;
 //   pair (i, j) is kept iff ((quadrant(i) ^ quadrant(j)) & mask) == 0.
 struct RollGeo {
@@ -38,27 +39,60 @@ __device__ __forceinline__ int wrap(int v, int n) { return v >= n ? v - n : v; }
 
 // A unit is 16 images of one channel and 4 window positions: all of a 28 x 28 map's, a quarter
 // of a 56 x 56 map's (units per channel: ceil(B / 16) image groups x NWIN / 4 position groups,
-// in a.groups). k0: the unit's first window position; wave k holds position k0 + k.
+// in a.groups); on 14 x 14 maps 64 images (ceil(B / 64) per channel). k0: the unit's first window
+// position.
+template <class S>
+constexpr int roll_imgs() { return S::NWIN == 1 ? 64 : 16; }
 template <class S>
 __device__ __forceinline__ Unit roll_unit(const FastArgs& a, int u, int& k0) {
-  constexpr int NPG = S::NWIN / 4;
-  static_assert(S::NWIN % 4 == 0, "whole position groups");
+  constexpr int NPG = S::NWIN == 1 ? 1 : S::NWIN / 4;
+  static_assert(S::NWIN == 1 || S::NWIN % 4 == 0, "whole position groups");
   Unit U;
   U.c = u / a.groups;
   const int rem = u - U.c * a.groups, ig = rem / NPG;
   k0 = 4 * (rem - ig * NPG);
-  const int uimg0 = 16 * ig;
+  const int uimg0 = roll_imgs<S>() * ig;
   U.base = ((size_t)uimg0 * a.C + U.c) * S::PLANE;
   U.cp = a.C * S::PLANE;
   const int left = a.B - uimg0;
-  U.nimg = left < 16 ? left : 16;
+  U.nimg = left < roll_imgs<S>() ? left : roll_imgs<S>();
   return U;
 }
+// Wave k's part of the unit: its images (a Unit of at most 16) and its window position.
 template <class S>
-int roll_groups(int B) { return (B + 15) / 16 * (S::NWIN / 4); }
+__device__ __forceinline__ Unit roll_wave(const Unit& U, int k0, int wave, int& pos, int& img0) {
+  Unit W = U;
+  if constexpr (S::NWIN == 1) {
+    img0 = 16 * wave;
+    W.base = U.base + (size_t)img0 * U.cp;
+    const int left = U.nimg - img0;
+    W.nimg = left < 0 ? 0 : (left < 16 ? left : 16);
+    pos = 0;
+  } else {
+    img0 = 0;
+    pos = k0 + wave;
+  }
+  return W;
+}
+// Table-gradient chunk ci (4 windows): its first image within the unit and its window position.
+// Its windows sit in region ci / 4 at slots 4 (ci % 4) .. + 3 either way.
+template <class S>
+__device__ __forceinline__ void roll_chunk(int k0, int ci, int& img0, int& pos) {
+  if constexpr (S::NWIN == 1) {
+    img0 = 4 * ci;
+    pos = 0;
+  } else {
+    img0 = 4 * (ci & 3);
+    pos = k0 + (ci >> 2);
+  }
+}
+template <class S>
+int roll_groups(int B) {
+  return S::NWIN == 1 ? (B + 63) / 64 : (B + 15) / 16 * (S::NWIN / 4);
+}
 // whole images in one unit: the forward applies the 3 x 3 mix on chip
 template <class S>
-constexpr bool roll_staged() { return S::NWIN == 4; }
+constexpr bool roll_staged() { return S::NWIN <= 4; }
 
 typedef float f4a4 __attribute__((ext_vector_type(4), aligned(4)));
 typedef float f3a4 __attribute__((ext_vector_type(3), aligned(4)));
@@ -191,7 +225,7 @@ __device__ __forceinline__ void roll_store(float* o, float* o2, const Unit& U, c
     }
 }
 
-// The unit's 16 pre-mix maps in LDS (map coordinates) -> y (3 x 3 mix, or a copy) and z_save.
+// The unit's pre-mix maps in LDS (map coordinates) -> y (3 x 3 mix, or a copy) and z_save.
 // A thread walks an image column down the 28 rows with a 3 x 3 register window (3 LDS reads per
 // pixel; the neighbour columns' reads are clamped to the own column at the image border and
 // selected away); consecutive threads own consecutive columns, so the stores are row runs.
@@ -204,7 +238,7 @@ __device__ __forceinline__ void roll_epilogue(const FastArgs& a, const float* Z,
 #pragma unroll
     for (int q = 0; q < 9; ++q) w9[q] = a.mixw[(size_t)U.c * 9 + q];
   }
-  for (int col = threadIdx.x; col < 16 * S::IW; col += kThreads) {
+  for (int col = threadIdx.x; col < roll_imgs<S>() * S::IW; col += kThreads) {
     const int n = col / S::IW, v = col % S::IW;
     if (n >= U.nimg) break;  // columns are image-major: the rest are past the batch too
     const float* zc = Z + n * S::PLANE + v;
@@ -272,7 +306,7 @@ __device__ __forceinline__ void roll_stage(float* Z, const RollGeo& g, const v4f
 // accumulators and the mix runs as a pass of its own.)
 template <class S>
 constexpr int roll_fwd_floats() {
-  return roll_staged<S>() ? S::LP + 16 * S::PLANE : S::LP + (S::CMAX + 4) / 4 * 4;
+  return roll_staged<S>() ? S::LP + roll_imgs<S>() * S::PLANE : S::LP + (S::CMAX + 4) / 4 * 4;
 }
 
 template <class S, bool MIX>
@@ -281,13 +315,15 @@ k_roll_fwd(FastArgs a) {
   extern __shared__ __attribute__((aligned(16))) float smem_f[];
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   float* Ts = smem_f;
-  constexpr int ZOFF = roll_staged<S>() ? S::LP + 16 * S::PLANE - (S::CMAX + 4) / 4 * 4 : S::LP;
+  constexpr int ZOFF =
+      roll_staged<S>() ? S::LP + roll_imgs<S>() * S::PLANE - (S::CMAX + 4) / 4 * 4 : S::LP;
   static_assert(ZOFF >= S::LP && (roll_staged<S>() || !MIX), "zeros after the table");
-  int k0;
+  int k0, pos, img0;
   const Unit U = roll_unit<S>(a, blockIdx.x, k0);
-  const RollGeo g = roll_geo<S>(a, k0 + wave);
+  const Unit W = roll_wave<S>(U, k0, wave, pos, img0);
+  const RollGeo g = roll_geo<S>(a, pos);
   RollQuad<S> xq;
-  xq.load(a.x + U.base, U, g, lane);
+  xq.load(a.x + W.base, W, g, lane);
   for (int q = threadIdx.x; q < S::L; q += kThreads) Ts[q] = a.T[(size_t)U.c * S::L + q];
   for (int q = threadIdx.x; q <= S::CMAX; q += kThreads) Ts[ZOFF + q] = 0.f;
   __syncthreads();
@@ -299,26 +335,26 @@ k_roll_fwd(FastArgs a) {
     contract_roll<S, false, ZOFF, 5, 4>(Ts, xq.v, lane, g.gm, acc1);
     contract_roll<S, false, ZOFF, 9, 4>(Ts, xq.v, lane, g.gm, acc2);
     __syncthreads();
-    roll_stage<S, 0, 5>(Z, g, acc0, lane);
-    roll_stage<S, 5, 4>(Z, g, acc1, lane);
-    roll_stage<S, 9, 4>(Z, g, acc2, lane);
+    roll_stage<S, 0, 5>(Z + img0 * S::PLANE, g, acc0, lane);
+    roll_stage<S, 5, 4>(Z + img0 * S::PLANE, g, acc1, lane);
+    roll_stage<S, 9, 4>(Z + img0 * S::PLANE, g, acc2, lane);
     __syncthreads();
     roll_epilogue<S, MIX>(a, Z, U);
   } else {  // each third stored while the next is contracted
     {
       v4f acc[5];
       contract_roll<S, false, ZOFF, 0, 5>(Ts, xq.v, lane, g.gm, acc);
-      roll_store<S, 0, 5>(a.y, a.zsave, U, g, acc, lane);
+      roll_store<S, 0, 5>(a.y, a.zsave, W, g, acc, lane);
     }
     {
       v4f acc[4];
       contract_roll<S, false, ZOFF, 5, 4>(Ts, xq.v, lane, g.gm, acc);
-      roll_store<S, 5, 4>(a.y, a.zsave, U, g, acc, lane);
+      roll_store<S, 5, 4>(a.y, a.zsave, W, g, acc, lane);
     }
     {
       v4f acc[4];
       contract_roll<S, false, ZOFF, 9, 4>(Ts, xq.v, lane, g.gm, acc);
-      roll_store<S, 9, 4>(a.y, a.zsave, U, g, acc, lane);
+      roll_store<S, 9, 4>(a.y, a.zsave, W, g, acc, lane);
     }
   }
 }
@@ -356,9 +392,9 @@ __device__ __forceinline__ void roll_dt_chunk(const float* regions, const float*
 
 // Backward on the offset grid (dy is the map gradient G of the product; the mix adjoint, if any,
 // has run before): dX = masked M^T G per wave, stored through the roll; the table-gradient pass
-// walks the unit in 16 chunks of 4 windows of one position (chunk ci: position k0 + ci / 4 of
-// images 4 (ci % 4) .. +3), with the row pairs of one band only where the rows are split and the
-// column mask applied when the class's chains are promoted.
+// walks the unit in 16 chunks of 4 windows of one position (roll_chunk), with the row pairs of one
+// band only where the rows are split and the column mask applied when the class's chains are
+// promoted.
 template <class S>
 __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3, 8)))
 k_roll_bwd(FastArgs a) {
@@ -368,15 +404,16 @@ k_roll_bwd(FastArgs a) {
   float* regions = smem_f + bwd_tsz<S, false>();
   float* R = regions + wave * S::RSZ;
   const int u = blockIdx.x;
-  int k0;
+  int k0, pos, img0;
   const Unit U = roll_unit<S>(a, u, k0);
-  const RollGeo g = roll_geo<S>(a, k0 + wave);
+  const Unit W = roll_wave<S>(U, k0, wave, pos, img0);
+  const RollGeo g = roll_geo<S>(a, pos);
   // G of the wave's windows in registers; during dX the zeros of the masked operands sit at the
   // start of the regions, which take G (for the table gradient) only after dX
   constexpr int ZOFF = bwd_tsz<S, false>();
   static_assert(S::CMAX < S::RSZ, "zeros inside the first region");
   RollQuad<S> gq;
-  gq.load(a.dy + U.base, U, g, lane);
+  gq.load(a.dy + W.base, W, g, lane);
   for (int q = threadIdx.x; q < S::L; q += kThreads) Ts[q] = a.T[(size_t)U.c * S::L + q];
   for (int q = threadIdx.x; q <= S::CMAX; q += kThreads) Ts[ZOFF + q] = 0.f;
   __syncthreads();
@@ -385,17 +422,17 @@ k_roll_bwd(FastArgs a) {
     {
       v4f acc[5];
       contract_roll<S, true, ZOFF, 0, 5>(Ts, gq.v, lane, g.gm, acc);
-      roll_store<S, 0, 5>(a.dx, nullptr, U, g, acc, lane);
+      roll_store<S, 0, 5>(a.dx, nullptr, W, g, acc, lane);
     }
     {
       v4f acc[4];
       contract_roll<S, true, ZOFF, 5, 4>(Ts, gq.v, lane, g.gm, acc);
-      roll_store<S, 5, 4>(a.dx, nullptr, U, g, acc, lane);
+      roll_store<S, 5, 4>(a.dx, nullptr, W, g, acc, lane);
     }
     {
       v4f acc[4];
       contract_roll<S, true, ZOFF, 9, 4>(Ts, gq.v, lane, g.gm, acc);
-      roll_store<S, 9, 4>(a.dx, nullptr, U, g, acc, lane);
+      roll_store<S, 9, 4>(a.dx, nullptr, W, g, acc, lane);
     }
   }
   if (!a.want_dT) return;
@@ -420,8 +457,10 @@ k_roll_bwd(FastArgs a) {
     const int maxoff = (U.nimg - 1) * U.cp + S::PLANE - 1;
     float stgA[EPT], stgB[EPT];
     auto load_chunk = [&](float (&stg)[EPT], int ci) {
-      const RollGeo cg = roll_geo<S>(a, k0 + (ci >> 2));
-      const int cbase = 4 * (ci & 3) * U.cp;
+      int cimg, cpos;
+      roll_chunk<S>(k0, ci, cimg, cpos);
+      const RollGeo cg = roll_geo<S>(a, cpos);
+      const int cbase = cimg * U.cp;
       const int tid = opaque_lane(threadIdx.x);
 #pragma unroll
       for (int j = 0; j < EPT; ++j) {
@@ -448,7 +487,9 @@ k_roll_bwd(FastArgs a) {
       }
       __syncthreads();
       load_chunk(stg, ci + 2 < 16 ? ci + 2 : 15);
-      const RollGeo cg = roll_geo<S>(a, k0 + (ci >> 2));
+      int cimg, cpos;
+      roll_chunk<S>(k0, ci, cimg, cpos);
+      const RollGeo cg = roll_geo<S>(a, cpos);
       const bool band = (cg.gm & 2) != 0, split = (cg.gm & 1) != 0;
       const int n0 = 16 * (ci >> 2) + 4 * (ci & 3);
       const bool flush = (ci & 3) == 3;
@@ -491,7 +532,8 @@ k_roll_bwd(FastArgs a) {
 }
 
 static_assert(lds_fits(roll_fwd_floats<S28>() * 4, 3) && lds_fits(bwd_lds<S28>(), 3) &&
-                  lds_fits(roll_fwd_floats<S56>() * 4, 3) && lds_fits(bwd_lds<S56>(), 3),
+                  lds_fits(roll_fwd_floats<S56>() * 4, 3) && lds_fits(bwd_lds<S56>(), 3) &&
+                  lds_fits(roll_fwd_floats<S14>() * 4, 3) && lds_fits(bwd_lds<S14>(), 3),
               "three rolled-grid workgroups per CU");
 
 namespace {
@@ -505,12 +547,14 @@ hipError_t launch_roll(Fn fn, int lds, FastArgs a, hipStream_t st) {
 }
 }  // namespace
 
-// The offset grid on the rolled map: fp32, w = 14, NCHW 28 x 28 or 56 x 56, offsets 0 or 7 (not
-// both 0).
+// The offset grid on the rolled map: fp32, w = 14, NCHW 14 x 14, 28 x 28 or 56 x 56, offsets 0 or
+// 7 (not both 0).
 static bool roll_shape_ok(int B, int C, int H, int W, int w, int layout, int oy, int ox) {
-  return w == 14 && layout == 0 && H == W && (H == 28 || H == 56) && (oy == 0 || oy == 7) &&
+  return w == 14 && layout == 0 && H == W && (H == 14 || H == 28 || H == 56) &&
+         (oy == 0 || oy == 7) &&
          (ox == 0 || ox == 7) && (oy != 0 || ox != 0) && B >= 1 && C >= 1 &&
-         offsets_fit(C, H, W);
+         offsets_fit(C, H, W) &&
+         (H != 14 || (size_t)64 * C * H * W < ((size_t)1 << 31));  // 64-image units: int offsets
 }
 
 bool fast_roll_forward_ok(const FwdRequest& r) {
@@ -529,8 +573,8 @@ size_t fast_roll_forward_workspace(const FwdRequest& r) {
              : 0;
 }
 
-// The layer on the offset grid: y (the 3 x 3 mix applied on chip on 28 x 28 maps, as a pass of
-// its own after the product on 56 x 56 ones) and z_save (the pre-mix map).
+// The layer on the offset grid: y (the 3 x 3 mix applied on chip on 14 x 14 and 28 x 28 maps, as
+// a pass of its own after the product on 56 x 56 ones) and z_save (the pre-mix map).
 hipError_t launch_forward_fast_roll(const FwdRequest& r, hipStream_t st) {
   if (!fast_roll_forward_ok(r)) return hipErrorInvalidValue;
   FastArgs a{};
@@ -546,6 +590,9 @@ hipError_t launch_forward_fast_roll(const FwdRequest& r, hipStream_t st) {
   if (r.H == 28)
     return r.mixw ? launch_roll<S28>(k_roll_fwd<S28, true>, roll_fwd_floats<S28>() * 4, a, st)
                   : launch_roll<S28>(k_roll_fwd<S28, false>, roll_fwd_floats<S28>() * 4, a, st);
+  if (r.H == 14)
+    return r.mixw ? launch_roll<S14>(k_roll_fwd<S14, true>, roll_fwd_floats<S14>() * 4, a, st)
+                  : launch_roll<S14>(k_roll_fwd<S14, false>, roll_fwd_floats<S14>() * 4, a, st);
   if (!r.mixw) return launch_roll<S56>(k_roll_fwd<S56, false>, roll_fwd_floats<S56>() * 4, a, st);
   float* z = (float*)(r.zsave ? r.zsave : r.ws);
   a.mixw = nullptr;
@@ -560,7 +607,8 @@ hipError_t launch_forward_fast_roll(const FwdRequest& r, hipStream_t st) {
 size_t fast_roll_backward_workspace(const BwdRequest& r) {
   if (!fast_roll_backward_ok(r)) return 0;
   const size_t L = (size_t)(2 * r.w - 1) * (2 * r.w - 1);
-  const int g = r.H == 28 ? roll_groups<S28>(r.B) : roll_groups<S56>(r.B);
+  const int g = r.H == 14 ? roll_groups<S14>(r.B)
+                : r.H == 28 ? roll_groups<S28>(r.B) : roll_groups<S56>(r.B);
   return ((size_t)r.C * g * L * 8 + 255) / 256 * 256;
 }
 
@@ -581,13 +629,14 @@ hipError_t launch_backward_fast_roll(const BwdRequest& r, hipStream_t st) {
   a.roy = r.oy;
   a.rox = r.ox;
   if (!a.want_dx && !a.want_dT) return hipSuccess;
-  const bool s28 = r.H == 28;
-  hipError_t e = s28 ? launch_roll<S28>(k_roll_bwd<S28>, bwd_lds<S28>(), a, st)
-                     : launch_roll<S56>(k_roll_bwd<S56>, bwd_lds<S56>(), a, st);
+  hipError_t e = r.H == 14   ? launch_roll<S14>(k_roll_bwd<S14>, bwd_lds<S14>(), a, st)
+                  : r.H == 28 ? launch_roll<S28>(k_roll_bwd<S28>, bwd_lds<S28>(), a, st)
+                              : launch_roll<S56>(k_roll_bwd<S56>, bwd_lds<S56>(), a, st);
   if (e != hipSuccess || !a.want_dT) return e;
   const int L = (2 * r.w - 1) * (2 * r.w - 1);
-  return launch_bwd_reduce(a.partT, nullptr, s28 ? roll_groups<S28>(r.B) : roll_groups<S56>(r.B),
-                           r.C, L, r.dT, nullptr, st);
+  const int g = r.H == 14 ? roll_groups<S14>(r.B)
+                : r.H == 28 ? roll_groups<S28>(r.B) : roll_groups<S56>(r.B);
+  return launch_bwd_reduce(a.partT, nullptr, g, r.C, L, r.dT, nullptr, st);
 }
 
 }  // namespace wbmm

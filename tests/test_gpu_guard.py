@@ -310,7 +310,7 @@ def test_guard_bf16_backward(B, H, mix):
 
 @pytest.mark.parametrize("B,C,H,W,w,o", [(5, 3, 28, 28, 14, 7), (2, 2, 30, 25, 14, 3),
                                          (2, 2, 17, 13, 4, 2), (17, 3, 28, 28, 14, 7),
-                                         (3, 2, 56, 56, 14, 7)])
+                                         (3, 2, 56, 56, 14, 7), (66, 2, 14, 14, 14, 7)])
 def test_guard_shifted(B, C, H, W, w, o):
     """The interleaved grid (the rolled-map kernels for offset 7 on 28x28 maps, the table kernel
     and repacked fast kernels for other w = 14 grids): outputs and workspaces guarded."""

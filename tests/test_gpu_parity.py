@@ -1009,7 +1009,8 @@ SHIFT_CASES = [(2, 3, 28, 28, 14, 7, 7), (1, 2, 30, 25, 14, 3, 11), (2, 3, 17, 1
                (1, 2, 128, 128, 14, 7, 7), (2, 2, 9, 9, 7, 0, 3), (5, 4, 28, 28, 14, 7, 7),
                (3, 2, 5, 40, 14, 13, 0), (1, 2, 40, 40, 20, 10, 10), (2, 3, 42, 36, 14, 6, 4),
                (1, 2, 14, 14, 14, 1, 13), (17, 3, 28, 28, 14, 7, 0), (3, 2, 28, 28, 14, 0, 7),
-               (2, 3, 56, 56, 14, 7, 7), (5, 2, 56, 56, 14, 0, 7)]
+               (2, 3, 56, 56, 14, 7, 7), (5, 2, 56, 56, 14, 0, 7), (70, 2, 14, 14, 14, 7, 7),
+               (3, 2, 14, 14, 14, 7, 0)]
 
 
 def _window_shift_grid(x, w, oy, ox, dy, dx):
@@ -1027,7 +1028,8 @@ def _window_shift_grid(x, w, oy, ox, dy, dx):
                                            (2, 140, 128, 128, 7, 7), (17, 40, 28, 28, 7, 0),
                                            (33, 24, 28, 28, 0, 7), (16, 33, 28, 28, 7, 7),
                                            (3, 40, 56, 56, 7, 7), (17, 24, 56, 56, 7, 0),
-                                           (2, 33, 56, 56, 0, 7)])
+                                           (2, 33, 56, 56, 0, 7), (65, 20, 14, 14, 7, 7),
+                                           (5, 24, 14, 14, 0, 7)])
 def test_forward_shifted_tab_bitwise_all_channels(B, C, H, W, oy, ox):
     """One-hot tables at a different offset in every channel on an offset window grid: the fp32
     w = 14 kernels' output (the table kernel; for offsets of 0 or 7 on 28x28 maps the rolled-map
@@ -1120,9 +1122,9 @@ def test_backward_shifted(B, C, H, W, w, oy, ox, mix, src):
 
 @pytest.mark.parametrize("B,C,H,oy,ox", [(4, 150, 28, 7, 7), (17, 40, 28, 7, 0),
                                          (33, 24, 28, 0, 7), (3, 40, 56, 7, 7),
-                                         (17, 16, 56, 0, 7)])
+                                         (17, 16, 56, 0, 7), (70, 16, 14, 7, 7)])
 def test_backward_shifted_roll_dx_bitwise_all_channels(B, C, H, oy, ox):
-    """One-hot tables on the rolled map (offsets 0 or 7, 28x28 and 56x56): dX = M^T G is G shifted
+    """One-hot tables on the rolled map (offsets 0 or 7, 14x14 to 56x56): dX = M^T G is G shifted
     back inside each window of the offset grid, bit for bit, in every channel, so the masked
     transposed product drops every pair across pieces and the stores go back through the roll."""
     w = 14
@@ -1138,7 +1140,7 @@ def test_backward_shifted_roll_dx_bitwise_all_channels(B, C, H, oy, ox):
     assert np.array_equal(host(got), _window_shift_grid(g, w, oy, ox, -dy, -dx))
 
 
-@pytest.mark.parametrize("H", [28, 56])
+@pytest.mark.parametrize("H", [14, 28, 56])
 def test_backward_shifted_roll_partial_outputs(H):
     """The rolled-map backward with only dx or only dT: the other stays unwritten, the one asked
     for matches the oracle."""
