@@ -224,6 +224,16 @@ def load_traffic(workload: str, kernel: str):
     return k.get("hbm_bytes_per_launch")
 
 
+def profiled_kernel_name(workload: str, kernel: str):
+    """The kernel that the committed counter run of this workload saw under a bench label."""
+    p = os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
+    if not os.path.exists(p):
+        return None
+    with open(p) as f:
+        k = json.load(f).get("kernels", {}).get(kernel)
+    return None if k is None else k.get("kernel_name")
+
+
 # ----------------------------------------------------------------------------- HIP events
 class HipEvents:
     """Raw hipEvent_t handles (the library records them around its main kernel launch)."""
@@ -505,6 +515,7 @@ def run(args):
     roof["frac_of_measured"] = round(roof["achieved"] / meas, 4)
     roof["traffic"] = load_traffic(wl.name + ("_cached" if args.cached else ""), kname)
     roof["kernel"] = kname
+    roof["kernel_profiled_as"] = profiled_kernel_name(wl.name + ("_cached" if args.cached else ""), kname)
     roof["kernel_us"] = round(ksec * 1e6, 2)
     roof["algorithmic_per_launch"] = kflops if mfma_bound else kbytes
 
