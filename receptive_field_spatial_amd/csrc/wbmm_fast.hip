@@ -232,26 +232,43 @@ k_bwd_ls(FastArgs a) {
   const int ir0 = wave * S::IPW;
   const bool mix = a.mixw != nullptr, wantW = mix && a.want_dW;
 
-  // z for the dWmix sums (one register column per pass), table and dy, all in flight together
   float zpre[BwdCol<S>::NP][S::IH];
-  if (wantW) {
-    const float* zu = a.zsaved + U.base;
-#pragma unroll
-    for (int p = 0; p < BwdCol<S>::NP; ++p) {
-      const BwdCol<S> col(p, lane);
-      const int ir = ir0 + col.im < U.nimg ? ir0 + col.im : U.nimg - 1;
-      const int o = ir * U.cp + col.v;
-#pragma unroll
-      for (int h = 0; h < S::IH; ++h) zpre[p][h] = zu[o + h * S::IW];
-    }
-  }
   {
     PlaneLoad<S> pl;
     pl.issue(a.dy + U.base, U, ir0, lane);
-    for (int q = threadIdx.x; q < S::L; q += kThreads) {
-      const float v = a.T[(size_t)U.c * S::L + q];
-      Ts[q] = v;
-      if constexpr (HIER) Ts[S::LP + q] = v + sub_entry<S>(a.Tsub, U.c, q);
+    // Issue order dy, table, z (z only feeds the dWmix sums). Loads complete in issue order for
+    // the wait counter, so the table's LDS writes and the dy commit wait for dy and the table
+    // only, and z lands during the sweep; the table's loads are clamped and unconditional, all
+    // in flight before its writes.
+    constexpr int TQ = (S::L + kThreads - 1) / kThreads;
+    float tv[TQ], tsv[TQ];
+#pragma unroll
+    for (int j = 0; j < TQ; ++j) {
+      const int q = threadIdx.x + j * kThreads, qc = q < S::L ? q : S::L - 1;
+      tv[j] = a.T[(size_t)U.c * S::L + qc];
+      if constexpr (HIER) tsv[j] = sub_entry<S>(a.Tsub, U.c, qc);
+    }
+    {
+      // z, one register column per pass; unconditional (without dWmix these read dy, always
+      // given, and go unused), so the wait for the table below is not widened at a branch merge
+      const float* zu = (wantW ? a.zsaved : a.dy) + U.base;
+#pragma unroll
+      for (int p = 0; p < BwdCol<S>::NP; ++p) {
+        const BwdCol<S> col(p, lane);
+        const int ir = ir0 + col.im < U.nimg ? ir0 + col.im : U.nimg - 1;
+        const int o = ir * U.cp + col.v;
+#pragma unroll
+        for (int h = 0; h < S::IH; ++h) zpre[p][h] = zu[o + h * S::IW];
+      }
+    }
+    // unguarded writes (entries past the table land in its padding, which nothing reads), so
+    // no load is sunk into a guard that would wait for every load in flight
+    static_assert(S::LP > S::L, "table padding");
+#pragma unroll
+    for (int j = 0; j < TQ; ++j) {
+      const int q = threadIdx.x + j * kThreads, qd = q < S::L ? q : S::L;
+      Ts[qd] = tv[j];
+      if constexpr (HIER) Ts[S::LP + qd] = tv[j] + tsv[j];
     }
     pl.commit(R, lane);
   }
